@@ -1,0 +1,357 @@
+"""Pins for the CPU oracle: each oracle function is checked against something
+other than itself -- a closed form, a textbook route, a library routine, brute
+force or an exact invariant -- and every planted mistake in the oracle source
+must trip at least one pin (mutation check at the bottom).
+
+Sources: "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU"
+(Methodology 1-3), SinkSLOT README (Tensor Contract, API Reference), and
+"Sinkhorn Distances: Lightspeed Computation of Optimal Transportation
+Distances" (named in the FlashSinkhorn 2 reference list) for the matrix-scaling
+form used as the brute-force route.
+"""
+import itertools
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+from scipy.optimize import linear_sum_assignment
+from scipy.spatial.distance import cdist
+from scipy.special import logsumexp
+
+import oracle
+from sk_inputs import random_problem
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _problem(n, m, d, seed, scale=1.0):
+    x, y, a, b = random_problem(n, m, d, seed, scale=scale)
+    return (x.astype(np.float64), y.astype(np.float64), a.astype(np.float64) / a.astype(np.float64).sum(),
+            b.astype(np.float64) / b.astype(np.float64).sum())
+
+
+def _scaling_form(x, y, a, b, eps, n_iters):
+    """Matrix scaling u = a / (K v), v = b / (K^T u), K = exp(-C/eps), started at v = b
+    (the scaling-form image of g = 0); returns (f, g, P) with f = eps log(u/a),
+    g = eps log(v/b) and P = diag(u) K diag(v)."""
+    K = np.exp(-cdist(x, y, "sqeuclidean") / eps)
+    v = b.copy()
+    u = None
+    for _ in range(n_iters):
+        u = a / (K @ v)
+        v = b / (K.T @ u)
+    return eps * np.log(u / a), eps * np.log(v / b), u[:, None] * K * v[None, :]
+
+
+# --------------------------------------------------------------------------- pins
+def pin_scaling_form_trajectory(lib):
+    """Log-domain iterates equal the matrix-scaling iterates (tiny, moderate eps)."""
+    for (n, m, d, seed, eps, iters) in [(7, 5, 2, 11, 0.5, 1), (7, 5, 2, 11, 0.5, 2), (6, 9, 3, 12, 2.0, 15),
+                                        (8, 8, 1, 13, 0.3, 40), (5, 11, 4, 14, 1.0, 7)]:
+        x, y, a, b = _problem(n, m, d, seed)
+        f, g, _ = oracle.sinkhorn(x, y, a, b, eps, iters, lib=lib)
+        fs, gs, _ = _scaling_form(x, y, a, b, eps, iters)
+        scale = cdist(x, y, "sqeuclidean").max()
+        assert np.max(np.abs(f - fs)) <= 1e-11 * scale, (n, m, d, iters)
+        assert np.max(np.abs(g - gs)) <= 1e-11 * scale, (n, m, d, iters)
+
+
+def pin_marginals_scaling_form(lib):
+    """Plan marginals and residual norms equal those of the explicit scaled plan."""
+    for (n, m, d, seed, eps, iters) in [(7, 5, 2, 21, 0.5, 3), (9, 6, 3, 22, 0.8, 1)]:
+        x, y, a, b = _problem(n, m, d, seed)
+        f, g, _ = oracle.sinkhorn(x, y, a, b, eps, iters, lib=lib)
+        _, _, P = _scaling_form(x, y, a, b, eps, iters)
+        rs, cs = oracle.marginals(x, y, a, b, f, g, eps, lib=lib)
+        assert np.allclose(rs, P.sum(1), rtol=1e-11, atol=0)
+        assert np.allclose(cs, P.sum(0), rtol=1e-11, atol=0)
+        r = oracle.residual(x, y, a, b, f, g, eps, lib=lib)
+        er, ec = P.sum(1) - a, P.sum(0) - b
+        want = [np.abs(er).max(), np.abs(ec).max(), np.abs(er).sum(), np.abs(ec).sum()]
+        assert np.allclose(r, want, rtol=1e-8, atol=1e-15)
+        assert want[0] > 1e-6  # a non-trivial residual was compared
+
+
+def pin_m1_closed_form(lib):
+    """m = 1: after one iteration f_i = C_i1 - eps log b_1 (b_1 = sum a), g = 0,
+    grad_i = 2 a_i (x_i - y_1), cost = sum_i a_i C_i1 (unit mass)."""
+    x, y, a, b = _problem(6, 1, 2, 31)
+    eps = 0.37
+    f, g, _ = oracle.sinkhorn(x, y, a, b, eps, 1, lib=lib)
+    C = ((x - y[0]) ** 2).sum(1)
+    assert np.allclose(f, C - eps * np.log(b[0]), rtol=0, atol=1e-13)
+    assert abs(g[0]) <= 1e-13
+    grad = oracle.grad_x(x, y, a, b, g, eps, lib=lib)
+    assert np.allclose(grad, 2 * a[:, None] * (x - y[0]), rtol=0, atol=1e-13)
+    assert abs(oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib) - (a * C).sum()) <= 1e-13
+    # n = 1 (the transpose): f_1 = C_1j-weighted LSE, g_j = C_1j - f_1 + ... ; the plan is b itself
+    x1, y1, a1, b1 = _problem(1, 5, 2, 32)
+    f1, g1, _ = oracle.sinkhorn(x1, y1, a1, b1, eps, 1, lib=lib)
+    C1 = ((y1 - x1[0]) ** 2).sum(1)
+    assert np.allclose(f1 + g1, C1, rtol=0, atol=1e-13)
+    assert abs(oracle.dual_cost(x1, y1, a1, b1, f1, g1, eps, lib=lib) - (b1 * C1).sum()) <= 1e-13
+
+
+def pin_grad_finite_difference(lib):
+    """grad equals the derivative of x -> sum_i a_i f~_i(x) at fixed g (envelope theorem)."""
+    x, y, a, b = _problem(5, 7, 3, 41)
+    rng = np.random.default_rng(42)
+    g = rng.normal(size=7)
+    eps = 0.3
+    grad = oracle.grad_x(x, y, a, b, g, eps, lib=lib)
+    h = 1e-5
+    fd = np.zeros_like(x)
+    for i in range(x.shape[0]):
+        for t in range(x.shape[1]):
+            xp, xm = x.copy(), x.copy()
+            xp[i, t] += h
+            xm[i, t] -= h
+            fp = (a * oracle.half_step(xp, y, b, g, eps, lib=lib)).sum()
+            fm = (a * oracle.half_step(xm, y, b, g, eps, lib=lib)).sum()
+            fd[i, t] = (fp - fm) / (2 * h)
+    assert np.allclose(grad, fd, rtol=1e-7, atol=1e-9)
+    # restricted rows agree with the full computation
+    sub = oracle.grad_x(x, y, a, b, g, eps, idx=[4, 0, 2], lib=lib)
+    assert np.array_equal(sub, grad[[4, 0, 2]])
+
+
+def pin_column_marginal_exact(lib):
+    """After the g half-step the plan's column sums equal b (to rounding)."""
+    x, y, a, b = _problem(9, 13, 2, 51)
+    f, g, _ = oracle.sinkhorn(x, y, a, b, 0.05, 4, lib=lib)
+    _, cs = oracle.marginals(x, y, a, b, f, g, 0.05, lib=lib)
+    assert np.allclose(cs, b, rtol=1e-12, atol=0)
+
+
+def pin_dual_cost_identity(lib):
+    """With exact column marginals, D(f,g) = <a,f> + <b,g> - eps * M (1 - M), M = sum a = sum b."""
+    for scale_mass in (1.0, 2.5):
+        x, y, a, b = _problem(8, 6, 2, 52)
+        a, b = a * scale_mass, b * scale_mass
+        eps = 0.2
+        f, g, _ = oracle.sinkhorn(x, y, a, b, eps, 5, lib=lib)
+        M = a.sum()
+        want = (a * f).sum() + (b * g).sum() - eps * M * (1 - M)
+        assert abs(oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib) - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def pin_gauge_invariance(lib):
+    """Plan, residual, grad and cost are unchanged under (f + c, g - c) with balanced mass."""
+    x, y, a, b = _problem(7, 9, 2, 61)
+    eps = 0.4
+    f, g, _ = oracle.sinkhorn(x, y, a, b, eps, 3, lib=lib)
+    c = 0.731
+    r0, r1 = oracle.residual(x, y, a, b, f, g, eps, lib=lib), oracle.residual(x, y, a, b, f + c, g - c, eps, lib=lib)
+    assert np.allclose(r0, r1, rtol=1e-10, atol=1e-16)
+    g0, g1 = oracle.grad_x(x, y, a, b, g, eps, lib=lib), oracle.grad_x(x, y, a, b, g - c, eps, lib=lib)
+    assert np.allclose(g0, g1, rtol=1e-12, atol=1e-15)
+    c0 = oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib)
+    c1 = oracle.dual_cost(x, y, a, b, f + c, g - c, eps, lib=lib)
+    assert abs(c0 - c1) <= 1e-12
+
+
+def pin_translation_covariance(lib):
+    """Shifting y by t adds alpha_i = |t|^2 - 2<t,x_i> to f and beta_j = 2<t,y_j> to g
+    along the whole trajectory when g starts at beta."""
+    x, y, a, b = _problem(6, 8, 3, 71)
+    t = np.array([0.7, -1.3, 2.1])
+    eps = 0.25
+    alpha = t @ t - 2 * x @ t
+    beta = 2 * y @ t
+    f, g, _ = oracle.sinkhorn(x, y, a, b, eps, 6, lib=lib)
+    f2, g2, _ = oracle.sinkhorn(x, y + t, a, b, eps, 6, g_init=beta, lib=lib)
+    assert np.allclose(f2, f + alpha, rtol=0, atol=1e-10)
+    assert np.allclose(g2, g + beta, rtol=0, atol=1e-10)
+
+
+def pin_strong_duality(lib):
+    """At convergence the dual cost equals the primal <P,C> + eps KL(P | a x b) of the scaled plan."""
+    x, y, a, b = _problem(6, 5, 2, 81)
+    eps = 0.5
+    f, g, _ = oracle.sinkhorn(x, y, a, b, eps, 3000, lib=lib)
+    _, _, P = _scaling_form(x, y, a, b, eps, 3000)
+    C = cdist(x, y, "sqeuclidean")
+    ab = a[:, None] * b[None, :]
+    primal = (P * C).sum() + eps * ((P * np.log(P / ab)).sum() - P.sum() + ab.sum())
+    assert abs(oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib) - primal) <= 1e-10 * max(1.0, abs(primal))
+    assert oracle.residual(x, y, a, b, f, g, eps, lib=lib)[0] < 1e-12
+
+
+def pin_large_eps_limit(lib):
+    """As eps grows the plan tends to a x b and the cost to sum_ij a_i b_j C_ij."""
+    x, y, a, b = _problem(7, 6, 2, 91)
+    eps = 1e6
+    f, g, _ = oracle.sinkhorn(x, y, a, b, eps, 5, lib=lib)
+    want = (a[:, None] * b[None, :] * cdist(x, y, "sqeuclidean")).sum()
+    assert abs(oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib) - want) <= 1e-5 * want
+
+
+def pin_small_eps_bruteforce(lib):
+    """Uniform n = m: OT_0 <= D <= OT_0 + eps log n at convergence, OT_0 by enumerating permutations."""
+    x, y, a, b = _problem(6, 6, 2, 101)
+    a, b = np.full(6, 1 / 6), np.full(6, 1 / 6)
+    C = cdist(x, y, "sqeuclidean")
+    ot0 = min(C[np.arange(6), list(p)].mean() for p in itertools.permutations(range(6)))
+    r, c = linear_sum_assignment(C)
+    assert abs(C[r, c].mean() - ot0) <= 1e-12
+    # converged: both bounds; OT_0 <= OT_eps <= OT_0 + eps log n (permutation plan)
+    f, g, _ = oracle.sinkhorn(x, y, a, b, 0.2, 20000, lib=lib)
+    assert oracle.residual(x, y, a, b, f, g, 0.2, lib=lib)[0] < 1e-12
+    D = oracle.dual_cost(x, y, a, b, f, g, 0.2, lib=lib)
+    assert ot0 - 1e-9 <= D <= ot0 + 0.2 * math.log(6) + 1e-9
+    # any iterate: weak duality, D(f, g) <= OT_eps <= OT_0 + eps log n
+    for eps in (0.05, 0.01):
+        for k in (1, 10, 300):
+            f, g, _ = oracle.sinkhorn(x, y, a, b, eps, k, lib=lib)
+            assert oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib) <= ot0 + eps * math.log(6) + 1e-9
+
+
+def pin_1d_sorting(lib):
+    """1-D uniform measures: OT_0 is the cost of the sorted (monotone) matching."""
+    rng = np.random.default_rng(111)
+    x = rng.normal(size=(40, 1))
+    y = rng.normal(size=(40, 1)) * 0.7 + 0.4
+    a = np.full(40, 1 / 40)
+    ot0 = ((np.sort(x[:, 0]) - np.sort(y[:, 0])) ** 2).mean()
+    eps = 0.05
+    f, g, _ = oracle.sinkhorn(x, y, a, a, eps, 30000, lib=lib)
+    assert oracle.residual(x, y, a, a, f, g, eps, lib=lib)[0] < 1e-6
+    D = oracle.dual_cost(x, y, a, a, f, g, eps, lib=lib)
+    assert ot0 - 1e-6 <= D <= ot0 + eps * math.log(40) + 1e-9
+
+
+def pin_self_term(lib):
+    """(x, x, a, a) at convergence: f - g is constant and 0 <= OT_eps(x,x) <= eps H(a)
+    (the diagonal plan bounds it), unlike a divergence that vanishes at (x, x)."""
+    x, _, a, _ = _problem(9, 9, 2, 121)
+    eps = 0.3
+    f, g, _ = oracle.sinkhorn(x, x, a, a, eps, 4000, lib=lib)
+    assert np.ptp(f - g) < 1e-7
+    D = oracle.dual_cost(x, x, a, a, f, g, eps, lib=lib)
+    H = -(a * np.log(a)).sum()
+    assert 0.0 < D <= eps * H
+
+
+def pin_zero_weights(lib):
+    """Zero-weight points change nothing for the others: the problem with them removed
+    gives the same f, g, cost and gradient on the remaining points; grad is 0 where a_i = 0."""
+    x, y, a, b = _problem(10, 8, 2, 131)
+    a[[1, 4, 7]] = 0.0
+    b[[0, 5]] = 0.0
+    a, b = a / a.sum(), b / b.sum()
+    eps = 0.15
+    f, g, _ = oracle.sinkhorn(x, y, a, b, eps, 6, lib=lib)
+    ka, kb = a > 0, b > 0
+    fr, gr, _ = oracle.sinkhorn(x[ka], y[kb], a[ka], b[kb], eps, 6, lib=lib)
+    assert np.all(np.isfinite(f)) and np.all(np.isfinite(g))
+    assert np.allclose(f[ka], fr, rtol=0, atol=1e-12)
+    assert np.allclose(g[kb], gr, rtol=0, atol=1e-12)
+    assert abs(oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib)
+               - oracle.dual_cost(x[ka], y[kb], a[ka], b[kb], fr, gr, eps, lib=lib)) <= 1e-12
+    gx = oracle.grad_x(x, y, a, b, g, eps, lib=lib)
+    assert np.all(gx[~ka] == 0.0)
+    assert np.allclose(gx[ka], oracle.grad_x(x[ka], y[kb], a[ka], b[kb], gr, eps, lib=lib), rtol=0, atol=1e-12)
+
+
+def pin_half_step_vs_logsumexp(lib):
+    """The c-transform equals -eps * scipy.special.logsumexp((g - C_i.)/eps, b=w), also at tiny eps."""
+    x, y, a, b = _problem(12, 30, 3, 141)
+    rng = np.random.default_rng(142)
+    g = rng.normal(size=30)
+    C = cdist(x, y, "sqeuclidean")
+    for eps in (1.0, 1e-2, 1e-4):
+        want = -eps * logsumexp((g[None, :] - C) / eps, b=b[None, :], axis=1)
+        got = oracle.half_step(x, y, b, g, eps, lib=lib)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * C.max())
+        sub = oracle.half_step(x, y, b, g, eps, idx=[3, 11], lib=lib)
+        assert np.array_equal(sub, got[[3, 11]])
+
+
+def pin_max_cost(lib):
+    """Exhaustive max cost equals scipy's cdist maximum; the hull shortcut equals the exhaustive scan."""
+    rng = np.random.default_rng(151)
+    x, y = rng.random((300, 3)), rng.random((400, 3)) * 1.3
+    want = cdist(x, y, "sqeuclidean").max()
+    assert oracle.max_cost(x, y, lib=lib) == pytest.approx(want, rel=1e-14)
+    assert oracle.max_cost_hull(x, y) == pytest.approx(want, rel=1e-14)
+
+
+def pin_residual_trace(lib):
+    """The residual trace holds the residual at (f_k, g_k) for k = c, 2c, ...; the run with
+    fewer iterations is a prefix of the longer one."""
+    x, y, a, b = _problem(8, 7, 2, 161)
+    eps = 0.2
+    f, g, tr = oracle.sinkhorn(x, y, a, b, eps, 9, check_every=3, lib=lib)
+    assert tr.shape == (3,)
+    for k, r in zip((3, 6, 9), tr):
+        fk, gk, _ = oracle.sinkhorn(x, y, a, b, eps, k, lib=lib)
+        res = oracle.residual(x, y, a, b, fk, gk, eps, lib=lib)
+        assert r == pytest.approx(max(res[0], res[1]), rel=1e-12, abs=1e-18)
+    assert np.array_equal(f, oracle.sinkhorn(x, y, a, b, eps, 9, lib=lib)[0])
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin(oracle.load())
+
+
+def test_sampled_rows_match_full():
+    """Restricting the half-step to a row subset gives bit-identical values (rows are
+    reduced independently and in index order, whatever the threading)."""
+    x, y, a, b = _problem(33, 29, 2, 171)
+    f, g, _ = oracle.sinkhorn(x, y, a, b, 0.1, 5)
+    g4 = oracle.sinkhorn(x, y, a, b, 0.1, 4)[1]
+    f_rows = np.array([oracle.half_step(x, y, b, g4, 0.1, idx=[i])[0] for i in range(33)])
+    assert np.array_equal(f_rows, f)
+    g_cols = oracle.half_step(y, x, a, f, 0.1, idx=np.arange(29)[::-1])
+    assert np.array_equal(g_cols[::-1], g)
+
+
+# --------------------------------------------------------------------------- mutation check
+ORACLE_SRC = os.path.join(os.path.dirname(oracle.__file__), "sk_oracle.c")
+
+MUTANTS = {
+    "l1_cost": ("s += diff * diff;", "s += fabs(diff);", 1),
+    "cost_sign": ("(pot[j] - sq_dist(p, key + j * d, d)) / eps", "(pot[j] + sq_dist(p, key + j * d, d)) / eps", 2),
+    "weight_sign": ("/ eps + logw[j];", "/ eps - logw[j];", 4),
+    "eps_times": ("/ eps + logw[j];", "* eps + logw[j];", 4),
+    "dropped_max": ("return -eps * (zmax + log(s));", "return -eps * log(s);", 1),
+    "raw_weight": ("return w > 0.0 ? log(w) : -INFINITY;", "return w;", 1),
+    "wrong_coord": ("double diff = p[t] - q[t];", "double diff = p[t] - q[0];", 1),
+    "g_first": ("        oracle_half_step(x, n, y, m, d, b, g, eps, NULL, n, f);\n"
+                "        oracle_half_step(y, m, x, n, d, a, f, eps, NULL, m, g);",
+                "        oracle_half_step(y, m, x, n, d, a, f, eps, NULL, m, g);\n"
+                "        oracle_half_step(x, n, y, m, d, b, g, eps, NULL, n, f);", 1),
+    "grad_no_weight": ("2.0 * a[i] * (xi[t] - bary[t] / s)", "2.0 * (xi[t] - bary[t] / s)", 1),
+    "grad_sign": ("2.0 * a[i] * (xi[t] - bary[t] / s)", "2.0 * a[i] * (bary[t] / s - xi[t])", 1),
+    "grad_unnormalised": ("2.0 * a[i] * (xi[t] - bary[t] / s)", "2.0 * a[i] * (xi[t] - bary[t])", 1),
+    "grad_half": ("2.0 * a[i] * (xi[t] - bary[t] / s)", "a[i] * (xi[t] - bary[t] / s)", 1),
+    "marginal_drop_a": ("            s += a[i] * b[j] * exp(", "            s += b[j] * exp(", 2, 1),
+    "dual_sign": ("return af + bg - eps * (mass_p - sa * sb);", "return af + bg + eps * (mass_p - sa * sb);", 1),
+    "dual_no_mass": ("return af + bg - eps * (mass_p - sa * sb);", "return af + bg - eps * mass_p;", 1),
+    "resid_no_abs": ("double e = fabs(rs[i] - a[i]);", "double e = rs[i] - a[i];", 1),
+    "trace_row_only": ("resid_trace[k / check_every - 1] = r[0] > r[1] ? r[0] : r[1];",
+                       "resid_trace[k / check_every - 1] = r[1];", 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new, count, *n_replace = MUTANTS[name]
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == count, f"mutation site for {name} not found exactly {count} time(s)"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new, *n_replace))
+    lib = oracle.load(oracle.build(str(mutated), str(tmp_path / "libmutant.so")))
+    failed = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, FloatingPointError, ValueError, ZeroDivisionError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
