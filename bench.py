@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the streamed log-domain Sinkhorn hot path on one MI355X.
+
+One step = the whole hot path over one synthetic problem already resident in
+HBM: sk_solve (centre + pack, n_iters alternating row/column streamed passes
+with the fused marginal-residual check every `check_every` iterations),
+sk_cost and sk_grad_x.  The default workload is the throughput headline:
+n = m = 50,000 points in 3-D drawn from 8-Gaussian mixtures in the unit cube,
+Exponential(1) weights, eps = 0.01, 100 iterations.
+
+Printed (one JSON line):
+  value        point-pair evaluations per second, counting the 2 n m n_iters
+               evaluations of the Sinkhorn iterations only (the residual probe
+               and gradient passes are done inside the timed step but not
+               counted), over the wall-clock of the timed steps;
+  roofline     the streamed-pass kernel (the dominant kernel, timed live with
+               HIP events on the launch stream) against the vector-ALU issue
+               ceiling of the chip (see roofline_alu);
+  cpu_baseline the CPU oracle as it stands, timed on one full Sinkhorn
+               iteration of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X unit counts and clock: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz.
+CUS, SIMDS, LANES, CLOCK_HZ = 256, 4, 16, 2.4e9
+LANE_OPS_PER_S = CUS * SIMDS * LANES * CLOCK_HZ  # 3.93e13 single-lane VALU ops / s (no packed fp32)
+# v_exp_f32 throughput relative to the full VALU lane rate, measured on gfx950
+# with the issue-rate micro-benchmark (`python bench.py --ceilings`): exp2 alone
+# issues at half rate (1.94e13/s vs 3.61e13/s for fp32 FMA), and a mix of 7
+# VALU ops + 1 exp2 per pair sustains more instructions per second than a single
+# issue port allows, so the exp2 runs on its own pipe concurrently with the
+# other VALU work.
+EXP_RATE_FRACTION = 0.5
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass_traffic.json")
+
+
+def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
+    """Vector-ALU roofline of one streamed pass.
+
+    Algorithmic work per pair evaluation: d FMAs (2d flops), one max, one
+    subtract, one add and one exp2 = 2d + 4 fp32 operations.  Issue model:
+    the d + 3 non-transcendental ops take one full-rate VALU slot each, and the
+    exp2 runs concurrently on the transcendental pipe at EXP_RATE_FRACTION of
+    the lane rate, so the chip's ceiling is
+    min(LANE_OPS_PER_S / (d + 3), EXP_RATE_FRACTION * LANE_OPS_PER_S) pairs/s;
+    the peak in operation units is that times (2d + 4).
+    """
+    ops_per_pair = 2 * d + 4
+    ceiling_pairs = min(LANE_OPS_PER_S / (d + 3), EXP_RATE_FRACTION * LANE_OPS_PER_S)
+    achieved = pairs_per_launch * ops_per_pair / avg_launch_s / 1e12
+    peak = ceiling_pairs * ops_per_pair / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "ops_per_pair": ops_per_pair, "pairs_per_launch": pairs_per_launch,
+            "avg_launch_us": round(avg_launch_s * 1e6, 3), "ceiling_pairs_per_s": ceiling_pairs}
+
+
+def load_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    from streaming_sinkhorn_solver_amd import build as skbuild
+    import hashlib
+
+    h = hashlib.sha256()
+    for src in skbuild.sources():
+        h.update(open(src, "rb").read())
+    entry = rec.get(kernel_key)
+    if not entry or entry.get("source_sha256") != h.hexdigest():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def run_ceilings():
+    import ctypes
+
+    import torch
+
+    from streaming_sinkhorn_solver_amd import build as skbuild
+
+    lib = ctypes.CDLL(skbuild.UBENCH_PATH)
+    lib.sku_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks, iters = 2048 * 4, 2000
+    out = torch.empty(blocks * 256, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for kind, name in ((0, "fma"), (1, "exp2"), (2, "pair_mix_d3")):
+        for _ in range(2):
+            lib.sku_launch(kind, blocks, 50, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = lib.sku_launch(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        e1.record()
+        torch.cuda.synchronize()
+        assert rc == 0, rc
+        ops = blocks * 256 * iters * 64
+        rate = ops / (e0.elapsed_time(e1) * 1e-3)
+        res[name] = {"ops_per_s": rate, "frac_of_lane_rate": rate / LANE_OPS_PER_S}
+    res["exp2_issue_cost"] = res["fma"]["ops_per_s"] / res["exp2"]["ops_per_s"]
+    res["lane_ops_per_s_nominal"] = LANE_OPS_PER_S
+    print(json.dumps(res))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="gmm8_d3_sq")
+    ap.add_argument("--iters", type=int, default=None, help="override the workload's iteration count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceilings", action="store_true", help="run the issue-rate micro-benchmarks and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d); run it with --gpus 1." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import streaming_sinkhorn_solver_amd as sk
+    from sk_inputs import WORKLOADS, eps32, make_inputs
+
+    if args.ceilings:
+        run_ceilings()
+        return
+
+    w = WORKLOADS[args.workload]
+    n_iters = w.n_iters if args.iters is None else args.iters
+    eps = eps32(w.eps)
+    x, y, a, b = make_inputs(args.workload)
+    n, m, d = w.n, w.m, w.d
+    dev = torch.device("cuda:0")
+    X, Y, A, B = (torch.from_numpy(v).to(dev) for v in (x, y, a, b))
+    ws = sk.workspace(n, m, d, dev)
+    f = torch.empty(n, dtype=torch.float32, device=dev)
+    g = torch.empty(m, dtype=torch.float32, device=dev)
+    ce = w.check_every
+    trace = torch.empty(max(n_iters // ce, 1) if ce else 1, dtype=torch.float32, device=dev)
+    cost_out = torch.empty(1, dtype=torch.float64, device=dev)
+    grad = torch.empty((n, d), dtype=torch.float32, device=dev)
+    sk.check_inputs(X, Y, A, B, ws)  # data validation once, outside the timed region
+
+    def step():
+        sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, check_every=ce, ws=ws, f=f, g=g, trace=trace, check=False)
+        sk.cost(A, B, f, g, eps=eps, out=cost_out)
+        if w.grad:
+            sk.grad_x(X, Y, A, B, g, eps=eps, ws=ws, out=grad)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    sk.timing_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pass_ms, launches, pairs = sk.timing_read()
+    sk.timing_enable(False)
+
+    wall_s = t1 - t0
+    gpu_s = ev0.elapsed_time(ev1) * 1e-3
+    step_s = max(wall_s, gpu_s) / args.steps
+    pair_evals = 2.0 * n * m * n_iters
+    value = pair_evals / step_s
+    avg_launch_s = pass_ms * 1e-3 / launches
+    pairs_per_launch = pairs / launches
+    roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
+    roof["traffic"] = load_traffic(f"{args.workload}:pass")
+    roof["kernel"] = f"k_pass_valu<{d}>"
+
+    out = {
+        "metric": "point-pair evals/sec and Sinkhorn iters/sec (n=m=50k,d=3); % fp32 peak",
+        "value": value,
+        "unit": "pair-evals/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n": n, "m": m, "d": d, "eps": eps, "n_iters": n_iters,
+                   "check_every": ce, "grad_x": bool(w.grad), "recipe": w.description},
+        "iters_per_s": n_iters / step_s,
+        "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s,
+        "roofline": roof,
+        "final_residual": float(trace[n_iters // ce - 1].item()) if ce else None,
+        "cost": float(cost_out.item()),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, y, a, b, eps, n, m)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(x, y, a, b, eps, n, m) -> dict:
+    """The CPU oracle as it stands on one full Sinkhorn iteration of the same problem."""
+    import oracle
+
+    lib = oracle.load()
+    t0 = time.perf_counter()
+    oracle.sinkhorn(x, y, a, b, eps, 1, lib=lib)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * n * m / dt, "unit": "pair-evals/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+            "sample": f"one full alternating iteration (row + column half-step, {2 * n * m:.3g} pair evaluations) "
+                      f"of the same workload from g = 0, float64, {dt:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

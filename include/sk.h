@@ -1,0 +1,167 @@
+/*
+ * sk.h -- C ABI of the streaming log-domain Sinkhorn library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library solves entropic optimal transport between two weighted point
+ * clouds under squared-Euclidean cost, C_ij = |x_i - y_j|^2, without ever
+ * forming the n x m cost or kernel matrix: every half-step is a streamed,
+ * tiled log-sum-exp with a running maximum, computed on the GPU.
+ *
+ * Conventions shared by every entry point
+ *  - Arrays are float32, row-major and contiguous, and live in device memory
+ *    of the current HIP device unless stated otherwise.  x is (n, d), y is
+ *    (m, d), a is (n), b is (m), f is (n), g is (m).  They are owned by the
+ *    caller; the library never allocates, frees or retains them.
+ *  - The library never allocates device memory.  Entry points that need
+ *    scratch space take a workspace `ws` of at least sk_workspace_bytes(n, m, d)
+ *    bytes, 256-byte aligned, owned by the caller.  A workspace may be reused
+ *    by later calls once the calls that used it have completed in stream order.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Compute entry
+ *    points only enqueue work and return; results are ready when the stream
+ *    reaches that point.  Only sk_check_inputs synchronises the stream.
+ *  - Weights are used exactly as given (not normalised); zeros are legal and
+ *    such points contribute nothing.  Data-dependent validity (negative or
+ *    non-finite values, unequal masses) is checked by sk_check_inputs, not by
+ *    the compute entry points, which assume valid data.
+ *  - Argument errors (NULL pointers, bad sizes, eps, iteration counts,
+ *    unsupported d, short workspace) are detected on the host before anything
+ *    is enqueued and are returned as an sk_status; nothing is launched then.
+ *    A failed launch returns SK_ERR_HIP.
+ *  - Supported dimensions: 1 <= d <= 256.  d <= 8 runs on the vector ALUs;
+ *    9 <= d <= 256 computes the x.y cross term on fp32 matrix cores.
+ *
+ * Sources (page title and section):
+ *  FS   = "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",
+ *         technical summary, Methodology 1-3.
+ *  SLOT = SinkSLOT README: Tensor Contract, API Reference, Low-Level Solver API.
+ */
+#ifndef SK_H
+#define SK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sk_status {
+    SK_OK = 0,
+    SK_ERR_NULL = 1,           /* a required pointer is NULL */
+    SK_ERR_SHAPE = 2,          /* n < 1, m < 1 or d < 1, or n, m beyond 2^31 - 1 */
+    SK_ERR_UNSUPPORTED_D = 3,  /* d > 256 */
+    SK_ERR_EPS = 4,            /* eps not finite or eps <= 0 */
+    SK_ERR_ITERS = 5,          /* n_iters < 0 */
+    SK_ERR_CHECK_EVERY = 6,    /* check_every < 0, or > 0 with resid_trace == NULL */
+    SK_ERR_NEG_WEIGHT = 7,     /* some a_i or b_j < 0 */
+    SK_ERR_MASS_MISMATCH = 8,  /* |sum a - sum b| > 1e-5 * max(sum a, sum b) */
+    SK_ERR_EMPTY_MEASURE = 9,  /* sum a == 0 or sum b == 0 */
+    SK_ERR_NONFINITE = 10,     /* NaN or Inf in x, y, a or b */
+    SK_ERR_WORKSPACE = 11,     /* ws NULL, misaligned, or ws_bytes too small */
+    SK_ERR_HIP = 12            /* a HIP runtime call or kernel launch failed */
+} sk_status;
+
+/* Version of this ABI (incremented on any signature change). */
+int sk_abi_version(void);
+
+/* Human-readable name of a status code; never NULL, static storage. */
+const char *sk_status_string(int status);
+
+/*
+ * Bytes of workspace needed by every entry point below for a problem of n
+ * source points, m target points in dimension d (0 for invalid sizes).  The
+ * size is O((n + m) d): the library keeps the clouds, potentials and per-row
+ * partial statistics, never an n x m array (FS, Methodology 3: linear memory).
+ */
+size_t sk_workspace_bytes(int64_t n, int64_t m, int32_t d);
+
+/*
+ * Validates the data of a problem (SLOT, Tensor Contract): x and y finite,
+ * a and b finite and nonnegative, sum(a) > 0, sum(b) > 0 and
+ * |sum(a) - sum(b)| <= 1e-5 * max(sum(a), sum(b)) with the sums taken in
+ * float64.  Synchronises `stream`.  Returns SK_OK or the first failing check
+ * in the order NONFINITE, NEG_WEIGHT, EMPTY_MEASURE, MASS_MISMATCH.
+ */
+int sk_check_inputs(const float *x, const float *y, const float *a, const float *b,
+                    int64_t n, int64_t m, int32_t d,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Fixed-count alternating log-domain Sinkhorn (FS, Methodology 1; SLOT, API
+ * Reference: variant "alternating", stop_mode "fixed").  Starting from g = 0,
+ * each of the n_iters iterations computes
+ *     f_i <- -eps * LSE_j[(g_j - C_ij)/eps + log b_j]      (row half-step)
+ *     g_j <- -eps * LSE_i[(f_i - C_ij)/eps + log a_i]      (column half-step,
+ *                                                           with the new f)
+ * each as one streamed pass with an on-chip running max / sum-exp (FS,
+ * Methodology 2).  On return f (n) and g (m) hold the potentials after the
+ * last iteration, in cost units (f, not f/eps); n_iters = 0 gives f = g = 0.
+ *
+ * Residual trace: when check_every > 0, resid_trace (device, n_iters /
+ * check_every floats) receives, for k = check_every, 2*check_every, ...,
+ * the marginal residual max(|P1 - a|_inf, |P^T 1 - b|_inf) of the plan
+ * P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps) at the potentials after
+ * iteration k (SLOT, API Reference, stop_mode "marginal" norm).  No early
+ * stop is taken.  check_every = 0 disables the trace (resid_trace may be NULL).
+ */
+int sk_solve(const float *x, const float *y, const float *a, const float *b,
+             int64_t n, int64_t m, int32_t d, float eps, int32_t n_iters,
+             float *f, float *g, int32_t check_every, float *resid_trace,
+             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Entropic OT cost at potentials (f, g) that come out of a column half-step
+ * (so the plan's column sums equal b): the dual objective
+ *     <a, f> + <b, g> - eps * sum(b) * (1 - sum(a)),
+ * accumulated in float64 in a fixed order (deterministic).  Terms with a zero
+ * weight are skipped.  `out` is one device double.  For unit mass this is
+ * <a, f> + <b, g>.
+ */
+int sk_cost(const float *a, const float *b, const float *f, const float *g,
+            int64_t n, int64_t m, float eps, double *out, void *stream);
+
+/*
+ * Marginal residual of the plan P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps) at
+ * arbitrary potentials (f, g) (SLOT, API Reference: the "marginal" stop norm).
+ * Two streamed passes (row sums and column sums of P, never stored).  `out`
+ * is 4 device floats: [max_i |(P1)_i - a_i|, max_j |(P^T 1)_j - b_j|,
+ * sum_i |(P1)_i - a_i|, sum_j |(P^T 1)_j - b_j|].
+ */
+int sk_marginal_residual(const float *x, const float *y, const float *a, const float *b,
+                         int64_t n, int64_t m, int32_t d, float eps,
+                         const float *f, const float *g, float *out,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Analytic gradient with respect to x at fixed g (FS, Methodology 3:
+ * barycentric projection as a weighted average; no differentiation through
+ * the iterations):
+ *     grad_i = 2 a_i (x_i - sum_j w_ij y_j),
+ *     w_ij = softmax_j((g_j - C_ij)/eps + log b_j),
+ * one streamed pass with an on-chip running max and rescaled weighted sums.
+ * `grad` is (n, d) device memory.
+ */
+int sk_grad_x(const float *x, const float *y, const float *a, const float *b,
+              int64_t n, int64_t m, int32_t d, float eps, const float *g,
+              float *grad, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Kernel timing of the streamed log-sum-exp passes (benchmark diagnostics).
+ * sk_timing_enable(1) resets the counters and from then on records a HIP
+ * event pair on the launch stream around every streamed-pass kernel that
+ * sk_solve and sk_marginal_residual enqueue (the split merge and the other
+ * kernels are outside the pair); sk_timing_enable(0) stops recording.
+ * sk_timing_read waits for the recorded events and returns the total kernel
+ * milliseconds, the number of launches and the number of (query, key) pairs
+ * those launches evaluated.  Events come from a process-wide pool that grows
+ * on demand; calls from several threads at once are serialised.  Returns
+ * SK_ERR_NULL for NULL outputs, SK_ERR_HIP on a HIP failure.
+ */
+int sk_timing_enable(int enable);
+int sk_timing_read(double *total_ms, int64_t *launches, double *pairs);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SK_H */

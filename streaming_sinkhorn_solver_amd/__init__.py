@@ -1,0 +1,236 @@
+"""Streaming log-domain Sinkhorn on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/sk.h`` (libsk.so): argument
+marshalling only.  Every step of the computation runs in the library's HIP
+kernels; PyTorch provides device memory and the current stream.  There is no
+CPU fallback: if libsk.so is missing or cannot be loaded, every call raises.
+
+Tensor contract (SinkSLOT README, Tensor Contract): x (n, d) and y (m, d)
+float32 point clouds, optional nonnegative weights a (n,), b (m,) -- uniform
+if omitted, used exactly as given, sum(a) must equal sum(b) (ValueError
+otherwise), zeros legal -- all on the same CUDA/HIP device.  float64 inputs
+raise ValueError: the kernels are float32-only.  The cost is
+C_ij = |x_i - y_j|^2 with no 1/2 factor; eps is measured against it.
+Potentials are returned in cost units (f, g), not divided by eps.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_build", "libsk.so")
+
+SK_OK = 0
+_STATUS_NAMES = {
+    0: "SK_OK", 1: "SK_ERR_NULL", 2: "SK_ERR_SHAPE", 3: "SK_ERR_UNSUPPORTED_D", 4: "SK_ERR_EPS",
+    5: "SK_ERR_ITERS", 6: "SK_ERR_CHECK_EVERY", 7: "SK_ERR_NEG_WEIGHT", 8: "SK_ERR_MASS_MISMATCH",
+    9: "SK_ERR_EMPTY_MEASURE", 10: "SK_ERR_NONFINITE", 11: "SK_ERR_WORKSPACE", 12: "SK_ERR_HIP",
+}
+_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10}
+
+# C ABI: (name, restype, argtypes)
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "sk_abi_version": (ctypes.c_int, []),
+    "sk_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sk_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "sk_check_inputs": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "sk_solve": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _vp, _vp, _i32, _vp, _vp, _sz,
+                                _vp]),
+    "sk_cost": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp]),
+    "sk_marginal_residual": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz,
+                                            _vp]),
+    "sk_grad_x": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "sk_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "sk_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(ctypes.c_double)]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SinkhornError(RuntimeError):
+    """A HIP failure inside the library."""
+
+
+def load_library(path: str | None = None):
+    """Load libsk.so (raises if it is missing: there is no fallback path)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"libsk.so not found at {p}; build it with "
+                               "`python -m streaming_sinkhorn_solver_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().sk_status_string(int(code)).decode()
+
+
+def _raise(code: int, where: str):
+    if code == SK_OK:
+        return
+    msg = f"{where}: {_STATUS_NAMES.get(code, code)} ({status_string(code)})"
+    if code in _VALUE_ERRORS:
+        raise ValueError(msg)
+    raise SinkhornError(msg)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _as_problem(x, y, a, b):
+    if not isinstance(x, torch.Tensor) or not isinstance(y, torch.Tensor):
+        raise TypeError("x and y must be torch tensors")
+    if x.dtype != torch.float32 or y.dtype != torch.float32:
+        raise ValueError("the kernels are float32-only (got %s, %s)" % (x.dtype, y.dtype))
+    if x.dim() != 2 or y.dim() != 2 or x.shape[1] != y.shape[1]:
+        raise ValueError("x must be (n, d) and y (m, d) with the same d")
+    if x.device.type != "cuda" or y.device != x.device:
+        raise ValueError("x and y must be on the same GPU device")
+    n, d = x.shape
+    m = y.shape[0]
+    if a is None:
+        a = torch.full((n,), 1.0 / n, dtype=torch.float32, device=x.device)
+    if b is None:
+        b = torch.full((m,), 1.0 / m, dtype=torch.float32, device=x.device)
+    for name, w, k in (("a", a, n), ("b", b, m)):
+        if w.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 (got {w.dtype})")
+        if w.shape != (k,) or w.device != x.device:
+            raise ValueError(f"{name} must have shape ({k},) on {x.device}")
+    return x.contiguous(), y.contiguous(), a.contiguous(), b.contiguous(), n, m, d
+
+
+def workspace_bytes(n: int, m: int, d: int) -> int:
+    return int(load_library().sk_workspace_bytes(n, m, d))
+
+
+def workspace(n: int, m: int, d: int, device) -> torch.Tensor:
+    """A workspace tensor for problems of this size (uint8, 256-byte aligned by torch's allocator)."""
+    nb = workspace_bytes(n, m, d)
+    if nb == 0:
+        raise ValueError(f"invalid problem size n={n} m={m} d={d}")
+    ws = torch.empty(nb, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("allocator returned a workspace that is not 256-byte aligned")
+    return ws
+
+
+def check_inputs(x, y, a=None, b=None, ws: torch.Tensor | None = None) -> None:
+    """Validate the data (finite, nonnegative weights, equal nonzero masses); raises ValueError."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    _raise(lib.sk_check_inputs(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, _ptr(ws), ws.numel(),
+                               _stream(x.device)), "sk_check_inputs")
+
+
+def solve(x, y, a=None, b=None, *, eps: float, n_iters: int, check_every: int = 0,
+          ws: torch.Tensor | None = None, f: torch.Tensor | None = None, g: torch.Tensor | None = None,
+          trace: torch.Tensor | None = None, check: bool = True):
+    """Fixed-count alternating log-domain Sinkhorn from g = 0.
+
+    Returns (f, g, resid_trace); resid_trace holds n_iters // check_every
+    marginal residuals (empty when check_every == 0).  Outputs are enqueued on
+    the current stream.
+    """
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    if check:
+        check_inputs(x, y, a, b, ws)
+    f = f if f is not None else torch.empty(n, dtype=torch.float32, device=x.device)
+    g = g if g is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+    nt = n_iters // check_every if check_every > 0 else 0
+    if trace is None:
+        trace = torch.empty(max(nt, 0), dtype=torch.float32, device=x.device)
+    elif trace.numel() < nt or trace.dtype != torch.float32:
+        raise ValueError(f"trace must hold {nt} float32 values")
+    _raise(lib.sk_solve(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), _ptr(f), _ptr(g),
+                        int(check_every), _ptr(trace) if nt > 0 else None, _ptr(ws), ws.numel(),
+                        _stream(x.device)), "sk_solve")
+    return f, g, trace
+
+
+def cost(a, b, f, g, *, eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
+    """<a,f> + <b,g> - eps sum(b)(1 - sum(a)) in float64 (a 1-element device tensor)."""
+    lib = load_library()
+    for t in (a, b, f, g):
+        if t.dtype != torch.float32 or t.device.type != "cuda":
+            raise ValueError("a, b, f, g must be float32 GPU tensors")
+    n, m = a.numel(), b.numel()
+    if f.numel() != n or g.numel() != m:
+        raise ValueError("f must match a and g must match b in length")
+    out = out if out is not None else torch.empty(1, dtype=torch.float64, device=a.device)
+    a, b, f, g = a.contiguous(), b.contiguous(), f.contiguous(), g.contiguous()
+    _raise(lib.sk_cost(_ptr(a), _ptr(b), _ptr(f), _ptr(g), n, m, float(eps), _ptr(out), _stream(a.device)),
+           "sk_cost")
+    return out
+
+
+def marginal_residual(x, y, a, b, f, g, *, eps: float, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """[max|P1-a|, max|P^T1-b|, sum|P1-a|, sum|P^T1-b|] at (f, g), as a 4-element float32 tensor."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    out = torch.empty(4, dtype=torch.float32, device=x.device)
+    f, g = f.contiguous(), g.contiguous()
+    if f.shape != (n,) or g.shape != (m,) or f.dtype != torch.float32 or g.dtype != torch.float32:
+        raise ValueError("f must be (n,) and g (m,) float32")
+    _raise(lib.sk_marginal_residual(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g),
+                                    _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)), "sk_marginal_residual")
+    return out
+
+
+def grad_x(x, y, a, b, g, *, eps: float, ws: torch.Tensor | None = None,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """grad_i = 2 a_i (x_i - sum_j w_ij y_j), w_i. = softmax_j((g_j - C_ij)/eps + log b_j)."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    g = g.contiguous()
+    if g.shape != (m,) or g.dtype != torch.float32:
+        raise ValueError("g must be (m,) float32")
+    out = out if out is not None else torch.empty((n, d), dtype=torch.float32, device=x.device)
+    _raise(lib.sk_grad_x(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(g), _ptr(out), _ptr(ws),
+                         ws.numel(), _stream(x.device)), "sk_grad_x")
+    return out
+
+
+def timing_enable(enable: bool = True) -> None:
+    """Start (reset) or stop event timing of the streamed-pass kernels."""
+    _raise(load_library().sk_timing_enable(1 if enable else 0), "sk_timing_enable")
+
+
+def timing_read() -> tuple[float, int, float]:
+    """(total kernel ms, launches, pairs evaluated) since timing_enable(True)."""
+    ms, n, pairs = ctypes.c_double(), ctypes.c_int64(), ctypes.c_double()
+    _raise(load_library().sk_timing_read(ctypes.byref(ms), ctypes.byref(n), ctypes.byref(pairs)), "sk_timing_read")
+    return ms.value, n.value, pairs.value
+
+
+__all__ = ["timing_enable", "timing_read", "solve", "cost", "marginal_residual", "grad_x", "check_inputs", "workspace", "workspace_bytes",
+           "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES"]

@@ -1,0 +1,398 @@
+// sk_api.hip -- host side of the C ABI declared in include/sk.h: argument
+// validation, workspace carve-up and the launch sequence of each entry point.
+// All work is enqueued on the caller's stream; nothing here synchronises
+// except sk_check_inputs.
+#include "sk.h"
+#include "sk_internal.hpp"
+
+#include <algorithm>
+#include <cfloat>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+namespace sk {
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int64_t kTargetGroups = 2048;  // workgroups per pass: 8 per CU on 256 CUs
+constexpr int64_t kMinColsPerSplit = 512;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Split {
+    int nsplit;
+    int cols;
+};
+
+Split split_for(int64_t nq, int64_t nk, int rows_per_block) {
+    int64_t row_blocks = (nq + rows_per_block - 1) / rows_per_block;
+    int64_t sp = (kTargetGroups + row_blocks - 1) / row_blocks;
+    sp = std::min<int64_t>(sp, (nk + kMinColsPerSplit - 1) / kMinColsPerSplit);
+    sp = std::min<int64_t>(sp, kMaxSplit);
+    sp = std::max<int64_t>(sp, 1);
+    int64_t cols = (nk + sp - 1) / sp;
+    sp = (nk + cols - 1) / cols;
+    return Split{(int)sp, (int)cols};
+}
+
+int rows_per_block(int d) {
+    (void)d;
+    return valu_rows_per_block();
+}
+
+int check_sizes(int64_t n, int64_t m, int32_t d) {
+    if (n < 1 || m < 1 || d < 1 || n > INT32_MAX || m > INT32_MAX) return SK_ERR_SHAPE;
+    if (d > kValuMaxD) return SK_ERR_UNSUPPORTED_D;
+    return SK_OK;
+}
+
+int check_eps(float eps) {
+    if (!std::isfinite(eps) || eps <= 0.0f) return SK_ERR_EPS;
+    // the pre-scaled query 2 log2e / eps must stay finite in fp32
+    if (!(2.0 * (double)kLog2e / (double)eps < (double)FLT_MAX)) return SK_ERR_EPS;
+    return SK_OK;
+}
+
+struct Ws {
+    Layout L;
+    char* base;
+    float* f(size_t off) const { return reinterpret_cast<float*>(base + off); }
+    double* dbl(size_t off) const { return reinterpret_cast<double*>(base + off); }
+};
+
+int check_ws(void* ws, size_t ws_bytes, const Layout& L) {
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) % 256) != 0 || ws_bytes < L.total)
+        return SK_ERR_WORKSPACE;
+    return SK_OK;
+}
+
+#define SK_TRY(expr)                              \
+    do {                                          \
+        if ((expr) != hipSuccess) return SK_ERR_HIP; \
+    } while (0)
+
+// Shifts both clouds by their common centre and packs them.  x_bias / y_bias:
+// 0 = none, 1 = zero potential, 2 = from the given potential.
+int prepare(const Ws& W, const float* x, const float* y, const float* a, const float* b, float eps,
+            int x_bias, const float* f, int y_bias, const float* g, hipStream_t s) {
+    const Layout& L = W.L;
+    float* centre = W.f(L.centre);
+    SK_TRY(launch_centre(x, y, (int)L.n, (int)L.m, L.d, W.dbl(L.cen), centre, s));
+    SK_TRY(launch_pack(x, (int)L.n, L.d, L.P, L.mfma, centre, a, W.f(L.xp), W.f(L.nx), W.f(L.l2a), W.f(L.hx),
+                       1.0f / eps, x_bias, f, s));
+    SK_TRY(launch_pack(y, (int)L.m, L.d, L.P, L.mfma, centre, b, W.f(L.yp), W.f(L.ny), W.f(L.l2b), W.f(L.hy),
+                       1.0f / eps, y_bias, g, s));
+    return SK_OK;
+}
+
+// A streamed pass with queries from one side and keys from the other.
+// row_side = true: queries x (n), keys y (m); otherwise the transpose.
+PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q) {
+    const Layout& L = W.L;
+    PassArgs p{};
+    const int64_t nq = row_side ? L.n : L.m, nk = row_side ? L.m : L.n;
+    Split sp = split_for(nq, nk, rows_per_block(L.d));
+    p.q = W.f(row_side ? L.xp : L.yp);
+    p.k = W.f(row_side ? L.yp : L.xp);
+    p.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
+    p.nq = (int)nq;
+    p.nk = (int)nk;
+    p.P = L.P;
+    p.qscale = 2.0f * kLog2e / eps;
+    p.cols_per_split = sp.cols;
+    p.nsplit = sp.nsplit;
+    p.part = reinterpret_cast<float2*>(W.base + L.part);
+    Fin& F = p.fin;
+    F.mode = kFinSolve;
+    F.P = L.P;
+    F.d = L.d;
+    F.eps_ln2 = eps * kLn2;
+    F.inv_eps = 1.0f / eps;
+    F.lse = W.f(row_side ? L.lse_r : L.lse_c);
+    F.l2w = W.f(row_side ? L.l2a : L.l2b);
+    F.w = w_q;
+    F.nrm = W.f(row_side ? L.nx : L.ny);
+    F.pot = nullptr;
+    F.bias_packed = L.mfma ? nullptr : W.f(row_side ? L.xp : L.yp);
+    F.bias_sep = L.mfma ? W.f(row_side ? L.hx : L.hy) : nullptr;
+    F.rbuf = nullptr;
+    F.pot_in = nullptr;
+    return p;
+}
+
+// Optional event timing of the pass kernels (sk_timing_enable / sk_timing_read).
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> pool;  // pairs: [2k] start, [2k + 1] stop
+    size_t used = 0;               // pairs recorded since enable
+    double pairs = 0.0;
+};
+Timing& timing() {
+    static Timing t;
+    return t;
+}
+
+int run_pass(const Ws& W, const PassArgs& p, hipStream_t s) {
+    (void)W;
+    Timing& T = timing();
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(T.mu);
+        if (T.on) {
+            while (T.pool.size() < 2 * (T.used + 1)) {
+                hipEvent_t e;
+                SK_TRY(hipEventCreate(&e));
+                T.pool.push_back(e);
+            }
+            e0 = T.pool[2 * T.used];
+            e1 = T.pool[2 * T.used + 1];
+            ++T.used;
+            T.pairs += (double)p.nq * (double)p.nk;
+        }
+    }
+    SK_TRY(launch_pass_valu(p, W.L.d, s, e0, e1));
+    return SK_OK;
+}
+
+}  // namespace
+
+Layout make_layout(int64_t n, int64_t m, int d) {
+    Layout L{};
+    L.d = d;
+    L.P = packed_stride(d);
+    L.mfma = d > kValuMaxD;
+    L.n = n;
+    L.m = m;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + std::max<size_t>(bytes, 1), 256);
+        return o;
+    };
+    const size_t P = (size_t)L.P, un = (size_t)n, um = (size_t)m, umx = (size_t)std::max(n, m);
+    L.xp = take(un * P * 4);
+    L.yp = take(um * P * 4);
+    L.hx = take(un * 4);
+    L.hy = take(um * 4);
+    L.nx = take(un * 4);
+    L.ny = take(um * 4);
+    L.l2a = take(un * 4);
+    L.l2b = take(um * 4);
+    L.lse_r = take(un * 4);
+    L.lse_c = take(um * 4);
+    L.rbuf = take(umx * 4);
+    const int rpb = rows_per_block(d);
+    const Split sr = split_for(n, m, rpb), sc = split_for(m, n, rpb);
+    const size_t part_rows = std::max((size_t)sr.nsplit * un, (size_t)sc.nsplit * um);
+    L.part = take(part_rows * sizeof(float2));
+    L.partA = take(sr.nsplit > 1 ? (size_t)sr.nsplit * un * P * 4 : 0);
+    L.red = take((size_t)4 * kRedBlocks * 3 * sizeof(double));
+    L.cen = take((size_t)2 * kRedBlocks * d * sizeof(double));
+    L.centre = take((size_t)d * 4);
+    L.chk = take(8 * sizeof(double));
+    L.total = off;
+    return L;
+}
+
+int plan_split(int64_t nq, int64_t nk, int rpb) { return split_for(nq, nk, rpb).nsplit; }
+
+}  // namespace sk
+
+using namespace sk;
+
+extern "C" {
+
+int sk_abi_version(void) { return kAbiVersion; }
+
+const char* sk_status_string(int status) {
+    switch (status) {
+        case SK_OK: return "ok";
+        case SK_ERR_NULL: return "a required pointer is NULL";
+        case SK_ERR_SHAPE: return "invalid sizes (n, m, d must be >= 1 and n, m < 2^31)";
+        case SK_ERR_UNSUPPORTED_D: return "unsupported dimension d";
+        case SK_ERR_EPS: return "eps must be finite and > 0 (and 2*log2(e)/eps finite in fp32)";
+        case SK_ERR_ITERS: return "n_iters must be >= 0";
+        case SK_ERR_CHECK_EVERY: return "check_every must be >= 0, with resid_trace when > 0";
+        case SK_ERR_NEG_WEIGHT: return "weights must be nonnegative";
+        case SK_ERR_MASS_MISMATCH: return "sum(a) must equal sum(b)";
+        case SK_ERR_EMPTY_MEASURE: return "sum(a) and sum(b) must be > 0";
+        case SK_ERR_NONFINITE: return "inputs contain NaN or Inf";
+        case SK_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or too small";
+        case SK_ERR_HIP: return "HIP runtime or kernel launch failure";
+        default: return "unknown status";
+    }
+}
+
+int sk_timing_enable(int enable) {
+    Timing& T = timing();
+    std::lock_guard<std::mutex> lk(T.mu);
+    T.on = enable != 0;
+    T.used = 0;
+    T.pairs = 0.0;
+    return SK_OK;
+}
+
+int sk_timing_read(double* total_ms, int64_t* launches, double* pairs) {
+    if (!total_ms || !launches || !pairs) return SK_ERR_NULL;
+    Timing& T = timing();
+    std::lock_guard<std::mutex> lk(T.mu);
+    double tot = 0.0;
+    for (size_t k = 0; k < T.used; ++k) {
+        SK_TRY(hipEventSynchronize(T.pool[2 * k + 1]));
+        float ms = 0.0f;
+        SK_TRY(hipEventElapsedTime(&ms, T.pool[2 * k], T.pool[2 * k + 1]));
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = (int64_t)T.used;
+    *pairs = T.pairs;
+    return SK_OK;
+}
+
+size_t sk_workspace_bytes(int64_t n, int64_t m, int32_t d) {
+    if (n < 1 || m < 1 || d < 1 || d > kMaxD || n > INT32_MAX || m > INT32_MAX) return 0;
+    return make_layout(n, m, d).total;
+}
+
+int sk_check_inputs(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m,
+                    int32_t d, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    const Layout L = make_layout(n, m, d);
+    if ((st = check_ws(ws, ws_bytes, L))) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Ws W{L, static_cast<char*>(ws)};
+    SK_TRY(launch_check(x, y, a, b, (int)n, (int)m, d, W.dbl(L.red), W.dbl(L.chk), s));
+    double res[4];
+    SK_TRY(hipMemcpyAsync(res, W.dbl(L.chk), sizeof(res), hipMemcpyDeviceToHost, s));
+    SK_TRY(hipStreamSynchronize(s));
+    if (res[0] != 0.0) return SK_ERR_NONFINITE;
+    if (res[1] != 0.0) return SK_ERR_NEG_WEIGHT;
+    if (!(res[2] > 0.0) || !(res[3] > 0.0)) return SK_ERR_EMPTY_MEASURE;
+    if (std::fabs(res[2] - res[3]) > 1e-5 * std::max(res[2], res[3])) return SK_ERR_MASS_MISMATCH;
+    return SK_OK;
+}
+
+int sk_solve(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+             float eps, int32_t n_iters, float* f, float* g, int32_t check_every, float* resid_trace, void* ws,
+             size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if (n_iters < 0) return SK_ERR_ITERS;
+    if (check_every < 0 || (check_every > 0 && n_iters / check_every > 0 && !resid_trace))
+        return SK_ERR_CHECK_EVERY;
+    const Layout L = make_layout(n, m, d);
+    if ((st = check_ws(ws, ws_bytes, L))) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Ws W{L, static_cast<char*>(ws)};
+
+    if (n_iters == 0) {
+        SK_TRY(launch_fill(f, n, 0.0f, s));
+        SK_TRY(launch_fill(g, m, 0.0f, s));
+        return SK_OK;
+    }
+    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 1, nullptr, s))) return st;
+
+    PassArgs row = make_pass(W, true, eps, a);
+    row.fin.pot = f;
+    PassArgs col = make_pass(W, false, eps, b);
+    col.fin.pot = g;
+    float* rbuf = W.f(L.rbuf);
+
+    for (int k = 1; k <= n_iters; ++k) {
+        // the row pass of iteration k also yields the residual of iteration k-1's plan
+        const bool check_prev = check_every > 0 && k > 1 && (k - 1) % check_every == 0;
+        row.fin.rbuf = check_prev ? rbuf : nullptr;
+        if ((st = run_pass(W, row, s))) return st;
+        if (check_prev) SK_TRY(launch_resid_reduce(rbuf, (int)n, resid_trace + (k - 1) / check_every - 1, nullptr, s));
+        if ((st = run_pass(W, col, s))) return st;
+    }
+    if (check_every > 0 && n_iters % check_every == 0) {
+        PassArgs probe = row;
+        probe.fin.mode = kFinProbe;
+        probe.fin.rbuf = rbuf;
+        if ((st = run_pass(W, probe, s))) return st;
+        SK_TRY(launch_resid_reduce(rbuf, (int)n, resid_trace + n_iters / check_every - 1, nullptr, s));
+    }
+    return SK_OK;
+}
+
+int sk_cost(const float* a, const float* b, const float* f, const float* g, int64_t n, int64_t m, float eps,
+            double* out, void* stream) {
+    if (!a || !b || !f || !g || !out) return SK_ERR_NULL;
+    if (n < 1 || m < 1 || n > INT32_MAX || m > INT32_MAX) return SK_ERR_SHAPE;
+    int st = check_eps(eps);
+    if (st) return st;
+    SK_TRY(launch_cost(a, b, f, g, (int)n, (int)m, eps, out, reinterpret_cast<hipStream_t>(stream)));
+    return SK_OK;
+}
+
+int sk_marginal_residual(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m,
+                         int32_t d, float eps, const float* f, const float* g, float* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g || !out) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    const Layout L = make_layout(n, m, d);
+    if ((st = check_ws(ws, ws_bytes, L))) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Ws W{L, static_cast<char*>(ws)};
+    if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
+    float* rbuf = W.f(L.rbuf);
+
+    PassArgs row = make_pass(W, true, eps, a);
+    row.fin.mode = kFinResid;
+    row.fin.pot_in = f;
+    row.fin.rbuf = rbuf;
+    if ((st = run_pass(W, row, s))) return st;
+    SK_TRY(launch_resid_reduce(rbuf, (int)n, out + 0, out + 2, s));
+
+    PassArgs col = make_pass(W, false, eps, b);
+    col.fin.mode = kFinResid;
+    col.fin.pot_in = g;
+    col.fin.rbuf = rbuf;
+    if ((st = run_pass(W, col, s))) return st;
+    SK_TRY(launch_resid_reduce(rbuf, (int)m, out + 1, out + 3, s));
+    return SK_OK;
+}
+
+int sk_grad_x(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+              float eps, const float* g, float* grad, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !g || !grad) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    const Layout L = make_layout(n, m, d);
+    if ((st = check_ws(ws, ws_bytes, L))) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Ws W{L, static_cast<char*>(ws)};
+    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 2, g, s))) return st;
+
+    GradArgs ga{};
+    const Split sp = split_for(n, m, rows_per_block(d));
+    ga.q = W.f(L.xp);
+    ga.k = W.f(L.yp);
+    ga.kbias = L.mfma ? W.f(L.hy) : nullptr;
+    ga.nq = (int)n;
+    ga.nk = (int)m;
+    ga.P = L.P;
+    ga.d = d;
+    ga.qscale = 2.0f * kLog2e / eps;
+    ga.cols_per_split = sp.cols;
+    ga.nsplit = sp.nsplit;
+    ga.part = reinterpret_cast<float2*>(W.base + L.part);
+    ga.partA = W.f(L.partA);
+    ga.w = a;
+    ga.grad = grad;
+    SK_TRY(launch_grad_valu(ga, s));
+    return SK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// sk_internal.hpp -- shared definitions of the HIP implementation behind sk.h.
+//
+// Notation follows "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU"
+// (technical summary, Methodology 1): for squared-Euclidean cost the row
+// half-step f_i = -eps LSE_j[(g_j - C_ij)/eps + log b_j] is a log-sum-exp of a
+// biased dot-product score.  With C_ij = |x_i|^2 + |y_j|^2 - 2<x_i, y_j> and
+// everything in base 2 (log2e = 1/ln 2):
+//
+//     s_ij  = <q_i, y_j> + h_j,     q_i = (2 log2e / eps) x_i,
+//     h_j   = log2 b_j + log2e (g_j - |y_j|^2) / eps      (the "bias" of key j),
+//     lse_i = log2 sum_j 2^{s_ij}    (running max M and rescaled sum S),
+//     f_i   = |x_i|^2 - eps ln2 lse_i.
+//
+// The column half-step is the same with the roles of (x, a, f) and (y, b, g)
+// swapped.  Inside a solve the bias of the next pass is simply
+// h_i = log2 a_i - lse_i, because g (or f) enters only through lse.
+//
+// Both clouds are first shifted by a common centre c = (mean x + mean y)/2,
+// which leaves every C_ij unchanged and keeps |x|^2, |y|^2 small so the
+// expanded form loses little to fp32 cancellation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace sk {
+
+constexpr int kBlock = 256;               // threads per workgroup (4 wave64s)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -3.402823466e38f;  // running-max start: -FLT_MAX, never -inf
+constexpr int kMaxD = 256;
+constexpr int kValuMaxD = 8;              // d <= 8: vector-ALU kernels; else matrix cores
+constexpr int kRedBlocks = 512;           // fixed partial count of the 2-stage reductions
+constexpr int kMaxSplit = 64;             // column splits of one streamed pass
+
+// Packed stride (floats) of one point in the workspace.
+//  VALU layout:  [coords (d) | bias | zero pad] to a multiple of 4 (float4 loads).
+//  MFMA layout:  [coords (d) | zero pad] to a multiple of 16; bias kept apart.
+inline int packed_stride(int d) {
+    return d <= kValuMaxD ? ((d + 1 + 3) / 4) * 4 : ((d + 15) / 16) * 16;
+}
+
+// What a streamed pass does with each finished row's log-sum-exp.
+enum FinMode : int {
+    kFinSolve = 0,   // store lse, next-pass bias, output potential; optional fused residual
+    kFinProbe = 1,   // residual of the previous state only (no state change)
+    kFinResid = 2,   // residual against a caller-supplied potential
+};
+
+struct Fin {
+    int mode;
+    int P;               // packed stride of the query cloud (bias slot at index d)
+    int d;
+    float eps_ln2;       // eps * ln 2
+    float inv_eps;       // 1 / eps
+    float* lse;          // [nq] running state (read before write when a residual is taken)
+    const float* l2w;    // [nq] log2 of the query-side weights (-inf for zero weight)
+    const float* w;      // [nq] query-side weights
+    const float* nrm;    // [nq] |q~|^2 of the centred query points
+    float* pot;          // [nq] output potential in cost units, or null
+    float* bias_packed;  // query packed base (bias slot = index d), or null
+    float* bias_sep;     // separate bias array (matrix-core layout), or null
+    float* rbuf;         // [nq] |residual_i| output, or null
+    const float* pot_in; // [nq] caller potential (kFinResid)
+};
+
+// Arguments of one streamed log-sum-exp pass over all (query, key) pairs.
+struct PassArgs {
+    const float* q;      // query cloud, packed [nq][P]
+    const float* k;      // key cloud, packed [nk][P]
+    const float* kbias;  // separate key bias [nk] (matrix-core layout), else null
+    int nq, nk, P;
+    float qscale;        // 2 log2e / eps
+    int cols_per_split;
+    int nsplit;
+    float2* part;        // [nsplit][nq] partial (M, S) when nsplit > 1
+    Fin fin;
+};
+
+// Arguments of the streamed gradient pass.
+struct GradArgs {
+    const float* q;      // x packed [n][P]
+    const float* k;      // y packed [m][P] with bias slot holding h_j from g
+    const float* kbias;  // separate key bias (matrix-core layout), else null
+    int nq, nk, P, d;
+    float qscale;
+    int cols_per_split;
+    int nsplit;
+    float2* part;        // [nsplit][nq] partial (M, S)
+    float* partA;        // [nsplit][nq][P] partial weighted key sums
+    const float* w;      // a
+    float* grad;         // [nq][d] output
+};
+
+// Workspace carve-up, a pure function of (n, m, d).
+struct Layout {
+    int d, P;
+    bool mfma;
+    int64_t n, m;
+    size_t xp, yp, hx, hy, nx, ny, l2a, l2b, lse_r, lse_c, rbuf, part, partA, red, cen, centre, chk;
+    size_t total;
+};
+
+Layout make_layout(int64_t n, int64_t m, int d);
+
+// Split policy of a streamed pass: number of column splits for nq queries
+// against nk keys when one workgroup covers rows_per_block queries.
+int plan_split(int64_t nq, int64_t nk, int rows_per_block);
+
+// ----- launchers (return hipError_t of the launch) --------------------------------
+hipError_t launch_centre(const float* x, const float* y, int n, int m, int d, double* partials,
+                         float* centre, hipStream_t s);
+hipError_t launch_pack(const float* pts, int npts, int d, int P, bool mfma, const float* centre,
+                       const float* w, float* packed, float* nrm, float* l2w, float* bias_sep,
+                       float inv_eps, int bias_mode, const float* pot, hipStream_t s);
+hipError_t launch_fill(float* p, int64_t count, float value, hipStream_t s);
+hipError_t launch_check(const float* x, const float* y, const float* a, const float* b, int n, int m,
+                        int d, double* partials, double* result, hipStream_t s);
+hipError_t launch_cost(const float* a, const float* b, const float* f, const float* g, int n, int m,
+                       float eps, double* out, hipStream_t s);
+hipError_t launch_resid_reduce(const float* rbuf, int cnt, float* out_max, float* out_sum,
+                               hipStream_t s);
+// Vector-ALU passes (d <= 8): a streamed pass, plus the exact merge of the
+// split partials when nsplit > 1.
+// ev0 / ev1 (may be null): events recorded on s right before and right after
+// the pass kernel itself (not the merge).
+hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t ev0 = nullptr,
+                            hipEvent_t ev1 = nullptr);
+hipError_t launch_grad_valu(const GradArgs& a, hipStream_t s);
+int valu_rows_per_block();
+
+}  // namespace sk

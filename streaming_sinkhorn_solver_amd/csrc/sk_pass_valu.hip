@@ -1,0 +1,358 @@
+// sk_pass_valu.hip -- streamed log-sum-exp passes on the vector ALUs (d <= 8).
+//
+// One pass computes, for every query point i, lse_i = log2 sum_j 2^{s_ij} with
+// s_ij = <q_i, k_j> + h_j over all keys j, without storing any s_ij
+// ("FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU", Methodology 2:
+// no materialisation, online running max / sum-exp, fused score + bias + LSE +
+// potential update, row-stationary traversal).
+//
+// Mapping to CDNA4:
+//  * row-stationary: each lane owns R query rows in registers (pre-scaled
+//    coordinates, running max M and sum S); rows are strided by the workgroup
+//    size so a wave's loads are contiguous;
+//  * keys (coordinates + bias, one float4 for d <= 3) are staged tile by tile
+//    in LDS and read back as wave-wide broadcasts;
+//  * per (row, key) the work is d FMAs, one max, one subtract, one exp2 and one
+//    add; the running max is updated once per chunk of TJ keys, so the
+//    rescale of S costs one exp2 per chunk rather than per pair;
+//  * when the rows alone cannot fill 256 CUs the key range is split across
+//    workgroups and the partial (M, S) pairs are merged exactly afterwards:
+//    M = max_s M_s, S = sum_s S_s 2^{M_s - M}.
+// The running max starts at -FLT_MAX, not -inf, so keys with zero weight
+// (bias -inf) never produce (-inf) - (-inf).
+#include "sk_internal.hpp"
+
+#ifndef SK_VALU_R
+#define SK_VALU_R 4
+#endif
+#ifndef SK_VALU_TJ
+#define SK_VALU_TJ 8
+#endif
+#ifndef SK_VALU_TL
+#define SK_VALU_TL 256
+#endif
+
+namespace sk {
+namespace {
+
+constexpr int kR = SK_VALU_R;     // query rows per lane
+constexpr int kTJ = SK_VALU_TJ;   // keys per register chunk
+constexpr int kTL = SK_VALU_TL;   // keys per LDS tile
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Applies a finished row's log-sum-exp (base 2) to the pass outputs.
+__device__ __forceinline__ void finalize(const Fin& F, int i, float lse) {
+    if (F.mode == kFinSolve) {
+        if (F.rbuf) {
+            const float wi = F.w[i];
+            const float r = wi > 0.0f ? wi * expm1f((lse - F.lse[i]) * kLn2) : 0.0f;
+            F.rbuf[i] = fabsf(r);
+        }
+        F.lse[i] = lse;
+        const float h = F.l2w[i] - lse;
+        if (F.bias_packed) F.bias_packed[(size_t)i * F.P + F.d] = h;
+        if (F.bias_sep) F.bias_sep[i] = h;
+        if (F.pot) F.pot[i] = F.nrm[i] - F.eps_ln2 * lse;
+    } else if (F.mode == kFinProbe) {
+        const float wi = F.w[i];
+        const float r = wi > 0.0f ? wi * expm1f((lse - F.lse[i]) * kLn2) : 0.0f;
+        F.rbuf[i] = fabsf(r);
+    } else {  // kFinResid: (P1)_i / a_i - 1 = exp((f_i - f~_i)/eps) - 1
+        const float wi = F.w[i];
+        const float e = (F.pot_in[i] - F.nrm[i]) * F.inv_eps + kLn2 * lse;
+        const float r = wi > 0.0f ? wi * expm1f(e) : 0.0f;
+        F.rbuf[i] = fabsf(r);
+    }
+}
+
+// Stages keys [base, base + kTL) of the split [.., c1) into LDS; keys past c1
+// get zero coordinates and bias -inf, so they add exactly nothing.
+template <int D>
+__device__ __forceinline__ void stage_tile(float4* tile, const float4* __restrict__ kp, int base, int c1) {
+    constexpr int P = ((D + 1 + 3) / 4) * 4;
+    constexpr int V = P / 4;
+    for (int e = threadIdx.x; e < kTL * V; e += kBlock) {
+        const int col = base + e / V;
+        const int part = e % V;
+        float4 v;
+        if (col < c1) {
+            v = kp[(size_t)col * V + part];
+        } else {
+            v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (part == D / 4) {
+                float* c = reinterpret_cast<float*>(&v);
+                c[D % 4] = -INFINITY;
+            }
+        }
+        tile[e] = v;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
+    constexpr int P = ((D + 1 + 3) / 4) * 4;
+    constexpr int V = P / 4;
+    __shared__ float4 tile[kTL * V];
+
+    const int split = blockIdx.y;
+    const int row0 = blockIdx.x * (kBlock * kR) + threadIdx.x;
+
+    float q[kR][D];
+    float M[kR], S[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int i = row0 + r * kBlock;
+        const int ic = i < A.nq ? i : A.nq - 1;
+        const float* qr = A.q + (size_t)ic * P;
+#pragma unroll
+        for (int t = 0; t < D; ++t) q[r][t] = qr[t] * A.qscale;
+        M[r] = kNegBig;
+        S[r] = 0.0f;
+    }
+
+    const int c0 = split * A.cols_per_split;
+    const int c1 = min(c0 + A.cols_per_split, A.nk);
+    const float4* kp = reinterpret_cast<const float4*>(A.k);
+
+    for (int base = c0; base < c1; base += kTL) {
+        __syncthreads();
+        stage_tile<D>(tile, kp, base, c1);
+        __syncthreads();
+        const int ntile = min(kTL, c1 - base);
+        for (int c = 0; c < ntile; c += kTJ) {
+            float kk[kTJ][P];
+#pragma unroll
+            for (int t = 0; t < kTJ; ++t)
+#pragma unroll
+                for (int u = 0; u < V; ++u) {
+                    const float4 v = tile[(c + t) * V + u];
+                    kk[t][4 * u + 0] = v.x;
+                    kk[t][4 * u + 1] = v.y;
+                    kk[t][4 * u + 2] = v.z;
+                    kk[t][4 * u + 3] = v.w;
+                }
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                float s[kTJ];
+#pragma unroll
+                for (int t = 0; t < kTJ; ++t) {
+                    float acc = kk[t][D];
+#pragma unroll
+                    for (int dd = 0; dd < D; ++dd) acc = fmaf(q[r][dd], kk[t][dd], acc);
+                    s[t] = acc;
+                }
+                float mt = s[0];
+#pragma unroll
+                for (int t = 1; t < kTJ; ++t) mt = fmaxf(mt, s[t]);
+                const float mn = fmaxf(M[r], mt);
+                float acc = S[r] * ex2(M[r] - mn);
+#pragma unroll
+                for (int t = 0; t < kTJ; ++t) acc += ex2(s[t] - mn);
+                S[r] = acc;
+                M[r] = mn;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int i = row0 + r * kBlock;
+        if (i >= A.nq) continue;
+        if (A.nsplit == 1)
+            finalize(A.fin, i, M[r] + lg2(S[r]));
+        else
+            A.part[(size_t)split * A.nq + i] = make_float2(M[r], S[r]);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_merge(const float2* __restrict__ part, int nq, int nsplit, Fin F) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nq) return;
+    float M = kNegBig;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[(size_t)s * nq + i].x);
+    float S = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float2 p = part[(size_t)s * nq + i];
+        S += p.y * ex2(p.x - M);
+    }
+    finalize(F, i, M + lg2(S));
+}
+
+// Gradient pass: the same traversal with the running weighted key sum
+// A_i = sum_j 2^{s_ij - M_i} k_j (rescaled with S on every max change);
+// grad_i = 2 a_i (x~_i - A_i / S_i), where x~ and k are centred alike.
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_grad_valu(GradArgs A) {
+    constexpr int P = ((D + 1 + 3) / 4) * 4;
+    constexpr int V = P / 4;
+    __shared__ float4 tile[kTL * V];
+
+    const int split = blockIdx.y;
+    const int row0 = blockIdx.x * (kBlock * kR) + threadIdx.x;
+
+    float q[kR][D];
+    float M[kR], S[kR], Acc[kR][D];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int i = row0 + r * kBlock;
+        const int ic = i < A.nq ? i : A.nq - 1;
+        const float* qr = A.q + (size_t)ic * P;
+#pragma unroll
+        for (int t = 0; t < D; ++t) {
+            q[r][t] = qr[t] * A.qscale;
+            Acc[r][t] = 0.0f;
+        }
+        M[r] = kNegBig;
+        S[r] = 0.0f;
+    }
+
+    const int c0 = split * A.cols_per_split;
+    const int c1 = min(c0 + A.cols_per_split, A.nk);
+    const float4* kp = reinterpret_cast<const float4*>(A.k);
+
+    for (int base = c0; base < c1; base += kTL) {
+        __syncthreads();
+        stage_tile<D>(tile, kp, base, c1);
+        __syncthreads();
+        const int ntile = min(kTL, c1 - base);
+        for (int c = 0; c < ntile; c += kTJ) {
+            float kk[kTJ][P];
+#pragma unroll
+            for (int t = 0; t < kTJ; ++t)
+#pragma unroll
+                for (int u = 0; u < V; ++u) {
+                    const float4 v = tile[(c + t) * V + u];
+                    kk[t][4 * u + 0] = v.x;
+                    kk[t][4 * u + 1] = v.y;
+                    kk[t][4 * u + 2] = v.z;
+                    kk[t][4 * u + 3] = v.w;
+                }
+#pragma unroll
+            for (int r = 0; r < kR; ++r) {
+                float s[kTJ];
+#pragma unroll
+                for (int t = 0; t < kTJ; ++t) {
+                    float acc = kk[t][D];
+#pragma unroll
+                    for (int dd = 0; dd < D; ++dd) acc = fmaf(q[r][dd], kk[t][dd], acc);
+                    s[t] = acc;
+                }
+                float mt = s[0];
+#pragma unroll
+                for (int t = 1; t < kTJ; ++t) mt = fmaxf(mt, s[t]);
+                const float mn = fmaxf(M[r], mt);
+                const float sc = ex2(M[r] - mn);
+                float acc = S[r] * sc;
+#pragma unroll
+                for (int dd = 0; dd < D; ++dd) Acc[r][dd] *= sc;
+#pragma unroll
+                for (int t = 0; t < kTJ; ++t) {
+                    const float e = ex2(s[t] - mn);
+                    acc += e;
+#pragma unroll
+                    for (int dd = 0; dd < D; ++dd) Acc[r][dd] = fmaf(e, kk[t][dd], Acc[r][dd]);
+                }
+                S[r] = acc;
+                M[r] = mn;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int i = row0 + r * kBlock;
+        if (i >= A.nq) continue;
+        if (A.nsplit == 1) {
+            const float two_w = 2.0f * A.w[i];
+            const float inv = 1.0f / S[r];
+#pragma unroll
+            for (int dd = 0; dd < D; ++dd)
+                A.grad[(size_t)i * D + dd] = two_w * (A.q[(size_t)i * P + dd] - Acc[r][dd] * inv);
+        } else {
+            A.part[(size_t)split * A.nq + i] = make_float2(M[r], S[r]);
+            float* pa = A.partA + ((size_t)split * A.nq + i) * P;
+#pragma unroll
+            for (int dd = 0; dd < D; ++dd) pa[dd] = Acc[r][dd];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_grad_merge(GradArgs A) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= A.nq) return;
+    float M = kNegBig;
+    for (int s = 0; s < A.nsplit; ++s) M = fmaxf(M, A.part[(size_t)s * A.nq + i].x);
+    float S = 0.0f;
+    float acc[kMaxD > 8 ? 8 : kMaxD];
+    for (int dd = 0; dd < A.d; ++dd) acc[dd] = 0.0f;
+    for (int s = 0; s < A.nsplit; ++s) {
+        const float2 p = A.part[(size_t)s * A.nq + i];
+        const float sc = ex2(p.x - M);
+        S += p.y * sc;
+        const float* pa = A.partA + ((size_t)s * A.nq + i) * A.P;
+        for (int dd = 0; dd < A.d; ++dd) acc[dd] += pa[dd] * sc;
+    }
+    const float two_w = 2.0f * A.w[i];
+    const float inv = 1.0f / S;
+    for (int dd = 0; dd < A.d; ++dd)
+        A.grad[(size_t)i * A.d + dd] = two_w * (A.q[(size_t)i * A.P + dd] - acc[dd] * inv);
+}
+
+template <int D>
+hipError_t launch_pass_d(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    const int rpb = kBlock * kR;
+    dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
+    if (ev0) (void)hipEventRecord(ev0, s);
+    hipLaunchKernelGGL(k_pass_valu<D>, grid, dim3(kBlock), 0, s, a);
+    if (ev1) (void)hipEventRecord(ev1, s);
+    if (a.nsplit > 1)
+        hipLaunchKernelGGL(k_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a.part, a.nq,
+                           a.nsplit, a.fin);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_grad_d(const GradArgs& a, hipStream_t s) {
+    const int rpb = kBlock * kR;
+    dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
+    hipLaunchKernelGGL(k_grad_valu<D>, grid, dim3(kBlock), 0, s, a);
+    if (a.nsplit > 1)
+        hipLaunchKernelGGL(k_grad_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int valu_rows_per_block() { return kBlock * kR; }
+
+hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    switch (d) {
+        case 1: return launch_pass_d<1>(a, s, ev0, ev1);
+        case 2: return launch_pass_d<2>(a, s, ev0, ev1);
+        case 3: return launch_pass_d<3>(a, s, ev0, ev1);
+        case 4: return launch_pass_d<4>(a, s, ev0, ev1);
+        case 5: return launch_pass_d<5>(a, s, ev0, ev1);
+        case 6: return launch_pass_d<6>(a, s, ev0, ev1);
+        case 7: return launch_pass_d<7>(a, s, ev0, ev1);
+        case 8: return launch_pass_d<8>(a, s, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_grad_valu(const GradArgs& a, hipStream_t s) {
+    switch (a.d) {
+        case 1: return launch_grad_d<1>(a, s);
+        case 2: return launch_grad_d<2>(a, s);
+        case 3: return launch_grad_d<3>(a, s);
+        case 4: return launch_grad_d<4>(a, s);
+        case 5: return launch_grad_d<5>(a, s);
+        case 6: return launch_grad_d<6>(a, s);
+        case 7: return launch_grad_d<7>(a, s);
+        case 8: return launch_grad_d<8>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sk

@@ -1,0 +1,250 @@
+// sk_prep.hip -- once-per-call preparation and the small deterministic reductions:
+// common centre, packing of the clouds with norms and log-weights, data checks,
+// the cost <a,f> + <b,g>, and the residual max / sum.
+//
+// Every reduction is two-stage with a fixed partition (kRedBlocks partials, or
+// one workgroup walking the data in a fixed order) and a fixed-order final
+// sum, so results are bit-identical from run to run.
+#include "sk_internal.hpp"
+
+#include <cmath>
+
+namespace sk {
+namespace {
+
+__device__ inline double block_sum_f64(double v, double* sh) {
+    const int t = threadIdx.x;
+    sh[t] = v;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (t < w) sh[t] += sh[t + w];
+        __syncthreads();
+    }
+    double r = sh[0];
+    __syncthreads();
+    return r;
+}
+
+__device__ inline float block_max_f32(float v, float* sh) {
+    const int t = threadIdx.x;
+    sh[t] = v;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+        if (t < w) sh[t] = fmaxf(sh[t], sh[t + w]);
+        __syncthreads();
+    }
+    float r = sh[0];
+    __syncthreads();
+    return r;
+}
+
+// Per-block column sums of a (npts, d) cloud in float64.  Thread t < span owns
+// coordinate t % d and walks the flat array with stride span (a multiple of d),
+// so loads stay contiguous across threads.
+__global__ __launch_bounds__(kBlock) void k_colsum_partial(const float* __restrict__ pts, int64_t total,
+                                                           int d, double* __restrict__ partial) {
+    __shared__ double sh[kBlock];
+    const int span = (kBlock / d) * d;
+    const int t = threadIdx.x;
+    const int64_t per_block = ((total + gridDim.x - 1) / gridDim.x + d - 1) / d * d;
+    const int64_t lo = (int64_t)blockIdx.x * per_block;
+    const int64_t hi = lo + per_block < total ? lo + per_block : total;
+    double acc = 0.0;
+    if (t < span)
+        for (int64_t e = lo + t; e < hi; e += span) acc += (double)pts[e];
+    sh[t] = acc;
+    __syncthreads();
+    if (t < d) {
+        double s = 0.0;
+        for (int u = t; u < span; u += d) s += sh[u];
+        partial[(size_t)blockIdx.x * d + t] = s;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_centre_final(const double* __restrict__ px,
+                                                         const double* __restrict__ py, int nblk, int d,
+                                                         int n, int m, float* __restrict__ centre) {
+    for (int t = threadIdx.x; t < d; t += blockDim.x) {
+        double sx = 0.0, sy = 0.0;
+        for (int b = 0; b < nblk; ++b) {
+            sx += px[(size_t)b * d + t];
+            sy += py[(size_t)b * d + t];
+        }
+        centre[t] = (float)(0.5 * (sx / n + sy / m));
+    }
+}
+
+// Pack one cloud: centred coordinates, zero padding, |p~|^2, log2 w and the
+// initial bias.  bias_mode: 0 = none (0), 1 = zero potential, 2 = from pot.
+__global__ __launch_bounds__(kBlock) void k_pack(const float* __restrict__ pts, int npts, int d, int P,
+                                                 int mfma, const float* __restrict__ centre,
+                                                 const float* __restrict__ w, float* __restrict__ packed,
+                                                 float* __restrict__ nrm, float* __restrict__ l2w,
+                                                 float* __restrict__ bias_sep, float inv_eps, int bias_mode,
+                                                 const float* __restrict__ pot) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= npts) return;
+    float s = 0.0f;
+    float* row = packed + (size_t)i * P;
+    for (int t = 0; t < d; ++t) {
+        float v = pts[(size_t)i * d + t] - centre[t];
+        row[t] = v;
+        s = fmaf(v, v, s);
+    }
+    for (int t = d; t < P; ++t) row[t] = 0.0f;
+    const float wi = w[i];
+    const float lw = wi > 0.0f ? log2f(wi) : -INFINITY;
+    nrm[i] = s;
+    l2w[i] = lw;
+    float h = 0.0f;
+    if (bias_mode == 1) h = lw - s * kLog2e * inv_eps;
+    if (bias_mode == 2) h = lw + (pot[i] - s) * kLog2e * inv_eps;
+    if (mfma)
+        bias_sep[i] = h;
+    else
+        row[d] = h;
+}
+
+__global__ __launch_bounds__(kBlock) void k_fill(float* __restrict__ p, int64_t count, float v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = v;
+}
+
+// Data checks of one flat array: [nonfinite flag, negative flag, float64 sum].
+__global__ __launch_bounds__(kBlock) void k_check_partial(const float* __restrict__ v, int64_t total,
+                                                          double* __restrict__ partial) {
+    __shared__ double sh[kBlock];
+    const int64_t per_block = (total + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = (int64_t)blockIdx.x * per_block;
+    const int64_t hi = lo + per_block < total ? lo + per_block : total;
+    double bad = 0.0, neg = 0.0, sum = 0.0;
+    for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x) {
+        float x = v[e];
+        if (!isfinite(x)) bad = 1.0;
+        if (x < 0.0f) neg = 1.0;
+        sum += (double)x;
+    }
+    bad = block_sum_f64(bad, sh);
+    neg = block_sum_f64(neg, sh);
+    sum = block_sum_f64(sum, sh);
+    if (threadIdx.x == 0) {
+        partial[3 * blockIdx.x + 0] = bad;
+        partial[3 * blockIdx.x + 1] = neg;
+        partial[3 * blockIdx.x + 2] = sum;
+    }
+}
+
+// result: [nonfinite, negative weight, sum a, sum b]; partials holds 4 arrays x, y, a, b.
+__global__ __launch_bounds__(kBlock) void k_check_final(const double* __restrict__ partial, int nblk,
+                                                        double* __restrict__ result) {
+    if (threadIdx.x != 0) return;
+    double bad = 0.0, neg = 0.0, sa = 0.0, sb = 0.0;
+    for (int arr = 0; arr < 4; ++arr)
+        for (int b = 0; b < nblk; ++b) {
+            const double* p = partial + (size_t)(arr * nblk + b) * 3;
+            bad += p[0];
+            if (arr >= 2) neg += p[1];
+            if (arr == 2) sa += p[2];
+            if (arr == 3) sb += p[2];
+        }
+    result[0] = bad;
+    result[1] = neg;
+    result[2] = sa;
+    result[3] = sb;
+}
+
+// Cost: one workgroup walks both vectors in a fixed order with float64 sums.
+__global__ __launch_bounds__(1024) void k_cost(const float* __restrict__ a, const float* __restrict__ b,
+                                               const float* __restrict__ f, const float* __restrict__ g,
+                                               int n, int m, float eps, double* __restrict__ out) {
+    __shared__ double sh[1024];
+    double af = 0.0, sa = 0.0, bg = 0.0, sb = 0.0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        float ai = a[i];
+        if (ai != 0.0f) af += (double)ai * (double)f[i];
+        sa += (double)ai;
+    }
+    for (int j = threadIdx.x; j < m; j += blockDim.x) {
+        float bj = b[j];
+        if (bj != 0.0f) bg += (double)bj * (double)g[j];
+        sb += (double)bj;
+    }
+    af = block_sum_f64(af, sh);
+    sa = block_sum_f64(sa, sh);
+    bg = block_sum_f64(bg, sh);
+    sb = block_sum_f64(sb, sh);
+    if (threadIdx.x == 0) out[0] = af + bg - (double)eps * sb * (1.0 - sa);
+}
+
+// Residual reduction: max and float64 sum of |r_i|.
+__global__ __launch_bounds__(1024) void k_resid_reduce(const float* __restrict__ r, int cnt,
+                                                       float* __restrict__ out_max,
+                                                       float* __restrict__ out_sum) {
+    __shared__ double sh[1024];
+    __shared__ float shf[1024];
+    float mx = 0.0f;
+    double sm = 0.0;
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+        float v = r[i];
+        mx = fmaxf(mx, v);
+        sm += (double)v;
+    }
+    mx = block_max_f32(mx, shf);
+    sm = block_sum_f64(sm, sh);
+    if (threadIdx.x == 0) {
+        out_max[0] = mx;
+        if (out_sum) out_sum[0] = (float)sm;
+    }
+}
+
+inline int grid_for(int64_t count, int block) { return (int)((count + block - 1) / block); }
+
+}  // namespace
+
+hipError_t launch_centre(const float* x, const float* y, int n, int m, int d, double* partials,
+                         float* centre, hipStream_t s) {
+    double* px = partials;
+    double* py = partials + (size_t)kRedBlocks * d;
+    hipLaunchKernelGGL(k_colsum_partial, dim3(kRedBlocks), dim3(kBlock), 0, s, x, (int64_t)n * d, d, px);
+    hipLaunchKernelGGL(k_colsum_partial, dim3(kRedBlocks), dim3(kBlock), 0, s, y, (int64_t)m * d, d, py);
+    hipLaunchKernelGGL(k_centre_final, dim3(1), dim3(kBlock), 0, s, px, py, kRedBlocks, d, n, m, centre);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const float* pts, int npts, int d, int P, bool mfma, const float* centre,
+                       const float* w, float* packed, float* nrm, float* l2w, float* bias_sep,
+                       float inv_eps, int bias_mode, const float* pot, hipStream_t s) {
+    hipLaunchKernelGGL(k_pack, dim3(grid_for(npts, kBlock)), dim3(kBlock), 0, s, pts, npts, d, P,
+                       mfma ? 1 : 0, centre, w, packed, nrm, l2w, bias_sep, inv_eps, bias_mode, pot);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, int64_t count, float value, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill, dim3(grid_for(count, kBlock)), dim3(kBlock), 0, s, p, count, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_check(const float* x, const float* y, const float* a, const float* b, int n, int m,
+                        int d, double* partials, double* result, hipStream_t s) {
+    const float* arrs[4] = {x, y, a, b};
+    const int64_t lens[4] = {(int64_t)n * d, (int64_t)m * d, n, m};
+    for (int k = 0; k < 4; ++k)
+        hipLaunchKernelGGL(k_check_partial, dim3(kRedBlocks), dim3(kBlock), 0, s, arrs[k], lens[k],
+                           partials + (size_t)k * kRedBlocks * 3);
+    hipLaunchKernelGGL(k_check_final, dim3(1), dim3(64), 0, s, partials, kRedBlocks, result);
+    return hipGetLastError();
+}
+
+hipError_t launch_cost(const float* a, const float* b, const float* f, const float* g, int n, int m,
+                       float eps, double* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_cost, dim3(1), dim3(1024), 0, s, a, b, f, g, n, m, eps, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_resid_reduce(const float* rbuf, int cnt, float* out_max, float* out_sum, hipStream_t s) {
+    hipLaunchKernelGGL(k_resid_reduce, dim3(1), dim3(1024), 0, s, rbuf, cnt, out_max, out_sum);
+    return hipGetLastError();
+}
+
+}  // namespace sk

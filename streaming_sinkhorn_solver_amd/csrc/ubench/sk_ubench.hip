@@ -1,0 +1,98 @@
+// sk_ubench.hip -- issue-rate micro-benchmarks that fix the vector-ALU ceiling
+// of the streamed passes on gfx950: fp32 FMA, the transcendental exp2
+// (v_exp_f32), and the per-pair instruction mix of a d = 3 pass.  Built as a
+// separate library (libsk_ubench.so); the solver does not use it.
+//
+// Each thread runs kChains independent dependency chains so issue rate, not
+// latency, is measured.  The kernels write one value per thread so the work
+// cannot be removed.
+#include <hip/hip_runtime.h>
+
+namespace {
+
+constexpr int kChains = 8;
+
+__global__ __launch_bounds__(256) void k_fma(float* out, int iters, float a, float b) {
+    float v[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) v[c] = threadIdx.x * 1e-3f + c;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) v[c] = fmaf(v[c], a, b);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += v[c];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void k_exp(float* out, int iters) {
+    float v[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) v[c] = -(threadIdx.x * 1e-3f + c * 0.1f);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) v[c] = __builtin_amdgcn_exp2f(-v[c]);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += v[c];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// One "pair" = 3 FMA (score), 1 max, 1 subtract, 1 exp2, 1 add, as in a d = 3
+// pass.  The key coordinate advances once per 8 pairs (one extra add per
+// chain group) so nothing is loop-invariant.
+__global__ __launch_bounds__(256) void k_mix(float* out, int iters, float k0, float k1, float k2, float h) {
+    const float q1 = threadIdx.x * 1e-5f + 0.5f, q2 = -0.25f - threadIdx.x * 1e-5f;
+    float q0[kChains], m[kChains], s[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+        q0[c] = threadIdx.x * 1e-4f + c;
+        m[c] = -1.0f;
+        s[c] = 0.0f;
+    }
+    float kx = k0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            kx += 1e-7f;
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+                const float sc = fmaf(q2, k2, fmaf(q1, k1, fmaf(q0[c], kx, h)));
+                m[c] = fmaxf(m[c], sc);
+                s[c] += __builtin_amdgcn_exp2f(sc - m[c]);
+            }
+        }
+    }
+    float r = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) r += s[c] + m[c];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
+}  // namespace
+
+extern "C" {
+
+// kind 0: fp32 FMA, 1: exp2, 2: d = 3 pair mix.  Launches `blocks` x 256
+// threads; each thread performs iters * 8 * 8 operations (FMAs, exp2s or
+// pairs).  out must hold blocks * 256 floats.  Returns a hipError_t.
+int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (kind == 0)
+        hipLaunchKernelGGL(k_fma, dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 1)
+        hipLaunchKernelGGL(k_exp, dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 2)
+        hipLaunchKernelGGL(k_mix, dim3(blocks), dim3(256), 0, s, out, iters, 0.3f, 0.2f, 0.1f, 0.05f);
+    else
+        return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

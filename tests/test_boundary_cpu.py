@@ -1,0 +1,138 @@
+"""CPU-side checks of the C ABI boundary: the library loads, exports every entry
+point the header declares, sizes its workspace linearly in n + m, and rejects
+bad arguments with the documented status codes before enqueuing any GPU work
+(so these run without a GPU).  No compute entry point is executed here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import streaming_sinkhorn_solver_amd as sk
+from streaming_sinkhorn_solver_amd import build as skbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sk.h")
+
+SK_OK, SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_UNSUPPORTED_D, SK_ERR_EPS = 0, 1, 2, 3, 4
+SK_ERR_ITERS, SK_ERR_CHECK_EVERY, SK_ERR_WORKSPACE = 5, 6, 11
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sk.LIB_PATH):
+        skbuild.build()
+    return sk.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sk_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = header_functions()
+    for must in ("sk_solve", "sk_cost", "sk_marginal_residual", "sk_grad_x", "sk_workspace_bytes",
+                 "sk_check_inputs", "sk_status_string", "sk_abi_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = header_functions()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing
+    # the binding declares a signature for each of them
+    assert sorted(sk.SIGNATURES) == names
+
+
+def test_status_strings(lib):
+    for code in range(0, 13):
+        s = lib.sk_status_string(code)
+        assert s and len(s) > 1
+    assert lib.sk_status_string(999) == b"unknown status"
+    assert lib.sk_abi_version() == 1
+
+
+def test_workspace_is_linear(lib):
+    for d in (1, 2, 3, 8):
+        w1 = lib.sk_workspace_bytes(10000, 12000, d)
+        w2 = lib.sk_workspace_bytes(20000, 24000, d)
+        w4 = lib.sk_workspace_bytes(40000, 48000, d)
+        assert 0 < w1 < w2 < w4
+        assert w4 - w2 <= 2.2 * (w2 - w1) + 65536  # grows no faster than linearly
+        # far below an n x m float array
+        assert w4 < 40000 * 48000 * 4 / 20
+    assert lib.sk_workspace_bytes(1 << 20, 1 << 20, 3) < 200 << 20
+
+
+def test_workspace_rejects_bad_sizes(lib):
+    for n, m, d in [(0, 5, 2), (5, 0, 2), (5, 5, 0), (5, 5, 257), (-1, 5, 2), (1 << 31, 5, 2)]:
+        assert lib.sk_workspace_bytes(n, m, d) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation returns first
+
+
+def _solve(lib, *, x=FAKE, n=10, m=12, d=2, eps=0.1, iters=5, check_every=0, trace=None, ws=FAKE,
+           ws_bytes=None):
+    wb = lib.sk_workspace_bytes(max(n, 1), max(m, 1), max(min(d, 256), 1)) if ws_bytes is None else ws_bytes
+    return lib.sk_solve(x, FAKE, FAKE, FAKE, n, m, d, eps, iters, FAKE, FAKE, check_every, trace, ws, wb, None)
+
+
+def test_solve_argument_errors(lib):
+    assert _solve(lib, x=None) == SK_ERR_NULL
+    assert _solve(lib, n=0) == SK_ERR_SHAPE
+    assert _solve(lib, m=-3) == SK_ERR_SHAPE
+    assert _solve(lib, d=0) == SK_ERR_SHAPE
+    assert _solve(lib, d=300) == SK_ERR_UNSUPPORTED_D
+    assert _solve(lib, eps=0.0) == SK_ERR_EPS
+    assert _solve(lib, eps=-1.0) == SK_ERR_EPS
+    assert _solve(lib, eps=float("nan")) == SK_ERR_EPS
+    assert _solve(lib, eps=float("inf")) == SK_ERR_EPS
+    assert _solve(lib, eps=1e-39) == SK_ERR_EPS  # 2 log2e / eps overflows fp32
+    assert _solve(lib, iters=-1) == SK_ERR_ITERS
+    assert _solve(lib, check_every=-1) == SK_ERR_CHECK_EVERY
+    assert _solve(lib, check_every=2, trace=None) == SK_ERR_CHECK_EVERY
+    assert _solve(lib, ws=None) == SK_ERR_WORKSPACE
+    assert _solve(lib, ws=ctypes.c_void_p(0x100010)) == SK_ERR_WORKSPACE  # not 256-byte aligned
+    assert _solve(lib, ws_bytes=1000) == SK_ERR_WORKSPACE
+
+
+def test_other_entry_points_argument_errors(lib):
+    wb = lib.sk_workspace_bytes(10, 12, 2)
+    assert lib.sk_cost(None, FAKE, FAKE, FAKE, 10, 12, 0.1, FAKE, None) == SK_ERR_NULL
+    assert lib.sk_cost(FAKE, FAKE, FAKE, FAKE, 0, 12, 0.1, FAKE, None) == SK_ERR_SHAPE
+    assert lib.sk_cost(FAKE, FAKE, FAKE, FAKE, 10, 12, 0.0, FAKE, None) == SK_ERR_EPS
+    assert lib.sk_marginal_residual(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, 0.1, FAKE, None, FAKE, FAKE, wb,
+                                    None) == SK_ERR_NULL
+    assert lib.sk_marginal_residual(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, 0.1, FAKE, FAKE, FAKE, FAKE, 10,
+                                    None) == SK_ERR_WORKSPACE
+    assert lib.sk_grad_x(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, float("nan"), FAKE, FAKE, FAKE, wb,
+                         None) == SK_ERR_EPS
+    assert lib.sk_grad_x(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, 0.1, None, FAKE, FAKE, wb, None) == SK_ERR_NULL
+    assert lib.sk_check_inputs(FAKE, FAKE, None, FAKE, 10, 12, 2, FAKE, wb, None) == SK_ERR_NULL
+    assert lib.sk_check_inputs(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, None, wb, None) == SK_ERR_WORKSPACE
+
+
+def test_python_contract_errors_before_gpu():
+    x = torch.zeros(4, 2, dtype=torch.float64)
+    y = torch.zeros(5, 2, dtype=torch.float64)
+    with pytest.raises(ValueError, match="float32"):
+        sk.solve(x, y, eps=0.1, n_iters=3)
+    with pytest.raises(ValueError):
+        sk.solve(torch.zeros(4, 2), torch.zeros(5, 3), eps=0.1, n_iters=3)
+    with pytest.raises(ValueError, match="GPU"):
+        sk.grad_x(torch.zeros(4, 2), torch.zeros(5, 2), None, None, torch.zeros(5), eps=0.1)
+
+
+def test_no_oracle_on_product_path():
+    """The product package never imports or loads the oracle."""
+    pkg = os.path.join(ROOT, "streaming_sinkhorn_solver_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "liboracle" not in text and "sk_oracle" not in text, fn

@@ -1,0 +1,221 @@
+"""GPU parity: the HIP library (through the C ABI, via the thin binding) against
+the CPU float64 oracle on identical seeded float32 inputs.
+
+Tolerances
+  * potentials: max|f - f*|, max|g - g*| <= 1e-4 * max C  (end to end, same
+    fixed iteration count from g = 0);
+  * cost: relative error <= 1e-4;
+  * single half-steps (sampled rows at full size): <= 1e-4 * max C / (2 K),
+    so that, each half-step being 1-Lipschitz in the sup norm, K iterations of
+    such steps stay within the end-to-end bound;
+  * evaluations at identical inputs (gradient at the same g, residual at the
+    same (f, g)) are bounded by the float32 precision of the exponent,
+    kappa = 2^-24 (max|f| + max|g| + max C) / eps, which every float32 route
+    to these quantities shares.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import streaming_sinkhorn_solver_amd as sk
+from sk_inputs import WORKLOADS, eps32, make_inputs, random_problem
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U32 = 2.0 ** -24
+
+
+def say(*args):
+    print("[case]", *args, file=sys.stderr, flush=True)
+
+
+def dev(*arrs):
+    return [torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in arrs]
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def gpu_solve(x, y, a, b, eps, iters, check_every=0):
+    X, Y, A, B = dev(x, y, a, b)
+    f, g, tr = sk.solve(X, Y, A, B, eps=eps, n_iters=iters, check_every=check_every)
+    return host(f), host(g), host(tr)
+
+
+def kappa(f, g, maxc, eps):
+    return U32 * (np.abs(f).max() + np.abs(g).max() + maxc) / eps
+
+
+SHAPES = [
+    # n, m, d, eps, iters, seed, scale, zero_frac
+    (1, 1, 1, 0.1, 3, 1, 1.0, 0.0),
+    (1, 9, 2, 0.1, 4, 2, 1.0, 0.0),
+    (9, 1, 3, 0.1, 4, 3, 1.0, 0.0),
+    (257, 1023, 3, 0.05, 20, 4, 0.3, 0.0),
+    (1025, 513, 2, 0.02, 30, 5, 1.0, 0.0),
+    (2500, 3100, 1, 0.1, 10, 6, 1.0, 0.0),
+    (2500, 3100, 2, 0.1, 10, 7, 1.0, 0.0),
+    (2500, 3100, 3, 0.1, 10, 8, 1.0, 0.0),
+    (3100, 2500, 4, 0.2, 10, 9, 1.0, 0.0),
+    (2500, 3100, 5, 0.3, 10, 10, 1.0, 0.0),
+    (2500, 3100, 6, 0.3, 10, 11, 1.0, 0.0),
+    (2500, 3100, 7, 0.5, 10, 12, 1.0, 0.0),
+    (2500, 3100, 8, 0.5, 10, 13, 1.0, 0.0),
+    (3000, 2999, 3, 0.05, 15, 14, 0.5, 0.25),
+    (4099, 130, 2, 0.01, 25, 15, 1.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}d{s[2]}z{s[7]}" for s in SHAPES])
+def test_solve_matches_oracle(shape):
+    n, m, d, eps, iters, seed, scale, zf = shape
+    x, y, a, b = random_problem(n, m, d, seed, scale=scale, shift=0.2, zero_frac=zf)
+    eps = eps32(eps)
+    say("solve", shape)
+    f, g, _ = gpu_solve(x, y, a, b, eps, iters)
+    fo, go, _ = oracle.sinkhorn(x, y, a, b, eps, iters)
+    maxc = oracle.max_cost(x, y)
+    tol = 1e-4 * maxc
+    assert np.all(np.isfinite(f)) and np.all(np.isfinite(g))
+    say("err/tol f", np.max(np.abs(f - fo)) / tol, "g", np.max(np.abs(g - go)) / tol)
+    assert np.max(np.abs(f - fo)) <= tol
+    assert np.max(np.abs(g - go)) <= tol
+    # cost: the library's float64 reduction at the GPU potentials vs the oracle's dual value
+    F, G, A, B = dev(f.astype(np.float32), g.astype(np.float32), a, b)
+    c_gpu = float(host(sk.cost(A, B, F, G, eps=eps))[0])
+    c_or = oracle.dual_cost(x, y, a, b, fo, go, eps)
+    assert abs(c_gpu - c_or) <= 1e-4 * abs(c_or) + 1e-12
+
+
+def test_gradient_flow_workload_end_to_end():
+    """The 1000-point, eps = 0.01, 200-iteration problem in full, against a live oracle run."""
+    w = WORKLOADS["gflow_d2"]
+    x, y, a, b = make_inputs("gflow_d2")
+    eps = eps32(w.eps)
+    say("gflow_d2 full")
+    X, Y, A, B = dev(x, y, a, b)
+    f_t, g_t, _ = sk.solve(X, Y, A, B, eps=eps, n_iters=w.n_iters)
+    c_t = sk.cost(A, B, f_t, g_t, eps=eps)
+    grad_t = sk.grad_x(X, Y, A, B, g_t, eps=eps)
+    f, g, c, grad = host(f_t), host(g_t), float(host(c_t)[0]), host(grad_t)
+    fo, go, _ = oracle.sinkhorn(x, y, a, b, eps, w.n_iters)
+    maxc = oracle.max_cost(x, y)
+    assert np.max(np.abs(f - fo)) <= 1e-4 * maxc
+    assert np.max(np.abs(g - go)) <= 1e-4 * maxc
+    c_or = oracle.dual_cost(x, y, a, b, fo, go, eps)
+    assert abs(c - c_or) <= 1e-4 * abs(c_or)
+    # gradient at the GPU's own g: evaluation parity
+    gr_same = oracle.grad_x(x, y, a, b, g, eps)
+    k = kappa(f, g, maxc, eps)
+    tol_eval = 2 * a.max() * 16 * k * math.sqrt(maxc)
+    assert np.max(np.abs(grad - gr_same)) <= tol_eval
+    # end to end, with the bound implied by the potential error
+    gr_or = oracle.grad_x(x, y, a, b, go, eps)
+    dg = np.max(np.abs(g - go))
+    tol_e2e = tol_eval + 2 * a.max() * 2 * math.sqrt(maxc) * math.expm1(2 * dg / eps)
+    assert np.max(np.abs(grad - gr_or)) <= tol_e2e
+
+
+GRAD_SHAPES = [(1, 5, 2, 0.1, 21), (700, 1300, 3, 0.05, 22), (2100, 2600, 2, 0.02, 23),
+               (1500, 900, 5, 0.3, 24), (1200, 2000, 8, 0.5, 25)]
+
+
+@pytest.mark.parametrize("shape", GRAD_SHAPES, ids=[f"{s[0]}x{s[1]}d{s[2]}" for s in GRAD_SHAPES])
+def test_grad_matches_oracle(shape):
+    n, m, d, eps, seed = shape
+    x, y, a, b = random_problem(n, m, d, seed, zero_frac=0.1)
+    eps = eps32(eps)
+    rng = np.random.default_rng(seed)
+    g = (0.3 * rng.standard_normal(m)).astype(np.float32)
+    say("grad", shape)
+    X, Y, A, B, G = dev(x, y, a, b, g)
+    grad = host(sk.grad_x(X, Y, A, B, G, eps=eps))
+    want = oracle.grad_x(x, y, a, b, g, eps)
+    maxc = oracle.max_cost(x, y)
+    k = kappa(np.zeros(1), g, maxc, eps)
+    assert np.all(grad[a == 0] == 0.0)
+    say("grad err/tol", np.max(np.abs(grad - want)) / (2 * a.max() * 16 * k * math.sqrt(maxc)))
+    assert np.max(np.abs(grad - want)) <= 2 * a.max() * 16 * k * math.sqrt(maxc)
+
+
+RESID_SHAPES = [(600, 800, 2, 0.05, 7, 31), (2300, 1700, 3, 0.02, 12, 32), (1000, 1000, 6, 0.3, 3, 33)]
+
+
+@pytest.mark.parametrize("shape", RESID_SHAPES, ids=[f"{s[0]}x{s[1]}d{s[2]}" for s in RESID_SHAPES])
+def test_marginal_residual_matches_oracle(shape):
+    n, m, d, eps, iters, seed = shape
+    x, y, a, b = random_problem(n, m, d, seed, zero_frac=0.05)
+    eps = eps32(eps)
+    say("residual", shape)
+    f, g, _ = gpu_solve(x, y, a, b, eps, iters)
+    X, Y, A, B, F, G = dev(x, y, a, b, f.astype(np.float32), g.astype(np.float32))
+    r = host(sk.marginal_residual(X, Y, A, B, F, G, eps=eps))
+    ro = oracle.residual(x, y, a, b, f, g, eps)
+    maxc = oracle.max_cost(x, y)
+    k = kappa(f, g, maxc, eps)
+    tol_inf = 32 * k * (max(a.max(), b.max()) + ro[:2].max())
+    assert abs(r[0] - ro[0]) <= tol_inf
+    assert abs(r[1] - ro[1]) <= tol_inf
+    assert abs(r[2] - ro[2]) <= 32 * k * (a.sum() + ro[2])
+    assert abs(r[3] - ro[3]) <= 32 * k * (b.sum() + ro[3])
+    say("residual err/tol", abs(r[0] - ro[0]) / tol_inf, abs(r[1] - ro[1]) / tol_inf, "value/tol", ro[0] / tol_inf)
+    assert ro[0] > 10 * tol_inf  # a residual well above the noise floor was compared
+
+
+def test_residual_trace_matches_oracle_at_same_iterates():
+    """The fused trace after iteration k equals the residual of the GPU's own
+    (f_k, g_k) (deterministic prefixes) as the oracle evaluates it."""
+    x, y, a, b = make_inputs("gauss_d2", n=2000, m=2000)
+    eps = eps32(0.05)
+    say("trace 2000x2000")
+    _, _, tr = gpu_solve(x, y, a, b, eps, 30, check_every=10)
+    assert tr.shape == (3,)
+    maxc = oracle.max_cost(x, y)
+    for idx, k in enumerate((10, 20, 30)):
+        fk, gk, _ = gpu_solve(x, y, a, b, eps, k)
+        ro = oracle.residual(x, y, a, b, fk, gk, eps)
+        kap = kappa(fk, gk, maxc, eps)
+        assert abs(tr[idx] - max(ro[0], ro[1])) <= 32 * kap * (a.max() + ro[0]), (k, tr[idx], ro)
+
+
+def test_deterministic_and_zero_iterations():
+    x, y, a, b = random_problem(3000, 2000, 3, 41)
+    say("determinism")
+    f1, g1, t1 = gpu_solve(x, y, a, b, 0.05, 12, check_every=4)
+    f2, g2, t2 = gpu_solve(x, y, a, b, 0.05, 12, check_every=4)
+    assert np.array_equal(f1, f2) and np.array_equal(g1, g2) and np.array_equal(t1, t2)
+    f0, g0, t0 = gpu_solve(x, y, a, b, 0.05, 0)
+    assert np.all(f0 == 0) and np.all(g0 == 0) and t0.size == 0
+    # check_every that does not divide n_iters: floor(n_iters / check_every) entries
+    _, _, t3 = gpu_solve(x, y, a, b, 0.05, 13, check_every=4)
+    assert t3.shape == (3,) and np.array_equal(t3, t1)
+
+
+def test_check_inputs_rejects_bad_data():
+    x, y, a, b = random_problem(100, 80, 2, 51)
+    X, Y, A, B = dev(x, y, a, b)
+    sk.check_inputs(X, Y, A, B)
+    bad = A.clone()
+    bad[3] = -1e-3
+    with pytest.raises(ValueError, match="NEG_WEIGHT"):
+        sk.check_inputs(X, Y, bad, B)
+    with pytest.raises(ValueError, match="MASS_MISMATCH"):
+        sk.check_inputs(X, Y, A * 1.01, B)
+    with pytest.raises(ValueError, match="EMPTY"):
+        sk.check_inputs(X, Y, A * 0, B * 0)
+    xn = X.clone()
+    xn[5, 1] = float("nan")
+    with pytest.raises(ValueError, match="NONFINITE"):
+        sk.check_inputs(xn, Y, A, B)
+    with pytest.raises(ValueError, match="float32"):
+        sk.solve(X.double(), Y.double(), eps=0.1, n_iters=2)
+    # uniform default weights
+    f, g, _ = sk.solve(X, Y, eps=0.1, n_iters=3)
+    fo, go, _ = oracle.sinkhorn(x, y, np.full(100, 1 / 100), np.full(80, 1 / 80), eps32(0.1), 3)
+    assert np.max(np.abs(host(f) - fo)) <= 1e-4 * oracle.max_cost(x, y)
