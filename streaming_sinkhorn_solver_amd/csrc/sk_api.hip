@@ -9,7 +9,9 @@
 #include <cfloat>
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 namespace sk {
@@ -40,6 +42,31 @@ Split split_for(int64_t nq, int64_t nk, int rows_per_block) {
 int rows_per_block(int d) {
     (void)d;
     return valu_rows_per_block();
+}
+
+// Upper bound on the workgroups of a streamed pass, from the sizes alone (the
+// workspace is sized with it): at most kMaxGroups, each with >= kMinKeysPerGroup keys.
+int64_t groups_bound(int64_t nq, int64_t nk, int rpb) {
+    const int64_t total = (nq + rpb - 1) / rpb * nk;
+    int64_t w = (total + kMinKeysPerGroup - 1) / kMinKeysPerGroup;
+    w = std::min<int64_t>(w, kMaxGroups);
+    w = std::min<int64_t>(w, ((int64_t)1 << 62) / total);  // keeps w * total in int64
+    return std::max<int64_t>(w, 1);
+}
+
+// Workgroups the GPU holds at once for the d-dimensional pass, per device.
+int pass_capacity(int d) {
+    static std::mutex mu;
+    static std::map<std::pair<int, int>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    auto key = std::make_pair(dev, d);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    const int c = valu_pass_capacity(d);
+    if (c > 0) cache[key] = c;
+    return c;
 }
 
 int check_sizes(int64_t n, int64_t m, int32_t d) {
@@ -89,11 +116,13 @@ int prepare(const Ws& W, const float* x, const float* y, const float* a, const f
 
 // A streamed pass with queries from one side and keys from the other.
 // row_side = true: queries x (n), keys y (m); otherwise the transpose.
-PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q) {
+PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int capacity) {
     const Layout& L = W.L;
     PassArgs p{};
     const int64_t nq = row_side ? L.n : L.m, nk = row_side ? L.m : L.n;
-    Split sp = split_for(nq, nk, rows_per_block(L.d));
+    p.rpb = rows_per_block(L.d);
+    p.total = (nq + p.rpb - 1) / p.rpb * nk;
+    p.W = (int)std::min<int64_t>(groups_bound(nq, nk, p.rpb), std::max(capacity, 1));
     p.q = W.f(row_side ? L.xp : L.yp);
     p.k = W.f(row_side ? L.yp : L.xp);
     p.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
@@ -101,8 +130,6 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q) {
     p.nk = (int)nk;
     p.P = L.P;
     p.qscale = 2.0f * kLog2e / eps;
-    p.cols_per_split = sp.cols;
-    p.nsplit = sp.nsplit;
     p.part = reinterpret_cast<float2*>(W.base + L.part);
     Fin& F = p.fin;
     F.mode = kFinSolve;
@@ -185,8 +212,9 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.lse_c = take(um * 4);
     L.rbuf = take(umx * 4);
     const int rpb = rows_per_block(d);
-    const Split sr = split_for(n, m, rpb), sc = split_for(m, n, rpb);
-    const size_t part_rows = std::max((size_t)sr.nsplit * un, (size_t)sc.nsplit * um);
+    const Split sr = split_for(n, m, rpb);
+    const size_t stream_k = (size_t)std::max(groups_bound(n, m, rpb), groups_bound(m, n, rpb)) * 2 * rpb;
+    const size_t part_rows = std::max((size_t)sr.nsplit * un, stream_k);
     L.part = take(part_rows * sizeof(float2));
     L.partA = take(sr.nsplit > 1 ? (size_t)sr.nsplit * un * P * 4 : 0);
     L.red = take((size_t)4 * kRedBlocks * 3 * sizeof(double));
@@ -297,11 +325,13 @@ int sk_solve(const float* x, const float* y, const float* a, const float* b, int
         SK_TRY(launch_fill(g, m, 0.0f, s));
         return SK_OK;
     }
+    const int cap = pass_capacity(d);
+    if (cap <= 0) return SK_ERR_HIP;
     if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 1, nullptr, s))) return st;
 
-    PassArgs row = make_pass(W, true, eps, a);
+    PassArgs row = make_pass(W, true, eps, a, cap);
     row.fin.pot = f;
-    PassArgs col = make_pass(W, false, eps, b);
+    PassArgs col = make_pass(W, false, eps, b, cap);
     col.fin.pot = g;
     float* rbuf = W.f(L.rbuf);
 
@@ -344,17 +374,19 @@ int sk_marginal_residual(const float* x, const float* y, const float* a, const f
     if ((st = check_ws(ws, ws_bytes, L))) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     Ws W{L, static_cast<char*>(ws)};
+    const int cap = pass_capacity(d);
+    if (cap <= 0) return SK_ERR_HIP;
     if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
     float* rbuf = W.f(L.rbuf);
 
-    PassArgs row = make_pass(W, true, eps, a);
+    PassArgs row = make_pass(W, true, eps, a, cap);
     row.fin.mode = kFinResid;
     row.fin.pot_in = f;
     row.fin.rbuf = rbuf;
     if ((st = run_pass(W, row, s))) return st;
     SK_TRY(launch_resid_reduce(rbuf, (int)n, out + 0, out + 2, s));
 
-    PassArgs col = make_pass(W, false, eps, b);
+    PassArgs col = make_pass(W, false, eps, b, cap);
     col.fin.mode = kFinResid;
     col.fin.pot_in = g;
     col.fin.rbuf = rbuf;

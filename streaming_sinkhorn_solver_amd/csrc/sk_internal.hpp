@@ -34,7 +34,9 @@ constexpr float kNegBig = -3.402823466e38f;  // running-max start: -FLT_MAX, nev
 constexpr int kMaxD = 256;
 constexpr int kValuMaxD = 8;              // d <= 8: vector-ALU kernels; else matrix cores
 constexpr int kRedBlocks = 512;           // fixed partial count of the 2-stage reductions
-constexpr int kMaxSplit = 64;             // column splits of one streamed pass
+constexpr int kMaxSplit = 64;             // column splits of one gradient pass
+constexpr int kMaxGroups = 2048;          // workgroups of one streamed pass (upper bound)
+constexpr int kMinKeysPerGroup = 256;     // smallest key range a workgroup is given
 
 // Packed stride (floats) of one point in the workspace.
 //  VALU layout:  [coords (d) | bias | zero pad] to a multiple of 4 (float4 loads).
@@ -68,15 +70,25 @@ struct Fin {
 };
 
 // Arguments of one streamed log-sum-exp pass over all (query, key) pairs.
+//
+// Work decomposition ("stream-K"): the queries are cut into row blocks of
+// rpb rows; the flattened space of (row block, key) units u = rb * nk + j,
+// total = n_row_blocks * nk, is cut into W equal contiguous ranges
+// [w * total / W, (w + 1) * total / W), one per workgroup, with W the number
+// of workgroups the GPU holds at once.  A range covering a whole row block
+// finishes it in place; a range that starts or ends inside a row block leaves
+// a partial (M, S) for it in slot 0 (its first segment) or slot 1 (its last),
+// and the merge combines the partials of each row block in workgroup order.
 struct PassArgs {
     const float* q;      // query cloud, packed [nq][P]
     const float* k;      // key cloud, packed [nk][P]
     const float* kbias;  // separate key bias [nk] (matrix-core layout), else null
     int nq, nk, P;
     float qscale;        // 2 log2e / eps
-    int cols_per_split;
-    int nsplit;
-    float2* part;        // [nsplit][nq] partial (M, S) when nsplit > 1
+    int rpb;             // rows per block
+    int W;               // workgroups
+    int64_t total;       // n_row_blocks * nk
+    float2* part;        // [W][2][rpb] partial (M, S)
     Fin fin;
 };
 
@@ -131,5 +143,8 @@ hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t 
                             hipEvent_t ev1 = nullptr);
 hipError_t launch_grad_valu(const GradArgs& a, hipStream_t s);
 int valu_rows_per_block();
+// Workgroups of the d-dimensional pass kernel resident at once on the current
+// device (CUs x occupancy), 0 on failure.
+int valu_pass_capacity(int d);
 
 }  // namespace sk

@@ -90,37 +90,18 @@ __device__ __forceinline__ void stage_tile(float4* tile, const float4* __restric
     }
 }
 
+// Streams keys [j0, j1) past the R query rows each lane holds, updating the
+// running max M and rescaled sum S of every row (base 2).
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
+__device__ __forceinline__ void scan_keys(float4* tile, const float4* __restrict__ kp, const float (&q)[kR][D],
+                                          float (&M)[kR], float (&S)[kR], int j0, int j1) {
     constexpr int P = ((D + 1 + 3) / 4) * 4;
     constexpr int V = P / 4;
-    __shared__ float4 tile[kTL * V];
-
-    const int split = blockIdx.y;
-    const int row0 = blockIdx.x * (kBlock * kR) + threadIdx.x;
-
-    float q[kR][D];
-    float M[kR], S[kR];
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-        const int i = row0 + r * kBlock;
-        const int ic = i < A.nq ? i : A.nq - 1;
-        const float* qr = A.q + (size_t)ic * P;
-#pragma unroll
-        for (int t = 0; t < D; ++t) q[r][t] = qr[t] * A.qscale;
-        M[r] = kNegBig;
-        S[r] = 0.0f;
-    }
-
-    const int c0 = split * A.cols_per_split;
-    const int c1 = min(c0 + A.cols_per_split, A.nk);
-    const float4* kp = reinterpret_cast<const float4*>(A.k);
-
-    for (int base = c0; base < c1; base += kTL) {
+    for (int base = j0; base < j1; base += kTL) {
         __syncthreads();
-        stage_tile<D>(tile, kp, base, c1);
+        stage_tile<D>(tile, kp, base, j1);
         __syncthreads();
-        const int ntile = min(kTL, c1 - base);
+        const int ntile = min(kTL, j1 - base);
         for (int c = 0; c < ntile; c += kTJ) {
             float kk[kTJ][P];
 #pragma unroll
@@ -155,29 +136,76 @@ __global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
             }
         }
     }
+}
 
+__device__ __forceinline__ int64_t range_lo(int w, int64_t total, int W) { return (int64_t)w * total / W; }
+
+// The workgroup whose range holds unit u: the largest w with range_lo(w) <= u.
+__device__ __forceinline__ int range_owner(int64_t u, int64_t total, int W) {
+    return (int)(((u + 1) * W + total - 1) / total) - 1;
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
+    constexpr int P = ((D + 1 + 3) / 4) * 4;
+    __shared__ float4 tile[kTL * (P / 4)];
+    const float4* kp = reinterpret_cast<const float4*>(A.k);
+
+    const int w = blockIdx.x;
+    const int64_t lo = range_lo(w, A.total, A.W), hi = range_lo(w + 1, A.total, A.W);
+    for (int64_t u = lo; u < hi;) {
+        const int rb = (int)(u / A.nk);
+        const int j0 = (int)(u - (int64_t)rb * A.nk);
+        const int j1 = (int)min<int64_t>((int64_t)A.nk, (int64_t)j0 + (hi - u));
+        const int row0 = rb * A.rpb + threadIdx.x;
+
+        float q[kR][D];
+        float M[kR], S[kR];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-        const int i = row0 + r * kBlock;
-        if (i >= A.nq) continue;
-        if (A.nsplit == 1)
-            finalize(A.fin, i, M[r] + lg2(S[r]));
-        else
-            A.part[(size_t)split * A.nq + i] = make_float2(M[r], S[r]);
+        for (int r = 0; r < kR; ++r) {
+            const int i = row0 + r * kBlock;
+            const int ic = i < A.nq ? i : A.nq - 1;
+            const float* qr = A.q + (size_t)ic * P;
+#pragma unroll
+            for (int t = 0; t < D; ++t) q[r][t] = qr[t] * A.qscale;
+            M[r] = kNegBig;
+            S[r] = 0.0f;
+        }
+        scan_keys<D>(tile, kp, q, M, S, j0, j1);
+
+        const bool complete = (j0 == 0 && j1 == A.nk);
+        float2* slot = A.part + ((size_t)w * 2 + (u == lo ? 0 : 1)) * A.rpb;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int i = row0 + r * kBlock;
+            if (i >= A.nq) continue;
+            if (complete)
+                finalize(A.fin, i, M[r] + lg2(S[r]));
+            else
+                slot[r * kBlock + threadIdx.x] = make_float2(M[r], S[r]);
+        }
+        u += j1 - j0;
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_merge(const float2* __restrict__ part, int nq, int nsplit, Fin F) {
+// Combines, for every row of a row block split across workgroups, the partial
+// (M, S) pairs in workgroup order: M = max M_w, S = sum S_w 2^{M_w - M}.
+__global__ __launch_bounds__(kBlock) void k_merge(PassArgs A) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= nq) return;
-    float M = kNegBig;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[(size_t)s * nq + i].x);
-    float S = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float2 p = part[(size_t)s * nq + i];
-        S += p.y * ex2(p.x - M);
+    if (i >= A.nq) return;
+    const int rb = i / A.rpb, lr = i - rb * A.rpb;
+    const int64_t u0 = (int64_t)rb * A.nk, u1 = u0 + A.nk;
+    const int wf = range_owner(u0, A.total, A.W), wl = range_owner(u1 - 1, A.total, A.W);
+    if (wf == wl) return;  // one workgroup held the whole row block and finished it
+    float M = kNegBig, S = 0.0f;
+    for (int w = wf; w <= wl; ++w) {
+        const int slot = range_lo(w, A.total, A.W) >= u0 ? 0 : 1;
+        const float2 p = A.part[((size_t)w * 2 + slot) * A.rpb + lr];
+        const float mn = fmaxf(M, p.x);
+        S = S * ex2(M - mn) + p.y * ex2(p.x - mn);
+        M = mn;
     }
-    finalize(F, i, M + lg2(S));
+    finalize(A.fin, i, M + lg2(S));
 }
 
 // Gradient pass: the same traversal with the running weighted key sum
@@ -302,15 +330,22 @@ __global__ __launch_bounds__(kBlock) void k_grad_merge(GradArgs A) {
 
 template <int D>
 hipError_t launch_pass_d(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    const int rpb = kBlock * kR;
-    dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
     if (ev0) (void)hipEventRecord(ev0, s);
-    hipLaunchKernelGGL(k_pass_valu<D>, grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_pass_valu<D>, dim3(a.W), dim3(kBlock), 0, s, a);
     if (ev1) (void)hipEventRecord(ev1, s);
-    if (a.nsplit > 1)
-        hipLaunchKernelGGL(k_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a.part, a.nq,
-                           a.nsplit, a.fin);
+    const int64_t n_row_blocks = a.total / a.nk;
+    if (a.W > n_row_blocks || a.total % a.W != 0 || (a.total / a.W) % a.nk != 0)
+        hipLaunchKernelGGL(k_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
     return hipGetLastError();
+}
+
+template <int D>
+int capacity_d() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pass_valu<D>, kBlock, 0) != hipSuccess) return 0;
+    return cus * per_cu;
 }
 
 template <int D>
@@ -326,6 +361,20 @@ hipError_t launch_grad_d(const GradArgs& a, hipStream_t s) {
 }  // namespace
 
 int valu_rows_per_block() { return kBlock * kR; }
+
+int valu_pass_capacity(int d) {
+    switch (d) {
+        case 1: return capacity_d<1>();
+        case 2: return capacity_d<2>();
+        case 3: return capacity_d<3>();
+        case 4: return capacity_d<4>();
+        case 5: return capacity_d<5>();
+        case 6: return capacity_d<6>();
+        case 7: return capacity_d<7>();
+        case 8: return capacity_d<8>();
+        default: return 0;
+    }
+}
 
 hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     switch (d) {
