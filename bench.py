@@ -65,6 +65,18 @@ def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
             "avg_launch_us": round(avg_launch_s * 1e6, 3), "ceiling_pairs_per_s": ceiling_pairs}
 
 
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+
+
+def roofline_mfma(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
+    """Matrix-core roofline of one streamed pass for d > 8: the algorithmic work is
+    the cross term, 2d flops per pair evaluation, against the fp32 MFMA peak."""
+    achieved = pairs_per_launch * 2 * d / avg_launch_s / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4), "traffic": None, "ops_per_pair": 2 * d,
+            "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
+
+
 def load_traffic(kernel_key: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
     were taken on the current kernel source (else None)."""
@@ -187,9 +199,13 @@ def main():
     value = pair_evals / step_s
     avg_launch_s = pass_ms * 1e-3 / launches
     pairs_per_launch = pairs / launches
-    roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
+    if d <= 8:
+        roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
+        roof["kernel"] = f"k_pass_valu<{d}>"
+    else:
+        roof = roofline_mfma(d, pairs_per_launch, avg_launch_s)
+        roof["kernel"] = "k_pass_mfma<%d>" % max(16, 1 << (d - 1).bit_length())
     roof["traffic"] = load_traffic(f"{args.workload}:pass")
-    roof["kernel"] = f"k_pass_valu<{d}>"
 
     out = {
         "metric": "point-pair evals/sec and Sinkhorn iters/sec (n=m=50k,d=3); % fp32 peak",

@@ -40,8 +40,7 @@ Split split_for(int64_t nq, int64_t nk, int rows_per_block) {
 }
 
 int rows_per_block(int d) {
-    (void)d;
-    return valu_rows_per_block();
+    return d <= kValuMaxD ? valu_rows_per_block() : mfma_rows_per_block(packed_stride(d));
 }
 
 // Upper bound on the workgroups of a streamed pass, from the sizes alone (the
@@ -64,14 +63,14 @@ int pass_capacity(int d) {
     auto key = std::make_pair(dev, d);
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
-    const int c = valu_pass_capacity(d);
+    const int c = d <= kValuMaxD ? valu_pass_capacity(d) : mfma_pass_capacity(packed_stride(d));
     if (c > 0) cache[key] = c;
     return c;
 }
 
 int check_sizes(int64_t n, int64_t m, int32_t d) {
     if (n < 1 || m < 1 || d < 1 || n > INT32_MAX || m > INT32_MAX) return SK_ERR_SHAPE;
-    if (d > kValuMaxD) return SK_ERR_UNSUPPORTED_D;
+    if (d > kMaxD) return SK_ERR_UNSUPPORTED_D;
     return SK_OK;
 }
 
@@ -180,7 +179,10 @@ int run_pass(const Ws& W, const PassArgs& p, hipStream_t s) {
             T.pairs += (double)p.nq * (double)p.nk;
         }
     }
-    SK_TRY(launch_pass_valu(p, W.L.d, s, e0, e1));
+    if (W.L.mfma)
+        SK_TRY(launch_pass_mfma(p, s, e0, e1));
+    else
+        SK_TRY(launch_pass_valu(p, W.L.d, s, e0, e1));
     return SK_OK;
 }
 
@@ -400,6 +402,7 @@ int sk_grad_x(const float* x, const float* y, const float* a, const float* b, in
     if (!x || !y || !a || !b || !g || !grad) return SK_ERR_NULL;
     int st = check_sizes(n, m, d);
     if (st) return st;
+    if (d > kValuMaxD) return SK_ERR_UNSUPPORTED_D;
     if ((st = check_eps(eps))) return st;
     const Layout L = make_layout(n, m, d);
     if ((st = check_ws(ws, ws_bytes, L))) return st;

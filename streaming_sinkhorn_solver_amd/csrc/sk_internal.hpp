@@ -40,9 +40,13 @@ constexpr int kMinKeysPerGroup = 256;     // smallest key range a workgroup is g
 
 // Packed stride (floats) of one point in the workspace.
 //  VALU layout:  [coords (d) | bias | zero pad] to a multiple of 4 (float4 loads).
-//  MFMA layout:  [coords (d) | zero pad] to a multiple of 16; bias kept apart.
+//  MFMA layout:  [coords (d) | zero pad] to max(16, next power of two >= d);
+//                the bias is kept in a separate array.
 inline int packed_stride(int d) {
-    return d <= kValuMaxD ? ((d + 1 + 3) / 4) * 4 : ((d + 15) / 16) * 16;
+    if (d <= kValuMaxD) return ((d + 1 + 3) / 4) * 4;
+    int p = 16;
+    while (p < d) p *= 2;
+    return p;
 }
 
 // What a streamed pass does with each finished row's log-sum-exp.
@@ -143,6 +147,13 @@ hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t 
                             hipEvent_t ev1 = nullptr);
 hipError_t launch_grad_valu(const GradArgs& a, hipStream_t s);
 int valu_rows_per_block();
+// Matrix-core passes (9 <= d <= 256), by packed stride P in {16, 32, 64, 128, 256}.
+hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+int mfma_rows_per_block(int P);
+int mfma_pass_capacity(int P);
+// Merges the partial (M, S) pairs of row blocks split across workgroups (no-op
+// launch-wise when every row block was finished by one workgroup).
+hipError_t launch_merge(const PassArgs& a, hipStream_t s);
 // Workgroups of the d-dimensional pass kernel resident at once on the current
 // device (CUs x occupancy), 0 on failure.
 int valu_pass_capacity(int d);

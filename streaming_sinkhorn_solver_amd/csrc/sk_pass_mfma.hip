@@ -1,0 +1,213 @@
+// sk_pass_mfma.hip -- streamed log-sum-exp passes with the cross term on fp32
+// matrix cores (9 <= d <= 256).
+//
+// The score of a (query, key) pair is s_ij = <q_i, k_j> + h_j (base 2, see
+// sk_internal.hpp): a dense contraction over the padded dimension P, followed
+// by a per-row online log-sum-exp ("FlashSinkhorn: IO-Aware Entropic Optimal
+// Transport on GPU", Methodology 1-2: biased dot-product scores, streamed
+// tiles, running max / sum-exp, no materialisation).
+//
+// Mapping to CDNA4 (v_mfma_f32_16x16x4f32, D = A B + C, wave64):
+//  * lane l = 16 g + c; A is 16 keys x 4 k (lane: key c, k-step slot g),
+//    B is 4 k x 16 queries (lane: query c, slot g), D is 16 keys x 16 queries
+//    with lane l holding keys 4g..4g+3 of query c;
+//  * the contraction index is permuted so that lane group g owns the
+//    contiguous k range [g P/4, (g+1) P/4): step t of the K loop uses
+//    k = g P/4 + t.  Each lane therefore keeps its query's P/4 coordinates in
+//    registers for the whole pass (row-stationary) and reads its key's P/4
+//    coordinates from LDS as float4s;
+//  * the accumulator starts at the key biases, so the bias add is free;
+//  * each lane runs an online (M, S) over the keys it sees; the four lane
+//    groups that share a query are merged with two cross-lane exchanges at
+//    the end of a segment;
+//  * NQB independent 16-query blocks per wave interleave their MFMA chains.
+// Work is split across workgroups with the same stream-K ranges as the vector
+// passes; a row block here is 4 waves x NQB x 16 queries.
+#include "sk_internal.hpp"
+#include "sk_pass_common.hpp"
+
+namespace sk {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = kBlock / 64;
+
+template <int P>
+constexpr int mfma_nqb() {
+    return P <= 64 ? 4 : (P == 128 ? 2 : 1);
+}
+
+template <int P>
+constexpr int mfma_tile_keys() {
+    return 8192 / P < 16 ? 16 : 8192 / P;
+}
+
+__device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
+    const float mn = fmaxf(M, m2);
+    S = S * ex2(M - mn) + s2 * ex2(m2 - mn);
+    M = mn;
+}
+
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
+    constexpr int KT = P / 4;           // MFMA k-steps per 16-key block
+    constexpr int PS = P + 4;           // padded LDS row stride (floats): conflict-free float4 reads
+    constexpr int NQB = mfma_nqb<P>();  // 16-query blocks per wave
+    constexpr int TL = mfma_tile_keys<P>();
+    __shared__ __align__(16) float ktile[TL * PS];
+    __shared__ __align__(16) float btile[TL];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const float4* kp = reinterpret_cast<const float4*>(A.k);
+
+    const int w = blockIdx.x;
+    const int64_t lo = range_lo(w, A.total, A.W), hi = range_lo(w + 1, A.total, A.W);
+    for (int64_t u = lo; u < hi;) {
+        const int rb = (int)(u / A.nk);
+        const int j0 = (int)(u - (int64_t)rb * A.nk);
+        const int j1 = (int)min<int64_t>((int64_t)A.nk, (int64_t)j0 + (hi - u));
+        const int qrow0 = rb * A.rpb + wave * (NQB * 16);
+
+        float qf[NQB][KT];
+        float M[NQB], S[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            const int i = qrow0 + qb * 16 + c;
+            const int ic = i < A.nq ? i : A.nq - 1;
+            const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
+#pragma unroll
+            for (int t4 = 0; t4 < KT / 4; ++t4) {
+                const float4 v = qr[t4];
+                qf[qb][4 * t4 + 0] = v.x * A.qscale;
+                qf[qb][4 * t4 + 1] = v.y * A.qscale;
+                qf[qb][4 * t4 + 2] = v.z * A.qscale;
+                qf[qb][4 * t4 + 3] = v.w * A.qscale;
+            }
+            M[qb] = kNegBig;
+            S[qb] = 0.0f;
+        }
+
+        for (int base = j0; base < j1; base += TL) {
+            __syncthreads();
+            for (int e = threadIdx.x; e < TL * (P / 4); e += kBlock) {
+                const int key = e / (P / 4), part = e - key * (P / 4);
+                const int col = base + key;
+                const float4 v = col < j1 ? kp[(size_t)col * (P / 4) + part] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                *reinterpret_cast<float4*>(&ktile[key * PS + part * 4]) = v;
+            }
+            for (int e = threadIdx.x; e < TL; e += kBlock) btile[e] = base + e < j1 ? A.kbias[base + e] : -INFINITY;
+            __syncthreads();
+            const int ntile = min(TL, j1 - base);
+            for (int kb = 0; kb < ntile; kb += 16) {
+                float kf[KT];
+                const float4* kr = reinterpret_cast<const float4*>(&ktile[(kb + c) * PS + g * KT]);
+#pragma unroll
+                for (int t4 = 0; t4 < KT / 4; ++t4) {
+                    const float4 v = kr[t4];
+                    kf[4 * t4 + 0] = v.x;
+                    kf[4 * t4 + 1] = v.y;
+                    kf[4 * t4 + 2] = v.z;
+                    kf[4 * t4 + 3] = v.w;
+                }
+                const f4 bias = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
+                f4 acc[NQB];
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) acc[qb] = bias;
+#pragma unroll
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+                        acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    const float mt = fmaxf(fmaxf(acc[qb][0], acc[qb][1]), fmaxf(acc[qb][2], acc[qb][3]));
+                    const float mn = fmaxf(M[qb], mt);
+                    float s = S[qb] * ex2(M[qb] - mn);
+                    s += ex2(acc[qb][0] - mn);
+                    s += ex2(acc[qb][1] - mn);
+                    s += ex2(acc[qb][2] - mn);
+                    s += ex2(acc[qb][3] - mn);
+                    S[qb] = s;
+                    M[qb] = mn;
+                }
+            }
+        }
+
+        // the four lane groups hold disjoint key subsets of the same queries
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            lse_merge(M[qb], S[qb], __shfl_xor(M[qb], 16), __shfl_xor(S[qb], 16));
+            lse_merge(M[qb], S[qb], __shfl_xor(M[qb], 32), __shfl_xor(S[qb], 32));
+        }
+        const bool complete = (j0 == 0 && j1 == A.nk);
+        float2* slot = A.part + ((size_t)w * 2 + (u == lo ? 0 : 1)) * A.rpb;
+        if (g == 0) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                const int i = qrow0 + qb * 16 + c;
+                if (i >= A.nq) continue;
+                if (complete)
+                    finalize(A.fin, i, M[qb] + lg2(S[qb]));
+                else
+                    slot[wave * (NQB * 16) + qb * 16 + c] = make_float2(M[qb], S[qb]);
+            }
+        }
+        u += j1 - j0;
+    }
+}
+
+template <int P>
+hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (ev0) (void)hipEventRecord(ev0, s);
+    hipLaunchKernelGGL(k_pass_mfma<P>, dim3(a.W), dim3(kBlock), 0, s, a);
+    if (ev1) (void)hipEventRecord(ev1, s);
+    return launch_merge(a, s);
+}
+
+template <int P>
+int capacity_p() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pass_mfma<P>, kBlock, 0) != hipSuccess) return 0;
+    return cus * per_cu;
+}
+
+}  // namespace
+
+int mfma_rows_per_block(int P) {
+    switch (P) {
+        case 16: return kWaves * mfma_nqb<16>() * 16;
+        case 32: return kWaves * mfma_nqb<32>() * 16;
+        case 64: return kWaves * mfma_nqb<64>() * 16;
+        case 128: return kWaves * mfma_nqb<128>() * 16;
+        case 256: return kWaves * mfma_nqb<256>() * 16;
+        default: return 0;
+    }
+}
+
+hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    switch (a.P) {
+        case 16: return launch_mfma_p<16>(a, s, ev0, ev1);
+        case 32: return launch_mfma_p<32>(a, s, ev0, ev1);
+        case 64: return launch_mfma_p<64>(a, s, ev0, ev1);
+        case 128: return launch_mfma_p<128>(a, s, ev0, ev1);
+        case 256: return launch_mfma_p<256>(a, s, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int mfma_pass_capacity(int P) {
+    switch (P) {
+        case 16: return capacity_p<16>();
+        case 32: return capacity_p<32>();
+        case 64: return capacity_p<64>();
+        case 128: return capacity_p<128>();
+        case 256: return capacity_p<256>();
+        default: return 0;
+    }
+}
+
+}  // namespace sk

@@ -21,6 +21,7 @@
 // The running max starts at -FLT_MAX, not -inf, so keys with zero weight
 // (bias -inf) never produce (-inf) - (-inf).
 #include "sk_internal.hpp"
+#include "sk_pass_common.hpp"
 
 #ifndef SK_VALU_R
 #define SK_VALU_R 4
@@ -38,34 +39,6 @@ namespace {
 constexpr int kR = SK_VALU_R;     // query rows per lane
 constexpr int kTJ = SK_VALU_TJ;   // keys per register chunk
 constexpr int kTL = SK_VALU_TL;   // keys per LDS tile
-
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
-
-// Applies a finished row's log-sum-exp (base 2) to the pass outputs.
-__device__ __forceinline__ void finalize(const Fin& F, int i, float lse) {
-    if (F.mode == kFinSolve) {
-        if (F.rbuf) {
-            const float wi = F.w[i];
-            const float r = wi > 0.0f ? wi * expm1f((lse - F.lse[i]) * kLn2) : 0.0f;
-            F.rbuf[i] = fabsf(r);
-        }
-        F.lse[i] = lse;
-        const float h = F.l2w[i] - lse;
-        if (F.bias_packed) F.bias_packed[(size_t)i * F.P + F.d] = h;
-        if (F.bias_sep) F.bias_sep[i] = h;
-        if (F.pot) F.pot[i] = F.nrm[i] - F.eps_ln2 * lse;
-    } else if (F.mode == kFinProbe) {
-        const float wi = F.w[i];
-        const float r = wi > 0.0f ? wi * expm1f((lse - F.lse[i]) * kLn2) : 0.0f;
-        F.rbuf[i] = fabsf(r);
-    } else {  // kFinResid: (P1)_i / a_i - 1 = exp((f_i - f~_i)/eps) - 1
-        const float wi = F.w[i];
-        const float e = (F.pot_in[i] - F.nrm[i]) * F.inv_eps + kLn2 * lse;
-        const float r = wi > 0.0f ? wi * expm1f(e) : 0.0f;
-        F.rbuf[i] = fabsf(r);
-    }
-}
 
 // Stages keys [base, base + kTL) of the split [.., c1) into LDS; keys past c1
 // get zero coordinates and bias -inf, so they add exactly nothing.
@@ -136,13 +109,6 @@ __device__ __forceinline__ void scan_keys(float4* tile, const float4* __restrict
             }
         }
     }
-}
-
-__device__ __forceinline__ int64_t range_lo(int w, int64_t total, int W) { return (int64_t)w * total / W; }
-
-// The workgroup whose range holds unit u: the largest w with range_lo(w) <= u.
-__device__ __forceinline__ int range_owner(int64_t u, int64_t total, int W) {
-    return (int)(((u + 1) * W + total - 1) / total) - 1;
 }
 
 template <int D>
@@ -333,10 +299,7 @@ hipError_t launch_pass_d(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEv
     if (ev0) (void)hipEventRecord(ev0, s);
     hipLaunchKernelGGL(k_pass_valu<D>, dim3(a.W), dim3(kBlock), 0, s, a);
     if (ev1) (void)hipEventRecord(ev1, s);
-    const int64_t n_row_blocks = a.total / a.nk;
-    if (a.W > n_row_blocks || a.total % a.W != 0 || (a.total / a.W) % a.nk != 0)
-        hipLaunchKernelGGL(k_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch_merge(a, s);
 }
 
 template <int D>
@@ -361,6 +324,13 @@ hipError_t launch_grad_d(const GradArgs& a, hipStream_t s) {
 }  // namespace
 
 int valu_rows_per_block() { return kBlock * kR; }
+
+hipError_t launch_merge(const PassArgs& a, hipStream_t s) {
+    const int64_t n_row_blocks = a.total / a.nk;
+    if (a.W > n_row_blocks || a.total % a.W != 0 || (a.total / a.W) % a.nk != 0)
+        hipLaunchKernelGGL(k_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
 
 int valu_pass_capacity(int d) {
     switch (d) {

@@ -69,6 +69,15 @@ SHAPES = [
     (2500, 3100, 8, 0.5, 10, 13, 1.0, 0.0),
     (3000, 2999, 3, 0.05, 15, 14, 0.5, 0.25),
     (4099, 130, 2, 0.01, 25, 15, 1.0, 0.0),
+    # matrix-core path: d > 8, padded to 16, 32, 64, 128, 256
+    (1500, 1700, 9, 0.2, 8, 16, 0.33, 0.0),
+    (2000, 1100, 16, 0.3, 8, 17, 0.25, 0.1),
+    (1200, 1300, 33, 0.3, 6, 18, 0.17, 0.0),
+    (2100, 2300, 64, 0.5, 10, 19, 0.125, 0.0),
+    (700, 900, 100, 0.5, 5, 20, 0.1, 0.0),
+    (600, 700, 128, 0.5, 5, 21, 0.09, 0.0),
+    (300, 500, 256, 0.5, 4, 22, 0.0625, 0.0),
+    (17, 5, 64, 0.1, 3, 23, 0.125, 0.0),
 ]
 
 
@@ -144,13 +153,14 @@ def test_grad_matches_oracle(shape):
     assert np.max(np.abs(grad - want)) <= 2 * a.max() * 16 * k * math.sqrt(maxc)
 
 
-RESID_SHAPES = [(600, 800, 2, 0.05, 7, 31), (2300, 1700, 3, 0.02, 12, 32), (1000, 1000, 6, 0.3, 3, 33)]
+RESID_SHAPES = [(600, 800, 2, 0.05, 7, 31), (2300, 1700, 3, 0.02, 12, 32), (1000, 1000, 6, 0.3, 3, 33),
+                (1100, 900, 64, 0.02, 2, 34)]
 
 
 @pytest.mark.parametrize("shape", RESID_SHAPES, ids=[f"{s[0]}x{s[1]}d{s[2]}" for s in RESID_SHAPES])
 def test_marginal_residual_matches_oracle(shape):
     n, m, d, eps, iters, seed = shape
-    x, y, a, b = random_problem(n, m, d, seed, zero_frac=0.05)
+    x, y, a, b = random_problem(n, m, d, seed, scale=1.0 / math.sqrt(d), zero_frac=0.05)
     eps = eps32(eps)
     say("residual", shape)
     f, g, _ = gpu_solve(x, y, a, b, eps, iters)
