@@ -135,6 +135,8 @@ def main():
     ap.add_argument("--iters", type=int, default=None, help="override the workload's iteration count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceilings", action="store_true", help="run the issue-rate micro-benchmarks and exit")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -167,6 +169,14 @@ def main():
     cost_out = torch.empty(1, dtype=torch.float64, device=dev)
     grad = torch.empty((n, d), dtype=torch.float32, device=dev)
     sk.check_inputs(X, Y, A, B, ws)  # data validation once, outside the timed region
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy calibration: {args.copy_calibration} MiB read + {args.copy_calibration} MiB written",
+              file=sys.stderr)
+        del src, dst
 
     def step():
         sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, check_every=ce, ws=ws, f=f, g=g, trace=trace, check=False)
