@@ -214,7 +214,7 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.lse_c = take(um * 4);
     L.rbuf = take(umx * 4);
     const int rpb = rows_per_block(d);
-    const Split sr = split_for(n, m, rpb);
+    const Split sr = split_for(n, m, valu_rows_per_block());  // gradient pass (vector ALU, d <= 8)
     const size_t stream_k = (size_t)std::max(groups_bound(n, m, rpb), groups_bound(m, n, rpb)) * 2 * rpb;
     const size_t part_rows = std::max((size_t)sr.nsplit * un, stream_k);
     L.part = take(part_rows * sizeof(float2));
@@ -411,7 +411,7 @@ int sk_grad_x(const float* x, const float* y, const float* a, const float* b, in
     if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 2, g, s))) return st;
 
     GradArgs ga{};
-    const Split sp = split_for(n, m, rows_per_block(d));
+    const Split sp = split_for(n, m, valu_rows_per_block());
     ga.q = W.f(L.xp);
     ga.k = W.f(L.yp);
     ga.kbias = L.mfma ? W.f(L.hy) : nullptr;

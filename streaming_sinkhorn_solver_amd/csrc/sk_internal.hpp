@@ -36,7 +36,10 @@ constexpr int kValuMaxD = 8;              // d <= 8: vector-ALU kernels; else ma
 constexpr int kRedBlocks = 512;           // fixed partial count of the 2-stage reductions
 constexpr int kMaxSplit = 64;             // column splits of one gradient pass
 constexpr int kMaxGroups = 2048;          // workgroups of one streamed pass (upper bound)
-constexpr int kMinKeysPerGroup = 256;     // smallest key range a workgroup is given
+#ifndef SK_MIN_KEYS
+#define SK_MIN_KEYS 64
+#endif
+constexpr int kMinKeysPerGroup = SK_MIN_KEYS;  // smallest key range a workgroup is given
 
 // Packed stride (floats) of one point in the workspace.
 //  VALU layout:  [coords (d) | bias | zero pad] to a multiple of 4 (float4 loads).
@@ -82,7 +85,10 @@ struct Fin {
 // of workgroups the GPU holds at once.  A range covering a whole row block
 // finishes it in place; a range that starts or ends inside a row block leaves
 // a partial (M, S) for it in slot 0 (its first segment) or slot 1 (its last),
-// and the merge combines the partials of each row block in workgroup order.
+// and a merge kernel combines the partials of each row block in workgroup
+// order.  (Merging inside the pass by the last workgroup to arrive was
+// measured slower: every contributor then pays a device-scope release fence,
+// and the merging workgroup's loop over all partials is serial.)
 struct PassArgs {
     const float* q;      // query cloud, packed [nq][P]
     const float* k;      // key cloud, packed [nk][P]
@@ -147,13 +153,13 @@ hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t 
                             hipEvent_t ev1 = nullptr);
 hipError_t launch_grad_valu(const GradArgs& a, hipStream_t s);
 int valu_rows_per_block();
+// Merges the partial (M, S) pairs of row blocks split across workgroups (no
+// launch when every row block was finished by one workgroup).
+hipError_t launch_merge(const PassArgs& a, hipStream_t s);
 // Matrix-core passes (9 <= d <= 256), by packed stride P in {16, 32, 64, 128, 256}.
 hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 int mfma_rows_per_block(int P);
 int mfma_pass_capacity(int P);
-// Merges the partial (M, S) pairs of row blocks split across workgroups (no-op
-// launch-wise when every row block was finished by one workgroup).
-hipError_t launch_merge(const PassArgs& a, hipStream_t s);
 // Workgroups of the d-dimensional pass kernel resident at once on the current
 // device (CUs x occupancy), 0 on failure.
 int valu_pass_capacity(int d);

@@ -14,7 +14,9 @@
 //    in LDS and read back as wave-wide broadcasts;
 //  * per (row, key) the work is d FMAs, one max, one subtract, one exp2 and one
 //    add; the running max is updated once per chunk of TJ keys, so the
-//    rescale of S costs one exp2 per chunk rather than per pair;
+//    rescale of S costs one exp2 per chunk rather than per pair (R = 2 rows
+//    per lane and TJ = 16 keys per chunk were the fastest of 20 measured
+//    tilings at n = m = 50,000, d = 3);
 //  * when the rows alone cannot fill 256 CUs the key range is split across
 //    workgroups and the partial (M, S) pairs are merged exactly afterwards:
 //    M = max_s M_s, S = sum_s S_s 2^{M_s - M}.
@@ -24,10 +26,10 @@
 #include "sk_pass_common.hpp"
 
 #ifndef SK_VALU_R
-#define SK_VALU_R 4
+#define SK_VALU_R 2
 #endif
 #ifndef SK_VALU_TJ
-#define SK_VALU_TJ 8
+#define SK_VALU_TJ 16
 #endif
 #ifndef SK_VALU_TL
 #define SK_VALU_TL 256
@@ -155,23 +157,36 @@ __global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
 }
 
 // Combines, for every row of a row block split across workgroups, the partial
-// (M, S) pairs in workgroup order: M = max M_w, S = sum S_w 2^{M_w - M}.
+// (M, S) pairs: M = max M_w, S = sum S_w 2^{M_w - M}.  kMergeLanes lanes share
+// a row, each taking every kMergeLanes-th contributing workgroup, then a fixed
+// xor-shuffle tree joins them (the order is fixed, so results are repeatable).
+constexpr int kMergeLanes = 8;
+
 __global__ __launch_bounds__(kBlock) void k_merge(PassArgs A) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= A.nq) return;
-    const int rb = i / A.rpb, lr = i - rb * A.rpb;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    const int i = t / kMergeLanes, sub = t % kMergeLanes;
+    const bool live = i < A.nq;
+    const int ic = live ? i : A.nq - 1;
+    const int rb = ic / A.rpb, lr = ic - rb * A.rpb;
     const int64_t u0 = (int64_t)rb * A.nk, u1 = u0 + A.nk;
     const int wf = range_owner(u0, A.total, A.W), wl = range_owner(u1 - 1, A.total, A.W);
-    if (wf == wl) return;  // one workgroup held the whole row block and finished it
     float M = kNegBig, S = 0.0f;
-    for (int w = wf; w <= wl; ++w) {
+    for (int w = wf + sub; w <= wl; w += kMergeLanes) {
         const int slot = range_lo(w, A.total, A.W) >= u0 ? 0 : 1;
         const float2 p = A.part[((size_t)w * 2 + slot) * A.rpb + lr];
         const float mn = fmaxf(M, p.x);
         S = S * ex2(M - mn) + p.y * ex2(p.x - mn);
         M = mn;
     }
-    finalize(A.fin, i, M + lg2(S));
+#pragma unroll
+    for (int off = kMergeLanes / 2; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(M, off), s2 = __shfl_xor(S, off);
+        const float mn = fmaxf(M, m2);
+        S = S * ex2(M - mn) + s2 * ex2(m2 - mn);
+        M = mn;
+    }
+    // a row block held whole by one workgroup was finished by the pass itself
+    if (live && sub == 0 && wf != wl) finalize(A.fin, i, M + lg2(S));
 }
 
 // Gradient pass: the same traversal with the running weighted key sum
@@ -328,9 +343,10 @@ int valu_rows_per_block() { return kBlock * kR; }
 hipError_t launch_merge(const PassArgs& a, hipStream_t s) {
     const int64_t n_row_blocks = a.total / a.nk;
     if (a.W > n_row_blocks || a.total % a.W != 0 || (a.total / a.W) % a.nk != 0)
-        hipLaunchKernelGGL(k_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL(k_merge, dim3(((int64_t)a.nq * kMergeLanes + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
+
 
 int valu_pass_capacity(int d) {
     switch (d) {
