@@ -43,6 +43,11 @@ int rows_per_block(int d) {
     return d <= kValuMaxD ? valu_rows_per_block() : mfma_rows_per_block(packed_stride(d));
 }
 
+// Key-range split of the gradient pass (a plain split grid: it runs once per solve).
+Split grad_split(int64_t n, int64_t m, int d) {
+    return split_for(n, m, d <= kValuMaxD ? valu_rows_per_block() : mfma_grad_rows_per_block());
+}
+
 // Upper bound on the workgroups of a streamed pass, from the sizes alone (the
 // workspace is sized with it): at most kMaxGroups, each with >= kMinKeysPerGroup keys.
 int64_t groups_bound(int64_t nq, int64_t nk, int rpb) {
@@ -214,7 +219,7 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.lse_c = take(um * 4);
     L.rbuf = take(umx * 4);
     const int rpb = rows_per_block(d);
-    const Split sr = split_for(n, m, valu_rows_per_block());  // gradient pass (vector ALU, d <= 8)
+    const Split sr = grad_split(n, m, d);
     const size_t stream_k = (size_t)std::max(groups_bound(n, m, rpb), groups_bound(m, n, rpb)) * 2 * rpb;
     const size_t part_rows = std::max((size_t)sr.nsplit * un, stream_k);
     L.part = take(part_rows * sizeof(float2));
@@ -402,16 +407,17 @@ int sk_grad_x(const float* x, const float* y, const float* a, const float* b, in
     if (!x || !y || !a || !b || !g || !grad) return SK_ERR_NULL;
     int st = check_sizes(n, m, d);
     if (st) return st;
-    if (d > kValuMaxD) return SK_ERR_UNSUPPORTED_D;
     if ((st = check_eps(eps))) return st;
     const Layout L = make_layout(n, m, d);
     if ((st = check_ws(ws, ws_bytes, L))) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     Ws W{L, static_cast<char*>(ws)};
+    int cap = 0;
+    if (L.mfma && (cap = pass_capacity(d)) <= 0) return SK_ERR_HIP;
     if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 2, g, s))) return st;
 
     GradArgs ga{};
-    const Split sp = split_for(n, m, valu_rows_per_block());
+    const Split sp = grad_split(n, m, d);
     ga.q = W.f(L.xp);
     ga.k = W.f(L.yp);
     ga.kbias = L.mfma ? W.f(L.hy) : nullptr;
@@ -426,7 +432,16 @@ int sk_grad_x(const float* x, const float* y, const float* a, const float* b, in
     ga.partA = W.f(L.partA);
     ga.w = a;
     ga.grad = grad;
-    SK_TRY(launch_grad_valu(ga, s));
+    if (!L.mfma) {
+        SK_TRY(launch_grad_valu(ga, s));
+        return SK_OK;
+    }
+    // d > 8: first the row lse of the same scores, then the weighted key sums
+    PassArgs lse_pass = make_pass(W, true, eps, a, cap);
+    lse_pass.fin.mode = kFinStore;
+    if ((st = run_pass(W, lse_pass, s))) return st;
+    ga.lse = W.f(L.lse_r);
+    SK_TRY(launch_grad_mfma(ga, s));
     return SK_OK;
 }
 

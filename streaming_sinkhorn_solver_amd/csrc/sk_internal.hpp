@@ -57,6 +57,7 @@ enum FinMode : int {
     kFinSolve = 0,   // store lse, next-pass bias, output potential; optional fused residual
     kFinProbe = 1,   // residual of the previous state only (no state change)
     kFinResid = 2,   // residual against a caller-supplied potential
+    kFinStore = 3,   // store lse only
 };
 
 struct Fin {
@@ -115,6 +116,7 @@ struct GradArgs {
     float* partA;        // [nsplit][nq][P] partial weighted key sums
     const float* w;      // a
     float* grad;         // [nq][d] output
+    const float* lse;    // [nq] row log-sum-exp (matrix-core gradient, from a first pass)
 };
 
 // Workspace carve-up, a pure function of (n, m, d).
@@ -160,6 +162,9 @@ hipError_t launch_merge(const PassArgs& a, hipStream_t s);
 hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 int mfma_rows_per_block(int P);
 int mfma_pass_capacity(int P);
+// Matrix-core gradient pass (needs the row lse of the same scores); rows per workgroup.
+hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
+int mfma_grad_rows_per_block();
 // Workgroups of the d-dimensional pass kernel resident at once on the current
 // device (CUs x occupancy), 0 on failure.
 int valu_pass_capacity(int d);

@@ -28,6 +28,8 @@ __device__ __forceinline__ void finalize(const Fin& F, int i, float lse) {
         const float wi = F.w[i];
         const float r = wi > 0.0f ? wi * expm1f((lse - F.lse[i]) * kLn2) : 0.0f;
         F.rbuf[i] = fabsf(r);
+    } else if (F.mode == kFinStore) {
+        F.lse[i] = lse;
     } else {  // kFinResid: (P1)_i / a_i - 1 = exp((f_i - f~_i)/eps) - 1
         const float wi = F.w[i];
         const float e = (F.pot_in[i] - F.nrm[i]) * F.inv_eps + kLn2 * lse;

@@ -158,6 +158,147 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
     }
 }
 
+// Gradient for d > 8: T_i = sum_j w_ij y_j with w_ij = 2^{s_ij - lse_i}, the
+// row lse coming from a first streamed pass over the same scores (so every
+// w_ij <= 1 and no rescaling is needed).  Per 16-key block the scores are
+// recomputed on the matrix cores exactly as in the pass, and T accumulates
+// with a second MFMA: A = weights (16 queries x 4 keys per step; a lane's own
+// four weights, keys 4g + v, are exactly its A operand for steps v = 0..3),
+// B = the block's key coordinates (4 keys x 16 dims, read from the LDS tile).
+// The output tile of dims [16 nb, 16 nb + 16) leaves lane l holding
+// T[query 4(l/16) + v][dim 16 nb + l%16].  grad_i = 2 a_i (x~_i - T_i / S_i)
+// with S_i = sum_j w_ij (1 up to rounding).  One 16-query block per wave; the
+// key range is split across workgroups (blockIdx.y) and partial (S, T) are
+// plain sums.
+template <int P>
+__global__ __launch_bounds__(kBlock) void k_grad_mfma(GradArgs A) {
+    constexpr int KT = P / 4;
+    constexpr int PS = P + 4;
+    constexpr int NB = P / 16;  // 16-dim output blocks
+    constexpr int TL = mfma_tile_keys<P>();
+    __shared__ __align__(16) float ktile[TL * PS];
+    __shared__ __align__(16) float btile[TL];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const float4* kp = reinterpret_cast<const float4*>(A.k);
+    const int split = blockIdx.y;
+    const int c0 = split * A.cols_per_split;
+    const int c1 = min(c0 + A.cols_per_split, A.nk);
+    const int qrow0 = blockIdx.x * (kWaves * 16) + wave * 16;
+
+    float qf[KT];
+    {
+        const int i = qrow0 + c;
+        const int ic = i < A.nq ? i : A.nq - 1;
+        const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
+#pragma unroll
+        for (int t4 = 0; t4 < KT / 4; ++t4) {
+            const float4 v = qr[t4];
+            qf[4 * t4 + 0] = v.x * A.qscale;
+            qf[4 * t4 + 1] = v.y * A.qscale;
+            qf[4 * t4 + 2] = v.z * A.qscale;
+            qf[4 * t4 + 3] = v.w * A.qscale;
+        }
+    }
+    const float lse_c = A.lse[min(qrow0 + c, A.nq - 1)];
+    float S = 0.0f;
+    f4 T[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) T[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int base = c0; base < c1; base += TL) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < TL * (P / 4); e += kBlock) {
+            const int key = e / (P / 4), part = e - key * (P / 4);
+            const int col = base + key;
+            const float4 v = col < c1 ? kp[(size_t)col * (P / 4) + part] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            *reinterpret_cast<float4*>(&ktile[key * PS + part * 4]) = v;
+        }
+        for (int e = threadIdx.x; e < TL; e += kBlock) btile[e] = base + e < c1 ? A.kbias[base + e] : -INFINITY;
+        __syncthreads();
+        const int ntile = min(TL, c1 - base);
+        for (int kb = 0; kb < ntile; kb += 16) {
+            float kf[KT];
+            const float4* kr = reinterpret_cast<const float4*>(&ktile[(kb + c) * PS + g * KT]);
+#pragma unroll
+            for (int t4 = 0; t4 < KT / 4; ++t4) {
+                const float4 v = kr[t4];
+                kf[4 * t4 + 0] = v.x;
+                kf[4 * t4 + 1] = v.y;
+                kf[4 * t4 + 2] = v.z;
+                kf[4 * t4 + 3] = v.w;
+            }
+            f4 acc = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
+#pragma unroll
+            for (int t = 0; t < KT; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[t], acc, 0, 0, 0);
+            float wv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                wv[v] = ex2(acc[v] - lse_c);
+                S += wv[v];
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    T[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[v], ktile[(kb + 4 * g + v) * PS + nb * 16 + c],
+                                                                 T[nb], 0, 0, 0);
+        }
+    }
+    // S: lane (g, c) summed keys 4g.. of query c; join the four groups
+    S += __shfl_xor(S, 16);
+    S += __shfl_xor(S, 32);
+    if (A.nsplit == 1) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int qi = 4 * g + v;                 // query of T[nb][v] in this lane
+            const float Sq = __shfl(S, qi);           // lane qi holds query qi's S
+            const int i = qrow0 + qi;
+            if (i >= A.nq) continue;
+            const float two_w = 2.0f * A.w[i];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int dim = nb * 16 + c;
+                if (dim < A.d) A.grad[(size_t)i * A.d + dim] = two_w * (A.q[(size_t)i * P + dim] - T[nb][v] / Sq);
+            }
+        }
+    } else {
+        if (g == 0 && qrow0 + c < A.nq) A.part[(size_t)split * A.nq + qrow0 + c] = make_float2(0.0f, S);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = qrow0 + 4 * g + v;
+            if (i >= A.nq) continue;
+            float* pa = A.partA + ((size_t)split * A.nq + i) * P;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) pa[nb * 16 + c] = T[nb][v];
+        }
+    }
+}
+
+// Sums the split partials (S, T) of the matrix-core gradient in split order.
+__global__ __launch_bounds__(kBlock) void k_grad_mfma_merge(GradArgs A) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)A.nq * A.d) return;
+    const int i = (int)(t / A.d), dim = (int)(t - (int64_t)i * A.d);
+    float S = 0.0f, T = 0.0f;
+    for (int s = 0; s < A.nsplit; ++s) {
+        S += A.part[(size_t)s * A.nq + i].y;
+        T += A.partA[((size_t)s * A.nq + i) * A.P + dim];
+    }
+    A.grad[t] = 2.0f * A.w[i] * (A.q[(size_t)i * A.P + dim] - T / S);
+}
+
+template <int P>
+hipError_t launch_grad_mfma_p(const GradArgs& a, hipStream_t s) {
+    dim3 grid((a.nq + kWaves * 16 - 1) / (kWaves * 16), a.nsplit);
+    hipLaunchKernelGGL(k_grad_mfma<P>, grid, dim3(kBlock), 0, s, a);
+    if (a.nsplit > 1)
+        hipLaunchKernelGGL(k_grad_mfma_merge, dim3((unsigned)(((int64_t)a.nq * a.d + kBlock - 1) / kBlock)),
+                           dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int P>
 hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
@@ -195,6 +336,19 @@ hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hi
         case 64: return launch_mfma_p<64>(a, s, ev0, ev1);
         case 128: return launch_mfma_p<128>(a, s, ev0, ev1);
         case 256: return launch_mfma_p<256>(a, s, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+int mfma_grad_rows_per_block() { return kWaves * 16; }
+
+hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s) {
+    switch (a.P) {
+        case 16: return launch_grad_mfma_p<16>(a, s);
+        case 32: return launch_grad_mfma_p<32>(a, s);
+        case 64: return launch_grad_mfma_p<64>(a, s);
+        case 128: return launch_grad_mfma_p<128>(a, s);
+        case 256: return launch_grad_mfma_p<256>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

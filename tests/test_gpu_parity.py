@@ -132,13 +132,15 @@ def test_gradient_flow_workload_end_to_end():
 
 
 GRAD_SHAPES = [(1, 5, 2, 0.1, 21), (700, 1300, 3, 0.05, 22), (2100, 2600, 2, 0.02, 23),
-               (1500, 900, 5, 0.3, 24), (1200, 2000, 8, 0.5, 25)]
+               (1500, 900, 5, 0.3, 24), (1200, 2000, 8, 0.5, 25),
+               # matrix-core gradient (d > 8): lse pass + weighted key sums
+               (900, 1100, 12, 0.3, 26), (1700, 1300, 64, 0.3, 27), (300, 700, 130, 0.5, 28), (5, 3, 64, 0.2, 29)]
 
 
 @pytest.mark.parametrize("shape", GRAD_SHAPES, ids=[f"{s[0]}x{s[1]}d{s[2]}" for s in GRAD_SHAPES])
 def test_grad_matches_oracle(shape):
     n, m, d, eps, seed = shape
-    x, y, a, b = random_problem(n, m, d, seed, zero_frac=0.1)
+    x, y, a, b = random_problem(n, m, d, seed, scale=1.0 if d <= 8 else 1.0 / math.sqrt(d), zero_frac=0.1)
     eps = eps32(eps)
     rng = np.random.default_rng(seed)
     g = (0.3 * rng.standard_normal(m)).astype(np.float32)
