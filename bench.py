@@ -34,12 +34,12 @@ if ROOT not in sys.path:
 # MI355X unit counts and clock: 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz.
 CUS, SIMDS, LANES, CLOCK_HZ = 256, 4, 16, 2.4e9
 LANE_OPS_PER_S = CUS * SIMDS * LANES * CLOCK_HZ  # 3.93e13 single-lane VALU ops / s (no packed fp32)
-# v_exp_f32 throughput relative to the full VALU lane rate, measured on gfx950
-# with the issue-rate micro-benchmark (`python bench.py --ceilings`): exp2 alone
-# issues at half rate (1.94e13/s vs 3.61e13/s for fp32 FMA), and a mix of 7
-# VALU ops + 1 exp2 per pair sustains more instructions per second than a single
-# issue port allows, so the exp2 runs on its own pipe concurrently with the
-# other VALU work.
+# Issue model of the vector ALUs on gfx950, from hardware counters on the d = 3
+# pass (SQ_INSTS_VALU: 0.244 wave-instructions per SIMD-cycle of a 0.25 maximum)
+# and the issue-rate micro-benchmarks (`python bench.py --ceilings`): every VALU
+# instruction, v_exp_f32 included, takes one issue slot (a wave64 instruction
+# every 4 cycles on a 16-lane SIMD); the exp2 unit itself completes at half the
+# lane rate, which binds only above one exp2 per two VALU slots.
 EXP_RATE_FRACTION = 0.5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass_traffic.json")
 
@@ -48,15 +48,15 @@ def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
     """Vector-ALU roofline of one streamed pass.
 
     Algorithmic work per pair evaluation: d FMAs (2d flops), one max, one
-    subtract, one add and one exp2 = 2d + 4 fp32 operations.  Issue model:
-    the d + 3 non-transcendental ops take one full-rate VALU slot each, and the
-    exp2 runs concurrently on the transcendental pipe at EXP_RATE_FRACTION of
-    the lane rate, so the chip's ceiling is
-    min(LANE_OPS_PER_S / (d + 3), EXP_RATE_FRACTION * LANE_OPS_PER_S) pairs/s;
-    the peak in operation units is that times (2d + 4).
+    subtract, one add and one exp2 = 2d + 4 fp32 operations.  Fewest VALU issue
+    slots per pair: d FMAs (the bias rides in the first FMA's addend), 1/2 for
+    the running max (v_max3 takes two new scores per instruction), one
+    subtract, one exp2 and one add: d + 3.5.  The chip's ceiling is therefore
+    min(LANE_OPS_PER_S / (d + 3.5), EXP_RATE_FRACTION * LANE_OPS_PER_S) pairs/s,
+    and the peak in operation units is that times (2d + 4).
     """
     ops_per_pair = 2 * d + 4
-    ceiling_pairs = min(LANE_OPS_PER_S / (d + 3), EXP_RATE_FRACTION * LANE_OPS_PER_S)
+    ceiling_pairs = min(LANE_OPS_PER_S / (d + 3.5), EXP_RATE_FRACTION * LANE_OPS_PER_S)
     achieved = pairs_per_launch * ops_per_pair / avg_launch_s / 1e12
     peak = ceiling_pairs * ops_per_pair / 1e12
     return {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TFLOP/s",
@@ -109,7 +109,7 @@ def run_ceilings():
     out = torch.empty(blocks * 256, device="cuda:0")
     stream = torch.cuda.current_stream()
     res = {}
-    for kind, name in ((0, "fma"), (1, "exp2"), (2, "pair_mix_d3")):
+    for kind, name in ((0, "fma"), (1, "exp2"), (2, "pair_mix_d3"), (3, "mfma_f32_16x16x4"), (4, "mfma_f32_32x32x2")):
         for _ in range(2):
             lib.sku_launch(kind, blocks, 50, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -118,9 +118,13 @@ def run_ceilings():
         e1.record()
         torch.cuda.synchronize()
         assert rc == 0, rc
-        ops = blocks * 256 * iters * 64
-        rate = ops / (e0.elapsed_time(e1) * 1e-3)
-        res[name] = {"ops_per_s": rate, "frac_of_lane_rate": rate / LANE_OPS_PER_S}
+        secs = e0.elapsed_time(e1) * 1e-3
+        if kind <= 2:
+            rate = blocks * 256 * iters * 64 / secs
+            res[name] = {"ops_per_s": rate, "frac_of_lane_rate": rate / LANE_OPS_PER_S}
+        else:
+            flops = blocks * 4 * iters * 64 * (2048 if kind == 3 else 4096)
+            res[name] = {"tflops": flops / secs / 1e12, "frac_of_peak": flops / secs / 1e12 / MFMA_FP32_PEAK_TFLOPS}
     res["exp2_issue_cost"] = res["fma"]["ops_per_s"] / res["exp2"]["ops_per_s"]
     res["lane_ops_per_s_nominal"] = LANE_OPS_PER_S
     print(json.dumps(res))

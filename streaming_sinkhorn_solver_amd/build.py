@@ -21,8 +21,9 @@ UBENCH_PATH = os.path.join(BUILD_DIR, "libsk_ubench.so")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for the device code: the compiler
-# must emit scalar v_fma/v_add/v_mul_f32 only.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# must emit scalar v_fma/v_add/v_mul_f32 only.  Matrix-core accumulators are
+# kept in ordinary VGPRs (no AGPR copies before the LSE epilogue reads them).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -33,15 +33,72 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kBlock / 64;
 
+#ifndef SK_MFMA_NQB
+#define SK_MFMA_NQB 4
+#endif
+#ifndef SK_MFMA_TILE_FLOATS
+#define SK_MFMA_TILE_FLOATS 8192
+#endif
+
+// 16-query blocks per wave (register budget: NQB * P / 4 query VGPRs)
 template <int P>
 constexpr int mfma_nqb() {
-    return P <= 64 ? 4 : (P == 128 ? 2 : 1);
+    return P <= 64 ? SK_MFMA_NQB : (P == 128 ? 2 : 1);
 }
 
+// keys per LDS tile (about SK_MFMA_TILE_FLOATS floats of coordinates)
 template <int P>
 constexpr int mfma_tile_keys() {
-    return 8192 / P < 16 ? 16 : 8192 / P;
+    return SK_MFMA_TILE_FLOATS / P < 16 ? 16 : SK_MFMA_TILE_FLOATS / P;
 }
+
+// Register staging of one LDS tile of TL keys: each thread holds kStageF4
+// float4s of coordinates and up to kStageB biases.  Loads are unconditional
+// (clamped to the last valid key) and issued back to back, so a tile costs one
+// memory latency, and the loads for the next tile are issued before the
+// current tile is computed.
+template <int P>
+struct TileStage {
+    static constexpr int TL = mfma_tile_keys<P>();
+    static constexpr int F4 = TL * (P / 4) / kBlock;
+    static constexpr int NB = (TL + kBlock - 1) / kBlock;
+    static_assert(TL * (P / 4) % kBlock == 0, "tile must split evenly over the workgroup");
+    float4 v[F4];
+    float b[NB];
+
+    __device__ __forceinline__ void load(const float4* __restrict__ kp, const float* __restrict__ kbias, int base,
+                                         int j1) {
+#pragma unroll
+        for (int r = 0; r < F4; ++r) {
+            const int e = threadIdx.x + r * kBlock;
+            const int key = e / (P / 4), part = e - key * (P / 4);
+            const int col = base + key;
+            const float4 x = kp[(size_t)min(col, j1 - 1) * (P / 4) + part];
+            v[r] = col < j1 ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            const int col = base + threadIdx.x + r * kBlock;
+            const float x = kbias[min(col, j1 - 1)];
+            b[r] = col < j1 ? x : -INFINITY;
+        }
+    }
+
+    __device__ __forceinline__ void store(float* ktile, float* btile) const {
+        constexpr int PS = P + 4;
+#pragma unroll
+        for (int r = 0; r < F4; ++r) {
+            const int e = threadIdx.x + r * kBlock;
+            const int key = e / (P / 4), part = e - key * (P / 4);
+            *reinterpret_cast<float4*>(&ktile[key * PS + part * 4]) = v[r];
+        }
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            const int k = threadIdx.x + r * kBlock;
+            if (k < TL) btile[k] = b[r];
+        }
+    }
+};
 
 __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
     const float mn = fmaxf(M, m2);
@@ -89,16 +146,13 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
             S[qb] = 0.0f;
         }
 
+        TileStage<P> stage;
+        stage.load(kp, A.kbias, j0, j1);
         for (int base = j0; base < j1; base += TL) {
             __syncthreads();
-            for (int e = threadIdx.x; e < TL * (P / 4); e += kBlock) {
-                const int key = e / (P / 4), part = e - key * (P / 4);
-                const int col = base + key;
-                const float4 v = col < j1 ? kp[(size_t)col * (P / 4) + part] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                *reinterpret_cast<float4*>(&ktile[key * PS + part * 4]) = v;
-            }
-            for (int e = threadIdx.x; e < TL; e += kBlock) btile[e] = base + e < j1 ? A.kbias[base + e] : -INFINITY;
+            stage.store(ktile, btile);
             __syncthreads();
+            if (base + TL < j1) stage.load(kp, A.kbias, base + TL, j1);
             const int ntile = min(TL, j1 - base);
             for (int kb = 0; kb < ntile; kb += 16) {
                 float kf[KT];
@@ -207,16 +261,13 @@ __global__ __launch_bounds__(kBlock) void k_grad_mfma(GradArgs A) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) T[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    TileStage<P> stage;
+    if (c0 < c1) stage.load(kp, A.kbias, c0, c1);
     for (int base = c0; base < c1; base += TL) {
         __syncthreads();
-        for (int e = threadIdx.x; e < TL * (P / 4); e += kBlock) {
-            const int key = e / (P / 4), part = e - key * (P / 4);
-            const int col = base + key;
-            const float4 v = col < c1 ? kp[(size_t)col * (P / 4) + part] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            *reinterpret_cast<float4*>(&ktile[key * PS + part * 4]) = v;
-        }
-        for (int e = threadIdx.x; e < TL; e += kBlock) btile[e] = base + e < c1 ? A.kbias[base + e] : -INFINITY;
+        stage.store(ktile, btile);
         __syncthreads();
+        if (base + TL < c1) stage.load(kp, A.kbias, base + TL, c1);
         const int ntile = min(TL, c1 - base);
         for (int kb = 0; kb < ntile; kb += 16) {
             float kf[KT];

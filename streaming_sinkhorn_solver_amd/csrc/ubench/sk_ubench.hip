@@ -75,13 +75,56 @@ __global__ __launch_bounds__(256) void k_mix(float* out, int iters, float k0, fl
     out[blockIdx.x * blockDim.x + threadIdx.x] = r;
 }
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// fp32 matrix-core rate: kChains independent v_mfma_f32_16x16x4f32 chains per wave.
+__global__ __launch_bounds__(256) void k_mfma16(float* out, int iters) {
+    const float a = threadIdx.x * 1e-3f, b = 1.0f - threadIdx.x * 1e-4f;
+    f4 acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = f4{0.0f, 0.0f, 0.0f, (float)c};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][3];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// fp32 matrix-core rate with the 32x32x2 shape (4 independent chains, 16 accumulators each).
+__global__ __launch_bounds__(256) void k_mfma32(float* out, int iters) {
+    const float a = threadIdx.x * 1e-3f, b = 1.0f - threadIdx.x * 1e-4f;
+    f16v acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[c][e] = (float)(c + e);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s += acc[c][0] + acc[c][15];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
 
-// kind 0: fp32 FMA, 1: exp2, 2: d = 3 pair mix.  Launches `blocks` x 256
-// threads; each thread performs iters * 8 * 8 operations (FMAs, exp2s or
-// pairs).  out must hold blocks * 256 floats.  Returns a hipError_t.
+// kind 0: fp32 FMA, 1: exp2, 2: d = 3 pair mix; each thread performs
+// iters * 8 * 8 operations (FMAs, exp2s or pairs).  kind 3: each wave issues
+// iters * 64 v_mfma_f32_16x16x4f32 (2048 flops each); kind 4: each wave issues
+// iters * 64 v_mfma_f32_32x32x2f32 (4096 flops each).  Launches `blocks` x 256
+// threads; out must hold blocks * 256 floats.  Returns a hipError_t.
 int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (kind == 0)
@@ -90,6 +133,10 @@ int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
         hipLaunchKernelGGL(k_exp, dim3(blocks), dim3(256), 0, s, out, iters);
     else if (kind == 2)
         hipLaunchKernelGGL(k_mix, dim3(blocks), dim3(256), 0, s, out, iters, 0.3f, 0.2f, 0.1f, 0.05f);
+    else if (kind == 3)
+        hipLaunchKernelGGL(k_mfma16, dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 4)
+        hipLaunchKernelGGL(k_mfma32, dim3(blocks), dim3(256), 0, s, out, iters);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
