@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--iters", type=int, default=None, help="override the workload's iteration count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceilings", action="store_true", help="run the issue-rate micro-benchmarks and exit")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph and time its replays (kernel timing from an eager step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device (a known-size reference for HBM byte counters)")
     args = ap.parse_args()
@@ -192,19 +194,34 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    sk.timing_enable(True)
+    graph = None
+    if args.graph:
+        # pass-kernel durations from one eager step; the timed steps replay the graph
+        sk.timing_enable(True)
+        step()
+        torch.cuda.synchronize()
+        pass_ms, launches, pairs = sk.timing_read()
+        sk.timing_enable(False)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+    else:
+        sk.timing_enable(True)
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        step()
+        graph.replay() if graph is not None else step()
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    pass_ms, launches, pairs = sk.timing_read()
-    sk.timing_enable(False)
+    if graph is None:
+        pass_ms, launches, pairs = sk.timing_read()
+        sk.timing_enable(False)
 
     wall_s = t1 - t0
     gpu_s = ev0.elapsed_time(ev1) * 1e-3
@@ -237,6 +254,7 @@ def main():
         "config": {"workload": args.workload, "n": n, "m": m, "d": d, "eps": eps, "n_iters": n_iters,
                    "check_every": ce, "grad_x": bool(w.grad), "recipe": w.description},
         "iters_per_s": n_iters / step_s,
+        "hip_graph": bool(args.graph),
         "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s,
         "roofline": roof,
         "final_residual": float(trace[n_iters // ce - 1].item()) if ce else None,

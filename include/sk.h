@@ -18,7 +18,10 @@
  *    by later calls once the calls that used it have completed in stream order.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Compute entry
  *    points only enqueue work and return; results are ready when the stream
- *    reaches that point.  Only sk_check_inputs synchronises the stream.
+ *    reaches that point.  Only sk_check_inputs synchronises the stream.  The
+ *    compute entry points allocate nothing, synchronise nothing and use no
+ *    memset, so they may be captured into a HIP graph and replayed (inputs,
+ *    outputs and workspace at the captured addresses).
  *  - Weights are used exactly as given (not normalised); zeros are legal and
  *    such points contribute nothing.  Data-dependent validity (negative or
  *    non-finite values, unequal masses) is checked by sk_check_inputs, not by
@@ -153,7 +156,8 @@ int sk_grad_x(const float *x, const float *y, const float *a, const float *b,
  * kernels are outside the pair); sk_timing_enable(0) stops recording.
  * sk_timing_read waits for the recorded events and returns the total kernel
  * milliseconds, the number of launches and the number of (query, key) pairs
- * those launches evaluated.  Events come from a process-wide pool that grows
+ * those launches evaluated.  Launches enqueued while the stream is being
+ * captured into a graph are not timed.  Events come from a process-wide pool that grows
  * on demand; calls from several threads at once are serialised.  Returns
  * SK_ERR_NULL for NULL outputs, SK_ERR_HIP on a HIP failure.
  */

@@ -18,6 +18,12 @@ namespace sk {
 namespace {
 
 constexpr int kAbiVersion = 1;
+#ifndef SK_SMALL_PAIRS
+#define SK_SMALL_PAIRS 2.0e6
+#endif
+// Passes with at most this many (query, key) pairs use the single-kernel
+// small-problem path (d <= 8).
+constexpr double kSmallPairs = SK_SMALL_PAIRS;
 constexpr int64_t kTargetGroups = 2048;  // workgroups per pass: 8 per CU on 256 CUs
 constexpr int64_t kMinColsPerSplit = 512;
 
@@ -135,6 +141,7 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
     p.P = L.P;
     p.qscale = 2.0f * kLog2e / eps;
     p.part = reinterpret_cast<float2*>(W.base + L.part);
+    p.small = (!L.mfma && (double)nq * (double)nk <= kSmallPairs) ? 1 : 0;
     Fin& F = p.fin;
     F.mode = kFinSolve;
     F.P = L.P;
@@ -170,9 +177,11 @@ int run_pass(const Ws& W, const PassArgs& p, hipStream_t s) {
     (void)W;
     Timing& T = timing();
     hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return SK_ERR_HIP;
     {
         std::lock_guard<std::mutex> lk(T.mu);
-        if (T.on) {
+        if (T.on && cap == hipStreamCaptureStatusNone) {  // no event nodes inside a captured graph
             while (T.pool.size() < 2 * (T.used + 1)) {
                 hipEvent_t e;
                 SK_TRY(hipEventCreate(&e));

@@ -100,6 +100,7 @@ struct PassArgs {
     int W;               // workgroups
     int64_t total;       // n_row_blocks * nk
     float2* part;        // [W][2][rpb] partial (M, S)
+    int small;           // d <= 8 and small: one workgroup per few rows, whole key range, no merge
     Fin fin;
 };
 

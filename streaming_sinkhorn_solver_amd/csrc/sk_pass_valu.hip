@@ -156,6 +156,90 @@ __global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
     }
 }
 
+// Small problems (at most 2e6 pairs per pass, e.g. 1000 x 1000): one pass
+// kernel per half-step, no partials and no merge launch, which is what bounds
+// such passes (measured 7.1 us vs 7.8 us + the merge at 1000 x 1000; at
+// 10,000 x 10,000 the stream-K pass is faster, 27 us vs 44 us).
+// kSmallG consecutive lanes share a query row; lane `sub` of the group takes
+// keys sub, sub + G, sub + 2G, ... of each LDS tile (the lanes of a wave read
+// G consecutive keys per step, conflict-free), keeps its own running (M, S),
+// and the group joins them with a fixed xor-shuffle tree.
+#ifndef SK_SMALL_G
+#define SK_SMALL_G 64
+#endif
+constexpr int kSmallG = SK_SMALL_G;
+constexpr int kSmallRows = kBlock / kSmallG;   // query rows per workgroup
+constexpr int kSmallTJ = 8;                    // keys per lane per chunk
+constexpr int kSmallTile = 1024;               // keys per LDS tile (multiple of G * TJ)
+static_assert(kSmallTile % (kSmallG * kSmallTJ) == 0, "tile must hold whole chunks");
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_pass_small(PassArgs A) {
+    constexpr int P = ((D + 1 + 3) / 4) * 4;
+    constexpr int V = P / 4;
+    __shared__ float4 tile[kSmallTile * V];
+    const float4* kp = reinterpret_cast<const float4*>(A.k);
+    const int sub = threadIdx.x % kSmallG;
+    const int i = blockIdx.x * kSmallRows + threadIdx.x / kSmallG;
+    const int ic = i < A.nq ? i : A.nq - 1;
+    float q[D];
+#pragma unroll
+    for (int t = 0; t < D; ++t) q[t] = A.q[(size_t)ic * P + t] * A.qscale;
+    float M = kNegBig, S = 0.0f;
+
+    for (int base = 0; base < A.nk; base += kSmallTile) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < kSmallTile * V; e += kBlock) {
+            const int col = base + e / V, part = e % V;
+            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (col < A.nk) {
+                v = kp[(size_t)col * V + part];
+            } else if (part == D / 4) {
+                reinterpret_cast<float*>(&v)[D % 4] = -INFINITY;
+            }
+            tile[e] = v;
+        }
+        __syncthreads();
+        const int ntile = min(kSmallTile, A.nk - base);
+        for (int t0 = 0; t0 < kSmallTile / kSmallG && kSmallG * t0 < ntile; t0 += kSmallTJ) {
+            float s[kSmallTJ];
+#pragma unroll
+            for (int tt = 0; tt < kSmallTJ; ++tt) {
+                float kk[P];
+#pragma unroll
+                for (int u = 0; u < V; ++u) {
+                    const float4 v = tile[(sub + kSmallG * (t0 + tt)) * V + u];
+                    kk[4 * u + 0] = v.x;
+                    kk[4 * u + 1] = v.y;
+                    kk[4 * u + 2] = v.z;
+                    kk[4 * u + 3] = v.w;
+                }
+                float acc = kk[D];
+#pragma unroll
+                for (int dd = 0; dd < D; ++dd) acc = fmaf(q[dd], kk[dd], acc);
+                s[tt] = acc;
+            }
+            float mt = s[0];
+#pragma unroll
+            for (int tt = 1; tt < kSmallTJ; ++tt) mt = fmaxf(mt, s[tt]);
+            const float mn = fmaxf(M, mt);
+            float acc = S * ex2(M - mn);
+#pragma unroll
+            for (int tt = 0; tt < kSmallTJ; ++tt) acc += ex2(s[tt] - mn);
+            S = acc;
+            M = mn;
+        }
+    }
+#pragma unroll
+    for (int off = kSmallG / 2; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(M, off), s2 = __shfl_xor(S, off);
+        const float mn = fmaxf(M, m2);
+        S = S * ex2(M - mn) + s2 * ex2(m2 - mn);
+        M = mn;
+    }
+    if (sub == 0 && i < A.nq) finalize(A.fin, i, M + lg2(S));
+}
+
 // Combines, for every row of a row block split across workgroups, the partial
 // (M, S) pairs: M = max M_w, S = sum S_w 2^{M_w - M}.  kMergeLanes lanes share
 // a row, each taking every kMergeLanes-th contributing workgroup, then a fixed
@@ -312,6 +396,11 @@ __global__ __launch_bounds__(kBlock) void k_grad_merge(GradArgs A) {
 template <int D>
 hipError_t launch_pass_d(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
+    if (a.small) {
+        hipLaunchKernelGGL(k_pass_small<D>, dim3((a.nq + kSmallRows - 1) / kSmallRows), dim3(kBlock), 0, s, a);
+        if (ev1) (void)hipEventRecord(ev1, s);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_pass_valu<D>, dim3(a.W), dim3(kBlock), 0, s, a);
     if (ev1) (void)hipEventRecord(ev1, s);
     return launch_merge(a, s);
