@@ -77,21 +77,33 @@ def roofline_mfma(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
             "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
 
 
-def load_traffic(kernel_key: str):
+# Sources that determine each timed kernel's code (plus the device flags).
+KERNEL_SOURCES = {
+    "valu": ["sk_pass_valu.hip", "sk_pass_common.hpp", "sk_internal.hpp"],
+    "mfma": ["sk_pass_mfma.hip", "sk_pass_common.hpp", "sk_internal.hpp"],
+}
+
+
+def kernel_source_hash(family: str) -> str:
+    import hashlib
+
+    from streaming_sinkhorn_solver_amd import build as skbuild
+
+    h = hashlib.sha256(" ".join(skbuild.DEVICE_FLAGS).encode())
+    for name in KERNEL_SOURCES[family]:
+        h.update(open(os.path.join(skbuild.CSRC, name), "rb").read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel_key: str, family: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current kernel source (else None)."""
+    were taken on the current source of that kernel (else None)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    from streaming_sinkhorn_solver_amd import build as skbuild
-    import hashlib
-
-    h = hashlib.sha256()
-    for src in skbuild.sources():
-        h.update(open(src, "rb").read())
     entry = rec.get(kernel_key)
-    if not entry or entry.get("source_sha256") != h.hexdigest():
+    if not entry or entry.get("source_sha256") != kernel_source_hash(family):
         return None
     return entry.get("bytes_per_launch")
 
@@ -236,7 +248,7 @@ def main():
     else:
         roof = roofline_mfma(d, pairs_per_launch, avg_launch_s)
         roof["kernel"] = "k_pass_mfma<%d>" % max(16, 1 << (d - 1).bit_length())
-    roof["traffic"] = load_traffic(f"{args.workload}:pass")
+    roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma")
 
     out = {
         "metric": "point-pair evals/sec and Sinkhorn iters/sec (n=m=50k,d=3); % fp32 peak",
