@@ -15,8 +15,10 @@ Passages followed (page title and section):
     (the log-domain update and its transpose), Methodology 2 (exact running
     max/sum-exp LSE), Methodology 3 (gradient as a barycentric projection).
   * SinkSLOT README, Tensor Contract (cost |x-y|^2, weights as given, zeros
-    legal) and API Reference (alternating variant, fixed stop mode, the
-    infinity-norm marginal residual).
+    legal) and API Reference (alternating and symmetric variants, the fixed,
+    marginal and potential stop modes, the infinity-norm marginal residual),
+    Low-Level Solver API (iters_run, converged, final_viol), and the opening
+    section (entropic OT is not zero at (x, x): the debiased divergence).
 Pins: every function here is checked in tests/test_oracle_pins.py against
 closed forms, a textbook matrix-scaling route, library routines and brute
 force; none is pinned only against itself.
@@ -73,6 +75,11 @@ def load(path: str | None = None):
         lib.oracle_residual.restype = None
         lib.oracle_sinkhorn.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, i32, i32, _dp, _dp, _dp, _dp]
         lib.oracle_sinkhorn.restype = None
+        lib.oracle_sinkhorn_ex.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, i32, dbl, i32, dbl, i32, i32, _dp,
+                                           _dp, ctypes.POINTER(i32), ctypes.POINTER(i32), _dp]
+        lib.oracle_sinkhorn_ex.restype = None
+        lib.oracle_divergence.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, i32, dbl, i32, _dp]
+        lib.oracle_divergence.restype = None
         lib.oracle_grad_x.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, _dp, _i64p, i64, _dp]
         lib.oracle_grad_x.restype = None
         lib.oracle_dual_cost.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, _dp, _dp]
@@ -145,6 +152,37 @@ def sinkhorn(x, y, a, b, eps: float, n_iters: int, check_every: int = 0, g_init=
     lib.oracle_sinkhorn(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), int(check_every),
                         None if gi is None else _ptr(gi), _ptr(f), _ptr(g), _ptr(trace))
     return f, g, trace[:nt]
+
+
+VARIANTS = {"alternating": 0, "symmetric": 1}
+STOP_MODES = {"fixed": 0, "marginal": 1, "potential": 2}
+
+
+def sinkhorn_ex(x, y, a, b, eps: float, *, variant: str = "alternating", alpha: float = 0.5,
+                stop_mode: str = "fixed", stop_tol: float = 1e-6, max_iter: int = 200, check_every: int = 5, lib=None):
+    """Sinkhorn with update variant and stop rule.  Returns (f, g, iters_run, converged, final_viol);
+    converged is None and final_viol NaN under stop_mode="fixed"."""
+    lib = lib or load()
+    x, y, a, b = _cloud(x), _cloud(y), _f64(a), _f64(b)
+    n, d = x.shape
+    m = y.shape[0]
+    f, g = np.empty(n), np.empty(m)
+    it, conv, viol = ctypes.c_int(), ctypes.c_int(), ctypes.c_double()
+    lib.oracle_sinkhorn_ex(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), VARIANTS[variant], float(alpha),
+                           STOP_MODES[stop_mode], float(stop_tol), int(max_iter), int(check_every), _ptr(f), _ptr(g),
+                           ctypes.byref(it), ctypes.byref(conv), ctypes.byref(viol))
+    return f, g, it.value, (None if conv.value < 0 else bool(conv.value)), viol.value
+
+
+def divergence(x, y, a, b, eps: float, n_iters: int, variant: str = "alternating", alpha: float = 0.5, lib=None):
+    """Debiased entropic divergence OT(x,y) - OT(x,x)/2 - OT(y,y)/2, each term the dual objective after
+    n_iters iterations of the given variant (fixed stop).  Returns (S, (OT_xy, OT_xx, OT_yy))."""
+    lib = lib or load()
+    x, y, a, b = _cloud(x), _cloud(y), _f64(a), _f64(b)
+    out = np.empty(4)
+    lib.oracle_divergence(_ptr(x), _ptr(y), _ptr(a), _ptr(b), x.shape[0], y.shape[0], x.shape[1], float(eps),
+                          VARIANTS[variant], float(alpha), int(n_iters), _ptr(out))
+    return float(out[0]), tuple(float(v) for v in out[1:])
 
 
 def marginals(x, y, a, b, f, g, eps: float, lib=None):

@@ -31,7 +31,12 @@
  *  - SinkSLOT README, API Reference: variant "alternating" (Gauss-Seidel:
  *    each half-step uses the other potential's newest value), stop_mode
  *    "fixed" (exactly n_iters), and the "marginal" residual: the infinity
- *    norm of (P1 - a, P^T 1 - b).
+ *    norm of (P1 - a, P^T 1 - b).  The same section's "symmetric" (Jacobi)
+ *    variant with blend alpha, the "marginal" and "potential" stop modes with
+ *    their iteration cap, tolerance and check interval; Low-Level Solver API
+ *    for iters_run, converged and final_viol.
+ *  - SinkSLOT README, opening section: entropic OT is not zero at (x, x), so
+ *    a divergence built from it subtracts the two self-terms.
  * Readings where the pages are silent: g starts at 0 and each iteration is an
  * f half-step followed by a g half-step; the cost is the entropic dual
  * objective D(f,g) = <a,f> + <b,g> - eps * sum_ij a_i b_j (e^{(f_i+g_j-C_ij)/eps} - 1).
@@ -205,6 +210,91 @@ void oracle_sinkhorn(const double *x, const double *y, const double *a, const do
 }
 
 /*
+ * Sinkhorn with a choice of update variant and stop rule (SinkSLOT README, API
+ * Reference: variant "alternating" | "symmetric" with blend alpha; stop_mode
+ * "fixed" | "marginal" | "potential" with stop_max_iter, stop_tol and
+ * stop_check_every; Low-Level Solver API: iters_run, converged, final_viol).
+ *   variant 0 (alternating, Gauss-Seidel): f <- T_row(g), then g <- T_col(new f).
+ *   variant 1 (symmetric, Jacobi): from the old (f, g) compute T_row(g) and
+ *     T_col(f), then f <- (1 - alpha) f + alpha T_row(g), g likewise.
+ *   Both potentials start at 0.
+ *   stop_mode 0: exactly max_iter iterations, *converged = -1, *final_viol = NaN.
+ *   stop_mode 1: check after every check_every-th iteration and after the last
+ *     one; the check value is max(|P1 - a|_inf, |P^T 1 - b|_inf) at (f, g);
+ *     stop at the first check with value <= tol.
+ *   stop_mode 2: same checks; the value is max(max_i |f_i - f'_i|, max_j
+ *     |g_j - g'_j|) with (f', g') the potentials at the previous check (0 before
+ *     the first), i.e. eps times the change of the absorbed potentials f/eps;
+ *     stop at the first check with value < tol.
+ * *iters_run is the number of iterations performed; *final_viol the value of
+ * the last check.
+ */
+double oracle_dual_cost(const double *x, const double *y, const double *a, const double *b,
+                        int64_t n, int64_t m, int d, double eps, const double *f, const double *g);
+
+void oracle_sinkhorn_ex(const double *x, const double *y, const double *a, const double *b,
+                        int64_t n, int64_t m, int d, double eps, int variant, double alpha,
+                        int stop_mode, double tol, int max_iter, int check_every,
+                        double *f, double *g, int *iters_run, int *converged, double *final_viol)
+{
+    double *fn = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double *gn = (double *)malloc((size_t)(m > 0 ? m : 1) * sizeof(double));
+    double *fp = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+    double *gp = (double *)calloc((size_t)(m > 0 ? m : 1), sizeof(double));
+    for (int64_t i = 0; i < n; ++i)
+        f[i] = 0.0;
+    for (int64_t j = 0; j < m; ++j)
+        g[j] = 0.0;
+    *converged = stop_mode == 0 ? -1 : 0;
+    *final_viol = NAN;
+    int k = 0;
+    while (k < max_iter) {
+        ++k;
+        if (variant == 0) {
+            oracle_half_step(x, n, y, m, d, b, g, eps, NULL, n, f);
+            oracle_half_step(y, m, x, n, d, a, f, eps, NULL, m, g);
+        } else {
+            oracle_half_step(x, n, y, m, d, b, g, eps, NULL, n, fn);
+            oracle_half_step(y, m, x, n, d, a, f, eps, NULL, m, gn);
+            for (int64_t i = 0; i < n; ++i)
+                f[i] = (1.0 - alpha) * f[i] + alpha * fn[i];
+            for (int64_t j = 0; j < m; ++j)
+                g[j] = (1.0 - alpha) * g[j] + alpha * gn[j];
+        }
+        if (stop_mode == 0 || (k % check_every != 0 && k != max_iter))
+            continue;
+        double viol;
+        if (stop_mode == 1) {
+            double r[4];
+            oracle_residual(x, y, a, b, n, m, d, eps, f, g, r);
+            viol = r[0] > r[1] ? r[0] : r[1];
+        } else {
+            viol = 0.0;
+            for (int64_t i = 0; i < n; ++i) {
+                double e = fabs(f[i] - fp[i]);
+                viol = e > viol ? e : viol;
+                fp[i] = f[i];
+            }
+            for (int64_t j = 0; j < m; ++j) {
+                double e = fabs(g[j] - gp[j]);
+                viol = e > viol ? e : viol;
+                gp[j] = g[j];
+            }
+        }
+        *final_viol = viol;
+        if ((stop_mode == 1 && viol <= tol) || (stop_mode == 2 && viol < tol)) {
+            *converged = 1;
+            break;
+        }
+    }
+    *iters_run = k;
+    free(fn);
+    free(gn);
+    free(fp);
+    free(gp);
+}
+
+/*
  * Barycentric gradient with respect to x at fixed g:
  *   grad_i = 2 a_i (x_i - sum_j w_ij y_j),
  *   w_ij = exp(z_ij) / sum_j exp(z_ij),  z_ij = (g_j - C_ij)/eps + log b_j.
@@ -272,6 +362,37 @@ double oracle_dual_cost(const double *x, const double *y, const double *a, const
     free(rs);
     free(cs);
     return af + bg - eps * (mass_p - sa * sb);
+}
+
+/*
+ * Debiased entropic divergence S = OT(x,y) - OT(x,x)/2 - OT(y,y)/2, each term
+ * the dual objective after n_iters iterations of the chosen variant (fixed
+ * stop).  out[0] = S, out[1..3] = OT(x,y), OT(x,x), OT(y,y).  Reading: the
+ * SinkSLOT README (opening section) contrasts its own objective, which is zero
+ * at (x, x), with entropic OT, whose value at (x, x) is not zero and must be
+ * subtracted; the three terms use the same solver and settings.
+ */
+void oracle_divergence(const double *x, const double *y, const double *a, const double *b,
+                       int64_t n, int64_t m, int d, double eps, int variant, double alpha, int n_iters,
+                       double *out)
+{
+    int64_t mx = n > m ? n : m;
+    double *f = (double *)malloc((size_t)mx * sizeof(double));
+    double *g = (double *)malloc((size_t)mx * sizeof(double));
+    int it, conv;
+    double viol;
+    oracle_sinkhorn_ex(x, y, a, b, n, m, d, eps, variant, alpha, 0, 0.0, n_iters, 1, f, g, &it, &conv, &viol);
+    double t_xy = oracle_dual_cost(x, y, a, b, n, m, d, eps, f, g);
+    oracle_sinkhorn_ex(x, x, a, a, n, n, d, eps, variant, alpha, 0, 0.0, n_iters, 1, f, g, &it, &conv, &viol);
+    double t_xx = oracle_dual_cost(x, x, a, a, n, n, d, eps, f, g);
+    oracle_sinkhorn_ex(y, y, b, b, m, m, d, eps, variant, alpha, 0, 0.0, n_iters, 1, f, g, &it, &conv, &viol);
+    double t_yy = oracle_dual_cost(y, y, b, b, m, m, d, eps, f, g);
+    out[0] = t_xy - 0.5 * t_xx - 0.5 * t_yy;
+    out[1] = t_xy;
+    out[2] = t_xx;
+    out[3] = t_yy;
+    free(f);
+    free(g);
 }
 
 /* max_ij C_ij over all pairs (the scale of the parity tolerance). */

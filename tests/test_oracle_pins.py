@@ -292,6 +292,155 @@ def pin_residual_trace(lib):
     assert np.array_equal(f, oracle.sinkhorn(x, y, a, b, eps, 9, lib=lib)[0])
 
 
+# ---- update variants, stop rules and the debiased divergence (SinkSLOT README, API Reference,
+# Low-Level Solver API, opening section)
+def _plan(x, y, a, b, f, g, eps):
+    C = cdist(x, y, "sqeuclidean")
+    return a[:, None] * b[None, :] * np.exp((f[:, None] + g[None, :] - C) / eps)
+
+
+def pin_jacobi_first_steps(lib):
+    """Symmetric variant from zero potentials: one step gives alpha * T(0) on each side; the second
+    blends the first with the c-transforms of the OTHER side's first-step potential (both from old
+    values).  T is the c-transform written with scipy's logsumexp."""
+    x, y, a, b = _problem(9, 7, 2, 171)
+    eps, alpha = 0.3, 0.3
+    C = cdist(x, y, "sqeuclidean")
+    T_row = lambda g: -eps * logsumexp((g[None, :] - C) / eps, b=b[None, :], axis=1)
+    T_col = lambda f: -eps * logsumexp((f[:, None] - C) / eps, b=a[:, None], axis=0)
+    f1, g1, it, conv, viol = oracle.sinkhorn_ex(x, y, a, b, eps, variant="symmetric", alpha=alpha, max_iter=1, lib=lib)
+    assert it == 1 and conv is None and math.isnan(viol)
+    assert np.allclose(f1, alpha * T_row(np.zeros(7)), rtol=0, atol=1e-12)
+    assert np.allclose(g1, alpha * T_col(np.zeros(9)), rtol=0, atol=1e-12)
+    f2, g2, *_ = oracle.sinkhorn_ex(x, y, a, b, eps, variant="symmetric", alpha=alpha, max_iter=2, lib=lib)
+    assert np.allclose(f2, (1 - alpha) * f1 + alpha * T_row(g1), rtol=0, atol=1e-12)
+    assert np.allclose(g2, (1 - alpha) * g1 + alpha * T_col(f1), rtol=0, atol=1e-12)
+
+
+def pin_jacobi_alpha1_interleaves(lib):
+    """With alpha = 1 the Jacobi sequence holds the alternating one at every other step:
+    Jacobi f after 2k-1 steps is alternating f after k, Jacobi g after 2k is alternating g after k."""
+    x, y, a, b = _problem(8, 6, 3, 181)
+    eps = 0.4
+    for k in (1, 2, 5):
+        fa, ga, _ = oracle.sinkhorn(x, y, a, b, eps, k, lib=lib)
+        fj, _, *_ = oracle.sinkhorn_ex(x, y, a, b, eps, variant="symmetric", alpha=1.0, max_iter=2 * k - 1, lib=lib)
+        _, gj, *_ = oracle.sinkhorn_ex(x, y, a, b, eps, variant="symmetric", alpha=1.0, max_iter=2 * k, lib=lib)
+        assert np.allclose(fj, fa, rtol=0, atol=1e-12), k
+        assert np.allclose(gj, ga, rtol=0, atol=1e-12), k
+
+
+def pin_jacobi_fixed_point(lib):
+    """Blended Jacobi converges to the matrix-scaling plan (the fixed point does not depend on alpha)."""
+    x, y, a, b = _problem(7, 9, 2, 191)
+    eps = 0.5
+    _, _, P = _scaling_form(x, y, a, b, eps, 4000)
+    for alpha in (0.5, 0.3, 0.8):
+        f, g, it, conv, viol = oracle.sinkhorn_ex(x, y, a, b, eps, variant="symmetric", alpha=alpha,
+                                                  stop_mode="marginal", stop_tol=1e-13, max_iter=20000,
+                                                  check_every=10, lib=lib)
+        assert conv and viol <= 1e-13
+        assert np.max(np.abs(_plan(x, y, a, b, f, g, eps) - P)) <= 1e-12, alpha
+
+
+def pin_jacobi_symmetric_problem(lib):
+    """On (x, x, a, a) both Jacobi updates are the same computation, so f equals g exactly."""
+    x, _, a, _ = _problem(11, 11, 2, 201)
+    for k in (1, 4, 17):
+        f, g, *_ = oracle.sinkhorn_ex(x, x, a, a, 0.2, variant="symmetric", alpha=0.5, max_iter=k, lib=lib)
+        assert np.array_equal(f, g)
+
+
+def pin_stop_fixed(lib):
+    """Fixed stop: exactly max_iter alternating iterations, no check values."""
+    x, y, a, b = _problem(8, 7, 2, 211)
+    f, g, it, conv, viol = oracle.sinkhorn_ex(x, y, a, b, 0.2, max_iter=13, lib=lib)
+    f0, g0, _ = oracle.sinkhorn(x, y, a, b, 0.2, 13, lib=lib)
+    assert it == 13 and conv is None and math.isnan(viol)
+    assert np.array_equal(f, f0) and np.array_equal(g, g0)
+
+
+def pin_stop_marginal(lib):
+    """Marginal stop: the first check (every c-th iteration, and the last) whose residual is <= tol,
+    judged against the residual trace of the fixed-count run (pinned above)."""
+    x, y, a, b = _problem(9, 8, 2, 221)
+    eps, c = 0.2, 4
+    _, _, tr = oracle.sinkhorn(x, y, a, b, eps, 60, check_every=c, lib=lib)
+    assert np.all(np.diff(tr) < 0)
+    for k_star in (1, 3, 12):
+        tol = math.sqrt(tr[k_star - 1] * tr[k_star - 2]) if k_star > 1 else tr[0] * 1.5
+        f, g, it, conv, viol = oracle.sinkhorn_ex(x, y, a, b, eps, stop_mode="marginal", stop_tol=tol,
+                                                  max_iter=400, check_every=c, lib=lib)
+        assert conv and it == c * k_star, (k_star, it)
+        assert viol == pytest.approx(tr[k_star - 1], rel=1e-12)
+        f0, g0, _ = oracle.sinkhorn(x, y, a, b, eps, it, lib=lib)
+        assert np.array_equal(f, f0) and np.array_equal(g, g0)
+    # unreachable tolerance: runs to the cap, checking after the last iteration as well
+    f, g, it, conv, viol = oracle.sinkhorn_ex(x, y, a, b, eps, stop_mode="marginal", stop_tol=0.0,
+                                              max_iter=10, check_every=c, lib=lib)
+    f0, g0, _ = oracle.sinkhorn(x, y, a, b, eps, 10, lib=lib)
+    r = oracle.residual(x, y, a, b, f0, g0, eps, lib=lib)
+    assert it == 10 and conv is False and viol == pytest.approx(max(r[0], r[1]), rel=1e-12)
+
+
+def pin_stop_potential(lib):
+    """Potential stop: the change max(|f - f'|, |g - g'|) since the previous check (zero potentials
+    before the first) falls strictly below tol."""
+    x, y, a, b = _problem(9, 8, 2, 231)
+    eps, c = 0.2, 3
+    runs = [oracle.sinkhorn(x, y, a, b, eps, k, lib=lib)[:2] for k in range(0, 61, c)]
+    runs[0] = (np.zeros(9), np.zeros(8))
+    delta = [max(np.abs(runs[i][0] - runs[i - 1][0]).max(), np.abs(runs[i][1] - runs[i - 1][1]).max())
+             for i in range(1, len(runs))]
+    assert np.all(np.diff(delta[1:]) < 0)
+    for k_star in (2, 5, 11):
+        tol = math.sqrt(delta[k_star - 1] * delta[k_star - 2])
+        f, g, it, conv, viol = oracle.sinkhorn_ex(x, y, a, b, eps, stop_mode="potential", stop_tol=tol,
+                                                  max_iter=60, check_every=c, lib=lib)
+        assert conv and it == c * k_star, (k_star, it)
+        assert viol == pytest.approx(delta[k_star - 1], rel=1e-12)
+    # max_iter not a multiple of the interval: the last check compares against iteration 6
+    f, g, it, conv, viol = oracle.sinkhorn_ex(x, y, a, b, eps, stop_mode="potential", stop_tol=0.0,
+                                              max_iter=8, check_every=c, lib=lib)
+    f8, g8, _ = oracle.sinkhorn(x, y, a, b, eps, 8, lib=lib)
+    want = max(np.abs(f8 - runs[2][0]).max(), np.abs(g8 - runs[2][1]).max())
+    assert it == 8 and conv is False and viol == pytest.approx(want, rel=1e-12)
+
+
+def pin_divergence_dirac(lib):
+    """One point each: OT(x,y) = |x - y|^2 after one iteration, the self-terms vanish."""
+    x = np.array([[0.3, -1.2, 0.5]])
+    y = np.array([[1.1, 0.4, -0.7]])
+    one = np.ones(1)
+    for variant in ("alternating", "symmetric"):
+        S, (txy, txx, tyy) = oracle.divergence(x, y, one, one, 0.7, 1 if variant == "alternating" else 200,
+                                               variant=variant, alpha=0.5, lib=lib)
+        want = float(((x - y) ** 2).sum())
+        assert abs(txx) <= 1e-12 and abs(tyy) <= 1e-12
+        assert S == pytest.approx(want, rel=1e-12, abs=1e-12)
+
+
+def pin_divergence_translation(lib):
+    """S(x, x + t) = |t|^2 for unit mass: the translated cost differs by a separable term whose
+    integral is |t|^2, the self-terms are translation invariant; S(x, x) = 0 exactly."""
+    x, _, a, _ = _problem(12, 12, 2, 241)
+    t = np.array([0.35, -0.2])
+    for variant in ("alternating", "symmetric"):
+        S, _ = oracle.divergence(x, x + t, a, a, 1.0, 3000, variant=variant, lib=lib)
+        assert S == pytest.approx(t @ t, abs=1e-10), variant
+        S0, _ = oracle.divergence(x, x, a, a, 0.3, 50, variant=variant, lib=lib)
+        assert S0 == 0.0
+
+
+def pin_divergence_symmetric_positive(lib):
+    """At convergence S(x,y) = S(y,x) and S > 0 for distinct measures (different sizes)."""
+    x, y, a, b = _problem(10, 7, 2, 251)
+    Sxy, (txy, _, _) = oracle.divergence(x, y, a, b, 0.25, 4000, lib=lib)
+    Syx, (tyx, _, _) = oracle.divergence(y, x, b, a, 0.25, 4000, lib=lib)
+    assert abs(txy - tyx) <= 1e-10 and abs(Sxy - Syx) <= 1e-10
+    assert Sxy > 0.0
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -335,6 +484,15 @@ MUTANTS = {
     "dual_sign": ("return af + bg - eps * (mass_p - sa * sb);", "return af + bg + eps * (mass_p - sa * sb);", 1),
     "dual_no_mass": ("return af + bg - eps * (mass_p - sa * sb);", "return af + bg - eps * mass_p;", 1),
     "resid_no_abs": ("double e = fabs(rs[i] - a[i]);", "double e = rs[i] - a[i];", 1),
+    "jacobi_new_f": ("oracle_half_step(y, m, x, n, d, a, f, eps, NULL, m, gn);",
+                     "oracle_half_step(y, m, x, n, d, a, fn, eps, NULL, m, gn);", 1),
+    "alpha_swap": ("f[i] = (1.0 - alpha) * f[i] + alpha * fn[i];", "f[i] = alpha * f[i] + (1.0 - alpha) * fn[i];", 1),
+    "potential_no_snapshot": ("                fp[i] = f[i];\n", "", 1),
+    "check_phase": ("k % check_every != 0", "(k + 1) % check_every != 0", 1),
+    "no_last_check": (" && k != max_iter", "", 1),
+    "marginal_col_only": ("viol = r[0] > r[1] ? r[0] : r[1];", "viol = r[1];", 1),
+    "div_full_self": ("out[0] = t_xy - 0.5 * t_xx - 0.5 * t_yy;", "out[0] = t_xy - t_xx - t_yy;", 1),
+    "div_self_x_twice": ("oracle_sinkhorn_ex(y, y, b, b, m, m,", "oracle_sinkhorn_ex(x, x, a, a, n, n,", 1),
     "trace_row_only": ("resid_trace[k / check_every - 1] = r[0] > r[1] ? r[0] : r[1];",
                        "resid_trace[k / check_every - 1] = r[1];", 1),
 }
