@@ -18,10 +18,11 @@
  *    by later calls once the calls that used it have completed in stream order.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Compute entry
  *    points only enqueue work and return; results are ready when the stream
- *    reaches that point.  Only sk_check_inputs synchronises the stream.  The
- *    compute entry points allocate nothing, synchronise nothing and use no
- *    memset, so they may be captured into a HIP graph and replayed (inputs,
- *    outputs and workspace at the captured addresses).
+ *    reaches that point.  Only sk_check_inputs, and sk_solve_ex with a stop
+ *    rule, synchronise the stream.  The other compute entry points allocate
+ *    nothing, synchronise nothing and use no memset, so they may be captured
+ *    into a HIP graph and replayed (inputs, outputs and workspace at the
+ *    captured addresses).
  *  - Weights are used exactly as given (not normalised); zeros are legal and
  *    such points contribute nothing.  Data-dependent validity (negative or
  *    non-finite values, unequal masses) is checked by sk_check_inputs, not by
@@ -36,7 +37,8 @@
  * Sources (page title and section):
  *  FS   = "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",
  *         technical summary, Methodology 1-3.
- *  SLOT = SinkSLOT README: Tensor Contract, API Reference, Low-Level Solver API.
+ *  SLOT = SinkSLOT README: opening section, Tensor Contract, API Reference,
+ *         Low-Level Solver API.
  */
 #ifndef SK_H
 #define SK_H
@@ -61,7 +63,11 @@ typedef enum sk_status {
     SK_ERR_EMPTY_MEASURE = 9,  /* sum a == 0 or sum b == 0 */
     SK_ERR_NONFINITE = 10,     /* NaN or Inf in x, y, a or b */
     SK_ERR_WORKSPACE = 11,     /* ws NULL, misaligned, or ws_bytes too small */
-    SK_ERR_HIP = 12            /* a HIP runtime call or kernel launch failed */
+    SK_ERR_HIP = 12,           /* a HIP runtime call or kernel launch failed */
+    SK_ERR_VARIANT = 13,       /* variant not 0 or 1, or symmetric with alpha outside (0, 1] */
+    SK_ERR_STOP = 14,          /* stop_mode not 0, 1 or 2; or a stop rule with stop_tol < 0,
+                                  non-finite, or check_every < 1 */
+    SK_ERR_CAPTURE = 15        /* a stop rule was asked for on a stream under graph capture */
 } sk_status;
 
 /* Version of this ABI (incremented on any signature change). */
@@ -149,10 +155,82 @@ int sk_grad_x(const float *x, const float *y, const float *a, const float *b,
               float *grad, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Sinkhorn with a choice of update variant and stop rule (SLOT, API
+ * Reference: `variant`, `alpha`, `stop_mode`, `stop_max_iter`, `stop_tol`,
+ * `stop_check_every`; Low-Level Solver API: iters_run, converged,
+ * final_viol).  Both potentials start at 0.
+ *
+ * variant 0, alternating (Gauss-Seidel): each iteration is the row half-step
+ *   from the current g, then the column half-step from the new f, exactly as
+ *   sk_solve.
+ * variant 1, symmetric (Jacobi): each iteration computes both half-steps from
+ *   the potentials before it and blends, f <- (1 - alpha) f + alpha T_row(g),
+ *   g <- (1 - alpha) g + alpha T_col(f), with 0 < alpha <= 1 (alpha is
+ *   ignored for variant 0).
+ * stop_mode 0, fixed: exactly max_iter iterations, no check; *converged = -1
+ *   and *final_viol = NaN (the API's None).  Enqueues only, like sk_solve.
+ * stop_mode 1, marginal, and 2, potential: a check follows every
+ *   check_every-th iteration and the last one (max_iter is the cap).  The
+ *   marginal value is max(|P1 - a|_inf, |P^T 1 - b|_inf) at the current
+ *   potentials (for variant 0 the column term is zero by construction and is
+ *   not evaluated); the run stops at the first check with value <= stop_tol.
+ *   The potential value is max(max_i |f_i - f'_i|, max_j |g_j - g'_j|) against
+ *   the potentials at the previous check (zero before the first), i.e. eps
+ *   times the change of the absorbed potentials f/eps; the run stops at the
+ *   first check with value < stop_tol.  Each check synchronises `stream` and
+ *   reads one or two floats back; calling with a stop rule on a stream under
+ *   graph capture returns SK_ERR_CAPTURE before anything is enqueued.  The
+ *   marginal value of iteration k is produced by the passes of iteration
+ *   k + 1, so a check costs no extra pass except after the last iteration.
+ * Outputs: f, g (device) hold the potentials after *iters_run iterations;
+ *   iters_run, converged (1 met the tolerance, 0 hit the cap) and final_viol
+ *   (value of the last check) are host pointers, written on SK_OK.
+ * max_iter = 0 gives f = g = 0, *iters_run = 0 and no check.
+ */
+int sk_solve_ex(const float *x, const float *y, const float *a, const float *b,
+                int64_t n, int64_t m, int32_t d, float eps,
+                int32_t variant, float alpha, int32_t stop_mode, float stop_tol,
+                int32_t max_iter, int32_t check_every,
+                float *f, float *g, int32_t *iters_run, int32_t *converged,
+                float *final_viol, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Entropic dual objective at arbitrary potentials (f, g):
+ *     <a, f> + <b, g> - eps * (sum_ij P_ij - sum(a) sum(b)),
+ *     P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps),
+ * with the plan mass from one streamed row pass (the row sums of P, never
+ * stored) and every sum in float64 in a fixed order.  Unlike sk_cost it holds
+ * for any potentials, e.g. those of the symmetric variant.  `out` is one
+ * device double; ws as for sk_workspace_bytes(n, m, d).
+ */
+int sk_dual_cost(const float *x, const float *y, const float *a, const float *b,
+                 int64_t n, int64_t m, int32_t d, float eps,
+                 const float *f, const float *g, double *out,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of sk_divergence (0 for invalid sizes). */
+size_t sk_divergence_workspace_bytes(int64_t n, int64_t m, int32_t d);
+
+/*
+ * Debiased entropic divergence S = OT(x, y) - OT(x, x)/2 - OT(y, y)/2 (SLOT,
+ * opening section: entropic OT is not zero at (x, x), so a divergence built
+ * from it subtracts the self-terms).  Each term is the dual objective
+ * (sk_dual_cost) after n_iters iterations of the given variant and alpha
+ * (fixed stop) on that pair of clouds.  `out` is 4 device doubles:
+ * [S, OT(x,y), OT(x,x), OT(y,y)].  ws of at least
+ * sk_divergence_workspace_bytes(n, m, d) bytes, 256-byte aligned.  Enqueues
+ * only.
+ */
+int sk_divergence(const float *x, const float *y, const float *a, const float *b,
+                  int64_t n, int64_t m, int32_t d, float eps,
+                  int32_t variant, float alpha, int32_t n_iters, double *out,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Kernel timing of the streamed log-sum-exp passes (benchmark diagnostics).
  * sk_timing_enable(1) resets the counters and from then on records a HIP
  * event pair on the launch stream around every streamed-pass kernel that
- * sk_solve and sk_marginal_residual enqueue (the split merge and the other
+ * the solve, cost and residual entry points enqueue (the split merge and the other
  * kernels are outside the pair); sk_timing_enable(0) stops recording.
  * sk_timing_read waits for the recorded events and returns the total kernel
  * milliseconds, the number of launches and the number of (query, key) pairs

@@ -29,8 +29,13 @@ _STATUS_NAMES = {
     0: "SK_OK", 1: "SK_ERR_NULL", 2: "SK_ERR_SHAPE", 3: "SK_ERR_UNSUPPORTED_D", 4: "SK_ERR_EPS",
     5: "SK_ERR_ITERS", 6: "SK_ERR_CHECK_EVERY", 7: "SK_ERR_NEG_WEIGHT", 8: "SK_ERR_MASS_MISMATCH",
     9: "SK_ERR_EMPTY_MEASURE", 10: "SK_ERR_NONFINITE", 11: "SK_ERR_WORKSPACE", 12: "SK_ERR_HIP",
+    13: "SK_ERR_VARIANT", 14: "SK_ERR_STOP", 15: "SK_ERR_CAPTURE",
 }
-_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10}
+_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 13, 14, 15}
+
+# SinkSLOT README, API Reference: variant and stop_mode names
+VARIANTS = {"alternating": 0, "symmetric": 1}
+STOP_MODES = {"fixed": 0, "marginal": 1, "potential": 2}
 
 # C ABI: (name, restype, argtypes)
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -45,6 +50,13 @@ SIGNATURES = {
     "sk_marginal_residual": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz,
                                             _vp]),
     "sk_grad_x": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "sk_solve_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _f32, _i32, _f32, _i32, _i32,
+                                   _vp, _vp, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_f32), _vp,
+                                   _sz, _vp]),
+    "sk_dual_cost": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "sk_divergence_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "sk_divergence": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _f32, _i32, _vp, _vp, _sz,
+                                     _vp]),
     "sk_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "sk_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_double)]),
@@ -175,6 +187,82 @@ def solve(x, y, a=None, b=None, *, eps: float, n_iters: int, check_every: int = 
     return f, g, trace
 
 
+def solve_ex(x, y, a=None, b=None, *, eps: float, variant: str = "alternating", alpha: float = 0.5,
+             stop_mode: str = "fixed", stop_tol: float = 1e-6, max_iter: int = 200, check_every: int = 5,
+             ws: torch.Tensor | None = None, f: torch.Tensor | None = None, g: torch.Tensor | None = None,
+             check: bool = True):
+    """Sinkhorn with update variant ("alternating" | "symmetric" with blend alpha) and stop rule
+    ("fixed" | "marginal" | "potential"; max_iter is the iteration count or cap).
+
+    Returns (f, g, iters_run, converged, final_viol); converged and final_viol
+    are None under stop_mode="fixed" (then nothing synchronises and the
+    outputs are enqueued on the current stream).
+    """
+    lib = load_library()
+    if variant not in VARIANTS or stop_mode not in STOP_MODES:
+        raise ValueError(f"variant must be one of {list(VARIANTS)}, stop_mode one of {list(STOP_MODES)}")
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    if check:
+        check_inputs(x, y, a, b, ws)
+    f = f if f is not None else torch.empty(n, dtype=torch.float32, device=x.device)
+    g = g if g is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+    it, conv, viol = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_float()
+    _raise(lib.sk_solve_ex(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), VARIANTS[variant],
+                           float(alpha), STOP_MODES[stop_mode], float(stop_tol), int(max_iter), int(check_every),
+                           _ptr(f), _ptr(g), ctypes.byref(it), ctypes.byref(conv), ctypes.byref(viol), _ptr(ws),
+                           ws.numel(), _stream(x.device)), "sk_solve_ex")
+    if stop_mode == "fixed":
+        return f, g, it.value, None, None
+    return f, g, it.value, bool(conv.value), viol.value
+
+
+def dual_cost(x, y, a, b, f, g, *, eps: float, ws: torch.Tensor | None = None,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """<a,f> + <b,g> - eps (sum_ij P_ij - sum(a) sum(b)) at any potentials (1-element float64 tensor)."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    f, g = f.contiguous(), g.contiguous()
+    if f.shape != (n,) or g.shape != (m,) or f.dtype != torch.float32 or g.dtype != torch.float32:
+        raise ValueError("f must be (n,) and g (m,) float32")
+    out = out if out is not None else torch.empty(1, dtype=torch.float64, device=x.device)
+    _raise(lib.sk_dual_cost(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g), _ptr(out),
+                            _ptr(ws), ws.numel(), _stream(x.device)), "sk_dual_cost")
+    return out
+
+
+def divergence_workspace(n: int, m: int, d: int, device) -> torch.Tensor:
+    nb = int(load_library().sk_divergence_workspace_bytes(n, m, d))
+    if nb == 0:
+        raise ValueError(f"invalid problem size n={n} m={m} d={d}")
+    ws = torch.empty(nb, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("allocator returned a workspace that is not 256-byte aligned")
+    return ws
+
+
+def divergence(x, y, a=None, b=None, *, eps: float, n_iters: int, variant: str = "alternating",
+               alpha: float = 0.5, ws: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               check: bool = True) -> torch.Tensor:
+    """Debiased divergence OT(x,y) - OT(x,x)/2 - OT(y,y)/2 after n_iters iterations per term.
+
+    Returns a 4-element float64 device tensor [S, OT(x,y), OT(x,x), OT(y,y)].
+    """
+    lib = load_library()
+    if variant not in VARIANTS:
+        raise ValueError(f"variant must be one of {list(VARIANTS)}")
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    if check:
+        check_inputs(x, y, a, b)
+    ws = ws if ws is not None else divergence_workspace(n, m, d, x.device)
+    out = out if out is not None else torch.empty(4, dtype=torch.float64, device=x.device)
+    _raise(lib.sk_divergence(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), VARIANTS[variant],
+                             float(alpha), int(n_iters), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)),
+           "sk_divergence")
+    return out
+
+
 def cost(a, b, f, g, *, eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
     """<a,f> + <b,g> - eps sum(b)(1 - sum(a)) in float64 (a 1-element device tensor)."""
     lib = load_library()
@@ -232,5 +320,6 @@ def timing_read() -> tuple[float, int, float]:
     return ms.value, n.value, pairs.value
 
 
-__all__ = ["timing_enable", "timing_read", "solve", "cost", "marginal_residual", "grad_x", "check_inputs", "workspace", "workspace_bytes",
-           "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES"]
+__all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "cost", "dual_cost", "divergence",
+           "divergence_workspace", "marginal_residual", "grad_x", "check_inputs", "workspace", "workspace_bytes",
+           "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES", "VARIANTS", "STOP_MODES"]

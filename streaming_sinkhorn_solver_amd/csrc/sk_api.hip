@@ -1,7 +1,7 @@
 // sk_api.hip -- host side of the C ABI declared in include/sk.h: argument
 // validation, workspace carve-up and the launch sequence of each entry point.
 // All work is enqueued on the caller's stream; nothing here synchronises
-// except sk_check_inputs.
+// except sk_check_inputs and the convergence checks of sk_solve_ex.
 #include "sk.h"
 #include "sk_internal.hpp"
 
@@ -17,7 +17,7 @@
 namespace sk {
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 #ifndef SK_SMALL_PAIRS
 #define SK_SMALL_PAIRS 2.0e6
 #endif
@@ -112,15 +112,17 @@ int check_ws(void* ws, size_t ws_bytes, const Layout& L) {
 
 // Shifts both clouds by their common centre and packs them.  x_bias / y_bias:
 // 0 = none, 1 = zero potential, 2 = from the given potential.
+// u_x / u_y (may be null) receive the states that the initial biases encode.
 int prepare(const Ws& W, const float* x, const float* y, const float* a, const float* b, float eps,
-            int x_bias, const float* f, int y_bias, const float* g, hipStream_t s) {
+            int x_bias, const float* f, int y_bias, const float* g, hipStream_t s, float* u_x = nullptr,
+            float* u_y = nullptr) {
     const Layout& L = W.L;
     float* centre = W.f(L.centre);
     SK_TRY(launch_centre(x, y, (int)L.n, (int)L.m, L.d, W.dbl(L.cen), centre, s));
     SK_TRY(launch_pack(x, (int)L.n, L.d, L.P, L.mfma, centre, a, W.f(L.xp), W.f(L.nx), W.f(L.l2a), W.f(L.hx),
-                       1.0f / eps, x_bias, f, s));
+                       1.0f / eps, x_bias, f, u_x, s));
     SK_TRY(launch_pack(y, (int)L.m, L.d, L.P, L.mfma, centre, b, W.f(L.yp), W.f(L.ny), W.f(L.l2b), W.f(L.hy),
-                       1.0f / eps, y_bias, g, s));
+                       1.0f / eps, y_bias, g, u_y, s));
     return SK_OK;
 }
 
@@ -148,7 +150,9 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
     F.d = L.d;
     F.eps_ln2 = eps * kLn2;
     F.inv_eps = 1.0f / eps;
+    F.alpha = 1.0f;
     F.lse = W.f(row_side ? L.lse_r : L.lse_c);
+    F.lse_out = F.lse;
     F.l2w = W.f(row_side ? L.l2a : L.l2b);
     F.w = w_q;
     F.nrm = W.f(row_side ? L.nx : L.ny);
@@ -237,11 +241,211 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.cen = take((size_t)2 * kRedBlocks * d * sizeof(double));
     L.centre = take((size_t)d * 4);
     L.chk = take(8 * sizeof(double));
+    L.lse_r2 = take(un * 4);
+    L.lse_c2 = take(um * 4);
+    L.snap_f = take(un * 4);
+    L.snap_g = take(um * 4);
+    L.chkf = take(8 * sizeof(float));
     L.total = off;
     return L;
 }
 
 int plan_split(int64_t nq, int64_t nk, int rpb) { return split_for(nq, nk, rpb).nsplit; }
+
+namespace {
+
+// Options of sk_solve_ex (validated by the caller).
+struct ExOpts {
+    int variant;     // 0 alternating, 1 symmetric
+    float alpha;     // blend of the symmetric variant
+    int stop_mode;   // 0 fixed, 1 marginal, 2 potential
+    float tol;
+    int max_iter;
+    int check_every;
+};
+
+struct ExResult {
+    int iters;
+    int converged;   // -1 under the fixed rule
+    float viol;      // NaN when no check ran
+};
+
+// Reads n floats of the workspace back to the host (waits for the stream).
+int read_back(const float* dev, float* host, int n, hipStream_t s) {
+    SK_TRY(hipMemcpyAsync(host, dev, (size_t)n * sizeof(float), hipMemcpyDeviceToHost, s));
+    SK_TRY(hipStreamSynchronize(s));
+    return SK_OK;
+}
+
+// Sinkhorn with an update variant and a stop rule (SinkSLOT README, API
+// Reference).  Iteration k of the alternating variant is a row pass from the
+// current g then a column pass from the new f; the symmetric variant runs both
+// passes from the state before the iteration, blends each result into its
+// side's state and then rewrites both key biases.
+//
+// Checks come after every check_every-th iteration and after the last.  The
+// marginal residual of the state after iteration k falls out of the passes of
+// iteration k + 1 (the row pass for the alternating variant, whose column sums
+// are exact by construction; both passes for the symmetric one), so a check
+// costs no extra pass except after the last iteration, where a probe pass
+// (which changes nothing) takes its place.  Passes that produce a residual
+// write their new state into the second state buffer, so the state that was
+// checked is still at hand when it meets the tolerance: its potentials are
+// then rewritten from it and the run ends with iters = k.  The potential rule
+// compares the output potentials with a snapshot taken at the previous check.
+int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const float* b, float eps,
+             const ExOpts& o, float* f, float* g, ExResult* res, hipStream_t s) {
+    const Layout& L = W.L;
+    res->iters = o.max_iter;
+    res->converged = o.stop_mode == 0 ? -1 : 0;
+    res->viol = NAN;
+    if (o.max_iter == 0) {
+        SK_TRY(launch_fill(f, L.n, 0.0f, s));
+        SK_TRY(launch_fill(g, L.m, 0.0f, s));
+        return SK_OK;
+    }
+    const int cap = pass_capacity(L.d);
+    if (cap <= 0) return SK_ERR_HIP;
+    const bool sym = o.variant == 1;
+    float* ur[2] = {W.f(L.lse_r), W.f(L.lse_r2)};
+    float* uc[2] = {W.f(L.lse_c), W.f(L.lse_c2)};
+    int cr = 0, cc = 0;
+    int st;
+    if ((st = prepare(W, x, y, a, b, eps, sym ? 1 : 0, nullptr, 1, nullptr, s, sym ? ur[0] : nullptr,
+                      sym ? uc[0] : nullptr)))
+        return st;
+
+    PassArgs row = make_pass(W, true, eps, a, cap);
+    row.fin.pot = f;
+    PassArgs col = make_pass(W, false, eps, b, cap);
+    col.fin.pot = g;
+    if (sym) {  // biases are rewritten once both passes have read the old ones
+        row.fin.alpha = col.fin.alpha = o.alpha;
+        row.fin.bias_packed = row.fin.bias_sep = nullptr;
+        col.fin.bias_packed = col.fin.bias_sep = nullptr;
+    }
+    float* rbuf = W.f(L.rbuf);
+    float* chk = W.f(L.chkf);
+    float host[2] = {0.0f, 0.0f};
+    if (o.stop_mode == 2) {
+        SK_TRY(launch_fill(W.f(L.snap_f), L.n, 0.0f, s));
+        SK_TRY(launch_fill(W.f(L.snap_g), L.m, 0.0f, s));
+    }
+    auto is_check = [&](int k) { return o.stop_mode != 0 && k >= 1 && (k % o.check_every == 0 || k == o.max_iter); };
+    // the state after iteration k met the tolerance: restore its potentials and stop
+    auto stop_at = [&](int k, bool restore_f, bool restore_g) -> int {
+        if (restore_f) SK_TRY(launch_pot_from_state(ur[cr], W.f(L.nx), eps * kLn2, f, (int)L.n, s));
+        if (restore_g) SK_TRY(launch_pot_from_state(uc[cc], W.f(L.ny), eps * kLn2, g, (int)L.m, s));
+        res->iters = k;
+        res->converged = 1;
+        return SK_OK;
+    };
+
+    for (int k = 1; k <= o.max_iter; ++k) {
+        const bool fused = o.stop_mode == 1 && is_check(k - 1);
+        row.fin.lse = ur[cr];
+        row.fin.lse_out = fused ? ur[cr ^ 1] : ur[cr];
+        row.fin.rbuf = fused ? rbuf : nullptr;
+        if ((st = run_pass(W, row, s))) return st;
+        if (fused) SK_TRY(launch_resid_reduce(rbuf, (int)L.n, chk + 0, nullptr, s));
+        if (fused && !sym) {
+            if ((st = read_back(chk, host, 1, s))) return st;
+            res->viol = host[0];
+            if (host[0] <= o.tol) return stop_at(k - 1, true, false);
+            cr ^= 1;
+        }
+        const bool fused_col = fused && sym;
+        col.fin.lse = uc[cc];
+        col.fin.lse_out = fused_col ? uc[cc ^ 1] : uc[cc];
+        col.fin.rbuf = fused_col ? rbuf : nullptr;
+        if ((st = run_pass(W, col, s))) return st;
+        if (fused_col) {
+            SK_TRY(launch_resid_reduce(rbuf, (int)L.m, chk + 1, nullptr, s));
+            if ((st = read_back(chk, host, 2, s))) return st;
+            res->viol = std::max(host[0], host[1]);
+            if (res->viol <= o.tol) return stop_at(k - 1, true, true);
+            cr ^= 1;
+            cc ^= 1;
+        }
+        if (sym) {
+            BiasSide bx{ur[cr], W.f(L.l2a), L.mfma ? nullptr : W.f(L.xp), L.mfma ? W.f(L.hx) : nullptr, (int)L.n};
+            BiasSide by{uc[cc], W.f(L.l2b), L.mfma ? nullptr : W.f(L.yp), L.mfma ? W.f(L.hy) : nullptr, (int)L.m};
+            SK_TRY(launch_apply_bias(bx, by, L.P, L.d, s));
+        }
+        if (o.stop_mode == 2 && is_check(k)) {
+            SK_TRY(launch_pot_change(f, W.f(L.snap_f), (int)L.n, g, W.f(L.snap_g), (int)L.m, chk, s));
+            if ((st = read_back(chk, host, 1, s))) return st;
+            res->viol = host[0];
+            if (host[0] < o.tol) return stop_at(k, false, false);
+        }
+    }
+    if (o.stop_mode == 1) {  // the check after the last iteration: probe passes
+        PassArgs probe = row;
+        probe.fin.mode = kFinProbe;
+        probe.fin.lse = ur[cr];
+        probe.fin.rbuf = rbuf;
+        if ((st = run_pass(W, probe, s))) return st;
+        SK_TRY(launch_resid_reduce(rbuf, (int)L.n, chk + 0, nullptr, s));
+        int cnt = 1;
+        if (sym) {
+            probe = col;
+            probe.fin.mode = kFinProbe;
+            probe.fin.lse = uc[cc];
+            probe.fin.rbuf = rbuf;
+            if ((st = run_pass(W, probe, s))) return st;
+            SK_TRY(launch_resid_reduce(rbuf, (int)L.m, chk + 1, nullptr, s));
+            cnt = 2;
+        }
+        if ((st = read_back(chk, host, cnt, s))) return st;
+        res->viol = cnt == 2 ? std::max(host[0], host[1]) : host[0];
+        if (res->viol <= o.tol) res->converged = 1;
+    }
+    return SK_OK;
+}
+
+// Dual objective at arbitrary potentials: one row pass for the plan's row sums.
+int dual_cost(const Ws& W, const float* x, const float* y, const float* a, const float* b, float eps,
+              const float* f, const float* g, double* out, hipStream_t s) {
+    const Layout& L = W.L;
+    const int cap = pass_capacity(L.d);
+    if (cap <= 0) return SK_ERR_HIP;
+    int st;
+    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 2, g, s))) return st;
+    PassArgs row = make_pass(W, true, eps, a, cap);
+    row.fin.mode = kFinMass;
+    row.fin.pot_in = f;
+    row.fin.rbuf = W.f(L.rbuf);
+    if ((st = run_pass(W, row, s))) return st;
+    SK_TRY(launch_cost_mass(a, b, f, g, W.f(L.rbuf), (int)L.n, (int)L.m, eps, out, s));
+    return SK_OK;
+}
+
+int check_ex(int variant, float alpha, int stop_mode, float tol, int max_iter, int check_every) {
+    if (variant != 0 && variant != 1) return SK_ERR_VARIANT;
+    if (variant == 1 && !(alpha > 0.0f && alpha <= 1.0f)) return SK_ERR_VARIANT;
+    if (max_iter < 0) return SK_ERR_ITERS;
+    if (stop_mode < 0 || stop_mode > 2) return SK_ERR_STOP;
+    if (stop_mode != 0 && (!(tol >= 0.0f) || !std::isfinite(tol) || check_every < 1)) return SK_ERR_STOP;
+    return SK_OK;
+}
+
+// Workspace of sk_divergence: the largest of the three solver layouts, then
+// one potential pair of max(n, m) floats each.
+struct DivLayout {
+    size_t solver, f, g, total;
+};
+DivLayout div_layout(int64_t n, int64_t m, int d) {
+    DivLayout D{};
+    D.solver = std::max({make_layout(n, m, d).total, make_layout(n, n, d).total, make_layout(m, m, d).total});
+    D.solver = align_up(D.solver, 256);
+    const size_t pot = align_up((size_t)std::max(n, m) * 4, 256);
+    D.f = D.solver;
+    D.g = D.f + pot;
+    D.total = D.g + pot;
+    return D;
+}
+
+}  // namespace
 
 }  // namespace sk
 
@@ -266,6 +470,9 @@ const char* sk_status_string(int status) {
         case SK_ERR_NONFINITE: return "inputs contain NaN or Inf";
         case SK_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or too small";
         case SK_ERR_HIP: return "HIP runtime or kernel launch failure";
+        case SK_ERR_VARIANT: return "variant must be 0 (alternating) or 1 (symmetric, 0 < alpha <= 1)";
+        case SK_ERR_STOP: return "stop_mode must be 0, 1 or 2; a stop rule needs tol >= 0 finite and check_every >= 1";
+        case SK_ERR_CAPTURE: return "a stop rule synchronises the stream and cannot run under graph capture";
         default: return "unknown status";
     }
 }
@@ -451,6 +658,81 @@ int sk_grad_x(const float* x, const float* y, const float* a, const float* b, in
     if ((st = run_pass(W, lse_pass, s))) return st;
     ga.lse = W.f(L.lse_r);
     SK_TRY(launch_grad_mfma(ga, s));
+    return SK_OK;
+}
+
+int sk_solve_ex(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+                float eps, int32_t variant, float alpha, int32_t stop_mode, float stop_tol, int32_t max_iter,
+                int32_t check_every, float* f, float* g, int32_t* iters_run, int32_t* converged,
+                float* final_viol, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g || !iters_run || !converged || !final_viol) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if ((st = check_ex(variant, alpha, stop_mode, stop_tol, max_iter, check_every))) return st;
+    const Layout L = make_layout(n, m, d);
+    if ((st = check_ws(ws, ws_bytes, L))) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (stop_mode != 0) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cap) != hipSuccess) return SK_ERR_HIP;
+        if (cap != hipStreamCaptureStatusNone) return SK_ERR_CAPTURE;
+    }
+    Ws W{L, static_cast<char*>(ws)};
+    ExOpts o{variant, variant == 1 ? alpha : 1.0f, stop_mode, stop_tol, max_iter, check_every};
+    ExResult r{};
+    if ((st = solve_ex(W, x, y, a, b, eps, o, f, g, &r, s))) return st;
+    *iters_run = r.iters;
+    *converged = r.converged;
+    *final_viol = r.viol;
+    return SK_OK;
+}
+
+int sk_dual_cost(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+                 float eps, const float* f, const float* g, double* out, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g || !out) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    const Layout L = make_layout(n, m, d);
+    if ((st = check_ws(ws, ws_bytes, L))) return st;
+    Ws W{L, static_cast<char*>(ws)};
+    return dual_cost(W, x, y, a, b, eps, f, g, out, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t sk_divergence_workspace_bytes(int64_t n, int64_t m, int32_t d) {
+    if (check_sizes(n, m, d) != SK_OK) return 0;
+    return div_layout(n, m, d).total;
+}
+
+int sk_divergence(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+                  float eps, int32_t variant, float alpha, int32_t n_iters, double* out, void* ws, size_t ws_bytes,
+                  void* stream) {
+    if (!x || !y || !a || !b || !out) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if ((st = check_ex(variant, alpha, 0, 0.0f, n_iters, 1))) return st;
+    const DivLayout D = div_layout(n, m, d);
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) % 256) != 0 || ws_bytes < D.total) return SK_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(ws);
+    float* fb = reinterpret_cast<float*>(base + D.f);
+    float* gb = reinterpret_cast<float*>(base + D.g);
+    const ExOpts o{variant, variant == 1 ? alpha : 1.0f, 0, 0.0f, n_iters, 1};
+    struct Term {
+        const float *p, *q, *wp, *wq;
+        int64_t np, nq;
+    };
+    const Term terms[3] = {{x, y, a, b, n, m}, {x, x, a, a, n, n}, {y, y, b, b, m, m}};
+    for (int t = 0; t < 3; ++t) {
+        const Term& T = terms[t];
+        Ws W{make_layout(T.np, T.nq, d), base};
+        ExResult r{};
+        if ((st = solve_ex(W, T.p, T.q, T.wp, T.wq, eps, o, fb, gb, &r, s))) return st;
+        if ((st = dual_cost(W, T.p, T.q, T.wp, T.wq, eps, fb, gb, out + 1 + t, s))) return st;
+    }
+    SK_TRY(launch_div_combine(out, s));
     return SK_OK;
 }
 

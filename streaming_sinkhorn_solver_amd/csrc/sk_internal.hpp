@@ -58,23 +58,30 @@ enum FinMode : int {
     kFinProbe = 1,   // residual of the previous state only (no state change)
     kFinResid = 2,   // residual against a caller-supplied potential
     kFinStore = 3,   // store lse only
+    kFinMass = 4,    // row sums of the plan at a caller-supplied potential
 };
 
+// kFinSolve keeps the state as u_i = (|q~_i|^2 - f_i) / (eps ln 2), the base-2
+// log-sum-exp of the last pass for a plain update.  A blended update (the
+// symmetric variant) stores u' = u + alpha (lse - u), i.e. f' = (1 - alpha) f +
+// alpha f~ in cost units; alpha = 1 is the plain update and reads no old state.
 struct Fin {
     int mode;
     int P;               // packed stride of the query cloud (bias slot at index d)
     int d;
     float eps_ln2;       // eps * ln 2
     float inv_eps;       // 1 / eps
-    float* lse;          // [nq] running state (read before write when a residual is taken)
+    float alpha;         // blend weight of kFinSolve (1 = replace)
+    float* lse;          // [nq] state u before the pass (read for a residual or a blend)
+    float* lse_out;      // [nq] state after the pass (may equal lse)
     const float* l2w;    // [nq] log2 of the query-side weights (-inf for zero weight)
     const float* w;      // [nq] query-side weights
     const float* nrm;    // [nq] |q~|^2 of the centred query points
     float* pot;          // [nq] output potential in cost units, or null
     float* bias_packed;  // query packed base (bias slot = index d), or null
     float* bias_sep;     // separate bias array (matrix-core layout), or null
-    float* rbuf;         // [nq] |residual_i| output, or null
-    const float* pot_in; // [nq] caller potential (kFinResid)
+    float* rbuf;         // [nq] |residual_i| (kFinSolve, kFinProbe, kFinResid) or (P1)_i (kFinMass)
+    const float* pot_in; // [nq] caller potential (kFinResid, kFinMass)
 };
 
 // Arguments of one streamed log-sum-exp pass over all (query, key) pairs.
@@ -126,6 +133,9 @@ struct Layout {
     bool mfma;
     int64_t n, m;
     size_t xp, yp, hx, hy, nx, ny, l2a, l2b, lse_r, lse_c, rbuf, part, partA, red, cen, centre, chk;
+    size_t lse_r2, lse_c2;    // second state buffers (a check keeps the previous state)
+    size_t snap_f, snap_g;    // potentials at the previous check (potential stop rule)
+    size_t chkf;              // a few floats read back by the host at a check
     size_t total;
 };
 
@@ -138,10 +148,32 @@ int plan_split(int64_t nq, int64_t nk, int rows_per_block);
 // ----- launchers (return hipError_t of the launch) --------------------------------
 hipError_t launch_centre(const float* x, const float* y, int n, int m, int d, double* partials,
                          float* centre, hipStream_t s);
+// u_out (may be null): the state u matching the initial bias (0 for bias_mode 0).
 hipError_t launch_pack(const float* pts, int npts, int d, int P, bool mfma, const float* centre,
                        const float* w, float* packed, float* nrm, float* l2w, float* bias_sep,
-                       float inv_eps, int bias_mode, const float* pot, hipStream_t s);
+                       float inv_eps, int bias_mode, const float* pot, float* u_out, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t count, float value, hipStream_t s);
+// Key bias h = log2 w - u of both clouds from their states (one launch).
+struct BiasSide {
+    const float* u;
+    const float* l2w;
+    float* packed;  // VALU layout: bias slot at index d of each packed row, else null
+    float* sep;     // matrix-core layout: separate bias array, else null
+    int npts;
+};
+hipError_t launch_apply_bias(const BiasSide& x, const BiasSide& y, int P, int d, hipStream_t s);
+// pot_i = nrm_i - eps ln2 u_i (the potential of a stored state).
+hipError_t launch_pot_from_state(const float* u, const float* nrm, float eps_ln2, float* pot, int npts,
+                                 hipStream_t s);
+// out[0] = max(max_i |f_i - sf_i|, max_j |g_j - sg_j|), then sf = f, sg = g.
+hipError_t launch_pot_change(const float* f, float* sf, int n, const float* g, float* sg, int m, float* out,
+                             hipStream_t s);
+// mass (may be null): per-row plan sums (P1)_i; the cost then uses their float64
+// sum as the plan mass instead of sum(b).
+hipError_t launch_cost_mass(const float* a, const float* b, const float* f, const float* g, const float* mass,
+                            int n, int m, float eps, double* out, hipStream_t s);
+// out[0] = out[1] - out[2] / 2 - out[3] / 2.
+hipError_t launch_div_combine(double* out, hipStream_t s);
 hipError_t launch_check(const float* x, const float* y, const float* a, const float* b, int n, int m,
                         int d, double* partials, double* result, hipStream_t s);
 hipError_t launch_cost(const float* a, const float* b, const float* f, const float* g, int n, int m,

@@ -14,22 +14,28 @@ __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x);
 // Applies a finished row's log-sum-exp (base 2) to the pass outputs.
 __device__ __forceinline__ void finalize(const Fin& F, int i, float lse) {
     if (F.mode == kFinSolve) {
+        const float old = (F.rbuf || F.alpha != 1.0f) ? F.lse[i] : 0.0f;
         if (F.rbuf) {
             const float wi = F.w[i];
-            const float r = wi > 0.0f ? wi * expm1f((lse - F.lse[i]) * kLn2) : 0.0f;
+            const float r = wi > 0.0f ? wi * expm1f((lse - old) * kLn2) : 0.0f;
             F.rbuf[i] = fabsf(r);
         }
-        F.lse[i] = lse;
-        const float h = F.l2w[i] - lse;
+        const float u = F.alpha == 1.0f ? lse : fmaf(F.alpha, lse - old, old);
+        F.lse_out[i] = u;
+        const float h = F.l2w[i] - u;
         if (F.bias_packed) F.bias_packed[(size_t)i * F.P + F.d] = h;
         if (F.bias_sep) F.bias_sep[i] = h;
-        if (F.pot) F.pot[i] = F.nrm[i] - F.eps_ln2 * lse;
+        if (F.pot) F.pot[i] = F.nrm[i] - F.eps_ln2 * u;
     } else if (F.mode == kFinProbe) {
         const float wi = F.w[i];
         const float r = wi > 0.0f ? wi * expm1f((lse - F.lse[i]) * kLn2) : 0.0f;
         F.rbuf[i] = fabsf(r);
     } else if (F.mode == kFinStore) {
         F.lse[i] = lse;
+    } else if (F.mode == kFinMass) {  // (P1)_i = a_i exp((f_i - f~_i)/eps)
+        const float wi = F.w[i];
+        const float e = (F.pot_in[i] - F.nrm[i]) * F.inv_eps + kLn2 * lse;
+        F.rbuf[i] = wi > 0.0f ? wi * expf(e) : 0.0f;
     } else {  // kFinResid: (P1)_i / a_i - 1 = exp((f_i - f~_i)/eps) - 1
         const float wi = F.w[i];
         const float e = (F.pot_in[i] - F.nrm[i]) * F.inv_eps + kLn2 * lse;

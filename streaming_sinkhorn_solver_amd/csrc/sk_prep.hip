@@ -1,6 +1,7 @@
 // sk_prep.hip -- once-per-call preparation and the small deterministic reductions:
 // common centre, packing of the clouds with norms and log-weights, data checks,
-// the cost <a,f> + <b,g>, and the residual max / sum.
+// the dual cost, the residual max / sum, the state-to-bias and state-to-potential
+// maps of the stop rules and blended updates, and the potential-change check.
 //
 // Every reduction is two-stage with a fixed partition (kRedBlocks partials, or
 // one workgroup walking the data in a fixed order) and a fixed-order final
@@ -76,12 +77,14 @@ __global__ __launch_bounds__(kBlock) void k_centre_final(const double* __restric
 
 // Pack one cloud: centred coordinates, zero padding, |p~|^2, log2 w and the
 // initial bias.  bias_mode: 0 = none (0), 1 = zero potential, 2 = from pot.
+// u_out (may be null) receives the state u = (|p~|^2 - pot) log2e / eps that
+// the bias encodes (h = log2 w - u); 0 for bias_mode 0.
 __global__ __launch_bounds__(kBlock) void k_pack(const float* __restrict__ pts, int npts, int d, int P,
                                                  int mfma, const float* __restrict__ centre,
                                                  const float* __restrict__ w, float* __restrict__ packed,
                                                  float* __restrict__ nrm, float* __restrict__ l2w,
                                                  float* __restrict__ bias_sep, float inv_eps, int bias_mode,
-                                                 const float* __restrict__ pot) {
+                                                 const float* __restrict__ pot, float* __restrict__ u_out) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= npts) return;
     float s = 0.0f;
@@ -96,9 +99,11 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float* __restrict__ pts, 
     const float lw = wi > 0.0f ? log2f(wi) : -INFINITY;
     nrm[i] = s;
     l2w[i] = lw;
-    float h = 0.0f;
-    if (bias_mode == 1) h = lw - s * kLog2e * inv_eps;
-    if (bias_mode == 2) h = lw + (pot[i] - s) * kLog2e * inv_eps;
+    float u = 0.0f;
+    if (bias_mode == 1) u = s * kLog2e * inv_eps;
+    if (bias_mode == 2) u = (s - pot[i]) * kLog2e * inv_eps;
+    const float h = bias_mode == 0 ? 0.0f : lw - u;
+    if (u_out) u_out[i] = u;
     if (mfma)
         bias_sep[i] = h;
     else
@@ -108,6 +113,27 @@ __global__ __launch_bounds__(kBlock) void k_pack(const float* __restrict__ pts, 
 __global__ __launch_bounds__(kBlock) void k_fill(float* __restrict__ p, int64_t count, float v) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < count) p[i] = v;
+}
+
+// Key bias of both clouds from their states: threads [0, x.npts) serve x, the rest y.
+__global__ __launch_bounds__(kBlock) void k_apply_bias(BiasSide x, BiasSide y, int P, int d) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const BiasSide& S = i < x.npts ? x : y;
+    if (i >= x.npts) i -= x.npts;
+    if (i >= S.npts) return;
+    const float h = S.l2w[i] - S.u[i];
+    if (S.sep)
+        S.sep[i] = h;
+    else
+        S.packed[(size_t)i * P + d] = h;
+}
+
+// Potential of a stored state; the same expression as the pass epilogue.
+__global__ __launch_bounds__(kBlock) void k_pot_from_state(const float* __restrict__ u,
+                                                           const float* __restrict__ nrm, float eps_ln2,
+                                                           float* __restrict__ pot, int npts) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < npts) pot[i] = nrm[i] - eps_ln2 * u[i];
 }
 
 // Data checks of one flat array: [nonfinite flag, negative flag, float64 sum].
@@ -154,15 +180,19 @@ __global__ __launch_bounds__(kBlock) void k_check_final(const double* __restrict
 }
 
 // Cost: one workgroup walks both vectors in a fixed order with float64 sums.
+// With `mass` (per-row plan sums) the plan mass is their sum; without it the
+// potentials are taken to come out of a column half-step, whose plan mass is sum(b).
 __global__ __launch_bounds__(1024) void k_cost(const float* __restrict__ a, const float* __restrict__ b,
                                                const float* __restrict__ f, const float* __restrict__ g,
-                                               int n, int m, float eps, double* __restrict__ out) {
+                                               const float* __restrict__ mass, int n, int m, float eps,
+                                               double* __restrict__ out) {
     __shared__ double sh[1024];
-    double af = 0.0, sa = 0.0, bg = 0.0, sb = 0.0;
+    double af = 0.0, sa = 0.0, bg = 0.0, sb = 0.0, mp = 0.0;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
         float ai = a[i];
         if (ai != 0.0f) af += (double)ai * (double)f[i];
         sa += (double)ai;
+        if (mass) mp += (double)mass[i];
     }
     for (int j = threadIdx.x; j < m; j += blockDim.x) {
         float bj = b[j];
@@ -173,7 +203,33 @@ __global__ __launch_bounds__(1024) void k_cost(const float* __restrict__ a, cons
     sa = block_sum_f64(sa, sh);
     bg = block_sum_f64(bg, sh);
     sb = block_sum_f64(sb, sh);
-    if (threadIdx.x == 0) out[0] = af + bg - (double)eps * sb * (1.0 - sa);
+    if (mass) mp = block_sum_f64(mp, sh);
+    if (threadIdx.x == 0)
+        out[0] = mass ? af + bg - (double)eps * (mp - sa * sb) : af + bg - (double)eps * sb * (1.0 - sa);
+}
+
+// Largest change of the potentials since the snapshot, then the snapshot is refreshed.
+__global__ __launch_bounds__(1024) void k_pot_change(const float* __restrict__ f, float* __restrict__ sf, int n,
+                                                     const float* __restrict__ g, float* __restrict__ sg, int m,
+                                                     float* __restrict__ out) {
+    __shared__ float shf[1024];
+    float mx = 0.0f;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const float v = f[i];
+        mx = fmaxf(mx, fabsf(v - sf[i]));
+        sf[i] = v;
+    }
+    for (int j = threadIdx.x; j < m; j += blockDim.x) {
+        const float v = g[j];
+        mx = fmaxf(mx, fabsf(v - sg[j]));
+        sg[j] = v;
+    }
+    mx = block_max_f32(mx, shf);
+    if (threadIdx.x == 0) out[0] = mx;
+}
+
+__global__ void k_div_combine(double* out) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) out[0] = out[1] - 0.5 * out[2] - 0.5 * out[3];
 }
 
 // Residual reduction: max and float64 sum of |r_i|.
@@ -213,9 +269,39 @@ hipError_t launch_centre(const float* x, const float* y, int n, int m, int d, do
 
 hipError_t launch_pack(const float* pts, int npts, int d, int P, bool mfma, const float* centre,
                        const float* w, float* packed, float* nrm, float* l2w, float* bias_sep,
-                       float inv_eps, int bias_mode, const float* pot, hipStream_t s) {
+                       float inv_eps, int bias_mode, const float* pot, float* u_out, hipStream_t s) {
     hipLaunchKernelGGL(k_pack, dim3(grid_for(npts, kBlock)), dim3(kBlock), 0, s, pts, npts, d, P,
-                       mfma ? 1 : 0, centre, w, packed, nrm, l2w, bias_sep, inv_eps, bias_mode, pot);
+                       mfma ? 1 : 0, centre, w, packed, nrm, l2w, bias_sep, inv_eps, bias_mode, pot, u_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply_bias(const BiasSide& x, const BiasSide& y, int P, int d, hipStream_t s) {
+    hipLaunchKernelGGL(k_apply_bias, dim3(grid_for((int64_t)x.npts + y.npts, kBlock)), dim3(kBlock), 0, s, x, y,
+                       P, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_pot_from_state(const float* u, const float* nrm, float eps_ln2, float* pot, int npts,
+                                 hipStream_t s) {
+    hipLaunchKernelGGL(k_pot_from_state, dim3(grid_for(npts, kBlock)), dim3(kBlock), 0, s, u, nrm, eps_ln2, pot,
+                       npts);
+    return hipGetLastError();
+}
+
+hipError_t launch_pot_change(const float* f, float* sf, int n, const float* g, float* sg, int m, float* out,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(k_pot_change, dim3(1), dim3(1024), 0, s, f, sf, n, g, sg, m, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_cost_mass(const float* a, const float* b, const float* f, const float* g, const float* mass,
+                            int n, int m, float eps, double* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_cost, dim3(1), dim3(1024), 0, s, a, b, f, g, mass, n, m, eps, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_div_combine(double* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_div_combine, dim3(1), dim3(64), 0, s, out);
     return hipGetLastError();
 }
 
@@ -238,7 +324,7 @@ hipError_t launch_check(const float* x, const float* y, const float* a, const fl
 
 hipError_t launch_cost(const float* a, const float* b, const float* f, const float* g, int n, int m,
                        float eps, double* out, hipStream_t s) {
-    hipLaunchKernelGGL(k_cost, dim3(1), dim3(1024), 0, s, a, b, f, g, n, m, eps, out);
+    hipLaunchKernelGGL(k_cost, dim3(1), dim3(1024), 0, s, a, b, f, g, nullptr, n, m, eps, out);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "sk.h")
 
 SK_OK, SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_UNSUPPORTED_D, SK_ERR_EPS = 0, 1, 2, 3, 4
 SK_ERR_ITERS, SK_ERR_CHECK_EVERY, SK_ERR_WORKSPACE = 5, 6, 11
+SK_ERR_VARIANT, SK_ERR_STOP, SK_ERR_CAPTURE = 13, 14, 15
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +36,8 @@ def header_functions():
 def test_header_declares_entry_points():
     names = header_functions()
     for must in ("sk_solve", "sk_cost", "sk_marginal_residual", "sk_grad_x", "sk_workspace_bytes",
-                 "sk_check_inputs", "sk_status_string", "sk_abi_version"):
+                 "sk_check_inputs", "sk_status_string", "sk_abi_version", "sk_solve_ex", "sk_dual_cost",
+                 "sk_divergence", "sk_divergence_workspace_bytes"):
         assert must in names
 
 
@@ -48,11 +50,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 13):
+    for code in range(0, 16):
         s = lib.sk_status_string(code)
-        assert s and len(s) > 1
+        assert s and len(s) > 1 and s != b"unknown status"
     assert lib.sk_status_string(999) == b"unknown status"
-    assert lib.sk_abi_version() == 1
+    assert lib.sk_abi_version() == 2
 
 
 def test_workspace_is_linear(lib):
@@ -116,6 +118,59 @@ def test_other_entry_points_argument_errors(lib):
     assert lib.sk_check_inputs(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, None, wb, None) == SK_ERR_WORKSPACE
 
 
+def _solve_ex(lib, *, x=FAKE, n=10, m=12, d=2, eps=0.1, variant=0, alpha=0.5, stop=0, tol=1e-6, max_iter=20,
+              check_every=5, iters=None, ws=FAKE, ws_bytes=None):
+    wb = lib.sk_workspace_bytes(max(n, 1), max(m, 1), max(min(d, 256), 1)) if ws_bytes is None else ws_bytes
+    it, conv, viol = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_float()
+    return lib.sk_solve_ex(x, FAKE, FAKE, FAKE, n, m, d, eps, variant, alpha, stop, tol, max_iter, check_every,
+                           FAKE, FAKE, ctypes.byref(it) if iters is None else iters, ctypes.byref(conv),
+                           ctypes.byref(viol), ws, wb, None)
+
+
+def test_solve_ex_argument_errors(lib):
+    assert _solve_ex(lib, x=None) == SK_ERR_NULL
+    assert _solve_ex(lib, iters=ctypes.POINTER(ctypes.c_int32)()) == SK_ERR_NULL
+    assert _solve_ex(lib, n=0) == SK_ERR_SHAPE
+    assert _solve_ex(lib, d=257) == SK_ERR_UNSUPPORTED_D
+    assert _solve_ex(lib, eps=0.0) == SK_ERR_EPS
+    assert _solve_ex(lib, variant=2) == SK_ERR_VARIANT
+    assert _solve_ex(lib, variant=-1) == SK_ERR_VARIANT
+    assert _solve_ex(lib, variant=1, alpha=0.0) == SK_ERR_VARIANT
+    assert _solve_ex(lib, variant=1, alpha=1.5) == SK_ERR_VARIANT
+    assert _solve_ex(lib, variant=1, alpha=float("nan")) == SK_ERR_VARIANT
+    assert _solve_ex(lib, max_iter=-1) == SK_ERR_ITERS
+    assert _solve_ex(lib, stop=3) == SK_ERR_STOP
+    assert _solve_ex(lib, stop=1, tol=-1e-3) == SK_ERR_STOP
+    assert _solve_ex(lib, stop=2, tol=float("nan")) == SK_ERR_STOP
+    assert _solve_ex(lib, stop=1, tol=float("inf")) == SK_ERR_STOP
+    assert _solve_ex(lib, stop=1, check_every=0) == SK_ERR_STOP
+    assert _solve_ex(lib, ws=None) == SK_ERR_WORKSPACE
+    assert _solve_ex(lib, ws_bytes=lib.sk_workspace_bytes(10, 12, 2) - 1) == SK_ERR_WORKSPACE
+
+
+def test_dual_cost_and_divergence_argument_errors(lib):
+    wb = lib.sk_workspace_bytes(10, 12, 2)
+    assert lib.sk_dual_cost(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, 0.1, FAKE, FAKE, None, FAKE, wb, None) == SK_ERR_NULL
+    assert lib.sk_dual_cost(FAKE, FAKE, FAKE, FAKE, 10, 12, 0, 0.1, FAKE, FAKE, FAKE, FAKE, wb, None) == SK_ERR_SHAPE
+    assert lib.sk_dual_cost(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, 0.1, FAKE, FAKE, FAKE, FAKE, 8, None) == SK_ERR_WORKSPACE
+    db = lib.sk_divergence_workspace_bytes(10, 12, 2)
+    # holds the largest of the three problems (x,y), (x,x), (y,y) plus a potential pair
+    assert db >= max(lib.sk_workspace_bytes(10, 12, 2), lib.sk_workspace_bytes(12, 12, 2)) + 2 * 12 * 4
+    assert lib.sk_divergence_workspace_bytes(0, 12, 2) == 0
+    assert lib.sk_divergence_workspace_bytes(10, 12, 300) == 0
+    div = lambda **k: lib.sk_divergence(k.get("x", FAKE), FAKE, FAKE, FAKE, 10, 12, 2, k.get("eps", 0.1),
+                                        k.get("variant", 0), k.get("alpha", 0.5), k.get("iters", 10),
+                                        k.get("out", FAKE), k.get("ws", FAKE), k.get("wb", db), None)
+    assert div(x=None) == SK_ERR_NULL
+    assert div(out=None) == SK_ERR_NULL
+    assert div(eps=-1.0) == SK_ERR_EPS
+    assert div(variant=5) == SK_ERR_VARIANT
+    assert div(variant=1, alpha=2.0) == SK_ERR_VARIANT
+    assert div(iters=-2) == SK_ERR_ITERS
+    assert div(wb=db - 1) == SK_ERR_WORKSPACE
+    assert div(ws=ctypes.c_void_p(0x100040)) == SK_ERR_WORKSPACE
+
+
 def test_python_contract_errors_before_gpu():
     x = torch.zeros(4, 2, dtype=torch.float64)
     y = torch.zeros(5, 2, dtype=torch.float64)
@@ -125,6 +180,12 @@ def test_python_contract_errors_before_gpu():
         sk.solve(torch.zeros(4, 2), torch.zeros(5, 3), eps=0.1, n_iters=3)
     with pytest.raises(ValueError, match="GPU"):
         sk.grad_x(torch.zeros(4, 2), torch.zeros(5, 2), None, None, torch.zeros(5), eps=0.1)
+    with pytest.raises(ValueError, match="variant"):
+        sk.solve_ex(torch.zeros(4, 2), torch.zeros(5, 2), eps=0.1, variant="jacobi")
+    with pytest.raises(ValueError, match="stop_mode"):
+        sk.solve_ex(torch.zeros(4, 2), torch.zeros(5, 2), eps=0.1, stop_mode="residual")
+    with pytest.raises(ValueError, match="GPU"):
+        sk.divergence(torch.zeros(4, 2), torch.zeros(5, 2), eps=0.1, n_iters=3)
 
 
 def test_no_oracle_on_product_path():

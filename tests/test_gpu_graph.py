@@ -55,3 +55,43 @@ def test_graph_replay_matches_eager(case):
         for got, exp in zip((f, g, tr, c, gr), want):
             assert torch.equal(got, exp), f"replay {rep} differs from the eager step"
         _ = (X * 2.0).sum().item()  # unrelated eager work between replays
+
+
+def test_graph_replay_symmetric_dual_cost_and_divergence():
+    """Fixed-stop entry points of the other variant, the general dual cost and the
+    divergence are capturable too."""
+    x, y, a, b = random_problem(1900, 1400, 3, 78, shift=0.3)
+    eps, iters = eps32(0.05), 9
+    dev = torch.device("cuda:0")
+    X, Y, A, B = (torch.from_numpy(v).to(dev) for v in (x, y, a, b))
+    n, m, d = x.shape[0], y.shape[0], x.shape[1]
+    ws = sk.workspace(n, m, d, dev)
+    wsd = sk.divergence_workspace(n, m, d, dev)
+    f = torch.empty(n, device=dev)
+    g = torch.empty(m, device=dev)
+    c = torch.empty(1, dtype=torch.float64, device=dev)
+    dv = torch.empty(4, dtype=torch.float64, device=dev)
+
+    def step():
+        sk.solve_ex(X, Y, A, B, eps=eps, variant="symmetric", alpha=0.5, max_iter=iters, ws=ws, f=f, g=g,
+                    check=False)
+        sk.dual_cost(X, Y, A, B, f, g, eps=eps, ws=ws, out=c)
+        sk.divergence(X, Y, A, B, eps=eps, n_iters=iters, ws=wsd, out=dv, check=False)
+
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (f, g, c, dv)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        for t in (f, g):
+            t.fill_(float("nan"))
+        c.fill_(-1.0)
+        dv.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip((f, g, c, dv), want):
+            assert torch.equal(got, exp), f"replay {rep} differs from the eager step"
+        _ = (X * 2.0).sum().item()
