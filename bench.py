@@ -14,10 +14,22 @@ Printed (one JSON line):
                and gradient passes are done inside the timed step but not
                counted), over the wall-clock of the timed steps;
   roofline     the streamed-pass kernel (the dominant kernel, timed live with
-               HIP events on the launch stream) against the vector-ALU issue
+               HIP events on the launch stream around every --timing-stride-th
+               pass launch of the timed steps) against the vector-ALU issue
                ceiling of the chip (see roofline_alu);
   cpu_baseline the CPU oracle as it stands, timed on one full Sinkhorn
                iteration of the same workload on this host.
+
+Other steps (--mode, same workload and JSON fields; value counts the pair
+evaluations of the counted iterations only):
+  symmetric   sk_solve_ex, symmetric (Jacobi) variant with blend --alpha,
+              fixed n_iters, then the general dual cost sk_dual_cost;
+  marginal,   sk_solve_ex, alternating, stop rule with --stop-tol, cap n_iters,
+  potential   check every --check-every; the line adds iters_run, converged,
+              final_viol and the time of a fixed run of iters_run iterations
+              (the stop rule's overhead);
+  divergence  sk_divergence, n_iters per term: 2 n_iters (n m + n^2 + m^2)
+              pair evaluations.
 """
 from __future__ import annotations
 
@@ -155,6 +167,12 @@ def main():
                     help="capture one step into a HIP graph and time its replays (kernel timing from an eager step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device (a known-size reference for HBM byte counters)")
+    ap.add_argument("--timing-stride", type=int, default=7,
+                    help="time every k-th pass launch with HIP events (odd, so row and column passes alternate)")
+    ap.add_argument("--mode", default="solve", choices=["solve", "symmetric", "marginal", "potential", "divergence"])
+    ap.add_argument("--alpha", type=float, default=0.5, help="blend of the symmetric variant")
+    ap.add_argument("--stop-tol", type=float, default=1e-5, help="tolerance of the marginal / potential stop rule")
+    ap.add_argument("--check-every", type=int, default=10, help="check interval of the stop rules")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -172,6 +190,9 @@ def main():
         run_ceilings()
         return
 
+    if args.graph and args.mode in ("marginal", "potential"):
+        print("a stop rule synchronises at every check and cannot be captured: drop --graph", file=sys.stderr)
+        sys.exit(2)
     w = WORKLOADS[args.workload]
     n_iters = w.n_iters if args.iters is None else args.iters
     eps = eps32(w.eps)
@@ -196,11 +217,29 @@ def main():
               file=sys.stderr)
         del src, dst
 
+    mode = args.mode
+    stop = {}
+    dv_out = torch.empty(4, dtype=torch.float64, device=dev)
+    ws_div = sk.divergence_workspace(n, m, d, dev) if mode == "divergence" else None
+
     def step():
-        sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, check_every=ce, ws=ws, f=f, g=g, trace=trace, check=False)
-        sk.cost(A, B, f, g, eps=eps, out=cost_out)
-        if w.grad:
-            sk.grad_x(X, Y, A, B, g, eps=eps, ws=ws, out=grad)
+        if mode == "solve":
+            sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, check_every=ce, ws=ws, f=f, g=g, trace=trace, check=False)
+            sk.cost(A, B, f, g, eps=eps, out=cost_out)
+            if w.grad:
+                sk.grad_x(X, Y, A, B, g, eps=eps, ws=ws, out=grad)
+        elif mode == "symmetric":
+            sk.solve_ex(X, Y, A, B, eps=eps, variant="symmetric", alpha=args.alpha, max_iter=n_iters, ws=ws, f=f,
+                        g=g, check=False)
+            sk.dual_cost(X, Y, A, B, f, g, eps=eps, ws=ws, out=cost_out)
+        elif mode in ("marginal", "potential"):
+            _, _, it, conv, viol = sk.solve_ex(X, Y, A, B, eps=eps, stop_mode=mode, stop_tol=args.stop_tol,
+                                               max_iter=n_iters, check_every=args.check_every, ws=ws, f=f, g=g,
+                                               check=False)
+            stop.update(iters_run=it, converged=conv, final_viol=viol)
+            sk.cost(A, B, f, g, eps=eps, out=cost_out)
+        else:
+            sk.divergence(X, Y, A, B, eps=eps, n_iters=n_iters, ws=ws_div, out=dv_out, check=False)
 
     for _ in range(args.warmup):
         step()
@@ -209,7 +248,7 @@ def main():
     graph = None
     if args.graph:
         # pass-kernel durations from one eager step; the timed steps replay the graph
-        sk.timing_enable(True)
+        sk.timing_enable(True, args.timing_stride)
         step()
         torch.cuda.synchronize()
         pass_ms, launches, pairs = sk.timing_read()
@@ -220,7 +259,7 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
     else:
-        sk.timing_enable(True)
+        sk.timing_enable(True, args.timing_stride)
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -238,7 +277,30 @@ def main():
     wall_s = t1 - t0
     gpu_s = ev0.elapsed_time(ev1) * 1e-3
     step_s = max(wall_s, gpu_s) / args.steps
-    pair_evals = 2.0 * n * m * n_iters
+    counted_iters = stop.get("iters_run", n_iters)
+    pair_evals = 2.0 * n * m * counted_iters
+    if mode == "divergence":
+        pair_evals = 2.0 * n_iters * (n * m + n * n + m * m)
+    extra = {}
+    if mode in ("marginal", "potential"):
+        # the same iterations without checks, with the same pass timing events
+        # as the timed steps: what the stop rule costs on top
+        sk.solve_ex(X, Y, A, B, eps=eps, max_iter=counted_iters, ws=ws, f=f, g=g, check=False)
+        torch.cuda.synchronize()
+        sk.timing_enable(not args.graph, args.timing_stride)
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            sk.solve_ex(X, Y, A, B, eps=eps, max_iter=counted_iters, ws=ws, f=f, g=g, check=False)
+        torch.cuda.synchronize()
+        fixed_s = (time.perf_counter() - t2) / args.steps
+        sk.timing_enable(False)
+        extra = {"stop_mode": mode, "stop_tol": args.stop_tol, "check_every": args.check_every,
+                 "iters_run": counted_iters, "converged": stop["converged"], "final_viol": stop["final_viol"],
+                 "fixed_run_ms": fixed_s * 1e3, "stop_rule_overhead": step_s / fixed_s - 1.0}
+    elif mode == "symmetric":
+        extra = {"variant": "symmetric", "alpha": args.alpha}
+    elif mode == "divergence":
+        extra = {"divergence": [float(v) for v in dv_out.cpu()]}
     value = pair_evals / step_s
     avg_launch_s = pass_ms * 1e-3 / launches
     pairs_per_launch = pairs / launches
@@ -265,14 +327,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "n": n, "m": m, "d": d, "eps": eps, "n_iters": n_iters,
                    "check_every": ce, "grad_x": bool(w.grad), "recipe": w.description},
-        "iters_per_s": n_iters / step_s,
+        "mode": mode,
+        "iters_per_s": (3 * n_iters if mode == "divergence" else counted_iters) / step_s,
         "hip_graph": bool(args.graph),
         "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s,
         "roofline": roof,
-        "final_residual": float(trace[n_iters // ce - 1].item()) if ce else None,
-        "cost": float(cost_out.item()),
+        "final_residual": float(trace[n_iters // ce - 1].item()) if (ce and mode == "solve") else None,
+        "cost": float(cost_out.item()) if mode != "divergence" else None,
+        **extra,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and mode == "solve":
         out["cpu_baseline"] = cpu_baseline(x, y, a, b, eps, n, m)
     print(json.dumps(out), flush=True)
 

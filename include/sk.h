@@ -12,14 +12,15 @@
  *    of the current HIP device unless stated otherwise.  x is (n, d), y is
  *    (m, d), a is (n), b is (m), f is (n), g is (m).  They are owned by the
  *    caller; the library never allocates, frees or retains them.
- *  - The library never allocates device memory.  Entry points that need
+ *  - The library never allocates device memory (sk_solve_ex with a stop rule
+ *    keeps a few pinned host bytes for its check values).  Entry points that need
  *    scratch space take a workspace `ws` of at least sk_workspace_bytes(n, m, d)
  *    bytes, 256-byte aligned, owned by the caller.  A workspace may be reused
  *    by later calls once the calls that used it have completed in stream order.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Compute entry
  *    points only enqueue work and return; results are ready when the stream
  *    reaches that point.  Only sk_check_inputs, and sk_solve_ex with a stop
- *    rule, synchronise the stream.  The other compute entry points allocate
+ *    rule (at each check), wait for the stream.  The other compute entry points allocate
  *    nothing, synchronise nothing and use no memset, so they may be captured
  *    into a HIP graph and replayed (inputs, outputs and workspace at the
  *    captured addresses).
@@ -177,9 +178,14 @@ int sk_grad_x(const float *x, const float *y, const float *a, const float *b,
  *   The potential value is max(max_i |f_i - f'_i|, max_j |g_j - g'_j|) against
  *   the potentials at the previous check (zero before the first), i.e. eps
  *   times the change of the absorbed potentials f/eps; the run stops at the
- *   first check with value < stop_tol.  Each check synchronises `stream` and
- *   reads one or two floats back; calling with a stop rule on a stream under
- *   graph capture returns SK_ERR_CAPTURE before anything is enqueued.  The
+ *   first check with value < stop_tol.  At each check the host waits until
+ *   `stream` has produced that check's value: the GPU stores it straight into
+ *   pinned, mapped host memory and raises a flag there, which the host polls
+ *   (a 64-byte slot per call in flight, allocated with hipHostMalloc on first
+ *   need and kept by the library for the life of the process).  Work the
+ *   caller enqueued on `stream` before the call is waited for as well.
+ *   Calling with a stop rule on a stream under graph capture returns
+ *   SK_ERR_CAPTURE before anything is enqueued.  The
  *   marginal value of iteration k is produced by the passes of iteration
  *   k + 1, so a check costs no extra pass except after the last iteration.
  * Outputs: f, g (device) hold the potentials after *iters_run iterations;
@@ -228,16 +234,18 @@ int sk_divergence(const float *x, const float *y, const float *a, const float *b
 
 /*
  * Kernel timing of the streamed log-sum-exp passes (benchmark diagnostics).
- * sk_timing_enable(1) resets the counters and from then on records a HIP
- * event pair on the launch stream around every streamed-pass kernel that
- * the solve, cost and residual entry points enqueue (the split merge and the other
- * kernels are outside the pair); sk_timing_enable(0) stops recording.
- * sk_timing_read waits for the recorded events and returns the total kernel
- * milliseconds, the number of launches and the number of (query, key) pairs
- * those launches evaluated.  Launches enqueued while the stream is being
- * captured into a graph are not timed.  Events come from a process-wide pool that grows
- * on demand; calls from several threads at once are serialised.  Returns
- * SK_ERR_NULL for NULL outputs, SK_ERR_HIP on a HIP failure.
+ * sk_timing_enable(k) with k >= 1 resets the counters and from then on records
+ * a HIP event pair on the launch stream around every k-th streamed-pass kernel
+ * that the solve, cost and residual entry points enqueue (k = 1: every one;
+ * a larger k keeps the host cost of the events off small problems); the split
+ * merge and the other kernels are outside the pairs.  sk_timing_enable(0)
+ * stops recording.  sk_timing_read waits for the recorded events and returns
+ * the total kernel milliseconds, the number of timed launches and the number
+ * of (query, key) pairs those launches evaluated.  Launches enqueued while the
+ * stream is being captured into a graph are not timed (nor counted).  Events
+ * come from a process-wide pool that grows on demand; calls from several
+ * threads at once are serialised.  Returns SK_ERR_NULL for NULL outputs,
+ * SK_ERR_HIP on a HIP failure.
  */
 int sk_timing_enable(int enable);
 int sk_timing_read(double *total_ms, int64_t *launches, double *pairs);

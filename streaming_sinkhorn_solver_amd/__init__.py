@@ -308,9 +308,12 @@ def grad_x(x, y, a, b, g, *, eps: float, ws: torch.Tensor | None = None,
     return out
 
 
-def timing_enable(enable: bool = True) -> None:
-    """Start (reset) or stop event timing of the streamed-pass kernels."""
-    _raise(load_library().sk_timing_enable(1 if enable else 0), "sk_timing_enable")
+def timing_enable(enable: bool = True, stride: int = 1) -> None:
+    """Start (reset) or stop event timing of the streamed-pass kernels; every
+    stride-th pass launch is timed."""
+    if stride < 1:
+        raise ValueError("stride must be >= 1")
+    _raise(load_library().sk_timing_enable(int(stride) if enable else 0), "sk_timing_enable")
 
 
 def timing_read() -> tuple[float, int, float]:

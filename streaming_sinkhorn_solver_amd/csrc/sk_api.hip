@@ -6,6 +6,7 @@
 #include "sk_internal.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 #include <cmath>
 #include <cstring>
@@ -168,6 +169,8 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
 struct Timing {
     std::mutex mu;
     bool on = false;
+    int stride = 1;                // time every stride-th pass launch
+    int64_t seen = 0;              // pass launches since enable
     std::vector<hipEvent_t> pool;  // pairs: [2k] start, [2k + 1] stop
     size_t used = 0;               // pairs recorded since enable
     double pairs = 0.0;
@@ -185,7 +188,8 @@ int run_pass(const Ws& W, const PassArgs& p, hipStream_t s) {
     if (hipStreamIsCapturing(s, &cap) != hipSuccess) return SK_ERR_HIP;
     {
         std::lock_guard<std::mutex> lk(T.mu);
-        if (T.on && cap == hipStreamCaptureStatusNone) {  // no event nodes inside a captured graph
+        // no event nodes inside a captured graph
+        if (T.on && cap == hipStreamCaptureStatusNone && (T.seen++ % T.stride) == 0) {
             while (T.pool.size() < 2 * (T.used + 1)) {
                 hipEvent_t e;
                 SK_TRY(hipEventCreate(&e));
@@ -245,7 +249,6 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.lse_c2 = take(um * 4);
     L.snap_f = take(un * 4);
     L.snap_g = take(um * 4);
-    L.chkf = take(8 * sizeof(float));
     L.total = off;
     return L;
 }
@@ -270,12 +273,77 @@ struct ExResult {
     float viol;      // NaN when no check ran
 };
 
-// Reads n floats of the workspace back to the host (waits for the stream).
-int read_back(const float* dev, float* host, int n, hipStream_t s) {
-    SK_TRY(hipMemcpyAsync(host, dev, (size_t)n * sizeof(float), hipMemcpyDeviceToHost, s));
-    SK_TRY(hipStreamSynchronize(s));
-    return SK_OK;
+// Check values travel through pinned, mapped host memory: the reduction kernel
+// stores them there directly, then raises a sequence flag behind a
+// system-scope fence, and the host polls the flag instead of synchronising
+// the stream (a stream synchronisation costs far more than a small pass).
+// The poll also asks the stream whether it is idle, so it ends even if the
+// flag never comes (a failed launch).  Slots of 16 words are taken from a pool
+// that grows on demand (one slot per call in flight) and is kept for the life
+// of the process.
+constexpr int kSlotWords = 16;
+constexpr int kFlagWord = kSlotWords - 1;
+
+struct HostSlots {
+    std::mutex mu;
+    std::vector<float*> free;
+};
+HostSlots& host_slots() {
+    static HostSlots h;
+    return h;
 }
+
+class HostSlot {
+  public:
+    int acquire() {
+        HostSlots& H = host_slots();
+        std::lock_guard<std::mutex> lk(H.mu);
+        if (!H.free.empty()) {
+            host_ = H.free.back();
+            H.free.pop_back();
+        } else if (hipHostMalloc(reinterpret_cast<void**>(&host_), kSlotWords * sizeof(float),
+                                 hipHostMallocMapped | hipHostMallocPortable | hipHostMallocCoherent) != hipSuccess) {
+            host_ = nullptr;
+            return SK_ERR_HIP;
+        }
+        if (hipHostGetDevicePointer(reinterpret_cast<void**>(&dev_), host_, 0) != hipSuccess) return SK_ERR_HIP;
+        seq_ = reinterpret_cast<volatile int*>(host_)[kFlagWord];
+        return SK_OK;
+    }
+    ~HostSlot() {
+        if (!host_) return;
+        HostSlots& H = host_slots();
+        std::lock_guard<std::mutex> lk(H.mu);
+        H.free.push_back(host_);
+    }
+    float* dev() const { return dev_; }
+    int* flag() const { return reinterpret_cast<int*>(dev_ + kFlagWord); }
+    // the sequence number the next check's kernel raises
+    int next() { return ++seq_; }
+    // waits until the check numbered seq_ has been published, then reads it
+    int read(float* out, int n, hipStream_t s) const {
+        volatile int* f = reinterpret_cast<volatile int*>(host_) + kFlagWord;
+        for (;;) {
+            bool seen = false;
+            for (int k = 0; k < 4096 && !seen; ++k) seen = *f == seq_;
+            if (seen) break;
+            const hipError_t q = hipStreamQuery(s);
+            if (q == hipSuccess) {
+                if (*f != seq_) return SK_ERR_HIP;  // stream idle without the flag
+                break;
+            }
+            if (q != hipErrorNotReady) return SK_ERR_HIP;
+        }
+        std::atomic_thread_fence(std::memory_order_acquire);
+        for (int k = 0; k < n; ++k) out[k] = reinterpret_cast<volatile float*>(host_)[k];
+        return SK_OK;
+    }
+
+  private:
+    float* host_ = nullptr;
+    float* dev_ = nullptr;
+    int seq_ = 0;
+};
 
 // Sinkhorn with an update variant and a stop rule (SinkSLOT README, API
 // Reference).  Iteration k of the alternating variant is a row pass from the
@@ -325,7 +393,9 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
         col.fin.bias_packed = col.fin.bias_sep = nullptr;
     }
     float* rbuf = W.f(L.rbuf);
-    float* chk = W.f(L.chkf);
+    HostSlot slot;
+    if (o.stop_mode != 0 && (st = slot.acquire())) return st;
+    float* chk = slot.dev();
     float host[2] = {0.0f, 0.0f};
     if (o.stop_mode == 2) {
         SK_TRY(launch_fill(W.f(L.snap_f), L.n, 0.0f, s));
@@ -347,9 +417,13 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
         row.fin.lse_out = fused ? ur[cr ^ 1] : ur[cr];
         row.fin.rbuf = fused ? rbuf : nullptr;
         if ((st = run_pass(W, row, s))) return st;
-        if (fused) SK_TRY(launch_resid_reduce(rbuf, (int)L.n, chk + 0, nullptr, s));
+        if (fused) {
+            const bool last = !sym;  // the row value alone is the check
+            SK_TRY(launch_resid_reduce(rbuf, (int)L.n, chk + 0, nullptr, s, last ? slot.flag() : nullptr,
+                                       last ? slot.next() : 0));
+        }
         if (fused && !sym) {
-            if ((st = read_back(chk, host, 1, s))) return st;
+            if ((st = slot.read(host, 1, s))) return st;
             res->viol = host[0];
             if (host[0] <= o.tol) return stop_at(k - 1, true, false);
             cr ^= 1;
@@ -360,8 +434,8 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
         col.fin.rbuf = fused_col ? rbuf : nullptr;
         if ((st = run_pass(W, col, s))) return st;
         if (fused_col) {
-            SK_TRY(launch_resid_reduce(rbuf, (int)L.m, chk + 1, nullptr, s));
-            if ((st = read_back(chk, host, 2, s))) return st;
+            SK_TRY(launch_resid_reduce(rbuf, (int)L.m, chk + 1, nullptr, s, slot.flag(), slot.next()));
+            if ((st = slot.read(host, 2, s))) return st;
             res->viol = std::max(host[0], host[1]);
             if (res->viol <= o.tol) return stop_at(k - 1, true, true);
             cr ^= 1;
@@ -373,8 +447,9 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
             SK_TRY(launch_apply_bias(bx, by, L.P, L.d, s));
         }
         if (o.stop_mode == 2 && is_check(k)) {
-            SK_TRY(launch_pot_change(f, W.f(L.snap_f), (int)L.n, g, W.f(L.snap_g), (int)L.m, chk, s));
-            if ((st = read_back(chk, host, 1, s))) return st;
+            SK_TRY(launch_pot_change(f, W.f(L.snap_f), (int)L.n, g, W.f(L.snap_g), (int)L.m, chk, s, slot.flag(),
+                                     slot.next()));
+            if ((st = slot.read(host, 1, s))) return st;
             res->viol = host[0];
             if (host[0] < o.tol) return stop_at(k, false, false);
         }
@@ -385,7 +460,8 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
         probe.fin.lse = ur[cr];
         probe.fin.rbuf = rbuf;
         if ((st = run_pass(W, probe, s))) return st;
-        SK_TRY(launch_resid_reduce(rbuf, (int)L.n, chk + 0, nullptr, s));
+        SK_TRY(launch_resid_reduce(rbuf, (int)L.n, chk + 0, nullptr, s, sym ? nullptr : slot.flag(),
+                                   sym ? 0 : slot.next()));
         int cnt = 1;
         if (sym) {
             probe = col;
@@ -393,10 +469,10 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
             probe.fin.lse = uc[cc];
             probe.fin.rbuf = rbuf;
             if ((st = run_pass(W, probe, s))) return st;
-            SK_TRY(launch_resid_reduce(rbuf, (int)L.m, chk + 1, nullptr, s));
+            SK_TRY(launch_resid_reduce(rbuf, (int)L.m, chk + 1, nullptr, s, slot.flag(), slot.next()));
             cnt = 2;
         }
-        if ((st = read_back(chk, host, cnt, s))) return st;
+        if ((st = slot.read(host, cnt, s))) return st;
         res->viol = cnt == 2 ? std::max(host[0], host[1]) : host[0];
         if (res->viol <= o.tol) res->converged = 1;
     }
@@ -480,7 +556,9 @@ const char* sk_status_string(int status) {
 int sk_timing_enable(int enable) {
     Timing& T = timing();
     std::lock_guard<std::mutex> lk(T.mu);
-    T.on = enable != 0;
+    T.on = enable > 0;
+    T.stride = enable > 0 ? enable : 1;
+    T.seen = 0;
     T.used = 0;
     T.pairs = 0.0;
     return SK_OK;

@@ -135,7 +135,6 @@ struct Layout {
     size_t xp, yp, hx, hy, nx, ny, l2a, l2b, lse_r, lse_c, rbuf, part, partA, red, cen, centre, chk;
     size_t lse_r2, lse_c2;    // second state buffers (a check keeps the previous state)
     size_t snap_f, snap_g;    // potentials at the previous check (potential stop rule)
-    size_t chkf;              // a few floats read back by the host at a check
     size_t total;
 };
 
@@ -166,8 +165,9 @@ hipError_t launch_apply_bias(const BiasSide& x, const BiasSide& y, int P, int d,
 hipError_t launch_pot_from_state(const float* u, const float* nrm, float eps_ln2, float* pot, int npts,
                                  hipStream_t s);
 // out[0] = max(max_i |f_i - sf_i|, max_j |g_j - sg_j|), then sf = f, sg = g.
+// flag (may be null): set to seq once out[0] is visible to the host.
 hipError_t launch_pot_change(const float* f, float* sf, int n, const float* g, float* sg, int m, float* out,
-                             hipStream_t s);
+                             hipStream_t s, int* flag = nullptr, int seq = 0);
 // mass (may be null): per-row plan sums (P1)_i; the cost then uses their float64
 // sum as the plan mass instead of sum(b).
 hipError_t launch_cost_mass(const float* a, const float* b, const float* f, const float* g, const float* mass,
@@ -178,8 +178,9 @@ hipError_t launch_check(const float* x, const float* y, const float* a, const fl
                         int d, double* partials, double* result, hipStream_t s);
 hipError_t launch_cost(const float* a, const float* b, const float* f, const float* g, int n, int m,
                        float eps, double* out, hipStream_t s);
-hipError_t launch_resid_reduce(const float* rbuf, int cnt, float* out_max, float* out_sum,
-                               hipStream_t s);
+// flag (may be null): set to seq once out_max[0] is visible to the host.
+hipError_t launch_resid_reduce(const float* rbuf, int cnt, float* out_max, float* out_sum, hipStream_t s,
+                               int* flag = nullptr, int seq = 0);
 // Vector-ALU passes (d <= 8): a streamed pass, plus the exact merge of the
 // split partials when nsplit > 1.
 // ev0 / ev1 (may be null): events recorded on s right before and right after

@@ -209,9 +209,20 @@ __global__ __launch_bounds__(1024) void k_cost(const float* __restrict__ a, cons
 }
 
 // Largest change of the potentials since the snapshot, then the snapshot is refreshed.
+// A check value may go to host memory: then `flag` (may be null) is set to
+// `seq` after it, behind a system-scope fence, so a host that sees the flag
+// sees the value.
+__device__ inline void publish(float* out, float v, int* flag, int seq) {
+    out[0] = v;
+    if (flag) {
+        __threadfence_system();
+        reinterpret_cast<volatile int*>(flag)[0] = seq;
+    }
+}
+
 __global__ __launch_bounds__(1024) void k_pot_change(const float* __restrict__ f, float* __restrict__ sf, int n,
                                                      const float* __restrict__ g, float* __restrict__ sg, int m,
-                                                     float* __restrict__ out) {
+                                                     float* __restrict__ out, int* flag, int seq) {
     __shared__ float shf[1024];
     float mx = 0.0f;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(1024) void k_pot_change(const float* __restrict__ f
         sg[j] = v;
     }
     mx = block_max_f32(mx, shf);
-    if (threadIdx.x == 0) out[0] = mx;
+    if (threadIdx.x == 0) publish(out, mx, flag, seq);
 }
 
 __global__ void k_div_combine(double* out) {
@@ -235,7 +246,7 @@ __global__ void k_div_combine(double* out) {
 // Residual reduction: max and float64 sum of |r_i|.
 __global__ __launch_bounds__(1024) void k_resid_reduce(const float* __restrict__ r, int cnt,
                                                        float* __restrict__ out_max,
-                                                       float* __restrict__ out_sum) {
+                                                       float* __restrict__ out_sum, int* flag, int seq) {
     __shared__ double sh[1024];
     __shared__ float shf[1024];
     float mx = 0.0f;
@@ -248,8 +259,8 @@ __global__ __launch_bounds__(1024) void k_resid_reduce(const float* __restrict__
     mx = block_max_f32(mx, shf);
     sm = block_sum_f64(sm, sh);
     if (threadIdx.x == 0) {
-        out_max[0] = mx;
         if (out_sum) out_sum[0] = (float)sm;
+        publish(out_max, mx, flag, seq);
     }
 }
 
@@ -289,8 +300,8 @@ hipError_t launch_pot_from_state(const float* u, const float* nrm, float eps_ln2
 }
 
 hipError_t launch_pot_change(const float* f, float* sf, int n, const float* g, float* sg, int m, float* out,
-                             hipStream_t s) {
-    hipLaunchKernelGGL(k_pot_change, dim3(1), dim3(1024), 0, s, f, sf, n, g, sg, m, out);
+                             hipStream_t s, int* flag, int seq) {
+    hipLaunchKernelGGL(k_pot_change, dim3(1), dim3(1024), 0, s, f, sf, n, g, sg, m, out, flag, seq);
     return hipGetLastError();
 }
 
@@ -328,8 +339,9 @@ hipError_t launch_cost(const float* a, const float* b, const float* f, const flo
     return hipGetLastError();
 }
 
-hipError_t launch_resid_reduce(const float* rbuf, int cnt, float* out_max, float* out_sum, hipStream_t s) {
-    hipLaunchKernelGGL(k_resid_reduce, dim3(1), dim3(1024), 0, s, rbuf, cnt, out_max, out_sum);
+hipError_t launch_resid_reduce(const float* rbuf, int cnt, float* out_max, float* out_sum, hipStream_t s,
+                               int* flag, int seq) {
+    hipLaunchKernelGGL(k_resid_reduce, dim3(1), dim3(1024), 0, s, rbuf, cnt, out_max, out_sum, flag, seq);
     return hipGetLastError();
 }
 
