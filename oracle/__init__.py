@@ -18,7 +18,8 @@ Passages followed (page title and section):
     legal) and API Reference (alternating and symmetric variants, the fixed,
     marginal and potential stop modes, the infinity-norm marginal residual),
     Low-Level Solver API (iters_run, converged, final_viol), and the opening
-    section (entropic OT is not zero at (x, x): the debiased divergence).
+    section (entropic OT is not zero at (x, x): the debiased divergence), Gradient Flow (descent on the
+    analytic gradient).
 Pins: every function here is checked in tests/test_oracle_pins.py against
 closed forms, a textbook matrix-scaling route, library routines and brute
 force; none is pinned only against itself.
@@ -80,6 +81,9 @@ def load(path: str | None = None):
         lib.oracle_sinkhorn_ex.restype = None
         lib.oracle_divergence.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, i32, dbl, i32, _dp]
         lib.oracle_divergence.restype = None
+        lib.oracle_gradient_flow.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, i32, i32, dbl, _dp, _dp, _dp,
+                                             _dp]
+        lib.oracle_gradient_flow.restype = None
         lib.oracle_grad_x.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, _dp, _i64p, i64, _dp]
         lib.oracle_grad_x.restype = None
         lib.oracle_dual_cost.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, _dp, _dp]
@@ -221,6 +225,22 @@ def grad_x(x, y, a, b, g, eps: float, idx=None, lib=None) -> np.ndarray:
         lib.oracle_grad_x(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, y.shape[0], d, float(eps), _ptr(g),
                           ix.ctypes.data_as(_i64p), ix.size, _ptr(out))
     return out
+
+
+def gradient_flow(x, y, a, b, eps: float, n_iters: int, n_steps: int, lr: float, lib=None):
+    """n_steps of x <- x - lr * grad_x, each at a fresh n_iters-iteration solve.
+
+    Returns (x_final, cost_trace, f, g, grad) with f, g, grad of the last step."""
+    lib = lib or load()
+    x = _cloud(x).copy()
+    y, a, b = _cloud(y), _f64(a), _f64(b)
+    n, d = x.shape
+    m = y.shape[0]
+    f, g, grad = np.empty(n), np.empty(m), np.empty((n, d))
+    trace = np.empty(max(n_steps, 1))
+    lib.oracle_gradient_flow(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), int(n_steps),
+                             float(lr), _ptr(trace), _ptr(f), _ptr(g), _ptr(grad))
+    return x, trace[:n_steps], f, g, grad
 
 
 def dual_cost(x, y, a, b, f, g, eps: float, lib=None) -> float:

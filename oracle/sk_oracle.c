@@ -37,6 +37,8 @@
  *    for iters_run, converged and final_viol.
  *  - SinkSLOT README, opening section: entropic OT is not zero at (x, x), so
  *    a divergence built from it subtracts the two self-terms.
+ *  - SinkSLOT README, Gradient Flow: plain descent x <- x - lr * grad on the
+ *    analytic gradient, with a fresh solve at every step.
  * Readings where the pages are silent: g starts at 0 and each iteration is an
  * f half-step followed by a g half-step; the cost is the entropic dual
  * objective D(f,g) = <a,f> + <b,g> - eps * sum_ij a_i b_j (e^{(f_i+g_j-C_ij)/eps} - 1).
@@ -393,6 +395,29 @@ void oracle_divergence(const double *x, const double *y, const double *a, const 
     out[3] = t_yy;
     free(f);
     free(g);
+}
+
+/*
+ * Gradient flow of the entropic cost in x (SinkSLOT README, Gradient Flow: an
+ * explicit descent loop on the analytic gradient).  Each of the n_steps steps
+ * solves afresh from g = 0 with n_iters alternating iterations at the current
+ * x, takes the barycentric gradient at the final g, and moves
+ * x <- x - lr * grad.  x (n x d) is updated in place; f, g and grad are those
+ * of the last step (at the x before its move); cost_trace[k] (if not NULL) is
+ * the dual cost at step k's potentials.
+ */
+void oracle_gradient_flow(double *x, const double *y, const double *a, const double *b,
+                          int64_t n, int64_t m, int d, double eps, int n_iters, int n_steps, double lr,
+                          double *cost_trace, double *f, double *g, double *grad)
+{
+    for (int k = 0; k < n_steps; ++k) {
+        oracle_sinkhorn(x, y, a, b, n, m, d, eps, n_iters, 0, NULL, f, g, NULL);
+        if (cost_trace)
+            cost_trace[k] = oracle_dual_cost(x, y, a, b, n, m, d, eps, f, g);
+        oracle_grad_x(x, y, a, b, n, m, d, eps, g, NULL, n, grad);
+        for (int64_t e = 0; e < n * d; ++e)
+            x[e] -= lr * grad[e];
+    }
 }
 
 /* max_ij C_ij over all pairs (the scale of the parity tolerance). */

@@ -441,6 +441,57 @@ def pin_divergence_symmetric_positive(lib):
     assert Sxy > 0.0
 
 
+# ---- gradient flow (SinkSLOT README, Gradient Flow)
+def pin_flow_single_target(lib):
+    """One target point: w_i1 = 1, so grad_i = 2 a_i (x_i - y) and each point decays geometrically,
+    x_i^K - y = (1 - 2 lr a_i)^K (x_i^0 - y); the cost at step k is sum_i a_i |x_i^k - y|^2."""
+    rng = np.random.default_rng(261)
+    x0 = rng.normal(size=(7, 3))
+    y = np.array([[0.4, -0.2, 1.1]])
+    a = rng.exponential(size=7)
+    a /= a.sum()
+    lr, K = 0.3, 6
+    xK, trace, f, g, grad = oracle.gradient_flow(x0, y, a, np.ones(1), 0.2, 4, K, lr, lib=lib)
+    decay = (1.0 - 2.0 * lr * a)[:, None]
+    assert np.allclose(xK - y, decay ** K * (x0 - y), rtol=0, atol=1e-13)
+    for k in range(K):
+        xk = y + decay ** k * (x0 - y)
+        assert trace[k] == pytest.approx((a * ((xk - y) ** 2).sum(axis=1)).sum(), rel=1e-12)
+    x_last = y + decay ** (K - 1) * (x0 - y)
+    assert np.allclose(grad, 2 * a[:, None] * (x_last - y), rtol=0, atol=1e-13)
+
+
+def pin_flow_steps_compose(lib):
+    """Two steps equal two explicit moves, each with its own solve from g = 0 (no warm start);
+    the returned f, g, grad are the last step's."""
+    x0, y, a, b = _problem(8, 6, 2, 271)
+    eps, iters, lr = 0.3, 3, 0.7
+    x = x0.copy()
+    for _ in range(2):
+        f, g, _ = oracle.sinkhorn(x, y, a, b, eps, iters, lib=lib)
+        grad = oracle.grad_x(x, y, a, b, g, eps, lib=lib)
+        x_prev, x = x, x - lr * grad
+    xK, trace, fK, gK, gradK = oracle.gradient_flow(x0, y, a, b, eps, iters, 2, lr, lib=lib)
+    assert np.allclose(xK, x, rtol=0, atol=1e-13)
+    assert np.allclose(fK, f, rtol=0, atol=1e-13) and np.allclose(gK, g, rtol=0, atol=1e-13)
+    assert np.allclose(gradK, grad, rtol=0, atol=1e-13)
+    assert trace[1] == pytest.approx(oracle.dual_cost(x_prev, y, a, b, f, g, eps, lib=lib), rel=1e-12)
+
+
+def pin_flow_mean_converged(lib):
+    """Uniform weights and converged solves: the plan's column sums are b, so the gradients sum to
+    2 (mean x - mean y) and the mean gap shrinks by exactly (1 - 2 lr / n) per step."""
+    rng = np.random.default_rng(281)
+    n, m = 6, 5
+    x0 = rng.normal(size=(n, 2))
+    y = rng.normal(size=(m, 2)) + 1.5
+    a, b = np.full(n, 1 / n), np.full(m, 1 / m)
+    lr, K = 0.5, 4
+    xK, *_ = oracle.gradient_flow(x0, y, a, b, 2.0, 3000, K, lr, lib=lib)
+    gap0 = x0.mean(axis=0) - y.mean(axis=0)
+    assert np.allclose(xK.mean(axis=0) - y.mean(axis=0), (1 - 2 * lr / n) ** K * gap0, rtol=0, atol=1e-12)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -493,6 +544,15 @@ MUTANTS = {
     "marginal_col_only": ("viol = r[0] > r[1] ? r[0] : r[1];", "viol = r[1];", 1),
     "div_full_self": ("out[0] = t_xy - 0.5 * t_xx - 0.5 * t_yy;", "out[0] = t_xy - t_xx - t_yy;", 1),
     "div_self_x_twice": ("oracle_sinkhorn_ex(y, y, b, b, m, m,", "oracle_sinkhorn_ex(x, x, a, a, n, n,", 1),
+    "flow_warm_start": ("oracle_sinkhorn(x, y, a, b, n, m, d, eps, n_iters, 0, NULL, f, g, NULL);",
+                        "oracle_sinkhorn(x, y, a, b, n, m, d, eps, n_iters, 0, k ? g : NULL, f, g, NULL);", 1),
+    "flow_ascent": ("x[e] -= lr * grad[e];", "x[e] += lr * grad[e];", 1),
+    "flow_cost_after_move": ("        if (cost_trace)\n            cost_trace[k] = oracle_dual_cost(x, y, a, b, n, m, d, eps, f, g);\n"
+                             "        oracle_grad_x(x, y, a, b, n, m, d, eps, g, NULL, n, grad);\n"
+                             "        for (int64_t e = 0; e < n * d; ++e)\n            x[e] -= lr * grad[e];",
+                             "        oracle_grad_x(x, y, a, b, n, m, d, eps, g, NULL, n, grad);\n"
+                             "        for (int64_t e = 0; e < n * d; ++e)\n            x[e] -= lr * grad[e];\n"
+                             "        if (cost_trace)\n            cost_trace[k] = oracle_dual_cost(x, y, a, b, n, m, d, eps, f, g);", 1),
     "trace_row_only": ("resid_trace[k / check_every - 1] = r[0] > r[1] ? r[0] : r[1];",
                        "resid_trace[k / check_every - 1] = r[1];", 1),
 }
