@@ -29,7 +29,10 @@ evaluations of the counted iterations only):
               final_viol and the time of a fixed run of iters_run iterations
               (the stop rule's overhead);
   divergence  sk_divergence, n_iters per term: 2 n_iters (n m + n^2 + m^2)
-              pair evaluations.
+              pair evaluations;
+  flow        one step of the gradient flow (sk_gradient_flow with one step:
+              fresh solve of n_iters iterations, cost, gradient, x <- x - lr
+              grad, x updated in place); --graph replays it as a HIP graph.
 """
 from __future__ import annotations
 
@@ -169,7 +172,9 @@ def main():
                     help="first copy MIB MiB device-to-device (a known-size reference for HBM byte counters)")
     ap.add_argument("--timing-stride", type=int, default=7,
                     help="time every k-th pass launch with HIP events (odd, so row and column passes alternate)")
-    ap.add_argument("--mode", default="solve", choices=["solve", "symmetric", "marginal", "potential", "divergence"])
+    ap.add_argument("--mode", default="solve",
+                    choices=["solve", "symmetric", "marginal", "potential", "divergence", "flow"])
+    ap.add_argument("--lr", type=float, default=0.1, help="step size of the gradient flow")
     ap.add_argument("--alpha", type=float, default=0.5, help="blend of the symmetric variant")
     ap.add_argument("--stop-tol", type=float, default=1e-5, help="tolerance of the marginal / potential stop rule")
     ap.add_argument("--check-every", type=int, default=10, help="check interval of the stop rules")
@@ -238,6 +243,9 @@ def main():
                                                check=False)
             stop.update(iters_run=it, converged=conv, final_viol=viol)
             sk.cost(A, B, f, g, eps=eps, out=cost_out)
+        elif mode == "flow":
+            sk.gradient_flow(X, Y, A, B, eps=eps, n_iters=n_iters, n_steps=1, lr=args.lr, ws=ws, f=f, g=g,
+                             grad=grad, cost_trace=cost_out, check=False)
         else:
             sk.divergence(X, Y, A, B, eps=eps, n_iters=n_iters, ws=ws_div, out=dv_out, check=False)
 
@@ -301,12 +309,16 @@ def main():
         extra = {"variant": "symmetric", "alpha": args.alpha}
     elif mode == "divergence":
         extra = {"divergence": [float(v) for v in dv_out.cpu()]}
+    elif mode == "flow":
+        extra = {"lr": args.lr, "flow_steps_per_s": 1.0 / step_s,
+                 "flow_steps_run": args.warmup + args.steps + (1 if args.graph else 0) * 2}
     value = pair_evals / step_s
     avg_launch_s = pass_ms * 1e-3 / launches
     pairs_per_launch = pairs / launches
     if d <= 8:
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
-        roof["kernel"] = f"k_pass_valu<{d}>"
+        small = pairs_per_launch <= 2.0e6  # the library's single-kernel path for small passes
+        roof["kernel"] = f"k_pass_small<{d}>" if small else f"k_pass_valu<{d}>"
     else:
         roof = roofline_mfma(d, pairs_per_launch, avg_launch_s)
         roof["kernel"] = "k_pass_mfma<%d>" % max(16, 1 << (d - 1).bit_length())

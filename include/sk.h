@@ -38,8 +38,8 @@
  * Sources (page title and section):
  *  FS   = "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",
  *         technical summary, Methodology 1-3.
- *  SLOT = SinkSLOT README: opening section, Tensor Contract, API Reference,
- *         Low-Level Solver API.
+ *  SLOT = SinkSLOT README: opening section, Tensor Contract, Gradient Flow,
+ *         API Reference, Low-Level Solver API.
  */
 #ifndef SK_H
 #define SK_H
@@ -68,7 +68,8 @@ typedef enum sk_status {
     SK_ERR_VARIANT = 13,       /* variant not 0 or 1, or symmetric with alpha outside (0, 1] */
     SK_ERR_STOP = 14,          /* stop_mode not 0, 1 or 2; or a stop rule with stop_tol < 0,
                                   non-finite, or check_every < 1 */
-    SK_ERR_CAPTURE = 15        /* a stop rule was asked for on a stream under graph capture */
+    SK_ERR_CAPTURE = 15,       /* a stop rule was asked for on a stream under graph capture */
+    SK_ERR_LR = 16             /* the gradient-flow step size is not finite */
 } sk_status;
 
 /* Version of this ABI (incremented on any signature change). */
@@ -231,6 +232,23 @@ int sk_divergence(const float *x, const float *y, const float *a, const float *b
                   int64_t n, int64_t m, int32_t d, float eps,
                   int32_t variant, float alpha, int32_t n_iters, double *out,
                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Gradient flow of the entropic cost in x (SLOT, Gradient Flow: explicit
+ * descent on the analytic gradient).  Each of the n_steps steps enqueues a
+ * fresh sk_solve of n_iters iterations at the current x (from g = 0), the
+ * gradient sk_grad_x at the resulting g, and the move x <- x - lr * grad.
+ * x (n, d, device) is updated in place.  On return f, g and grad (n, d) hold
+ * the last step's potentials and gradient, taken at the x before its move;
+ * cost_trace (device doubles, n_steps entries, or NULL) receives each step's
+ * sk_cost.  n_steps = 0 leaves everything untouched.  ws as for
+ * sk_workspace_bytes(n, m, d).  Enqueues only (capturable into a graph).
+ */
+int sk_gradient_flow(float *x, const float *y, const float *a, const float *b,
+                     int64_t n, int64_t m, int32_t d, float eps,
+                     int32_t n_iters, int32_t n_steps, float lr,
+                     float *f, float *g, float *grad, double *cost_trace,
+                     void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Kernel timing of the streamed log-sum-exp passes (benchmark diagnostics).

@@ -29,9 +29,9 @@ _STATUS_NAMES = {
     0: "SK_OK", 1: "SK_ERR_NULL", 2: "SK_ERR_SHAPE", 3: "SK_ERR_UNSUPPORTED_D", 4: "SK_ERR_EPS",
     5: "SK_ERR_ITERS", 6: "SK_ERR_CHECK_EVERY", 7: "SK_ERR_NEG_WEIGHT", 8: "SK_ERR_MASS_MISMATCH",
     9: "SK_ERR_EMPTY_MEASURE", 10: "SK_ERR_NONFINITE", 11: "SK_ERR_WORKSPACE", 12: "SK_ERR_HIP",
-    13: "SK_ERR_VARIANT", 14: "SK_ERR_STOP", 15: "SK_ERR_CAPTURE",
+    13: "SK_ERR_VARIANT", 14: "SK_ERR_STOP", 15: "SK_ERR_CAPTURE", 16: "SK_ERR_LR",
 }
-_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 13, 14, 15}
+_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 13, 14, 15, 16}
 
 # SinkSLOT README, API Reference: variant and stop_mode names
 VARIANTS = {"alternating": 0, "symmetric": 1}
@@ -57,6 +57,8 @@ SIGNATURES = {
     "sk_divergence_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "sk_divergence": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _f32, _i32, _vp, _vp, _sz,
                                      _vp]),
+    "sk_gradient_flow": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _i32, _f32, _vp, _vp, _vp,
+                                        _vp, _vp, _sz, _vp]),
     "sk_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "sk_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_double)]),
@@ -263,6 +265,34 @@ def divergence(x, y, a=None, b=None, *, eps: float, n_iters: int, variant: str =
     return out
 
 
+def gradient_flow(x, y, a=None, b=None, *, eps: float, n_iters: int, n_steps: int, lr: float,
+                  ws: torch.Tensor | None = None, f: torch.Tensor | None = None, g: torch.Tensor | None = None,
+                  grad: torch.Tensor | None = None, cost_trace: torch.Tensor | None = None, check: bool = True):
+    """n_steps of x <- x - lr * grad_x, each at a fresh n_iters-iteration solve; x is updated in place.
+
+    Returns (x, f, g, grad, cost_trace): f, g, grad of the last step, cost_trace (float64, n_steps) of
+    every step."""
+    lib = load_library()
+    x_in = x
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    if x.data_ptr() != x_in.data_ptr():
+        raise ValueError("x is updated in place and must be contiguous")
+    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    if check:
+        check_inputs(x, y, a, b, ws)
+    f = f if f is not None else torch.empty(n, dtype=torch.float32, device=x.device)
+    g = g if g is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+    grad = grad if grad is not None else torch.empty((n, d), dtype=torch.float32, device=x.device)
+    if cost_trace is None:
+        cost_trace = torch.empty(max(n_steps, 1), dtype=torch.float64, device=x.device)
+    elif cost_trace.numel() < n_steps or cost_trace.dtype != torch.float64:
+        raise ValueError(f"cost_trace must hold {n_steps} float64 values")
+    _raise(lib.sk_gradient_flow(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), int(n_steps),
+                                float(lr), _ptr(f), _ptr(g), _ptr(grad), _ptr(cost_trace), _ptr(ws), ws.numel(),
+                                _stream(x.device)), "sk_gradient_flow")
+    return x, f, g, grad, cost_trace[:n_steps]
+
+
 def cost(a, b, f, g, *, eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
     """<a,f> + <b,g> - eps sum(b)(1 - sum(a)) in float64 (a 1-element device tensor)."""
     lib = load_library()
@@ -323,6 +353,6 @@ def timing_read() -> tuple[float, int, float]:
     return ms.value, n.value, pairs.value
 
 
-__all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "cost", "dual_cost", "divergence",
+__all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "gradient_flow", "cost", "dual_cost", "divergence",
            "divergence_workspace", "marginal_residual", "grad_x", "check_inputs", "workspace", "workspace_bytes",
            "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES", "VARIANTS", "STOP_MODES"]

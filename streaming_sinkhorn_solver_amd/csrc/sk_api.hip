@@ -479,6 +479,85 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
     return SK_OK;
 }
 
+// Fixed-count alternating solve with the optional fused residual trace (sk_solve).
+int solve_fixed(const Ws& W, const float* x, const float* y, const float* a, const float* b, float eps,
+                int n_iters, float* f, float* g, int check_every, float* resid_trace, hipStream_t s) {
+    const Layout& L = W.L;
+    const int64_t n = L.n, m = L.m;
+    int st;
+    if (n_iters == 0) {
+        SK_TRY(launch_fill(f, n, 0.0f, s));
+        SK_TRY(launch_fill(g, m, 0.0f, s));
+        return SK_OK;
+    }
+    const int cap = pass_capacity(L.d);
+    if (cap <= 0) return SK_ERR_HIP;
+    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 1, nullptr, s))) return st;
+
+    PassArgs row = make_pass(W, true, eps, a, cap);
+    row.fin.pot = f;
+    PassArgs col = make_pass(W, false, eps, b, cap);
+    col.fin.pot = g;
+    float* rbuf = W.f(L.rbuf);
+
+    for (int k = 1; k <= n_iters; ++k) {
+        // the row pass of iteration k also yields the residual of iteration k-1's plan
+        const bool check_prev = check_every > 0 && k > 1 && (k - 1) % check_every == 0;
+        row.fin.rbuf = check_prev ? rbuf : nullptr;
+        if ((st = run_pass(W, row, s))) return st;
+        if (check_prev) SK_TRY(launch_resid_reduce(rbuf, (int)n, resid_trace + (k - 1) / check_every - 1, nullptr, s));
+        if ((st = run_pass(W, col, s))) return st;
+    }
+    if (check_every > 0 && n_iters % check_every == 0) {
+        PassArgs probe = row;
+        probe.fin.mode = kFinProbe;
+        probe.fin.rbuf = rbuf;
+        if ((st = run_pass(W, probe, s))) return st;
+        SK_TRY(launch_resid_reduce(rbuf, (int)n, resid_trace + n_iters / check_every - 1, nullptr, s));
+    }
+    return SK_OK;
+}
+
+// Gradient with respect to x at fixed g (sk_grad_x).
+int grad_core(const Ws& W, const float* x, const float* y, const float* a, const float* b, float eps,
+              const float* g, float* grad, hipStream_t s) {
+    const Layout& L = W.L;
+    const int64_t n = L.n, m = L.m;
+    const int d = L.d;
+    int st;
+    int cap = 0;
+    if (L.mfma && (cap = pass_capacity(d)) <= 0) return SK_ERR_HIP;
+    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 2, g, s))) return st;
+
+    GradArgs ga{};
+    const Split sp = grad_split(n, m, d);
+    ga.q = W.f(L.xp);
+    ga.k = W.f(L.yp);
+    ga.kbias = L.mfma ? W.f(L.hy) : nullptr;
+    ga.nq = (int)n;
+    ga.nk = (int)m;
+    ga.P = L.P;
+    ga.d = d;
+    ga.qscale = 2.0f * kLog2e / eps;
+    ga.cols_per_split = sp.cols;
+    ga.nsplit = sp.nsplit;
+    ga.part = reinterpret_cast<float2*>(W.base + L.part);
+    ga.partA = W.f(L.partA);
+    ga.w = a;
+    ga.grad = grad;
+    if (!L.mfma) {
+        SK_TRY(launch_grad_valu(ga, s));
+        return SK_OK;
+    }
+    // d > 8: first the row lse of the same scores, then the weighted key sums
+    PassArgs lse_pass = make_pass(W, true, eps, a, cap);
+    lse_pass.fin.mode = kFinStore;
+    if ((st = run_pass(W, lse_pass, s))) return st;
+    ga.lse = W.f(L.lse_r);
+    SK_TRY(launch_grad_mfma(ga, s));
+    return SK_OK;
+}
+
 // Dual objective at arbitrary potentials: one row pass for the plan's row sums.
 int dual_cost(const Ws& W, const float* x, const float* y, const float* a, const float* b, float eps,
               const float* f, const float* g, double* out, hipStream_t s) {
@@ -549,6 +628,7 @@ const char* sk_status_string(int status) {
         case SK_ERR_VARIANT: return "variant must be 0 (alternating) or 1 (symmetric, 0 < alpha <= 1)";
         case SK_ERR_STOP: return "stop_mode must be 0, 1 or 2; a stop rule needs tol >= 0 finite and check_every >= 1";
         case SK_ERR_CAPTURE: return "a stop rule synchronises the stream and cannot run under graph capture";
+        case SK_ERR_LR: return "the step size must be finite";
         default: return "unknown status";
     }
 }
@@ -618,40 +698,9 @@ int sk_solve(const float* x, const float* y, const float* a, const float* b, int
         return SK_ERR_CHECK_EVERY;
     const Layout L = make_layout(n, m, d);
     if ((st = check_ws(ws, ws_bytes, L))) return st;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     Ws W{L, static_cast<char*>(ws)};
-
-    if (n_iters == 0) {
-        SK_TRY(launch_fill(f, n, 0.0f, s));
-        SK_TRY(launch_fill(g, m, 0.0f, s));
-        return SK_OK;
-    }
-    const int cap = pass_capacity(d);
-    if (cap <= 0) return SK_ERR_HIP;
-    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 1, nullptr, s))) return st;
-
-    PassArgs row = make_pass(W, true, eps, a, cap);
-    row.fin.pot = f;
-    PassArgs col = make_pass(W, false, eps, b, cap);
-    col.fin.pot = g;
-    float* rbuf = W.f(L.rbuf);
-
-    for (int k = 1; k <= n_iters; ++k) {
-        // the row pass of iteration k also yields the residual of iteration k-1's plan
-        const bool check_prev = check_every > 0 && k > 1 && (k - 1) % check_every == 0;
-        row.fin.rbuf = check_prev ? rbuf : nullptr;
-        if ((st = run_pass(W, row, s))) return st;
-        if (check_prev) SK_TRY(launch_resid_reduce(rbuf, (int)n, resid_trace + (k - 1) / check_every - 1, nullptr, s));
-        if ((st = run_pass(W, col, s))) return st;
-    }
-    if (check_every > 0 && n_iters % check_every == 0) {
-        PassArgs probe = row;
-        probe.fin.mode = kFinProbe;
-        probe.fin.rbuf = rbuf;
-        if ((st = run_pass(W, probe, s))) return st;
-        SK_TRY(launch_resid_reduce(rbuf, (int)n, resid_trace + n_iters / check_every - 1, nullptr, s));
-    }
-    return SK_OK;
+    return solve_fixed(W, x, y, a, b, eps, n_iters, f, g, check_every, resid_trace,
+                       reinterpret_cast<hipStream_t>(stream));
 }
 
 int sk_cost(const float* a, const float* b, const float* f, const float* g, int64_t n, int64_t m, float eps,
@@ -704,41 +753,9 @@ int sk_grad_x(const float* x, const float* y, const float* a, const float* b, in
     if ((st = check_eps(eps))) return st;
     const Layout L = make_layout(n, m, d);
     if ((st = check_ws(ws, ws_bytes, L))) return st;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     Ws W{L, static_cast<char*>(ws)};
-    int cap = 0;
-    if (L.mfma && (cap = pass_capacity(d)) <= 0) return SK_ERR_HIP;
-    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 2, g, s))) return st;
-
-    GradArgs ga{};
-    const Split sp = grad_split(n, m, d);
-    ga.q = W.f(L.xp);
-    ga.k = W.f(L.yp);
-    ga.kbias = L.mfma ? W.f(L.hy) : nullptr;
-    ga.nq = (int)n;
-    ga.nk = (int)m;
-    ga.P = L.P;
-    ga.d = d;
-    ga.qscale = 2.0f * kLog2e / eps;
-    ga.cols_per_split = sp.cols;
-    ga.nsplit = sp.nsplit;
-    ga.part = reinterpret_cast<float2*>(W.base + L.part);
-    ga.partA = W.f(L.partA);
-    ga.w = a;
-    ga.grad = grad;
-    if (!L.mfma) {
-        SK_TRY(launch_grad_valu(ga, s));
-        return SK_OK;
-    }
-    // d > 8: first the row lse of the same scores, then the weighted key sums
-    PassArgs lse_pass = make_pass(W, true, eps, a, cap);
-    lse_pass.fin.mode = kFinStore;
-    if ((st = run_pass(W, lse_pass, s))) return st;
-    ga.lse = W.f(L.lse_r);
-    SK_TRY(launch_grad_mfma(ga, s));
-    return SK_OK;
+    return grad_core(W, x, y, a, b, eps, g, grad, reinterpret_cast<hipStream_t>(stream));
 }
-
 int sk_solve_ex(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
                 float eps, int32_t variant, float alpha, int32_t stop_mode, float stop_tol, int32_t max_iter,
                 int32_t check_every, float* f, float* g, int32_t* iters_run, int32_t* converged,
@@ -811,6 +828,28 @@ int sk_divergence(const float* x, const float* y, const float* a, const float* b
         if ((st = dual_cost(W, T.p, T.q, T.wp, T.wq, eps, fb, gb, out + 1 + t, s))) return st;
     }
     SK_TRY(launch_div_combine(out, s));
+    return SK_OK;
+}
+
+int sk_gradient_flow(float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+                     float eps, int32_t n_iters, int32_t n_steps, float lr, float* f, float* g, float* grad,
+                     double* cost_trace, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g || !grad) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if (n_iters < 0 || n_steps < 0) return SK_ERR_ITERS;
+    if (!std::isfinite(lr)) return SK_ERR_LR;
+    const Layout L = make_layout(n, m, d);
+    if ((st = check_ws(ws, ws_bytes, L))) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Ws W{L, static_cast<char*>(ws)};
+    for (int k = 0; k < n_steps; ++k) {
+        if ((st = solve_fixed(W, x, y, a, b, eps, n_iters, f, g, 0, nullptr, s))) return st;
+        if (cost_trace) SK_TRY(launch_cost(a, b, f, g, (int)n, (int)m, eps, cost_trace + k, s));
+        if ((st = grad_core(W, x, y, a, b, eps, g, grad, s))) return st;
+        SK_TRY(launch_axpy(x, grad, n * d, -lr, s));
+    }
     return SK_OK;
 }
 

@@ -172,6 +172,8 @@ hipError_t launch_pot_change(const float* f, float* sf, int n, const float* g, f
 // sum as the plan mass instead of sum(b).
 hipError_t launch_cost_mass(const float* a, const float* b, const float* f, const float* g, const float* mass,
                             int n, int m, float eps, double* out, hipStream_t s);
+// v <- v + alpha * u over count floats.
+hipError_t launch_axpy(float* v, const float* u, int64_t count, float alpha, hipStream_t s);
 // out[0] = out[1] - out[2] / 2 - out[3] / 2.
 hipError_t launch_div_combine(double* out, hipStream_t s);
 hipError_t launch_check(const float* x, const float* y, const float* a, const float* b, int n, int m,

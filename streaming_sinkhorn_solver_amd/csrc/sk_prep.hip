@@ -136,6 +136,13 @@ __global__ __launch_bounds__(kBlock) void k_pot_from_state(const float* __restri
     if (i < npts) pot[i] = nrm[i] - eps_ln2 * u[i];
 }
 
+// v <- v + alpha * u (the descent step of the gradient flow).
+__global__ __launch_bounds__(kBlock) void k_axpy(float* __restrict__ v, const float* __restrict__ u, int64_t count,
+                                                 float alpha) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) v[i] += alpha * u[i];
+}
+
 // Data checks of one flat array: [nonfinite flag, negative flag, float64 sum].
 __global__ __launch_bounds__(kBlock) void k_check_partial(const float* __restrict__ v, int64_t total,
                                                           double* __restrict__ partial) {
@@ -308,6 +315,12 @@ hipError_t launch_pot_change(const float* f, float* sf, int n, const float* g, f
 hipError_t launch_cost_mass(const float* a, const float* b, const float* f, const float* g, const float* mass,
                             int n, int m, float eps, double* out, hipStream_t s) {
     hipLaunchKernelGGL(k_cost, dim3(1), dim3(1024), 0, s, a, b, f, g, mass, n, m, eps, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_axpy(float* v, const float* u, int64_t count, float alpha, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_axpy, dim3(grid_for(count, kBlock)), dim3(kBlock), 0, s, v, u, count, alpha);
     return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ def test_header_declares_entry_points():
     names = header_functions()
     for must in ("sk_solve", "sk_cost", "sk_marginal_residual", "sk_grad_x", "sk_workspace_bytes",
                  "sk_check_inputs", "sk_status_string", "sk_abi_version", "sk_solve_ex", "sk_dual_cost",
-                 "sk_divergence", "sk_divergence_workspace_bytes"):
+                 "sk_divergence", "sk_divergence_workspace_bytes", "sk_gradient_flow"):
         assert must in names
 
 
@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 16):
+    for code in range(0, 17):
         s = lib.sk_status_string(code)
         assert s and len(s) > 1 and s != b"unknown status"
     assert lib.sk_status_string(999) == b"unknown status"
@@ -169,6 +169,23 @@ def test_dual_cost_and_divergence_argument_errors(lib):
     assert div(iters=-2) == SK_ERR_ITERS
     assert div(wb=db - 1) == SK_ERR_WORKSPACE
     assert div(ws=ctypes.c_void_p(0x100040)) == SK_ERR_WORKSPACE
+
+
+def test_gradient_flow_argument_errors(lib):
+    wb = lib.sk_workspace_bytes(10, 12, 2)
+    flow = lambda **k: lib.sk_gradient_flow(k.get("x", FAKE), FAKE, FAKE, FAKE, 10, 12, k.get("d", 2),
+                                            k.get("eps", 0.1), k.get("iters", 5), k.get("steps", 3), k.get("lr", 0.1),
+                                            FAKE, FAKE, k.get("grad", FAKE), None, k.get("ws", FAKE), k.get("wb", wb),
+                                            None)
+    assert flow(x=None) == SK_ERR_NULL
+    assert flow(grad=None) == SK_ERR_NULL
+    assert flow(d=0) == SK_ERR_SHAPE
+    assert flow(eps=0.0) == SK_ERR_EPS
+    assert flow(iters=-1) == SK_ERR_ITERS
+    assert flow(steps=-1) == SK_ERR_ITERS
+    assert flow(lr=float("nan")) == 16
+    assert flow(lr=float("inf")) == 16
+    assert flow(wb=wb - 256) == SK_ERR_WORKSPACE
 
 
 def test_python_contract_errors_before_gpu():
