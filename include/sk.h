@@ -251,6 +251,58 @@ int sk_gradient_flow(float *x, const float *y, const float *a, const float *b,
                      void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Workspace bytes of sk_transport and sk_hvp (0 for invalid sizes or
+ * d > 8).  It is larger than sk_workspace_bytes: it adds the split partials
+ * of the transport passes and the vectors of the Hessian-vector product, all
+ * O((n + m) d).
+ */
+size_t sk_transport_workspace_bytes(int64_t n, int64_t m, int32_t d);
+
+/*
+ * Transport product with the plan at potentials (f, g) (FS, Methodology 3:
+ * the transport matrix applied by the same streamed traversal as the
+ * half-steps, never stored):
+ *     P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps),
+ *     transpose = 0:  out (n, k) = P v,    v (m, k);
+ *     transpose = 1:  out (m, k) = P^T v,  v (n, k).
+ * Row-major, device memory; k >= 1 (columns are processed 9 per pass).
+ * Currently 1 <= d <= 8 (SK_ERR_UNSUPPORTED_D above).  Each row runs an
+ * on-chip running maximum, so the result is exact up to float32 rounding for
+ * any potentials.  ws of at least sk_transport_workspace_bytes(n, m, d).
+ * Enqueues only.
+ */
+int sk_transport(const float *x, const float *y, const float *a, const float *b,
+                 int64_t n, int64_t m, int32_t d, float eps,
+                 const float *f, const float *g, int32_t transpose,
+                 const float *v, int32_t k, float *out,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Hessian-vector product of the entropic OT cost OT_eps(x, y) in the source
+ * points x, at the plan of (f, g) (FS, Methodology 3: a streamed product built
+ * from transport-vector and transport-matrix products, O((n + m) d) memory).
+ * By implicit differentiation at the plan, with r = P 1, c = P^T 1 and
+ * Cdot_ij = 2 <x_i - y_j, v_i>, the potential derivatives (phi, psi) solve
+ *     r_i phi_i + (P psi)_i = sum_j P_ij Cdot_ij,
+ *     (P^T phi)_j + c_j psi_j = sum_i P_ij Cdot_ij,
+ * and out_i = 2 r_i v_i - (2/eps) sum_j P_ij (phi_i + psi_j - Cdot_ij) y_j.
+ * At the optimal (f, g) this is the exact Hessian of the entropic cost; for
+ * other potentials it is the same formula at their plan.  The system is
+ * solved by cg_iters steps of conjugate gradients preconditioned by
+ * diag(r, c)^-1 (two streamed passes each), with the residual kept
+ * orthogonal to the gauge direction (1, -1), on which the system is
+ * singular; the iterate with the smallest residual is used, so extra steps
+ * never make the result worse.  cg_resid (one device float, or NULL)
+ * receives that iterate's preconditioned residual relative to the start.
+ * v and out are (n, d) device arrays.  Currently 1 <= d <= 8.  ws of at least
+ * sk_transport_workspace_bytes(n, m, d).  Enqueues only.
+ */
+int sk_hvp(const float *x, const float *y, const float *a, const float *b,
+           int64_t n, int64_t m, int32_t d, float eps,
+           const float *f, const float *g, const float *v, int32_t cg_iters,
+           float *out, float *cg_resid, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Kernel timing of the streamed log-sum-exp passes (benchmark diagnostics).
  * sk_timing_enable(k) with k >= 1 resets the counters and from then on records
  * a HIP event pair on the launch stream around every k-th streamed-pass kernel

@@ -59,6 +59,11 @@ SIGNATURES = {
                                      _vp]),
     "sk_gradient_flow": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _i32, _f32, _vp, _vp, _vp,
                                         _vp, _vp, _sz, _vp]),
+    "sk_transport_workspace_bytes": (_sz, [_i64, _i64, _i32]),
+    "sk_transport": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _i32, _vp, _i32, _vp, _vp,
+                                    _sz, _vp]),
+    "sk_hvp": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
+                              _vp]),
     "sk_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "sk_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_double)]),
@@ -293,6 +298,63 @@ def gradient_flow(x, y, a=None, b=None, *, eps: float, n_iters: int, n_steps: in
     return x, f, g, grad, cost_trace[:n_steps]
 
 
+def transport_workspace(n: int, m: int, d: int, device) -> torch.Tensor:
+    nb = int(load_library().sk_transport_workspace_bytes(n, m, d))
+    if nb == 0:
+        raise ValueError(f"invalid problem size n={n} m={m} d={d} (transport products need d <= 8)")
+    ws = torch.empty(nb, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("allocator returned a workspace that is not 256-byte aligned")
+    return ws
+
+
+def _potentials(f, g, n, m):
+    f, g = f.contiguous(), g.contiguous()
+    if f.shape != (n,) or g.shape != (m,) or f.dtype != torch.float32 or g.dtype != torch.float32:
+        raise ValueError("f must be (n,) and g (m,) float32")
+    return f, g
+
+
+def transport(x, y, a, b, f, g, v, *, eps: float, transpose: bool = False, ws: torch.Tensor | None = None,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """P v (v: (m,) or (m, k)) or, with transpose, P^T v (v: (n,) or (n, k)), with
+    P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps)."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    f, g = _potentials(f, g, n, m)
+    rows_in, rows_out = (n, m) if transpose else (m, n)
+    vec = v.dim() == 1
+    v2 = (v.reshape(-1, 1) if vec else v).contiguous()
+    if v2.dtype != torch.float32 or v2.dim() != 2 or v2.shape[0] != rows_in:
+        raise ValueError(f"v must be float32 with {rows_in} rows")
+    k = v2.shape[1]
+    ws = ws if ws is not None else transport_workspace(n, m, d, x.device)
+    out = out if out is not None else torch.empty((rows_out, k), dtype=torch.float32, device=x.device)
+    _raise(lib.sk_transport(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g),
+                            1 if transpose else 0, _ptr(v2), k, _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)),
+           "sk_transport")
+    return out.reshape(-1) if vec else out
+
+
+def hvp(x, y, a, b, f, g, v, *, eps: float, cg_iters: int = 50, ws: torch.Tensor | None = None,
+        out: torch.Tensor | None = None, cg_resid: torch.Tensor | None = None):
+    """Hessian-vector product of OT_eps(x, y) in x at the plan of (f, g); v and the result are (n, d).
+
+    Returns (H v, cg_resid) with cg_resid a 1-element device tensor."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    f, g = _potentials(f, g, n, m)
+    v = v.contiguous()
+    if v.shape != (n, d) or v.dtype != torch.float32:
+        raise ValueError("v must be (n, d) float32")
+    ws = ws if ws is not None else transport_workspace(n, m, d, x.device)
+    out = out if out is not None else torch.empty((n, d), dtype=torch.float32, device=x.device)
+    cg_resid = cg_resid if cg_resid is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    _raise(lib.sk_hvp(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g), _ptr(v),
+                      int(cg_iters), _ptr(out), _ptr(cg_resid), _ptr(ws), ws.numel(), _stream(x.device)), "sk_hvp")
+    return out, cg_resid
+
+
 def cost(a, b, f, g, *, eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
     """<a,f> + <b,g> - eps sum(b)(1 - sum(a)) in float64 (a 1-element device tensor)."""
     lib = load_library()
@@ -353,6 +415,7 @@ def timing_read() -> tuple[float, int, float]:
     return ms.value, n.value, pairs.value
 
 
-__all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "gradient_flow", "cost", "dual_cost", "divergence",
+__all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "gradient_flow", "transport", "hvp",
+           "transport_workspace", "cost", "dual_cost", "divergence",
            "divergence_workspace", "marginal_residual", "grad_x", "check_inputs", "workspace", "workspace_bytes",
            "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES", "VARIANTS", "STOP_MODES"]

@@ -575,6 +575,87 @@ int dual_cost(const Ws& W, const float* x, const float* y, const float* a, const
     return SK_OK;
 }
 
+// Workspace of the transport products and the Hessian-vector product: the
+// solver layout, then the split partials of the transport passes and the
+// vectors of the product (all O((n + m) d)).
+struct TLayout {
+    Layout L;
+    size_t part, partA;
+    size_t A, st, U, B, E, diag, rhs, z, zb, res, p, prod, scal;
+    size_t total;
+};
+constexpr int kTransMaxK = 9;  // payload columns per transport pass
+
+TLayout make_tlayout(int64_t n, int64_t m, int d) {
+    TLayout T{};
+    T.L = make_layout(n, m, d);
+    size_t off = align_up(T.L.total, 256);
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + std::max<size_t>(bytes, 1), 256);
+        return o;
+    };
+    const int rpb = transport_rows_per_block();
+    const size_t nsr = (size_t)split_for(n, m, rpb).nsplit, nsc = (size_t)split_for(m, n, rpb).nsplit;
+    const size_t prow = std::max(nsr > 1 ? nsr * n : 0, nsc > 1 ? nsc * m : 0);
+    const size_t un = (size_t)n, um = (size_t)m, N = un + um, ud = (size_t)d;
+    T.part = take(prow * sizeof(float2));
+    T.partA = take(prow * kTransMaxK * 4);
+    T.A = take(un * ud * 4);
+    T.st = take(un * 4);
+    T.U = take(un * (ud + 1) * 4);
+    T.B = take(um * (ud + 1) * 4);
+    T.E = take(un * ud * 4);
+    T.diag = take(N * 4);
+    T.rhs = take(N * 4);
+    T.z = take(N * 4);
+    T.zb = take(N * 4);
+    T.res = take(N * 4);
+    T.p = take(N * 4);
+    T.prod = take(N * 4);
+    T.scal = take(4 * sizeof(double));
+    T.total = off;
+    return T;
+}
+
+// One transport pass over the packed clouds of W (both packed from their
+// potentials): row_side = queries x, keys y; otherwise the transpose.
+int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int mode, const float* pay, int ldp,
+                   int kin, const float* rowv, float* out, int ldo, int kout, float* mass, hipStream_t s) {
+    const Layout& L = W.L;
+    TransArgs t{};
+    t.nq = (int)(row_side ? L.n : L.m);
+    t.nk = (int)(row_side ? L.m : L.n);
+    t.q = W.f(row_side ? L.xp : L.yp);
+    t.k = W.f(row_side ? L.yp : L.xp);
+    t.pay = pay;
+    t.rowv = rowv;
+    t.P = L.P;
+    t.d = L.d;
+    t.qscale = 2.0f * kLog2e / eps;
+    const Split sp = split_for(t.nq, t.nk, transport_rows_per_block());
+    t.cols_per_split = sp.cols;
+    t.nsplit = sp.nsplit;
+    t.part = reinterpret_cast<float2*>(W.base + T.part);
+    t.partA = W.f(T.partA);
+    t.out = out;
+    t.ldo = ldo;
+    t.kout = kout;
+    t.ldp = ldp;
+    t.kin = kin;
+    t.mass = mass;
+    const int kwidth = kin <= 1 ? 1 : (kin <= 4 ? 4 : kTransMaxK);
+    SK_TRY(launch_transport(t, mode, kwidth, s));
+    return SK_OK;
+}
+
+int check_transport_sizes(int64_t n, int64_t m, int32_t d) {
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if (d > kValuMaxD) return SK_ERR_UNSUPPORTED_D;
+    return SK_OK;
+}
+
 int check_ex(int variant, float alpha, int stop_mode, float tol, int max_iter, int check_every) {
     if (variant != 0 && variant != 1) return SK_ERR_VARIANT;
     if (variant == 1 && !(alpha > 0.0f && alpha <= 1.0f)) return SK_ERR_VARIANT;
@@ -850,6 +931,71 @@ int sk_gradient_flow(float* x, const float* y, const float* a, const float* b, i
         if ((st = grad_core(W, x, y, a, b, eps, g, grad, s))) return st;
         SK_TRY(launch_axpy(x, grad, n * d, -lr, s));
     }
+    return SK_OK;
+}
+
+size_t sk_transport_workspace_bytes(int64_t n, int64_t m, int32_t d) {
+    if (check_transport_sizes(n, m, d) != SK_OK) return 0;
+    return make_tlayout(n, m, d).total;
+}
+
+int sk_transport(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+                 float eps, const float* f, const float* g, int32_t transpose, const float* v, int32_t k, float* out,
+                 void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g || !v || !out) return SK_ERR_NULL;
+    int st = check_transport_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if (k < 1 || (transpose != 0 && transpose != 1)) return SK_ERR_SHAPE;
+    const TLayout T = make_tlayout(n, m, d);
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) % 256) != 0 || ws_bytes < T.total) return SK_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Ws W{T.L, static_cast<char*>(ws)};
+    if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
+    for (int c0 = 0; c0 < k; c0 += kTransMaxK) {
+        const int kin = std::min(kTransMaxK, k - c0);
+        if ((st = transport_pass(W, T, transpose == 0, eps, 0, v + c0, k, kin, nullptr, out + c0, k, kin, nullptr, s)))
+            return st;
+    }
+    return SK_OK;
+}
+
+int sk_hvp(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+           float eps, const float* f, const float* g, const float* v, int32_t cg_iters, float* out, float* cg_resid,
+           void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g || !v || !out) return SK_ERR_NULL;
+    int st = check_transport_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if (cg_iters < 0) return SK_ERR_ITERS;
+    const TLayout T = make_tlayout(n, m, d);
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) % 256) != 0 || ws_bytes < T.total) return SK_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Ws W{T.L, static_cast<char*>(ws)};
+    const Layout& L = T.L;
+    const int in = (int)n, im = (int)m, N = in + im;
+    float *A = W.f(T.A), *stv = W.f(T.st), *U = W.f(T.U), *B = W.f(T.B), *E = W.f(T.E);
+    float *diag = W.f(T.diag), *rhs = W.f(T.rhs), *z = W.f(T.z), *zb = W.f(T.zb), *res = W.f(T.res), *p = W.f(T.p);
+    float* prod = W.f(T.prod);
+    double* scal = W.dbl(T.scal);
+    if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
+    // A = P y~ and r = P 1
+    if ((st = transport_pass(W, T, true, eps, 0, W.f(L.yp), L.P, d, nullptr, A, d, d, diag, s))) return st;
+    SK_TRY(launch_hvp_rows(W.f(L.xp), L.P, d, in, v, A, diag, stv, rhs, U, s));
+    // B = P^T [st, v] and c = P^T 1
+    if ((st = transport_pass(W, T, false, eps, 0, U, d + 1, d + 1, nullptr, B, d + 1, d + 1, diag + in, s)))
+        return st;
+    SK_TRY(launch_hvp_cols(W.f(L.yp), L.P, d, im, B, rhs + in, s));
+    SK_TRY(launch_cg_init(N, in, diag, rhs, z, zb, res, p, scal, s));
+    for (int it = 0; it < cg_iters; ++it) {
+        if ((st = transport_pass(W, T, true, eps, 0, p + in, 1, 1, nullptr, prod, 1, 1, nullptr, s))) return st;
+        if ((st = transport_pass(W, T, false, eps, 0, p, 1, 1, nullptr, prod + in, 1, 1, nullptr, s))) return st;
+        SK_TRY(launch_cg_step(N, in, diag, prod, z, zb, res, p, scal, s));
+    }
+    if (cg_resid) SK_TRY(launch_cg_report(scal, cg_resid, s));
+    // E = sum_j P_ij (psi_j + 2 <y~_j, v_i>) y~_j, then the product
+    if ((st = transport_pass(W, T, true, eps, 2, zb + in, 1, 1, v, E, d, d, nullptr, s))) return st;
+    SK_TRY(launch_hvp_final(in, d, eps, v, diag, stv, zb, A, E, out, s));
     return SK_OK;
 }
 

@@ -127,6 +127,22 @@ struct GradArgs {
     const float* lse;    // [nq] row log-sum-exp (matrix-core gradient, from a first pass)
 };
 
+// Arguments of a streamed transport product (d <= 8; see sk_transport.hip).
+struct TransArgs {
+    const float* q;      // query cloud, packed [nq][P], bias slot = log2 w + log2e (pot - |q~|^2)/eps
+    const float* k;      // key cloud, packed [nk][P], same bias from the key-side potential
+    const float* pay;    // payload: key j's columns at pay[j * ldp + c], c < kin
+    const float* rowv;   // per-row direction [nq][d] (weighted mode), else null
+    int nq, nk, P, d;
+    float qscale;        // 2 log2e / eps
+    int cols_per_split, nsplit;
+    float2* part;        // [nsplit][nq] partial (M, S)
+    float* partA;        // [nsplit][nq][accumulators] partial payload sums
+    float* out;          // out[i * ldo + c], c < kout
+    int ldo, kout, ldp, kin;
+    float* mass;         // [nq] row sums of the plan, or null
+};
+
 // Workspace carve-up, a pure function of (n, m, d).
 struct Layout {
     int d, P;
@@ -172,6 +188,21 @@ hipError_t launch_pot_change(const float* f, float* sf, int n, const float* g, f
 // sum as the plan mass instead of sum(b).
 hipError_t launch_cost_mass(const float* a, const float* b, const float* f, const float* g, const float* mass,
                             int n, int m, float eps, double* out, hipStream_t s);
+// Transport products (sk_transport.hip).  mode 0: K-column payload, kwidth in
+// {1, 4, 9} (>= kin); mode 2: the Hessian-vector product's weighted pass.
+int transport_rows_per_block();
+hipError_t launch_transport(const TransArgs& a, int mode, int kwidth, hipStream_t s);
+hipError_t launch_hvp_rows(const float* xp, int P, int d, int n, const float* v, const float* A, const float* r,
+                           float* st, float* rho, float* U, hipStream_t s);
+hipError_t launch_hvp_cols(const float* yp, int P, int d, int m, const float* B, float* gam, hipStream_t s);
+hipError_t launch_hvp_final(int n, int d, float eps, const float* v, const float* r, const float* st,
+                            const float* phi, const float* A, const float* E, float* out, hipStream_t s);
+hipError_t launch_cg_init(int N, int n, const float* diag, const float* rhs, float* z, float* zb, float* res, float* p,
+                          double* scal, hipStream_t s);
+hipError_t launch_cg_step(int N, int n, const float* diag, const float* prod, float* z, float* zb, float* res, float* p,
+                          double* scal, hipStream_t s);
+hipError_t launch_cg_report(const double* scal, float* out, hipStream_t s);
+
 // v <- v + alpha * u over count floats.
 hipError_t launch_axpy(float* v, const float* u, int64_t count, float alpha, hipStream_t s);
 // out[0] = out[1] - out[2] / 2 - out[3] / 2.

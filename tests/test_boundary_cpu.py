@@ -37,7 +37,8 @@ def test_header_declares_entry_points():
     names = header_functions()
     for must in ("sk_solve", "sk_cost", "sk_marginal_residual", "sk_grad_x", "sk_workspace_bytes",
                  "sk_check_inputs", "sk_status_string", "sk_abi_version", "sk_solve_ex", "sk_dual_cost",
-                 "sk_divergence", "sk_divergence_workspace_bytes", "sk_gradient_flow"):
+                 "sk_divergence", "sk_divergence_workspace_bytes", "sk_gradient_flow", "sk_transport",
+                 "sk_transport_workspace_bytes", "sk_hvp"):
         assert must in names
 
 
@@ -186,6 +187,36 @@ def test_gradient_flow_argument_errors(lib):
     assert flow(lr=float("nan")) == 16
     assert flow(lr=float("inf")) == 16
     assert flow(wb=wb - 256) == SK_ERR_WORKSPACE
+
+
+def test_transport_and_hvp_argument_errors(lib):
+    tb = lib.sk_transport_workspace_bytes(10, 12, 2)
+    assert tb > lib.sk_workspace_bytes(10, 12, 2)
+    assert lib.sk_transport_workspace_bytes(10, 12, 9) == 0  # d > 8 not supported yet
+    assert lib.sk_transport_workspace_bytes(0, 12, 2) == 0
+    w1 = lib.sk_transport_workspace_bytes(10000, 12000, 3)
+    w2 = lib.sk_transport_workspace_bytes(20000, 24000, 3)
+    w4 = lib.sk_transport_workspace_bytes(40000, 48000, 3)
+    assert w4 - w2 <= 2.2 * (w2 - w1) + 65536 and w4 < 40000 * 48000 * 4 / 20
+    tr = lambda **k: lib.sk_transport(k.get("x", FAKE), FAKE, FAKE, FAKE, 10, 12, k.get("d", 2), k.get("eps", 0.1),
+                                      FAKE, k.get("g", FAKE), k.get("t", 0), FAKE, k.get("k", 3), FAKE,
+                                      k.get("ws", FAKE), k.get("wb", tb), None)
+    assert tr(x=None) == SK_ERR_NULL
+    assert tr(g=None) == SK_ERR_NULL
+    assert tr(d=9) == SK_ERR_UNSUPPORTED_D
+    assert tr(d=0) == SK_ERR_SHAPE
+    assert tr(eps=-1.0) == SK_ERR_EPS
+    assert tr(k=0) == SK_ERR_SHAPE
+    assert tr(t=2) == SK_ERR_SHAPE
+    assert tr(wb=tb - 1) == SK_ERR_WORKSPACE
+    assert tr(ws=ctypes.c_void_p(0x100080)) == SK_ERR_WORKSPACE
+    hv = lambda **k: lib.sk_hvp(k.get("x", FAKE), FAKE, FAKE, FAKE, 10, 12, k.get("d", 2), 0.1, FAKE, FAKE,
+                                k.get("v", FAKE), k.get("it", 10), k.get("out", FAKE), None, FAKE, k.get("wb", tb), None)
+    assert hv(v=None) == SK_ERR_NULL
+    assert hv(out=None) == SK_ERR_NULL
+    assert hv(d=16) == SK_ERR_UNSUPPORTED_D
+    assert hv(it=-1) == SK_ERR_ITERS
+    assert hv(wb=100) == SK_ERR_WORKSPACE
 
 
 def test_python_contract_errors_before_gpu():

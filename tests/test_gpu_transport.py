@@ -1,0 +1,152 @@
+"""GPU parity of the streamed transport products and the Hessian-vector product
+("FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU", Methodology 3)
+against the dense float64 oracle (oracle/transport.py), through the C ABI.
+
+Tolerances (all at identical float32 inputs and potentials)
+  * transport products: every plan entry carries the float32 error of its
+    exponent, at most a few kappa relative, kappa = 2^-24 (max|f| + max|g| +
+    max C) / eps; so |P v - (P v)*|_i <= 32 kappa (P |v|)_i, elementwise;
+  * Hessian-vector product: relative 1e-4 of the magnitude of the terms it
+    sums, S_i = 2 r_i |v_i| + (2/eps) sum_j P_ij (|phi_i| + |psi_j| + |Cdot_ij|)
+    |y_j| (oracle values), once conjugate gradients has reduced its
+    preconditioned residual below 1e-5; at sizes beyond the dense oracle the
+    closed form for a common translation (H v)_i = 2 a_i t and the symmetry
+    <u, H v> = <v, H u> are checked instead.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import streaming_sinkhorn_solver_amd as sk
+from oracle import transport as T
+from sk_inputs import eps32, random_problem
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U32 = 2.0 ** -24
+
+
+def say(*args):
+    print("[case]", *args, file=sys.stderr, flush=True)
+
+
+def dev(*arrs):
+    return [torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in arrs]
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def kappa(f, g, maxc, eps):
+    return U32 * (np.abs(f).max() + np.abs(g).max() + maxc) / eps
+
+
+def gpu_potentials(x, y, a, b, eps, iters):
+    X, Y, A, B = dev(x, y, a, b)
+    f, g, _ = sk.solve(X, Y, A, B, eps=eps, n_iters=iters)
+    return host(f).astype(np.float32), host(g).astype(np.float32)
+
+
+TRANSPORT_CASES = [
+    # n, m, d, eps, iters, k, transpose, seed, zero_frac
+    (1, 5, 2, 0.2, 3, 1, False, 1, 0.0),
+    (7, 1, 3, 0.2, 3, 2, True, 2, 0.0),
+    (1100, 900, 2, 0.05, 10, 1, False, 3, 0.0),
+    (1100, 900, 3, 0.1, 10, 4, True, 4, 0.1),
+    (2600, 1900, 1, 0.1, 5, 3, False, 5, 0.0),
+    (900, 1300, 5, 0.3, 5, 9, False, 6, 0.0),
+    (1300, 700, 8, 0.5, 5, 11, True, 7, 0.05),
+    (3000, 2500, 4, 0.2, 5, 7, False, 8, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", TRANSPORT_CASES, ids=[f"{c[0]}x{c[1]}d{c[2]}k{c[5]}{'T' if c[6] else ''}"
+                                                       for c in TRANSPORT_CASES])
+def test_transport_matches_oracle(case):
+    n, m, d, eps, iters, k, transpose, seed, zf = case
+    x, y, a, b = random_problem(n, m, d, seed, scale=1.0 / math.sqrt(d), shift=0.3, zero_frac=zf)
+    eps = eps32(eps)
+    f, g = gpu_potentials(x, y, a, b, eps, iters)
+    rows_in = n if transpose else m
+    v = np.random.default_rng(seed + 50).normal(size=(rows_in, k)).astype(np.float32)
+    say("transport", case)
+    X, Y, A, B, F, G, Vt = dev(x, y, a, b, f, g, v)
+    got = host(sk.transport(X, Y, A, B, F, G, Vt, eps=eps, transpose=transpose))
+    want = T.transport(x, y, a, b, f, g, eps, v, transpose=transpose)
+    scale = T.transport(x, y, a, b, f, g, eps, np.abs(v), transpose=transpose)
+    kap = kappa(f, g, oracle.max_cost(x, y), eps)
+    err = np.abs(got - want)
+    say("max err / bound", (err / (32 * kap * scale + 1e-30)).max(), "kappa", kap)
+    assert np.all(err <= 32 * kap * scale + 1e-30)
+    # vector form and the plan marginals
+    if k == 1:
+        one = np.ones(rows_in, dtype=np.float32)
+        got1 = host(sk.transport(X, Y, A, B, F, G, dev(one)[0], eps=eps, transpose=transpose))
+        rs, cs = oracle.marginals(x, y, a, b, f, g, eps)
+        ref = cs if transpose else rs
+        assert np.all(np.abs(got1 - ref) <= 32 * kap * ref + 1e-30)
+
+
+HVP_CASES = [
+    # n, m, d, eps, solve iters, cg iters, seed
+    (1, 6, 2, 0.3, 200, 20, 11),
+    (300, 257, 2, 0.3, 300, 80, 12),
+    (1100, 900, 3, 0.5, 300, 80, 13),
+    (700, 600, 1, 0.2, 500, 150, 14),
+    (500, 800, 8, 1.0, 200, 60, 15),
+    (900, 700, 5, 0.5, 100, 80, 16),  # away from the optimum: the same formula at that plan
+]
+
+
+@pytest.mark.parametrize("case", HVP_CASES, ids=[f"{c[0]}x{c[1]}d{c[2]}" for c in HVP_CASES])
+def test_hvp_matches_oracle(case):
+    n, m, d, eps, iters, cg_iters, seed = case
+    x, y, a, b = random_problem(n, m, d, seed, scale=1.0 / math.sqrt(d), shift=0.3)
+    eps = eps32(eps)
+    f, g = gpu_potentials(x, y, a, b, eps, iters)
+    v = np.random.default_rng(seed + 70).normal(size=(n, d)).astype(np.float32)
+    say("hvp", case)
+    X, Y, A, B, F, G, Vt = dev(x, y, a, b, f, g, v)
+    out, res = sk.hvp(X, Y, A, B, F, G, Vt, eps=eps, cg_iters=cg_iters)
+    got, cg_res = host(out), float(host(res)[0])
+    want, parts = T.hvp(x, y, a, b, f, g, eps, v, return_parts=True)
+    P = T.plan(x, y, a, b, f, g, eps)
+    xd, yd = x.astype(np.float64), y.astype(np.float64)
+    cdot = 2.0 * ((xd[:, None, :] - yd[None, :, :]) * v[:, None, :]).sum(axis=-1)
+    terms = P * (np.abs(parts["phi"])[:, None] + np.abs(parts["psi"])[None, :] + np.abs(cdot))
+    S = 2 * parts["r"][:, None] * np.abs(v) + (2.0 / eps) * (terms @ np.abs(yd))
+    err = np.abs(got - want)
+    say("cg residual", cg_res, "max err / (1e-4 S)", (err / (1e-4 * S + 1e-30)).max(), "|HV| max", np.abs(want).max())
+    assert cg_res <= 1e-5
+    assert np.all(err <= 1e-4 * S + 1e-30)
+
+
+def test_hvp_translation_and_symmetry_at_size():
+    """20k x 20k, d = 3, converged: (H v)_i = 2 a_i t for v_i = t, and <u, H v> = <v, H u>."""
+    x, y, a, b = random_problem(20000, 20000, 3, 21, scale=0.5, shift=0.3)
+    eps = eps32(0.2)
+    X, Y, A, B = dev(x, y, a, b)
+    F, G, _ = sk.solve(X, Y, A, B, eps=eps, n_iters=300)
+    r = host(sk.marginal_residual(X, Y, A, B, F, G, eps=eps))
+    say("residual after 300 iterations", r[:2])
+    t = np.array([0.5, -0.25, 0.125], dtype=np.float32)
+    vt = np.tile(t, (20000, 1))
+    out, res = sk.hvp(X, Y, A, B, F, G, dev(vt)[0], eps=eps, cg_iters=100)
+    got = host(out)
+    want = 2 * a[:, None].astype(np.float64) * t
+    say("translation: max err", np.abs(got - want).max(), "scale", np.abs(want).max(), "cg", float(host(res)[0]))
+    assert np.abs(got - want).max() <= 1e-3 * np.abs(want).max()
+    rng = np.random.default_rng(22)
+    u = rng.normal(size=(20000, 3)).astype(np.float32)
+    v = rng.normal(size=(20000, 3)).astype(np.float32)
+    Hv, _ = sk.hvp(X, Y, A, B, F, G, dev(v)[0], eps=eps, cg_iters=100)
+    Hu, _ = sk.hvp(X, Y, A, B, F, G, dev(u)[0], eps=eps, cg_iters=100)
+    lhs, rhs = float((u * host(Hv)).sum()), float((v * host(Hu)).sum())
+    say("symmetry", lhs, rhs)
+    assert abs(lhs - rhs) <= 1e-3 * max(abs(lhs), abs(rhs))
