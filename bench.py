@@ -32,7 +32,14 @@ evaluations of the counted iterations only):
               pair evaluations;
   flow        one step of the gradient flow (sk_gradient_flow with one step:
               fresh solve of n_iters iterations, cost, gradient, x <- x - lr
-              grad, x updated in place); --graph replays it as a HIP graph.
+              grad, x updated in place); --graph replays it as a HIP graph;
+  hvp         one Hessian-vector product sk_hvp with --cg-iters conjugate-
+              gradient steps at the potentials of an n_iters solve done
+              before timing: (3 + 2 cg_iters) n m pair evaluations;
+  transport   one transport product P Y~-sized: sk_transport with a k = d
+              payload (the barycentric numerator), n m pair evaluations.
+The roofline of the hvp / transport modes is that of the transport kernel
+(the dominant one) with its payload work per pair.
 """
 from __future__ import annotations
 
@@ -59,7 +66,7 @@ EXP_RATE_FRACTION = 0.5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass_traffic.json")
 
 
-def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
+def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int = 0) -> dict:
     """Vector-ALU roofline of one streamed pass.
 
     Algorithmic work per pair evaluation: d FMAs (2d flops), one max, one
@@ -68,10 +75,11 @@ def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
     the running max (v_max3 takes two new scores per instruction), one
     subtract, one exp2 and one add: d + 3.5.  The chip's ceiling is therefore
     min(LANE_OPS_PER_S / (d + 3.5), EXP_RATE_FRACTION * LANE_OPS_PER_S) pairs/s,
-    and the peak in operation units is that times (2d + 4).
+    and the peak in operation units is that times (2d + 4).  A transport pass
+    with a payload of K columns adds K FMAs per pair (2K operations, K slots).
     """
-    ops_per_pair = 2 * d + 4
-    ceiling_pairs = min(LANE_OPS_PER_S / (d + 3.5), EXP_RATE_FRACTION * LANE_OPS_PER_S)
+    ops_per_pair = 2 * d + 4 + 2 * payload
+    ceiling_pairs = min(LANE_OPS_PER_S / (d + 3.5 + payload), EXP_RATE_FRACTION * LANE_OPS_PER_S)
     achieved = pairs_per_launch * ops_per_pair / avg_launch_s / 1e12
     peak = ceiling_pairs * ops_per_pair / 1e12
     return {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TFLOP/s",
@@ -173,7 +181,8 @@ def main():
     ap.add_argument("--timing-stride", type=int, default=7,
                     help="time every k-th pass launch with HIP events (odd, so row and column passes alternate)")
     ap.add_argument("--mode", default="solve",
-                    choices=["solve", "symmetric", "marginal", "potential", "divergence", "flow"])
+                    choices=["solve", "symmetric", "marginal", "potential", "divergence", "flow", "hvp", "transport"])
+    ap.add_argument("--cg-iters", type=int, default=20, help="conjugate-gradient steps of the hvp mode")
     ap.add_argument("--lr", type=float, default=0.1, help="step size of the gradient flow")
     ap.add_argument("--alpha", type=float, default=0.5, help="blend of the symmetric variant")
     ap.add_argument("--stop-tol", type=float, default=1e-5, help="tolerance of the marginal / potential stop rule")
@@ -224,6 +233,14 @@ def main():
 
     mode = args.mode
     stop = {}
+    if mode in ("hvp", "transport"):
+        # potentials of a full solve, outside the timed region
+        sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, ws=ws, f=f, g=g, check=False)
+        ws_t = sk.transport_workspace(n, m, d, dev)
+        v_dir = torch.randn((n, d), generator=torch.Generator(device="cpu").manual_seed(7)).to(dev)
+        hv_out = torch.empty((n, d), dtype=torch.float32, device=dev)
+        cg_res = torch.empty(1, dtype=torch.float32, device=dev)
+        y_pay = Y.contiguous()
     dv_out = torch.empty(4, dtype=torch.float64, device=dev)
     ws_div = sk.divergence_workspace(n, m, d, dev) if mode == "divergence" else None
 
@@ -243,6 +260,10 @@ def main():
                                                check=False)
             stop.update(iters_run=it, converged=conv, final_viol=viol)
             sk.cost(A, B, f, g, eps=eps, out=cost_out)
+        elif mode == "hvp":
+            sk.hvp(X, Y, A, B, f, g, v_dir, eps=eps, cg_iters=args.cg_iters, ws=ws_t, out=hv_out, cg_resid=cg_res)
+        elif mode == "transport":
+            sk.transport(X, Y, A, B, f, g, y_pay, eps=eps, ws=ws_t, out=hv_out)
         elif mode == "flow":
             sk.gradient_flow(X, Y, A, B, eps=eps, n_iters=n_iters, n_steps=1, lr=args.lr, ws=ws, f=f, g=g,
                              grad=grad, cost_trace=cost_out, check=False)
@@ -289,6 +310,10 @@ def main():
     pair_evals = 2.0 * n * m * counted_iters
     if mode == "divergence":
         pair_evals = 2.0 * n_iters * (n * m + n * n + m * m)
+    if mode == "hvp":
+        pair_evals = (3.0 + 2.0 * args.cg_iters) * n * m
+    if mode == "transport":
+        pair_evals = 1.0 * n * m
     extra = {}
     if mode in ("marginal", "potential"):
         # the same iterations without checks, with the same pass timing events
@@ -309,13 +334,19 @@ def main():
         extra = {"variant": "symmetric", "alpha": args.alpha}
     elif mode == "divergence":
         extra = {"divergence": [float(v) for v in dv_out.cpu()]}
+    elif mode == "hvp":
+        extra = {"cg_iters": args.cg_iters, "cg_resid": float(cg_res.item()), "hvp_per_s": 1.0 / step_s}
     elif mode == "flow":
         extra = {"lr": args.lr, "flow_steps_per_s": 1.0 / step_s,
                  "flow_steps_run": args.warmup + args.steps + (1 if args.graph else 0) * 2}
     value = pair_evals / step_s
     avg_launch_s = pass_ms * 1e-3 / launches
     pairs_per_launch = pairs / launches
-    if d <= 8:
+    if mode in ("hvp", "transport"):
+        payload = 1 if mode == "hvp" else d  # columns of the dominant launches (CG steps / the product)
+        roof = roofline_alu(d, pairs_per_launch, avg_launch_s, payload)
+        roof["kernel"] = "k_transport<%d,%d,0>" % (d, 1 if payload == 1 else (4 if payload <= 4 else 9))
+    elif d <= 8:
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
         small = pairs_per_launch <= 2.0e6  # the library's single-kernel path for small passes
         roof["kernel"] = f"k_pass_small<{d}>" if small else f"k_pass_valu<{d}>"
@@ -345,7 +376,7 @@ def main():
         "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s,
         "roofline": roof,
         "final_residual": float(trace[n_iters // ce - 1].item()) if (ce and mode == "solve") else None,
-        "cost": float(cost_out.item()) if mode != "divergence" else None,
+        "cost": float(cost_out.item()) if mode not in ("divergence", "hvp", "transport") else None,
         **extra,
     }
     if not args.no_cpu_baseline and mode == "solve":

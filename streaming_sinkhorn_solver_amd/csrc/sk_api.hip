@@ -180,27 +180,34 @@ Timing& timing() {
     return t;
 }
 
-int run_pass(const Ws& W, const PassArgs& p, hipStream_t s) {
-    (void)W;
+// Takes the event pair for the next streamed-pass launch of nq x nk pairs when
+// timing is on, the stream is not being captured and the stride selects it;
+// otherwise leaves both null.
+int timing_events(int64_t nq, int64_t nk, hipStream_t s, hipEvent_t* e0, hipEvent_t* e1) {
     Timing& T = timing();
-    hipEvent_t e0 = nullptr, e1 = nullptr;
+    *e0 = *e1 = nullptr;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cap) != hipSuccess) return SK_ERR_HIP;
-    {
-        std::lock_guard<std::mutex> lk(T.mu);
-        // no event nodes inside a captured graph
-        if (T.on && cap == hipStreamCaptureStatusNone && (T.seen++ % T.stride) == 0) {
-            while (T.pool.size() < 2 * (T.used + 1)) {
-                hipEvent_t e;
-                SK_TRY(hipEventCreate(&e));
-                T.pool.push_back(e);
-            }
-            e0 = T.pool[2 * T.used];
-            e1 = T.pool[2 * T.used + 1];
-            ++T.used;
-            T.pairs += (double)p.nq * (double)p.nk;
+    std::lock_guard<std::mutex> lk(T.mu);
+    // no event nodes inside a captured graph
+    if (T.on && cap == hipStreamCaptureStatusNone && (T.seen++ % T.stride) == 0) {
+        while (T.pool.size() < 2 * (T.used + 1)) {
+            hipEvent_t e;
+            SK_TRY(hipEventCreate(&e));
+            T.pool.push_back(e);
         }
+        *e0 = T.pool[2 * T.used];
+        *e1 = T.pool[2 * T.used + 1];
+        ++T.used;
+        T.pairs += (double)nq * (double)nk;
     }
+    return SK_OK;
+}
+
+int run_pass(const Ws& W, const PassArgs& p, hipStream_t s) {
+    hipEvent_t e0, e1;
+    int st = timing_events(p.nq, p.nk, s, &e0, &e1);
+    if (st) return st;
     if (W.L.mfma)
         SK_TRY(launch_pass_mfma(p, s, e0, e1));
     else
@@ -645,7 +652,10 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     t.kin = kin;
     t.mass = mass;
     const int kwidth = kin <= 1 ? 1 : (kin <= 4 ? 4 : kTransMaxK);
-    SK_TRY(launch_transport(t, mode, kwidth, s));
+    hipEvent_t e0, e1;
+    int st = timing_events(t.nq, t.nk, s, &e0, &e1);
+    if (st) return st;
+    SK_TRY(launch_transport(t, mode, kwidth, s, e0, e1));
     return SK_OK;
 }
 

@@ -191,7 +191,9 @@ hipError_t launch_cost_mass(const float* a, const float* b, const float* f, cons
 // Transport products (sk_transport.hip).  mode 0: K-column payload, kwidth in
 // {1, 4, 9} (>= kin); mode 2: the Hessian-vector product's weighted pass.
 int transport_rows_per_block();
-hipError_t launch_transport(const TransArgs& a, int mode, int kwidth, hipStream_t s);
+// ev0 / ev1 (may be null): recorded right before and after the pass kernel (not the merge).
+hipError_t launch_transport(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0 = nullptr,
+                            hipEvent_t ev1 = nullptr);
 hipError_t launch_hvp_rows(const float* xp, int P, int d, int n, const float* v, const float* A, const float* r,
                            float* st, float* rho, float* U, hipStream_t s);
 hipError_t launch_hvp_cols(const float* yp, int P, int d, int m, const float* B, float* gam, hipStream_t s);

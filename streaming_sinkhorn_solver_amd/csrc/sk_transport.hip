@@ -190,23 +190,25 @@ __global__ __launch_bounds__(kBlock) void k_transport_merge(TransArgs A) {
 }
 
 template <int D, int K, int MODE>
-hipError_t launch_t(const TransArgs& a, hipStream_t s) {
+hipError_t launch_t(const TransArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int KA = MODE == 0 ? K : D;
     const int rpb = kBlock * kTR;
     dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
+    if (ev0) (void)hipEventRecord(ev0, s);
     hipLaunchKernelGGL((k_transport<D, K, MODE>), grid, dim3(kBlock), 0, s, a);
+    if (ev1) (void)hipEventRecord(ev1, s);
     if (a.nsplit > 1)
         hipLaunchKernelGGL(k_transport_merge<KA>, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_t_d(const TransArgs& a, int mode, int kwidth, hipStream_t s) {
-    if (mode == 2) return launch_t<D, 1, 2>(a, s);
+hipError_t launch_t_d(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (mode == 2) return launch_t<D, 1, 2>(a, s, ev0, ev1);
     switch (kwidth) {
-        case 1: return launch_t<D, 1, 0>(a, s);
-        case 4: return launch_t<D, 4, 0>(a, s);
-        case 9: return launch_t<D, 9, 0>(a, s);
+        case 1: return launch_t<D, 1, 0>(a, s, ev0, ev1);
+        case 4: return launch_t<D, 4, 0>(a, s, ev0, ev1);
+        case 9: return launch_t<D, 9, 0>(a, s, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -372,16 +374,16 @@ inline int grid_of(int64_t count) { return (int)((count + kBlock - 1) / kBlock);
 
 int transport_rows_per_block() { return kBlock * kTR; }
 
-hipError_t launch_transport(const TransArgs& a, int mode, int kwidth, hipStream_t s) {
+hipError_t launch_transport(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     switch (a.d) {
-        case 1: return launch_t_d<1>(a, mode, kwidth, s);
-        case 2: return launch_t_d<2>(a, mode, kwidth, s);
-        case 3: return launch_t_d<3>(a, mode, kwidth, s);
-        case 4: return launch_t_d<4>(a, mode, kwidth, s);
-        case 5: return launch_t_d<5>(a, mode, kwidth, s);
-        case 6: return launch_t_d<6>(a, mode, kwidth, s);
-        case 7: return launch_t_d<7>(a, mode, kwidth, s);
-        case 8: return launch_t_d<8>(a, mode, kwidth, s);
+        case 1: return launch_t_d<1>(a, mode, kwidth, s, ev0, ev1);
+        case 2: return launch_t_d<2>(a, mode, kwidth, s, ev0, ev1);
+        case 3: return launch_t_d<3>(a, mode, kwidth, s, ev0, ev1);
+        case 4: return launch_t_d<4>(a, mode, kwidth, s, ev0, ev1);
+        case 5: return launch_t_d<5>(a, mode, kwidth, s, ev0, ev1);
+        case 6: return launch_t_d<6>(a, mode, kwidth, s, ev0, ev1);
+        case 7: return launch_t_d<7>(a, mode, kwidth, s, ev0, ev1);
+        case 8: return launch_t_d<8>(a, mode, kwidth, s, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }
