@@ -91,12 +91,14 @@ def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float, payload: 
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 
 
-def roofline_mfma(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
+def roofline_mfma(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int = 0) -> dict:
     """Matrix-core roofline of one streamed pass for d > 8: the algorithmic work is
-    the cross term, 2d flops per pair evaluation, against the fp32 MFMA peak."""
-    achieved = pairs_per_launch * 2 * d / avg_launch_s / 1e12
+    the cross term, 2d flops per pair evaluation (plus 2 per payload column of a
+    transport pass), against the fp32 MFMA peak."""
+    ops = 2 * d + 2 * payload
+    achieved = pairs_per_launch * ops / avg_launch_s / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4), "traffic": None, "ops_per_pair": 2 * d,
+            "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4), "traffic": None, "ops_per_pair": ops,
             "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
 
 
@@ -344,8 +346,13 @@ def main():
     pairs_per_launch = pairs / launches
     if mode in ("hvp", "transport"):
         payload = 1 if mode == "hvp" else d  # columns of the dominant launches (CG steps / the product)
-        roof = roofline_alu(d, pairs_per_launch, avg_launch_s, payload)
-        roof["kernel"] = "k_transport<%d,%d,0>" % (d, 1 if payload == 1 else (4 if payload <= 4 else 9))
+        if d <= 8:
+            roof = roofline_alu(d, pairs_per_launch, avg_launch_s, payload)
+            roof["kernel"] = "k_transport<%d,%d,0>" % (d, 1 if payload == 1 else (4 if payload <= 4 else 9))
+        else:
+            roof = roofline_mfma(d, pairs_per_launch, avg_launch_s, payload)
+            p2 = max(16, 1 << (d - 1).bit_length())
+            roof["kernel"] = "k_transport_mfma<%d,1,%d>" % (p2, 0 if mode == "hvp" else 1)
     elif d <= 8:
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
         small = pairs_per_launch <= 2.0e6  # the library's single-kernel path for small passes

@@ -251,10 +251,9 @@ int sk_gradient_flow(float *x, const float *y, const float *a, const float *b,
                      void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Workspace bytes of sk_transport and sk_hvp (0 for invalid sizes or
- * d > 8).  It is larger than sk_workspace_bytes: it adds the split partials
- * of the transport passes and the vectors of the Hessian-vector product, all
- * O((n + m) d).
+ * Workspace bytes of sk_transport and sk_hvp (0 for invalid sizes).  It is
+ * larger than sk_workspace_bytes: it adds the split partials of the transport
+ * passes and the vectors of the Hessian-vector product, all O((n + m) d).
  */
 size_t sk_transport_workspace_bytes(int64_t n, int64_t m, int32_t d);
 
@@ -265,11 +264,12 @@ size_t sk_transport_workspace_bytes(int64_t n, int64_t m, int32_t d);
  *     P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps),
  *     transpose = 0:  out (n, k) = P v,    v (m, k);
  *     transpose = 1:  out (m, k) = P^T v,  v (n, k).
- * Row-major, device memory; k >= 1 (columns are processed 9 per pass).
- * Currently 1 <= d <= 8 (SK_ERR_UNSUPPORTED_D above).  Each row runs an
- * on-chip running maximum, so the result is exact up to float32 rounding for
- * any potentials.  ws of at least sk_transport_workspace_bytes(n, m, d).
- * Enqueues only.
+ * Row-major, device memory; k >= 1 (columns are processed 9 per pass for
+ * d <= 8, 16 or 64 per pass on the matrix cores).  For d <= 8 each row runs
+ * an on-chip running maximum; for d > 8 a first pass stores each row's
+ * log-sum-exp of the scores so that every weight is at most 1; either way the
+ * result is exact up to float32 rounding for any potentials.  ws of at least
+ * sk_transport_workspace_bytes(n, m, d).  Enqueues only.
  */
 int sk_transport(const float *x, const float *y, const float *a, const float *b,
                  int64_t n, int64_t m, int32_t d, float eps,
@@ -294,8 +294,9 @@ int sk_transport(const float *x, const float *y, const float *a, const float *b,
  * singular; the iterate with the smallest residual is used, so extra steps
  * never make the result worse.  cg_resid (one device float, or NULL)
  * receives that iterate's preconditioned residual relative to the start.
- * v and out are (n, d) device arrays.  Currently 1 <= d <= 8.  ws of at least
- * sk_transport_workspace_bytes(n, m, d).  Enqueues only.
+ * v and out are (n, d) device arrays.  For d > 8 the two log-sum-exp passes
+ * that the matrix-core products need are taken once, the plan being fixed.
+ * ws of at least sk_transport_workspace_bytes(n, m, d).  Enqueues only.
  */
 int sk_hvp(const float *x, const float *y, const float *a, const float *b,
            int64_t n, int64_t m, int32_t d, float eps,

@@ -301,7 +301,7 @@ def gradient_flow(x, y, a=None, b=None, *, eps: float, n_iters: int, n_steps: in
 def transport_workspace(n: int, m: int, d: int, device) -> torch.Tensor:
     nb = int(load_library().sk_transport_workspace_bytes(n, m, d))
     if nb == 0:
-        raise ValueError(f"invalid problem size n={n} m={m} d={d} (transport products need d <= 8)")
+        raise ValueError(f"invalid problem size n={n} m={m} d={d}")
     ws = torch.empty(nb, dtype=torch.uint8, device=device)
     if ws.data_ptr() % 256:
         raise RuntimeError("allocator returned a workspace that is not 256-byte aligned")

@@ -591,7 +591,12 @@ struct TLayout {
     size_t A, st, U, B, E, diag, rhs, z, zb, res, p, prod, scal;
     size_t total;
 };
-constexpr int kTransMaxK = 9;  // payload columns per transport pass
+constexpr int kTransMaxK = 9;  // payload columns per vector-ALU transport pass
+
+// Payload columns per transport pass, and accumulators per row of a split partial.
+int trans_chunk(const Layout& L) { return !L.mfma ? kTransMaxK : (L.P >= 64 ? 64 : 16); }
+int trans_acc(const Layout& L) { return !L.mfma ? kTransMaxK : std::max(64, L.P); }
+int trans_rows(const Layout& L) { return L.mfma ? mfma_transport_rows_per_block() : transport_rows_per_block(); }
 
 TLayout make_tlayout(int64_t n, int64_t m, int d) {
     TLayout T{};
@@ -602,12 +607,12 @@ TLayout make_tlayout(int64_t n, int64_t m, int d) {
         off = align_up(off + std::max<size_t>(bytes, 1), 256);
         return o;
     };
-    const int rpb = transport_rows_per_block();
+    const int rpb = trans_rows(T.L);
     const size_t nsr = (size_t)split_for(n, m, rpb).nsplit, nsc = (size_t)split_for(m, n, rpb).nsplit;
     const size_t prow = std::max(nsr > 1 ? nsr * n : 0, nsc > 1 ? nsc * m : 0);
     const size_t un = (size_t)n, um = (size_t)m, N = un + um, ud = (size_t)d;
     T.part = take(prow * sizeof(float2));
-    T.partA = take(prow * kTransMaxK * 4);
+    T.partA = take(prow * (size_t)trans_acc(T.L) * 4);
     T.A = take(un * ud * 4);
     T.st = take(un * 4);
     T.U = take(un * (ud + 1) * 4);
@@ -625,8 +630,19 @@ TLayout make_tlayout(int64_t n, int64_t m, int d) {
     return T;
 }
 
+// The row log-sum-exp of the scores of one side, for the matrix-core
+// transport kernels (their weights 2^{s - lse} are then <= 1).
+int store_lse(const Ws& W, bool row_side, float eps, const float* w_q, hipStream_t s) {
+    const int cap = pass_capacity(W.L.d);
+    if (cap <= 0) return SK_ERR_HIP;
+    PassArgs p = make_pass(W, row_side, eps, w_q, cap);
+    p.fin.mode = kFinStore;
+    return run_pass(W, p, s);
+}
+
 // One transport pass over the packed clouds of W (both packed from their
-// potentials): row_side = queries x, keys y; otherwise the transpose.
+// potentials): row_side = queries x, keys y; otherwise the transpose.  mode 0
+// takes kin <= trans_chunk payload columns; modes 1 and 2 write d columns.
 int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int mode, const float* pay, int ldp,
                    int kin, const float* rowv, float* out, int ldo, int kout, float* mass, hipStream_t s) {
     const Layout& L = W.L;
@@ -635,12 +651,15 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     t.nk = (int)(row_side ? L.m : L.n);
     t.q = W.f(row_side ? L.xp : L.yp);
     t.k = W.f(row_side ? L.yp : L.xp);
+    t.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
+    t.qbias = L.mfma ? W.f(row_side ? L.hx : L.hy) : nullptr;
+    t.lse = L.mfma ? W.f(row_side ? L.lse_r : L.lse_c) : nullptr;
     t.pay = pay;
     t.rowv = rowv;
     t.P = L.P;
     t.d = L.d;
     t.qscale = 2.0f * kLog2e / eps;
-    const Split sp = split_for(t.nq, t.nk, transport_rows_per_block());
+    const Split sp = split_for(t.nq, t.nk, trans_rows(L));
     t.cols_per_split = sp.cols;
     t.nsplit = sp.nsplit;
     t.part = reinterpret_cast<float2*>(W.base + T.part);
@@ -651,20 +670,33 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     t.ldp = ldp;
     t.kin = kin;
     t.mass = mass;
-    const int kwidth = kin <= 1 ? 1 : (kin <= 4 ? 4 : kTransMaxK);
     hipEvent_t e0, e1;
     int st = timing_events(t.nq, t.nk, s, &e0, &e1);
     if (st) return st;
-    SK_TRY(launch_transport(t, mode, kwidth, s, e0, e1));
+    if (L.mfma) {
+        SK_TRY(launch_transport_mfma(t, mode, kin <= 16 ? 16 : 64, s, e0, e1));
+    } else {
+        SK_TRY(launch_transport(t, mode, kin <= 1 ? 1 : (kin <= 4 ? 4 : kTransMaxK), s, e0, e1));
+    }
     return SK_OK;
 }
 
-int check_transport_sizes(int64_t n, int64_t m, int32_t d) {
-    int st = check_sizes(n, m, d);
-    if (st) return st;
-    if (d > kValuMaxD) return SK_ERR_UNSUPPORTED_D;
+// out (rows x k) = P v or P^T v in chunks of payload columns; mass (may be null)
+// receives the plan's row (or column) sums with the first chunk.
+int transport_cols(const Ws& W, const TLayout& T, bool row_side, float eps, const float* v, int k, float* out,
+                   float* mass, hipStream_t s) {
+    const int chunk = trans_chunk(W.L);
+    int st;
+    for (int c0 = 0; c0 < k; c0 += chunk) {
+        const int kin = std::min(chunk, k - c0);
+        if ((st = transport_pass(W, T, row_side, eps, 0, v + c0, k, kin, nullptr, out + c0, k, kin,
+                                 c0 == 0 ? mass : nullptr, s)))
+            return st;
+    }
     return SK_OK;
 }
+
+int check_transport_sizes(int64_t n, int64_t m, int32_t d) { return check_sizes(n, m, d); }
 
 int check_ex(int variant, float alpha, int stop_mode, float tol, int max_iter, int check_every) {
     if (variant != 0 && variant != 1) return SK_ERR_VARIANT;
@@ -961,13 +993,10 @@ int sk_transport(const float* x, const float* y, const float* a, const float* b,
     if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) % 256) != 0 || ws_bytes < T.total) return SK_ERR_WORKSPACE;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     Ws W{T.L, static_cast<char*>(ws)};
+    const bool row_side = transpose == 0;
     if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
-    for (int c0 = 0; c0 < k; c0 += kTransMaxK) {
-        const int kin = std::min(kTransMaxK, k - c0);
-        if ((st = transport_pass(W, T, transpose == 0, eps, 0, v + c0, k, kin, nullptr, out + c0, k, kin, nullptr, s)))
-            return st;
-    }
-    return SK_OK;
+    if (T.L.mfma && (st = store_lse(W, row_side, eps, row_side ? a : b, s))) return st;
+    return transport_cols(W, T, row_side, eps, v, k, out, nullptr, s);
 }
 
 int sk_hvp(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
@@ -989,12 +1018,19 @@ int sk_hvp(const float* x, const float* y, const float* a, const float* b, int64
     float* prod = W.f(T.prod);
     double* scal = W.dbl(T.scal);
     if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
+    if (L.mfma) {  // the plan is fixed: one lse pass per side serves every product below
+        if ((st = store_lse(W, true, eps, a, s))) return st;
+        if ((st = store_lse(W, false, eps, b, s))) return st;
+    }
     // A = P y~ and r = P 1
-    if ((st = transport_pass(W, T, true, eps, 0, W.f(L.yp), L.P, d, nullptr, A, d, d, diag, s))) return st;
+    if (L.mfma) {
+        if ((st = transport_pass(W, T, true, eps, 1, nullptr, 0, 0, nullptr, A, d, d, diag, s))) return st;
+    } else {
+        if ((st = transport_pass(W, T, true, eps, 0, W.f(L.yp), L.P, d, nullptr, A, d, d, diag, s))) return st;
+    }
     SK_TRY(launch_hvp_rows(W.f(L.xp), L.P, d, in, v, A, diag, stv, rhs, U, s));
     // B = P^T [st, v] and c = P^T 1
-    if ((st = transport_pass(W, T, false, eps, 0, U, d + 1, d + 1, nullptr, B, d + 1, d + 1, diag + in, s)))
-        return st;
+    if ((st = transport_cols(W, T, false, eps, U, d + 1, B, diag + in, s))) return st;
     SK_TRY(launch_hvp_cols(W.f(L.yp), L.P, d, im, B, rhs + in, s));
     SK_TRY(launch_cg_init(N, in, diag, rhs, z, zb, res, p, scal, s));
     for (int it = 0; it < cg_iters; ++it) {

@@ -131,6 +131,9 @@ struct GradArgs {
 struct TransArgs {
     const float* q;      // query cloud, packed [nq][P], bias slot = log2 w + log2e (pot - |q~|^2)/eps
     const float* k;      // key cloud, packed [nk][P], same bias from the key-side potential
+    const float* kbias;  // matrix-core layout: key biases [nk], else null
+    const float* qbias;  // matrix-core layout: query biases [nq], else null
+    const float* lse;    // matrix-core layout: row log-sum-exp of the scores [nq] (a first pass)
     const float* pay;    // payload: key j's columns at pay[j * ldp + c], c < kin
     const float* rowv;   // per-row direction [nq][d] (weighted mode), else null
     int nq, nk, P, d;
@@ -191,6 +194,12 @@ hipError_t launch_cost_mass(const float* a, const float* b, const float* f, cons
 // Transport products (sk_transport.hip).  mode 0: K-column payload, kwidth in
 // {1, 4, 9} (>= kin); mode 2: the Hessian-vector product's weighted pass.
 int transport_rows_per_block();
+// Matrix-core transport products (d > 8, sk_pass_mfma.hip): mode 0 with up to
+// 64 payload columns (kwidth 16 or 64), mode 1 (payload = the key coordinates),
+// mode 2 (weighted pass); needs lse from a kFinStore pass over the same scores.
+int mfma_transport_rows_per_block();
+hipError_t launch_transport_mfma(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0 = nullptr,
+                                 hipEvent_t ev1 = nullptr);
 // ev0 / ev1 (may be null): recorded right before and after the pass kernel (not the merge).
 hipError_t launch_transport(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0 = nullptr,
                             hipEvent_t ev1 = nullptr);

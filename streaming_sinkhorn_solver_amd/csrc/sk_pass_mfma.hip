@@ -350,6 +350,186 @@ hipError_t launch_grad_mfma_p(const GradArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+
+// Transport products for d > 8 (see sk_transport.hip for the d <= 8 kernel and
+// the quantities).  As in the gradient, w_ij = 2^{s_ij - lse_i} <= 1 with lse
+// from a first pass over the same scores, and the payload sums accumulate with
+// a second MFMA whose A operand is the lane's own four weights:
+//   T_i[col] = sum_j w_ij psi_j[col],   P psi = 2^{lse_i + h_i} T_i,
+//   row mass = 2^{lse_i + h_i} sum_j w_ij.
+//  MODE 0: psi_j = NP payload columns (16 * NP, zero-padded) staged in LDS;
+//  MODE 1: psi_j = the key's coordinates (read from the key tile);
+//  MODE 2: the key's coordinates with w_ij (pay_j + <y~_j, 2 v_i>), the inner
+//          product taken on the matrix cores like the score.
+template <int P, int NP, int MODE>
+__global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
+    constexpr int KT = P / 4;
+    constexpr int PS = P + 4;
+    constexpr int NB = MODE == 0 ? NP : P / 16;  // 16-column output blocks
+    constexpr int KP = MODE == 0 ? 16 * NP : 1;  // payload floats per key in LDS
+    constexpr int TL = mfma_tile_keys<P>();
+    __shared__ __align__(16) float ktile[TL * PS];
+    __shared__ __align__(16) float btile[TL];
+    __shared__ __align__(16) float ptile[MODE == 1 ? 1 : TL * KP];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const float4* kp = reinterpret_cast<const float4*>(A.k);
+    const int split = blockIdx.y;
+    const int c0 = split * A.cols_per_split;
+    const int c1 = min(c0 + A.cols_per_split, A.nk);
+    const int qrow0 = blockIdx.x * (kWaves * 16) + wave * 16;
+
+    float qf[KT], vf[KT];
+    {
+        const int i = qrow0 + c;
+        const int ic = i < A.nq ? i : A.nq - 1;
+        const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
+#pragma unroll
+        for (int t4 = 0; t4 < KT / 4; ++t4) {
+            const float4 v = qr[t4];
+            qf[4 * t4 + 0] = v.x * A.qscale;
+            qf[4 * t4 + 1] = v.y * A.qscale;
+            qf[4 * t4 + 2] = v.z * A.qscale;
+            qf[4 * t4 + 3] = v.w * A.qscale;
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            const int dim = g * KT + t;
+            vf[t] = (MODE == 2 && dim < A.d) ? 2.0f * A.rowv[(size_t)ic * A.d + dim] : 0.0f;
+        }
+    }
+    const float lse_c = A.lse[min(qrow0 + c, A.nq - 1)];
+    float S = 0.0f;
+    f4 T[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) T[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    TileStage<P> stage;
+    if (c0 < c1) stage.load(kp, A.kbias, c0, c1);
+    for (int base = c0; base < c1; base += TL) {
+        __syncthreads();
+        stage.store(ktile, btile);
+        if (MODE != 1)
+            for (int e = threadIdx.x; e < TL * KP; e += kBlock) {
+                const int col = base + e / KP;
+                const int cc = e % KP;
+                ptile[e] = (col < c1 && cc < A.kin) ? A.pay[(size_t)col * A.ldp + cc] : 0.0f;
+            }
+        __syncthreads();
+        if (base + TL < c1) stage.load(kp, A.kbias, base + TL, c1);
+        const int ntile = min(TL, c1 - base);
+        for (int kb = 0; kb < ntile; kb += 16) {
+            float kf[KT];
+            const float4* kr = reinterpret_cast<const float4*>(&ktile[(kb + c) * PS + g * KT]);
+#pragma unroll
+            for (int t4 = 0; t4 < KT / 4; ++t4) {
+                const float4 v = kr[t4];
+                kf[4 * t4 + 0] = v.x;
+                kf[4 * t4 + 1] = v.y;
+                kf[4 * t4 + 2] = v.z;
+                kf[4 * t4 + 3] = v.w;
+            }
+            f4 acc = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
+#pragma unroll
+            for (int t = 0; t < KT; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[t], acc, 0, 0, 0);
+            f4 dv = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (MODE == 2) {
+#pragma unroll
+                for (int t = 0; t < KT; ++t) dv = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], vf[t], dv, 0, 0, 0);
+            }
+            float wv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float w = ex2(acc[v] - lse_c);
+                S += w;
+                wv[v] = MODE == 2 ? w * (ptile[kb + 4 * g + v] + dv[v]) : w;
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float b = MODE == 0 ? ptile[(kb + 4 * g + v) * KP + nb * 16 + c]
+                                              : ktile[(kb + 4 * g + v) * PS + nb * 16 + c];
+                    T[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[v], b, T[nb], 0, 0, 0);
+                }
+        }
+    }
+    // S: lane (g, c) summed keys 4g.. of query c; join the four groups
+    S += __shfl_xor(S, 16);
+    S += __shfl_xor(S, 32);
+    constexpr int KA = 16 * NB;
+    if (A.nsplit == 1) {
+        if (g == 0 && qrow0 + c < A.nq && A.mass) {
+            const int i = qrow0 + c;
+            A.mass[i] = S * ex2(A.lse[i] + A.qbias[i]);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = qrow0 + 4 * g + v;
+            if (i >= A.nq) continue;
+            const float scale = ex2(A.lse[i] + A.qbias[i]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int col = nb * 16 + c;
+                if (col < A.kout) A.out[(size_t)i * A.ldo + col] = T[nb][v] * scale;
+            }
+        }
+    } else {
+        if (g == 0 && qrow0 + c < A.nq) A.part[(size_t)split * A.nq + qrow0 + c] = make_float2(0.0f, S);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = qrow0 + 4 * g + v;
+            if (i >= A.nq) continue;
+            float* pa = A.partA + ((size_t)split * A.nq + i) * KA;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) pa[nb * 16 + c] = T[nb][v];
+        }
+    }
+}
+
+// Sums the split partials (S, T) in split order, then applies the plan scale.
+__global__ __launch_bounds__(kBlock) void k_transport_mfma_merge(TransArgs A, int KA) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int cols = A.kout + 1;  // the payload columns, then the row mass
+    if (t >= (int64_t)A.nq * cols) return;
+    const int i = (int)(t / cols), col = (int)(t - (int64_t)i * cols);
+    const float scale = ex2(A.lse[i] + A.qbias[i]);
+    float acc = 0.0f;
+    if (col < A.kout) {
+        for (int s = 0; s < A.nsplit; ++s) acc += A.partA[((size_t)s * A.nq + i) * KA + col];
+        A.out[(size_t)i * A.ldo + col] = acc * scale;
+    } else if (A.mass) {
+        for (int s = 0; s < A.nsplit; ++s) acc += A.part[(size_t)s * A.nq + i].y;
+        A.mass[i] = acc * scale;
+    }
+}
+
+template <int P, int NP, int MODE>
+hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    constexpr int KA = MODE == 0 ? 16 * NP : P;
+    dim3 grid((a.nq + kWaves * 16 - 1) / (kWaves * 16), a.nsplit);
+    if (ev0) (void)hipEventRecord(ev0, s);
+    hipLaunchKernelGGL((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), 0, s, a);
+    if (ev1) (void)hipEventRecord(ev1, s);
+    if (a.nsplit > 1)
+        hipLaunchKernelGGL(k_transport_mfma_merge, dim3((unsigned)(((int64_t)a.nq * (a.kout + 1) + kBlock - 1) / kBlock)),
+                           dim3(kBlock), 0, s, a, KA);
+    return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_transport_mfma_pp(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0,
+                                    hipEvent_t ev1) {
+    if (mode == 1) return launch_transport_mfma_p<P, 1, 1>(a, s, ev0, ev1);
+    if (mode == 2) return launch_transport_mfma_p<P, 1, 2>(a, s, ev0, ev1);
+    if (kwidth == 16) return launch_transport_mfma_p<P, 1, 0>(a, s, ev0, ev1);
+    if constexpr (P >= 64) {  // a 64-column payload tile fits LDS beside the key tile from P = 64 on
+        if (kwidth == 64) return launch_transport_mfma_p<P, 4, 0>(a, s, ev0, ev1);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int P>
 hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
@@ -392,6 +572,20 @@ hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hi
 }
 
 int mfma_grad_rows_per_block() { return kWaves * 16; }
+
+int mfma_transport_rows_per_block() { return kWaves * 16; }
+
+hipError_t launch_transport_mfma(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0,
+                                 hipEvent_t ev1) {
+    switch (a.P) {
+        case 16: return launch_transport_mfma_pp<16>(a, mode, kwidth, s, ev0, ev1);
+        case 32: return launch_transport_mfma_pp<32>(a, mode, kwidth, s, ev0, ev1);
+        case 64: return launch_transport_mfma_pp<64>(a, mode, kwidth, s, ev0, ev1);
+        case 128: return launch_transport_mfma_pp<128>(a, mode, kwidth, s, ev0, ev1);
+        case 256: return launch_transport_mfma_pp<256>(a, mode, kwidth, s, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s) {
     switch (a.P) {

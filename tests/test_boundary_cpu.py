@@ -192,7 +192,8 @@ def test_gradient_flow_argument_errors(lib):
 def test_transport_and_hvp_argument_errors(lib):
     tb = lib.sk_transport_workspace_bytes(10, 12, 2)
     assert tb > lib.sk_workspace_bytes(10, 12, 2)
-    assert lib.sk_transport_workspace_bytes(10, 12, 9) == 0  # d > 8 not supported yet
+    assert lib.sk_transport_workspace_bytes(10, 12, 64) > lib.sk_workspace_bytes(10, 12, 64)
+    assert lib.sk_transport_workspace_bytes(10, 12, 257) == 0
     assert lib.sk_transport_workspace_bytes(0, 12, 2) == 0
     w1 = lib.sk_transport_workspace_bytes(10000, 12000, 3)
     w2 = lib.sk_transport_workspace_bytes(20000, 24000, 3)
@@ -203,7 +204,7 @@ def test_transport_and_hvp_argument_errors(lib):
                                       k.get("ws", FAKE), k.get("wb", tb), None)
     assert tr(x=None) == SK_ERR_NULL
     assert tr(g=None) == SK_ERR_NULL
-    assert tr(d=9) == SK_ERR_UNSUPPORTED_D
+    assert tr(d=257) == SK_ERR_UNSUPPORTED_D
     assert tr(d=0) == SK_ERR_SHAPE
     assert tr(eps=-1.0) == SK_ERR_EPS
     assert tr(k=0) == SK_ERR_SHAPE
@@ -214,7 +215,7 @@ def test_transport_and_hvp_argument_errors(lib):
                                 k.get("v", FAKE), k.get("it", 10), k.get("out", FAKE), None, FAKE, k.get("wb", tb), None)
     assert hv(v=None) == SK_ERR_NULL
     assert hv(out=None) == SK_ERR_NULL
-    assert hv(d=16) == SK_ERR_UNSUPPORTED_D
+    assert hv(d=300) == SK_ERR_UNSUPPORTED_D
     assert hv(it=-1) == SK_ERR_ITERS
     assert hv(wb=100) == SK_ERR_WORKSPACE
 

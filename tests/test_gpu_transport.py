@@ -63,6 +63,12 @@ TRANSPORT_CASES = [
     (900, 1300, 5, 0.3, 5, 9, False, 6, 0.0),
     (1300, 700, 8, 0.5, 5, 11, True, 7, 0.05),
     (3000, 2500, 4, 0.2, 5, 7, False, 8, 0.0),
+    # matrix cores (d > 8): a log-sum-exp pass, then weights <= 1 into a second MFMA
+    (900, 700, 16, 0.3, 5, 1, False, 9, 0.0),
+    (700, 900, 64, 0.5, 5, 70, True, 10, 0.05),
+    (300, 500, 130, 0.5, 4, 5, False, 11, 0.0),
+    (17, 5, 64, 0.2, 3, 3, True, 12, 0.0),
+    (2600, 3100, 33, 0.3, 4, 16, False, 13, 0.0),
 ]
 
 
@@ -101,6 +107,11 @@ HVP_CASES = [
     (700, 600, 1, 0.2, 500, 150, 14),
     (500, 800, 8, 1.0, 200, 60, 15),
     (900, 700, 5, 0.5, 100, 80, 16),  # away from the optimum: the same formula at that plan
+    # matrix cores (d > 8)
+    (600, 500, 16, 0.5, 200, 80, 17),
+    (500, 700, 64, 1.0, 200, 60, 18),
+    (200, 300, 130, 1.0, 100, 60, 19),
+    (1, 9, 64, 0.5, 50, 20, 20),
 ]
 
 
