@@ -38,6 +38,7 @@
  * Sources (page title and section):
  *  FS   = "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",
  *         technical summary, Methodology 1-3.
+ *  FS2  = "FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport", abstract.
  *  SLOT = SinkSLOT README: opening section, Tensor Contract, Gradient Flow,
  *         API Reference, Low-Level Solver API.
  */
@@ -302,6 +303,60 @@ int sk_hvp(const float *x, const float *y, const float *a, const float *b,
            int64_t n, int64_t m, int32_t d, float eps,
            const float *f, const float *g, const float *v, int32_t cg_iters,
            float *out, float *cg_resid, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Workspace bytes of sk_fs2_solve for the given block size and sample count
+ * (0 for invalid arguments, or when the radix sort's scratch size cannot be
+ * queried because no device is present).
+ */
+size_t sk_fs2_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t block, int32_t n_sample);
+
+/*
+ * Two-stage block-sparse solver (FS2): a coarse stage on block centroids, then
+ * block-sparse point-level iterations, for low-dimensional clouds (1 <= d <= 8).
+ * The pages describe it only in outline; the steps taken are:
+ *  1. Morton order of each cloud in the bounding box of both (float32
+ *     quantisation to 30 / d bits per coordinate, at most 10; a stable radix
+ *     sort of (code, index)), and blocks of `block` consecutive points
+ *     (1 <= block <= 512) with their mass, weighted centroid and box;
+ *  2. coarse stage: alternating Sinkhorn on the centroid measures (from G = 0,
+ *     then continuing) in rounds of coarse_iters; after each round both
+ *     potentials are lifted to the points by one c-transform against the
+ *     other side's centroids, and the check value is the largest row
+ *     deviation |(P1)_i - a_i| of the lifted plan over n_sample evenly spaced
+ *     rows (P over all points).  The coarse stage ends when the check value
+ *     is <= tol, or fell by less than the fraction coarse_gain since the last
+ *     round, or after max_rounds rounds;
+ *  3. fine stage from the lifted potentials: before every screen_every-th
+ *     iteration each block pair (I, J) gets the bound
+ *       (max_I f + max_J g - dmin_IJ^2)/eps + log max(B_J NBy, A_I NBx)
+ *     (dmin the distance between the blocks' boxes; maxima over points of
+ *     positive weight; NBx, NBy the block counts) and is kept iff it exceeds
+ *     log delta (every pair when delta = 0), so that the omitted pairs add at
+ *     most delta a_i to any row's and delta b_j to any column's mass; each
+ *     block also keeps its pair of largest bound.  Each iteration is a row
+ *     and a column half-step over kept pairs only (one workgroup per query
+ *     block, scanning only its kept key blocks); after every check_every-th
+ *     iteration and the last, the row residual of the kept-pair plan (its
+ *     column sums are exact) is checked and the stage stops at <= tol.
+ * Outputs f, g (device, caller's order).  info_i (host, 4): coarse rounds,
+ * fine iterations, kept block pairs at the last screening, converged (0/1);
+ * info_f (host, 2): last fine residual (NaN without a check), last coarse
+ * check value.  perm_x, perm_y (device, n and m ints, or NULL) receive the
+ * Morton order (original index of each sorted point).  Host-synchronous
+ * (the checks are read back); refuses graph capture (SK_ERR_CAPTURE).
+ * Also SK_ERR_SHAPE for a block outside [1, 512] or more than 2^26 block
+ * pairs, SK_ERR_STOP for a negative or non-finite tol, delta or coarse_gain,
+ * SK_ERR_ITERS for counts below 1 (max_iters may be 0).
+ */
+int sk_fs2_solve(const float *x, const float *y, const float *a, const float *b,
+                 int64_t n, int64_t m, int32_t d, float eps, int32_t block,
+                 float tol, float delta, int32_t coarse_iters, int32_t max_rounds,
+                 float coarse_gain, int32_t n_sample, int32_t max_iters,
+                 int32_t check_every, int32_t screen_every,
+                 float *f, float *g, int32_t *info_i, float *info_f,
+                 int32_t *perm_x, int32_t *perm_y,
+                 void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Kernel timing of the streamed log-sum-exp passes (benchmark diagnostics).

@@ -64,6 +64,10 @@ SIGNATURES = {
                                     _sz, _vp]),
     "sk_hvp": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
                               _vp]),
+    "sk_fs2_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32, _i32]),
+    "sk_fs2_solve": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _f32, _f32, _i32, _i32, _f32,
+                                    _i32, _i32, _i32, _i32, _vp, _vp, ctypes.POINTER(_i32), ctypes.POINTER(_f32), _vp,
+                                    _vp, _vp, _sz, _vp]),
     "sk_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "sk_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                       ctypes.POINTER(ctypes.c_double)]),
@@ -355,6 +359,41 @@ def hvp(x, y, a, b, f, g, v, *, eps: float, cg_iters: int = 50, ws: torch.Tensor
     return out, cg_resid
 
 
+def fs2_solve(x, y, a=None, b=None, *, eps: float, block: int = 512, tol: float = 1e-4, delta: float = 1e-6,
+              coarse_iters: int = 20, max_rounds: int = 10, coarse_gain: float = 0.1, n_sample: int = 1024,
+              max_iters: int = 1000, check_every: int = 10, screen_every: int = 10, ws: torch.Tensor | None = None,
+              f: torch.Tensor | None = None, g: torch.Tensor | None = None, return_perm: bool = False,
+              check: bool = True):
+    """Two-stage block-sparse solver (d <= 8).  Returns (f, g, info); info holds rounds, fine_iters,
+    kept (block pairs at the last screening), kept_fraction, converged, residual, last_check and,
+    with return_perm, the Morton orders perm_x, perm_y (device int32)."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    if check:
+        check_inputs(x, y, a, b)
+    if ws is None:
+        nb = int(lib.sk_fs2_workspace_bytes(n, m, d, int(block), int(n_sample)))
+        if nb == 0:
+            raise ValueError(f"invalid arguments for the block-sparse solver (n={n} m={m} d={d} block={block})")
+        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
+    f = f if f is not None else torch.empty(n, dtype=torch.float32, device=x.device)
+    g = g if g is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+    px = torch.empty(n, dtype=torch.int32, device=x.device) if return_perm else None
+    py = torch.empty(m, dtype=torch.int32, device=x.device) if return_perm else None
+    ii = (ctypes.c_int32 * 4)()
+    ff = (ctypes.c_float * 2)()
+    _raise(lib.sk_fs2_solve(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(block), float(tol),
+                            float(delta), int(coarse_iters), int(max_rounds), float(coarse_gain), int(n_sample),
+                            int(max_iters), int(check_every), int(screen_every), _ptr(f), _ptr(g), ii, ff, _ptr(px),
+                            _ptr(py), _ptr(ws), ws.numel(), _stream(x.device)), "sk_fs2_solve")
+    nbx, nby = (n + block - 1) // block, (m + block - 1) // block
+    info = dict(rounds=ii[0], fine_iters=ii[1], kept=ii[2], kept_fraction=ii[2] / (nbx * nby), converged=bool(ii[3]),
+                residual=ff[0], last_check=ff[1])
+    if return_perm:
+        info["perm_x"], info["perm_y"] = px, py
+    return f, g, info
+
+
 def cost(a, b, f, g, *, eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
     """<a,f> + <b,g> - eps sum(b)(1 - sum(a)) in float64 (a 1-element device tensor)."""
     lib = load_library()
@@ -415,7 +454,7 @@ def timing_read() -> tuple[float, int, float]:
     return ms.value, n.value, pairs.value
 
 
-__all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "gradient_flow", "transport", "hvp",
+__all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "gradient_flow", "transport", "hvp", "fs2_solve",
            "transport_workspace", "cost", "dual_cost", "divergence",
            "divergence_workspace", "marginal_residual", "grad_x", "check_inputs", "workspace", "workspace_bytes",
            "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES", "VARIANTS", "STOP_MODES"]

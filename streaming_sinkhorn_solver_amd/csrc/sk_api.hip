@@ -165,6 +165,19 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
     return p;
 }
 
+// Points a pass at other query / key arrays (same packed layout) and resizes
+// its stream-K decomposition; nq <= n and nk <= m of the layout keep the
+// partials within the workspace.
+void retarget(PassArgs& p, const float* q, int64_t nq, const float* k, int64_t nk, int capacity) {
+    p.q = q;
+    p.k = k;
+    p.nq = (int)nq;
+    p.nk = (int)nk;
+    p.total = (nq + p.rpb - 1) / p.rpb * nk;
+    p.W = (int)std::min<int64_t>(groups_bound(nq, nk, p.rpb), std::max(capacity, 1));
+    p.small = (!(p.kbias) && (double)nq * (double)nk <= kSmallPairs) ? 1 : 0;
+}
+
 // Optional event timing of the pass kernels (sk_timing_enable / sk_timing_read).
 struct Timing {
     std::mutex mu;
@@ -698,6 +711,284 @@ int transport_cols(const Ws& W, const TLayout& T, bool row_side, float eps, cons
 
 int check_transport_sizes(int64_t n, int64_t m, int32_t d) { return check_sizes(n, m, d); }
 
+// ---------------------------------------------------------------- two-stage block-sparse solver
+// Workspace: the solver layout of the problem in block order, the layout of
+// the centroid problem, and the sort, block, lift, sample and tile arrays.
+struct FLayout {
+    Layout L, Lc;
+    int B, nbx, nby, ns, bits;
+    size_t coarse;
+    size_t box, boxpart, code_in, code_out, idx_in, idx_out, sort_temp, sort_bytes;
+    size_t xs, ys, as, bs, permx, permy;
+    size_t amass, bmass, xcen, ycen, xlo, xhi, ylo, yhi, fmax, gmax, F, G;
+    size_t ky, kx, knrm, kl2w;
+    size_t sq, sf, sa, snrm;
+    size_t fs, gs;
+    size_t score, keep, rcnt, rptr, ridx, ccnt, cptr, cidx;
+    size_t total;
+};
+
+constexpr int64_t kMaxTiles = (int64_t)1 << 26;  // block pairs of the tile matrices
+
+int morton_bits_for(int d) { return std::max(1, std::min(10, 30 / d)); }
+
+// false when the sort's scratch size cannot be queried
+bool make_flayout(int64_t n, int64_t m, int d, int B, int n_sample, FLayout* out) {
+    FLayout F{};
+    F.L = make_layout(n, m, d);
+    F.B = B;
+    F.nbx = (int)((n + B - 1) / B);
+    F.nby = (int)((m + B - 1) / B);
+    F.Lc = make_layout(F.nbx, F.nby, d);
+    F.ns = (int)std::min<int64_t>(n, n_sample);
+    F.bits = morton_bits_for(d);
+    size_t off = align_up(F.L.total, 256);
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align_up(off + std::max<size_t>(bytes, 1), 256);
+        return o;
+    };
+    const size_t un = (size_t)n, um = (size_t)m, ud = (size_t)d, umx = (size_t)std::max(n, m);
+    const size_t bx = (size_t)F.nbx, by = (size_t)F.nby, bmx = std::max(bx, by), P = (size_t)F.L.P;
+    F.coarse = take(F.Lc.total);
+    F.box = take(2 * ud * 4);
+    F.boxpart = take((size_t)kRedBlocks * 2 * ud * 4);
+    F.code_in = take(umx * 4);
+    F.code_out = take(umx * 4);
+    F.idx_in = take(umx * 4);
+    F.idx_out = take(umx * 4);
+    F.sort_bytes = sort_temp_bytes((int)umx, F.bits * d);
+    if (F.sort_bytes == 0) return false;
+    F.sort_temp = take(F.sort_bytes);
+    F.xs = take(un * ud * 4);
+    F.ys = take(um * ud * 4);
+    F.as = take(un * 4);
+    F.bs = take(um * 4);
+    F.permx = take(un * 4);
+    F.permy = take(um * 4);
+    F.amass = take(bx * 4);
+    F.bmass = take(by * 4);
+    F.xcen = take(bx * ud * 4);
+    F.ycen = take(by * ud * 4);
+    F.xlo = take(bx * ud * 4);
+    F.xhi = take(bx * ud * 4);
+    F.ylo = take(by * ud * 4);
+    F.yhi = take(by * ud * 4);
+    F.fmax = take(bx * 4);
+    F.gmax = take(by * 4);
+    F.F = take(bx * 4);
+    F.G = take(by * 4);
+    F.ky = take(by * P * 4);
+    F.kx = take(bx * P * 4);
+    F.knrm = take(bmx * 4);
+    F.kl2w = take(bmx * 4);
+    F.sq = take((size_t)F.ns * P * 4);
+    F.sf = take((size_t)F.ns * 4);
+    F.sa = take((size_t)F.ns * 4);
+    F.snrm = take((size_t)F.ns * 4);
+    F.fs = take(un * 4);
+    F.gs = take(um * 4);
+    F.score = take(bx * by * 4);
+    F.keep = take(bx * by);
+    F.rcnt = take(bx * 4);
+    F.rptr = take((bx + 1) * 4);
+    F.ridx = take(bx * by * 4);
+    F.ccnt = take(by * 4);
+    F.cptr = take((by + 1) * 4);
+    F.cidx = take(bx * by * 4);
+    F.total = off;
+    *out = F;
+    return true;
+}
+
+struct Fs2Opts {
+    int B;
+    float tol, delta;
+    int coarse_iters, max_rounds;
+    float coarse_gain;
+    int n_sample, max_iters, check_every, screen_every;
+};
+
+struct Fs2Info {
+    int rounds = 0, fine_iters = 0, kept = 0, converged = 0;
+    float residual = NAN, last_check = NAN;
+};
+
+// Morton order of one cloud: codes, stable radix sort of (code, index), gather.
+int morton_sort(char* base, const FLayout& F, const float* p, const float* w, int npts, int d, float* ps, float* ws,
+                int* perm, hipStream_t s) {
+    uint32_t *cin = reinterpret_cast<uint32_t*>(base + F.code_in), *cout = reinterpret_cast<uint32_t*>(base + F.code_out);
+    uint32_t *iin = reinterpret_cast<uint32_t*>(base + F.idx_in), *iout = reinterpret_cast<uint32_t*>(base + F.idx_out);
+    SK_TRY(launch_morton(p, npts, d, F.bits, reinterpret_cast<float*>(base + F.box), cin, iin, s));
+    SK_TRY(launch_sort_pairs(base + F.sort_temp, F.sort_bytes, cin, cout, iin, iout, npts, F.bits * d, s));
+    SK_TRY(launch_gather_points(p, w, iout, npts, d, ps, ws, perm, s));
+    return SK_OK;
+}
+
+int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, const float* a, const float* b, float eps,
+              const Fs2Opts& o, float* f_out, float* g_out, int* perm_x, int* perm_y, Fs2Info* info, hipStream_t s) {
+    const Layout& L = F.L;
+    const int n = (int)L.n, m = (int)L.m, d = L.d;
+    Ws W{L, base};
+    Ws Wc{F.Lc, base + F.coarse};
+    auto fp = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+    auto ip = [&](size_t off) { return reinterpret_cast<int*>(base + off); };
+    float *xs = fp(F.xs), *ys = fp(F.ys), *as = fp(F.as), *bs = fp(F.bs);
+    float *fs = fp(F.fs), *gs = fp(F.gs), *Fc = fp(F.F), *Gc = fp(F.G);
+    int st;
+    const int cap = pass_capacity(d);
+    if (cap <= 0) return SK_ERR_HIP;
+    HostSlot slot;
+    if ((st = slot.acquire())) return st;
+    float host[2];
+
+    // 1-2: Morton order and blocks
+    SK_TRY(launch_bbox(x, n, y, m, d, fp(F.boxpart), fp(F.box), s));
+    if ((st = morton_sort(base, F, x, a, n, d, xs, as, ip(F.permx), s))) return st;
+    if ((st = morton_sort(base, F, y, b, m, d, ys, bs, ip(F.permy), s))) return st;
+    if ((st = prepare(W, xs, ys, as, bs, eps, 0, nullptr, 1, nullptr, s))) return st;
+    SK_TRY(launch_block_stats(xs, as, n, d, F.B, fp(F.amass), fp(F.xcen), fp(F.xlo), fp(F.xhi), s));
+    SK_TRY(launch_block_stats(ys, bs, m, d, F.B, fp(F.bmass), fp(F.ycen), fp(F.ylo), fp(F.yhi), s));
+
+    // 3: coarse stage on the centroids, lifted to the points after every round
+    PassArgs lift_f = make_pass(W, true, eps, as, cap);
+    lift_f.fin.pot = fs;
+    retarget(lift_f, W.f(L.xp), n, fp(F.ky), F.nby, cap);
+    PassArgs lift_g = make_pass(W, false, eps, bs, cap);
+    lift_g.fin.pot = gs;
+    retarget(lift_g, W.f(L.yp), m, fp(F.kx), F.nbx, cap);
+    PassArgs check = make_pass(W, true, eps, as, cap);
+    check.fin.mode = kFinResid;
+    check.fin.w = fp(F.sa);
+    check.fin.nrm = fp(F.snrm);
+    check.fin.pot_in = fp(F.sf);
+    check.fin.rbuf = W.f(L.rbuf);
+    retarget(check, fp(F.sq), F.ns, W.f(L.yp), m, cap);
+    const int stride = n / F.ns;
+    float prev = NAN;
+    for (int round = 1;; ++round) {
+        if ((st = prepare(Wc, fp(F.xcen), fp(F.ycen), fp(F.amass), fp(F.bmass), eps, 0, nullptr, round == 1 ? 1 : 2,
+                          Gc, s)))
+            return st;
+        PassArgs row = make_pass(Wc, true, eps, fp(F.amass), cap);
+        row.fin.pot = Fc;
+        PassArgs col = make_pass(Wc, false, eps, fp(F.bmass), cap);
+        col.fin.pot = Gc;
+        for (int k = 0; k < o.coarse_iters; ++k) {
+            if ((st = run_pass(Wc, row, s))) return st;
+            if ((st = run_pass(Wc, col, s))) return st;
+        }
+        // lift: one c-transform of each side against the other side's centroids
+        SK_TRY(launch_pack(fp(F.ycen), F.nby, d, L.P, false, W.f(L.centre), fp(F.bmass), fp(F.ky), fp(F.knrm),
+                           fp(F.kl2w), nullptr, 1.0f / eps, 2, Gc, nullptr, s));
+        if ((st = run_pass(W, lift_f, s))) return st;
+        SK_TRY(launch_pack(fp(F.xcen), F.nbx, d, L.P, false, W.f(L.centre), fp(F.amass), fp(F.kx), fp(F.knrm),
+                           fp(F.kl2w), nullptr, 1.0f / eps, 2, Fc, nullptr, s));
+        if ((st = run_pass(W, lift_g, s))) return st;
+        // sampled check of the lifted plan's rows over all points
+        SK_TRY(launch_gather_rows(W.f(L.xp), L.P, fs, as, W.f(L.nx), F.ns, stride, fp(F.sq), fp(F.sf), fp(F.sa),
+                                  fp(F.snrm), s));
+        if ((st = run_pass(W, check, s))) return st;
+        SK_TRY(launch_resid_reduce(W.f(L.rbuf), F.ns, slot.dev(), nullptr, s, slot.flag(), slot.next()));
+        if ((st = slot.read(host, 1, s))) return st;
+        info->rounds = round;
+        info->last_check = host[0];
+        if (host[0] <= o.tol || round >= o.max_rounds) break;
+        if (round >= 2 && host[0] > (1.0f - o.coarse_gain) * prev) break;
+        prev = host[0];
+    }
+
+    // 4-5: block-sparse fine stage from the lifted potentials
+    ScreenArgs sa{};
+    sa.fmax = fp(F.fmax);
+    sa.gmax = fp(F.gmax);
+    sa.amass = fp(F.amass);
+    sa.bmass = fp(F.bmass);
+    sa.xlo = fp(F.xlo);
+    sa.xhi = fp(F.xhi);
+    sa.ylo = fp(F.ylo);
+    sa.yhi = fp(F.yhi);
+    sa.nbx = F.nbx;
+    sa.nby = F.nby;
+    sa.d = d;
+    sa.eps = eps;
+    sa.delta = o.delta;
+    sa.log_delta = o.delta > 0.0f ? (float)std::log((double)o.delta) : -INFINITY;
+    sa.score = fp(F.score);
+    sa.keep = reinterpret_cast<uint8_t*>(base + F.keep);
+    SparseArgs rowp{}, colp{};
+    rowp.q = W.f(L.xp);
+    rowp.k = W.f(L.yp);
+    rowp.nq = n;
+    rowp.nk = m;
+    rowp.B = F.B;
+    rowp.qscale = 2.0f * kLog2e / eps;
+    rowp.ptr = ip(F.rptr);
+    rowp.idx = ip(F.ridx);
+    rowp.fin = make_pass(W, true, eps, as, cap).fin;
+    rowp.fin.pot = fs;
+    colp = rowp;
+    colp.q = W.f(L.yp);
+    colp.k = W.f(L.xp);
+    colp.nq = m;
+    colp.nk = n;
+    colp.ptr = ip(F.cptr);
+    colp.idx = ip(F.cidx);
+    colp.fin = make_pass(W, false, eps, bs, cap).fin;
+    colp.fin.pot = gs;
+    SparseArgs probe = rowp;
+    probe.fin.mode = kFinProbe;
+    probe.fin.rbuf = W.f(L.rbuf);
+    for (int it = 1; it <= o.max_iters; ++it) {
+        if ((it - 1) % o.screen_every == 0) {
+            SK_TRY(launch_block_max(fs, as, n, F.B, fp(F.fmax), s));
+            SK_TRY(launch_block_max(gs, bs, m, F.B, fp(F.gmax), s));
+            SK_TRY(launch_screen(sa, ip(F.rcnt), ip(F.rptr), ip(F.ridx), ip(F.ccnt), ip(F.cptr), ip(F.cidx), s));
+        }
+        SK_TRY(launch_pass_sparse(rowp, d, s));
+        SK_TRY(launch_pass_sparse(colp, d, s));
+        info->fine_iters = it;
+        if (it % o.check_every == 0 || it == o.max_iters) {
+            SK_TRY(launch_pass_sparse(probe, d, s));
+            SK_TRY(launch_resid_reduce(W.f(L.rbuf), n, slot.dev(), nullptr, s, slot.flag(), slot.next()));
+            if ((st = slot.read(host, 1, s))) return st;
+            info->residual = host[0];
+            if (host[0] <= o.tol) {
+                info->converged = 1;
+                break;
+            }
+        }
+    }
+    if (o.max_iters > 0) {
+        int kept = 0;
+        SK_TRY(hipMemcpyAsync(&kept, ip(F.rptr) + F.nbx, sizeof(int), hipMemcpyDeviceToHost, s));
+        SK_TRY(hipStreamSynchronize(s));
+        info->kept = kept;
+    }
+    SK_TRY(launch_scatter(fs, ip(F.permx), n, f_out, s));
+    SK_TRY(launch_scatter(gs, ip(F.permy), m, g_out, s));
+    if (perm_x) SK_TRY(hipMemcpyAsync(perm_x, ip(F.permx), (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+    if (perm_y) SK_TRY(hipMemcpyAsync(perm_y, ip(F.permy), (size_t)m * 4, hipMemcpyDeviceToDevice, s));
+    return SK_OK;
+}
+
+int check_fs2(int64_t n, int64_t m, int32_t d, const Fs2Opts& o) {
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if (d > kValuMaxD) return SK_ERR_UNSUPPORTED_D;
+    if (o.B < 1 || o.B > valu_rows_per_block()) return SK_ERR_SHAPE;
+    const int64_t nbx = (n + o.B - 1) / o.B, nby = (m + o.B - 1) / o.B;
+    if (nbx * nby > kMaxTiles) return SK_ERR_SHAPE;
+    if (!(o.tol >= 0.0f) || !std::isfinite(o.tol) || !(o.delta >= 0.0f) || !std::isfinite(o.delta) ||
+        !std::isfinite(o.coarse_gain))
+        return SK_ERR_STOP;
+    if (o.coarse_iters < 1 || o.max_rounds < 1 || o.n_sample < 1 || o.max_iters < 0 || o.check_every < 1 ||
+        o.screen_every < 1)
+        return SK_ERR_ITERS;
+    return SK_OK;
+}
+
+
 int check_ex(int variant, float alpha, int stop_mode, float tol, int max_iter, int check_every) {
     if (variant != 0 && variant != 1) return SK_ERR_VARIANT;
     if (variant == 1 && !(alpha > 0.0f && alpha <= 1.0f)) return SK_ERR_VARIANT;
@@ -1042,6 +1333,43 @@ int sk_hvp(const float* x, const float* y, const float* a, const float* b, int64
     // E = sum_j P_ij (psi_j + 2 <y~_j, v_i>) y~_j, then the product
     if ((st = transport_pass(W, T, true, eps, 2, zb + in, 1, 1, v, E, d, d, nullptr, s))) return st;
     SK_TRY(launch_hvp_final(in, d, eps, v, diag, stv, zb, A, E, out, s));
+    return SK_OK;
+}
+
+size_t sk_fs2_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t block, int32_t n_sample) {
+    Fs2Opts o{block, 0.0f, 0.0f, 1, 1, 0.0f, std::max(n_sample, 1), 0, 1, 1};
+    if (check_fs2(n, m, d, o) != SK_OK) return 0;
+    FLayout F;
+    if (!make_flayout(n, m, d, block, std::max(n_sample, 1), &F)) return 0;
+    return F.total;
+}
+
+int sk_fs2_solve(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+                 float eps, int32_t block, float tol, float delta, int32_t coarse_iters, int32_t max_rounds,
+                 float coarse_gain, int32_t n_sample, int32_t max_iters, int32_t check_every, int32_t screen_every,
+                 float* f, float* g, int32_t* info_i, float* info_f, int32_t* perm_x, int32_t* perm_y, void* ws,
+                 size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g || !info_i || !info_f) return SK_ERR_NULL;
+    int st;
+    if ((st = check_eps(eps))) return st;
+    const Fs2Opts o{block, tol, delta, coarse_iters, max_rounds, coarse_gain, n_sample, max_iters, check_every,
+                    screen_every};
+    if ((st = check_fs2(n, m, d, o))) return st;
+    FLayout F;
+    if (!make_flayout(n, m, d, block, n_sample, &F)) return SK_ERR_HIP;
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) % 256) != 0 || ws_bytes < F.total) return SK_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return SK_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return SK_ERR_CAPTURE;
+    Fs2Info info;
+    if ((st = fs2_solve(static_cast<char*>(ws), F, x, y, a, b, eps, o, f, g, perm_x, perm_y, &info, s))) return st;
+    info_i[0] = info.rounds;
+    info_i[1] = info.fine_iters;
+    info_i[2] = info.kept;
+    info_i[3] = info.converged;
+    info_f[0] = info.residual;
+    info_f[1] = info.last_check;
     return SK_OK;
 }
 

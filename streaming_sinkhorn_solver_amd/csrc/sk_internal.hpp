@@ -127,6 +127,30 @@ struct GradArgs {
     const float* lse;    // [nq] row log-sum-exp (matrix-core gradient, from a first pass)
 };
 
+// Arguments of a block-sparse pass (d <= 8): query block I (rows
+// [I B, (I + 1) B)) scans the key blocks idx[ptr[I] .. ptr[I + 1]) (keys
+// [J B, (J + 1) B)); rows and keys are in block (Morton) order.
+struct SparseArgs {
+    const float* q;      // query cloud, packed [nq][P]
+    const float* k;      // key cloud, packed [nk][P]
+    int nq, nk, B;
+    float qscale;        // 2 log2e / eps
+    const int* ptr;      // [n_query_blocks + 1]
+    const int* idx;      // kept key blocks
+    Fin fin;
+};
+
+// Tile bounds of the block-sparse fine stage (sk_fs2.hip).
+struct ScreenArgs {
+    const float *fmax, *gmax;    // per-block maxima of the potentials (points of positive weight)
+    const float *amass, *bmass;  // block masses
+    const float *xlo, *xhi, *ylo, *yhi;  // block boxes [blocks][d]
+    int nbx, nby, d;
+    float eps, delta, log_delta;
+    float* score;                // [nbx][nby]
+    uint8_t* keep;               // [nbx][nby]
+};
+
 // Arguments of a streamed transport product (d <= 8; see sk_transport.hip).
 struct TransArgs {
     const float* q;      // query cloud, packed [nq][P], bias slot = log2 w + log2e (pot - |q~|^2)/eps
@@ -214,6 +238,24 @@ hipError_t launch_cg_step(int N, int n, const float* diag, const float* prod, fl
                           double* scal, hipStream_t s);
 hipError_t launch_cg_report(const double* scal, float* out, hipStream_t s);
 
+// Two-stage block-sparse solver pieces (sk_fs2.hip).
+hipError_t launch_bbox(const float* x, int n, const float* y, int m, int d, float* part, float* box, hipStream_t s);
+hipError_t launch_morton(const float* p, int n, int d, int bits, const float* box, uint32_t* code, uint32_t* idx,
+                         hipStream_t s);
+size_t sort_temp_bytes(int n, int end_bit);  // 0 when the size cannot be queried
+hipError_t launch_sort_pairs(void* temp, size_t temp_bytes, const uint32_t* kin, uint32_t* kout, const uint32_t* vin,
+                             uint32_t* vout, int n, int end_bit, hipStream_t s);
+hipError_t launch_gather_points(const float* p, const float* w, const uint32_t* idx, int n, int d, float* ps, float* ws,
+                                int* perm, hipStream_t s);
+hipError_t launch_block_stats(const float* ps, const float* ws, int n, int d, int B, float* mass, float* cen,
+                              float* blo, float* bhi, hipStream_t s);
+hipError_t launch_gather_rows(const float* qp, int P, const float* pot, const float* w, const float* nrm, int ns,
+                              int stride, float* qs, float* pots, float* ws, float* nrms, hipStream_t s);
+hipError_t launch_block_max(const float* pot, const float* w, int n, int B, float* out, hipStream_t s);
+hipError_t launch_screen(const ScreenArgs& a, int* rcnt, int* rptr, int* ridx, int* ccnt, int* cptr, int* cidx,
+                         hipStream_t s);
+hipError_t launch_scatter(const float* in, const int* perm, int n, float* out, hipStream_t s);
+
 // v <- v + alpha * u over count floats.
 hipError_t launch_axpy(float* v, const float* u, int64_t count, float alpha, hipStream_t s);
 // out[0] = out[1] - out[2] / 2 - out[3] / 2.
@@ -233,6 +275,9 @@ hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t 
                             hipEvent_t ev1 = nullptr);
 hipError_t launch_grad_valu(const GradArgs& a, hipStream_t s);
 int valu_rows_per_block();
+// Block-sparse vector-ALU pass (B <= 512 rows per query block).
+hipError_t launch_pass_sparse(const SparseArgs& a, int d, hipStream_t s, hipEvent_t ev0 = nullptr,
+                              hipEvent_t ev1 = nullptr);
 // Merges the partial (M, S) pairs of row blocks split across workgroups (no
 // launch when every row block was finished by one workgroup).
 hipError_t launch_merge(const PassArgs& a, hipStream_t s);

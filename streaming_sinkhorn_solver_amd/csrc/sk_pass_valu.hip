@@ -113,6 +113,39 @@ __device__ __forceinline__ void scan_keys(float4* tile, const float4* __restrict
     }
 }
 
+// Block-sparse pass: one workgroup per query block of B <= kBlock * kR rows,
+// scanning only the key blocks listed for it (a CSR list of kept tiles; both
+// clouds are in block order, so a key block is a contiguous key range).
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_pass_sparse(SparseArgs A) {
+    constexpr int P = ((D + 1 + 3) / 4) * 4;
+    __shared__ float4 tile[kTL * (P / 4)];
+    const float4* kp = reinterpret_cast<const float4*>(A.k);
+    const int I = blockIdx.x;
+    const int r0 = I * A.B;
+    const int r1 = min(r0 + A.B, A.nq);
+    float q[kR][D], M[kR], S[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int i = r0 + threadIdx.x + r * kBlock;
+        const int ic = i < r1 ? i : r1 - 1;
+#pragma unroll
+        for (int t = 0; t < D; ++t) q[r][t] = A.q[(size_t)ic * P + t] * A.qscale;
+        M[r] = kNegBig;
+        S[r] = 0.0f;
+    }
+    const int t1 = A.ptr[I + 1];
+    for (int t = A.ptr[I]; t < t1; ++t) {
+        const int j0 = A.idx[t] * A.B;
+        scan_keys<D>(tile, kp, q, M, S, j0, min(j0 + A.B, A.nk));
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        const int i = r0 + threadIdx.x + r * kBlock;
+        if (i < r1) finalize(A.fin, i, M[r] + lg2(S[r]));
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
     constexpr int P = ((D + 1 + 3) / 4) * 4;
@@ -461,6 +494,29 @@ hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t 
         case 6: return launch_pass_d<6>(a, s, ev0, ev1);
         case 7: return launch_pass_d<7>(a, s, ev0, ev1);
         case 8: return launch_pass_d<8>(a, s, ev0, ev1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D>
+hipError_t launch_sparse_d(const SparseArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (ev0) (void)hipEventRecord(ev0, s);
+    hipLaunchKernelGGL(k_pass_sparse<D>, dim3((a.nq + a.B - 1) / a.B), dim3(kBlock), 0, s, a);
+    if (ev1) (void)hipEventRecord(ev1, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_pass_sparse(const SparseArgs& a, int d, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (a.B < 1 || a.B > kBlock * kR) return hipErrorInvalidValue;
+    switch (d) {
+        case 1: return launch_sparse_d<1>(a, s, ev0, ev1);
+        case 2: return launch_sparse_d<2>(a, s, ev0, ev1);
+        case 3: return launch_sparse_d<3>(a, s, ev0, ev1);
+        case 4: return launch_sparse_d<4>(a, s, ev0, ev1);
+        case 5: return launch_sparse_d<5>(a, s, ev0, ev1);
+        case 6: return launch_sparse_d<6>(a, s, ev0, ev1);
+        case 7: return launch_sparse_d<7>(a, s, ev0, ev1);
+        case 8: return launch_sparse_d<8>(a, s, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }

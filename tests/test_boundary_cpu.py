@@ -30,7 +30,7 @@ def lib():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sk_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sk_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_entry_points():
@@ -38,7 +38,7 @@ def test_header_declares_entry_points():
     for must in ("sk_solve", "sk_cost", "sk_marginal_residual", "sk_grad_x", "sk_workspace_bytes",
                  "sk_check_inputs", "sk_status_string", "sk_abi_version", "sk_solve_ex", "sk_dual_cost",
                  "sk_divergence", "sk_divergence_workspace_bytes", "sk_gradient_flow", "sk_transport",
-                 "sk_transport_workspace_bytes", "sk_hvp"):
+                 "sk_transport_workspace_bytes", "sk_hvp", "sk_fs2_solve", "sk_fs2_workspace_bytes"):
         assert must in names
 
 
@@ -218,6 +218,27 @@ def test_transport_and_hvp_argument_errors(lib):
     assert hv(d=300) == SK_ERR_UNSUPPORTED_D
     assert hv(it=-1) == SK_ERR_ITERS
     assert hv(wb=100) == SK_ERR_WORKSPACE
+
+
+def test_fs2_argument_errors(lib):
+    # the workspace size needs the radix sort's scratch size, queried from the device: only shape errors here
+    assert lib.sk_fs2_workspace_bytes(1000, 1000, 9, 256, 64) == 0
+    assert lib.sk_fs2_workspace_bytes(1000, 1000, 2, 0, 64) == 0
+    assert lib.sk_fs2_workspace_bytes(1000, 1000, 2, 513, 64) == 0
+    assert lib.sk_fs2_workspace_bytes(1 << 20, 1 << 20, 2, 16, 64) == 0  # 2^32 block pairs
+    ii, ff = (ctypes.c_int32 * 4)(), (ctypes.c_float * 2)()
+    fs = lambda **k: lib.sk_fs2_solve(k.get("x", FAKE), FAKE, FAKE, FAKE, 1000, 900, k.get("d", 2), k.get("eps", 0.01),
+                                      k.get("B", 64), k.get("tol", 1e-5), k.get("delta", 1e-6), k.get("ci", 10),
+                                      k.get("mr", 5), k.get("gain", 0.1), k.get("ns", 64), k.get("mi", 100),
+                                      k.get("ce", 10), k.get("se", 10), FAKE, FAKE, ii, ff, None, None, FAKE, 1 << 30,
+                                      None)
+    assert fs(x=None) == SK_ERR_NULL
+    assert fs(d=9) == SK_ERR_UNSUPPORTED_D
+    assert fs(eps=0.0) == SK_ERR_EPS
+    assert fs(B=0) == SK_ERR_SHAPE and fs(B=600) == SK_ERR_SHAPE
+    assert fs(tol=-1.0) == SK_ERR_STOP and fs(delta=float("nan")) == SK_ERR_STOP and fs(gain=float("inf")) == SK_ERR_STOP
+    assert fs(ci=0) == SK_ERR_ITERS and fs(mr=0) == SK_ERR_ITERS and fs(ns=0) == SK_ERR_ITERS
+    assert fs(mi=-1) == SK_ERR_ITERS and fs(ce=0) == SK_ERR_ITERS and fs(se=0) == SK_ERR_ITERS
 
 
 def test_python_contract_errors_before_gpu():

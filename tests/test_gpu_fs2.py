@@ -1,0 +1,138 @@
+"""GPU parity of the two-stage block-sparse solver ("FlashSinkhorn 2:
+Block-Sparse Entropic Optimal Transport", abstract) against its float64
+reference (oracle/fs2.py), through the C ABI.
+
+  * The Morton order is integer work decided in float32 on both sides: equal
+    bit for bit (ties by index).
+  * With every data-dependent decision switched off (tol = 0 and a coarse gain
+    that never stops the coarse stage, so exactly max_rounds rounds and
+    max_iters fine iterations), the potentials match the reference to
+    1e-4 max C, the tolerance of the dense solve: each step is a Sinkhorn
+    half-step over the same blocks; a tile whose keep decision differs between
+    float32 and float64 sits at the threshold, so its mass is at most delta
+    times the row or column mass.
+  * Beyond the reference's reach, the stopping rule is checked against the
+    all-particle residual of the returned potentials, evaluated densely on
+    the GPU: at most tol + delta max(a, b) plus the float32 floor of the
+    residual, 32 kappa max(a, b).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import streaming_sinkhorn_solver_amd as sk
+from oracle import fs2 as FS
+from sk_inputs import eps32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U32 = 2.0 ** -24
+
+
+def say(*args):
+    print("[case]", *args, file=sys.stderr, flush=True)
+
+
+def dev(*arrs):
+    return [torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for v in arrs]
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def clustered(n, d, k, std, seed, skew=0.0):
+    rng = np.random.default_rng(seed)
+    cen = rng.random((k, d))
+    lab = rng.integers(0, k, n)
+    p = (cen[lab] + std * rng.normal(size=(n, d))).astype(np.float32)
+    w = rng.exponential(size=n) if skew == 0.0 else np.exp(skew * rng.normal(size=n))
+    return p, (w / w.sum()).astype(np.float32)
+
+
+@pytest.mark.parametrize("d", [1, 2, 3, 5])
+def test_morton_order_matches_reference(d):
+    x, a = clustered(6000, d, 12, 0.05, 1 + d)
+    y, b = clustered(5000, d, 12, 0.05, 11 + d)
+    x[100:140] = x[100]  # exact ties keep index order
+    X, Y, A, B = dev(x, y, a, b)
+    _, _, info = sk.fs2_solve(X, Y, A, B, eps=eps32(0.05), block=128, max_rounds=1, coarse_iters=1, max_iters=0,
+                              n_sample=16, return_perm=True)
+    lo, hi = np.minimum(x.min(0), y.min(0)), np.maximum(x.max(0), y.max(0))
+    assert np.array_equal(host(info["perm_x"]).astype(np.int64), FS.morton_order(x, lo, hi))
+    assert np.array_equal(host(info["perm_y"]).astype(np.int64), FS.morton_order(y, lo, hi))
+
+
+FIXED_CASES = [
+    # n, m, d, k clusters, std, eps, B, delta, rounds, coarse iters, fine iters, seed
+    (1500, 1300, 2, 10, 0.03, 0.004, 64, 1e-6, 3, 10, 60, 21),
+    (1200, 1400, 3, 8, 0.05, 0.01, 50, 1e-5, 2, 15, 40, 22),
+    (700, 900, 2, 6, 0.04, 0.02, 512, 1e-6, 2, 10, 30, 23),  # one block per side
+    (1000, 800, 1, 5, 0.02, 0.002, 32, 1e-4, 3, 10, 50, 24),
+]
+
+
+@pytest.mark.parametrize("case", FIXED_CASES, ids=[f"{c[0]}x{c[1]}d{c[2]}B{c[6]}" for c in FIXED_CASES])
+def test_fixed_counts_match_reference(case):
+    n, m, d, k, std, eps, B, delta, rounds, ci, iters, seed = case
+    x, a = clustered(n, d, k, std, seed)
+    y, b = clustered(m, d, k, std, seed + 100, skew=1.5)
+    eps = eps32(eps)
+    kw = dict(B=B, tol=0.0, delta=delta, coarse_iters=ci, max_rounds=rounds, coarse_gain=-1e6, n_sample=64,
+              max_iters=iters, check_every=10, screen_every=10)
+    say("fs2 fixed", case)
+    X, Y, A, Bt = dev(x, y, a, b)
+    f_t, g_t, info = sk.fs2_solve(X, Y, A, Bt, eps=eps, block=B, tol=0.0, delta=delta, coarse_iters=ci,
+                                  max_rounds=rounds, coarse_gain=-1e6, n_sample=64, max_iters=iters, check_every=10,
+                                  screen_every=10)
+    f, g = host(f_t), host(g_t)
+    fo, go, io = FS.solve(x, y, a, b, eps, **kw)
+    maxc = oracle.max_cost(x, y)
+    err = max(np.abs(f - fo).max(), np.abs(g - go).max())
+    say("rounds", info["rounds"], io["rounds"], "iters", info["fine_iters"], io["fine_iters"], "err/tol",
+        err / (1e-4 * maxc), "kept", info["kept_fraction"], io["kept_fraction"][-1], "resid", info["residual"],
+        io["residual"])
+    assert info["rounds"] == rounds == io["rounds"] and info["fine_iters"] == iters == io["fine_iters"]
+    assert np.all(np.isfinite(f)) and np.all(np.isfinite(g))
+    assert err <= 1e-4 * maxc
+    assert abs(info["kept_fraction"] - io["kept_fraction"][-1]) <= 0.02
+
+
+def dense_residual(X, Y, A, B, f_t, g_t, eps):
+    r = host(sk.marginal_residual(X, Y, A, B, f_t, g_t, eps=eps))
+    return max(r[0], r[1])
+
+
+@pytest.mark.parametrize("n,d,k,std,eps,B,seed", [(40000, 2, 64, 0.01, 1e-3, 256, 31),
+                                                  (60000, 3, 128, 0.01, 2e-3, 512, 32)])
+def test_reaches_target_residual(n, d, k, std, eps, B, seed):
+    """Adaptive run (coarse rounds and stop rule on): the all-particle residual of the result,
+    evaluated densely, is within tol + delta max(w) + the float32 floor, and its dual cost agrees to
+    relative 1e-4 with that of a dense solve stopped by the same marginal tolerance."""
+    x, a = clustered(n, d, k, std, seed)
+    y, b = clustered(n, d, k, std, seed + 7)
+    eps = eps32(eps)
+    tol, delta = 1e-5 / n * 1000, 1e-6
+    X, Y, A, B_ = dev(x, y, a, b)
+    f_t, g_t, info = sk.fs2_solve(X, Y, A, B_, eps=eps, block=B, tol=tol, delta=delta, max_iters=20000)
+    say("fs2", (n, d), info)
+    assert info["converged"]
+    wmax = float(max(a.max(), b.max()))
+    f, g = host(f_t), host(g_t)
+    maxc = float(d)  # the unit box
+    kap = U32 * (np.abs(f).max() + np.abs(g).max() + maxc) / eps
+    r = dense_residual(X, Y, A, B_, f_t, g_t, eps)
+    say("all-particle residual", r, "bound", tol + delta * wmax + 32 * kap * wmax)
+    assert r <= tol + delta * wmax + 32 * kap * wmax
+    assert info["kept_fraction"] < 0.5
+    fd, gd, it, conv, viol = sk.solve_ex(X, Y, A, B_, eps=eps, stop_mode="marginal", stop_tol=tol, max_iter=20000,
+                                         check_every=10)
+    c_fs2 = float(host(sk.dual_cost(X, Y, A, B_, f_t, g_t, eps=eps))[0])
+    c_dense = float(host(sk.dual_cost(X, Y, A, B_, fd, gd, eps=eps))[0])
+    say("dense", it, "iterations; cost fs2", c_fs2, "dense", c_dense)
+    assert conv and abs(c_fs2 - c_dense) <= 1e-4 * abs(c_dense)
