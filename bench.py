@@ -38,8 +38,16 @@ evaluations of the counted iterations only):
               before timing: (3 + 2 cg_iters) n m pair evaluations;
   transport   one transport product P Y~-sized: sk_transport with a k = d
               payload (the barycentric numerator), n m pair evaluations.
+  fs2         the two-stage block-sparse solver sk_fs2_solve to a marginal
+              target of --fs2-tol-rel times the largest point mass; value
+              counts the dense-equivalent 2 n m evaluations per fine
+              iteration; the line adds the solver's counts, the kept fraction,
+              the all-particle residual of the result (two dense passes) and,
+              with --fs2-dense, the time of the dense solver (stop rule
+              "marginal", same tolerance) for the same problem.
 The roofline of the hvp / transport modes is that of the transport kernel
-(the dominant one) with its payload work per pair.
+(the dominant one) with its payload work per pair; the fs2 mode reports none
+(its work per iteration depends on the screening).
 """
 from __future__ import annotations
 
@@ -174,6 +182,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="gmm8_d3_sq")
     ap.add_argument("--iters", type=int, default=None, help="override the workload's iteration count")
+    ap.add_argument("--size", type=int, default=None, help="override n = m (same recipe, e.g. a smaller problem)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceilings", action="store_true", help="run the issue-rate micro-benchmarks and exit")
     ap.add_argument("--graph", action="store_true",
@@ -183,7 +192,13 @@ def main():
     ap.add_argument("--timing-stride", type=int, default=7,
                     help="time every k-th pass launch with HIP events (odd, so row and column passes alternate)")
     ap.add_argument("--mode", default="solve",
-                    choices=["solve", "symmetric", "marginal", "potential", "divergence", "flow", "hvp", "transport"])
+                    choices=["solve", "symmetric", "marginal", "potential", "divergence", "flow", "hvp", "transport",
+                             "fs2"])
+    ap.add_argument("--fs2-block", type=int, default=512)
+    ap.add_argument("--fs2-tol-rel", type=float, default=0.01, help="target residual / largest point mass")
+    ap.add_argument("--fs2-delta", type=float, default=1e-6)
+    ap.add_argument("--fs2-max-iters", type=int, default=5000)
+    ap.add_argument("--fs2-dense", action="store_true", help="also time the dense solver to the same tolerance")
     ap.add_argument("--cg-iters", type=int, default=20, help="conjugate-gradient steps of the hvp mode")
     ap.add_argument("--lr", type=float, default=0.1, help="step size of the gradient flow")
     ap.add_argument("--alpha", type=float, default=0.5, help="blend of the symmetric variant")
@@ -212,8 +227,8 @@ def main():
     w = WORKLOADS[args.workload]
     n_iters = w.n_iters if args.iters is None else args.iters
     eps = eps32(w.eps)
-    x, y, a, b = make_inputs(args.workload)
-    n, m, d = w.n, w.m, w.d
+    x, y, a, b = make_inputs(args.workload, n=args.size, m=args.size)
+    n, m, d = x.shape[0], y.shape[0], w.d
     dev = torch.device("cuda:0")
     X, Y, A, B = (torch.from_numpy(v).to(dev) for v in (x, y, a, b))
     ws = sk.workspace(n, m, d, dev)
@@ -235,6 +250,11 @@ def main():
 
     mode = args.mode
     stop = {}
+    fs2_info = {}
+    if mode == "fs2":
+        fs2_tol = args.fs2_tol_rel * float(max(A.max().item(), B.max().item()))
+        nb = sk.load_library().sk_fs2_workspace_bytes(n, m, d, args.fs2_block, 1024)
+        ws_fs2 = torch.empty(nb, dtype=torch.uint8, device=dev)
     if mode in ("hvp", "transport"):
         # potentials of a full solve, outside the timed region
         sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, ws=ws, f=f, g=g, check=False)
@@ -266,6 +286,10 @@ def main():
             sk.hvp(X, Y, A, B, f, g, v_dir, eps=eps, cg_iters=args.cg_iters, ws=ws_t, out=hv_out, cg_resid=cg_res)
         elif mode == "transport":
             sk.transport(X, Y, A, B, f, g, y_pay, eps=eps, ws=ws_t, out=hv_out)
+        elif mode == "fs2":
+            _, _, inf = sk.fs2_solve(X, Y, A, B, eps=eps, block=args.fs2_block, tol=fs2_tol, delta=args.fs2_delta,
+                                     max_iters=args.fs2_max_iters, ws=ws_fs2, f=f, g=g, check=False)
+            fs2_info.update(inf)
         elif mode == "flow":
             sk.gradient_flow(X, Y, A, B, eps=eps, n_iters=n_iters, n_steps=1, lr=args.lr, ws=ws, f=f, g=g,
                              grad=grad, cost_trace=cost_out, check=False)
@@ -316,6 +340,8 @@ def main():
         pair_evals = (3.0 + 2.0 * args.cg_iters) * n * m
     if mode == "transport":
         pair_evals = 1.0 * n * m
+    if mode == "fs2":
+        pair_evals = 2.0 * n * m * fs2_info["fine_iters"]
     extra = {}
     if mode in ("marginal", "potential"):
         # the same iterations without checks, with the same pass timing events
@@ -336,15 +362,30 @@ def main():
         extra = {"variant": "symmetric", "alpha": args.alpha}
     elif mode == "divergence":
         extra = {"divergence": [float(v) for v in dv_out.cpu()]}
+    elif mode == "fs2":
+        r = sk.marginal_residual(X, Y, A, B, f, g, eps=eps)
+        extra = {"fs2": {k: v for k, v in fs2_info.items() if not k.startswith("perm")}, "fs2_tol": fs2_tol,
+                 "block": args.fs2_block, "delta": args.fs2_delta, "solve_s": step_s,
+                 "all_particle_residual": float(max(r[0].item(), r[1].item()))}
+        if args.fs2_dense:
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            _, _, it_d, conv_d, viol_d = sk.solve_ex(X, Y, A, B, eps=eps, stop_mode="marginal", stop_tol=fs2_tol,
+                                                     max_iter=args.fs2_max_iters, check_every=10, ws=ws, check=False)
+            torch.cuda.synchronize()
+            extra["dense"] = {"solve_s": time.perf_counter() - t3, "iters": it_d, "converged": conv_d,
+                              "final_viol": viol_d}
     elif mode == "hvp":
         extra = {"cg_iters": args.cg_iters, "cg_resid": float(cg_res.item()), "hvp_per_s": 1.0 / step_s}
     elif mode == "flow":
         extra = {"lr": args.lr, "flow_steps_per_s": 1.0 / step_s,
                  "flow_steps_run": args.warmup + args.steps + (1 if args.graph else 0) * 2}
     value = pair_evals / step_s
-    avg_launch_s = pass_ms * 1e-3 / launches
-    pairs_per_launch = pairs / launches
-    if mode in ("hvp", "transport"):
+    avg_launch_s = pass_ms * 1e-3 / launches if launches else float("nan")
+    pairs_per_launch = pairs / launches if launches else float("nan")
+    if mode == "fs2":
+        roof = None
+    elif mode in ("hvp", "transport"):
         payload = 1 if mode == "hvp" else d  # columns of the dominant launches (CG steps / the product)
         if d <= 8:
             roof = roofline_alu(d, pairs_per_launch, avg_launch_s, payload)
@@ -360,7 +401,8 @@ def main():
     else:
         roof = roofline_mfma(d, pairs_per_launch, avg_launch_s)
         roof["kernel"] = "k_pass_mfma<%d>" % max(16, 1 << (d - 1).bit_length())
-    roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma")
+    if roof is not None:
+        roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma")
 
     out = {
         "metric": "point-pair evals/sec and Sinkhorn iters/sec (n=m=50k,d=3); % fp32 peak",
@@ -380,7 +422,7 @@ def main():
         "mode": mode,
         "iters_per_s": (3 * n_iters if mode == "divergence" else counted_iters) / step_s,
         "hip_graph": bool(args.graph),
-        "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s,
+        "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s if launches else None,
         "roofline": roof,
         "final_residual": float(trace[n_iters // ce - 1].item()) if (ce and mode == "solve") else None,
         "cost": float(cost_out.item()) if mode not in ("divergence", "hvp", "transport") else None,

@@ -137,6 +137,8 @@ struct SparseArgs {
     float qscale;        // 2 log2e / eps
     const int* ptr;      // [n_query_blocks + 1]
     const int* idx;      // kept key blocks
+    int nsplit;          // workgroups per query block (each takes an equal chunk of its list)
+    float2* part;        // [nsplit][nq] partial (M, S) when nsplit > 1
     Fin fin;
 };
 

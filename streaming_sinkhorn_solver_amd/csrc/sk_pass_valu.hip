@@ -113,15 +113,18 @@ __device__ __forceinline__ void scan_keys(float4* tile, const float4* __restrict
     }
 }
 
-// Block-sparse pass: one workgroup per query block of B <= kBlock * kR rows,
-// scanning only the key blocks listed for it (a CSR list of kept tiles; both
-// clouds are in block order, so a key block is a contiguous key range).
+// Block-sparse pass: query block I (B <= kBlock * kR rows) scans only the
+// key blocks listed for it (a CSR list of kept tiles; both clouds are in
+// block order, so a key block is a contiguous key range).  The list of each
+// query block is cut into nsplit equal chunks, one workgroup each
+// (blockIdx.y); with nsplit > 1 the partial (M, S) are merged exactly by
+// k_sparse_merge, as for the dense split passes.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_pass_sparse(SparseArgs A) {
     constexpr int P = ((D + 1 + 3) / 4) * 4;
     __shared__ float4 tile[kTL * (P / 4)];
     const float4* kp = reinterpret_cast<const float4*>(A.k);
-    const int I = blockIdx.x;
+    const int I = blockIdx.x, split = blockIdx.y;
     const int r0 = I * A.B;
     const int r1 = min(r0 + A.B, A.nq);
     float q[kR][D], M[kR], S[kR];
@@ -134,16 +137,35 @@ __global__ __launch_bounds__(kBlock) void k_pass_sparse(SparseArgs A) {
         M[r] = kNegBig;
         S[r] = 0.0f;
     }
-    const int t1 = A.ptr[I + 1];
-    for (int t = A.ptr[I]; t < t1; ++t) {
+    const int p0 = A.ptr[I], cnt = A.ptr[I + 1] - p0;
+    const int per = (cnt + A.nsplit - 1) / A.nsplit;
+    const int t0 = p0 + min(cnt, split * per), t1 = p0 + min(cnt, (split + 1) * per);
+    for (int t = t0; t < t1; ++t) {
         const int j0 = A.idx[t] * A.B;
         scan_keys<D>(tile, kp, q, M, S, j0, min(j0 + A.B, A.nk));
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
         const int i = r0 + threadIdx.x + r * kBlock;
-        if (i < r1) finalize(A.fin, i, M[r] + lg2(S[r]));
+        if (i >= r1) continue;
+        if (A.nsplit == 1)
+            finalize(A.fin, i, M[r] + lg2(S[r]));
+        else
+            A.part[(size_t)split * A.nq + i] = make_float2(M[r], S[r]);
     }
+}
+
+__global__ __launch_bounds__(kBlock) void k_sparse_merge(SparseArgs A) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= A.nq) return;
+    float M = kNegBig;
+    for (int s = 0; s < A.nsplit; ++s) M = fmaxf(M, A.part[(size_t)s * A.nq + i].x);
+    float S = 0.0f;
+    for (int s = 0; s < A.nsplit; ++s) {
+        const float2 p = A.part[(size_t)s * A.nq + i];
+        S += p.y * ex2(p.x - M);
+    }
+    finalize(A.fin, i, M + lg2(S));
 }
 
 template <int D>
@@ -501,13 +523,15 @@ hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t 
 template <int D>
 hipError_t launch_sparse_d(const SparseArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
-    hipLaunchKernelGGL(k_pass_sparse<D>, dim3((a.nq + a.B - 1) / a.B), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_pass_sparse<D>, dim3((a.nq + a.B - 1) / a.B, a.nsplit), dim3(kBlock), 0, s, a);
     if (ev1) (void)hipEventRecord(ev1, s);
+    if (a.nsplit > 1)
+        hipLaunchKernelGGL(k_sparse_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_pass_sparse(const SparseArgs& a, int d, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (a.B < 1 || a.B > kBlock * kR) return hipErrorInvalidValue;
+    if (a.B < 1 || a.B > kBlock * kR || a.nsplit < 1 || (a.nsplit > 1 && !a.part)) return hipErrorInvalidValue;
     switch (d) {
         case 1: return launch_sparse_d<1>(a, s, ev0, ev1);
         case 2: return launch_sparse_d<2>(a, s, ev0, ev1);
