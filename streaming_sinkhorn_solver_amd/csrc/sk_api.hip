@@ -725,18 +725,12 @@ struct FLayout {
     size_t sq, sf, sa, snrm;
     size_t fs, gs;
     size_t score, keep, rcnt, rptr, ridx, ccnt, cptr, cidx, spart;
-    int rsplit, csplit;
+    int sparse_groups;
     size_t total;
 };
 
 constexpr int64_t kMaxTiles = (int64_t)1 << 26;  // block pairs of the tile matrices
-constexpr int kMaxSparseSplit = 16;              // workgroups per query block of a sparse pass
-
-// Workgroups per query block of a sparse pass: enough query blocks x splits to
-// fill the chip several times over (kTargetGroups), at most kMaxSparseSplit.
-int sparse_split(int nblocks) {
-    return (int)std::max<int64_t>(1, std::min<int64_t>(kMaxSparseSplit, (kTargetGroups + nblocks - 1) / nblocks));
-}
+constexpr int kSparseGroups = 2048;              // workgroups of a sparse pass (8 per CU on 256 CUs)
 
 int morton_bits_for(int d) { return std::max(1, std::min(10, 30 / d)); }
 
@@ -804,9 +798,8 @@ bool make_flayout(int64_t n, int64_t m, int d, int B, int n_sample, FLayout* out
     F.ccnt = take(by * 4);
     F.cptr = take((by + 1) * 4);
     F.cidx = take(bx * by * 4);
-    F.rsplit = sparse_split(F.nbx);
-    F.csplit = sparse_split(F.nby);
-    F.spart = take((size_t)std::max(F.rsplit * un, F.csplit * um) * sizeof(float2));
+    F.sparse_groups = kSparseGroups;
+    F.spart = take((size_t)F.sparse_groups * 2 * B * sizeof(float2));
     F.total = off;
     *out = F;
     return true;
@@ -938,7 +931,8 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     rowp.idx = ip(F.ridx);
     rowp.fin = make_pass(W, true, eps, as, cap).fin;
     rowp.fin.pot = fs;
-    rowp.nsplit = F.rsplit;
+    rowp.nqb = F.nbx;
+    rowp.W = F.sparse_groups;
     rowp.part = reinterpret_cast<float2*>(base + F.spart);
     colp = rowp;
     colp.q = W.f(L.yp);
@@ -949,7 +943,7 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     colp.idx = ip(F.cidx);
     colp.fin = make_pass(W, false, eps, bs, cap).fin;
     colp.fin.pot = gs;
-    colp.nsplit = F.csplit;
+    colp.nqb = F.nby;
     SparseArgs probe = rowp;
     probe.fin.mode = kFinProbe;
     probe.fin.rbuf = W.f(L.rbuf);

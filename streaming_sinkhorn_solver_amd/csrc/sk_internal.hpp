@@ -129,16 +129,17 @@ struct GradArgs {
 
 // Arguments of a block-sparse pass (d <= 8): query block I (rows
 // [I B, (I + 1) B)) scans the key blocks idx[ptr[I] .. ptr[I + 1]) (keys
-// [J B, (J + 1) B)); rows and keys are in block (Morton) order.
+// [J B, (J + 1) B)); rows and keys are in block (Morton) order.  The kept
+// tiles are shared out stream-K style over W workgroups.
 struct SparseArgs {
     const float* q;      // query cloud, packed [nq][P]
     const float* k;      // key cloud, packed [nk][P]
-    int nq, nk, B;
+    int nq, nk, B, nqb;  // nqb = ceil(nq / B) query blocks
     float qscale;        // 2 log2e / eps
-    const int* ptr;      // [n_query_blocks + 1]
+    const int* ptr;      // [nqb + 1]
     const int* idx;      // kept key blocks
-    int nsplit;          // workgroups per query block (each takes an equal chunk of its list)
-    float2* part;        // [nsplit][nq] partial (M, S) when nsplit > 1
+    int W;               // workgroups
+    float2* part;        // [W][2][B] partial (M, S) of split blocks
     Fin fin;
 };
 

@@ -113,57 +113,91 @@ __device__ __forceinline__ void scan_keys(float4* tile, const float4* __restrict
     }
 }
 
-// Block-sparse pass: query block I (B <= kBlock * kR rows) scans only the
-// key blocks listed for it (a CSR list of kept tiles; both clouds are in
-// block order, so a key block is a contiguous key range).  The list of each
-// query block is cut into nsplit equal chunks, one workgroup each
-// (blockIdx.y); with nsplit > 1 the partial (M, S) are merged exactly by
-// k_sparse_merge, as for the dense split passes.
+// Block-sparse pass, stream-K over the kept tiles.  The kept (query block,
+// key block) tiles, in CSR order (query block I owns tiles ptr[I] ..
+// ptr[I + 1]), are cut into W equal contiguous ranges, one per workgroup,
+// whatever the query blocks, so the work balances however unevenly the
+// tiles fall.  A workgroup walks its range query block by query block; a
+// segment that covers a block's whole list finishes it in place, a first or
+// last segment that does not leaves partial (M, S) in slot 0 or 1 for the
+// merge.  Both clouds are in block order, so a key block is a contiguous key
+// range and each tile is one call of the dense key scan.
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_pass_sparse(SparseArgs A) {
     constexpr int P = ((D + 1 + 3) / 4) * 4;
     __shared__ float4 tile[kTL * (P / 4)];
     const float4* kp = reinterpret_cast<const float4*>(A.k);
-    const int I = blockIdx.x, split = blockIdx.y;
-    const int r0 = I * A.B;
-    const int r1 = min(r0 + A.B, A.nq);
-    float q[kR][D], M[kR], S[kR];
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-        const int i = r0 + threadIdx.x + r * kBlock;
-        const int ic = i < r1 ? i : r1 - 1;
-#pragma unroll
-        for (int t = 0; t < D; ++t) q[r][t] = A.q[(size_t)ic * P + t] * A.qscale;
-        M[r] = kNegBig;
-        S[r] = 0.0f;
-    }
-    const int p0 = A.ptr[I], cnt = A.ptr[I + 1] - p0;
-    const int per = (cnt + A.nsplit - 1) / A.nsplit;
-    const int t0 = p0 + min(cnt, split * per), t1 = p0 + min(cnt, (split + 1) * per);
-    for (int t = t0; t < t1; ++t) {
-        const int j0 = A.idx[t] * A.B;
-        scan_keys<D>(tile, kp, q, M, S, j0, min(j0 + A.B, A.nk));
-    }
-#pragma unroll
-    for (int r = 0; r < kR; ++r) {
-        const int i = r0 + threadIdx.x + r * kBlock;
-        if (i >= r1) continue;
-        if (A.nsplit == 1)
-            finalize(A.fin, i, M[r] + lg2(S[r]));
+    const int w = blockIdx.x;
+    const int64_t nnz = A.ptr[A.nqb];
+    int64_t t = range_lo(w, nnz, A.W);
+    const int64_t u1 = range_lo(w + 1, nnz, A.W);
+    if (t >= u1) return;
+    // query block of tile t: the largest I with ptr[I] <= t (empty blocks never qualify last)
+    int lo = 0, hi = A.nqb - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (A.ptr[mid] <= t)
+            lo = mid;
         else
-            A.part[(size_t)split * A.nq + i] = make_float2(M[r], S[r]);
+            hi = mid - 1;
+    }
+    int I = lo;
+    bool first = true;
+    while (t < u1) {
+        const int64_t b0 = A.ptr[I], b1 = A.ptr[I + 1];
+        const int64_t seg_hi = min(u1, b1);
+        const int r0 = I * A.B;
+        const int r1 = min(r0 + A.B, A.nq);
+        float q[kR][D], M[kR], S[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int i = r0 + threadIdx.x + r * kBlock;
+            const int ic = i < r1 ? i : r1 - 1;
+#pragma unroll
+            for (int c = 0; c < D; ++c) q[r][c] = A.q[(size_t)ic * P + c] * A.qscale;
+            M[r] = kNegBig;
+            S[r] = 0.0f;
+        }
+        for (int64_t tt = t; tt < seg_hi; ++tt) {
+            const int j0 = A.idx[tt] * A.B;
+            scan_keys<D>(tile, kp, q, M, S, j0, min(j0 + A.B, A.nk));
+        }
+        const bool whole = t == b0 && seg_hi == b1;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+            const int i = r0 + threadIdx.x + r * kBlock;
+            if (i >= r1) continue;
+            if (whole)
+                finalize(A.fin, i, M[r] + lg2(S[r]));
+            else
+                A.part[((size_t)w * 2 + (first ? 0 : 1)) * A.B + (i - r0)] = make_float2(M[r], S[r]);
+        }
+        first = false;
+        t = seg_hi;
+        while (I + 1 < A.nqb && A.ptr[I + 1] <= t) ++I;
     }
 }
 
+// Rows of query blocks split across workgroups: combine the partials of the
+// workgroups whose ranges meet the block's tile list, in workgroup order.
 __global__ __launch_bounds__(kBlock) void k_sparse_merge(SparseArgs A) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= A.nq) return;
-    float M = kNegBig;
-    for (int s = 0; s < A.nsplit; ++s) M = fmaxf(M, A.part[(size_t)s * A.nq + i].x);
-    float S = 0.0f;
-    for (int s = 0; s < A.nsplit; ++s) {
-        const float2 p = A.part[(size_t)s * A.nq + i];
-        S += p.y * ex2(p.x - M);
+    const int I = i / A.B;
+    const int64_t nnz = A.ptr[A.nqb];
+    const int64_t p0 = A.ptr[I], p1 = A.ptr[I + 1];
+    if (p0 >= p1) return;  // no tiles (every block keeps one, so this does not occur)
+    const int w0 = range_owner(p0, nnz, A.W), w1 = range_owner(p1 - 1, nnz, A.W);
+    if (w0 == w1) return;  // finished in place
+    float M = kNegBig, S = 0.0f;
+    for (int w = w0; w <= w1; ++w) {
+        const int64_t lo = range_lo(w, nnz, A.W);
+        if (lo == range_lo(w + 1, nnz, A.W)) continue;  // an empty range wrote nothing
+        const int slot = (w == w0 && lo < p0) ? 1 : 0;
+        const float2 p = A.part[((size_t)w * 2 + slot) * A.B + (i - I * A.B)];
+        const float mn = fmaxf(M, p.x);
+        S = S * ex2(M - mn) + p.y * ex2(p.x - mn);
+        M = mn;
     }
     finalize(A.fin, i, M + lg2(S));
 }
@@ -523,15 +557,15 @@ hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t 
 template <int D>
 hipError_t launch_sparse_d(const SparseArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
-    hipLaunchKernelGGL(k_pass_sparse<D>, dim3((a.nq + a.B - 1) / a.B, a.nsplit), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_pass_sparse<D>, dim3(a.W), dim3(kBlock), 0, s, a);
     if (ev1) (void)hipEventRecord(ev1, s);
-    if (a.nsplit > 1)
-        hipLaunchKernelGGL(k_sparse_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_sparse_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_pass_sparse(const SparseArgs& a, int d, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (a.B < 1 || a.B > kBlock * kR || a.nsplit < 1 || (a.nsplit > 1 && !a.part)) return hipErrorInvalidValue;
+    if (a.B < 1 || a.B > kBlock * kR || a.W < 1 || !a.part || a.nqb != (a.nq + a.B - 1) / a.B)
+        return hipErrorInvalidValue;
     switch (d) {
         case 1: return launch_sparse_d<1>(a, s, ev0, ev1);
         case 2: return launch_sparse_d<2>(a, s, ev0, ev1);
