@@ -46,8 +46,9 @@ evaluations of the counted iterations only):
               with --fs2-dense, the time of the dense solver (stop rule
               "marginal", same tolerance) for the same problem.
 The roofline of the hvp / transport modes is that of the transport kernel
-(the dominant one) with its payload work per pair; the fs2 mode reports none
-(its work per iteration depends on the screening).
+(the dominant one) with its payload work per pair; that of the fs2 mode is the
+block-sparse pass of the fine stage, counting the point pairs of the kept tiles
+(its iters_per_s counts fine iterations).
 """
 from __future__ import annotations
 
@@ -384,7 +385,10 @@ def main():
     avg_launch_s = pass_ms * 1e-3 / launches if launches else float("nan")
     pairs_per_launch = pairs / launches if launches else float("nan")
     if mode == "fs2":
-        roof = None
+        # the block-sparse pass over the kept tiles: the dense pass's per-pair work
+        roof = roofline_alu(d, pairs_per_launch, avg_launch_s) if launches else None
+        if roof is not None:
+            roof["kernel"] = f"k_pass_sparse<{d}>"
     elif mode in ("hvp", "transport"):
         payload = 1 if mode == "hvp" else d  # columns of the dominant launches (CG steps / the product)
         if d <= 8:
@@ -401,8 +405,10 @@ def main():
     else:
         roof = roofline_mfma(d, pairs_per_launch, avg_launch_s)
         roof["kernel"] = "k_pass_mfma<%d>" % max(16, 1 << (d - 1).bit_length())
-    if roof is not None:
+    if roof is not None and mode != "fs2":
         roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma")
+    elif roof is not None:
+        roof["traffic"] = None  # no counter run of the sparse pass
 
     out = {
         "metric": "point-pair evals/sec and Sinkhorn iters/sec (n=m=50k,d=3); % fp32 peak",
@@ -420,7 +426,8 @@ def main():
         "config": {"workload": args.workload, "n": n, "m": m, "d": d, "eps": eps, "n_iters": n_iters,
                    "check_every": ce, "grad_x": bool(w.grad), "recipe": w.description},
         "mode": mode,
-        "iters_per_s": (3 * n_iters if mode == "divergence" else counted_iters) / step_s,
+        "iters_per_s": (3 * n_iters if mode == "divergence" else
+                        fs2_info["fine_iters"] if mode == "fs2" else counted_iters) / step_s,
         "hip_graph": bool(args.graph),
         "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s if launches else None,
         "roofline": roof,

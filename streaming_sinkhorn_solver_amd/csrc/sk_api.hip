@@ -12,6 +12,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <optional>
 #include <utility>
 #include <vector>
 
@@ -187,23 +188,24 @@ struct Timing {
     std::vector<hipEvent_t> pool;  // pairs: [2k] start, [2k + 1] stop
     size_t used = 0;               // pairs recorded since enable
     double pairs = 0.0;
+    int paused = 0;                // > 0: launches are not timed (TimingPause)
 };
 Timing& timing() {
     static Timing t;
     return t;
 }
 
-// Takes the event pair for the next streamed-pass launch of nq x nk pairs when
-// timing is on, the stream is not being captured and the stride selects it;
-// otherwise leaves both null.
-int timing_events(int64_t nq, int64_t nk, hipStream_t s, hipEvent_t* e0, hipEvent_t* e1) {
+// Takes the event pair for the next streamed-pass launch of `pairs` point
+// pairs when timing is on, the stream is not being captured and the stride
+// selects it; otherwise leaves both null.
+int timing_events_pairs(double pairs, hipStream_t s, hipEvent_t* e0, hipEvent_t* e1) {
     Timing& T = timing();
     *e0 = *e1 = nullptr;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cap) != hipSuccess) return SK_ERR_HIP;
     std::lock_guard<std::mutex> lk(T.mu);
     // no event nodes inside a captured graph
-    if (T.on && cap == hipStreamCaptureStatusNone && (T.seen++ % T.stride) == 0) {
+    if (T.on && T.paused == 0 && cap == hipStreamCaptureStatusNone && (T.seen++ % T.stride) == 0) {
         while (T.pool.size() < 2 * (T.used + 1)) {
             hipEvent_t e;
             SK_TRY(hipEventCreate(&e));
@@ -212,10 +214,35 @@ int timing_events(int64_t nq, int64_t nk, hipStream_t s, hipEvent_t* e0, hipEven
         *e0 = T.pool[2 * T.used];
         *e1 = T.pool[2 * T.used + 1];
         ++T.used;
-        T.pairs += (double)nq * (double)nk;
+        T.pairs += pairs;
     }
     return SK_OK;
 }
+
+int timing_events(int64_t nq, int64_t nk, hipStream_t s, hipEvent_t* e0, hipEvent_t* e1) {
+    return timing_events_pairs((double)nq * (double)nk, s, e0, e1);
+}
+
+bool timing_on() {
+    Timing& T = timing();
+    std::lock_guard<std::mutex> lk(T.mu);
+    return T.on;
+}
+
+// Leaves the pass launches made during its lifetime untimed (auxiliary passes
+// that would blur the average of the kernel being measured).
+struct TimingPause {
+    TimingPause() {
+        std::lock_guard<std::mutex> lk(timing().mu);
+        ++timing().paused;
+    }
+    ~TimingPause() {
+        std::lock_guard<std::mutex> lk(timing().mu);
+        --timing().paused;
+    }
+    TimingPause(const TimingPause&) = delete;
+    TimingPause& operator=(const TimingPause&) = delete;
+};
 
 int run_pass(const Ws& W, const PassArgs& p, hipStream_t s) {
     hipEvent_t e0, e1;
@@ -855,6 +882,9 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     SK_TRY(launch_block_stats(ys, bs, m, d, F.B, fp(F.bmass), fp(F.ycen), fp(F.ylo), fp(F.yhi), s));
 
     // 3: coarse stage on the centroids, lifted to the points after every round
+    // (untimed: the pass timing covers the block-sparse passes of the fine stage)
+    std::optional<TimingPause> pause;
+    pause.emplace();
     PassArgs lift_f = make_pass(W, true, eps, as, cap);
     lift_f.fin.pot = fs;
     retarget(lift_f, W.f(L.xp), n, fp(F.ky), F.nby, cap);
@@ -903,6 +933,7 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     }
 
     // 4-5: block-sparse fine stage from the lifted potentials
+    pause.reset();
     ScreenArgs sa{};
     sa.fmax = fp(F.fmax);
     sa.gmax = fp(F.gmax);
@@ -947,14 +978,32 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     SparseArgs probe = rowp;
     probe.fin.mode = kFinProbe;
     probe.fin.rbuf = W.f(L.rbuf);
+    double kept_pairs = 0.0;
     for (int it = 1; it <= o.max_iters; ++it) {
         if ((it - 1) % o.screen_every == 0) {
             SK_TRY(launch_block_max(fs, as, n, F.B, fp(F.fmax), s));
             SK_TRY(launch_block_max(gs, bs, m, F.B, fp(F.gmax), s));
             SK_TRY(launch_screen(sa, ip(F.rcnt), ip(F.rptr), ip(F.ridx), ip(F.ccnt), ip(F.cptr), ip(F.cidx), s));
+            if (timing_on()) {
+                // point pairs of the kept tiles, for the pass timing only (a host read
+                // per screening): full B x B tiles, less the short last row / column block
+                int rp[2], cp[2];
+                uint8_t last = 0;
+                SK_TRY(hipMemcpyAsync(rp, ip(F.rptr) + F.nbx - 1, sizeof rp, hipMemcpyDeviceToHost, s));
+                SK_TRY(hipMemcpyAsync(cp, ip(F.cptr) + F.nby - 1, sizeof cp, hipMemcpyDeviceToHost, s));
+                SK_TRY(hipMemcpyAsync(&last, sa.keep + F.nbx * F.nby - 1, 1, hipMemcpyDeviceToHost, s));
+                SK_TRY(hipStreamSynchronize(s));
+                const double Bd = F.B, sr = Bd - (double)(n - (int64_t)(F.nbx - 1) * F.B),
+                             sc = Bd - (double)(m - (int64_t)(F.nby - 1) * F.B);
+                kept_pairs = Bd * Bd * rp[1] - Bd * sr * (rp[1] - rp[0]) - Bd * sc * (cp[1] - cp[0]) +
+                             sr * sc * (last ? 1.0 : 0.0);
+            }
         }
-        SK_TRY(launch_pass_sparse(rowp, d, s));
-        SK_TRY(launch_pass_sparse(colp, d, s));
+        hipEvent_t e0, e1;
+        if ((st = timing_events_pairs(kept_pairs, s, &e0, &e1))) return st;
+        SK_TRY(launch_pass_sparse(rowp, d, s, e0, e1));
+        if ((st = timing_events_pairs(kept_pairs, s, &e0, &e1))) return st;
+        SK_TRY(launch_pass_sparse(colp, d, s, e0, e1));
         info->fine_iters = it;
         if (it % o.check_every == 0 || it == o.max_iters) {
             SK_TRY(launch_pass_sparse(probe, d, s));
