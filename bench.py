@@ -366,7 +366,7 @@ def main():
     elif mode == "fs2":
         r = sk.marginal_residual(X, Y, A, B, f, g, eps=eps)
         extra = {"fs2": {k: v for k, v in fs2_info.items() if not k.startswith("perm")}, "fs2_tol": fs2_tol,
-                 "block": args.fs2_block, "delta": args.fs2_delta, "solve_s": step_s,
+                 "block": args.fs2_block, "delta": args.fs2_delta, "solve_s": step_s, "workspace_mb": nb / 1e6,
                  "all_particle_residual": float(max(r[0].item(), r[1].item()))}
         if args.fs2_dense:
             torch.cuda.synchronize()
