@@ -397,7 +397,9 @@ def main():
         else:
             roof = roofline_mfma(d, pairs_per_launch, avg_launch_s, payload)
             p2 = max(16, 1 << (d - 1).bit_length())
-            roof["kernel"] = "k_transport_mfma<%d,1,%d>" % (p2, 0 if mode == "hvp" else 1)
+            # one column: MODE 3 (vector-ALU payload); d columns: 16- or 64-column tiles (MODE 0)
+            roof["kernel"] = ("k_transport_mfma<%d,1,3>" % p2 if payload == 1 else
+                              "k_transport_mfma<%d,%d,0>" % (p2, 1 if d <= 16 else 4))
     elif d <= 8:
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
         small = pairs_per_launch <= 2.0e6  # the library's single-kernel path for small passes

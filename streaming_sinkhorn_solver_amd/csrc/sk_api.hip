@@ -636,7 +636,9 @@ constexpr int kTransMaxK = 9;  // payload columns per vector-ALU transport pass
 // Payload columns per transport pass, and accumulators per row of a split partial.
 int trans_chunk(const Layout& L) { return !L.mfma ? kTransMaxK : (L.P >= 64 ? 64 : 16); }
 int trans_acc(const Layout& L) { return !L.mfma ? kTransMaxK : std::max(64, L.P); }
-int trans_rows(const Layout& L) { return L.mfma ? mfma_transport_rows_per_block() : transport_rows_per_block(); }
+// Rows per workgroup: the largest over the kernel's modes (workspace sizing),
+// or those of one mode and payload width.
+int trans_rows(const Layout& L) { return L.mfma ? mfma_transport_max_rows_per_block(L.P) : transport_rows_per_block(); }
 
 TLayout make_tlayout(int64_t n, int64_t m, int d) {
     TLayout T{};
@@ -699,7 +701,10 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     t.P = L.P;
     t.d = L.d;
     t.qscale = 2.0f * kLog2e / eps;
-    const Split sp = split_for(t.nq, t.nk, trans_rows(L));
+    // a single payload column runs on the vector ALUs inside the matrix-core kernel
+    const int kmode = (L.mfma && mode == 0 && kin == 1) ? 3 : mode, kwidth = kin <= 16 ? 16 : 64;
+    const Split sp = split_for(t.nq, t.nk, L.mfma ? mfma_transport_rows_per_block(L.P, kmode, kwidth)
+                                                  : transport_rows_per_block());
     t.cols_per_split = sp.cols;
     t.nsplit = sp.nsplit;
     t.part = reinterpret_cast<float2*>(W.base + T.part);
@@ -714,7 +719,7 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     int st = timing_events(t.nq, t.nk, s, &e0, &e1);
     if (st) return st;
     if (L.mfma) {
-        SK_TRY(launch_transport_mfma(t, mode, kin <= 16 ? 16 : 64, s, e0, e1));
+        SK_TRY(launch_transport_mfma(t, kmode, kwidth, s, e0, e1));
     } else {
         SK_TRY(launch_transport(t, mode, kin <= 1 ? 1 : (kin <= 4 ? 4 : kTransMaxK), s, e0, e1));
     }
@@ -1343,7 +1348,10 @@ int sk_transport(const float* x, const float* y, const float* a, const float* b,
     Ws W{T.L, static_cast<char*>(ws)};
     const bool row_side = transpose == 0;
     if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
-    if (T.L.mfma && (st = store_lse(W, row_side, eps, row_side ? a : b, s))) return st;
+    if (T.L.mfma) {
+        TimingPause pause;  // the pass timing covers the transport kernel
+        if ((st = store_lse(W, row_side, eps, row_side ? a : b, s))) return st;
+    }
     return transport_cols(W, T, row_side, eps, v, k, out, nullptr, s);
 }
 
@@ -1366,20 +1374,24 @@ int sk_hvp(const float* x, const float* y, const float* a, const float* b, int64
     float* prod = W.f(T.prod);
     double* scal = W.dbl(T.scal);
     if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
-    if (L.mfma) {  // the plan is fixed: one lse pass per side serves every product below
-        if ((st = store_lse(W, true, eps, a, s))) return st;
-        if ((st = store_lse(W, false, eps, b, s))) return st;
+    {
+        // the pass timing covers the single-column products of the CG steps
+        TimingPause pause;
+        if (L.mfma) {  // the plan is fixed: one lse pass per side serves every product below
+            if ((st = store_lse(W, true, eps, a, s))) return st;
+            if ((st = store_lse(W, false, eps, b, s))) return st;
+        }
+        // A = P y~ and r = P 1
+        if (L.mfma) {
+            if ((st = transport_pass(W, T, true, eps, 1, nullptr, 0, 0, nullptr, A, d, d, diag, s))) return st;
+        } else {
+            if ((st = transport_pass(W, T, true, eps, 0, W.f(L.yp), L.P, d, nullptr, A, d, d, diag, s))) return st;
+        }
+        SK_TRY(launch_hvp_rows(W.f(L.xp), L.P, d, in, v, A, diag, stv, rhs, U, s));
+        // B = P^T [st, v] and c = P^T 1
+        if ((st = transport_cols(W, T, false, eps, U, d + 1, B, diag + in, s))) return st;
+        SK_TRY(launch_hvp_cols(W.f(L.yp), L.P, d, im, B, rhs + in, s));
     }
-    // A = P y~ and r = P 1
-    if (L.mfma) {
-        if ((st = transport_pass(W, T, true, eps, 1, nullptr, 0, 0, nullptr, A, d, d, diag, s))) return st;
-    } else {
-        if ((st = transport_pass(W, T, true, eps, 0, W.f(L.yp), L.P, d, nullptr, A, d, d, diag, s))) return st;
-    }
-    SK_TRY(launch_hvp_rows(W.f(L.xp), L.P, d, in, v, A, diag, stv, rhs, U, s));
-    // B = P^T [st, v] and c = P^T 1
-    if ((st = transport_cols(W, T, false, eps, U, d + 1, B, diag + in, s))) return st;
-    SK_TRY(launch_hvp_cols(W.f(L.yp), L.P, d, im, B, rhs + in, s));
     SK_TRY(launch_cg_init(N, in, diag, rhs, z, zb, res, p, scal, s));
     for (int it = 0; it < cg_iters; ++it) {
         if ((st = transport_pass(W, T, true, eps, 0, p + in, 1, 1, nullptr, prod, 1, 1, nullptr, s))) return st;
@@ -1388,7 +1400,10 @@ int sk_hvp(const float* x, const float* y, const float* a, const float* b, int64
     }
     if (cg_resid) SK_TRY(launch_cg_report(scal, cg_resid, s));
     // E = sum_j P_ij (psi_j + 2 <y~_j, v_i>) y~_j, then the product
-    if ((st = transport_pass(W, T, true, eps, 2, zb + in, 1, 1, v, E, d, d, nullptr, s))) return st;
+    {
+        TimingPause pause;
+        if ((st = transport_pass(W, T, true, eps, 2, zb + in, 1, 1, v, E, d, d, nullptr, s))) return st;
+    }
     SK_TRY(launch_hvp_final(in, d, eps, v, diag, stv, zb, A, E, out, s));
     return SK_OK;
 }

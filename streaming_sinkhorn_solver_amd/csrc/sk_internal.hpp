@@ -224,7 +224,10 @@ int transport_rows_per_block();
 // Matrix-core transport products (d > 8, sk_pass_mfma.hip): mode 0 with up to
 // 64 payload columns (kwidth 16 or 64), mode 1 (payload = the key coordinates),
 // mode 2 (weighted pass); needs lse from a kFinStore pass over the same scores.
-int mfma_transport_rows_per_block();
+// Rows per workgroup of the matrix-core transport kernel for padded width P,
+// mode and payload width (16 or 64); the largest over modes and widths.
+int mfma_transport_rows_per_block(int P, int mode, int kwidth);
+int mfma_transport_max_rows_per_block(int P);
 hipError_t launch_transport_mfma(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0 = nullptr,
                                  hipEvent_t ev1 = nullptr);
 // ev0 / ev1 (may be null): recorded right before and after the pass kernel (not the merge).

@@ -26,6 +26,8 @@
 #include "sk_internal.hpp"
 #include "sk_pass_common.hpp"
 
+#include <algorithm>
+
 namespace sk {
 namespace {
 
@@ -38,6 +40,9 @@ constexpr int kWaves = kBlock / 64;
 #endif
 #ifndef SK_MFMA_TILE_FLOATS
 #define SK_MFMA_TILE_FLOATS 8192
+#endif
+#ifndef SK_MFMA_PIPE
+#define SK_MFMA_PIPE 0
 #endif
 
 // 16-query blocks per wave (register budget: NQB * P / 4 query VGPRs)
@@ -100,6 +105,33 @@ struct TileStage {
     }
 };
 
+// A lane's KT key coordinates of one 16-key block, from the padded LDS tile.
+template <int KT>
+__device__ __forceinline__ void load_keys(float (&kf)[KT], const float* ktile, int off) {
+    const float4* kr = reinterpret_cast<const float4*>(&ktile[off]);
+#pragma unroll
+    for (int t4 = 0; t4 < KT / 4; ++t4) {
+        const float4 v = kr[t4];
+        kf[4 * t4 + 0] = v.x;
+        kf[4 * t4 + 1] = v.y;
+        kf[4 * t4 + 2] = v.z;
+        kf[4 * t4 + 3] = v.w;
+    }
+}
+
+// Online log-sum-exp over the four scores a lane holds for one 16-key block.
+__device__ __forceinline__ void lse_block(float& M, float& S, const f4 acc) {
+    const float mt = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+    const float mn = fmaxf(M, mt);
+    float s = S * ex2(M - mn);
+    s += ex2(acc[0] - mn);
+    s += ex2(acc[1] - mn);
+    s += ex2(acc[2] - mn);
+    s += ex2(acc[3] - mn);
+    S = s;
+    M = mn;
+}
+
 __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
     const float mn = fmaxf(M, m2);
     S = S * ex2(M - mn) + s2 * ex2(m2 - mn);
@@ -154,17 +186,55 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
             __syncthreads();
             if (base + TL < j1) stage.load(kp, A.kbias, base + TL, j1);
             const int ntile = min(TL, j1 - base);
+#if SK_MFMA_PIPE
+            // software pipeline over pairs of 16-key blocks with two register
+            // sets: the MFMA chain of one block is issued before the log-sum-exp
+            // epilogue of the previous one (independent registers), and the next
+            // block's keys are read from LDS meanwhile, so vector ALU and LDS work
+            // hides under the MFMAs.  The tile holds a whole number of pairs and
+            // its keys past the segment end carry bias -inf, so a pair may run
+            // past ntile: such scores are -inf and add nothing.
+            constexpr int kBlocks = TL / 16;
+            static_assert(kBlocks % 2 == 0, "the tile must hold whole pairs of 16-key blocks");
+            const int npair = (ntile + 31) >> 5;
+            float ka[KT], kc[KT];
+            f4 accA[NQB], accB[NQB];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) accB[qb] = f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            load_keys<KT>(ka, ktile, c * PS + g * KT);
+            for (int pr = 0; pr < npair; ++pr) {
+                const int b0 = 2 * pr;
+                load_keys<KT>(kc, ktile, ((b0 + 1) * 16 + c) * PS + g * KT);
+                const f4 biasA = *reinterpret_cast<const f4*>(&btile[b0 * 16 + 4 * g]);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) accA[qb] = biasA;
+#pragma unroll
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+                        accA[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[t], qf[qb][t], accA[qb], 0, 0, 0);
+                // block b0 - 1 (a no-op on the -inf scores before the first pair)
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], accB[qb]);
+                const int bn = min(b0 + 2, kBlocks - 1);  // next pair's first block (clamped: unused past the end)
+                load_keys<KT>(ka, ktile, (bn * 16 + c) * PS + g * KT);
+                const f4 biasB = *reinterpret_cast<const f4*>(&btile[(b0 + 1) * 16 + 4 * g]);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) accB[qb] = biasB;
+#pragma unroll
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+                        accB[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[t], qf[qb][t], accB[qb], 0, 0, 0);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], accA[qb]);
+            }
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], accB[qb]);
+#else
             for (int kb = 0; kb < ntile; kb += 16) {
                 float kf[KT];
-                const float4* kr = reinterpret_cast<const float4*>(&ktile[(kb + c) * PS + g * KT]);
-#pragma unroll
-                for (int t4 = 0; t4 < KT / 4; ++t4) {
-                    const float4 v = kr[t4];
-                    kf[4 * t4 + 0] = v.x;
-                    kf[4 * t4 + 1] = v.y;
-                    kf[4 * t4 + 2] = v.z;
-                    kf[4 * t4 + 3] = v.w;
-                }
+                load_keys<KT>(kf, ktile, (kb + c) * PS + g * KT);
                 const f4 bias = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
                 f4 acc[NQB];
 #pragma unroll
@@ -175,18 +245,9 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
                     for (int qb = 0; qb < NQB; ++qb)
                         acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
-                    const float mt = fmaxf(fmaxf(acc[qb][0], acc[qb][1]), fmaxf(acc[qb][2], acc[qb][3]));
-                    const float mn = fmaxf(M[qb], mt);
-                    float s = S[qb] * ex2(M[qb] - mn);
-                    s += ex2(acc[qb][0] - mn);
-                    s += ex2(acc[qb][1] - mn);
-                    s += ex2(acc[qb][2] - mn);
-                    s += ex2(acc[qb][3] - mn);
-                    S[qb] = s;
-                    M[qb] = mn;
-                }
+                for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], acc[qb]);
             }
+#endif
         }
 
         // the four lane groups hold disjoint key subsets of the same queries
@@ -360,14 +421,28 @@ hipError_t launch_grad_mfma_p(const GradArgs& a, hipStream_t s) {
 //  MODE 0: psi_j = NP payload columns (16 * NP, zero-padded) staged in LDS;
 //  MODE 1: psi_j = the key's coordinates (read from the key tile);
 //  MODE 2: the key's coordinates with w_ij (pay_j + <y~_j, 2 v_i>), the inner
-//          product taken on the matrix cores like the score.
+//          product taken on the matrix cores like the score;
+//  MODE 3: one payload column, summed with four vector FMAs per lane and
+//          16 keys (a 16-column MFMA tile would be 15/16 padding).
+// 16-query blocks per wave of the transport kernel: their MFMA chains
+// interleave, at a register cost of NQB * P / 4 query VGPRs plus NQB output
+// tiles.  Measured at d = 64 (16384 x 16384): the 64-column product takes
+// 1019 / 727 / 606 us with 1 / 2 / 4 blocks, the per-row-direction pass
+// (MODE 2, 2 NQB P / 4 query VGPRs) 797 / 785 / 902 us, the single-column
+// product 402 / 355 / 358 us.
+constexpr int transport_nqb(int P, int NP, int MODE) {
+    const int base = (MODE == 0 && NP > 1) ? 4 : 2;
+    return P <= 64 ? base : (P == 128 ? base / 2 : 1);
+}
+
 template <int P, int NP, int MODE>
 __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     constexpr int KT = P / 4;
     constexpr int PS = P + 4;
-    constexpr int NB = MODE == 0 ? NP : P / 16;  // 16-column output blocks
+    constexpr int NB = (MODE == 1 || MODE == 2) ? P / 16 : NP;  // 16-column output blocks (unused in MODE 3)
     constexpr int KP = MODE == 0 ? 16 * NP : 1;  // payload floats per key in LDS
     constexpr int TL = mfma_tile_keys<P>();
+    constexpr int NQB = transport_nqb(P, NP, MODE);
     __shared__ __align__(16) float ktile[TL * PS];
     __shared__ __align__(16) float btile[TL];
     __shared__ __align__(16) float ptile[MODE == 1 ? 1 : TL * KP];
@@ -378,32 +453,37 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     const int split = blockIdx.y;
     const int c0 = split * A.cols_per_split;
     const int c1 = min(c0 + A.cols_per_split, A.nk);
-    const int qrow0 = blockIdx.x * (kWaves * 16) + wave * 16;
+    const int qrow0 = blockIdx.x * (kWaves * 16 * NQB) + wave * (16 * NQB);
 
-    float qf[KT], vf[KT];
-    {
-        const int i = qrow0 + c;
+    float qf[NQB][KT], vf[MODE == 2 ? NQB : 1][KT];
+    float lse_c[NQB], S[NQB], Tv[NQB];
+    f4 T[NQB][NB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int i = qrow0 + qb * 16 + c;
         const int ic = i < A.nq ? i : A.nq - 1;
         const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
 #pragma unroll
         for (int t4 = 0; t4 < KT / 4; ++t4) {
             const float4 v = qr[t4];
-            qf[4 * t4 + 0] = v.x * A.qscale;
-            qf[4 * t4 + 1] = v.y * A.qscale;
-            qf[4 * t4 + 2] = v.z * A.qscale;
-            qf[4 * t4 + 3] = v.w * A.qscale;
+            qf[qb][4 * t4 + 0] = v.x * A.qscale;
+            qf[qb][4 * t4 + 1] = v.y * A.qscale;
+            qf[qb][4 * t4 + 2] = v.z * A.qscale;
+            qf[qb][4 * t4 + 3] = v.w * A.qscale;
         }
+        if (MODE == 2) {
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            const int dim = g * KT + t;
-            vf[t] = (MODE == 2 && dim < A.d) ? 2.0f * A.rowv[(size_t)ic * A.d + dim] : 0.0f;
+            for (int t = 0; t < KT; ++t) {
+                const int dim = g * KT + t;
+                vf[MODE == 2 ? qb : 0][t] = dim < A.d ? 2.0f * A.rowv[(size_t)ic * A.d + dim] : 0.0f;
+            }
         }
+        lse_c[qb] = A.lse[ic];
+        S[qb] = 0.0f;
+        Tv[qb] = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) T[qb][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    const float lse_c = A.lse[min(qrow0 + c, A.nq - 1)];
-    float S = 0.0f;
-    f4 T[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) T[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
     TileStage<P> stage;
     if (c0 < c1) stage.load(kp, A.kbias, c0, c1);
@@ -421,69 +501,100 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
         const int ntile = min(TL, c1 - base);
         for (int kb = 0; kb < ntile; kb += 16) {
             float kf[KT];
-            const float4* kr = reinterpret_cast<const float4*>(&ktile[(kb + c) * PS + g * KT]);
+            load_keys<KT>(kf, ktile, (kb + c) * PS + g * KT);
+            const f4 bias = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
+            f4 acc[NQB], dv[NQB];
 #pragma unroll
-            for (int t4 = 0; t4 < KT / 4; ++t4) {
-                const float4 v = kr[t4];
-                kf[4 * t4 + 0] = v.x;
-                kf[4 * t4 + 1] = v.y;
-                kf[4 * t4 + 2] = v.z;
-                kf[4 * t4 + 3] = v.w;
+            for (int qb = 0; qb < NQB; ++qb) {
+                acc[qb] = bias;
+                dv[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            f4 acc = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
 #pragma unroll
-            for (int t = 0; t < KT; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[t], acc, 0, 0, 0);
-            f4 dv = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+                    acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
             if (MODE == 2) {
 #pragma unroll
-                for (int t = 0; t < KT; ++t) dv = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], vf[t], dv, 0, 0, 0);
-            }
-            float wv[4];
+                for (int t = 0; t < KT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float w = ex2(acc[v] - lse_c);
-                S += w;
-                wv[v] = MODE == 2 ? w * (ptile[kb + 4 * g + v] + dv[v]) : w;
+                    for (int qb = 0; qb < NQB; ++qb)
+                        dv[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], vf[MODE == 2 ? qb : 0][t], dv[qb], 0, 0, 0);
             }
+            float wv[NQB][4];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float b = MODE == 0 ? ptile[(kb + 4 * g + v) * KP + nb * 16 + c]
-                                              : ktile[(kb + 4 * g + v) * PS + nb * 16 + c];
-                    T[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[v], b, T[nb], 0, 0, 0);
+                    const float w = ex2(acc[qb][v] - lse_c[qb]);
+                    S[qb] += w;
+                    wv[qb][v] = MODE == 2 ? w * (ptile[kb + 4 * g + v] + dv[qb][v]) : w;
                 }
-        }
-    }
-    // S: lane (g, c) summed keys 4g.. of query c; join the four groups
-    S += __shfl_xor(S, 16);
-    S += __shfl_xor(S, 32);
-    constexpr int KA = 16 * NB;
-    if (A.nsplit == 1) {
-        if (g == 0 && qrow0 + c < A.nq && A.mass) {
-            const int i = qrow0 + c;
-            A.mass[i] = S * ex2(A.lse[i] + A.qbias[i]);
-        }
+            if (MODE == 3) {
+                // one payload column: four FMAs per lane beat a 16-column MFMA tile
+                const f4 pv = *reinterpret_cast<const f4*>(&ptile[kb + 4 * g]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int i = qrow0 + 4 * g + v;
-            if (i >= A.nq) continue;
-            const float scale = ex2(A.lse[i] + A.qbias[i]);
+                for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int col = nb * 16 + c;
-                if (col < A.kout) A.out[(size_t)i * A.ldo + col] = T[nb][v] * scale;
+                    for (int v = 0; v < 4; ++v) Tv[qb] = fmaf(wv[qb][v], pv[v], Tv[qb]);
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float b = MODE == 0 ? ptile[(kb + 4 * g + v) * KP + nb * 16 + c]
+                                                  : ktile[(kb + 4 * g + v) * PS + nb * 16 + c];
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb)
+                            T[qb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[qb][v], b, T[qb][nb], 0, 0, 0);
+                    }
             }
         }
-    } else {
-        if (g == 0 && qrow0 + c < A.nq) A.part[(size_t)split * A.nq + qrow0 + c] = make_float2(0.0f, S);
+    }
+    constexpr int KA = 16 * NB;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int i = qrow0 + 4 * g + v;
-            if (i >= A.nq) continue;
-            float* pa = A.partA + ((size_t)split * A.nq + i) * KA;
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int q0 = qrow0 + qb * 16;
+        // S: lane (g, c) summed keys 4g.. of query c; join the four groups
+        float Sq = S[qb];
+        Sq += __shfl_xor(Sq, 16);
+        Sq += __shfl_xor(Sq, 32);
+        float Tq = Tv[qb];
+        if (MODE == 3) {
+            Tq += __shfl_xor(Tq, 16);
+            Tq += __shfl_xor(Tq, 32);
+        }
+        if (A.nsplit == 1) {
+            if (g == 0 && q0 + c < A.nq) {
+                const int i = q0 + c;
+                const float scale = ex2(A.lse[i] + A.qbias[i]);
+                if (A.mass) A.mass[i] = Sq * scale;
+                if (MODE == 3) A.out[(size_t)i * A.ldo] = Tq * scale;
+            }
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) pa[nb * 16 + c] = T[nb][v];
+            for (int v = 0; v < 4 && MODE != 3; ++v) {
+                const int i = q0 + 4 * g + v;
+                if (i >= A.nq) continue;
+                const float scale = ex2(A.lse[i] + A.qbias[i]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int col = nb * 16 + c;
+                    if (col < A.kout) A.out[(size_t)i * A.ldo + col] = T[qb][nb][v] * scale;
+                }
+            }
+        } else {
+            if (g == 0 && q0 + c < A.nq) {
+                A.part[(size_t)split * A.nq + q0 + c] = make_float2(0.0f, Sq);
+                if (MODE == 3) A.partA[((size_t)split * A.nq + q0 + c) * KA] = Tq;
+            }
+#pragma unroll
+            for (int v = 0; v < 4 && MODE != 3; ++v) {
+                const int i = q0 + 4 * g + v;
+                if (i >= A.nq) continue;
+                float* pa = A.partA + ((size_t)split * A.nq + i) * KA;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) pa[nb * 16 + c] = T[qb][nb][v];
+            }
         }
     }
 }
@@ -507,8 +618,9 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma_merge(TransArgs A, in
 
 template <int P, int NP, int MODE>
 hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    constexpr int KA = MODE == 0 ? 16 * NP : P;
-    dim3 grid((a.nq + kWaves * 16 - 1) / (kWaves * 16), a.nsplit);
+    constexpr int KA = (MODE == 1 || MODE == 2) ? P : 16 * NP;
+    constexpr int rpb = kWaves * 16 * transport_nqb(P, NP, MODE);
+    dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
     if (ev0) (void)hipEventRecord(ev0, s);
     hipLaunchKernelGGL((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), 0, s, a);
     if (ev1) (void)hipEventRecord(ev1, s);
@@ -523,6 +635,7 @@ hipError_t launch_transport_mfma_pp(const TransArgs& a, int mode, int kwidth, hi
                                     hipEvent_t ev1) {
     if (mode == 1) return launch_transport_mfma_p<P, 1, 1>(a, s, ev0, ev1);
     if (mode == 2) return launch_transport_mfma_p<P, 1, 2>(a, s, ev0, ev1);
+    if (mode == 3) return launch_transport_mfma_p<P, 1, 3>(a, s, ev0, ev1);
     if (kwidth == 16) return launch_transport_mfma_p<P, 1, 0>(a, s, ev0, ev1);
     if constexpr (P >= 64) {  // a 64-column payload tile fits LDS beside the key tile from P = 64 on
         if (kwidth == 64) return launch_transport_mfma_p<P, 4, 0>(a, s, ev0, ev1);
@@ -573,7 +686,16 @@ hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hi
 
 int mfma_grad_rows_per_block() { return kWaves * 16; }
 
-int mfma_transport_rows_per_block() { return kWaves * 16; }
+int mfma_transport_rows_per_block(int P, int mode, int kwidth) {
+    return kWaves * 16 * transport_nqb(P, kwidth > 16 ? 4 : 1, mode);
+}
+
+int mfma_transport_max_rows_per_block(int P) {
+    int r = 0;
+    for (int mode = 0; mode <= 3; ++mode)
+        for (int kw : {16, 64}) r = std::max(r, mfma_transport_rows_per_block(P, mode, kw));
+    return r;
+}
 
 hipError_t launch_transport_mfma(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0,
                                  hipEvent_t ev1) {

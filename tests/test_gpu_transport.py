@@ -69,6 +69,9 @@ TRANSPORT_CASES = [
     (300, 500, 130, 0.5, 4, 5, False, 11, 0.0),
     (17, 5, 64, 0.2, 3, 3, True, 12, 0.0),
     (2600, 3100, 33, 0.3, 4, 16, False, 13, 0.0),
+    # one payload column on the vector ALUs inside the matrix-core kernel, split key range
+    (1500, 2100, 64, 0.5, 5, 1, True, 14, 0.05),
+    (2100, 1500, 130, 0.5, 4, 1, False, 15, 0.0),
 ]
 
 
