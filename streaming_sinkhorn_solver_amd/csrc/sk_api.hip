@@ -13,6 +13,7 @@
 #include <map>
 #include <mutex>
 #include <optional>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -45,6 +46,36 @@ Split split_for(int64_t nq, int64_t nk, int rows_per_block) {
     int64_t cols = (nk + sp - 1) / sp;
     sp = (nk + cols - 1) / cols;
     return Split{(int)sp, (int)cols};
+}
+
+// The split of a transport pass: no more key splits than split_for allows (the
+// workspace is sized by it), but when the row blocks fit the GPU's resident
+// workgroups (cap) at once, only as many splits as keep them all resident, so
+// the grid runs as one full wave instead of a full wave and a ragged one.
+Split split_resident(int64_t nq, int64_t nk, int rows_per_block, int cap) {
+    const Split base = split_for(nq, nk, rows_per_block);
+    const int64_t row_blocks = (nq + rows_per_block - 1) / rows_per_block;
+    if (cap <= 0 || row_blocks >= cap) return base;
+    int64_t sp = std::min<int64_t>(base.nsplit, std::max<int64_t>(1, cap / row_blocks));
+    const int64_t cols = (nk + sp - 1) / sp;
+    sp = (nk + cols - 1) / cols;
+    return Split{(int)sp, (int)cols};
+}
+
+// Resident workgroups of a transport kernel, per device (cached).
+int transport_capacity_cached(const Layout& L, int mode, int kwidth) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, int>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const int dim = L.mfma ? L.P : L.d;
+    std::lock_guard<std::mutex> lk(mu);
+    const auto key = std::make_tuple(dev, (L.mfma ? 1000 : 0) + dim, mode, kwidth);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    const int c = L.mfma ? mfma_transport_capacity(dim, mode, kwidth) : transport_capacity(dim, mode, kwidth);
+    if (c > 0) cache[key] = c;
+    return c;
 }
 
 int rows_per_block(int d) {
@@ -702,9 +733,12 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     t.d = L.d;
     t.qscale = 2.0f * kLog2e / eps;
     // a single payload column runs on the vector ALUs inside the matrix-core kernel
-    const int kmode = (L.mfma && mode == 0 && kin == 1) ? 3 : mode, kwidth = kin <= 16 ? 16 : 64;
-    const Split sp = split_for(t.nq, t.nk, L.mfma ? mfma_transport_rows_per_block(L.P, kmode, kwidth)
-                                                  : transport_rows_per_block());
+    const int kmode = (L.mfma && mode == 0 && kin == 1) ? 3 : mode;
+    const int kwidth = L.mfma ? (kin <= 16 ? 16 : 64) : (kin <= 1 ? 1 : (kin <= 4 ? 4 : kTransMaxK));
+    const Split sp = split_resident(t.nq, t.nk,
+                                    L.mfma ? mfma_transport_rows_per_block(L.P, kmode, kwidth)
+                                           : transport_rows_per_block(),
+                                    transport_capacity_cached(L, kmode, kwidth));
     t.cols_per_split = sp.cols;
     t.nsplit = sp.nsplit;
     t.part = reinterpret_cast<float2*>(W.base + T.part);
@@ -721,7 +755,7 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     if (L.mfma) {
         SK_TRY(launch_transport_mfma(t, kmode, kwidth, s, e0, e1));
     } else {
-        SK_TRY(launch_transport(t, mode, kin <= 1 ? 1 : (kin <= 4 ? 4 : kTransMaxK), s, e0, e1));
+        SK_TRY(launch_transport(t, mode, kwidth, s, e0, e1));
     }
     return SK_OK;
 }

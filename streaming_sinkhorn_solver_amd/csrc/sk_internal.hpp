@@ -228,6 +228,9 @@ int transport_rows_per_block();
 // mode and payload width (16 or 64); the largest over modes and widths.
 int mfma_transport_rows_per_block(int P, int mode, int kwidth);
 int mfma_transport_max_rows_per_block(int P);
+// Workgroups of one transport kernel the GPU holds at once (current device; 0 on error).
+int mfma_transport_capacity(int P, int mode, int kwidth);
+int transport_capacity(int d, int mode, int kwidth);
 hipError_t launch_transport_mfma(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0 = nullptr,
                                  hipEvent_t ev1 = nullptr);
 // ev0 / ev1 (may be null): recorded right before and after the pass kernel (not the merge).

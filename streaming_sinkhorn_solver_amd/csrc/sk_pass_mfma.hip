@@ -651,6 +651,28 @@ hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEv
     return launch_merge(a, s);
 }
 
+template <int P, int NP, int MODE>
+int capacity_tp() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_transport_mfma<P, NP, MODE>, kBlock, 0) != hipSuccess)
+        return 0;
+    return cus * per_cu;
+}
+
+template <int P>
+int capacity_tpp(int mode, int kwidth) {
+    if (mode == 1) return capacity_tp<P, 1, 1>();
+    if (mode == 2) return capacity_tp<P, 1, 2>();
+    if (mode == 3) return capacity_tp<P, 1, 3>();
+    if (kwidth == 16) return capacity_tp<P, 1, 0>();
+    if constexpr (P >= 64) {
+        if (kwidth == 64) return capacity_tp<P, 4, 0>();
+    }
+    return 0;
+}
+
 template <int P>
 int capacity_p() {
     int dev = 0, cus = 0, per_cu = 0;
@@ -688,6 +710,17 @@ int mfma_grad_rows_per_block() { return kWaves * 16; }
 
 int mfma_transport_rows_per_block(int P, int mode, int kwidth) {
     return kWaves * 16 * transport_nqb(P, kwidth > 16 ? 4 : 1, mode);
+}
+
+int mfma_transport_capacity(int P, int mode, int kwidth) {
+    switch (P) {
+        case 16: return capacity_tpp<16>(mode, kwidth);
+        case 32: return capacity_tpp<32>(mode, kwidth);
+        case 64: return capacity_tpp<64>(mode, kwidth);
+        case 128: return capacity_tpp<128>(mode, kwidth);
+        case 256: return capacity_tpp<256>(mode, kwidth);
+        default: return 0;
+    }
 }
 
 int mfma_transport_max_rows_per_block(int P) {

@@ -202,6 +202,27 @@ hipError_t launch_t(const TransArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
     return hipGetLastError();
 }
 
+template <int D, int K, int MODE>
+int capacity_t() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_transport<D, K, MODE>, kBlock, 0) != hipSuccess)
+        return 0;
+    return cus * per_cu;
+}
+
+template <int D>
+int capacity_t_d(int mode, int kwidth) {
+    if (mode == 2) return capacity_t<D, 1, 2>();
+    switch (kwidth) {
+        case 1: return capacity_t<D, 1, 0>();
+        case 4: return capacity_t<D, 4, 0>();
+        case 9: return capacity_t<D, 9, 0>();
+        default: return 0;
+    }
+}
+
 template <int D>
 hipError_t launch_t_d(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (mode == 2) return launch_t<D, 1, 2>(a, s, ev0, ev1);
@@ -373,6 +394,20 @@ inline int grid_of(int64_t count) { return (int)((count + kBlock - 1) / kBlock);
 }  // namespace
 
 int transport_rows_per_block() { return kBlock * kTR; }
+
+int transport_capacity(int d, int mode, int kwidth) {
+    switch (d) {
+        case 1: return capacity_t_d<1>(mode, kwidth);
+        case 2: return capacity_t_d<2>(mode, kwidth);
+        case 3: return capacity_t_d<3>(mode, kwidth);
+        case 4: return capacity_t_d<4>(mode, kwidth);
+        case 5: return capacity_t_d<5>(mode, kwidth);
+        case 6: return capacity_t_d<6>(mode, kwidth);
+        case 7: return capacity_t_d<7>(mode, kwidth);
+        case 8: return capacity_t_d<8>(mode, kwidth);
+        default: return 0;
+    }
+}
 
 hipError_t launch_transport(const TransArgs& a, int mode, int kwidth, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     switch (a.d) {
