@@ -326,7 +326,9 @@ size_t sk_fs2_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t block, in
  *     deviation |(P1)_i - a_i| of the lifted plan over n_sample evenly spaced
  *     rows (P over all points).  The coarse stage ends when the check value
  *     is <= tol, or fell by less than the fraction coarse_gain since the last
- *     round, or after max_rounds rounds;
+ *     round, or after max_rounds rounds.  These comparisons are made on the
+ *     base-2 logarithm of the check value, which stays finite when the value
+ *     itself (a far-off lift at small eps) is beyond float32 range;
  *  3. fine stage from the lifted potentials: before every screen_every-th
  *     iteration each block pair (I, J) gets the bound
  *       (max_I f + max_J g - dmin_IJ^2)/eps + log max(B_J NBy, A_I NBx)
@@ -335,14 +337,14 @@ size_t sk_fs2_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t block, in
  *     log delta (every pair when delta = 0), so that the omitted pairs add at
  *     most delta a_i to any row's and delta b_j to any column's mass; each
  *     block also keeps its pair of largest bound.  Each iteration is a row
- *     and a column half-step over kept pairs only (one workgroup per query
- *     block, scanning only its kept key blocks); after every check_every-th
+ *     and a column half-step over kept pairs only (the kept pairs shared out
+ *     evenly over the workgroups); after every check_every-th
  *     iteration and the last, the row residual of the kept-pair plan (its
  *     column sums are exact) is checked and the stage stops at <= tol.
  * Outputs f, g (device, caller's order).  info_i (host, 4): coarse rounds,
  * fine iterations, kept block pairs at the last screening, converged (0/1);
  * info_f (host, 2): last fine residual (NaN without a check), last coarse
- * check value.  perm_x, perm_y (device, n and m ints, or NULL) receive the
+ * check value (+inf when beyond float32 range).  perm_x, perm_y (device, n and m ints, or NULL) receive the
  * Morton order (original index of each sorted point).  Host-synchronous
  * (the checks are read back); refuses graph capture (SK_ERR_CAPTURE).
  * Also SK_ERR_SHAPE for a block outside [1, 512] or more than 2^26 block
@@ -362,9 +364,14 @@ int sk_fs2_solve(const float *x, const float *y, const float *a, const float *b,
  * Kernel timing of the streamed log-sum-exp passes (benchmark diagnostics).
  * sk_timing_enable(k) with k >= 1 resets the counters and from then on records
  * a HIP event pair on the launch stream around every k-th streamed-pass kernel
- * that the solve, cost and residual entry points enqueue (k = 1: every one;
- * a larger k keeps the host cost of the events off small problems); the split
- * merge and the other kernels are outside the pairs.  sk_timing_enable(0)
+ * that the entry points enqueue (k = 1: every one; a larger k keeps the host
+ * cost of the events off small problems); the split merge and the other
+ * kernels are outside the pairs.  Auxiliary passes are left out so that the
+ * timed launches are of one kernel: the store-lse passes of the transport
+ * products and the Hessian-vector product, the HVP's products outside its
+ * conjugate-gradient steps, and the coarse stage of sk_fs2_solve (whose timed
+ * launches are the block-sparse passes of the fine stage, counted by the
+ * point pairs of the kept blocks).  sk_timing_enable(0)
  * stops recording.  sk_timing_read waits for the recorded events and returns
  * the total kernel milliseconds, the number of timed launches and the number
  * of (query, key) pairs those launches evaluated.  Launches enqueued while the

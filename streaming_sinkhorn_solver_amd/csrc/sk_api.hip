@@ -931,14 +931,17 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     lift_g.fin.pot = gs;
     retarget(lift_g, W.f(L.yp), m, fp(F.kx), F.nbx, cap);
     PassArgs check = make_pass(W, true, eps, as, cap);
-    check.fin.mode = kFinResid;
+    check.fin.mode = kFinResidLog2;  // the lift can be far off: log2 of the residual stays finite
     check.fin.w = fp(F.sa);
     check.fin.nrm = fp(F.snrm);
     check.fin.pot_in = fp(F.sf);
     check.fin.rbuf = W.f(L.rbuf);
     retarget(check, fp(F.sq), F.ns, W.f(L.yp), m, cap);
     const int stride = n / F.ns;
-    float prev = NAN;
+    // decisions on log2 of the check value: the same comparisons as on the value itself
+    const double log2_tol = o.tol > 0.0f ? std::log2((double)o.tol) : -INFINITY;
+    const double log2_keep = 1.0 - (double)o.coarse_gain > 0.0 ? std::log2(1.0 - (double)o.coarse_gain) : INFINITY;
+    double prev = NAN;
     for (int round = 1;; ++round) {
         if ((st = prepare(Wc, fp(F.xcen), fp(F.ycen), fp(F.amass), fp(F.bmass), eps, 0, nullptr, round == 1 ? 1 : 2,
                           Gc, s)))
@@ -962,13 +965,16 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
         SK_TRY(launch_gather_rows(W.f(L.xp), L.P, fs, as, W.f(L.nx), F.ns, stride, fp(F.sq), fp(F.sf), fp(F.sa),
                                   fp(F.snrm), s));
         if ((st = run_pass(W, check, s))) return st;
-        SK_TRY(launch_resid_reduce(W.f(L.rbuf), F.ns, slot.dev(), nullptr, s, slot.flag(), slot.next()));
+        SK_TRY(launch_max_reduce(W.f(L.rbuf), F.ns, slot.dev(), s, slot.flag(), slot.next()));
         if ((st = slot.read(host, 1, s))) return st;
+        const double lc = host[0];  // log2 of the largest sampled |(P1)_i - a_i|
         info->rounds = round;
-        info->last_check = host[0];
-        if (host[0] <= o.tol || round >= o.max_rounds) break;
-        if (round >= 2 && host[0] > (1.0f - o.coarse_gain) * prev) break;
-        prev = host[0];
+        info->last_check = (float)std::exp2(lc);
+        if (lc <= log2_tol || round >= o.max_rounds) break;
+        // stop when the check fell by less than the fraction coarse_gain: c > (1 - gain) c_prev
+        // (a fall of 100% or more is impossible: then always)
+        if (round >= 2 && (log2_keep == INFINITY || lc > log2_keep + prev)) break;
+        prev = lc;
     }
 
     // 4-5: block-sparse fine stage from the lifted potentials

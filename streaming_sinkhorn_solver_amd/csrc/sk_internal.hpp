@@ -59,6 +59,7 @@ enum FinMode : int {
     kFinResid = 2,   // residual against a caller-supplied potential
     kFinStore = 3,   // store lse only
     kFinMass = 4,    // row sums of the plan at a caller-supplied potential
+    kFinResidLog2 = 5,  // log2 |residual| against a caller-supplied potential (finite beyond float32 range)
 };
 
 // kFinSolve keeps the state as u_i = (|q~_i|^2 - f_i) / (eps ln 2), the base-2
@@ -274,6 +275,8 @@ hipError_t launch_check(const float* x, const float* y, const float* a, const fl
 hipError_t launch_cost(const float* a, const float* b, const float* f, const float* g, int n, int m,
                        float eps, double* out, hipStream_t s);
 // flag (may be null): set to seq once out_max[0] is visible to the host.
+// max of v[0..cnt) (-inf when empty) into out[0], then the flag as in launch_resid_reduce
+hipError_t launch_max_reduce(const float* v, int cnt, float* out, hipStream_t s, int* flag, int seq);
 hipError_t launch_resid_reduce(const float* rbuf, int cnt, float* out_max, float* out_sum, hipStream_t s,
                                int* flag = nullptr, int seq = 0);
 // Vector-ALU passes (d <= 8): a streamed pass, plus the exact merge of the

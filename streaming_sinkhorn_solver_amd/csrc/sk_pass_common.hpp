@@ -36,6 +36,13 @@ __device__ __forceinline__ void finalize(const Fin& F, int i, float lse) {
         const float wi = F.w[i];
         const float e = (F.pot_in[i] - F.nrm[i]) * F.inv_eps + kLn2 * lse;
         F.rbuf[i] = wi > 0.0f ? wi * expf(e) : 0.0f;
+    } else if (F.mode == kFinResidLog2) {
+        // log2 |a_i (exp(e) - 1)|, e = (f_i - f~_i)/eps, without forming exp(e):
+        // for e > 0, log2(exp(e) - 1) = e / ln 2 + log2(1 - exp(-e)); -inf for a zero residual
+        const float wi = F.w[i];
+        const float e = (F.pot_in[i] - F.nrm[i]) * F.inv_eps + kLn2 * lse;
+        const float l = e > 0.0f ? fmaf(e, kLog2e, log2f(-expm1f(-e))) : log2f(-expm1f(e));
+        F.rbuf[i] = wi > 0.0f ? log2f(wi) + l : -INFINITY;
     } else {  // kFinResid: (P1)_i / a_i - 1 = exp((f_i - f~_i)/eps) - 1
         const float wi = F.w[i];
         const float e = (F.pot_in[i] - F.nrm[i]) * F.inv_eps + kLn2 * lse;

@@ -271,6 +271,16 @@ __global__ __launch_bounds__(1024) void k_resid_reduce(const float* __restrict__
     }
 }
 
+// Maximum of v[0..cnt), -inf when cnt == 0 (one workgroup).
+__global__ __launch_bounds__(1024) void k_max_reduce(const float* __restrict__ v, int cnt, float* __restrict__ out,
+                                                     int* flag, int seq) {
+    __shared__ float shf[1024];
+    float mx = -INFINITY;
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) mx = fmaxf(mx, v[i]);
+    mx = block_max_f32(mx, shf);
+    if (threadIdx.x == 0) publish(out, mx, flag, seq);
+}
+
 inline int grid_for(int64_t count, int block) { return (int)((count + block - 1) / block); }
 
 }  // namespace
@@ -349,6 +359,11 @@ hipError_t launch_check(const float* x, const float* y, const float* a, const fl
 hipError_t launch_cost(const float* a, const float* b, const float* f, const float* g, int n, int m,
                        float eps, double* out, hipStream_t s) {
     hipLaunchKernelGGL(k_cost, dim3(1), dim3(1024), 0, s, a, b, f, g, nullptr, n, m, eps, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_max_reduce(const float* v, int cnt, float* out, hipStream_t s, int* flag, int seq) {
+    hipLaunchKernelGGL(k_max_reduce, dim3(1), dim3(1024), 0, s, v, cnt, out, flag, seq);
     return hipGetLastError();
 }
 

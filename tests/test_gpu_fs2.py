@@ -103,6 +103,41 @@ def test_fixed_counts_match_reference(case):
     assert abs(info["kept_fraction"] - io["kept_fraction"][-1]) <= 0.02
 
 
+ADAPTIVE_COARSE_CASES = [
+    # eps, B, seed: the coarse stage runs 3 rounds (the check falls, then rises) / 2 rounds with
+    # check values near 1e263 and 1e266, far beyond float32 (the decisions are taken on log2)
+    (5e-4, 64, 41),
+    (2e-4, 128, 44),
+]
+
+
+@pytest.mark.parametrize("eps,B,seed", ADAPTIVE_COARSE_CASES)
+def test_coarse_decisions_match_reference(eps, B, seed):
+    """The coarse stage's own stopping rule (coarse_gain 0.1, tol 0) takes the reference's
+    decisions, also where the check value overflows float32, and the potentials then match."""
+    x, a = clustered(1400, 2, 10, 0.03, seed)
+    y, b = clustered(1200, 2, 10, 0.03, seed + 100, skew=1.5)
+    eps = eps32(eps)
+    kw = dict(tol=0.0, delta=1e-6, coarse_iters=10, max_rounds=6, coarse_gain=0.1, n_sample=64, max_iters=20,
+              check_every=10, screen_every=10)
+    say("fs2 coarse", (eps, B, seed))
+    fo, go, io = FS.solve(x, y, a, b, eps, B=B, **kw)
+    X, Y, A, Bt = dev(x, y, a, b)
+    f_t, g_t, info = sk.fs2_solve(X, Y, A, Bt, eps=eps, block=B, **kw)
+    f, g = host(f_t), host(g_t)
+    err = max(np.abs(f - fo).max(), np.abs(g - go).max())
+    maxc = oracle.max_cost(x, y)
+    say("rounds", info["rounds"], io["rounds"], "checks", io["checks"], "gpu last", info["last_check"],
+        "err/tol", err / (1e-4 * maxc))
+    assert 1 < io["rounds"] < kw["max_rounds"]
+    assert info["rounds"] == io["rounds"]
+    if io["checks"][-1] > np.finfo(np.float32).max:
+        assert info["last_check"] == np.inf
+    else:
+        assert abs(info["last_check"] - io["checks"][-1]) <= 0.05 * io["checks"][-1]
+    assert err <= 1e-4 * maxc
+
+
 def dense_residual(X, Y, A, B, f_t, g_t, eps):
     r = host(sk.marginal_residual(X, Y, A, B, f_t, g_t, eps=eps))
     return max(r[0], r[1])
