@@ -103,6 +103,56 @@ def test_fixed_counts_match_reference(case):
     assert abs(info["kept_fraction"] - io["kept_fraction"][-1]) <= 0.02
 
 
+def _edge_weights(rng, n, zero_frac):
+    v = rng.exponential(size=n)
+    if zero_frac:
+        v[rng.random(n) < zero_frac] = 0.0
+    return (v / v.sum()).astype(np.float32)
+
+
+EDGE_CASES = [
+    # name, n, m, d, zero fractions (a, b), eps, B, coarse rounds
+    ("one_source", 1, 7, 2, (0.0, 0.0), 0.05, 4, 1),
+    ("one_target", 9, 1, 3, (0.0, 0.0), 0.05, 4, 1),
+    ("d8", 300, 260, 8, (0.0, 0.0), 0.2, 32, 2),
+    ("zero_weights", 400, 350, 2, (0.3, 0.2), 0.01, 32, 2),
+    ("identical_points", 50, 40, 2, (0.0, 0.0), 0.05, 16, 1),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_edge_cases_match_reference(case):
+    """One point on a side, d = 8 (3 Morton bits per coordinate), zero weights (excluded from the
+    block maxima of the screening), and a flat bounding box (all Morton codes 0)."""
+    name, n, m, d, (za, zb), eps, B, rounds = case
+    rng = np.random.default_rng(90 + len(name))
+    x = rng.random((n, d)).astype(np.float32)
+    y = rng.random((m, d)).astype(np.float32)
+    if name == "identical_points":
+        x[:] = 0.25
+        y[:] = 0.25
+    a, b = _edge_weights(rng, n, za), _edge_weights(rng, m, zb)
+    eps = eps32(eps)
+    # the residual is checked after the last iteration only: with one point on a side it can be
+    # exactly 0 in float32 (and 1e-8 in float64), which would meet tol = 0 at an earlier check
+    kw = dict(tol=0.0, delta=1e-6, coarse_iters=5, max_rounds=rounds, coarse_gain=-1e6, n_sample=16, max_iters=20,
+              check_every=1000, screen_every=10)
+    say("fs2 edge", case)
+    fo, go, io = FS.solve(x, y, a, b, eps, B=B, **kw)
+    X, Y, A, Bt = dev(x, y, a, b)
+    f_t, g_t, info = sk.fs2_solve(X, Y, A, Bt, eps=eps, block=B, **kw)
+    f, g = host(f_t), host(g_t)
+    # the dense solve's bar, 1e-4 max C; with every cost 0 (identical points) the potentials are
+    # of the size of eps times a log-sum of weights, so eps sets the scale there
+    scale = max(oracle.max_cost(x, y), eps)
+    err = max(np.abs(f - fo).max(), np.abs(g - go).max())
+    say("err/tol", err / (1e-4 * scale), "kept", info["kept_fraction"], io["kept_fraction"][-1])
+    assert info["rounds"] == rounds and info["fine_iters"] == 20
+    assert np.all(np.isfinite(f)) and np.all(np.isfinite(g))
+    assert err <= 1e-4 * scale
+    assert abs(info["kept_fraction"] - io["kept_fraction"][-1]) <= 0.02
+
+
 ADAPTIVE_COARSE_CASES = [
     # eps, B, seed: the coarse stage runs 3 rounds (the check falls, then rises) / 2 rounds with
     # check values near 1e263 and 1e266, far beyond float32 (the decisions are taken on log2)
