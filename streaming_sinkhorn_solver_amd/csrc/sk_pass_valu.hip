@@ -274,6 +274,8 @@ __global__ __launch_bounds__(kBlock) void k_pass_small(PassArgs A) {
     float q[D];
 #pragma unroll
     for (int t = 0; t < D; ++t) q[t] = A.q[(size_t)ic * P + t] * A.qscale;
+    // the row's finalisation inputs, loaded now so that their latency overlaps the key loads
+    const FinIn pre = fin_load(A.fin, ic);
     float M = kNegBig, S = 0.0f;
 
     for (int base = 0; base < A.nk; base += kSmallTile) {
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(kBlock) void k_pass_small(PassArgs A) {
         S = S * ex2(M - mn) + s2 * ex2(m2 - mn);
         M = mn;
     }
-    if (sub == 0 && i < A.nq) finalize(A.fin, i, M + lg2(S));
+    if (sub == 0 && i < A.nq) finalize(A.fin, i, M + lg2(S), pre);
 }
 
 // Combines, for every row of a row block split across workgroups, the partial

@@ -8,6 +8,8 @@
 // sum, so results are bit-identical from run to run.
 #include "sk_internal.hpp"
 
+#include <algorithm>
+
 #include <cmath>
 
 namespace sk {
@@ -62,17 +64,19 @@ __global__ __launch_bounds__(kBlock) void k_colsum_partial(const float* __restri
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_centre_final(const double* __restrict__ px,
-                                                         const double* __restrict__ py, int nblk, int d,
+// One workgroup per coordinate t: the partial sums of each cloud joined by a
+// fixed-shape tree (deterministic), then c_t = (mean_x + mean_y) / 2.
+__global__ __launch_bounds__(kBlock) void k_centre_final(const double* __restrict__ px, int nbx,
+                                                         const double* __restrict__ py, int nby, int d,
                                                          int n, int m, float* __restrict__ centre) {
-    for (int t = threadIdx.x; t < d; t += blockDim.x) {
-        double sx = 0.0, sy = 0.0;
-        for (int b = 0; b < nblk; ++b) {
-            sx += px[(size_t)b * d + t];
-            sy += py[(size_t)b * d + t];
-        }
-        centre[t] = (float)(0.5 * (sx / n + sy / m));
-    }
+    __shared__ double sh[kBlock];
+    const int t = blockIdx.x;
+    double sx = 0.0, sy = 0.0;
+    for (int b = threadIdx.x; b < nbx; b += blockDim.x) sx += px[(size_t)b * d + t];
+    for (int b = threadIdx.x; b < nby; b += blockDim.x) sy += py[(size_t)b * d + t];
+    sx = block_sum_f64(sx, sh);
+    sy = block_sum_f64(sy, sh);
+    if (threadIdx.x == 0) centre[t] = (float)(0.5 * (sx / n + sy / m));
 }
 
 // Pack one cloud: centred coordinates, zero padding, |p~|^2, log2 w and the
@@ -289,9 +293,14 @@ hipError_t launch_centre(const float* x, const float* y, int n, int m, int d, do
                          float* centre, hipStream_t s) {
     double* px = partials;
     double* py = partials + (size_t)kRedBlocks * d;
-    hipLaunchKernelGGL(k_colsum_partial, dim3(kRedBlocks), dim3(kBlock), 0, s, x, (int64_t)n * d, d, px);
-    hipLaunchKernelGGL(k_colsum_partial, dim3(kRedBlocks), dim3(kBlock), 0, s, y, (int64_t)m * d, d, py);
-    hipLaunchKernelGGL(k_centre_final, dim3(1), dim3(kBlock), 0, s, px, py, kRedBlocks, d, n, m, centre);
+    // partial sums: as many workgroups as give each about 8 elements per thread, at most kRedBlocks
+    auto blocks = [](int64_t total) {
+        return (int)std::min<int64_t>(kRedBlocks, std::max<int64_t>(1, (total + 8 * kBlock - 1) / (8 * kBlock)));
+    };
+    const int nbx = blocks((int64_t)n * d), nby = blocks((int64_t)m * d);
+    hipLaunchKernelGGL(k_colsum_partial, dim3(nbx), dim3(kBlock), 0, s, x, (int64_t)n * d, d, px);
+    hipLaunchKernelGGL(k_colsum_partial, dim3(nby), dim3(kBlock), 0, s, y, (int64_t)m * d, d, py);
+    hipLaunchKernelGGL(k_centre_final, dim3(d), dim3(kBlock), 0, s, px, nbx, py, nby, d, n, m, centre);
     return hipGetLastError();
 }
 
