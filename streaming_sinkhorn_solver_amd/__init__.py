@@ -124,6 +124,47 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _buf(t, shape, dtype, device, name: str) -> torch.Tensor:
+    """A caller-supplied output (checked: dtype, device, shape, contiguous) or a new one."""
+    shape = tuple(int(k) for k in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be a {dtype} tensor on {device}")
+    if tuple(t.shape) != shape or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor of shape {shape} (got {tuple(t.shape)})")
+    return t
+
+
+def _in(t, shape, device, name: str) -> torch.Tensor:
+    """A float32 input of the given shape on the device, made contiguous."""
+    shape = tuple(int(k) for k in shape)
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device:
+        raise ValueError(f"{name} must be a float32 tensor on {device}")
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape} (got {tuple(t.shape)})")
+    return t.contiguous()
+
+
+def _at_least(t, count: int, dtype, device, name: str) -> torch.Tensor:
+    """A caller-supplied contiguous buffer of at least count elements (dtype, device checked)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on {device}")
+    if t.numel() < count:
+        raise ValueError(f"{name} must hold at least {count} values")
+    return t
+
+
+def _ws(ws, device, make) -> torch.Tensor:
+    """A caller-supplied workspace (a contiguous uint8 tensor on the device; the library checks its
+    size and alignment) or a new one from make()."""
+    if ws is None:
+        return make()
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"ws must be a contiguous uint8 tensor on {device}")
+    return ws
+
+
 def _as_problem(x, y, a, b):
     if not isinstance(x, torch.Tensor) or not isinstance(y, torch.Tensor):
         raise TypeError("x and y must be torch tensors")
@@ -166,7 +207,7 @@ def check_inputs(x, y, a=None, b=None, ws: torch.Tensor | None = None) -> None:
     """Validate the data (finite, nonnegative weights, equal nonzero masses); raises ValueError."""
     lib = load_library()
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
-    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    ws = _ws(ws, x.device, lambda: workspace(n, m, d, x.device))
     _raise(lib.sk_check_inputs(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, _ptr(ws), ws.numel(),
                                _stream(x.device)), "sk_check_inputs")
 
@@ -182,16 +223,16 @@ def solve(x, y, a=None, b=None, *, eps: float, n_iters: int, check_every: int = 
     """
     lib = load_library()
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
-    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    ws = _ws(ws, x.device, lambda: workspace(n, m, d, x.device))
     if check:
         check_inputs(x, y, a, b, ws)
-    f = f if f is not None else torch.empty(n, dtype=torch.float32, device=x.device)
-    g = g if g is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+    f = _buf(f, (n,), torch.float32, x.device, "f")
+    g = _buf(g, (m,), torch.float32, x.device, "g")
     nt = n_iters // check_every if check_every > 0 else 0
     if trace is None:
         trace = torch.empty(max(nt, 0), dtype=torch.float32, device=x.device)
-    elif trace.numel() < nt or trace.dtype != torch.float32:
-        raise ValueError(f"trace must hold {nt} float32 values")
+    else:
+        trace = _at_least(trace, nt, torch.float32, x.device, "trace")
     _raise(lib.sk_solve(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), _ptr(f), _ptr(g),
                         int(check_every), _ptr(trace) if nt > 0 else None, _ptr(ws), ws.numel(),
                         _stream(x.device)), "sk_solve")
@@ -213,11 +254,11 @@ def solve_ex(x, y, a=None, b=None, *, eps: float, variant: str = "alternating", 
     if variant not in VARIANTS or stop_mode not in STOP_MODES:
         raise ValueError(f"variant must be one of {list(VARIANTS)}, stop_mode one of {list(STOP_MODES)}")
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
-    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    ws = _ws(ws, x.device, lambda: workspace(n, m, d, x.device))
     if check:
         check_inputs(x, y, a, b, ws)
-    f = f if f is not None else torch.empty(n, dtype=torch.float32, device=x.device)
-    g = g if g is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+    f = _buf(f, (n,), torch.float32, x.device, "f")
+    g = _buf(g, (m,), torch.float32, x.device, "g")
     it, conv, viol = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_float()
     _raise(lib.sk_solve_ex(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), VARIANTS[variant],
                            float(alpha), STOP_MODES[stop_mode], float(stop_tol), int(max_iter), int(check_every),
@@ -233,11 +274,9 @@ def dual_cost(x, y, a, b, f, g, *, eps: float, ws: torch.Tensor | None = None,
     """<a,f> + <b,g> - eps (sum_ij P_ij - sum(a) sum(b)) at any potentials (1-element float64 tensor)."""
     lib = load_library()
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
-    ws = ws if ws is not None else workspace(n, m, d, x.device)
-    f, g = f.contiguous(), g.contiguous()
-    if f.shape != (n,) or g.shape != (m,) or f.dtype != torch.float32 or g.dtype != torch.float32:
-        raise ValueError("f must be (n,) and g (m,) float32")
-    out = out if out is not None else torch.empty(1, dtype=torch.float64, device=x.device)
+    ws = _ws(ws, x.device, lambda: workspace(n, m, d, x.device))
+    f, g = _potentials(f, g, n, m, x.device)
+    out = _buf(out, (1,), torch.float64, x.device, "out")
     _raise(lib.sk_dual_cost(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g), _ptr(out),
                             _ptr(ws), ws.numel(), _stream(x.device)), "sk_dual_cost")
     return out
@@ -266,8 +305,8 @@ def divergence(x, y, a=None, b=None, *, eps: float, n_iters: int, variant: str =
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
     if check:
         check_inputs(x, y, a, b)
-    ws = ws if ws is not None else divergence_workspace(n, m, d, x.device)
-    out = out if out is not None else torch.empty(4, dtype=torch.float64, device=x.device)
+    ws = _ws(ws, x.device, lambda: divergence_workspace(n, m, d, x.device))
+    out = _buf(out, (4,), torch.float64, x.device, "out")
     _raise(lib.sk_divergence(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), VARIANTS[variant],
                              float(alpha), int(n_iters), _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)),
            "sk_divergence")
@@ -286,16 +325,16 @@ def gradient_flow(x, y, a=None, b=None, *, eps: float, n_iters: int, n_steps: in
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
     if x.data_ptr() != x_in.data_ptr():
         raise ValueError("x is updated in place and must be contiguous")
-    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    ws = _ws(ws, x.device, lambda: workspace(n, m, d, x.device))
     if check:
         check_inputs(x, y, a, b, ws)
-    f = f if f is not None else torch.empty(n, dtype=torch.float32, device=x.device)
-    g = g if g is not None else torch.empty(m, dtype=torch.float32, device=x.device)
-    grad = grad if grad is not None else torch.empty((n, d), dtype=torch.float32, device=x.device)
+    f = _buf(f, (n,), torch.float32, x.device, "f")
+    g = _buf(g, (m,), torch.float32, x.device, "g")
+    grad = _buf(grad, (n, d), torch.float32, x.device, "grad")
     if cost_trace is None:
         cost_trace = torch.empty(max(n_steps, 1), dtype=torch.float64, device=x.device)
-    elif cost_trace.numel() < n_steps or cost_trace.dtype != torch.float64:
-        raise ValueError(f"cost_trace must hold {n_steps} float64 values")
+    else:
+        cost_trace = _at_least(cost_trace, n_steps, torch.float64, x.device, "cost_trace")
     _raise(lib.sk_gradient_flow(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), int(n_steps),
                                 float(lr), _ptr(f), _ptr(g), _ptr(grad), _ptr(cost_trace), _ptr(ws), ws.numel(),
                                 _stream(x.device)), "sk_gradient_flow")
@@ -312,11 +351,8 @@ def transport_workspace(n: int, m: int, d: int, device) -> torch.Tensor:
     return ws
 
 
-def _potentials(f, g, n, m):
-    f, g = f.contiguous(), g.contiguous()
-    if f.shape != (n,) or g.shape != (m,) or f.dtype != torch.float32 or g.dtype != torch.float32:
-        raise ValueError("f must be (n,) and g (m,) float32")
-    return f, g
+def _potentials(f, g, n, m, device):
+    return _in(f, (n,), device, "f"), _in(g, (m,), device, "g")
 
 
 def transport(x, y, a, b, f, g, v, *, eps: float, transpose: bool = False, ws: torch.Tensor | None = None,
@@ -325,15 +361,16 @@ def transport(x, y, a, b, f, g, v, *, eps: float, transpose: bool = False, ws: t
     P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps)."""
     lib = load_library()
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
-    f, g = _potentials(f, g, n, m)
+    f, g = _potentials(f, g, n, m, x.device)
     rows_in, rows_out = (n, m) if transpose else (m, n)
     vec = v.dim() == 1
-    v2 = (v.reshape(-1, 1) if vec else v).contiguous()
-    if v2.dtype != torch.float32 or v2.dim() != 2 or v2.shape[0] != rows_in:
-        raise ValueError(f"v must be float32 with {rows_in} rows")
+    v2 = v.reshape(-1, 1) if vec else v
+    if v2.dim() != 2 or v2.shape[0] != rows_in:
+        raise ValueError(f"v must have {rows_in} rows")
     k = v2.shape[1]
-    ws = ws if ws is not None else transport_workspace(n, m, d, x.device)
-    out = out if out is not None else torch.empty((rows_out, k), dtype=torch.float32, device=x.device)
+    v2 = _in(v2, (rows_in, k), x.device, "v")
+    ws = _ws(ws, x.device, lambda: transport_workspace(n, m, d, x.device))
+    out = _buf(out, (rows_out, k), torch.float32, x.device, "out")
     _raise(lib.sk_transport(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g),
                             1 if transpose else 0, _ptr(v2), k, _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)),
            "sk_transport")
@@ -347,13 +384,11 @@ def hvp(x, y, a, b, f, g, v, *, eps: float, cg_iters: int = 50, ws: torch.Tensor
     Returns (H v, cg_resid) with cg_resid a 1-element device tensor."""
     lib = load_library()
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
-    f, g = _potentials(f, g, n, m)
-    v = v.contiguous()
-    if v.shape != (n, d) or v.dtype != torch.float32:
-        raise ValueError("v must be (n, d) float32")
-    ws = ws if ws is not None else transport_workspace(n, m, d, x.device)
-    out = out if out is not None else torch.empty((n, d), dtype=torch.float32, device=x.device)
-    cg_resid = cg_resid if cg_resid is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    f, g = _potentials(f, g, n, m, x.device)
+    v = _in(v, (n, d), x.device, "v")
+    ws = _ws(ws, x.device, lambda: transport_workspace(n, m, d, x.device))
+    out = _buf(out, (n, d), torch.float32, x.device, "out")
+    cg_resid = _buf(cg_resid, (1,), torch.float32, x.device, "cg_resid")
     _raise(lib.sk_hvp(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g), _ptr(v),
                       int(cg_iters), _ptr(out), _ptr(cg_resid), _ptr(ws), ws.numel(), _stream(x.device)), "sk_hvp")
     return out, cg_resid
@@ -371,13 +406,15 @@ def fs2_solve(x, y, a=None, b=None, *, eps: float, block: int = 512, tol: float 
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
     if check:
         check_inputs(x, y, a, b)
-    if ws is None:
+    def make_ws():
         nb = int(lib.sk_fs2_workspace_bytes(n, m, d, int(block), int(n_sample)))
         if nb == 0:
             raise ValueError(f"invalid arguments for the block-sparse solver (n={n} m={m} d={d} block={block})")
-        ws = torch.empty(nb, dtype=torch.uint8, device=x.device)
-    f = f if f is not None else torch.empty(n, dtype=torch.float32, device=x.device)
-    g = g if g is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+        return torch.empty(nb, dtype=torch.uint8, device=x.device)
+
+    ws = _ws(ws, x.device, make_ws)
+    f = _buf(f, (n,), torch.float32, x.device, "f")
+    g = _buf(g, (m,), torch.float32, x.device, "g")
     px = torch.empty(n, dtype=torch.int32, device=x.device) if return_perm else None
     py = torch.empty(m, dtype=torch.int32, device=x.device) if return_perm else None
     ii = (ctypes.c_int32 * 4)()
@@ -397,14 +434,12 @@ def fs2_solve(x, y, a=None, b=None, *, eps: float, block: int = 512, tol: float 
 def cost(a, b, f, g, *, eps: float, out: torch.Tensor | None = None) -> torch.Tensor:
     """<a,f> + <b,g> - eps sum(b)(1 - sum(a)) in float64 (a 1-element device tensor)."""
     lib = load_library()
-    for t in (a, b, f, g):
-        if t.dtype != torch.float32 or t.device.type != "cuda":
-            raise ValueError("a, b, f, g must be float32 GPU tensors")
+    if not isinstance(a, torch.Tensor) or a.device.type != "cuda":
+        raise ValueError("a must be a float32 GPU tensor")
     n, m = a.numel(), b.numel()
-    if f.numel() != n or g.numel() != m:
-        raise ValueError("f must match a and g must match b in length")
-    out = out if out is not None else torch.empty(1, dtype=torch.float64, device=a.device)
-    a, b, f, g = a.contiguous(), b.contiguous(), f.contiguous(), g.contiguous()
+    a, b = _in(a, (n,), a.device, "a"), _in(b, (m,), a.device, "b")
+    f, g = _in(f, (n,), a.device, "f"), _in(g, (m,), a.device, "g")
+    out = _buf(out, (1,), torch.float64, a.device, "out")
     _raise(lib.sk_cost(_ptr(a), _ptr(b), _ptr(f), _ptr(g), n, m, float(eps), _ptr(out), _stream(a.device)),
            "sk_cost")
     return out
@@ -414,11 +449,9 @@ def marginal_residual(x, y, a, b, f, g, *, eps: float, ws: torch.Tensor | None =
     """[max|P1-a|, max|P^T1-b|, sum|P1-a|, sum|P^T1-b|] at (f, g), as a 4-element float32 tensor."""
     lib = load_library()
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
-    ws = ws if ws is not None else workspace(n, m, d, x.device)
+    ws = _ws(ws, x.device, lambda: workspace(n, m, d, x.device))
     out = torch.empty(4, dtype=torch.float32, device=x.device)
-    f, g = f.contiguous(), g.contiguous()
-    if f.shape != (n,) or g.shape != (m,) or f.dtype != torch.float32 or g.dtype != torch.float32:
-        raise ValueError("f must be (n,) and g (m,) float32")
+    f, g = _potentials(f, g, n, m, x.device)
     _raise(lib.sk_marginal_residual(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g),
                                     _ptr(out), _ptr(ws), ws.numel(), _stream(x.device)), "sk_marginal_residual")
     return out
@@ -429,11 +462,9 @@ def grad_x(x, y, a, b, g, *, eps: float, ws: torch.Tensor | None = None,
     """grad_i = 2 a_i (x_i - sum_j w_ij y_j), w_i. = softmax_j((g_j - C_ij)/eps + log b_j)."""
     lib = load_library()
     x, y, a, b, n, m, d = _as_problem(x, y, a, b)
-    ws = ws if ws is not None else workspace(n, m, d, x.device)
-    g = g.contiguous()
-    if g.shape != (m,) or g.dtype != torch.float32:
-        raise ValueError("g must be (m,) float32")
-    out = out if out is not None else torch.empty((n, d), dtype=torch.float32, device=x.device)
+    ws = _ws(ws, x.device, lambda: workspace(n, m, d, x.device))
+    g = _in(g, (m,), x.device, "g")
+    out = _buf(out, (n, d), torch.float32, x.device, "out")
     _raise(lib.sk_grad_x(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(g), _ptr(out), _ptr(ws),
                          ws.numel(), _stream(x.device)), "sk_grad_x")
     return out

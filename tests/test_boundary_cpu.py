@@ -267,3 +267,38 @@ def test_no_oracle_on_product_path():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "liboracle" not in text and "sk_oracle" not in text, fn
+
+
+def test_binding_checks_caller_buffers():
+    """Caller-supplied outputs, workspaces and inputs are checked for dtype, device, shape and
+    layout before their pointers reach the library (a wrong one would be written or read out of
+    bounds, or be a host address on the GPU)."""
+    dev = torch.device("cpu")  # the checks are device-generic; "cpu" stands in for the GPU here
+    assert sk._buf(None, (3, 2), torch.float32, dev, "out").shape == (3, 2)
+    good = torch.empty(3, 2)
+    assert sk._buf(good, (3, 2), torch.float32, dev, "out") is good
+    with pytest.raises(ValueError, match="shape"):
+        sk._buf(torch.empty(2, 2), (3, 2), torch.float32, dev, "out")
+    with pytest.raises(ValueError, match="contiguous"):
+        sk._buf(torch.empty(2, 3).t(), (3, 2), torch.float32, dev, "out")
+    with pytest.raises(ValueError, match="float32"):
+        sk._buf(torch.empty(3, 2, dtype=torch.float64), (3, 2), torch.float32, dev, "out")
+    with pytest.raises(ValueError, match="on meta"):
+        sk._buf(good, (3, 2), torch.float32, torch.device("meta"), "out")
+    # inputs: float32, device, exact shape; made contiguous
+    v = torch.empty(2, 3).t()
+    assert sk._in(v, (3, 2), dev, "v").is_contiguous()
+    with pytest.raises(ValueError, match="shape"):
+        sk._in(torch.empty(4), (3,), dev, "f")
+    with pytest.raises(ValueError, match="float32 tensor on meta"):
+        sk._in(torch.empty(3), (3,), torch.device("meta"), "f")
+    # at-least buffers (traces)
+    assert sk._at_least(torch.empty(5), 4, torch.float32, dev, "trace").numel() == 5
+    with pytest.raises(ValueError, match="at least 6"):
+        sk._at_least(torch.empty(5), 6, torch.float32, dev, "trace")
+    # workspaces: contiguous uint8 on the device (size and alignment are the library's checks)
+    ws = torch.empty(64, dtype=torch.uint8)
+    assert sk._ws(ws, dev, None) is ws
+    with pytest.raises(ValueError, match="uint8"):
+        sk._ws(torch.empty(16), dev, None)
+    assert sk._ws(None, dev, lambda: ws) is ws
