@@ -221,3 +221,19 @@ def test_reaches_target_residual(n, d, k, std, eps, B, seed):
     c_dense = float(host(sk.dual_cost(X, Y, A, B_, fd, gd, eps=eps))[0])
     say("dense", it, "iterations; cost fs2", c_fs2, "dense", c_dense)
     assert conv and abs(c_fs2 - c_dense) <= 1e-4 * abs(c_dense)
+
+
+def test_repeat_runs_are_bit_identical():
+    """Fixed-order reductions, a stable radix sort and ordered tile lists: two solves give the same
+    bits (potentials, counts, kept tiles, residual)."""
+    x, a = clustered(20000, 3, 40, 0.01, 51)
+    y, b = clustered(18000, 3, 40, 0.01, 52)
+    X, Y, A, B = dev(x, y, a, b)
+    runs = []
+    for _ in range(2):
+        f_t, g_t, info = sk.fs2_solve(X, Y, A, B, eps=eps32(2e-3), block=256, tol=1e-7, max_iters=300)
+        runs.append((host(f_t), host(g_t), info))
+    (f1, g1, i1), (f2, g2, i2) = runs
+    assert np.array_equal(f1, f2) and np.array_equal(g1, g2)
+    for k in ("rounds", "fine_iters", "kept", "converged", "residual"):
+        assert i1[k] == i2[k] or (k == "residual" and np.isnan(i1[k]) and np.isnan(i2[k])), k

@@ -95,3 +95,41 @@ def test_graph_replay_symmetric_dual_cost_and_divergence():
         for got, exp in zip((f, g, c, dv), want):
             assert torch.equal(got, exp), f"replay {rep} differs from the eager step"
         _ = (X * 2.0).sum().item()
+
+
+@pytest.mark.parametrize("d", [3, 64])
+def test_graph_replay_transport_and_hvp(d):
+    """The transport product and the Hessian-vector product with a fixed CG step count are
+    capturable (the CG's scalars live on the device; nothing synchronises)."""
+    x, y, a, b = random_problem(1300, 1100, d, 79 + d, scale=1.0 / np.sqrt(d), shift=0.3)
+    eps = eps32(0.2 if d == 3 else 0.5)
+    dev = torch.device("cuda:0")
+    X, Y, A, B = (torch.from_numpy(v).to(dev) for v in (x, y, a, b))
+    n, m = x.shape[0], y.shape[0]
+    F, G, _ = sk.solve(X, Y, A, B, eps=eps, n_iters=50)
+    wst = sk.transport_workspace(n, m, d, dev)
+    v = torch.from_numpy(np.random.default_rng(5).normal(size=(m, 4)).astype(np.float32)).to(dev)
+    u = torch.from_numpy(np.random.default_rng(6).normal(size=(n, d)).astype(np.float32)).to(dev)
+    pv = torch.empty((n, 4), device=dev)
+    hv = torch.empty((n, d), device=dev)
+    res = torch.empty(1, device=dev)
+
+    def step():
+        sk.transport(X, Y, A, B, F, G, v, eps=eps, ws=wst, out=pv)
+        sk.hvp(X, Y, A, B, F, G, u, eps=eps, cg_iters=10, ws=wst, out=hv, cg_resid=res)
+
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (pv, hv, res)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (pv, hv, res):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip((pv, hv, res), want):
+            assert torch.equal(got, exp), f"replay {rep} differs from the eager step"
+        _ = (X * 2.0).sum().item()
