@@ -28,6 +28,9 @@ constexpr int kAbiVersion = 2;
 // small-problem path (d <= 8).
 constexpr double kSmallPairs = SK_SMALL_PAIRS;
 constexpr int64_t kTargetGroups = 2048;  // workgroups per pass: 8 per CU on 256 CUs
+// Stop-rule checks are read one interval late below this many pairs per pass (about 2048 x 2048,
+// where an iteration takes ~10 us and a check's host round trip ~25 us).
+constexpr double kDeferPairs = 4.2e6;
 constexpr int64_t kMinColsPerSplit = 512;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -489,30 +492,83 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
         return SK_OK;
     };
 
+    // Deferred checks on small problems, where a check's host round trip costs as much as several
+    // iterations: a check value is read only when the next check is due (or after the loop), so
+    // the host keeps the GPU fed meanwhile.  The checked iteration's potentials stay restorable
+    // until then -- f's state in the buffer the fused pass did not overwrite and g in snap_g
+    // (marginal rule), both potentials in snap_f / snap_g (potential rule) -- and a stop
+    // returns exactly what the immediate check returns; only the iterations enqueued past the
+    // stopping one run in vain.  The symmetric variant's marginal check stays immediate.
+    // (Marginal rule: the column pass of a check iteration writes its state to the other buffer,
+    // so g's checked state survives in uc like f's in ur.)
+    const bool defer = o.stop_mode != 0 && (double)L.n * (double)L.m <= kDeferPairs && !(o.stop_mode == 1 && sym);
+    struct Pending {
+        bool on = false;
+        int k = 0;   // the checked iteration
+        int cr = 0;  // marginal rule: the buffers holding the checked row and column states
+        int cc = 0;
+    } pend;
+    // reads the pending check; *stopped = its iteration met the tolerance (potentials restored)
+    auto settle = [&](bool* stopped) -> int {
+        *stopped = false;
+        if (!pend.on) return SK_OK;
+        pend.on = false;
+        int rc;
+        if ((rc = slot.read(host, 1, s))) return rc;
+        res->viol = host[0];
+        const bool met = o.stop_mode == 1 ? host[0] <= o.tol : host[0] < o.tol;
+        if (!met) return SK_OK;
+        if (o.stop_mode == 1) {
+            SK_TRY(launch_pot_from_state(ur[pend.cr], W.f(L.nx), eps * kLn2, f, (int)L.n, s));
+            SK_TRY(launch_pot_from_state(uc[pend.cc], W.f(L.ny), eps * kLn2, g, (int)L.m, s));
+        } else {
+            SK_TRY(hipMemcpyAsync(f, W.f(L.snap_f), (size_t)L.n * sizeof(float), hipMemcpyDeviceToDevice, s));
+            SK_TRY(hipMemcpyAsync(g, W.f(L.snap_g), (size_t)L.m * sizeof(float), hipMemcpyDeviceToDevice, s));
+        }
+        res->iters = pend.k;
+        res->converged = 1;
+        *stopped = true;
+        return SK_OK;
+    };
+
     for (int k = 1; k <= o.max_iter; ++k) {
         const bool fused = o.stop_mode == 1 && is_check(k - 1);
+        if (defer && fused) {
+            // the previous check's buffers are about to be reused: settle it first
+            bool stopped;
+            if ((st = settle(&stopped))) return st;
+            if (stopped) return SK_OK;
+        }
         row.fin.lse = ur[cr];
         row.fin.lse_out = fused ? ur[cr ^ 1] : ur[cr];
         row.fin.rbuf = fused ? rbuf : nullptr;
         if ((st = run_pass(W, row, s))) return st;
         if (fused) {
             const bool last = !sym;  // the row value alone is the check
-            SK_TRY(launch_resid_reduce(rbuf, (int)L.n, chk + 0, nullptr, s, last ? slot.flag() : nullptr,
-                                       last ? slot.next() : 0));
+            SK_TRY(launch_max_reduce(rbuf, (int)L.n, chk + 0, s, last ? slot.flag() : nullptr, last ? slot.next() : 0));
         }
         if (fused && !sym) {
-            if ((st = slot.read(host, 1, s))) return st;
-            res->viol = host[0];
-            if (host[0] <= o.tol) return stop_at(k - 1, true, false);
+            if (defer) {
+                pend.on = true;
+                pend.k = k - 1;
+                pend.cr = cr;
+                pend.cc = cc;
+            } else {
+                if ((st = slot.read(host, 1, s))) return st;
+                res->viol = host[0];
+                if (host[0] <= o.tol) return stop_at(k - 1, true, false);
+            }
             cr ^= 1;
         }
         const bool fused_col = fused && sym;
+        const bool keep_col = fused && defer;  // keep g's checked state for a deferred stop
         col.fin.lse = uc[cc];
-        col.fin.lse_out = fused_col ? uc[cc ^ 1] : uc[cc];
+        col.fin.lse_out = (fused_col || keep_col) ? uc[cc ^ 1] : uc[cc];
         col.fin.rbuf = fused_col ? rbuf : nullptr;
         if ((st = run_pass(W, col, s))) return st;
+        if (keep_col) cc ^= 1;
         if (fused_col) {
-            SK_TRY(launch_resid_reduce(rbuf, (int)L.m, chk + 1, nullptr, s, slot.flag(), slot.next()));
+            SK_TRY(launch_max_reduce(rbuf, (int)L.m, chk + 1, s, slot.flag(), slot.next()));
             if ((st = slot.read(host, 2, s))) return st;
             res->viol = std::max(host[0], host[1]);
             if (res->viol <= o.tol) return stop_at(k - 1, true, true);
@@ -525,12 +581,27 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
             SK_TRY(launch_apply_bias(bx, by, L.P, L.d, s));
         }
         if (o.stop_mode == 2 && is_check(k)) {
+            if (defer) {  // the snapshots are about to be replaced: settle the previous check first
+                bool stopped;
+                if ((st = settle(&stopped))) return st;
+                if (stopped) return SK_OK;
+            }
             SK_TRY(launch_pot_change(f, W.f(L.snap_f), (int)L.n, g, W.f(L.snap_g), (int)L.m, chk, s, slot.flag(),
                                      slot.next()));
-            if ((st = slot.read(host, 1, s))) return st;
-            res->viol = host[0];
-            if (host[0] < o.tol) return stop_at(k, false, false);
+            if (defer) {
+                pend.on = true;
+                pend.k = k;
+            } else {
+                if ((st = slot.read(host, 1, s))) return st;
+                res->viol = host[0];
+                if (host[0] < o.tol) return stop_at(k, false, false);
+            }
         }
+    }
+    if (defer) {
+        bool stopped;
+        if ((st = settle(&stopped))) return st;
+        if (stopped) return SK_OK;
     }
     if (o.stop_mode == 1) {  // the check after the last iteration: probe passes
         PassArgs probe = row;
@@ -538,8 +609,7 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
         probe.fin.lse = ur[cr];
         probe.fin.rbuf = rbuf;
         if ((st = run_pass(W, probe, s))) return st;
-        SK_TRY(launch_resid_reduce(rbuf, (int)L.n, chk + 0, nullptr, s, sym ? nullptr : slot.flag(),
-                                   sym ? 0 : slot.next()));
+        SK_TRY(launch_max_reduce(rbuf, (int)L.n, chk + 0, s, sym ? nullptr : slot.flag(), sym ? 0 : slot.next()));
         int cnt = 1;
         if (sym) {
             probe = col;
@@ -547,7 +617,7 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
             probe.fin.lse = uc[cc];
             probe.fin.rbuf = rbuf;
             if ((st = run_pass(W, probe, s))) return st;
-            SK_TRY(launch_resid_reduce(rbuf, (int)L.m, chk + 1, nullptr, s, slot.flag(), slot.next()));
+            SK_TRY(launch_max_reduce(rbuf, (int)L.m, chk + 1, s, slot.flag(), slot.next()));
             cnt = 2;
         }
         if ((st = slot.read(host, cnt, s))) return st;

@@ -275,14 +275,24 @@ __global__ __launch_bounds__(1024) void k_resid_reduce(const float* __restrict__
     }
 }
 
-// Maximum of v[0..cnt), -inf when cnt == 0 (one workgroup).
+// Maximum of v[0..cnt), -inf when cnt == 0 (one workgroup): lane maxima, then
+// a shuffle tree per wave and one more across the waves (max is exact in any order).
 __global__ __launch_bounds__(1024) void k_max_reduce(const float* __restrict__ v, int cnt, float* __restrict__ out,
                                                      int* flag, int seq) {
-    __shared__ float shf[1024];
+    __shared__ float shw[16];
     float mx = -INFINITY;
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) mx = fmaxf(mx, v[i]);
-    mx = block_max_f32(mx, shf);
-    if (threadIdx.x == 0) publish(out, mx, flag, seq);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const int wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    if ((threadIdx.x & 63) == 0) shw[wave] = mx;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        mx = threadIdx.x < nw ? shw[threadIdx.x] : -INFINITY;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (threadIdx.x == 0) publish(out, mx, flag, seq);
+    }
 }
 
 inline int grid_for(int64_t count, int block) { return (int)((count + block - 1) / block); }
@@ -372,7 +382,9 @@ hipError_t launch_cost(const float* a, const float* b, const float* f, const flo
 }
 
 hipError_t launch_max_reduce(const float* v, int cnt, float* out, hipStream_t s, int* flag, int seq) {
-    hipLaunchKernelGGL(k_max_reduce, dim3(1), dim3(1024), 0, s, v, cnt, out, flag, seq);
+    // one wave per 64 values up to 16 waves: small problems need no more than their count
+    const int threads = (int)std::min<int64_t>(1024, std::max<int64_t>(64, ((int64_t)cnt + 63) / 64 * 64));
+    hipLaunchKernelGGL(k_max_reduce, dim3(1), dim3(threads), 0, s, v, cnt, out, flag, seq);
     return hipGetLastError();
 }
 

@@ -170,12 +170,15 @@ def test_stop_rule_matches_oracle(case):
     assert viol_o + bound < stol  # the GPU's value could not have landed on the other side
 
 
+@pytest.mark.parametrize("size", [(1300, 1100), (2200, 2000)], ids=["deferred", "immediate"])
 @pytest.mark.parametrize("variant", ["alternating", "symmetric"])
 @pytest.mark.parametrize("rule", ["marginal", "potential"])
-def test_stop_rule_cap_and_state(variant, rule):
+def test_stop_rule_cap_and_state(variant, rule, size):
     """An unreachable tolerance runs to the cap (not a multiple of the interval; the last
-    iteration is checked too), and an early stop leaves exactly the state of a fixed run."""
-    x, y, a, b = random_problem(1300, 1100, 3, 41, shift=0.3)
+    iteration is checked too), and an early stop leaves exactly the state of a fixed run --
+    both where checks are read one interval late (small problems) and where they are read at
+    once (above 4.2e6 pairs per pass)."""
+    x, y, a, b = random_problem(size[0], size[1], 3, 41, shift=0.3)
     eps = eps32(0.1)
     c, cap = 4, 10
     say("cap", variant, rule)
@@ -190,6 +193,18 @@ def test_stop_rule_cap_and_state(variant, rule):
     fc, gc, *_ = gpu_ex(x, y, a, b, eps, variant=variant, max_iter=c)
     assert it1 == c and conv1 is True
     assert np.array_equal(f1, fc) and np.array_equal(g1, gc)
+    # a tolerance met first at the second check (between its value and the first's): that check's state
+    _, _, _, _, v1 = gpu_ex(x, y, a, b, eps, variant=variant, stop_mode=rule, stop_tol=0.0, max_iter=c,
+                            check_every=c)
+    _, _, _, _, v2 = gpu_ex(x, y, a, b, eps, variant=variant, stop_mode=rule, stop_tol=0.0, max_iter=2 * c,
+                            check_every=c)
+    if v2 < v1:
+        tol2 = 0.5 * (v1 + v2)
+        f2, g2, it2, conv2, vv = gpu_ex(x, y, a, b, eps, variant=variant, stop_mode=rule, stop_tol=tol2,
+                                        max_iter=cap, check_every=c)
+        f2c, g2c, *_ = gpu_ex(x, y, a, b, eps, variant=variant, max_iter=2 * c)
+        assert it2 == 2 * c and conv2 is True and vv == v2
+        assert np.array_equal(f2, f2c) and np.array_equal(g2, g2c)
 
 
 def test_stop_rule_zero_iterations_and_capture_refusal():
