@@ -185,7 +185,12 @@ int sk_grad_x(const float *x, const float *y, const float *a, const float *b,
  *   pinned, mapped host memory and raises a flag there, which the host polls
  *   (a 64-byte slot per call in flight, allocated with hipHostMalloc on first
  *   need and kept by the library for the life of the process).  Work the
- *   caller enqueued on `stream` before the call is waited for as well.
+ *   caller enqueued on `stream` before the call is waited for as well.  On
+ *   small problems (at most 4.2e6 pairs per pass, except the symmetric
+ *   variant's marginal rule) a check's value is read only when the next check
+ *   is due, so the GPU never waits for the host; the checked iteration's state
+ *   is kept until then and a stop returns exactly the same outputs, after the
+ *   iterations already enqueued past it have run.
  *   Calling with a stop rule on a stream under graph capture returns
  *   SK_ERR_CAPTURE before anything is enqueued.  The
  *   marginal value of iteration k is produced by the passes of iteration
