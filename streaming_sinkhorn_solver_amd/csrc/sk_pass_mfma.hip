@@ -41,9 +41,6 @@ constexpr int kWaves = kBlock / 64;
 #ifndef SK_MFMA_TILE_FLOATS
 #define SK_MFMA_TILE_FLOATS 8192
 #endif
-#ifndef SK_MFMA_PIPE
-#define SK_MFMA_PIPE 0
-#endif
 
 // 16-query blocks per wave (register budget: NQB * P / 4 query VGPRs)
 template <int P>
@@ -186,52 +183,6 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
             __syncthreads();
             if (base + TL < j1) stage.load(kp, A.kbias, base + TL, j1);
             const int ntile = min(TL, j1 - base);
-#if SK_MFMA_PIPE
-            // software pipeline over pairs of 16-key blocks with two register
-            // sets: the MFMA chain of one block is issued before the log-sum-exp
-            // epilogue of the previous one (independent registers), and the next
-            // block's keys are read from LDS meanwhile, so vector ALU and LDS work
-            // hides under the MFMAs.  The tile holds a whole number of pairs and
-            // its keys past the segment end carry bias -inf, so a pair may run
-            // past ntile: such scores are -inf and add nothing.
-            constexpr int kBlocks = TL / 16;
-            static_assert(kBlocks % 2 == 0, "the tile must hold whole pairs of 16-key blocks");
-            const int npair = (ntile + 31) >> 5;
-            float ka[KT], kc[KT];
-            f4 accA[NQB], accB[NQB];
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) accB[qb] = f4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            load_keys<KT>(ka, ktile, c * PS + g * KT);
-            for (int pr = 0; pr < npair; ++pr) {
-                const int b0 = 2 * pr;
-                load_keys<KT>(kc, ktile, ((b0 + 1) * 16 + c) * PS + g * KT);
-                const f4 biasA = *reinterpret_cast<const f4*>(&btile[b0 * 16 + 4 * g]);
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) accA[qb] = biasA;
-#pragma unroll
-                for (int t = 0; t < KT; ++t)
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-                        accA[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[t], qf[qb][t], accA[qb], 0, 0, 0);
-                // block b0 - 1 (a no-op on the -inf scores before the first pair)
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], accB[qb]);
-                const int bn = min(b0 + 2, kBlocks - 1);  // next pair's first block (clamped: unused past the end)
-                load_keys<KT>(ka, ktile, (bn * 16 + c) * PS + g * KT);
-                const f4 biasB = *reinterpret_cast<const f4*>(&btile[(b0 + 1) * 16 + 4 * g]);
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) accB[qb] = biasB;
-#pragma unroll
-                for (int t = 0; t < KT; ++t)
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-                        accB[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kc[t], qf[qb][t], accB[qb], 0, 0, 0);
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], accA[qb]);
-            }
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], accB[qb]);
-#else
             for (int kb = 0; kb < ntile; kb += 16) {
                 float kf[KT];
                 load_keys<KT>(kf, ktile, (kb + c) * PS + g * KT);
@@ -247,7 +198,6 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], acc[qb]);
             }
-#endif
         }
 
         // the four lane groups hold disjoint key subsets of the same queries
