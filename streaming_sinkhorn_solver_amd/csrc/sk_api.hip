@@ -860,12 +860,14 @@ struct FLayout {
     size_t ky, kx, knrm, kl2w;
     size_t sq, sf, sa, snrm;
     size_t fs, gs;
-    size_t score, keep, rcnt, rptr, ridx, ccnt, cptr, cidx, spart;
+    size_t rowbest, colbest, rcnt, rptr, ridx, ccnt, cptr, cidx, spart;
+    int64_t list_cap;  // entries of each kept-tile list
     int sparse_groups;
     size_t total;
 };
 
-constexpr int64_t kMaxTiles = (int64_t)1 << 26;  // block pairs of the tile matrices
+constexpr int64_t kMaxTiles = (int64_t)1 << 32;     // block pairs the screening scores
+constexpr int64_t kMaxKeptTiles = (int64_t)1 << 28;  // entries of each kept-tile list
 constexpr int kSparseGroups = 2048;              // workgroups of a sparse pass (8 per CU on 256 CUs)
 
 int morton_bits_for(int d) { return std::max(1, std::min(10, 30 / d)); }
@@ -926,14 +928,15 @@ bool make_flayout(int64_t n, int64_t m, int d, int B, int n_sample, FLayout* out
     F.snrm = take((size_t)F.ns * 4);
     F.fs = take(un * 4);
     F.gs = take(um * 4);
-    F.score = take(bx * by * 4);
-    F.keep = take(bx * by);
+    F.list_cap = std::min<int64_t>((int64_t)bx * (int64_t)by, kMaxKeptTiles);
+    F.rowbest = take(bx * 4);
+    F.colbest = take(by * 4);
     F.rcnt = take(bx * 4);
     F.rptr = take((bx + 1) * 4);
-    F.ridx = take(bx * by * 4);
+    F.ridx = take((size_t)F.list_cap * 4);
     F.ccnt = take(by * 4);
     F.cptr = take((by + 1) * 4);
-    F.cidx = take(bx * by * 4);
+    F.cidx = take((size_t)F.list_cap * 4);
     F.sparse_groups = kSparseGroups;
     F.spart = take((size_t)F.sparse_groups * 2 * B * sizeof(float2));
     F.total = off;
@@ -1064,8 +1067,9 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     sa.eps = eps;
     sa.delta = o.delta;
     sa.log_delta = o.delta > 0.0f ? (float)std::log((double)o.delta) : -INFINITY;
-    sa.score = fp(F.score);
-    sa.keep = reinterpret_cast<uint8_t*>(base + F.keep);
+    sa.rowbest = ip(F.rowbest);
+    sa.colbest = ip(F.colbest);
+    sa.cap = F.list_cap;
     SparseArgs rowp{}, colp{};
     rowp.q = W.f(L.xp);
     rowp.k = W.f(L.yp);
@@ -1099,19 +1103,24 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
             SK_TRY(launch_block_max(fs, as, n, F.B, fp(F.fmax), s));
             SK_TRY(launch_block_max(gs, bs, m, F.B, fp(F.gmax), s));
             SK_TRY(launch_screen(sa, ip(F.rcnt), ip(F.rptr), ip(F.ridx), ip(F.ccnt), ip(F.cptr), ip(F.cidx), s));
+            // the kept total must fit the lists before any sparse pass reads them (a host
+            // read per screening); the last row block's list and the last column block's
+            // count give the point pairs of the kept tiles for the pass timing
+            int rp[2], cp[2], last = -1;
+            SK_TRY(hipMemcpyAsync(rp, ip(F.rptr) + F.nbx - 1, sizeof rp, hipMemcpyDeviceToHost, s));
+            SK_TRY(hipMemcpyAsync(cp, ip(F.cptr) + F.nby - 1, sizeof cp, hipMemcpyDeviceToHost, s));
+            SK_TRY(hipStreamSynchronize(s));
+            if ((int64_t)rp[1] > F.list_cap) return SK_ERR_SHAPE;  // more kept tiles than the lists hold
             if (timing_on()) {
-                // point pairs of the kept tiles, for the pass timing only (a host read
-                // per screening): full B x B tiles, less the short last row / column block
-                int rp[2], cp[2];
-                uint8_t last = 0;
-                SK_TRY(hipMemcpyAsync(rp, ip(F.rptr) + F.nbx - 1, sizeof rp, hipMemcpyDeviceToHost, s));
-                SK_TRY(hipMemcpyAsync(cp, ip(F.cptr) + F.nby - 1, sizeof cp, hipMemcpyDeviceToHost, s));
-                SK_TRY(hipMemcpyAsync(&last, sa.keep + F.nbx * F.nby - 1, 1, hipMemcpyDeviceToHost, s));
-                SK_TRY(hipStreamSynchronize(s));
+                // full B x B tiles, less the short last row / column block
+                if (rp[1] > rp[0]) {
+                    SK_TRY(hipMemcpyAsync(&last, ip(F.ridx) + rp[1] - 1, sizeof last, hipMemcpyDeviceToHost, s));
+                    SK_TRY(hipStreamSynchronize(s));
+                }
                 const double Bd = F.B, sr = Bd - (double)(n - (int64_t)(F.nbx - 1) * F.B),
                              sc = Bd - (double)(m - (int64_t)(F.nby - 1) * F.B);
                 kept_pairs = Bd * Bd * rp[1] - Bd * sr * (rp[1] - rp[0]) - Bd * sc * (cp[1] - cp[0]) +
-                             sr * sc * (last ? 1.0 : 0.0);
+                             sr * sc * (last == F.nby - 1 ? 1.0 : 0.0);
             }
         }
         hipEvent_t e0, e1;
@@ -1151,6 +1160,7 @@ int check_fs2(int64_t n, int64_t m, int32_t d, const Fs2Opts& o) {
     if (o.B < 1 || o.B > valu_rows_per_block()) return SK_ERR_SHAPE;
     const int64_t nbx = (n + o.B - 1) / o.B, nby = (m + o.B - 1) / o.B;
     if (nbx * nby > kMaxTiles) return SK_ERR_SHAPE;
+    if (o.delta <= 0.0f && nbx * nby > kMaxKeptTiles) return SK_ERR_SHAPE;  // delta 0 keeps every tile
     if (!(o.tol >= 0.0f) || !std::isfinite(o.tol) || !(o.delta >= 0.0f) || !std::isfinite(o.delta) ||
         !std::isfinite(o.coarse_gain))
         return SK_ERR_STOP;

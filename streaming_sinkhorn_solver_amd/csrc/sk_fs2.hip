@@ -232,47 +232,45 @@ __device__ inline void wg_argmax(float& bs, int& bi, float* shs, int* shi) {
     __syncthreads();
 }
 
-// One workgroup per row block I: scores, keep flags, and the row's best tile kept.
-__global__ __launch_bounds__(kBlock) void k_screen_rows(ScreenArgs A) {
+// The tile bounds are recomputed wherever they are needed instead of being
+// stored: evaluating one is a box distance and two logarithms, and an
+// NBx x NBy matrix of them would bound the problem size by memory.
+
+// One workgroup per line o (a row block when rows, else a column block): the
+// other index of the line's tile of largest bound (ties to the smaller index).
+__global__ __launch_bounds__(kBlock) void k_screen_best(ScreenArgs A, int rows) {
     __shared__ float shs[kBlock];
     __shared__ int shi[kBlock];
-    const int I = blockIdx.x;
+    const int o = blockIdx.x;
+    const int len = rows ? A.nby : A.nbx;
     float bs = -INFINITY;
     int bi = INT_MAX;
-    for (int J = threadIdx.x; J < A.nby; J += blockDim.x) {
-        const float s = tile_score(A, I, J);
-        A.score[(size_t)I * A.nby + J] = s;
-        A.keep[(size_t)I * A.nby + J] = (A.delta <= 0.0f || s > A.log_delta) ? 1 : 0;
-        better(bs, bi, s, J);
-    }
+    for (int u = threadIdx.x; u < len; u += blockDim.x) better(bs, bi, rows ? tile_score(A, o, u) : tile_score(A, u, o), u);
     wg_argmax(bs, bi, shs, shi);
-    if (threadIdx.x == 0 && bi < A.nby) A.keep[(size_t)I * A.nby + bi] = 1;
+    if (threadIdx.x == 0) (rows ? A.rowbest : A.colbest)[o] = bi < len ? bi : 0;
 }
 
-// One workgroup per column block J: the column's best tile kept.
-__global__ __launch_bounds__(kBlock) void k_screen_cols(ScreenArgs A) {
-    __shared__ float shs[kBlock];
-    __shared__ int shi[kBlock];
-    const int J = blockIdx.x;
-    float bs = -INFINITY;
-    int bi = INT_MAX;
-    for (int I = threadIdx.x; I < A.nbx; I += blockDim.x) better(bs, bi, A.score[(size_t)I * A.nby + J], I);
-    wg_argmax(bs, bi, shs, shi);
-    if (threadIdx.x == 0 && bi < A.nbx) A.keep[(size_t)bi * A.nby + J] = 1;
+// Whether tile (I, J) is kept: its bound is above log delta (every tile when
+// delta <= 0), or it is the best tile of its row block or of its column block.
+// Not inlined: the row lists and the column lists then take every decision
+// with the same machine code, so they hold the same tiles.
+__device__ __noinline__ bool tile_kept(const ScreenArgs& A, int I, int J) {
+    return A.delta <= 0.0f || A.rowbest[I] == J || A.colbest[J] == I || tile_score(A, I, J) > A.log_delta;
 }
 
-// Kept tiles of line o (a row block when rows, else a column block), in increasing order of
-// the other index: count (idx == null) or write at ptr[o].  Each thread takes a contiguous
-// run of the line, so a workgroup prefix sum keeps the order.
-__global__ __launch_bounds__(kBlock) void k_tile_list(const uint8_t* __restrict__ keep, int nbx, int nby, int rows,
-                                                      const int* __restrict__ ptr, int* __restrict__ cnt,
-                                                      int* __restrict__ idx) {
+// Kept tiles of line o (a row block when rows, else a column block), in
+// increasing order of the other index: count (idx == null) or write at ptr[o]
+// (entries at or beyond cap are not written; the caller checks the total).
+// Each thread takes a contiguous run of the line, so a workgroup prefix sum
+// keeps the order.
+__global__ __launch_bounds__(kBlock) void k_tile_list(ScreenArgs A, int rows, const int* __restrict__ ptr,
+                                                      int* __restrict__ cnt, int* __restrict__ idx) {
     __shared__ int sh[kBlock];
     const int o = blockIdx.x;
-    const int len = rows ? nby : nbx;
+    const int len = rows ? A.nby : A.nbx;
     const int per = (len + kBlock - 1) / kBlock;
-    const int u0 = threadIdx.x * per, u1 = min(u0 + per, len);
-    auto at = [&](int u) { return rows ? keep[(size_t)o * nby + u] : keep[(size_t)u * nby + o]; };
+    const int u0 = min(threadIdx.x * per, len), u1 = min(u0 + per, len);
+    auto at = [&](int u) { return rows ? tile_kept(A, o, u) : tile_kept(A, u, o); };
     int c = 0;
     for (int u = u0; u < u1; ++u) c += at(u) ? 1 : 0;
     sh[threadIdx.x] = c;
@@ -288,32 +286,39 @@ __global__ __launch_bounds__(kBlock) void k_tile_list(const uint8_t* __restrict_
         if (threadIdx.x == kBlock - 1) cnt[o] = sh[kBlock - 1];
         return;
     }
-    int pos = ptr[o] + sh[threadIdx.x] - c;
+    int64_t pos = (int64_t)ptr[o] + sh[threadIdx.x] - c;
     for (int u = u0; u < u1; ++u)
-        if (at(u)) idx[pos++] = u;
+        if (at(u)) {
+            if (pos < A.cap) idx[pos] = u;
+            ++pos;
+        }
 }
 
-// Exclusive prefix sum of cnt[0..len) into ptr[0..len] in one workgroup (fixed order).
-__global__ __launch_bounds__(kBlock) void k_exclusive_scan(const int* __restrict__ cnt, int len, int* __restrict__ ptr) {
-    __shared__ int sh[kBlock];
+// Exclusive prefix sum of cnt[0..len) into ptr[0..len] in one workgroup (fixed
+// order), summed in 64 bits; values above cap are stored as cap + 1, so a total
+// beyond the lists' capacity shows as ptr[len] > cap however large it is.
+__global__ __launch_bounds__(kBlock) void k_exclusive_scan(const int* __restrict__ cnt, int len, int64_t cap,
+                                                           int* __restrict__ ptr) {
+    __shared__ long long sh[kBlock];
     const int per = (len + kBlock - 1) / kBlock;
-    const int u0 = threadIdx.x * per, u1 = min(u0 + per, len);
-    int c = 0;
+    const int u0 = min(threadIdx.x * per, len), u1 = min(u0 + per, len);
+    long long c = 0;
     for (int u = u0; u < u1; ++u) c += cnt[u];
     sh[threadIdx.x] = c;
     __syncthreads();
     for (int w = 1; w < kBlock; w <<= 1) {
-        const int v = threadIdx.x >= w ? sh[threadIdx.x - w] : 0;
+        const long long v = threadIdx.x >= w ? sh[threadIdx.x - w] : 0;
         __syncthreads();
         sh[threadIdx.x] += v;
         __syncthreads();
     }
-    int run = sh[threadIdx.x] - c;
+    auto clamp = [&](long long v) { return (int)(v > cap ? cap + 1 : v); };
+    long long run = sh[threadIdx.x] - c;
     for (int u = u0; u < u1; ++u) {
-        ptr[u] = run;
+        ptr[u] = clamp(run);
         run += cnt[u];
     }
-    if (threadIdx.x == kBlock - 1) ptr[len] = sh[kBlock - 1];
+    if (threadIdx.x == kBlock - 1) ptr[len] = clamp(sh[kBlock - 1]);
 }
 
 __global__ __launch_bounds__(kBlock) void k_scatter(const float* __restrict__ in, const int* __restrict__ perm, int n,
@@ -376,14 +381,14 @@ hipError_t launch_block_max(const float* pot, const float* w, int n, int B, floa
 
 hipError_t launch_screen(const ScreenArgs& a, int* rcnt, int* rptr, int* ridx, int* ccnt, int* cptr, int* cidx,
                          hipStream_t s) {
-    hipLaunchKernelGGL(k_screen_rows, dim3(a.nbx), dim3(kBlock), 0, s, a);
-    hipLaunchKernelGGL(k_screen_cols, dim3(a.nby), dim3(kBlock), 0, s, a);
-    hipLaunchKernelGGL(k_tile_list, dim3(a.nbx), dim3(kBlock), 0, s, a.keep, a.nbx, a.nby, 1, nullptr, rcnt, nullptr);
-    hipLaunchKernelGGL(k_tile_list, dim3(a.nby), dim3(kBlock), 0, s, a.keep, a.nbx, a.nby, 0, nullptr, ccnt, nullptr);
-    hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(kBlock), 0, s, rcnt, a.nbx, rptr);
-    hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(kBlock), 0, s, ccnt, a.nby, cptr);
-    hipLaunchKernelGGL(k_tile_list, dim3(a.nbx), dim3(kBlock), 0, s, a.keep, a.nbx, a.nby, 1, rptr, rcnt, ridx);
-    hipLaunchKernelGGL(k_tile_list, dim3(a.nby), dim3(kBlock), 0, s, a.keep, a.nbx, a.nby, 0, cptr, ccnt, cidx);
+    hipLaunchKernelGGL(k_screen_best, dim3(a.nbx), dim3(kBlock), 0, s, a, 1);
+    hipLaunchKernelGGL(k_screen_best, dim3(a.nby), dim3(kBlock), 0, s, a, 0);
+    hipLaunchKernelGGL(k_tile_list, dim3(a.nbx), dim3(kBlock), 0, s, a, 1, nullptr, rcnt, nullptr);
+    hipLaunchKernelGGL(k_tile_list, dim3(a.nby), dim3(kBlock), 0, s, a, 0, nullptr, ccnt, nullptr);
+    hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(kBlock), 0, s, rcnt, a.nbx, a.cap, rptr);
+    hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(kBlock), 0, s, ccnt, a.nby, a.cap, cptr);
+    hipLaunchKernelGGL(k_tile_list, dim3(a.nbx), dim3(kBlock), 0, s, a, 1, rptr, rcnt, ridx);
+    hipLaunchKernelGGL(k_tile_list, dim3(a.nby), dim3(kBlock), 0, s, a, 0, cptr, ccnt, cidx);
     return hipGetLastError();
 }
 

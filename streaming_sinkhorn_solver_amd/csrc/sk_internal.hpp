@@ -151,8 +151,9 @@ struct ScreenArgs {
     const float *xlo, *xhi, *ylo, *yhi;  // block boxes [blocks][d]
     int nbx, nby, d;
     float eps, delta, log_delta;
-    float* score;                // [nbx][nby]
-    uint8_t* keep;               // [nbx][nby]
+    int* rowbest;                // [nbx] the tile of largest bound in each row block
+    int* colbest;                // [nby] ... in each column block
+    int64_t cap;                 // capacity of each tile list (entries)
 };
 
 // Arguments of a streamed transport product (d <= 8; see sk_transport.hip).
