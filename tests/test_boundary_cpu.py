@@ -225,9 +225,9 @@ def test_fs2_argument_errors(lib):
     assert lib.sk_fs2_workspace_bytes(1000, 1000, 9, 256, 64) == 0
     assert lib.sk_fs2_workspace_bytes(1000, 1000, 2, 0, 64) == 0
     assert lib.sk_fs2_workspace_bytes(1000, 1000, 2, 513, 64) == 0
-    assert lib.sk_fs2_workspace_bytes(1 << 20, 1 << 20, 2, 16, 64) == 0  # 2^32 block pairs
     ii, ff = (ctypes.c_int32 * 4)(), (ctypes.c_float * 2)()
-    fs = lambda **k: lib.sk_fs2_solve(k.get("x", FAKE), FAKE, FAKE, FAKE, 1000, 900, k.get("d", 2), k.get("eps", 0.01),
+    fs = lambda **k: lib.sk_fs2_solve(k.get("x", FAKE), FAKE, FAKE, FAKE, k.get("n", 1000), k.get("m", 900),
+                                      k.get("d", 2), k.get("eps", 0.01),
                                       k.get("B", 64), k.get("tol", 1e-5), k.get("delta", 1e-6), k.get("ci", 10),
                                       k.get("mr", 5), k.get("gain", 0.1), k.get("ns", 64), k.get("mi", 100),
                                       k.get("ce", 10), k.get("se", 10), FAKE, FAKE, ii, ff, None, None, FAKE, 1 << 30,
@@ -239,6 +239,9 @@ def test_fs2_argument_errors(lib):
     assert fs(tol=-1.0) == SK_ERR_STOP and fs(delta=float("nan")) == SK_ERR_STOP and fs(gain=float("inf")) == SK_ERR_STOP
     assert fs(ci=0) == SK_ERR_ITERS and fs(mr=0) == SK_ERR_ITERS and fs(ns=0) == SK_ERR_ITERS
     assert fs(mi=-1) == SK_ERR_ITERS and fs(ce=0) == SK_ERR_ITERS and fs(se=0) == SK_ERR_ITERS
+    # block-pair limits: at most 2^32 pairs scored; with delta = 0 (every pair kept) at most 2^28
+    assert fs(n=1 << 21, m=1 << 21, B=16) == SK_ERR_SHAPE  # 2^34 pairs
+    assert fs(n=(1 << 18) + 16, m=1 << 18, B=16, delta=0.0) == SK_ERR_SHAPE  # (2^14 + 1) 2^14 pairs, all kept
 
 
 def test_python_contract_errors_before_gpu():
