@@ -55,10 +55,12 @@ extern "C" {
 typedef enum sk_status {
     SK_OK = 0,
     SK_ERR_NULL = 1,           /* a required pointer is NULL */
-    SK_ERR_SHAPE = 2,          /* n < 1, m < 1 or d < 1, or n, m beyond 2^31 - 1 */
+    SK_ERR_SHAPE = 2,          /* n < 1, m < 1 or d < 1, or n, m beyond 2^31 - 1; also a payload
+                                  width, block size or block-pair count outside an entry
+                                  point's limits (see sk_transport, sk_fs2_solve) */
     SK_ERR_UNSUPPORTED_D = 3,  /* d > 256 */
     SK_ERR_EPS = 4,            /* eps not finite or eps <= 0 */
-    SK_ERR_ITERS = 5,          /* n_iters < 0 */
+    SK_ERR_ITERS = 5,          /* an iteration or step count out of range (n_iters < 0, ...) */
     SK_ERR_CHECK_EVERY = 6,    /* check_every < 0, or > 0 with resid_trace == NULL */
     SK_ERR_NEG_WEIGHT = 7,     /* some a_i or b_j < 0 */
     SK_ERR_MASS_MISMATCH = 8,  /* |sum a - sum b| > 1e-5 * max(sum a, sum b) */
@@ -68,8 +70,10 @@ typedef enum sk_status {
     SK_ERR_HIP = 12,           /* a HIP runtime call or kernel launch failed */
     SK_ERR_VARIANT = 13,       /* variant not 0 or 1, or symmetric with alpha outside (0, 1] */
     SK_ERR_STOP = 14,          /* stop_mode not 0, 1 or 2; or a stop rule with stop_tol < 0,
-                                  non-finite, or check_every < 1 */
-    SK_ERR_CAPTURE = 15,       /* a stop rule was asked for on a stream under graph capture */
+                                  non-finite, or check_every < 1; or a negative or non-finite
+                                  threshold of sk_fs2_solve */
+    SK_ERR_CAPTURE = 15,       /* a host-synchronous call (a stop rule, sk_fs2_solve) on a
+                                  stream under graph capture */
     SK_ERR_LR = 16             /* the gradient-flow step size is not finite */
 } sk_status;
 

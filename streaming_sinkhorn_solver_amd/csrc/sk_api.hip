@@ -1210,10 +1210,12 @@ const char* sk_status_string(int status) {
     switch (status) {
         case SK_OK: return "ok";
         case SK_ERR_NULL: return "a required pointer is NULL";
-        case SK_ERR_SHAPE: return "invalid sizes (n, m, d must be >= 1 and n, m < 2^31)";
+        case SK_ERR_SHAPE:
+            return "invalid sizes or shape arguments (n, m, d >= 1 and n, m < 2^31; payload widths, block sizes and "
+                   "block-pair counts within the entry point's limits)";
         case SK_ERR_UNSUPPORTED_D: return "unsupported dimension d";
         case SK_ERR_EPS: return "eps must be finite and > 0 (and 2*log2(e)/eps finite in fp32)";
-        case SK_ERR_ITERS: return "n_iters must be >= 0";
+        case SK_ERR_ITERS: return "an iteration or step count is out of range";
         case SK_ERR_CHECK_EVERY: return "check_every must be >= 0, with resid_trace when > 0";
         case SK_ERR_NEG_WEIGHT: return "weights must be nonnegative";
         case SK_ERR_MASS_MISMATCH: return "sum(a) must equal sum(b)";
@@ -1222,8 +1224,10 @@ const char* sk_status_string(int status) {
         case SK_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or too small";
         case SK_ERR_HIP: return "HIP runtime or kernel launch failure";
         case SK_ERR_VARIANT: return "variant must be 0 (alternating) or 1 (symmetric, 0 < alpha <= 1)";
-        case SK_ERR_STOP: return "stop_mode must be 0, 1 or 2; a stop rule needs tol >= 0 finite and check_every >= 1";
-        case SK_ERR_CAPTURE: return "a stop rule synchronises the stream and cannot run under graph capture";
+        case SK_ERR_STOP:
+            return "invalid stop or threshold arguments (stop_mode 0, 1 or 2; tolerances and thresholds finite and "
+                   ">= 0; check_every >= 1)";
+        case SK_ERR_CAPTURE: return "this call synchronises the stream and cannot run under graph capture";
         case SK_ERR_LR: return "the step size must be finite";
         default: return "unknown status";
     }
