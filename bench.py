@@ -42,7 +42,9 @@ evaluations of the counted iterations only):
               target of --fs2-tol-rel times the largest point mass; value
               counts the dense-equivalent 2 n m evaluations per fine
               iteration; the line adds the solver's counts, the kept fraction,
-              the all-particle residual of the result (two dense passes) and,
+              the time of the ordering, coarse stage and lift alone (a run
+              with no fine iteration, untimed), the all-particle residual of
+              the result (two dense passes, up to n m = 2e14) and,
               with --fs2-dense, the time of the dense solver (stop rule
               "marginal", same tolerance) for the same problem.
 The roofline of the hvp / transport modes is that of the transport kernel
@@ -184,6 +186,9 @@ def main():
     ap.add_argument("--workload", default="gmm8_d3_sq")
     ap.add_argument("--iters", type=int, default=None, help="override the workload's iteration count")
     ap.add_argument("--size", type=int, default=None, help="override n = m (same recipe, e.g. a smaller problem)")
+    ap.add_argument("--eps-blur", action="store_true",
+                    help="eps = n^(-2/3), the squared mean spacing of n points in the unit cube (the cluster_d3 "
+                         "workload's rule) at the --size given")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceilings", action="store_true", help="run the issue-rate micro-benchmarks and exit")
     ap.add_argument("--graph", action="store_true",
@@ -229,6 +234,8 @@ def main():
     n_iters = w.n_iters if args.iters is None else args.iters
     eps = eps32(w.eps)
     x, y, a, b = make_inputs(args.workload, n=args.size, m=args.size)
+    if args.eps_blur:
+        eps = eps32(float(x.shape[0]) ** (-2.0 / 3.0))
     n, m, d = x.shape[0], y.shape[0], w.d
     dev = torch.device("cuda:0")
     X, Y, A, B = (torch.from_numpy(v).to(dev) for v in (x, y, a, b))
@@ -364,10 +371,20 @@ def main():
     elif mode == "divergence":
         extra = {"divergence": [float(v) for v in dv_out.cpu()]}
     elif mode == "fs2":
-        r = sk.marginal_residual(X, Y, A, B, f, g, eps=eps)
+        # the all-particle residual takes two dense passes: skipped beyond about an hour's reach of them
+        dense_ok = float(n) * float(m) <= 2.0e14
+        r = sk.marginal_residual(X, Y, A, B, f, g, eps=eps) if dense_ok else None
+        # the order, blocks, coarse stage and lift alone (no fine iteration, so no screening), outside the timing
+        torch.cuda.synchronize()
+        t4 = time.perf_counter()
+        sk.fs2_solve(X, Y, A, B, eps=eps, block=args.fs2_block, tol=fs2_tol, delta=args.fs2_delta, max_iters=0,
+                     ws=ws_fs2, check=False)
+        torch.cuda.synchronize()
+        coarse_s = time.perf_counter() - t4
         extra = {"fs2": {k: v for k, v in fs2_info.items() if not k.startswith("perm")}, "fs2_tol": fs2_tol,
+                 "coarse_stage_s": coarse_s,
                  "block": args.fs2_block, "delta": args.fs2_delta, "solve_s": step_s, "workspace_mb": nb / 1e6,
-                 "all_particle_residual": float(max(r[0].item(), r[1].item()))}
+                 "all_particle_residual": float(max(r[0].item(), r[1].item())) if dense_ok else None}
         if args.fs2_dense:
             torch.cuda.synchronize()
             t3 = time.perf_counter()
@@ -425,8 +442,12 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "n": n, "m": m, "d": d, "eps": eps, "n_iters": n_iters,
-                   "check_every": ce, "grad_x": bool(w.grad), "recipe": w.description},
+        "config": {"workload": args.workload, "n": n, "m": m, "d": d, "eps": eps,
+                   # the two-stage solver runs to its target or its iteration cap, without the gradient
+                   "n_iters": args.fs2_max_iters if mode == "fs2" else n_iters,
+                   "check_every": ce if mode != "fs2" else 10, "grad_x": bool(w.grad) and mode != "fs2",
+                   "eps_rule": "n^(-2/3) at n = %d" % n if args.eps_blur else "the workload's",
+                   "recipe": w.description},
         "mode": mode,
         "iters_per_s": (3 * n_iters if mode == "divergence" else
                         fs2_info["fine_iters"] if mode == "fs2" else counted_iters) / step_s,
@@ -434,7 +455,7 @@ def main():
         "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s if launches else None,
         "roofline": roof,
         "final_residual": float(trace[n_iters // ce - 1].item()) if (ce and mode == "solve") else None,
-        "cost": float(cost_out.item()) if mode not in ("divergence", "hvp", "transport") else None,
+        "cost": float(cost_out.item()) if mode not in ("divergence", "hvp", "transport", "fs2") else None,
         **extra,
     }
     if not args.no_cpu_baseline and mode == "solve":

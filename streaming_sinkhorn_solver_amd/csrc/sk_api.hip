@@ -866,7 +866,7 @@ struct FLayout {
     size_t total;
 };
 
-constexpr int64_t kMaxTiles = (int64_t)1 << 32;     // block pairs the screening scores
+constexpr int64_t kMaxTiles = (int64_t)1 << 34;     // block pairs the screening scores
 constexpr int64_t kMaxKeptTiles = (int64_t)1 << 28;  // entries of each kept-tile list
 constexpr int kSparseGroups = 2048;              // workgroups of a sparse pass (8 per CU on 256 CUs)
 
@@ -1533,7 +1533,8 @@ int sk_hvp(const float* x, const float* y, const float* a, const float* b, int64
 }
 
 size_t sk_fs2_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t block, int32_t n_sample) {
-    Fs2Opts o{block, 0.0f, 0.0f, 1, 1, 0.0f, std::max(n_sample, 1), 0, 1, 1};
+    // the workspace does not depend on the thresholds: a positive delta stands in for any
+    Fs2Opts o{block, 0.0f, 1e-6f, 1, 1, 0.0f, std::max(n_sample, 1), 0, 1, 1};
     if (check_fs2(n, m, d, o) != SK_OK) return 0;
     FLayout F;
     if (!make_flayout(n, m, d, block, std::max(n_sample, 1), &F)) return 0;

@@ -237,3 +237,14 @@ def test_repeat_runs_are_bit_identical():
     assert np.array_equal(f1, f2) and np.array_equal(g1, g2)
     for k in ("rounds", "fine_iters", "kept", "converged", "residual"):
         assert i1[k] == i2[k] or (k == "residual" and np.isnan(i1[k]) and np.isnan(i2[k])), k
+
+
+def test_workspace_query_at_large_block_counts():
+    """The workspace size does not depend on the thresholds: it is returned for block counts whose
+    every-pair-kept total would exceed the kept-tile lists (2^14 x 2^14 blocks and more)."""
+    lib = sk.load_library()
+    for n in (1 << 23, 1 << 24):
+        nb = lib.sk_fs2_workspace_bytes(n, n, 3, 512, 1024)
+        assert nb > 0
+        # lists of 2^28 entries (two, 4 bytes each) plus O(n) arrays, not O(NB^2) ones
+        assert nb < 4 * (1 << 30) + 400 * n
