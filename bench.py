@@ -234,6 +234,7 @@ def main():
     n_iters = w.n_iters if args.iters is None else args.iters
     eps = eps32(w.eps)
     x, y, a, b = make_inputs(args.workload, n=args.size, m=args.size)
+    print(f"inputs ready: {x.shape[0]} x {y.shape[0]}, d = {x.shape[1]}", file=sys.stderr, flush=True)
     if args.eps_blur:
         eps = eps32(float(x.shape[0]) ** (-2.0 / 3.0))
     n, m, d = x.shape[0], y.shape[0], w.d
@@ -338,6 +339,7 @@ def main():
         sk.timing_enable(False)
 
     wall_s = t1 - t0
+    print(f"timed steps done: {wall_s:.3f} s", file=sys.stderr, flush=True)
     gpu_s = ev0.elapsed_time(ev1) * 1e-3
     step_s = max(wall_s, gpu_s) / args.steps
     counted_iters = stop.get("iters_run", n_iters)

@@ -356,7 +356,7 @@ size_t sk_fs2_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t block, in
  * check value (+inf when beyond float32 range).  perm_x, perm_y (device, n and m ints, or NULL) receive the
  * Morton order (original index of each sorted point).  Host-synchronous
  * (the checks are read back); refuses graph capture (SK_ERR_CAPTURE).
- * Also SK_ERR_SHAPE for a block outside [1, 512], more than 2^34 block pairs,
+ * Also SK_ERR_SHAPE for a block outside [1, 512], more than 2^36 block pairs,
  * delta = 0 (every pair kept) with more than 2^28 block pairs, or -- during
  * the solve, returned at the screening that found it -- more than 2^28 kept
  * pairs (raise delta or the block size), SK_ERR_STOP for a negative or non-finite tol, delta or coarse_gain,

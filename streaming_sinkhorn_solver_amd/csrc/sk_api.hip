@@ -858,15 +858,15 @@ struct FLayout {
     size_t xs, ys, as, bs, permx, permy;
     size_t amass, bmass, xcen, ycen, xlo, xhi, ylo, yhi, fmax, gmax, F, G;
     size_t ky, kx, knrm, kl2w;
-    size_t sq, sf, sa, snrm;
+    size_t sq, sf, sa, snrm, slse;
     size_t fs, gs;
-    size_t rowbest, colbest, rcnt, rptr, ridx, ccnt, cptr, cidx, spart;
+    size_t srx, sry, rowbest, colbest, rcnt, rptr, ridx, ccnt, cptr, cidx, spart;
     int64_t list_cap;  // entries of each kept-tile list
     int sparse_groups;
     size_t total;
 };
 
-constexpr int64_t kMaxTiles = (int64_t)1 << 34;     // block pairs the screening scores
+constexpr int64_t kMaxTiles = (int64_t)1 << 36;     // block pairs the screening scores
 constexpr int64_t kMaxKeptTiles = (int64_t)1 << 28;  // entries of each kept-tile list
 constexpr int kSparseGroups = 2048;              // workgroups of a sparse pass (8 per CU on 256 CUs)
 
@@ -926,9 +926,12 @@ bool make_flayout(int64_t n, int64_t m, int d, int B, int n_sample, FLayout* out
     F.sf = take((size_t)F.ns * 4);
     F.sa = take((size_t)F.ns * 4);
     F.snrm = take((size_t)F.ns * 4);
+    F.slse = take((size_t)F.ns * 4);
     F.fs = take(un * 4);
     F.gs = take(um * 4);
     F.list_cap = std::min<int64_t>((int64_t)bx * (int64_t)by, kMaxKeptTiles);
+    F.srx = take(bx * (size_t)screen_stride_of(d) * 4);
+    F.sry = take(by * (size_t)screen_stride_of(d) * 4);
     F.rowbest = take(bx * 4);
     F.colbest = take(by * 4);
     F.rcnt = take(bx * 4);
@@ -994,12 +997,27 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     SK_TRY(launch_block_stats(ys, bs, m, d, F.B, fp(F.bmass), fp(F.ycen), fp(F.ylo), fp(F.yhi), s));
 
     // 3: coarse stage on the centroids, lifted to the points after every round
-    // (untimed: the pass timing covers the block-sparse passes of the fine stage)
+    // (untimed: the pass timing covers the block-sparse passes of the fine stage).
+    // The check of a round needs the lifted g at every point but the lifted f
+    // only at its sampled rows, so a round lifts f at those rows alone and f
+    // is lifted at every point once, from the accepted round.
     std::optional<TimingPause> pause;
     pause.emplace();
     PassArgs lift_f = make_pass(W, true, eps, as, cap);
     lift_f.fin.pot = fs;
     retarget(lift_f, W.f(L.xp), n, fp(F.ky), F.nby, cap);
+    const int stride = n / F.ns;
+    // the sampled rows: coordinates, weights and norms (their potential is lifted every round)
+    SK_TRY(launch_gather_rows(W.f(L.xp), L.P, fs, as, W.f(L.nx), F.ns, stride, fp(F.sq), fp(F.sf), fp(F.sa),
+                              fp(F.snrm), s));
+    PassArgs lift_fs = make_pass(W, true, eps, fp(F.sa), cap);
+    retarget(lift_fs, fp(F.sq), F.ns, fp(F.ky), F.nby, cap);
+    lift_fs.fin.lse = lift_fs.fin.lse_out = fp(F.slse);
+    lift_fs.fin.l2w = fp(F.slse);  // read by the finalisation, used only for a bias, and none is written
+    lift_fs.fin.nrm = fp(F.snrm);
+    lift_fs.fin.pot = fp(F.sf);
+    lift_fs.fin.bias_packed = nullptr;
+    lift_fs.fin.bias_sep = nullptr;
     PassArgs lift_g = make_pass(W, false, eps, bs, cap);
     lift_g.fin.pot = gs;
     retarget(lift_g, W.f(L.yp), m, fp(F.kx), F.nbx, cap);
@@ -1010,7 +1028,6 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     check.fin.pot_in = fp(F.sf);
     check.fin.rbuf = W.f(L.rbuf);
     retarget(check, fp(F.sq), F.ns, W.f(L.yp), m, cap);
-    const int stride = n / F.ns;
     // decisions on log2 of the check value: the same comparisons as on the value itself
     const double log2_tol = o.tol > 0.0f ? std::log2((double)o.tol) : -INFINITY;
     const double log2_keep = 1.0 - (double)o.coarse_gain > 0.0 ? std::log2(1.0 - (double)o.coarse_gain) : INFINITY;
@@ -1028,15 +1045,14 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
             if ((st = run_pass(Wc, col, s))) return st;
         }
         // lift: one c-transform of each side against the other side's centroids
+        // (f at the sampled rows only)
         SK_TRY(launch_pack(fp(F.ycen), F.nby, d, L.P, false, W.f(L.centre), fp(F.bmass), fp(F.ky), fp(F.knrm),
                            fp(F.kl2w), nullptr, 1.0f / eps, 2, Gc, nullptr, s));
-        if ((st = run_pass(W, lift_f, s))) return st;
+        if ((st = run_pass(W, lift_fs, s))) return st;
         SK_TRY(launch_pack(fp(F.xcen), F.nbx, d, L.P, false, W.f(L.centre), fp(F.amass), fp(F.kx), fp(F.knrm),
                            fp(F.kl2w), nullptr, 1.0f / eps, 2, Fc, nullptr, s));
         if ((st = run_pass(W, lift_g, s))) return st;
         // sampled check of the lifted plan's rows over all points
-        SK_TRY(launch_gather_rows(W.f(L.xp), L.P, fs, as, W.f(L.nx), F.ns, stride, fp(F.sq), fp(F.sf), fp(F.sa),
-                                  fp(F.snrm), s));
         if ((st = run_pass(W, check, s))) return st;
         SK_TRY(launch_max_reduce(W.f(L.rbuf), F.ns, slot.dev(), s, slot.flag(), slot.next()));
         if ((st = slot.read(host, 1, s))) return st;
@@ -1049,6 +1065,8 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
         if (round >= 2 && (log2_keep == INFINITY || lc > log2_keep + prev)) break;
         prev = lc;
     }
+    // f at every point from the accepted round (the packed centroids ky are still that round's)
+    if ((st = run_pass(W, lift_f, s))) return st;
 
     // 4-5: block-sparse fine stage from the lifted potentials
     pause.reset();
@@ -1067,6 +1085,8 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     sa.eps = eps;
     sa.delta = o.delta;
     sa.log_delta = o.delta > 0.0f ? (float)std::log((double)o.delta) : -INFINITY;
+    sa.dx = fp(F.srx);
+    sa.dy = fp(F.sry);
     sa.rowbest = ip(F.rowbest);
     sa.colbest = ip(F.colbest);
     sa.cap = F.list_cap;

@@ -190,18 +190,72 @@ __global__ __launch_bounds__(kBlock) void k_block_max(const float* __restrict__ 
 }
 
 // The tile bound of (I, J):
-//   score = (fmax_I + gmax_J - dmin_IJ^2)/eps + log max(B_J NBy, A_I NBx),
+//   score = (fmax_I + gmax_J - dmin_IJ^2)/eps + log max(A_I NBx, B_J NBy),
 // dmin from the two boxes; kept iff score > log delta (every tile when delta <= 0).
-__device__ inline float tile_score(const ScreenArgs& A, int I, int J) {
+// Each block is first packed into one record (its box, its potential maximum
+// and log(mass x block count)), so a bound is a box distance, an add and one
+// fma; the logarithm of the larger mass term is the larger logarithm.
+// The bounds are recomputed wherever they are needed instead of being stored:
+// an NBx x NBy matrix of them would bound the problem size by memory.
+template <int D>
+struct Rec {
+    float lo[D], hi[D], pot, lam;
+};
+
+template <int D>
+__device__ inline Rec<D> load_rec(const float* __restrict__ recs, int b) {
+    constexpr int S = screen_stride_of(D);
+    float v[S];
+    const float4* p = reinterpret_cast<const float4*>(recs + (size_t)b * S);
+#pragma unroll
+    for (int k = 0; k < S / 4; ++k) {
+        const float4 t = p[k];
+        v[4 * k] = t.x;
+        v[4 * k + 1] = t.y;
+        v[4 * k + 2] = t.z;
+        v[4 * k + 3] = t.w;
+    }
+    Rec<D> r;
+#pragma unroll
+    for (int t = 0; t < D; ++t) {
+        r.lo[t] = v[t];
+        r.hi[t] = v[D + t];
+    }
+    r.pot = v[2 * D];
+    r.lam = v[2 * D + 1];
+    return r;
+}
+
+// X is always the row (x) block and Y the column (y) block, and every step is
+// an IEEE operation with no multiply-add left to the compiler's choice, so a
+// tile's bound has the same bits in every kernel that evaluates it: the row
+// lists and the column lists hold the same tiles.
+template <int D>
+__device__ inline float rec_score(const Rec<D>& X, const Rec<D>& Y, float inv_eps) {
     float gap2 = 0.0f;
-    for (int t = 0; t < A.d; ++t) {
-        const float g1 = A.ylo[(size_t)J * A.d + t] - A.xhi[(size_t)I * A.d + t];
-        const float g2 = A.xlo[(size_t)I * A.d + t] - A.yhi[(size_t)J * A.d + t];
-        const float g = fmaxf(0.0f, fmaxf(g1, g2));
+#pragma unroll
+    for (int t = 0; t < D; ++t) {
+        const float g = fmaxf(0.0f, fmaxf(Y.lo[t] - X.hi[t], X.lo[t] - Y.hi[t]));
         gap2 = fmaf(g, g, gap2);
     }
-    const float E = (A.fmax[I] + A.gmax[J] - gap2) / A.eps;
-    return E + logf(fmaxf(A.bmass[J] * (float)A.nby, A.amass[I] * (float)A.nbx));
+    return fmaf((X.pot + Y.pot) - gap2, inv_eps, fmaxf(X.lam, Y.lam));
+}
+
+// One record per block: lo[d], hi[d], the potential maximum, log(mass * nb),
+// zero padding up to the stride.
+__global__ __launch_bounds__(kBlock) void k_screen_rec(const float* __restrict__ pmax, const float* __restrict__ mass,
+                                                       const float* __restrict__ lo, const float* __restrict__ hi,
+                                                       int nb, int d, int S, float* __restrict__ rec) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nb) return;
+    float* r = rec + (size_t)b * S;
+    for (int t = 0; t < d; ++t) {
+        r[t] = lo[(size_t)b * d + t];
+        r[d + t] = hi[(size_t)b * d + t];
+    }
+    r[2 * d] = pmax[b];
+    r[2 * d + 1] = logf(mass[b] * (float)nb);
+    for (int t = 2 * d + 2; t < S; ++t) r[t] = 0.0f;
 }
 
 // argmax with ties to the smaller index (numpy's first maximum); -inf scores tie too.
@@ -212,86 +266,165 @@ __device__ inline void better(float& bs, int& bi, float s, int i) {
     }
 }
 
-__device__ inline void wg_argmax(float& bs, int& bi, float* shs, int* shi) {
-    const int t = threadIdx.x;
-    shs[t] = bs;
-    shi[t] = bi;
+// Lines (row or column blocks) per workgroup: the line records stay in
+// registers, so fewer lines at larger d.
+constexpr int lines_of(int D) { return D <= 4 ? 8 : 4; }
+constexpr int kWaves = kBlock / 64;
+
+// The lines o0 .. o0 + NL - 1 of a workgroup: row blocks when ROWS, else
+// column blocks; a line past the end repeats the last one and is not stored.
+// The line records pass through LDS, so each lane holds its own copy in vector
+// registers instead of the compiler keeping them in scalar registers, which
+// it runs out of and spills.
+template <int D, bool ROWS>
+struct Lines {
+    static constexpr int NL = lines_of(D);
+    Rec<D> r[NL];
+    int best[NL];  // the line's own best tile (list kernels)
+    int o0, nl, no;
+    const float* other;
+    const int* obest;  // the other side's best tiles
+
+    __device__ Lines(const ScreenArgs& A, bool with_best, float* stage) {
+        constexpr int S = screen_stride_of(D);
+        o0 = blockIdx.x * NL;
+        nl = ROWS ? A.nbx : A.nby;
+        no = ROWS ? A.nby : A.nbx;
+        other = ROWS ? A.dy : A.dx;
+        obest = ROWS ? A.colbest : A.rowbest;
+        const float* own = ROWS ? A.dx : A.dy;
+        const int* lbest = ROWS ? A.rowbest : A.colbest;
+        for (int k = threadIdx.x; k < NL * S; k += blockDim.x)
+            stage[k] = own[(size_t)min(o0 + k / S, nl - 1) * S + k % S];
+        __syncthreads();
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            r[l] = load_rec<D>(stage, l);
+            best[l] = with_best ? lbest[min(o0 + l, nl - 1)] : 0;
+        }
+    }
+    __device__ float score(int l, const Rec<D>& q, float inv_eps) const {
+        return ROWS ? rec_score<D>(r[l], q, inv_eps) : rec_score<D>(q, r[l], inv_eps);
+    }
+    // tile (line l, other block u) kept: its bound is above log delta (every
+    // tile when delta <= 0), or it is the best tile of its row or its column
+    __device__ bool kept(const ScreenArgs& A, int l, int u, const Rec<D>& q, int obu) const {
+        return A.delta <= 0.0f || best[l] == u || obu == o0 + l || score(l, q, A.inv_eps) > A.log_delta;
+    }
+};
+
+// Per line, the other index of its tile of largest bound (ties to the smaller
+// index) into rowbest (ROWS) or colbest.
+template <int D, bool ROWS>
+__global__ __launch_bounds__(kBlock) void k_screen_best(ScreenArgs A) {
+    constexpr int NL = lines_of(D);
+    __shared__ float shs[NL][kWaves];
+    __shared__ int shi[NL][kWaves];
+    __shared__ float4 stage[NL * screen_stride_of(D) / 4];
+    const Lines<D, ROWS> L(A, false, reinterpret_cast<float*>(stage));
+    float bs[NL];
+    int bi[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        bs[l] = -INFINITY;
+        bi[l] = INT_MAX;
+    }
+    for (int u = threadIdx.x; u < L.no; u += kBlock) {
+        const Rec<D> q = load_rec<D>(L.other, u);
+#pragma unroll
+        for (int l = 0; l < NL; ++l) better(bs[l], bi[l], L.score(l, q, A.inv_eps), u);
+    }
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        for (int k = 32; k > 0; k >>= 1) better(bs[l], bi[l], __shfl_xor(bs[l], k), __shfl_xor(bi[l], k));
+        if (lane == 0) {
+            shs[l][wv] = bs[l];
+            shi[l][wv] = bi[l];
+        }
+    }
     __syncthreads();
-    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-        if (t < w) {
-            float s = shs[t];
-            int i = shi[t];
-            better(s, i, shs[t + w], shi[t + w]);
-            shs[t] = s;
-            shi[t] = i;
+    const int l = threadIdx.x;
+    if (l < NL && L.o0 + l < L.nl) {
+        float s = shs[l][0];
+        int i = shi[l][0];
+        for (int w = 1; w < kWaves; ++w) better(s, i, shs[l][w], shi[l][w]);
+        (ROWS ? A.rowbest : A.colbest)[L.o0 + l] = i < L.no ? i : 0;
+    }
+}
+
+// Kept tiles per line: counted into cnt (idx == null), else written at
+// ptr[line] in increasing order of the other index (entries at or beyond cap
+// are not written; the caller checks the total).  The workgroup walks the
+// other blocks in chunks of kBlock, one per thread, and places each chunk's
+// kept entries with a ballot and the wave totals, which keeps the order.
+template <int D, bool ROWS>
+__global__ __launch_bounds__(kBlock) void k_tile_list(ScreenArgs A, const int* __restrict__ ptr,
+                                                      int* __restrict__ cnt, int* __restrict__ idx) {
+    constexpr int NL = lines_of(D);
+    __shared__ int wt[NL][kWaves];
+    __shared__ float4 stage[NL * screen_stride_of(D) / 4];
+    const Lines<D, ROWS> L(A, true, reinterpret_cast<float*>(stage));
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (!idx) {
+        int c[NL] = {};
+        for (int u = threadIdx.x; u < L.no; u += kBlock) {
+            const Rec<D> q = load_rec<D>(L.other, u);
+            const int obu = L.obest[u];
+#pragma unroll
+            for (int l = 0; l < NL; ++l) c[l] += L.kept(A, l, u, q, obu) ? 1 : 0;
+        }
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            for (int k = 32; k > 0; k >>= 1) c[l] += __shfl_xor(c[l], k);
+            if (lane == 0) wt[l][wv] = c[l];
         }
         __syncthreads();
-    }
-    bs = shs[0];
-    bi = shi[0];
-    __syncthreads();
-}
-
-// The tile bounds are recomputed wherever they are needed instead of being
-// stored: evaluating one is a box distance and two logarithms, and an
-// NBx x NBy matrix of them would bound the problem size by memory.
-
-// One workgroup per line o (a row block when rows, else a column block): the
-// other index of the line's tile of largest bound (ties to the smaller index).
-__global__ __launch_bounds__(kBlock) void k_screen_best(ScreenArgs A, int rows) {
-    __shared__ float shs[kBlock];
-    __shared__ int shi[kBlock];
-    const int o = blockIdx.x;
-    const int len = rows ? A.nby : A.nbx;
-    float bs = -INFINITY;
-    int bi = INT_MAX;
-    for (int u = threadIdx.x; u < len; u += blockDim.x) better(bs, bi, rows ? tile_score(A, o, u) : tile_score(A, u, o), u);
-    wg_argmax(bs, bi, shs, shi);
-    if (threadIdx.x == 0) (rows ? A.rowbest : A.colbest)[o] = bi < len ? bi : 0;
-}
-
-// Whether tile (I, J) is kept: its bound is above log delta (every tile when
-// delta <= 0), or it is the best tile of its row block or of its column block.
-// Not inlined: the row lists and the column lists then take every decision
-// with the same machine code, so they hold the same tiles.
-__device__ __noinline__ bool tile_kept(const ScreenArgs& A, int I, int J) {
-    return A.delta <= 0.0f || A.rowbest[I] == J || A.colbest[J] == I || tile_score(A, I, J) > A.log_delta;
-}
-
-// Kept tiles of line o (a row block when rows, else a column block), in
-// increasing order of the other index: count (idx == null) or write at ptr[o]
-// (entries at or beyond cap are not written; the caller checks the total).
-// Each thread takes a contiguous run of the line, so a workgroup prefix sum
-// keeps the order.
-__global__ __launch_bounds__(kBlock) void k_tile_list(ScreenArgs A, int rows, const int* __restrict__ ptr,
-                                                      int* __restrict__ cnt, int* __restrict__ idx) {
-    __shared__ int sh[kBlock];
-    const int o = blockIdx.x;
-    const int len = rows ? A.nby : A.nbx;
-    const int per = (len + kBlock - 1) / kBlock;
-    const int u0 = min(threadIdx.x * per, len), u1 = min(u0 + per, len);
-    auto at = [&](int u) { return rows ? tile_kept(A, o, u) : tile_kept(A, u, o); };
-    int c = 0;
-    for (int u = u0; u < u1; ++u) c += at(u) ? 1 : 0;
-    sh[threadIdx.x] = c;
-    __syncthreads();
-    // inclusive scan (Hillis-Steele) over the workgroup
-    for (int w = 1; w < kBlock; w <<= 1) {
-        const int v = threadIdx.x >= w ? sh[threadIdx.x - w] : 0;
-        __syncthreads();
-        sh[threadIdx.x] += v;
-        __syncthreads();
-    }
-    if (!idx) {
-        if (threadIdx.x == kBlock - 1) cnt[o] = sh[kBlock - 1];
+        const int l = threadIdx.x;
+        if (l < NL && L.o0 + l < L.nl) {
+            int t = 0;
+            for (int w = 0; w < kWaves; ++w) t += wt[l][w];
+            cnt[L.o0 + l] = t;
+        }
         return;
     }
-    int64_t pos = (int64_t)ptr[o] + sh[threadIdx.x] - c;
-    for (int u = u0; u < u1; ++u)
-        if (at(u)) {
-            if (pos < A.cap) idx[pos] = u;
-            ++pos;
+    int64_t base[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) base[l] = L.o0 + l < L.nl ? ptr[L.o0 + l] : 0;
+    const unsigned long long below_me = (1ull << lane) - 1ull;
+    for (int ub = 0; ub < L.no; ub += kBlock) {
+        const int u = ub + threadIdx.x;
+        const bool in = u < L.no;
+        const int uc = in ? u : L.no - 1;
+        const Rec<D> q = load_rec<D>(L.other, uc);
+        const int obu = L.obest[uc];
+        unsigned mine = 0;
+        int pre[NL];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const bool k = in && L.o0 + l < L.nl && L.kept(A, l, u, q, obu);
+            const unsigned long long bal = __ballot(k);
+            pre[l] = __popcll(bal & below_me);
+            mine |= (k ? 1u : 0u) << l;
+            if (lane == 0) wt[l][wv] = __popcll(bal);
         }
+        __syncthreads();
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            int lower = 0, tot = 0;
+            for (int w = 0; w < kWaves; ++w) {
+                const int c = wt[l][w];
+                lower += w < wv ? c : 0;
+                tot += c;
+            }
+            if ((mine >> l) & 1u) {
+                const int64_t pos = base[l] + lower + pre[l];
+                if (pos < A.cap) idx[pos] = u;
+            }
+            base[l] += tot;
+        }
+        __syncthreads();
+    }
 }
 
 // Exclusive prefix sum of cnt[0..len) into ptr[0..len] in one workgroup (fixed
@@ -379,16 +512,40 @@ hipError_t launch_block_max(const float* pot, const float* w, int n, int B, floa
     return hipGetLastError();
 }
 
-hipError_t launch_screen(const ScreenArgs& a, int* rcnt, int* rptr, int* ridx, int* ccnt, int* cptr, int* cidx,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(k_screen_best, dim3(a.nbx), dim3(kBlock), 0, s, a, 1);
-    hipLaunchKernelGGL(k_screen_best, dim3(a.nby), dim3(kBlock), 0, s, a, 0);
-    hipLaunchKernelGGL(k_tile_list, dim3(a.nbx), dim3(kBlock), 0, s, a, 1, nullptr, rcnt, nullptr);
-    hipLaunchKernelGGL(k_tile_list, dim3(a.nby), dim3(kBlock), 0, s, a, 0, nullptr, ccnt, nullptr);
+template <int D>
+void screen_d(const ScreenArgs& a, int* rcnt, int* rptr, int* ridx, int* ccnt, int* cptr, int* cidx, hipStream_t s) {
+    constexpr int NL = lines_of(D);
+    const dim3 gx((a.nbx + NL - 1) / NL), gy((a.nby + NL - 1) / NL);
+    hipLaunchKernelGGL((k_screen_best<D, true>), gx, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_screen_best<D, false>), gy, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_tile_list<D, true>), gx, dim3(kBlock), 0, s, a, nullptr, rcnt, nullptr);
+    hipLaunchKernelGGL((k_tile_list<D, false>), gy, dim3(kBlock), 0, s, a, nullptr, ccnt, nullptr);
     hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(kBlock), 0, s, rcnt, a.nbx, a.cap, rptr);
     hipLaunchKernelGGL(k_exclusive_scan, dim3(1), dim3(kBlock), 0, s, ccnt, a.nby, a.cap, cptr);
-    hipLaunchKernelGGL(k_tile_list, dim3(a.nbx), dim3(kBlock), 0, s, a, 1, rptr, rcnt, ridx);
-    hipLaunchKernelGGL(k_tile_list, dim3(a.nby), dim3(kBlock), 0, s, a, 0, cptr, ccnt, cidx);
+    hipLaunchKernelGGL((k_tile_list<D, true>), gx, dim3(kBlock), 0, s, a, rptr, rcnt, ridx);
+    hipLaunchKernelGGL((k_tile_list<D, false>), gy, dim3(kBlock), 0, s, a, cptr, ccnt, cidx);
+}
+
+hipError_t launch_screen(const ScreenArgs& a_in, int* rcnt, int* rptr, int* ridx, int* ccnt, int* cptr, int* cidx,
+                         hipStream_t s) {
+    ScreenArgs a = a_in;
+    a.inv_eps = 1.0f / a.eps;
+    const int S = screen_stride_of(a.d);
+    hipLaunchKernelGGL(k_screen_rec, dim3(grid_of(a.nbx)), dim3(kBlock), 0, s, a.fmax, a.amass, a.xlo, a.xhi, a.nbx,
+                       a.d, S, a.dx);
+    hipLaunchKernelGGL(k_screen_rec, dim3(grid_of(a.nby)), dim3(kBlock), 0, s, a.gmax, a.bmass, a.ylo, a.yhi, a.nby,
+                       a.d, S, a.dy);
+    switch (a.d) {
+        case 1: screen_d<1>(a, rcnt, rptr, ridx, ccnt, cptr, cidx, s); break;
+        case 2: screen_d<2>(a, rcnt, rptr, ridx, ccnt, cptr, cidx, s); break;
+        case 3: screen_d<3>(a, rcnt, rptr, ridx, ccnt, cptr, cidx, s); break;
+        case 4: screen_d<4>(a, rcnt, rptr, ridx, ccnt, cptr, cidx, s); break;
+        case 5: screen_d<5>(a, rcnt, rptr, ridx, ccnt, cptr, cidx, s); break;
+        case 6: screen_d<6>(a, rcnt, rptr, ridx, ccnt, cptr, cidx, s); break;
+        case 7: screen_d<7>(a, rcnt, rptr, ridx, ccnt, cptr, cidx, s); break;
+        case 8: screen_d<8>(a, rcnt, rptr, ridx, ccnt, cptr, cidx, s); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

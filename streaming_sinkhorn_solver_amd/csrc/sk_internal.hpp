@@ -149,12 +149,18 @@ struct ScreenArgs {
     const float *fmax, *gmax;    // per-block maxima of the potentials (points of positive weight)
     const float *amass, *bmass;  // block masses
     const float *xlo, *xhi, *ylo, *yhi;  // block boxes [blocks][d]
+    float *dx, *dy;              // per-block records [blocks][screen_stride_of(d)] (written by the screening)
     int nbx, nby, d;
     float eps, delta, log_delta;
+    float inv_eps;               // 1 / eps (set by the screening)
     int* rowbest;                // [nbx] the tile of largest bound in each row block
     int* colbest;                // [nby] ... in each column block
     int64_t cap;                 // capacity of each tile list (entries)
 };
+
+// Floats per block record of the screening: box lo[d], hi[d], potential
+// maximum, log mass term, padded to whole float4s.
+constexpr int screen_stride_of(int d) { return (2 * d + 2 + 3) / 4 * 4; }
 
 // Arguments of a streamed transport product (d <= 8; see sk_transport.hip).
 struct TransArgs {

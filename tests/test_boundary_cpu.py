@@ -239,8 +239,8 @@ def test_fs2_argument_errors(lib):
     assert fs(tol=-1.0) == SK_ERR_STOP and fs(delta=float("nan")) == SK_ERR_STOP and fs(gain=float("inf")) == SK_ERR_STOP
     assert fs(ci=0) == SK_ERR_ITERS and fs(mr=0) == SK_ERR_ITERS and fs(ns=0) == SK_ERR_ITERS
     assert fs(mi=-1) == SK_ERR_ITERS and fs(ce=0) == SK_ERR_ITERS and fs(se=0) == SK_ERR_ITERS
-    # block-pair limits: at most 2^34 pairs scored; with delta = 0 (every pair kept) at most 2^28
-    assert fs(n=(1 << 21) + 16, m=1 << 21, B=16) == SK_ERR_SHAPE  # (2^17 + 1) 2^17 pairs
+    # block-pair limits: at most 2^36 pairs scored; with delta = 0 (every pair kept) at most 2^28
+    assert fs(n=(1 << 22) + 16, m=1 << 22, B=16) == SK_ERR_SHAPE  # (2^18 + 1) 2^18 pairs
     assert fs(n=(1 << 18) + 16, m=1 << 18, B=16, delta=0.0) == SK_ERR_SHAPE  # (2^14 + 1) 2^14 pairs, all kept
 
 
