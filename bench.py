@@ -100,6 +100,7 @@ def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float, payload: 
 
 
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def roofline_mfma(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int = 0) -> dict:
@@ -110,6 +111,27 @@ def roofline_mfma(d: int, pairs_per_launch: float, avg_launch_s: float, payload:
     achieved = pairs_per_launch * ops / avg_launch_s / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4), "traffic": None, "ops_per_pair": ops,
+            "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
+
+
+def packed_stride(d: int) -> int:
+    """The library's padded dimension of the matrix-core layout (d > 8)."""
+    return max(16, 1 << (d - 1).bit_length())
+
+
+def roofline_split(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
+    """Matrix-core roofline of the solver pass from P = 32 up, where the cross term runs as six bf16
+    products of a three-part split of each coordinate: 12 d bf16 flops per pair evaluation against the
+    bf16 MFMA peak. The fp32-equivalent rate (2 d flops per pair, the fp32 contraction it replaces) is
+    reported beside it."""
+    ops = 12 * d
+    achieved = pairs_per_launch * ops / avg_launch_s / 1e12
+    fp32_eq = pairs_per_launch * 2 * d / avg_launch_s / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "ops_per_pair": ops,
+            "mfma_dtype": "bf16 (three-part split of fp32, six products)",
+            "fp32_equivalent": {"achieved": round(fp32_eq, 3), "ops_per_pair": 2 * d,
+                                "vs_fp32_mfma_peak": round(fp32_eq / MFMA_FP32_PEAK_TFLOPS, 4)},
             "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
 
 
@@ -157,7 +179,8 @@ def run_ceilings():
     out = torch.empty(blocks * 256, device="cuda:0")
     stream = torch.cuda.current_stream()
     res = {}
-    for kind, name in ((0, "fma"), (1, "exp2"), (2, "pair_mix_d3"), (3, "mfma_f32_16x16x4"), (4, "mfma_f32_32x32x2")):
+    for kind, name in ((0, "fma"), (1, "exp2"), (2, "pair_mix_d3"), (3, "mfma_f32_16x16x4"), (4, "mfma_f32_32x32x2"),
+                       (5, "mfma_f32_16x16x32_bf16"), (6, "mfma_bf16_with_8_fma")):
         for _ in range(2):
             lib.sku_launch(kind, blocks, 50, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -170,9 +193,18 @@ def run_ceilings():
         if kind <= 2:
             rate = blocks * 256 * iters * 64 / secs
             res[name] = {"ops_per_s": rate, "frac_of_lane_rate": rate / LANE_OPS_PER_S}
-        else:
+        elif kind <= 4:
             flops = blocks * 4 * iters * 64 * (2048 if kind == 3 else 4096)
             res[name] = {"tflops": flops / secs / 1e12, "frac_of_peak": flops / secs / 1e12 / MFMA_FP32_PEAK_TFLOPS}
+        else:
+            flops = blocks * 4 * iters * 64 * 16384
+            res[name] = {"tflops": flops / secs / 1e12, "frac_of_peak": flops / secs / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                         "ms": secs * 1e3}
+    # SIMD cycles per bf16 matrix instruction, alone and with 8 wave-wide FMAs (32 cycles at 16 lanes per cycle)
+    insts_per_simd = blocks * 4 / (CUS * SIMDS) * iters * 64
+    for key, name in (("bf16_mfma_cycles", "mfma_f32_16x16x32_bf16"), ("bf16_mfma_plus_8fma_cycles",
+                                                                      "mfma_bf16_with_8_fma")):
+        res[key] = res[name]["ms"] * 1e-3 * CLOCK_HZ / insts_per_simd
     res["exp2_issue_cost"] = res["fma"]["ops_per_s"] / res["exp2"]["ops_per_s"]
     res["lane_ops_per_s_nominal"] = LANE_OPS_PER_S
     print(json.dumps(res))
@@ -415,7 +447,7 @@ def main():
             roof["kernel"] = "k_transport<%d,%d,0>" % (d, 1 if payload == 1 else (4 if payload <= 4 else 9))
         else:
             roof = roofline_mfma(d, pairs_per_launch, avg_launch_s, payload)
-            p2 = max(16, 1 << (d - 1).bit_length())
+            p2 = packed_stride(d)
             # one column: MODE 3 (vector-ALU payload); d columns: 16- or 64-column tiles (MODE 0)
             roof["kernel"] = ("k_transport_mfma<%d,1,3>" % p2 if payload == 1 else
                               "k_transport_mfma<%d,%d,0>" % (p2, 1 if d <= 16 else 4))
@@ -423,9 +455,12 @@ def main():
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
         small = pairs_per_launch <= 2.0e6  # the library's single-kernel path for small passes
         roof["kernel"] = f"k_pass_small<{d}>" if small else f"k_pass_valu<{d}>"
+    elif packed_stride(d) >= 32:
+        roof = roofline_split(d, pairs_per_launch, avg_launch_s)
+        roof["kernel"] = "k_pass_mfma<%d, true>" % packed_stride(d)
     else:
         roof = roofline_mfma(d, pairs_per_launch, avg_launch_s)
-        roof["kernel"] = "k_pass_mfma<%d>" % max(16, 1 << (d - 1).bit_length())
+        roof["kernel"] = "k_pass_mfma<%d, false>" % packed_stride(d)
     if roof is not None and mode != "fs2":
         roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma")
     elif roof is not None:

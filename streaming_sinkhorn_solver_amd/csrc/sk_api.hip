@@ -132,6 +132,7 @@ struct Ws {
     Layout L;
     char* base;
     float* f(size_t off) const { return reinterpret_cast<float*>(base + off); }
+    uint16_t* h(size_t off) const { return reinterpret_cast<uint16_t*>(base + off); }
     double* dbl(size_t off) const { return reinterpret_cast<double*>(base + off); }
 };
 
@@ -159,6 +160,10 @@ int prepare(const Ws& W, const float* x, const float* y, const float* a, const f
                        1.0f / eps, x_bias, f, u_x, s));
     SK_TRY(launch_pack(y, (int)L.m, L.d, L.P, L.mfma, centre, b, W.f(L.yp), W.f(L.ny), W.f(L.l2b), W.f(L.hy),
                        1.0f / eps, y_bias, g, u_y, s));
+    if (L.split) {  // keys of the bf16 matrix-core pass
+        SK_TRY(launch_split3(W.f(L.xp), L.n, L.P, W.h(L.xb), s));
+        SK_TRY(launch_split3(W.f(L.yp), L.m, L.P, W.h(L.yb), s));
+    }
     return SK_OK;
 }
 
@@ -174,6 +179,7 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
     p.q = W.f(row_side ? L.xp : L.yp);
     p.k = W.f(row_side ? L.yp : L.xp);
     p.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
+    p.kb = L.split ? W.h(row_side ? L.yb : L.xb) : nullptr;
     p.nq = (int)nq;
     p.nk = (int)nk;
     p.P = L.P;
@@ -206,6 +212,7 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
 void retarget(PassArgs& p, const float* q, int64_t nq, const float* k, int64_t nk, int capacity) {
     p.q = q;
     p.k = k;
+    p.kb = nullptr;  // no split copy of other keys
     p.nq = (int)nq;
     p.nk = (int)nk;
     p.total = (nq + p.rpb - 1) / p.rpb * nk;
@@ -330,6 +337,9 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.lse_c2 = take(um * 4);
     L.snap_f = take(un * 4);
     L.snap_g = take(um * 4);
+    L.split = L.mfma && L.P >= 32;
+    L.xb = take(L.split ? un * 3 * P * 2 : 0);
+    L.yb = take(L.split ? um * 3 * P * 2 : 0);
     L.total = off;
     return L;
 }

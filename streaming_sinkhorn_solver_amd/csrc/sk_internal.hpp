@@ -102,6 +102,7 @@ struct PassArgs {
     const float* q;      // query cloud, packed [nq][P]
     const float* k;      // key cloud, packed [nk][P]
     const float* kbias;  // separate key bias [nk] (matrix-core layout), else null
+    const uint16_t* kb;  // matrix-core layout, P >= 32: bf16 parts of the keys [nk][3][P] (h, m, l), else null
     int nq, nk, P;
     float qscale;        // 2 log2e / eps
     int rpb;             // rows per block
@@ -187,6 +188,8 @@ struct Layout {
     bool mfma;
     int64_t n, m;
     size_t xp, yp, hx, hy, nx, ny, l2a, l2b, lse_r, lse_c, rbuf, part, partA, red, cen, centre, chk;
+    size_t xb, yb;            // bf16 parts of the packed clouds (matrix-core layout, P >= 32)
+    bool split;               // xb, yb are in use
     size_t lse_r2, lse_c2;    // second state buffers (a check keeps the previous state)
     size_t snap_f, snap_g;    // potentials at the previous check (potential stop rule)
     size_t total;
@@ -304,6 +307,8 @@ hipError_t launch_merge(const PassArgs& a, hipStream_t s);
 hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 int mfma_rows_per_block(int P);
 int mfma_pass_capacity(int P);
+// bf16 parts (h, m, l) of rows x P packed floats into out [rows][3][P].
+hipError_t launch_split3(const float* in, int64_t rows, int P, uint16_t* out, hipStream_t s);
 // Matrix-core gradient pass (needs the row lse of the same scores); rows per workgroup.
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
 int mfma_grad_rows_per_block();

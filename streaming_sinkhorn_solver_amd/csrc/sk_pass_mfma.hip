@@ -23,10 +23,14 @@
 //  * NQB independent 16-query blocks per wave interleave their MFMA chains.
 // Work is split across workgroups with the same stream-K ranges as the vector
 // passes; a row block here is 4 waves x NQB x 16 queries.
+//
+// From P = 32 up the solver pass takes the cross term on bf16 matrix cores
+// instead, exactly enough for fp32 (see split3 and k_pass_mfma<P, true>).
 #include "sk_internal.hpp"
 #include "sk_pass_common.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sk {
 namespace {
@@ -102,6 +106,112 @@ struct TileStage {
     }
 };
 
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+#ifndef SK_MFMA3_TILE
+#define SK_MFMA3_TILE 4096
+#endif
+
+// ---- three-part bf16 split of fp32 values
+//
+// v = h + m + l with h = bf16(v), m = bf16(v - h), l = bf16(v - h - m), each
+// rounded to nearest even. The two remainders are exact in fp32 (each part is
+// within a factor 2 of what it rounds), and |v - h - m - l| <= 2^-27 |v|. Then
+//   q.k ~ hq hk + hq mk + mq hk + hq lk + lq hk + mq mk:
+// every product of two bf16 values is exact in fp32, the matrix cores add in
+// fp32, and the dropped products (m l, l m, l l) are below 2^-26 of
+// |q_t k_t|, under the unit roundoff 2^-24 of an fp32 dot product. On gfx950
+// one v_mfma_f32_16x16x32_bf16 (16 keys x 16 queries x 32 coordinates) costs
+// half the issue time of one v_mfma_f32_16x16x4f32 (the bf16 rate is 16x the
+// fp32 rate), so the six products of 32 coordinates take 3/8 of the
+// matrix-core time of the eight fp32 steps they replace.
+__device__ __forceinline__ unsigned bf16_rne(float x) {  // finite x
+    unsigned u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float bf16_value(unsigned h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ void split3(float v, unsigned& h, unsigned& m, unsigned& l) {
+    h = bf16_rne(v);
+    const float r = v - bf16_value(h);
+    m = bf16_rne(r);
+    l = bf16_rne(r - bf16_value(m));
+}
+
+// The parts of packed rows: out[i][part][t] (parts h, m, l) from in[i][t].
+__global__ __launch_bounds__(kBlock) void k_split3(const float* __restrict__ in, int64_t count, int P,
+                                                   uint16_t* __restrict__ out) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= count) return;
+    const int64_t i = e / P;
+    const int t = (int)(e - i * P);
+    unsigned h, m, l;
+    split3(in[e], h, m, l);
+    uint16_t* o = out + i * 3 * P + t;
+    o[0] = (uint16_t)h;
+    o[P] = (uint16_t)m;
+    o[2 * P] = (uint16_t)l;
+}
+
+// keys per LDS tile of the split pass (SK_MFMA3_TILE coordinates: 3 x 2 bytes each)
+template <int P>
+constexpr int mfma3_tile_keys() {
+    return SK_MFMA3_TILE / P < 16 ? 16 : SK_MFMA3_TILE / P;
+}
+
+// Register staging of one LDS tile of split keys: a key row is RU 16-byte
+// units (h, m, l parts of P coordinates), stored RU + 1 apart in LDS, an odd
+// number of units, so 16 lanes reading 16 rows at one offset do not conflict.
+template <int P>
+struct TileStage3 {
+    static constexpr int TL = mfma3_tile_keys<P>();
+    static constexpr int RU = 3 * P / 8;
+    static constexpr int RS = RU + 1;
+    static constexpr int U = TL * RU / kBlock;
+    static constexpr int NB = (TL + kBlock - 1) / kBlock;
+    static_assert(TL * RU % kBlock == 0, "tile must split evenly over the workgroup");
+    u4v v[U];
+    float b[NB];
+
+    __device__ __forceinline__ void load(const u4v* __restrict__ kb, const float* __restrict__ kbias, int base,
+                                         int j1) {
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const int e = threadIdx.x + r * kBlock;
+            const int key = e / RU, part = e - key * RU;
+            const int col = base + key;
+            const u4v x = kb[(size_t)min(col, j1 - 1) * RU + part];
+            v[r] = col < j1 ? x : u4v{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            const int col = base + threadIdx.x + r * kBlock;
+            const float x = kbias[min(col, j1 - 1)];
+            b[r] = col < j1 ? x : -INFINITY;
+        }
+    }
+
+    __device__ __forceinline__ void store(u4v* ktile, float* btile) const {
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const int e = threadIdx.x + r * kBlock;
+            const int key = e / RU, part = e - key * RU;
+            ktile[key * RS + part] = v[r];
+        }
+#pragma unroll
+        for (int r = 0; r < NB; ++r) {
+            const int k = threadIdx.x + r * kBlock;
+            if (k < TL) btile[k] = b[r];
+        }
+    }
+};
+
+__device__ __forceinline__ f4 mfma_bf16(const u4v a, const u4v b, const f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0,
+                                                   0);
+}
+
 // A lane's KT key coordinates of one 16-key block, from the padded LDS tile.
 template <int KT>
 __device__ __forceinline__ void load_keys(float (&kf)[KT], const float* ktile, int off) {
@@ -135,18 +245,28 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2
     M = mn;
 }
 
-template <int P>
+// SPLIT: the cross term on bf16 matrix cores from the three-part split (keys
+// split in memory by k_split3, queries split in registers when a segment
+// starts), P >= 32; else on fp32 matrix cores.  Lane group g owns the same
+// coordinates [g P/4, (g+1) P/4) in both forms; in the split form, chunk kc of
+// a lane group is its 8 coordinates g P/4 + 8 kc .. + 7, one bf16 operand.
+template <int P, bool SPLIT>
 __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
-    constexpr int KT = P / 4;           // MFMA k-steps per 16-key block
+    constexpr int KT = P / 4;           // MFMA k-steps per 16-key block (fp32)
+    constexpr int KC = P / 32;          // 8-coordinate chunks per lane group (split)
     constexpr int PS = P + 4;           // padded LDS row stride (floats): conflict-free float4 reads
     constexpr int NQB = mfma_nqb<P>();  // 16-query blocks per wave
-    constexpr int TL = mfma_tile_keys<P>();
-    __shared__ __align__(16) float ktile[TL * PS];
+    static_assert(!SPLIT || P >= 32, "the split form needs 8 coordinates per lane group");
+    using Stage = std::conditional_t<SPLIT, TileStage3<P>, TileStage<P>>;
+    constexpr int TL = Stage::TL;
+    constexpr int LDS_WORDS = SPLIT ? TL * TileStage3<P>::RS * 4 : TL * PS;
+    __shared__ __align__(16) float ktile[LDS_WORDS];
     __shared__ __align__(16) float btile[TL];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     const float4* kp = reinterpret_cast<const float4*>(A.k);
+    const u4v* kb = reinterpret_cast<const u4v*>(A.kb);
 
     const int w = blockIdx.x;
     const int64_t lo = range_lo(w, A.total, A.W), hi = range_lo(w + 1, A.total, A.W);
@@ -156,7 +276,10 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
         const int j1 = (int)min<int64_t>((int64_t)A.nk, (int64_t)j0 + (hi - u));
         const int qrow0 = rb * A.rpb + wave * (NQB * 16);
 
-        float qf[NQB][KT];
+        // queries, scaled: fp32 coordinates, or their h, m, l parts
+        float qf[SPLIT ? 1 : NQB][SPLIT ? 1 : KT];
+        u4v qh[SPLIT ? NQB : 1][SPLIT ? KC : 1], qm[SPLIT ? NQB : 1][SPLIT ? KC : 1],
+            ql[SPLIT ? NQB : 1][SPLIT ? KC : 1];
         float M[NQB], S[NQB];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
@@ -166,35 +289,94 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
 #pragma unroll
             for (int t4 = 0; t4 < KT / 4; ++t4) {
                 const float4 v = qr[t4];
-                qf[qb][4 * t4 + 0] = v.x * A.qscale;
-                qf[qb][4 * t4 + 1] = v.y * A.qscale;
-                qf[qb][4 * t4 + 2] = v.z * A.qscale;
-                qf[qb][4 * t4 + 3] = v.w * A.qscale;
+                const float x[4] = {v.x * A.qscale, v.y * A.qscale, v.z * A.qscale, v.w * A.qscale};
+                if constexpr (SPLIT) {
+                    // coordinates 4 t4 .. 4 t4 + 3 of the lane group: chunk t4 / 2, words 2 (t4 % 2), + 1
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        unsigned h0, m0, l0, h1, m1, l1;
+                        split3(x[2 * e], h0, m0, l0);
+                        split3(x[2 * e + 1], h1, m1, l1);
+                        const int kc = t4 / 2, wd = 2 * (t4 % 2) + e;
+                        qh[qb][kc][wd] = h0 | (h1 << 16);
+                        qm[qb][kc][wd] = m0 | (m1 << 16);
+                        ql[qb][kc][wd] = l0 | (l1 << 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) qf[qb][4 * t4 + e] = x[e];
+                }
             }
             M[qb] = kNegBig;
             S[qb] = 0.0f;
         }
 
-        TileStage<P> stage;
-        stage.load(kp, A.kbias, j0, j1);
+        Stage stage;
+        if constexpr (SPLIT)
+            stage.load(kb, A.kbias, j0, j1);
+        else
+            stage.load(kp, A.kbias, j0, j1);
         for (int base = j0; base < j1; base += TL) {
             __syncthreads();
-            stage.store(ktile, btile);
+            if constexpr (SPLIT)
+                stage.store(reinterpret_cast<u4v*>(ktile), btile);
+            else
+                stage.store(ktile, btile);
             __syncthreads();
-            if (base + TL < j1) stage.load(kp, A.kbias, base + TL, j1);
+            if (base + TL < j1) {
+                if constexpr (SPLIT)
+                    stage.load(kb, A.kbias, base + TL, j1);
+                else
+                    stage.load(kp, A.kbias, base + TL, j1);
+            }
             const int ntile = min(TL, j1 - base);
-            for (int kb = 0; kb < ntile; kb += 16) {
-                float kf[KT];
-                load_keys<KT>(kf, ktile, (kb + c) * PS + g * KT);
-                const f4 bias = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
+            for (int kb16 = 0; kb16 < ntile; kb16 += 16) {
+                const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
                 f4 acc[NQB];
+                if constexpr (SPLIT) {
+                    // with four query blocks the four accumulator chains keep the matrix pipe busy; with
+                    // fewer, the small products go to a second accumulator per block (from zero)
+                    constexpr bool kTwoAcc = NQB < 4;
+                    constexpr int RS = TileStage3<P>::RS;
+                    const u4v* kr = reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS + g * KC;
+                    f4 acc2[NQB];
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) acc[qb] = bias;
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        acc[qb] = bias;
+                        acc2[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
+                    f4(&small)[NQB] = kTwoAcc ? acc2 : acc;
 #pragma unroll
-                for (int t = 0; t < KT; ++t)
+                    for (int kc = 0; kc < KC; ++kc) {
+                        const u4v kh = kr[kc], km = kr[P / 8 + kc], kl = kr[2 * (P / 8) + kc];
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-                        acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
+                        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qh[qb][kc], acc[qb]);
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kh, ql[qb][kc], small[qb]);
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qm[qb][kc], acc[qb]);
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kl, qh[qb][kc], small[qb]);
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(km, qh[qb][kc], acc[qb]);
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(km, qm[qb][kc], small[qb]);
+                    }
+                    if constexpr (kTwoAcc) {
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb) acc[qb] += acc2[qb];
+                    }
+                } else {
+                    float kf[KT];
+                    load_keys<KT>(kf, ktile, (kb16 + c) * PS + g * KT);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) acc[qb] = bias;
+#pragma unroll
+                    for (int t = 0; t < KT; ++t)
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb)
+                            acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
+                }
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], acc[qb]);
             }
@@ -596,7 +778,14 @@ hipError_t launch_transport_mfma_pp(const TransArgs& a, int mode, int kwidth, hi
 template <int P>
 hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
-    hipLaunchKernelGGL(k_pass_mfma<P>, dim3(a.W), dim3(kBlock), 0, s, a);
+    if constexpr (P >= 32) {
+        if (a.kb)
+            hipLaunchKernelGGL((k_pass_mfma<P, true>), dim3(a.W), dim3(kBlock), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_pass_mfma<P, false>), dim3(a.W), dim3(kBlock), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((k_pass_mfma<P, false>), dim3(a.W), dim3(kBlock), 0, s, a);
+    }
     if (ev1) (void)hipEventRecord(ev1, s);
     return launch_merge(a, s);
 }
@@ -628,7 +817,9 @@ int capacity_p() {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pass_mfma<P>, kBlock, 0) != hipSuccess) return 0;
+    // the form the solver's passes run (split from P = 32 up)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pass_mfma<P, (P >= 32)>, kBlock, 0) != hipSuccess)
+        return 0;
     return cus * per_cu;
 }
 
@@ -701,6 +892,13 @@ hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s) {
         case 256: return launch_grad_mfma_p<256>(a, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_split3(const float* in, int64_t rows, int P, uint16_t* out, hipStream_t s) {
+    const int64_t count = rows * P;
+    hipLaunchKernelGGL(k_split3, dim3((unsigned)((count + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, in, count, P,
+                       out);
+    return hipGetLastError();
 }
 
 int mfma_pass_capacity(int P) {

@@ -116,6 +116,62 @@ __global__ __launch_bounds__(256) void k_mfma32(float* out, int iters) {
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+// bf16 matrix-core rate: kChains independent v_mfma_f32_16x16x32_bf16 chains per wave.
+__global__ __launch_bounds__(256) void k_mfma_bf16(float* out, int iters) {
+    const unsigned t = threadIdx.x;
+    const u4v ua = {0x3F803F80u + t, 0x3F003F00u, 0x3E803E80u, 0x3F803F00u};
+    const u4v ub = {0x3F803F80u, 0x3F003F80u + t, 0x3E803E80u, 0x3F003F00u};
+    const bf8 a = __builtin_bit_cast(bf8, ua), b = __builtin_bit_cast(bf8, ub);
+    f4 acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = f4{0.0f, 0.0f, 0.0f, (float)c};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][3];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The same bf16 chains with 8 independent vector FMAs after every matrix
+// instruction: whether the vector ALU runs under the matrix pipe (time near
+// the larger of the two) or not (near their sum).
+__global__ __launch_bounds__(256) void k_mfma_bf16_valu(float* out, int iters) {
+    const unsigned t = threadIdx.x;
+    const u4v ua = {0x3F803F80u + t, 0x3F003F00u, 0x3E803E80u, 0x3F803F00u};
+    const u4v ub = {0x3F803F80u, 0x3F003F80u + t, 0x3E803E80u, 0x3F003F00u};
+    const bf8 a = __builtin_bit_cast(bf8, ua), b = __builtin_bit_cast(bf8, ub);
+    f4 acc[kChains];
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = f4{0.0f, 0.0f, 0.0f, (float)c};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = t * 1e-3f + e;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = fmaf(v[e], 0.999f, 1e-3f);
+            }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][3];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += v[e];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,7 +179,9 @@ extern "C" {
 // kind 0: fp32 FMA, 1: exp2, 2: d = 3 pair mix; each thread performs
 // iters * 8 * 8 operations (FMAs, exp2s or pairs).  kind 3: each wave issues
 // iters * 64 v_mfma_f32_16x16x4f32 (2048 flops each); kind 4: each wave issues
-// iters * 64 v_mfma_f32_32x32x2f32 (4096 flops each).  Launches `blocks` x 256
+// iters * 64 v_mfma_f32_32x32x2f32 (4096 flops each); kind 5: each wave issues
+// iters * 64 v_mfma_f32_16x16x32_bf16 (16384 flops each); kind 6: as kind 5
+// with 8 vector FMAs per matrix instruction.  Launches `blocks` x 256
 // threads; out must hold blocks * 256 floats.  Returns a hipError_t.
 int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -137,6 +195,10 @@ int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
         hipLaunchKernelGGL(k_mfma16, dim3(blocks), dim3(256), 0, s, out, iters);
     else if (kind == 4)
         hipLaunchKernelGGL(k_mfma32, dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 5)
+        hipLaunchKernelGGL(k_mfma_bf16, dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 6)
+        hipLaunchKernelGGL(k_mfma_bf16_valu, dim3(blocks), dim3(256), 0, s, out, iters);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();

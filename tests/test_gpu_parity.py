@@ -102,6 +102,31 @@ def test_solve_matches_oracle(shape):
     assert abs(c_gpu - c_or) <= 1e-4 * abs(c_or) + 1e-12
 
 
+# From P = 32 up the matrix-core pass forms the cross term from a three-part bf16 split of every coordinate
+# (six products, fp32 accumulation), which is as accurate as an fp32 dot product; P = 16 keeps fp32 matrix
+# instructions and serves as the reference here. One iteration from g = 0 must then stay within a few float32
+# roundings of the exponent of the oracle's iterate: 4 kappa eps, kappa as above. (Emulated on the CPU for
+# these inputs, the float32 rounding of q.y alone moves f by 0.07-0.3 kappa eps, the six products add under
+# 0.01 kappa eps, and keeping only the three largest products moves f by 2-7 kappa eps.)
+SPLIT_SHAPES = [(1500, 1300, 16, 0.05, 81), (1500, 1300, 32, 0.05, 82), (1200, 1100, 64, 0.05, 83),
+                (700, 900, 100, 0.05, 84), (600, 700, 128, 0.05, 85), (300, 500, 256, 0.05, 86)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=[f"{s[0]}x{s[1]}d{s[2]}" for s in SPLIT_SHAPES])
+def test_one_iteration_at_float32_precision(shape):
+    n, m, d, eps, seed = shape
+    x, y, a, b = random_problem(n, m, d, seed, scale=1.0 / math.sqrt(d), shift=0.2)
+    eps = eps32(eps)
+    say("one iteration", shape)
+    f, g, _ = gpu_solve(x, y, a, b, eps, 1)
+    fo, go, _ = oracle.sinkhorn(x, y, a, b, eps, 1)
+    maxc = oracle.max_cost(x, y)
+    tol = 4 * eps * kappa(fo, go, maxc, eps)
+    say("err/tol f", np.max(np.abs(f - fo)) / tol, "g", np.max(np.abs(g - go)) / tol)
+    assert np.max(np.abs(f - fo)) <= tol
+    assert np.max(np.abs(g - go)) <= tol
+
+
 def test_gradient_flow_workload_end_to_end():
     """The 1000-point, eps = 0.01, 200-iteration problem in full, against a live oracle run."""
     w = WORKLOADS["gflow_d2"]
