@@ -446,8 +446,12 @@ def main():
             roof = roofline_alu(d, pairs_per_launch, avg_launch_s, payload)
             roof["kernel"] = "k_transport<%d,%d,0>" % (d, 1 if payload == 1 else (4 if payload <= 4 else 9))
         else:
-            roof = roofline_mfma(d, pairs_per_launch, avg_launch_s, payload)
             p2 = packed_stride(d)
+            if payload == 1 and p2 >= 32:
+                # the one-column kernel forms its scores in the split form (payload FMAs on the vector ALUs)
+                roof = roofline_split(d, pairs_per_launch, avg_launch_s)
+            else:
+                roof = roofline_mfma(d, pairs_per_launch, avg_launch_s, payload)
             # one column: MODE 3 (vector-ALU payload); d columns: 16- or 64-column tiles (MODE 0)
             roof["kernel"] = ("k_transport_mfma<%d,1,3>" % p2 if payload == 1 else
                               "k_transport_mfma<%d,%d,0>" % (p2, 1 if d <= 16 else 4))

@@ -805,6 +805,7 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     t.q = W.f(row_side ? L.xp : L.yp);
     t.k = W.f(row_side ? L.yp : L.xp);
     t.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
+    t.kb = L.split ? W.h(row_side ? L.yb : L.xb) : nullptr;
     t.qbias = L.mfma ? W.f(row_side ? L.hx : L.hy) : nullptr;
     t.lse = L.mfma ? W.f(row_side ? L.lse_r : L.lse_c) : nullptr;
     t.pay = pay;

@@ -168,6 +168,7 @@ struct TransArgs {
     const float* q;      // query cloud, packed [nq][P], bias slot = log2 w + log2e (pot - |q~|^2)/eps
     const float* k;      // key cloud, packed [nk][P], same bias from the key-side potential
     const float* kbias;  // matrix-core layout: key biases [nk], else null
+    const uint16_t* kb;  // matrix-core layout, P >= 32: bf16 parts of the keys [nk][3][P] (one-column mode)
     const float* qbias;  // matrix-core layout: query biases [nq], else null
     const float* lse;    // matrix-core layout: row log-sum-exp of the scores [nq] (a first pass)
     const float* pay;    // payload: key j's columns at pay[j * ldp + c], c < kin

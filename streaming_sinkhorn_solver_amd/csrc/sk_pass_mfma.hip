@@ -212,6 +212,69 @@ __device__ __forceinline__ f4 mfma_bf16(const u4v a, const u4v b, const f4 c) {
                                                    0);
 }
 
+// A lane's query row for the split form: its P/4 coordinates from qr, scaled,
+// as h, m, l parts, chunk kc holding coordinates 8 kc .. 8 kc + 7.
+template <int P>
+__device__ __forceinline__ void load_query_split(const float* __restrict__ qr, float qscale, u4v (&qh)[P / 32],
+                                                 u4v (&qm)[P / 32], u4v (&ql)[P / 32]) {
+    const float4* q4 = reinterpret_cast<const float4*>(qr);
+#pragma unroll
+    for (int t4 = 0; t4 < P / 16; ++t4) {
+        const float4 v = q4[t4];
+        const float x[4] = {v.x * qscale, v.y * qscale, v.z * qscale, v.w * qscale};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            unsigned h0, m0, l0, h1, m1, l1;
+            split3(x[2 * e], h0, m0, l0);
+            split3(x[2 * e + 1], h1, m1, l1);
+            const int kc = t4 / 2, wd = 2 * (t4 % 2) + e;
+            qh[kc][wd] = h0 | (h1 << 16);
+            qm[kc][wd] = m0 | (m1 << 16);
+            ql[kc][wd] = l0 | (l1 << 16);
+        }
+    }
+}
+
+// Scores of one 16-key block for NQB query blocks in the split form: kr is the
+// lane's key row in the LDS tile (parts h, m, l, P/8 units apart), offset to
+// its lane group. With four query blocks the four accumulator chains keep the
+// matrix pipe busy; with fewer, the small products go to a second accumulator
+// per block (from zero).
+template <int P, int NQB>
+__device__ __forceinline__ void split_scores(const u4v* kr, const u4v (&qh)[NQB][P / 32],
+                                             const u4v (&qm)[NQB][P / 32], const u4v (&ql)[NQB][P / 32],
+                                             const f4 bias, f4 (&acc)[NQB]) {
+    constexpr int KC = P / 32;
+    constexpr bool kTwoAcc = NQB < 4;
+    f4 acc2[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        acc[qb] = bias;
+        acc2[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    f4(&small)[NQB] = kTwoAcc ? acc2 : acc;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+        const u4v kh = kr[kc], km = kr[P / 8 + kc], kl = kr[2 * (P / 8) + kc];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qh[qb][kc], acc[qb]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kh, ql[qb][kc], small[qb]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qm[qb][kc], acc[qb]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kl, qh[qb][kc], small[qb]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(km, qh[qb][kc], acc[qb]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(km, qm[qb][kc], small[qb]);
+    }
+    if constexpr (kTwoAcc) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) acc[qb] += acc2[qb];
+    }
+}
+
 // A lane's KT key coordinates of one 16-key block, from the padded LDS tile.
 template <int KT>
 __device__ __forceinline__ void load_keys(float (&kf)[KT], const float* ktile, int off) {
@@ -285,26 +348,17 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
         for (int qb = 0; qb < NQB; ++qb) {
             const int i = qrow0 + qb * 16 + c;
             const int ic = i < A.nq ? i : A.nq - 1;
-            const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
+            if constexpr (SPLIT) {
+                load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, qh[qb], qm[qb], ql[qb]);
+            } else {
+                const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
 #pragma unroll
-            for (int t4 = 0; t4 < KT / 4; ++t4) {
-                const float4 v = qr[t4];
-                const float x[4] = {v.x * A.qscale, v.y * A.qscale, v.z * A.qscale, v.w * A.qscale};
-                if constexpr (SPLIT) {
-                    // coordinates 4 t4 .. 4 t4 + 3 of the lane group: chunk t4 / 2, words 2 (t4 % 2), + 1
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        unsigned h0, m0, l0, h1, m1, l1;
-                        split3(x[2 * e], h0, m0, l0);
-                        split3(x[2 * e + 1], h1, m1, l1);
-                        const int kc = t4 / 2, wd = 2 * (t4 % 2) + e;
-                        qh[qb][kc][wd] = h0 | (h1 << 16);
-                        qm[qb][kc][wd] = m0 | (m1 << 16);
-                        ql[qb][kc][wd] = l0 | (l1 << 16);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) qf[qb][4 * t4 + e] = x[e];
+                for (int t4 = 0; t4 < KT / 4; ++t4) {
+                    const float4 v = qr[t4];
+                    qf[qb][4 * t4 + 0] = v.x * A.qscale;
+                    qf[qb][4 * t4 + 1] = v.y * A.qscale;
+                    qf[qb][4 * t4 + 2] = v.z * A.qscale;
+                    qf[qb][4 * t4 + 3] = v.w * A.qscale;
                 }
             }
             M[qb] = kNegBig;
@@ -334,38 +388,9 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
                 const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
                 f4 acc[NQB];
                 if constexpr (SPLIT) {
-                    // with four query blocks the four accumulator chains keep the matrix pipe busy; with
-                    // fewer, the small products go to a second accumulator per block (from zero)
-                    constexpr bool kTwoAcc = NQB < 4;
                     constexpr int RS = TileStage3<P>::RS;
                     const u4v* kr = reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS + g * KC;
-                    f4 acc2[NQB];
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) {
-                        acc[qb] = bias;
-                        acc2[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-                    }
-                    f4(&small)[NQB] = kTwoAcc ? acc2 : acc;
-#pragma unroll
-                    for (int kc = 0; kc < KC; ++kc) {
-                        const u4v kh = kr[kc], km = kr[P / 8 + kc], kl = kr[2 * (P / 8) + kc];
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qh[qb][kc], acc[qb]);
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kh, ql[qb][kc], small[qb]);
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qm[qb][kc], acc[qb]);
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kl, qh[qb][kc], small[qb]);
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(km, qh[qb][kc], acc[qb]);
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(km, qm[qb][kc], small[qb]);
-                    }
-                    if constexpr (kTwoAcc) {
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb) acc[qb] += acc2[qb];
-                    }
+                    split_scores<P, NQB>(kr, qh, qm, ql, bias, acc);
                 } else {
                     float kf[KT];
                     load_keys<KT>(kf, ktile, (kb16 + c) * PS + g * KT);
@@ -569,39 +594,50 @@ constexpr int transport_nqb(int P, int NP, int MODE) {
 
 template <int P, int NP, int MODE>
 __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
+    // one payload column (MODE 3, the conjugate-gradient product) takes the split form from P = 32
+    constexpr bool SPLIT = MODE == 3 && P >= 32;
     constexpr int KT = P / 4;
+    constexpr int KC = P / 32;
     constexpr int PS = P + 4;
     constexpr int NB = (MODE == 1 || MODE == 2) ? P / 16 : NP;  // 16-column output blocks (unused in MODE 3)
     constexpr int KP = MODE == 0 ? 16 * NP : 1;  // payload floats per key in LDS
-    constexpr int TL = mfma_tile_keys<P>();
+    using Stage = std::conditional_t<SPLIT, TileStage3<P>, TileStage<P>>;
+    constexpr int TL = Stage::TL;
     constexpr int NQB = transport_nqb(P, NP, MODE);
-    __shared__ __align__(16) float ktile[TL * PS];
+    constexpr int LDS_WORDS = SPLIT ? TL * TileStage3<P>::RS * 4 : TL * PS;
+    __shared__ __align__(16) float ktile[LDS_WORDS];
     __shared__ __align__(16) float btile[TL];
     __shared__ __align__(16) float ptile[MODE == 1 ? 1 : TL * KP];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     const float4* kp = reinterpret_cast<const float4*>(A.k);
+    const u4v* kb = reinterpret_cast<const u4v*>(A.kb);
     const int split = blockIdx.y;
     const int c0 = split * A.cols_per_split;
     const int c1 = min(c0 + A.cols_per_split, A.nk);
     const int qrow0 = blockIdx.x * (kWaves * 16 * NQB) + wave * (16 * NQB);
 
-    float qf[NQB][KT], vf[MODE == 2 ? NQB : 1][KT];
+    float qf[SPLIT ? 1 : NQB][SPLIT ? 1 : KT], vf[MODE == 2 ? NQB : 1][KT];
+    u4v qh[SPLIT ? NQB : 1][SPLIT ? KC : 1], qm[SPLIT ? NQB : 1][SPLIT ? KC : 1], ql[SPLIT ? NQB : 1][SPLIT ? KC : 1];
     float lse_c[NQB], S[NQB], Tv[NQB];
     f4 T[NQB][NB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
         const int i = qrow0 + qb * 16 + c;
         const int ic = i < A.nq ? i : A.nq - 1;
-        const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
+        if constexpr (SPLIT) {
+            load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, qh[qb], qm[qb], ql[qb]);
+        } else {
+            const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
 #pragma unroll
-        for (int t4 = 0; t4 < KT / 4; ++t4) {
-            const float4 v = qr[t4];
-            qf[qb][4 * t4 + 0] = v.x * A.qscale;
-            qf[qb][4 * t4 + 1] = v.y * A.qscale;
-            qf[qb][4 * t4 + 2] = v.z * A.qscale;
-            qf[qb][4 * t4 + 3] = v.w * A.qscale;
+            for (int t4 = 0; t4 < KT / 4; ++t4) {
+                const float4 v = qr[t4];
+                qf[qb][4 * t4 + 0] = v.x * A.qscale;
+                qf[qb][4 * t4 + 1] = v.y * A.qscale;
+                qf[qb][4 * t4 + 2] = v.z * A.qscale;
+                qf[qb][4 * t4 + 3] = v.w * A.qscale;
+            }
         }
         if (MODE == 2) {
 #pragma unroll
@@ -617,11 +653,19 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
         for (int nb = 0; nb < NB; ++nb) T[qb][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    TileStage<P> stage;
-    if (c0 < c1) stage.load(kp, A.kbias, c0, c1);
+    Stage stage;
+    if (c0 < c1) {
+        if constexpr (SPLIT)
+            stage.load(kb, A.kbias, c0, c1);
+        else
+            stage.load(kp, A.kbias, c0, c1);
+    }
     for (int base = c0; base < c1; base += TL) {
         __syncthreads();
-        stage.store(ktile, btile);
+        if constexpr (SPLIT)
+            stage.store(reinterpret_cast<u4v*>(ktile), btile);
+        else
+            stage.store(ktile, btile);
         if (MODE != 1)
             for (int e = threadIdx.x; e < TL * KP; e += kBlock) {
                 const int col = base + e / KP;
@@ -629,29 +673,41 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
                 ptile[e] = (col < c1 && cc < A.kin) ? A.pay[(size_t)col * A.ldp + cc] : 0.0f;
             }
         __syncthreads();
-        if (base + TL < c1) stage.load(kp, A.kbias, base + TL, c1);
+        if (base + TL < c1) {
+            if constexpr (SPLIT)
+                stage.load(kb, A.kbias, base + TL, c1);
+            else
+                stage.load(kp, A.kbias, base + TL, c1);
+        }
         const int ntile = min(TL, c1 - base);
-        for (int kb = 0; kb < ntile; kb += 16) {
-            float kf[KT];
-            load_keys<KT>(kf, ktile, (kb + c) * PS + g * KT);
-            const f4 bias = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
+        for (int kb16 = 0; kb16 < ntile; kb16 += 16) {
+            const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
             f4 acc[NQB], dv[NQB];
+            if constexpr (SPLIT) {
+                constexpr int RS = TileStage3<P>::RS;
+                const u4v* kr = reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS + g * KC;
+                split_scores<P, NQB>(kr, qh, qm, ql, bias, acc);
+            } else {
+                float kf[KT];
+                load_keys<KT>(kf, ktile, (kb16 + c) * PS + g * KT);
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                acc[qb] = bias;
-                dv[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
-#pragma unroll
-            for (int t = 0; t < KT; ++t)
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb)
-                    acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
-            if (MODE == 2) {
+                for (int qb = 0; qb < NQB; ++qb) {
+                    acc[qb] = bias;
+                    dv[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
 #pragma unroll
                 for (int t = 0; t < KT; ++t)
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb)
-                        dv[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], vf[MODE == 2 ? qb : 0][t], dv[qb], 0, 0, 0);
+                        acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
+                if (MODE == 2) {
+#pragma unroll
+                    for (int t = 0; t < KT; ++t)
+#pragma unroll
+                        for (int qb = 0; qb < NQB; ++qb)
+                            dv[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], vf[MODE == 2 ? qb : 0][t], dv[qb], 0,
+                                                                          0, 0);
+                }
             }
             float wv[NQB][4];
 #pragma unroll
@@ -660,11 +716,11 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
                 for (int v = 0; v < 4; ++v) {
                     const float w = ex2(acc[qb][v] - lse_c[qb]);
                     S[qb] += w;
-                    wv[qb][v] = MODE == 2 ? w * (ptile[kb + 4 * g + v] + dv[qb][v]) : w;
+                    wv[qb][v] = MODE == 2 ? w * (ptile[kb16 + 4 * g + v] + dv[qb][v]) : w;
                 }
             if (MODE == 3) {
                 // one payload column: four FMAs per lane beat a 16-column MFMA tile
-                const f4 pv = *reinterpret_cast<const f4*>(&ptile[kb + 4 * g]);
+                const f4 pv = *reinterpret_cast<const f4*>(&ptile[kb16 + 4 * g]);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
@@ -674,8 +730,8 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const float b = MODE == 0 ? ptile[(kb + 4 * g + v) * KP + nb * 16 + c]
-                                                  : ktile[(kb + 4 * g + v) * PS + nb * 16 + c];
+                        const float b = MODE == 0 ? ptile[(kb16 + 4 * g + v) * KP + nb * 16 + c]
+                                                  : ktile[(kb16 + 4 * g + v) * PS + nb * 16 + c];
 #pragma unroll
                         for (int qb = 0; qb < NQB; ++qb)
                             T[qb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[qb][v], b, T[qb][nb], 0, 0, 0);
