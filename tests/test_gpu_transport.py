@@ -69,9 +69,12 @@ TRANSPORT_CASES = [
     (300, 500, 130, 0.5, 4, 5, False, 11, 0.0),
     (17, 5, 64, 0.2, 3, 3, True, 12, 0.0),
     (2600, 3100, 33, 0.3, 4, 16, False, 13, 0.0),
-    # one payload column on the vector ALUs inside the matrix-core kernel, split key range
+    # one payload column on the vector ALUs inside the matrix-core kernel, split key range; from P = 32 its
+    # scores take the bf16 split form (P = 32, 64, 128, 256 below)
     (1500, 2100, 64, 0.5, 5, 1, True, 14, 0.05),
     (2100, 1500, 130, 0.5, 4, 1, False, 15, 0.0),
+    (1300, 1700, 20, 0.3, 5, 1, False, 16, 0.0),
+    (1100, 900, 100, 0.5, 4, 1, True, 17, 0.0),
 ]
 
 
@@ -115,6 +118,8 @@ HVP_CASES = [
     (500, 700, 64, 1.0, 200, 60, 18),
     (200, 300, 130, 1.0, 100, 60, 19),
     (1, 9, 64, 0.5, 50, 20, 20),
+    (400, 500, 24, 0.5, 200, 60, 21),
+    (300, 350, 100, 1.0, 100, 60, 22),
 ]
 
 
