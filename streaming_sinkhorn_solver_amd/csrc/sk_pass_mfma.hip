@@ -302,6 +302,19 @@ __device__ __forceinline__ void lse_block(float& M, float& S, const f4 acc) {
     M = mn;
 }
 
+// The same over the eight scores of two 16-key blocks (one rescale for both).
+__device__ __forceinline__ void lse_block2(float& M, float& S, const f4 a, const f4 b) {
+    const float mt = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+    const float mn = fmaxf(M, mt);
+    float s = S * ex2(M - mn);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s += ex2(a[v] - mn);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s += ex2(b[v] - mn);
+    S = s;
+    M = mn;
+}
+
 __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
     const float mn = fmaxf(M, m2);
     S = S * ex2(M - mn) + s2 * ex2(m2 - mn);
@@ -384,6 +397,23 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
                     stage.load(kp, A.kbias, base + TL, j1);
             }
             const int ntile = min(TL, j1 - base);
+            if constexpr (SPLIT && TL >= 32) {
+                // two 16-key blocks per step, one rescale for both (3.5% faster at d = 64 than one block per
+                // step); rows past the segment's keys hold bias -inf and add nothing
+                constexpr int RS = TileStage3<P>::RS;
+                for (int kb32 = 0; kb32 < ntile; kb32 += 32) {
+                    const f4 bias0 = *reinterpret_cast<const f4*>(&btile[kb32 + 4 * g]);
+                    const f4 bias1 = *reinterpret_cast<const f4*>(&btile[kb32 + 16 + 4 * g]);
+                    f4 acc0[NQB], acc1[NQB];
+                    split_scores<P, NQB>(reinterpret_cast<const u4v*>(ktile) + (kb32 + c) * RS + g * KC, qh, qm, ql,
+                                         bias0, acc0);
+                    split_scores<P, NQB>(reinterpret_cast<const u4v*>(ktile) + (kb32 + 16 + c) * RS + g * KC, qh, qm,
+                                         ql, bias1, acc1);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) lse_block2(M[qb], S[qb], acc0[qb], acc1[qb]);
+                }
+                continue;
+            }
             for (int kb16 = 0; kb16 < ntile; kb16 += 16) {
                 const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
                 f4 acc[NQB];
