@@ -618,7 +618,8 @@ hipError_t launch_grad_mfma_p(const GradArgs& a, hipStream_t s) {
 // (MODE 2, 2 NQB P / 4 query VGPRs) 797 / 785 / 902 us, the single-column
 // product 402 / 355 / 358 us.
 constexpr int transport_nqb(int P, int NP, int MODE) {
-    const int base = (MODE == 0 && NP > 1) ? 4 : 2;
+    // the one-column kernel in the split form: 4 blocks, 151 against 171 us with 2 (16384^2, d = 64)
+    const int base = ((MODE == 0 && NP > 1) || (MODE == 3 && P >= 32)) ? 4 : 2;
     return P <= 64 ? base : (P == 128 ? base / 2 : 1);
 }
 
