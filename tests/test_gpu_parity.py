@@ -109,7 +109,9 @@ def test_solve_matches_oracle(shape):
 # these inputs, the float32 rounding of q.y alone moves f by 0.07-0.3 kappa eps, the six products add under
 # 0.01 kappa eps, and keeping only the three largest products moves f by 2-7 kappa eps.)
 SPLIT_SHAPES = [(1500, 1300, 16, 0.05, 81), (1500, 1300, 32, 0.05, 82), (1200, 1100, 64, 0.05, 83),
-                (700, 900, 100, 0.05, 84), (600, 700, 128, 0.05, 85), (300, 500, 256, 0.05, 86)]
+                (700, 900, 100, 0.05, 84), (600, 700, 128, 0.05, 85), (300, 500, 256, 0.05, 86),
+                # ragged and tiny: partial 16-query blocks, a partial two-block step, one row or one key
+                (33, 47, 64, 0.05, 87), (1, 7, 32, 0.05, 88), (9, 1, 100, 0.05, 89), (3, 5, 256, 0.05, 90)]
 
 
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=[f"{s[0]}x{s[1]}d{s[2]}" for s in SPLIT_SHAPES])
