@@ -17,8 +17,12 @@ Printed (one JSON line):
                HIP events on the launch stream around every --timing-stride-th
                pass launch of the timed steps) against the vector-ALU issue
                ceiling of the chip (see roofline_alu);
-  cpu_baseline the CPU oracle as it stands, timed on one full Sinkhorn
-               iteration of the same workload on this host.
+  components_ms  each part of the step timed on its own after the timed
+               steps (median of 3): the solve alone, the cost, the gradient
+               and the standalone two-pass marginal residual, with the solve's
+               own pair-evals/s and iterations/s beside them;
+  cpu_baseline the CPU oracle as it stands, timed on alternating iterations
+               of the same workload on this host (about 10 s of them).
 
 Other steps (--mode, same workload and JSON fields; value counts the pair
 evaluations of the counted iterations only):
@@ -385,6 +389,32 @@ def main():
     if mode == "fs2":
         pair_evals = 2.0 * n * m * fs2_info["fine_iters"]
     extra = {}
+    if mode == "solve":
+        # each part of the step on its own (outside the timed steps; median of 3, HIP events on the stream
+        # the library launches on): the solve alone (prep + K iterations + fused residuals), the cost, the
+        # gradient and the standalone two-pass marginal residual
+        def part_ms(fn):
+            times = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            return sorted(times)[1]
+
+        parts = {
+            "solve": part_ms(lambda: sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, check_every=ce, ws=ws, f=f, g=g,
+                                              trace=trace, check=False)),
+            "cost": part_ms(lambda: sk.cost(A, B, f, g, eps=eps, out=cost_out)),
+            "marginal_residual": part_ms(lambda: sk.marginal_residual(X, Y, A, B, f, g, eps=eps, ws=ws)),
+        }
+        if w.grad:
+            parts["grad_x"] = part_ms(lambda: sk.grad_x(X, Y, A, B, g, eps=eps, ws=ws, out=grad))
+        extra = {"components_ms": {k: round(v, 4) for k, v in parts.items()},
+                 "solve_pair_evals_per_s": 2.0 * n * m * n_iters / (parts["solve"] * 1e-3),
+                 "solve_iters_per_s": n_iters / (parts["solve"] * 1e-3)}
     if mode in ("marginal", "potential"):
         # the same iterations without checks, with the same pass timing events
         # as the timed steps: what the stop rule costs on top
