@@ -549,7 +549,14 @@ def cpu_baseline(x, y, a, b, eps, n, m) -> dict:
     t0 = time.perf_counter()
     oracle.sinkhorn(x, y, a, b, eps, k, lib=lib)
     dt = time.perf_counter() - t0
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": 2.0 * n * m * k / dt, "unit": "pair-evals/s", "cores": oracle.num_threads(lib), "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"{k} full alternating iterations (row + column half-steps, {2 * n * m * k:.3g} pair evaluations) "
                       f"of the same workload from g = 0, float64, {dt:.1f} s wall (after one timed iteration "
                       f"that sets the count)"}
