@@ -1018,13 +1018,14 @@ int fs2_solve(char* base, const FLayout& F, const float* x, const float* y, cons
     lift_f.fin.pot = fs;
     retarget(lift_f, W.f(L.xp), n, fp(F.ky), F.nby, cap);
     const int stride = n / F.ns;
-    // the sampled rows: coordinates, weights and norms (their potential is lifted every round)
+    // the sampled rows: coordinates, weights and norms (the potential gathered with them, from fs, is not
+    // yet set and is overwritten by every round's lift before the check reads it)
     SK_TRY(launch_gather_rows(W.f(L.xp), L.P, fs, as, W.f(L.nx), F.ns, stride, fp(F.sq), fp(F.sf), fp(F.sa),
                               fp(F.snrm), s));
     PassArgs lift_fs = make_pass(W, true, eps, fp(F.sa), cap);
     retarget(lift_fs, fp(F.sq), F.ns, fp(F.ky), F.nby, cap);
     lift_fs.fin.lse = lift_fs.fin.lse_out = fp(F.slse);
-    lift_fs.fin.l2w = fp(F.slse);  // read by the finalisation, used only for a bias, and none is written
+    lift_fs.fin.l2w = nullptr;  // no bias is written for the sampled rows
     lift_fs.fin.nrm = fp(F.snrm);
     lift_fs.fin.pot = fp(F.sf);
     lift_fs.fin.bias_packed = nullptr;

@@ -75,7 +75,7 @@ struct Fin {
     float alpha;         // blend weight of kFinSolve (1 = replace)
     float* lse;          // [nq] state u before the pass (read for a residual or a blend)
     float* lse_out;      // [nq] state after the pass (may equal lse)
-    const float* l2w;    // [nq] log2 of the query-side weights (-inf for zero weight)
+    const float* l2w;    // [nq] log2 of the query-side weights (-inf for zero weight); read when a bias is written
     const float* w;      // [nq] query-side weights
     const float* nrm;    // [nq] |q~|^2 of the centred query points
     float* pot;          // [nq] output potential in cost units, or null

@@ -27,7 +27,7 @@ __device__ __forceinline__ FinIn fin_load(const Fin& F, int i) {
     if (F.mode == kFinSolve) {
         if (F.rbuf || F.alpha != 1.0f) p.old = F.lse[i];
         if (F.rbuf) p.w = F.w[i];
-        p.l2w = F.l2w[i];
+        if (F.bias_packed || F.bias_sep) p.l2w = F.l2w[i];  // only the next bias needs it
         if (F.pot) p.nrm = F.nrm[i];
     } else if (F.mode == kFinProbe) {
         p.w = F.w[i];
