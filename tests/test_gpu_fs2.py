@@ -74,6 +74,11 @@ FIXED_CASES = [
     (1200, 1400, 3, 8, 0.05, 0.01, 50, 1e-5, 2, 15, 40, 22),
     (700, 900, 2, 6, 0.04, 0.02, 512, 1e-6, 2, 10, 30, 23),  # one block per side
     (1000, 800, 1, 5, 0.02, 0.002, 32, 1e-4, 3, 10, 50, 24),
+    # d = 4 ... 7: the screening's per-dimension block records (58-78% of the tiles kept)
+    (900, 800, 4, 8, 0.02, 0.005, 32, 1e-5, 2, 10, 30, 25),
+    (800, 700, 5, 8, 0.02, 0.005, 32, 1e-5, 2, 10, 30, 26),
+    (700, 900, 6, 8, 0.02, 0.005, 32, 1e-5, 2, 10, 30, 27),
+    (600, 700, 7, 8, 0.02, 0.005, 32, 1e-5, 2, 10, 30, 28),
 ]
 
 
