@@ -78,6 +78,7 @@ SHAPES = [
     (600, 700, 128, 0.5, 5, 21, 0.09, 0.0),
     (300, 500, 256, 0.5, 4, 22, 0.0625, 0.0),
     (17, 5, 64, 0.1, 3, 23, 0.125, 0.0),
+    (1200, 1000, 40, 0.3, 6, 24, 0.15, 0.1),  # the bf16 split form with zero weights (keys of bias -inf)
 ]
 
 
