@@ -124,10 +124,10 @@ def packed_stride(d: int) -> int:
 
 
 def roofline_split(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
-    """Matrix-core roofline of the solver pass from P = 32 up, where the cross term runs as six bf16
-    products of a three-part split of each coordinate: 12 d bf16 flops per pair evaluation against the
-    bf16 MFMA peak. The fp32-equivalent rate (2 d flops per pair, the fp32 contraction it replaces) is
-    reported beside it."""
+    """Matrix-core roofline of the solver pass (and the one-column transport kernel), where the cross term
+    runs as six bf16 products of a three-part split of each coordinate: 12 d bf16 flops per pair evaluation
+    against the bf16 MFMA peak. The fp32-equivalent rate (2 d flops per pair, the fp32 contraction it
+    replaces) is reported beside it."""
     ops = 12 * d
     achieved = pairs_per_launch * ops / avg_launch_s / 1e12
     fp32_eq = pairs_per_launch * 2 * d / avg_launch_s / 1e12
@@ -477,7 +477,7 @@ def main():
             roof["kernel"] = "k_transport<%d,%d,0>" % (d, 1 if payload == 1 else (4 if payload <= 4 else 9))
         else:
             p2 = packed_stride(d)
-            if payload == 1 and p2 >= 32:
+            if payload == 1:
                 # the one-column kernel forms its scores in the split form (payload FMAs on the vector ALUs)
                 roof = roofline_split(d, pairs_per_launch, avg_launch_s)
             else:
@@ -489,12 +489,9 @@ def main():
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
         small = pairs_per_launch <= 2.0e6  # the library's single-kernel path for small passes
         roof["kernel"] = f"k_pass_small<{d}>" if small else f"k_pass_valu<{d}>"
-    elif packed_stride(d) >= 32:
-        roof = roofline_split(d, pairs_per_launch, avg_launch_s)
-        roof["kernel"] = "k_pass_mfma<%d, true>" % packed_stride(d)
     else:
-        roof = roofline_mfma(d, pairs_per_launch, avg_launch_s)
-        roof["kernel"] = "k_pass_mfma<%d, false>" % packed_stride(d)
+        roof = roofline_split(d, pairs_per_launch, avg_launch_s)
+        roof["kernel"] = "k_pass_mfma<%d>" % packed_stride(d)
     if roof is not None and mode != "fs2":
         roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma")
     elif roof is not None:

@@ -33,12 +33,11 @@
  *    is enqueued and are returned as an sk_status; nothing is launched then.
  *    A failed launch returns SK_ERR_HIP.
  *  - Supported dimensions: 1 <= d <= 256.  d <= 8 runs on the vector ALUs;
- *    9 <= d <= 256 computes the x.y cross term on matrix cores: for d <= 16
- *    with fp32 instructions, from d = 17 as six bf16 products of a three-part
- *    split of each fp32 coordinate, accumulated in fp32 (the dropped terms lie
- *    below 2^-26 of |x_t y_t|, under the rounding of an fp32 dot product).
- *    The workspace then also holds the keys' bf16 parts, 6 bytes per padded
- *    coordinate.
+ *    9 <= d <= 256 computes the x.y cross term of the solver passes on matrix
+ *    cores as six bf16 products of a three-part split of each fp32
+ *    coordinate, accumulated in fp32 (the dropped terms lie below 2^-26 of
+ *    |x_t y_t|, under the rounding of an fp32 dot product).  The workspace
+ *    then also holds the keys' bf16 parts, 6 bytes per padded coordinate.
  *
  * Sources (page title and section):
  *  FS   = "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",

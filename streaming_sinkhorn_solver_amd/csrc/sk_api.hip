@@ -337,7 +337,7 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.lse_c2 = take(um * 4);
     L.snap_f = take(un * 4);
     L.snap_g = take(um * 4);
-    L.split = L.mfma && L.P >= 32;
+    L.split = L.mfma;
     L.xb = take(L.split ? un * 3 * P * 2 : 0);
     L.yb = take(L.split ? um * 3 * P * 2 : 0);
     L.total = off;

@@ -1,4 +1,4 @@
-// sk_pass_mfma.hip -- streamed log-sum-exp passes with the cross term on fp32
+// sk_pass_mfma.hip -- streamed log-sum-exp passes with the cross term on
 // matrix cores (9 <= d <= 256).
 //
 // The score of a (query, key) pair is s_ij = <q_i, k_j> + h_j (base 2, see
@@ -7,15 +7,15 @@
 // Transport on GPU", Methodology 1-2: biased dot-product scores, streamed
 // tiles, running max / sum-exp, no materialisation).
 //
-// Mapping to CDNA4 (v_mfma_f32_16x16x4f32, D = A B + C, wave64):
-//  * lane l = 16 g + c; A is 16 keys x 4 k (lane: key c, k-step slot g),
-//    B is 4 k x 16 queries (lane: query c, slot g), D is 16 keys x 16 queries
-//    with lane l holding keys 4g..4g+3 of query c;
+// Mapping to CDNA4 (wave64, D = A B + C, keys as A, queries as B):
+//  * lane l = 16 g + c; D is 16 keys x 16 queries with lane l holding keys
+//    4g..4g+3 of query c, for both instructions used here:
+//    v_mfma_f32_16x16x4f32 (lane: key / query c, k slot g) and
+//    v_mfma_f32_16x16x32_bf16 (lane: key / query c, k slots 8g..8g+7);
 //  * the contraction index is permuted so that lane group g owns the
-//    contiguous k range [g P/4, (g+1) P/4): step t of the K loop uses
-//    k = g P/4 + t.  Each lane therefore keeps its query's P/4 coordinates in
-//    registers for the whole pass (row-stationary) and reads its key's P/4
-//    coordinates from LDS as float4s;
+//    contiguous coordinate range [g P/4, (g+1) P/4). Each lane keeps its
+//    query's coordinates in registers for the whole pass (row-stationary) and
+//    reads its key's from a padded LDS tile;
 //  * the accumulator starts at the key biases, so the bias add is free;
 //  * each lane runs an online (M, S) over the keys it sees; the four lane
 //    groups that share a query are merged with two cross-lane exchanges at
@@ -24,8 +24,10 @@
 // Work is split across workgroups with the same stream-K ranges as the vector
 // passes; a row block here is 4 waves x NQB x 16 queries.
 //
-// From P = 32 up the solver pass takes the cross term on bf16 matrix cores
-// instead, exactly enough for fp32 (see split3 and k_pass_mfma<P, true>).
+// The solver pass and the one-column transport kernel take the cross term on
+// bf16 matrix cores from a three-part split of every fp32 coordinate that is
+// as exact as an fp32 dot product (split3, split_scores); the gradient and the
+// payload-carrying transport modes use fp32 instructions.
 #include "sk_internal.hpp"
 #include "sk_pass_common.hpp"
 
@@ -212,39 +214,72 @@ __device__ __forceinline__ f4 mfma_bf16(const u4v a, const u4v b, const f4 c) {
                                                    0);
 }
 
-// A lane's query row for the split form: its P/4 coordinates from qr, scaled,
-// as h, m, l parts, chunk kc holding coordinates 8 kc .. 8 kc + 7.
+// Query operands per lane in the split form: P >= 32 keeps one (h, m, l)
+// triple of 8-coordinate chunks per chunk; P = 16 (4 coordinates per lane
+// group, half an operand) keeps three ready operands that pair two parts each.
 template <int P>
-__device__ __forceinline__ void load_query_split(const float* __restrict__ qr, float qscale, u4v (&qh)[P / 32],
-                                                 u4v (&qm)[P / 32], u4v (&ql)[P / 32]) {
+constexpr int split_qops() {
+    return P >= 32 ? P / 32 : 1;
+}
+
+// A lane's query row for the split form, from its P/4 coordinates at qr,
+// scaled. P >= 32: chunk kc of qh, qm, ql holds the h, m, l parts of
+// coordinates 8 kc .. 8 kc + 7. P = 16: qh = (h, h), qm = (m, h), ql = (l, m)
+// over the lane group's 4 coordinates, the B operands of the three products
+// split_scores<16> forms.
+template <int P>
+__device__ __forceinline__ void load_query_split(const float* __restrict__ qr, float qscale,
+                                                 u4v (&qh)[split_qops<P>()], u4v (&qm)[split_qops<P>()],
+                                                 u4v (&ql)[split_qops<P>()]) {
     const float4* q4 = reinterpret_cast<const float4*>(qr);
-#pragma unroll
-    for (int t4 = 0; t4 < P / 16; ++t4) {
-        const float4 v = q4[t4];
+    if constexpr (P == 16) {
+        const float4 v = q4[0];
         const float x[4] = {v.x * qscale, v.y * qscale, v.z * qscale, v.w * qscale};
+        unsigned hw[2], mw[2], lw[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             unsigned h0, m0, l0, h1, m1, l1;
             split3(x[2 * e], h0, m0, l0);
             split3(x[2 * e + 1], h1, m1, l1);
-            const int kc = t4 / 2, wd = 2 * (t4 % 2) + e;
-            qh[kc][wd] = h0 | (h1 << 16);
-            qm[kc][wd] = m0 | (m1 << 16);
-            ql[kc][wd] = l0 | (l1 << 16);
+            hw[e] = h0 | (h1 << 16);
+            mw[e] = m0 | (m1 << 16);
+            lw[e] = l0 | (l1 << 16);
+        }
+        qh[0] = u4v{hw[0], hw[1], hw[0], hw[1]};
+        qm[0] = u4v{mw[0], mw[1], hw[0], hw[1]};
+        ql[0] = u4v{lw[0], lw[1], mw[0], mw[1]};
+    } else {
+#pragma unroll
+        for (int t4 = 0; t4 < P / 16; ++t4) {
+            const float4 v = q4[t4];
+            const float x[4] = {v.x * qscale, v.y * qscale, v.z * qscale, v.w * qscale};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                unsigned h0, m0, l0, h1, m1, l1;
+                split3(x[2 * e], h0, m0, l0);
+                split3(x[2 * e + 1], h1, m1, l1);
+                const int kc = t4 / 2, wd = 2 * (t4 % 2) + e;
+                qh[kc][wd] = h0 | (h1 << 16);
+                qm[kc][wd] = m0 | (m1 << 16);
+                ql[kc][wd] = l0 | (l1 << 16);
+            }
         }
     }
 }
 
-// Scores of one 16-key block for NQB query blocks in the split form: kr is the
-// lane's key row in the LDS tile (parts h, m, l, P/8 units apart), offset to
-// its lane group. With four query blocks the four accumulator chains keep the
-// matrix pipe busy; with fewer, the small products go to a second accumulator
-// per block (from zero).
+// Scores of one 16-key block for NQB query blocks in the split form: row is
+// the lane's key row in the LDS tile (parts h, m, l, P/8 units apart) and g its
+// lane group. P >= 32: six products per 8-coordinate chunk. P = 16: the lane
+// group's 4 coordinates fill half an operand, so the six products go in pairs
+// into three instructions, (h, m) x (h, h), (h, l) x (m, h), (h, m) x (l, m).
+// With four query blocks the four accumulator chains keep the matrix pipe busy;
+// with fewer, the small products go to a second accumulator per block (from
+// zero).
 template <int P, int NQB>
-__device__ __forceinline__ void split_scores(const u4v* kr, const u4v (&qh)[NQB][P / 32],
-                                             const u4v (&qm)[NQB][P / 32], const u4v (&ql)[NQB][P / 32],
-                                             const f4 bias, f4 (&acc)[NQB]) {
-    constexpr int KC = P / 32;
+__device__ __forceinline__ void split_scores(const u4v* row, int g, const u4v (&qh)[NQB][split_qops<P>()],
+                                             const u4v (&qm)[NQB][split_qops<P>()],
+                                             const u4v (&ql)[NQB][split_qops<P>()], const f4 bias,
+                                             f4 (&acc)[NQB]) {
     constexpr bool kTwoAcc = NQB < 4;
     f4 acc2[NQB];
 #pragma unroll
@@ -253,21 +288,36 @@ __device__ __forceinline__ void split_scores(const u4v* kr, const u4v (&qh)[NQB]
         acc2[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     f4(&small)[NQB] = kTwoAcc ? acc2 : acc;
+    if constexpr (P == 16) {
+        // 8 bytes per part and lane group: part p at uint2 index 4 p + g of the row
+        const uint2* r2 = reinterpret_cast<const uint2*>(row);
+        const uint2 kh = r2[g], km = r2[4 + g], kl = r2[8 + g];
+        const u4v a1 = {kh.x, kh.y, km.x, km.y}, a2 = {kh.x, kh.y, kl.x, kl.y};
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-        const u4v kh = kr[kc], km = kr[P / 8 + kc], kl = kr[2 * (P / 8) + kc];
+        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(a1, qh[qb][0], acc[qb]);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qh[qb][kc], acc[qb]);
+        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(a2, qm[qb][0], small[qb]);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kh, ql[qb][kc], small[qb]);
+        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(a1, ql[qb][0], acc[qb]);
+    } else {
+        constexpr int KC = P / 32;
+        const u4v* kr = row + g * KC;
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qm[qb][kc], acc[qb]);
+        for (int kc = 0; kc < KC; ++kc) {
+            const u4v kh = kr[kc], km = kr[P / 8 + kc], kl = kr[2 * (P / 8) + kc];
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kl, qh[qb][kc], small[qb]);
+            for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qh[qb][kc], acc[qb]);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(km, qh[qb][kc], acc[qb]);
+            for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kh, ql[qb][kc], small[qb]);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(km, qm[qb][kc], small[qb]);
+            for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qm[qb][kc], acc[qb]);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kl, qh[qb][kc], small[qb]);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(km, qh[qb][kc], acc[qb]);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(km, qm[qb][kc], small[qb]);
+        }
     }
     if constexpr (kTwoAcc) {
 #pragma unroll
@@ -321,27 +371,22 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2
     M = mn;
 }
 
-// SPLIT: the cross term on bf16 matrix cores from the three-part split (keys
-// split in memory by k_split3, queries split in registers when a segment
-// starts), P >= 32; else on fp32 matrix cores.  Lane group g owns the same
-// coordinates [g P/4, (g+1) P/4) in both forms; in the split form, chunk kc of
-// a lane group is its 8 coordinates g P/4 + 8 kc .. + 7, one bf16 operand.
-template <int P, bool SPLIT>
+// The solver pass: the cross term on bf16 matrix cores from the three-part
+// split (keys split in memory by k_split3, queries split in registers when a
+// segment starts). Lane group g owns the coordinates [g P/4, (g+1) P/4).
+template <int P>
 __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
-    constexpr int KT = P / 4;           // MFMA k-steps per 16-key block (fp32)
-    constexpr int KC = P / 32;          // 8-coordinate chunks per lane group (split)
-    constexpr int PS = P + 4;           // padded LDS row stride (floats): conflict-free float4 reads
-    constexpr int NQB = mfma_nqb<P>();  // 16-query blocks per wave
-    static_assert(!SPLIT || P >= 32, "the split form needs 8 coordinates per lane group");
-    using Stage = std::conditional_t<SPLIT, TileStage3<P>, TileStage<P>>;
+    constexpr int KT = P / 4;            // coordinates per lane group
+    constexpr int KQ = split_qops<P>();  // query operands per part
+    constexpr int NQB = mfma_nqb<P>();   // 16-query blocks per wave
+    using Stage = TileStage3<P>;
     constexpr int TL = Stage::TL;
-    constexpr int LDS_WORDS = SPLIT ? TL * TileStage3<P>::RS * 4 : TL * PS;
-    __shared__ __align__(16) float ktile[LDS_WORDS];
+    constexpr int RS = Stage::RS;
+    __shared__ u4v ktile[TL * RS];
     __shared__ __align__(16) float btile[TL];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
-    const float4* kp = reinterpret_cast<const float4*>(A.k);
     const u4v* kb = reinterpret_cast<const u4v*>(A.kb);
 
     const int w = blockIdx.x;
@@ -352,88 +397,46 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
         const int j1 = (int)min<int64_t>((int64_t)A.nk, (int64_t)j0 + (hi - u));
         const int qrow0 = rb * A.rpb + wave * (NQB * 16);
 
-        // queries, scaled: fp32 coordinates, or their h, m, l parts
-        float qf[SPLIT ? 1 : NQB][SPLIT ? 1 : KT];
-        u4v qh[SPLIT ? NQB : 1][SPLIT ? KC : 1], qm[SPLIT ? NQB : 1][SPLIT ? KC : 1],
-            ql[SPLIT ? NQB : 1][SPLIT ? KC : 1];
+        // queries, scaled, as h, m, l parts
+        u4v qh[NQB][KQ], qm[NQB][KQ], ql[NQB][KQ];
         float M[NQB], S[NQB];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             const int i = qrow0 + qb * 16 + c;
             const int ic = i < A.nq ? i : A.nq - 1;
-            if constexpr (SPLIT) {
-                load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, qh[qb], qm[qb], ql[qb]);
-            } else {
-                const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
-#pragma unroll
-                for (int t4 = 0; t4 < KT / 4; ++t4) {
-                    const float4 v = qr[t4];
-                    qf[qb][4 * t4 + 0] = v.x * A.qscale;
-                    qf[qb][4 * t4 + 1] = v.y * A.qscale;
-                    qf[qb][4 * t4 + 2] = v.z * A.qscale;
-                    qf[qb][4 * t4 + 3] = v.w * A.qscale;
-                }
-            }
+            load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, qh[qb], qm[qb], ql[qb]);
             M[qb] = kNegBig;
             S[qb] = 0.0f;
         }
 
         Stage stage;
-        if constexpr (SPLIT)
-            stage.load(kb, A.kbias, j0, j1);
-        else
-            stage.load(kp, A.kbias, j0, j1);
+        stage.load(kb, A.kbias, j0, j1);
         for (int base = j0; base < j1; base += TL) {
             __syncthreads();
-            if constexpr (SPLIT)
-                stage.store(reinterpret_cast<u4v*>(ktile), btile);
-            else
-                stage.store(ktile, btile);
+            stage.store(ktile, btile);
             __syncthreads();
-            if (base + TL < j1) {
-                if constexpr (SPLIT)
-                    stage.load(kb, A.kbias, base + TL, j1);
-                else
-                    stage.load(kp, A.kbias, base + TL, j1);
-            }
+            if (base + TL < j1) stage.load(kb, A.kbias, base + TL, j1);
             const int ntile = min(TL, j1 - base);
-            if constexpr (SPLIT && TL >= 32) {
+            if constexpr (TL >= 32) {
                 // two 16-key blocks per step, one rescale for both (3.5% faster at d = 64 than one block per
                 // step); rows past the segment's keys hold bias -inf and add nothing
-                constexpr int RS = TileStage3<P>::RS;
                 for (int kb32 = 0; kb32 < ntile; kb32 += 32) {
                     const f4 bias0 = *reinterpret_cast<const f4*>(&btile[kb32 + 4 * g]);
                     const f4 bias1 = *reinterpret_cast<const f4*>(&btile[kb32 + 16 + 4 * g]);
                     f4 acc0[NQB], acc1[NQB];
-                    split_scores<P, NQB>(reinterpret_cast<const u4v*>(ktile) + (kb32 + c) * RS + g * KC, qh, qm, ql,
-                                         bias0, acc0);
-                    split_scores<P, NQB>(reinterpret_cast<const u4v*>(ktile) + (kb32 + 16 + c) * RS + g * KC, qh, qm,
-                                         ql, bias1, acc1);
+                    split_scores<P, NQB>(ktile + (kb32 + c) * RS, g, qh, qm, ql, bias0, acc0);
+                    split_scores<P, NQB>(ktile + (kb32 + 16 + c) * RS, g, qh, qm, ql, bias1, acc1);
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb) lse_block2(M[qb], S[qb], acc0[qb], acc1[qb]);
                 }
-                continue;
-            }
-            for (int kb16 = 0; kb16 < ntile; kb16 += 16) {
-                const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
-                f4 acc[NQB];
-                if constexpr (SPLIT) {
-                    constexpr int RS = TileStage3<P>::RS;
-                    const u4v* kr = reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS + g * KC;
-                    split_scores<P, NQB>(kr, qh, qm, ql, bias, acc);
-                } else {
-                    float kf[KT];
-                    load_keys<KT>(kf, ktile, (kb16 + c) * PS + g * KT);
+            } else {
+                for (int kb16 = 0; kb16 < ntile; kb16 += 16) {
+                    const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
+                    f4 acc[NQB];
+                    split_scores<P, NQB>(ktile + (kb16 + c) * RS, g, qh, qm, ql, bias, acc);
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) acc[qb] = bias;
-#pragma unroll
-                    for (int t = 0; t < KT; ++t)
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb)
-                            acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
+                    for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], acc[qb]);
                 }
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], acc[qb]);
             }
         }
 
@@ -618,17 +621,18 @@ hipError_t launch_grad_mfma_p(const GradArgs& a, hipStream_t s) {
 // (MODE 2, 2 NQB P / 4 query VGPRs) 797 / 785 / 902 us, the single-column
 // product 402 / 355 / 358 us.
 constexpr int transport_nqb(int P, int NP, int MODE) {
-    // the one-column kernel in the split form: 4 blocks, 151 against 171 us with 2 (16384^2, d = 64)
-    const int base = ((MODE == 0 && NP > 1) || (MODE == 3 && P >= 32)) ? 4 : 2;
+    // the one-column kernel (split form): 4 blocks, 151 against 171 us with 2 at 16384^2, d = 64; an HVP
+    // at d = 16 4.93 against 5.18 ms
+    const int base = ((MODE == 0 && NP > 1) || MODE == 3) ? 4 : 2;
     return P <= 64 ? base : (P == 128 ? base / 2 : 1);
 }
 
 template <int P, int NP, int MODE>
 __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     // one payload column (MODE 3, the conjugate-gradient product) takes the split form from P = 32
-    constexpr bool SPLIT = MODE == 3 && P >= 32;
+    constexpr bool SPLIT = MODE == 3;
     constexpr int KT = P / 4;
-    constexpr int KC = P / 32;
+    constexpr int KQ = split_qops<P>();
     constexpr int PS = P + 4;
     constexpr int NB = (MODE == 1 || MODE == 2) ? P / 16 : NP;  // 16-column output blocks (unused in MODE 3)
     constexpr int KP = MODE == 0 ? 16 * NP : 1;  // payload floats per key in LDS
@@ -650,7 +654,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     const int qrow0 = blockIdx.x * (kWaves * 16 * NQB) + wave * (16 * NQB);
 
     float qf[SPLIT ? 1 : NQB][SPLIT ? 1 : KT], vf[MODE == 2 ? NQB : 1][KT];
-    u4v qh[SPLIT ? NQB : 1][SPLIT ? KC : 1], qm[SPLIT ? NQB : 1][SPLIT ? KC : 1], ql[SPLIT ? NQB : 1][SPLIT ? KC : 1];
+    u4v qh[SPLIT ? NQB : 1][SPLIT ? KQ : 1], qm[SPLIT ? NQB : 1][SPLIT ? KQ : 1], ql[SPLIT ? NQB : 1][SPLIT ? KQ : 1];
     float lse_c[NQB], S[NQB], Tv[NQB];
     f4 T[NQB][NB];
 #pragma unroll
@@ -716,8 +720,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
             f4 acc[NQB], dv[NQB];
             if constexpr (SPLIT) {
                 constexpr int RS = TileStage3<P>::RS;
-                const u4v* kr = reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS + g * KC;
-                split_scores<P, NQB>(kr, qh, qm, ql, bias, acc);
+                split_scores<P, NQB>(reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS, g, qh, qm, ql, bias, acc);
             } else {
                 float kf[KT];
                 load_keys<KT>(kf, ktile, (kb16 + c) * PS + g * KT);
@@ -865,14 +868,8 @@ hipError_t launch_transport_mfma_pp(const TransArgs& a, int mode, int kwidth, hi
 template <int P>
 hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
-    if constexpr (P >= 32) {
-        if (a.kb)
-            hipLaunchKernelGGL((k_pass_mfma<P, true>), dim3(a.W), dim3(kBlock), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_pass_mfma<P, false>), dim3(a.W), dim3(kBlock), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((k_pass_mfma<P, false>), dim3(a.W), dim3(kBlock), 0, s, a);
-    }
+    if (!a.kb) return hipErrorInvalidValue;  // the split keys are written by every solver set-up
+    hipLaunchKernelGGL(k_pass_mfma<P>, dim3(a.W), dim3(kBlock), 0, s, a);
     if (ev1) (void)hipEventRecord(ev1, s);
     return launch_merge(a, s);
 }
@@ -904,8 +901,7 @@ int capacity_p() {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    // the form the solver's passes run (split from P = 32 up)
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pass_mfma<P, (P >= 32)>, kBlock, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pass_mfma<P>, kBlock, 0) != hipSuccess)
         return 0;
     return cus * per_cu;
 }

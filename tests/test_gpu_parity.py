@@ -103,10 +103,10 @@ def test_solve_matches_oracle(shape):
     assert abs(c_gpu - c_or) <= 1e-4 * abs(c_or) + 1e-12
 
 
-# From P = 32 up the matrix-core pass forms the cross term from a three-part bf16 split of every coordinate
-# (six products, fp32 accumulation), which is as accurate as an fp32 dot product; P = 16 keeps fp32 matrix
-# instructions and serves as the reference here. One iteration from g = 0 must then stay within a few float32
-# roundings of the exponent of the oracle's iterate: 4 kappa eps, kappa as above. (Emulated on the CPU for
+# The matrix-core pass forms the cross term from a three-part bf16 split of every coordinate (six products,
+# fp32 accumulation; at P = 16 two products share each instruction), which is as accurate as an fp32 dot
+# product. One iteration from g = 0 must then stay within a few float32 roundings of the exponent of the
+# oracle's iterate: 4 kappa eps, kappa as above. (Emulated on the CPU for
 # these inputs, the float32 rounding of q.y alone moves f by 0.07-0.3 kappa eps, the six products add under
 # 0.01 kappa eps, and keeping only the three largest products moves f by 2-7 kappa eps.)
 SPLIT_SHAPES = [(1500, 1300, 16, 0.05, 81), (1500, 1300, 32, 0.05, 82), (1200, 1100, 64, 0.05, 83),
