@@ -222,6 +222,7 @@ def main():
     ap.add_argument("--workload", default="gmm8_d3_sq")
     ap.add_argument("--iters", type=int, default=None, help="override the workload's iteration count")
     ap.add_argument("--size", type=int, default=None, help="override n = m (same recipe, e.g. a smaller problem)")
+    ap.add_argument("--dim", type=int, default=None, help="override d (same recipe in d dimensions)")
     ap.add_argument("--eps-blur", action="store_true",
                     help="eps = n^(-2/3), the squared mean spacing of n points in the unit cube (the cluster_d3 "
                          "workload's rule) at the --size given")
@@ -269,11 +270,11 @@ def main():
     w = WORKLOADS[args.workload]
     n_iters = w.n_iters if args.iters is None else args.iters
     eps = eps32(w.eps)
-    x, y, a, b = make_inputs(args.workload, n=args.size, m=args.size)
+    x, y, a, b = make_inputs(args.workload, n=args.size, m=args.size, d=args.dim)
     print(f"inputs ready: {x.shape[0]} x {y.shape[0]}, d = {x.shape[1]}", file=sys.stderr, flush=True)
     if args.eps_blur:
         eps = eps32(float(x.shape[0]) ** (-2.0 / 3.0))
-    n, m, d = x.shape[0], y.shape[0], w.d
+    n, m, d = x.shape[0], y.shape[0], x.shape[1]
     dev = torch.device("cuda:0")
     X, Y, A, B = (torch.from_numpy(v).to(dev) for v in (x, y, a, b))
     ws = sk.workspace(n, m, d, dev)
@@ -492,8 +493,11 @@ def main():
     else:
         roof = roofline_split(d, pairs_per_launch, avg_launch_s)
         roof["kernel"] = "k_pass_mfma<%d>" % packed_stride(d)
-    if roof is not None and mode != "fs2":
+    if roof is not None and mode != "fs2" and args.size is None and args.dim is None:
+        # the counter runs were taken on the workload at its own shape
         roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma")
+    elif roof is not None and mode != "fs2":
+        roof["traffic"] = None
     elif roof is not None:
         roof["traffic"] = None  # no counter run of the sparse pass
 
@@ -510,7 +514,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "n": n, "m": m, "d": d, "eps": eps,
+        "config": {"workload": args.workload + ("" if args.dim is None else " (d = %d)" % d), "n": n, "m": m,
+                   "d": d, "eps": eps,
                    # the two-stage solver runs to its target or its iteration cap, without the gradient
                    "n_iters": args.fs2_max_iters if mode == "fs2" else n_iters,
                    "check_every": ce if mode != "fs2" else 10, "grad_x": bool(w.grad) and mode != "fs2",

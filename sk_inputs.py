@@ -95,16 +95,18 @@ def _exp_weights(rng: np.random.Generator, k: int) -> np.ndarray:
     return w / w.sum()
 
 
-def make_inputs(name: str, n: int | None = None, m: int | None = None, seed: int | None = None):
+def make_inputs(name: str, n: int | None = None, m: int | None = None, seed: int | None = None,
+                d: int | None = None):
     """Draw (x, y, a, b) as contiguous float32 arrays for workload ``name``.
 
     ``n``/``m`` override the sizes (same recipe, smaller or ragged problem);
-    ``seed`` overrides the workload's seed.
+    ``seed`` overrides the workload's seed; ``d`` the dimension (same recipe
+    in d dimensions).
     """
     w = WORKLOADS[name]
     n = w.n if n is None else int(n)
     m = w.m if m is None else int(m)
-    d = w.d
+    d = w.d if d is None else int(d)
     rng = np.random.default_rng(w.seed if seed is None else seed)
     if w.recipe == "shifted_gauss":
         x = rng.standard_normal((n, d))
