@@ -320,7 +320,9 @@ int sk_hvp(const float *x, const float *y, const float *a, const float *b,
 /*
  * Workspace bytes of sk_fs2_solve for the given block size and sample count
  * (0 for invalid arguments, or when the radix sort's scratch size cannot be
- * queried because no device is present).
+ * queried because no device is present).  The size does not depend on the
+ * thresholds; the kept-tile lists take at most 2^28 entries per side, so it
+ * stays O(n + m + NBx + NBy).
  */
 size_t sk_fs2_workspace_bytes(int64_t n, int64_t m, int32_t d, int32_t block, int32_t n_sample);
 
