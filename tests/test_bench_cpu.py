@@ -34,3 +34,24 @@ def test_traffic_record_matches_current_kernels_or_is_absent():
     for key, fam in (("gmm8_d3_sq:pass", "valu"), ("gauss_d64:pass", "mfma")):
         t = bench.load_traffic(key, fam)
         assert t is None or t > 0
+
+
+def test_split_roofline_model():
+    # the split form: 12 d bf16 flops per pair against 2.5 PFLOP/s, the fp32-equivalent 2 d beside it
+    pairs = 16384.0 ** 2
+    r = bench.roofline_split(64, pairs, pairs * 768 / 2500e12)
+    assert abs(r["frac"] - 1.0) < 1e-4 and r["ops_per_pair"] == 768 and r["bound"] == "mfma"
+    assert r["fp32_equivalent"]["ops_per_pair"] == 128
+    assert abs(r["fp32_equivalent"]["vs_fp32_mfma_peak"] - 2500.0 / 6 / 157.3) < 1e-3
+    assert [bench.packed_stride(d) for d in (9, 16, 17, 32, 33, 64, 65, 256)] == [16, 16, 32, 32, 64, 64, 128, 256]
+
+
+def test_inputs_dimension_override():
+    from sk_inputs import make_inputs
+
+    x, y, a, b = make_inputs("gauss_d64", n=40, m=30, d=24)
+    assert x.shape == (40, 24) and y.shape == (30, 24) and a.shape == (40,) and b.shape == (30,)
+    x2, _, _, _ = make_inputs("gauss_d64", n=40, m=30, d=24)
+    assert (x == x2).all()  # seeded
+    x64, _, _, _ = make_inputs("gauss_d64", n=40, m=30)
+    assert x64.shape == (40, 64)
