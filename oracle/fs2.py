@@ -4,12 +4,13 @@ TEST INFRASTRUCTURE ONLY (like the rest of ``oracle/``): the GPU library never
 imports or calls it.  Dense numpy arrays throughout (the n x m cost is formed
 for the masked fine stage), so it is meant for a few thousand points.
 
-Source: "FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport", abstract:
-a coarse stage solves on cell centroids, lifts the potentials to every point
-and, when a sampled marginal check rejects the lift, continues on the
-centroids; a block-sparse fine stage on Morton-ordered blocks then removes the
-centroid error, omitting tiles under a threshold set by the block masses that
-bounds each omitted tile's contribution to every row and column.  The pages
+Source: "FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport", Abstract.
+The abstract outlines two stages.  First, Sinkhorn runs on the block centroids;
+its potentials are extended to all points, and the centroid solve goes on for
+as long as a marginal test on a sample of rows is not passed.  Second,
+point-level iterations over Morton-ordered blocks correct what the centroids
+got wrong, skipping the block pairs whose possible share of any row's or
+column's mass, bounded through the block masses, is negligible.  The pages
 give nothing beyond that; the reading written out here (each step a plain
 definition) is:
 

@@ -1,8 +1,10 @@
 """Pins for the two-stage block-sparse reference (oracle/fs2.py): textbook
 Z-order codes, the screening bound checked by brute force against the dense
 plan, the lift against the C oracle's c-transform, the sampled check against
-the C oracle's marginals, reductions to dense Sinkhorn (delta = 0, one point
-per block), far tiles omitted, and the all-particle residual at the end; every
+the C oracle's marginals, the coarse stage's acceptance rule against check
+values built by an independent route, reductions to dense Sinkhorn (delta = 0,
+one point per block), far tiles omitted, and the all-particle residual at the
+end; every
 planted mistake in its source must trip at least one pin.
 
 Source: "FlashSinkhorn 2: Block-Sparse Entropic Optimal Transport", abstract.
@@ -180,6 +182,62 @@ def pin_all_particle_residual(F):
     assert max(r[0], r[1]) <= tol + delta * max(a.max(), b.max()) * 1.0001
 
 
+def _coarse_checks(F, x, y, a, b, eps, B, coarse_iters, rounds, n_sample):
+    """Each round's check value built without the solver: blocks summed directly, the centroid solve by the C
+    oracle continued from the previous round's G (g_init), both lifts by the C oracle's half-step, and the sampled
+    row deviation from the C oracle's plan marginals at the lifted potentials."""
+    lo, hi = np.minimum(x.min(0), y.min(0)), np.maximum(x.max(0), y.max(0))
+    px, py = F.morton_order(x, lo, hi), F.morton_order(y, lo, hi)
+    xs, ys = x[px].astype(np.float64), y[py].astype(np.float64)
+    as_, bs = a[px], b[py]
+    starts_x, starts_y = np.arange(0, len(xs), B), np.arange(0, len(ys), B)
+    amass, bmass = np.add.reduceat(as_, starts_x), np.add.reduceat(bs, starts_y)
+    xcen = np.add.reduceat(as_[:, None] * xs, starts_x) / amass[:, None]
+    ycen = np.add.reduceat(bs[:, None] * ys, starts_y) / bmass[:, None]
+    s = min(len(xs), n_sample)
+    rows = np.array([k * (len(xs) // s) for k in range(s)])
+    G = np.zeros(len(bmass))
+    out = []
+    for _ in range(rounds):
+        Fc, G, _ = oracle.sinkhorn(xcen, ycen, amass, bmass, eps, coarse_iters, g_init=G)
+        f = oracle.half_step(xs, ycen, bmass, G, eps)
+        g = oracle.half_step(ys, xcen, amass, Fc, eps)
+        rs, _ = oracle.marginals(xs, ys, as_, bs, f, g, eps)
+        out.append(float(np.abs(rs[rows] - as_[rows]).max()))
+    return out
+
+
+def pin_coarse_acceptance_rule(F):
+    """The coarse stage ends at the first round whose check value is <= tol, or fell by less than the fraction
+    coarse_gain since the round before, or is the max_rounds-th (the abstract: a sampled marginal check accepts
+    or rejects the lift, and a rejection continues on the centroids).  The check values come from an independent
+    route; the four cases stop on the gain rule, on the tolerance, on the round cap, and on a rising check with
+    coarse_gain = 0, and each case asserts which rule ended it."""
+    x, a = _clustered(300, 2, 4, 0.1, 1)
+    y, b = _clustered(260, 2, 4, 0.1, 2)
+    eps, B, ci, ns = 0.05, 10, 1, 64
+    ref = _coarse_checks(F, x, y, a, b, eps, B, ci, 6, ns)
+    # the sequence these cases rely on: a large fall, a small fall, then a rise
+    assert ref[1] < 0.6 * ref[0] and 0.8 * ref[1] < ref[2] < ref[1] and ref[3] > ref[2]
+    for tol, gain, max_rounds, why in ((0.0, 0.3, 12, "gain"), (0.5 * (ref[0] + ref[1]), 0.3, 12, "tol"),
+                                        (0.0, 0.3, 2, "cap"), (0.0, 0.0, 12, "gain")):
+        rounds, rule = None, None
+        for r in range(1, len(ref) + 1):
+            if ref[r - 1] <= tol:
+                rounds, rule = r, "tol"
+            elif r >= max_rounds:
+                rounds, rule = r, "cap"
+            elif r >= 2 and ref[r - 1] > (1.0 - gain) * ref[r - 2]:
+                rounds, rule = r, "gain"
+            if rounds:
+                break
+        assert rule == why, (tol, gain, max_rounds, rule)
+        _, _, info = F.solve(x, y, a, b, eps, B=B, tol=tol, delta=1e-6, coarse_iters=ci, max_rounds=max_rounds,
+                             coarse_gain=gain, n_sample=ns, max_iters=1)
+        assert info["rounds"] == rounds, (why, info["rounds"], rounds)
+        assert np.allclose(info["checks"], ref[:rounds], rtol=1e-9, atol=0)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -198,6 +256,10 @@ MUTANTS = {
     "check_sign": ("r = as_[rows] * np.expm1((f[rows] - t) / eps)", "r = as_[rows] * np.expm1((t - f[rows]) / eps)"),
     "lift_unweighted": ("f = c_transform(xs, ycen, bmass, G, eps)", "f = c_transform(xs, ycen, np.ones_like(bmass), G, eps)"),
     "fine_col_stale": ("g = masked_update(C.T, as_, f, eps, mask.T)", "g = masked_update(C.T, as_, f * 0.0, eps, mask.T)"),
+    "gain_flipped": ("checks[-1] > (1.0 - coarse_gain) * checks[-2]", "checks[-1] < (1.0 - coarse_gain) * checks[-2]"),
+    "gain_removed": ("if len(checks) >= 2 and checks[-1] > (1.0 - coarse_gain) * checks[-2]:", "if False:"),
+    "coarse_restart": ("F, G = sinkhorn_dense(xcen, ycen, amass, bmass, eps, coarse_iters, G)",
+                       "F, G = sinkhorn_dense(xcen, ycen, amass, bmass, eps, coarse_iters, G * 0.0)"),
 }
 
 
