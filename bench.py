@@ -16,7 +16,9 @@ Printed (one JSON line):
   roofline     the streamed-pass kernel (the dominant kernel, timed live with
                HIP events on the launch stream around every --timing-stride-th
                pass launch of the timed steps) against the vector-ALU issue
-               ceiling of the chip (see roofline_alu);
+               ceiling of the chip in lane-slots/s, with its fp32 flop rate
+               against the published fp32 vector peaks beside it (see
+               roofline_alu);
   components_ms  each part of the step timed on its own after the timed
                steps (median of 3): the solve alone, the cost, the gradient
                and the standalone two-pass marginal residual, with the solve's
@@ -81,25 +83,43 @@ EXP_RATE_FRACTION = 0.5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass_traffic.json")
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak (packed fp32: two lanes' FMAs per slot)
+FP32_NONPACKED_PEAK_TFLOPS = 78.6  # the same units issuing one fp32 FMA per lane per cycle
+
+
 def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int = 0) -> dict:
     """Vector-ALU roofline of one streamed pass.
 
-    Algorithmic work per pair evaluation: d FMAs (2d flops), one max, one
-    subtract, one add and one exp2 = 2d + 4 fp32 operations.  Fewest VALU issue
-    slots per pair: d FMAs (the bias rides in the first FMA's addend), 1/2 for
+    The pass is bound by vector instruction issue.  Fewest VALU issue slots per
+    pair evaluation: d FMAs (the bias rides in the first FMA's addend), 1/2 for
     the running max (v_max3 takes two new scores per instruction), one
-    subtract, one exp2 and one add: d + 3.5.  The chip's ceiling is therefore
-    min(LANE_OPS_PER_S / (d + 3.5), EXP_RATE_FRACTION * LANE_OPS_PER_S) pairs/s,
-    and the peak in operation units is that times (2d + 4).  A transport pass
-    with a payload of K columns adds K FMAs per pair (2K operations, K slots).
+    subtract, one exp2 and one add: d + 3.5 lane-slots.  The chip issues
+    LANE_OPS_PER_S = 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 3.93e13 lane-slots
+    per second, the exp2 unit completing at half that rate, so the ceiling is
+    min(LANE_OPS_PER_S / (d + 3.5), EXP_RATE_FRACTION * LANE_OPS_PER_S) pairs/s.
+    `achieved`, `peak` and `frac` are in lane-slots per second: the minimal
+    slots of the pairs evaluated per launch over the launch duration, against
+    the slots the chip can issue (capped by the exp2 rate).
+
+    The same launch is also priced in fp32 flops against the chip's published
+    fp32 vector peaks: 2d + 3 flops per pair (d FMAs, the max, the subtract and
+    the add; the exp2 is a transcendental, not a flop), over 157.3 TFLOP/s
+    (packed fp32) and 78.6 TFLOP/s (one FMA per lane per cycle).  A transport
+    pass with a payload of K columns adds K FMAs per pair (K slots, 2K flops).
     """
-    ops_per_pair = 2 * d + 4 + 2 * payload
-    ceiling_pairs = min(LANE_OPS_PER_S / (d + 3.5 + payload), EXP_RATE_FRACTION * LANE_OPS_PER_S)
-    achieved = pairs_per_launch * ops_per_pair / avg_launch_s / 1e12
-    peak = ceiling_pairs * ops_per_pair / 1e12
-    return {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
-            "ops_per_pair": ops_per_pair, "pairs_per_launch": pairs_per_launch,
+    slots_per_pair = d + 3.5 + payload
+    ceiling_pairs = min(LANE_OPS_PER_S / slots_per_pair, EXP_RATE_FRACTION * LANE_OPS_PER_S)
+    achieved = pairs_per_launch * slots_per_pair / avg_launch_s / 1e12
+    peak = ceiling_pairs * slots_per_pair / 1e12
+    flops_per_pair = 2 * d + 3 + 2 * payload
+    tflops = pairs_per_launch * flops_per_pair / avg_launch_s / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3),
+            "unit": "T VALU lane-slots/s", "frac": round(achieved / peak, 4), "traffic": None,
+            "slots_per_pair": slots_per_pair, "fp32_flops_per_pair": flops_per_pair,
+            "fp32_tflops": round(tflops, 3),
+            "frac_fp32_peak": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "frac_fp32_nonpacked": round(tflops / FP32_NONPACKED_PEAK_TFLOPS, 4),
+            "pairs_per_launch": pairs_per_launch,
             "avg_launch_us": round(avg_launch_s * 1e6, 3), "ceiling_pairs_per_s": ceiling_pairs}
 
 
