@@ -13,7 +13,8 @@
  *    (m, d), a is (n), b is (m), f is (n), g is (m).  They are owned by the
  *    caller; the library never allocates, frees or retains them.
  *  - The library never allocates device memory (sk_solve_ex with a stop rule
- *    keeps a few pinned host bytes for its check values).  Entry points that need
+ *    keeps a few pinned host bytes for its check values; the code object holds
+ *    the static scratch of sk_solve_noalloc, one per GPU).  Entry points that need
  *    scratch space take a workspace `ws` of at least sk_workspace_bytes(n, m, d)
  *    bytes, 256-byte aligned, owned by the caller.  A workspace may be reused
  *    by later calls once the calls that used it have completed in stream order.
@@ -78,8 +79,13 @@ typedef enum sk_status {
                                   threshold of sk_fs2_solve */
     SK_ERR_CAPTURE = 15,       /* a host-synchronous call (a stop rule, sk_fs2_solve) on a
                                   stream under graph capture */
-    SK_ERR_LR = 16             /* the gradient-flow step size is not finite */
+    SK_ERR_LR = 16,            /* the gradient-flow step size is not finite */
+    SK_ERR_SCRATCH = 17        /* sk_solve_noalloc: sk_workspace_bytes(n, m, d) exceeds
+                                  SK_NOALLOC_SCRATCH_BYTES */
 } sk_status;
+
+/* Bytes of the static device scratch that sk_solve_noalloc works in (64 MiB). */
+#define SK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Version of this ABI (incremented on any signature change). */
 int sk_abi_version(void);
@@ -128,6 +134,28 @@ int sk_solve(const float *x, const float *y, const float *a, const float *b,
              int64_t n, int64_t m, int32_t d, float eps, int32_t n_iters,
              float *f, float *g, int32_t check_every, float *resid_trace,
              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * sk_solve without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels, results and errors as
+ * sk_solve, bit for bit; the workspace is instead a static device array of
+ * SK_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held from the first
+ * call on that GPU until the process ends.  Problems whose
+ * sk_workspace_bytes(n, m, d) exceeds it return SK_ERR_SCRATCH before
+ * anything is enqueued (64 MiB holds, e.g., n = m = 50,000 at d = 3 and
+ * n = m = 16,384 at d = 64).  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine) and enqueues only.  The scratch keeps
+ * the last call's contents; the solve writes every part of it before reading
+ * it, so nothing is cleared.  All calls on one GPU share the one array: calls
+ * whose work overlaps on that GPU (other streams, other threads, or the same
+ * stream captured into graphs replayed concurrently) race and give undefined
+ * results; serialise them.  The caller still passes inputs and outputs.
+ */
+int sk_solve_noalloc(const float *x, const float *y, const float *a, const float *b,
+                     int64_t n, int64_t m, int32_t d, float eps, int32_t n_iters,
+                     float *f, float *g, int32_t check_every, float *resid_trace,
+                     void *stream);
 
 /*
  * Entropic OT cost at potentials (f, g) that come out of a column half-step

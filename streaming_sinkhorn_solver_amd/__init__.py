@@ -29,9 +29,10 @@ _STATUS_NAMES = {
     0: "SK_OK", 1: "SK_ERR_NULL", 2: "SK_ERR_SHAPE", 3: "SK_ERR_UNSUPPORTED_D", 4: "SK_ERR_EPS",
     5: "SK_ERR_ITERS", 6: "SK_ERR_CHECK_EVERY", 7: "SK_ERR_NEG_WEIGHT", 8: "SK_ERR_MASS_MISMATCH",
     9: "SK_ERR_EMPTY_MEASURE", 10: "SK_ERR_NONFINITE", 11: "SK_ERR_WORKSPACE", 12: "SK_ERR_HIP",
-    13: "SK_ERR_VARIANT", 14: "SK_ERR_STOP", 15: "SK_ERR_CAPTURE", 16: "SK_ERR_LR",
+    13: "SK_ERR_VARIANT", 14: "SK_ERR_STOP", 15: "SK_ERR_CAPTURE", 16: "SK_ERR_LR", 17: "SK_ERR_SCRATCH",
 }
-_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 13, 14, 15, 16}
+_VALUE_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 13, 14, 15, 16, 17}
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SK_NOALLOC_SCRATCH_BYTES of include/sk.h
 
 # SinkSLOT README, API Reference: variant and stop_mode names
 VARIANTS = {"alternating": 0, "symmetric": 1}
@@ -46,6 +47,8 @@ SIGNATURES = {
     "sk_check_inputs": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]),
     "sk_solve": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _vp, _vp, _i32, _vp, _vp, _sz,
                                 _vp]),
+    "sk_solve_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _vp, _vp, _i32, _vp,
+                                        _vp]),
     "sk_cost": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp]),
     "sk_marginal_residual": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz,
                                             _vp]),
@@ -236,6 +239,27 @@ def solve(x, y, a=None, b=None, *, eps: float, n_iters: int, check_every: int = 
     _raise(lib.sk_solve(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), _ptr(f), _ptr(g),
                         int(check_every), _ptr(trace) if nt > 0 else None, _ptr(ws), ws.numel(),
                         _stream(x.device)), "sk_solve")
+    return f, g, trace
+
+
+def solve_noalloc(x, y, a=None, b=None, *, eps: float, n_iters: int, f: torch.Tensor, g: torch.Tensor,
+                  check_every: int = 0, trace: torch.Tensor | None = None):
+    """sk_solve_noalloc: the fixed-count solve of ``solve`` in the library's static device scratch, with
+    caller-supplied outputs (f (n,), g (m,) and, when check_every > 0, trace of n_iters // check_every
+    floats).  Nothing is allocated, so the data checks of ``check_inputs`` (which need a workspace) are not
+    run here; call it beforehand if the data may be invalid.  Problems whose workspace would exceed
+    NOALLOC_SCRATCH_BYTES raise ValueError.  Calls whose work overlaps on one GPU race (one scratch per GPU).
+    """
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    f = _buf(f, (n,), torch.float32, x.device, "f")
+    g = _buf(g, (m,), torch.float32, x.device, "g")
+    nt = n_iters // check_every if check_every > 0 else 0
+    if nt > 0:
+        trace = _at_least(trace, nt, torch.float32, x.device, "trace")
+    _raise(lib.sk_solve_noalloc(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), _ptr(f),
+                                _ptr(g), int(check_every), _ptr(trace) if nt > 0 else None, _stream(x.device)),
+           "sk_solve_noalloc")
     return f, g, trace
 
 
@@ -488,4 +512,5 @@ def timing_read() -> tuple[float, int, float]:
 __all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "gradient_flow", "transport", "hvp", "fs2_solve",
            "transport_workspace", "cost", "dual_cost", "divergence",
            "divergence_workspace", "marginal_residual", "grad_x", "check_inputs", "workspace", "workspace_bytes",
-           "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES", "VARIANTS", "STOP_MODES"]
+           "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES", "VARIANTS", "STOP_MODES",
+           "solve_noalloc", "NOALLOC_SCRATCH_BYTES"]

@@ -1232,6 +1232,38 @@ DivLayout div_layout(int64_t n, int64_t m, int d) {
 
 }  // namespace sk
 
+// Device scratch of sk_solve_noalloc, for callers that cannot allocate: one
+// copy per GPU, held until the process ends.  In host code this name stands
+// for a host-side shadow, not device memory; the device address is taken once
+// per device with hipGetSymbolAddress (scratch_address below) and only that
+// address reaches kernels.
+static __device__ __align__(256) unsigned char scratch[SK_NOALLOC_SCRATCH_BYTES];
+
+namespace sk {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device (null until first taken)
+
+// The current device's address of `scratch`, taken on the first call on that device.
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SK_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SK_ERR_HIP;
+        if (reinterpret_cast<uintptr_t>(p) % 256 != 0) return SK_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SK_OK;
+}
+
+}  // namespace
+}  // namespace sk
+
 using namespace sk;
 
 extern "C" {
@@ -1261,6 +1293,9 @@ const char* sk_status_string(int status) {
                    ">= 0; check_every >= 1)";
         case SK_ERR_CAPTURE: return "this call synchronises the stream and cannot run under graph capture";
         case SK_ERR_LR: return "the step size must be finite";
+        case SK_ERR_SCRATCH:
+            return "the problem needs more workspace than the static scratch of sk_solve_noalloc holds "
+                   "(sk_workspace_bytes(n, m, d) > SK_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -1331,6 +1366,26 @@ int sk_solve(const float* x, const float* y, const float* a, const float* b, int
     const Layout L = make_layout(n, m, d);
     if ((st = check_ws(ws, ws_bytes, L))) return st;
     Ws W{L, static_cast<char*>(ws)};
+    return solve_fixed(W, x, y, a, b, eps, n_iters, f, g, check_every, resid_trace,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
+int sk_solve_noalloc(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m,
+                     int32_t d, float eps, int32_t n_iters, float* f, float* g, int32_t check_every,
+                     float* resid_trace, void* stream) {
+    if (!x || !y || !a || !b || !f || !g) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if (n_iters < 0) return SK_ERR_ITERS;
+    if (check_every < 0 || (check_every > 0 && n_iters / check_every > 0 && !resid_trace))
+        return SK_ERR_CHECK_EVERY;
+    const Layout L = make_layout(n, m, d);
+    if (L.total > (size_t)SK_NOALLOC_SCRATCH_BYTES) return SK_ERR_SCRATCH;
+    void* ptr = nullptr;
+    if ((st = scratch_address(&ptr))) return st;
+    // every region the solve reads is written first by the same call: nothing needs clearing
+    Ws W{L, static_cast<char*>(ptr)};
     return solve_fixed(W, x, y, a, b, eps, n_iters, f, g, check_every, resid_trace,
                        reinterpret_cast<hipStream_t>(stream));
 }

@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "sk.h")
 SK_OK, SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_UNSUPPORTED_D, SK_ERR_EPS = 0, 1, 2, 3, 4
 SK_ERR_ITERS, SK_ERR_CHECK_EVERY, SK_ERR_WORKSPACE = 5, 6, 11
 SK_ERR_VARIANT, SK_ERR_STOP, SK_ERR_CAPTURE = 13, 14, 15
+SK_ERR_SCRATCH = 17
 
 
 @pytest.fixture(scope="module")
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 17):
+    for code in range(0, 18):
         s = lib.sk_status_string(code)
         assert s and len(s) > 1 and s != b"unknown status"
     assert lib.sk_status_string(999) == b"unknown status"
@@ -101,6 +102,25 @@ def test_solve_argument_errors(lib):
     assert _solve(lib, ws=None) == SK_ERR_WORKSPACE
     assert _solve(lib, ws=ctypes.c_void_p(0x100010)) == SK_ERR_WORKSPACE  # not 256-byte aligned
     assert _solve(lib, ws_bytes=1000) == SK_ERR_WORKSPACE
+
+
+def test_noalloc_argument_errors(lib):
+    # the same checks as sk_solve, then the scratch limit, all before any GPU work
+    def call(x=FAKE, n=10, m=12, d=2, eps=0.1, iters=5, check_every=0, trace=None):
+        return lib.sk_solve_noalloc(x, FAKE, FAKE, FAKE, n, m, d, eps, iters, FAKE, FAKE, check_every, trace, None)
+
+    assert call(x=None) == SK_ERR_NULL
+    assert call(n=0) == SK_ERR_SHAPE
+    assert call(d=300) == SK_ERR_UNSUPPORTED_D
+    assert call(eps=0.0) == SK_ERR_EPS
+    assert call(iters=-1) == SK_ERR_ITERS
+    assert call(check_every=2) == SK_ERR_CHECK_EVERY
+    limit = sk.NOALLOC_SCRATCH_BYTES
+    assert limit == 64 << 20
+    # 2^20 x 2^20 at d = 3 needs about 100 MiB; 16384^2 at d = 64 and 50,000^2 at d = 3 fit
+    assert lib.sk_workspace_bytes(1 << 20, 1 << 20, 3) > limit
+    assert call(n=1 << 20, m=1 << 20, d=3) == SK_ERR_SCRATCH
+    assert lib.sk_workspace_bytes(16384, 16384, 64) <= limit and lib.sk_workspace_bytes(50000, 50000, 3) <= limit
 
 
 def test_other_entry_points_argument_errors(lib):
