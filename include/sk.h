@@ -216,7 +216,8 @@ int sk_grad_x(const float *x, const float *y, const float *a, const float *b,
  *   The potential value is max(max_i |f_i - f'_i|, max_j |g_j - g'_j|) against
  *   the potentials at the previous check (zero before the first), i.e. eps
  *   times the change of the absorbed potentials f/eps; the run stops at the
- *   first check with value < stop_tol.  At each check the host waits until
+ *   first check with value < stop_tol.  A check value taken from a NaN
+ *   state is NaN and never meets the tolerance.  At each check the host waits until
  *   `stream` has produced that check's value: the GPU stores it straight into
  *   pinned, mapped host memory and raises a flag there, which the host polls
  *   (a 64-byte slot per call in flight, allocated with hipHostMalloc on first

@@ -436,6 +436,9 @@ class HostSlot {
     int seq_ = 0;
 };
 
+// The larger of two check values, NaN if either is NaN (a NaN check is never met).
+float max_nan(float a, float b) { return (std::isnan(a) || std::isnan(b)) ? NAN : std::max(a, b); }
+
 // Sinkhorn with an update variant and a stop rule (SinkSLOT README, API
 // Reference).  Iteration k of the alternating variant is a row pass from the
 // current g then a column pass from the new f; the symmetric variant runs both
@@ -580,7 +583,7 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
         if (fused_col) {
             SK_TRY(launch_max_reduce(rbuf, (int)L.m, chk + 1, s, slot.flag(), slot.next()));
             if ((st = slot.read(host, 2, s))) return st;
-            res->viol = std::max(host[0], host[1]);
+            res->viol = max_nan(host[0], host[1]);
             if (res->viol <= o.tol) return stop_at(k - 1, true, true);
             cr ^= 1;
             cc ^= 1;
@@ -631,7 +634,7 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
             cnt = 2;
         }
         if ((st = slot.read(host, cnt, s))) return st;
-        res->viol = cnt == 2 ? std::max(host[0], host[1]) : host[0];
+        res->viol = cnt == 2 ? max_nan(host[0], host[1]) : host[0];
         if (res->viol <= o.tol) res->converged = 1;
     }
     return SK_OK;

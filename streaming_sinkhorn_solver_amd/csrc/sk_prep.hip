@@ -28,12 +28,16 @@ __device__ inline double block_sum_f64(double v, double* sh) {
     return r;
 }
 
+// Maximum that propagates NaN (fmaxf returns the other operand): a check value
+// read from a NaN state must not look like a met tolerance.
+__device__ __forceinline__ float max_nan(float a, float b) { return (a != a || b != b) ? a + b : fmaxf(a, b); }
+
 __device__ inline float block_max_f32(float v, float* sh) {
     const int t = threadIdx.x;
     sh[t] = v;
     __syncthreads();
     for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-        if (t < w) sh[t] = fmaxf(sh[t], sh[t + w]);
+        if (t < w) sh[t] = max_nan(sh[t], sh[t + w]);
         __syncthreads();
     }
     float r = sh[0];
@@ -238,12 +242,12 @@ __global__ __launch_bounds__(1024) void k_pot_change(const float* __restrict__ f
     float mx = 0.0f;
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
         const float v = f[i];
-        mx = fmaxf(mx, fabsf(v - sf[i]));
+        mx = max_nan(mx, fabsf(v - sf[i]));
         sf[i] = v;
     }
     for (int j = threadIdx.x; j < m; j += blockDim.x) {
         const float v = g[j];
-        mx = fmaxf(mx, fabsf(v - sg[j]));
+        mx = max_nan(mx, fabsf(v - sg[j]));
         sg[j] = v;
     }
     mx = block_max_f32(mx, shf);
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(1024) void k_resid_reduce(const float* __restrict__
     double sm = 0.0;
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
         float v = r[i];
-        mx = fmaxf(mx, v);
+        mx = max_nan(mx, v);
         sm += (double)v;
     }
     mx = block_max_f32(mx, shf);
@@ -275,22 +279,22 @@ __global__ __launch_bounds__(1024) void k_resid_reduce(const float* __restrict__
     }
 }
 
-// Maximum of v[0..cnt), -inf when cnt == 0 (one workgroup): lane maxima, then
+// Maximum of v[0..cnt), -inf when cnt == 0, NaN if any v is NaN (one workgroup): lane maxima, then
 // a shuffle tree per wave and one more across the waves (max is exact in any order).
 __global__ __launch_bounds__(1024) void k_max_reduce(const float* __restrict__ v, int cnt, float* __restrict__ out,
                                                      int* flag, int seq) {
     __shared__ float shw[16];
     float mx = -INFINITY;
-    for (int i = threadIdx.x; i < cnt; i += blockDim.x) mx = fmaxf(mx, v[i]);
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) mx = max_nan(mx, v[i]);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    for (int off = 32; off > 0; off >>= 1) mx = max_nan(mx, __shfl_xor(mx, off));
     const int wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
     if ((threadIdx.x & 63) == 0) shw[wave] = mx;
     __syncthreads();
     if (threadIdx.x < 64) {
         mx = threadIdx.x < nw ? shw[threadIdx.x] : -INFINITY;
 #pragma unroll
-        for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        for (int off = 8; off > 0; off >>= 1) mx = max_nan(mx, __shfl_xor(mx, off));
         if (threadIdx.x == 0) publish(out, mx, flag, seq);
     }
 }

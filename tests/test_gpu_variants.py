@@ -283,3 +283,26 @@ def test_divergence_of_a_translate():
     scale = abs(out[1]) + 0.5 * abs(out[2]) + 0.5 * abs(out[3])
     say("translate S", out[0], "|t|^2", shift, "err/scale", abs(out[0] - shift) / scale)
     assert abs(out[0] - shift) <= 1e-4 * scale
+
+
+# ------------------------------------------------------------------ a NaN state is never converged
+@pytest.mark.parametrize("rule", ["marginal", "potential"])
+def test_nan_state_is_not_reported_converged(rule):
+    """At an eps near the smallest the library accepts (1e-37: 2 log2(e)/eps is still finite in float32) and
+    clouds spread over tens of units, the pre-scaled scores overflow to inf - inf = NaN, so the potentials
+    become NaN.  Every check value taken from that state must then be NaN, and a NaN check never meets the
+    tolerance: converged is False, final_viol NaN, the cap is run.  The same state gives a NaN residual trace
+    and a NaN standalone residual."""
+    x, y, a, b = random_problem(600, 500, 3, seed=41, scale=10.0)
+    X, Y, A, B = dev(x, y, a, b)
+    eps = 1e-37
+    say("nan state", rule)
+    f, g, it, conv, viol = sk.solve_ex(X, Y, A, B, eps=eps, stop_mode=rule, stop_tol=1e30, max_iter=6,
+                                       check_every=2)
+    fh, gh = host(f), host(g)
+    assert np.isnan(fh).any() or np.isnan(gh).any()
+    assert conv is False and math.isnan(viol) and it == 6
+    _, _, tr = sk.solve(X, Y, A, B, eps=eps, n_iters=4, check_every=2)
+    assert np.isnan(host(tr)).all()
+    r = host(sk.marginal_residual(X, Y, A, B, f, g, eps=eps))
+    assert np.isnan(r[0]) or np.isnan(r[1])
