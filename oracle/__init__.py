@@ -17,7 +17,8 @@ Passages followed (page title and section):
   * SinkSLOT README, Tensor Contract (cost |x-y|^2, weights as given, zeros
     legal) and API Reference (alternating and symmetric variants, the fixed,
     marginal and potential stop modes, the infinity-norm marginal residual),
-    Low-Level Solver API (iters_run, converged, final_viol), and the opening
+    Low-Level Solver API (iters_run, converged, final_viol), Basic Usage (the
+    loss returns the primal value of the achieved plan), and the opening
     section (entropic OT is not zero at (x, x): the debiased divergence), Gradient Flow (descent on the
     analytic gradient).
 Pins: every function here is checked in tests/test_oracle_pins.py against
@@ -88,6 +89,8 @@ def load(path: str | None = None):
         lib.oracle_grad_x.restype = None
         lib.oracle_dual_cost.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, _dp, _dp]
         lib.oracle_dual_cost.restype = dbl
+        lib.oracle_primal.argtypes = [_dp, _dp, _dp, _dp, i64, i64, i32, dbl, _dp, _dp, _dp]
+        lib.oracle_primal.restype = None
         lib.oracle_max_cost.argtypes = [_dp, _dp, i64, i64, i32]
         lib.oracle_max_cost.restype = dbl
         if path is None:
@@ -249,6 +252,17 @@ def dual_cost(x, y, a, b, f, g, eps: float, lib=None) -> float:
     x, y, a, b, f, g = _cloud(x), _cloud(y), _f64(a), _f64(b), _f64(f), _f64(g)
     return float(lib.oracle_dual_cost(_ptr(x), _ptr(y), _ptr(a), _ptr(b), x.shape[0], y.shape[0], x.shape[1],
                                       float(eps), _ptr(f), _ptr(g)))
+
+
+def primal(x, y, a, b, f, g, eps: float, lib=None):
+    """(<P,C> + eps KL(P | a x b), <P,C>) of the plan P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps), with the
+    generalised KL(P | Q) = sum P log(P/Q) - P + Q."""
+    lib = lib or load()
+    x, y, a, b, f, g = _cloud(x), _cloud(y), _f64(a), _f64(b), _f64(f), _f64(g)
+    out = np.empty(2)
+    lib.oracle_primal(_ptr(x), _ptr(y), _ptr(a), _ptr(b), x.shape[0], y.shape[0], x.shape[1], float(eps),
+                      _ptr(f), _ptr(g), _ptr(out))
+    return float(out[0]), float(out[1])
 
 
 def max_cost(x, y, lib=None) -> float:

@@ -367,6 +367,49 @@ double oracle_dual_cost(const double *x, const double *y, const double *a, const
 }
 
 /*
+ * Primal value of the plan at potentials (f, g),
+ *   P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps),
+ * out[0] = <P, C> + eps KL(P | a x b) with the generalised KL
+ *          KL(P | Q) = sum_ij P_ij log(P_ij / Q_ij) - P_ij + Q_ij,
+ * out[1] = <P, C>, the transport cost of the plan.
+ * Each entry of P is formed and used as written (0 log 0 = 0 where a weight
+ * is zero or an entry underflows); rows are summed in index order.  Reading:
+ * the SinkSLOT README (Basic Usage) has its loss return the primal value of
+ * the achieved plan; for entropic OT that is this objective, which equals the
+ * dual objective at the optimum.
+ */
+void oracle_primal(const double *x, const double *y, const double *a, const double *b,
+                   int64_t n, int64_t m, int d, double eps, const double *f, const double *g,
+                   double *out)
+{
+    double *row_obj = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double *row_pc = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+        double obj = 0.0, pc = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            double q = a[i] * b[j];
+            double c = sq_dist(x + i * d, y + j * d, d);
+            double p = q > 0.0 ? q * exp((f[i] + g[j] - c) / eps) : 0.0;
+            double kl = p > 0.0 ? p * log(p / q) - p + q : q;
+            pc += p * c;
+            obj += p * c + eps * kl;
+        }
+        row_obj[i] = obj;
+        row_pc[i] = pc;
+    }
+    double so = 0.0, sp = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        so += row_obj[i];
+        sp += row_pc[i];
+    }
+    out[0] = so;
+    out[1] = sp;
+    free(row_obj);
+    free(row_pc);
+}
+
+/*
  * Debiased entropic divergence S = OT(x,y) - OT(x,x)/2 - OT(y,y)/2, each term
  * the dual objective after n_iters iterations of the chosen variant (fixed
  * stop).  out[0] = S, out[1..3] = OT(x,y), OT(x,x), OT(y,y).  Reading: the

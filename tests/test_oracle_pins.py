@@ -58,6 +58,23 @@ def pin_scaling_form_trajectory(lib):
         assert np.max(np.abs(g - gs)) <= 1e-11 * scale, (n, m, d, iters)
 
 
+def pin_scaling_form_warm_start(lib):
+    """From a given g_init the log-domain iterates equal the matrix-scaling iterates started at
+    v = b exp(g_init / eps), the scaling-form image of g_init."""
+    for (n, m, d, seed, eps, iters) in [(7, 5, 2, 51, 0.5, 1), (6, 9, 3, 52, 2.0, 6), (8, 8, 1, 53, 0.3, 12)]:
+        x, y, a, b = _problem(n, m, d, seed)
+        g0 = np.random.default_rng(seed + 1).normal(size=m) * eps
+        f, g, _ = oracle.sinkhorn(x, y, a, b, eps, iters, g_init=g0, lib=lib)
+        K = np.exp(-cdist(x, y, "sqeuclidean") / eps)
+        v = b * np.exp(g0 / eps)
+        for _ in range(iters):
+            u = a / (K @ v)
+            v = b / (K.T @ u)
+        scale = cdist(x, y, "sqeuclidean").max()
+        assert np.max(np.abs(f - eps * np.log(u / a))) <= 1e-11 * scale, (n, m, d, iters)
+        assert np.max(np.abs(g - eps * np.log(v / b))) <= 1e-11 * scale, (n, m, d, iters)
+
+
 def pin_marginals_scaling_form(lib):
     """Plan marginals and residual norms equal those of the explicit scaled plan."""
     for (n, m, d, seed, eps, iters) in [(7, 5, 2, 21, 0.5, 3), (9, 6, 3, 22, 0.8, 1)]:
@@ -177,6 +194,52 @@ def pin_strong_duality(lib):
     primal = (P * C).sum() + eps * ((P * np.log(P / ab)).sum() - P.sum() + ab.sum())
     assert abs(oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib) - primal) <= 1e-10 * max(1.0, abs(primal))
     assert oracle.residual(x, y, a, b, f, g, eps, lib=lib)[0] < 1e-12
+
+
+def pin_primal_explicit_plan(lib):
+    """The primal value and <P,C> at potentials off the optimum equal those of the explicit matrix-scaling plan
+    with the generalised KL written out: the scaling plan diag(u) K diag(v) after a few iterations, with v
+    rescaled by exp(delta_j / eps), is the plan of (f, g + delta), whose mass differs from sum(a) sum(b)."""
+    for (n, m, d, seed, eps, iters) in [(7, 5, 2, 61, 0.5, 2), (6, 9, 3, 62, 0.8, 1), (5, 5, 1, 63, 0.3, 4)]:
+        x, y, a, b = _problem(n, m, d, seed)
+        f, g, _ = oracle.sinkhorn(x, y, a, b, eps, iters, lib=lib)
+        delta = 0.3 * eps * np.random.default_rng(seed).normal(size=m)
+        g = g + delta
+        _, _, P = _scaling_form(x, y, a, b, eps, iters)
+        P = P * np.exp(delta / eps)[None, :]
+        C = cdist(x, y, "sqeuclidean")
+        ab = a[:, None] * b[None, :]
+        want = (P * C).sum() + eps * ((P * np.log(P / ab)).sum() - P.sum() + ab.sum())
+        assert abs(P.sum() - 1.0) > 1e-6  # the mass terms of the KL matter here
+        got, pc = oracle.primal(x, y, a, b, f, g, eps, lib=lib)
+        assert abs(got - want) <= 1e-11 * max(1.0, abs(want)), (n, m, d)
+        assert abs(pc - (P * C).sum()) <= 1e-11 * max(1.0, (P * C).sum()), (n, m, d)
+
+
+def pin_primal_duality_and_closed_forms(lib):
+    """At convergence the primal value equals the dual cost; with one target point after one iteration the
+    plan is a itself, so <P,C> = sum_i a_i C_i1 and the KL vanishes (unit mass); zero-weight points add nothing."""
+    x, y, a, b = _problem(6, 5, 2, 81)
+    eps = 0.5
+    f, g, _ = oracle.sinkhorn(x, y, a, b, eps, 3000, lib=lib)
+    pr, pc = oracle.primal(x, y, a, b, f, g, eps, lib=lib)
+    assert abs(pr - oracle.dual_cost(x, y, a, b, f, g, eps, lib=lib)) <= 1e-10 * max(1.0, abs(pr))
+    assert pc < pr  # the entropic term is positive here
+    x1, y1, a1, b1 = _problem(6, 1, 2, 31)
+    f1, g1, _ = oracle.sinkhorn(x1, y1, a1, b1, 0.37, 1, lib=lib)
+    pr1, pc1 = oracle.primal(x1, y1, a1, b1, f1, g1, 0.37, lib=lib)
+    C1 = ((x1 - y1[0]) ** 2).sum(1)
+    assert abs(pc1 - (a1 * C1).sum()) <= 1e-13 and abs(pr1 - pc1) <= 1e-13
+    # zero weights: dropping the weightless points changes neither value
+    xz, yz, az, bz = _problem(9, 7, 2, 64)
+    az[[1, 4]] = 0.0
+    bz[2] = 0.0
+    az, bz = az / az.sum(), bz / bz.sum()
+    fz, gz, _ = oracle.sinkhorn(xz, yz, az, bz, 0.4, 5, lib=lib)
+    keep_a, keep_b = az > 0, bz > 0
+    full = oracle.primal(xz, yz, az, bz, fz, gz, 0.4, lib=lib)
+    part = oracle.primal(xz[keep_a], yz[keep_b], az[keep_a], bz[keep_b], fz[keep_a], gz[keep_b], 0.4, lib=lib)
+    assert np.allclose(full, part, rtol=1e-13, atol=0)
 
 
 def pin_large_eps_limit(lib):
@@ -516,6 +579,10 @@ def test_sampled_rows_match_full():
 ORACLE_SRC = os.path.join(os.path.dirname(oracle.__file__), "sk_oracle.c")
 
 MUTANTS = {
+    "g_init_ignored": ("g[j] = g_init ? g_init[j] : 0.0;", "g[j] = 0.0;", 1),
+    "primal_kl_no_mass": ("double kl = p > 0.0 ? p * log(p / q) - p + q : q;",
+                          "double kl = p > 0.0 ? p * log(p / q) : 0.0;", 1),
+    "primal_kl_sign": ("obj += p * c + eps * kl;", "obj += p * c - eps * kl;", 1),
     "l1_cost": ("s += diff * diff;", "s += fabs(diff);", 1),
     "cost_sign": ("(pot[j] - sq_dist(p, key + j * d, d)) / eps", "(pot[j] + sq_dist(p, key + j * d, d)) / eps", 2),
     "weight_sign": ("/ eps + logw[j];", "/ eps - logw[j];", 4),
