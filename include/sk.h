@@ -136,6 +136,21 @@ int sk_solve(const float *x, const float *y, const float *a, const float *b,
              void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * sk_solve started from a given g instead of 0 (SLOT, Low-Level Solver API:
+ * the solver state is the pair of potentials, so a solve can continue from
+ * one).  The first row half-step reads g_init (m, device, cost units); it may
+ * alias g, which is then updated in place.  Running k1 iterations and then
+ * k2 more from the resulting g is the (k1 + k2)-iteration trajectory up to
+ * float32 rounding of the state handed over.  n_iters = 0 gives f = 0 and
+ * g = g_init.  Everything else (trace, workspace, errors, capture) as
+ * sk_solve.
+ */
+int sk_solve_warm(const float *x, const float *y, const float *a, const float *b,
+                  int64_t n, int64_t m, int32_t d, float eps, int32_t n_iters,
+                  const float *g_init, float *f, float *g, int32_t check_every,
+                  float *resid_trace, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * sk_solve without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same arguments, kernels, results and errors as
@@ -257,6 +272,26 @@ int sk_dual_cost(const float *x, const float *y, const float *a, const float *b,
                  int64_t n, int64_t m, int32_t d, float eps,
                  const float *f, const float *g, double *out,
                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Primal value of the plan at potentials (f, g) (SLOT, Basic Usage: the loss
+ * reports the primal value of the plan it reached),
+ *     P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps),
+ *     out[0] = <P, C> + eps KL(P | a x b),
+ *              KL(P | Q) = sum_ij P_ij log(P_ij / Q_ij) - P_ij + Q_ij,
+ *     out[1] = <P, C>, the transport cost of the plan.
+ * With log(P_ij / (a_i b_j)) = (f_i + g_j - C_ij)/eps, out[0] is computed as
+ * <P1, f> + <P^T 1, g> - eps (sum P - sum(a) sum(b)); it equals the dual
+ * objective (sk_dual_cost) at the optimum.  <P, C> comes from the per-row
+ * sums of P [y, |y|^2] in the centred expanded form.  Three streamed passes
+ * (for d > 8 four: a log-sum-exp pass first), P never stored; float64 sums in
+ * a fixed order.  `out` is 2 device doubles; ws of at least
+ * sk_transport_workspace_bytes(n, m, d) bytes.  Enqueues only.
+ */
+int sk_primal_cost(const float *x, const float *y, const float *a, const float *b,
+                   int64_t n, int64_t m, int32_t d, float eps,
+                   const float *f, const float *g, double *out,
+                   void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace bytes of sk_divergence (0 for invalid sizes). */
 size_t sk_divergence_workspace_bytes(int64_t n, int64_t m, int32_t d);

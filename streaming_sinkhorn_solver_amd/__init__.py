@@ -47,8 +47,11 @@ SIGNATURES = {
     "sk_check_inputs": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]),
     "sk_solve": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _vp, _vp, _i32, _vp, _vp, _sz,
                                 _vp]),
+    "sk_solve_warm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _vp, _vp, _vp, _i32, _vp,
+                                     _vp, _sz, _vp]),
     "sk_solve_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _i32, _vp, _vp, _i32, _vp,
                                         _vp]),
+    "sk_primal_cost": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sk_cost": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp]),
     "sk_marginal_residual": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _f32, _vp, _vp, _vp, _vp, _sz,
                                             _vp]),
@@ -240,6 +243,43 @@ def solve(x, y, a=None, b=None, *, eps: float, n_iters: int, check_every: int = 
                         int(check_every), _ptr(trace) if nt > 0 else None, _ptr(ws), ws.numel(),
                         _stream(x.device)), "sk_solve")
     return f, g, trace
+
+
+def solve_warm(x, y, a=None, b=None, *, eps: float, n_iters: int, g_init: torch.Tensor, check_every: int = 0,
+               ws: torch.Tensor | None = None, f: torch.Tensor | None = None, g: torch.Tensor | None = None,
+               trace: torch.Tensor | None = None, check: bool = True):
+    """The fixed-count solve of ``solve`` started from g = g_init (m,) instead of 0; g_init may be g itself
+    (continued in place).  Returns (f, g, resid_trace)."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    ws = _ws(ws, x.device, lambda: workspace(n, m, d, x.device))
+    if check:
+        check_inputs(x, y, a, b, ws)
+    g_init = _in(g_init, (m,), x.device, "g_init")
+    f = _buf(f, (n,), torch.float32, x.device, "f")
+    g = _buf(g, (m,), torch.float32, x.device, "g")
+    nt = n_iters // check_every if check_every > 0 else 0
+    if trace is None:
+        trace = torch.empty(max(nt, 0), dtype=torch.float32, device=x.device)
+    else:
+        trace = _at_least(trace, nt, torch.float32, x.device, "trace")
+    _raise(lib.sk_solve_warm(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), int(n_iters), _ptr(g_init),
+                             _ptr(f), _ptr(g), int(check_every), _ptr(trace) if nt > 0 else None, _ptr(ws),
+                             ws.numel(), _stream(x.device)), "sk_solve_warm")
+    return f, g, trace
+
+
+def primal_cost(x, y, a, b, f, g, *, eps: float, ws: torch.Tensor | None = None,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """[<P,C> + eps KL(P | a x b), <P,C>] of the plan at (f, g), as a 2-element float64 tensor."""
+    lib = load_library()
+    x, y, a, b, n, m, d = _as_problem(x, y, a, b)
+    ws = _ws(ws, x.device, lambda: transport_workspace(n, m, d, x.device))
+    f, g = _potentials(f, g, n, m, x.device)
+    out = _buf(out, (2,), torch.float64, x.device, "out")
+    _raise(lib.sk_primal_cost(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps), _ptr(f), _ptr(g), _ptr(out),
+                              _ptr(ws), ws.numel(), _stream(x.device)), "sk_primal_cost")
+    return out
 
 
 def solve_noalloc(x, y, a=None, b=None, *, eps: float, n_iters: int, f: torch.Tensor, g: torch.Tensor,
@@ -513,4 +553,4 @@ __all__ = ["timing_enable", "timing_read", "solve", "solve_ex", "gradient_flow",
            "transport_workspace", "cost", "dual_cost", "divergence",
            "divergence_workspace", "marginal_residual", "grad_x", "check_inputs", "workspace", "workspace_bytes",
            "load_library", "status_string", "SinkhornError", "LIB_PATH", "SIGNATURES", "VARIANTS", "STOP_MODES",
-           "solve_noalloc", "NOALLOC_SCRATCH_BYTES"]
+           "solve_noalloc", "NOALLOC_SCRATCH_BYTES", "solve_warm", "primal_cost"]

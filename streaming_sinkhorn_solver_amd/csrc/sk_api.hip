@@ -641,19 +641,25 @@ int solve_ex(const Ws& W, const float* x, const float* y, const float* a, const 
 }
 
 // Fixed-count alternating solve with the optional fused residual trace (sk_solve).
+// g_init (may be null, may alias g): the starting g of the iteration (0 when null).
 int solve_fixed(const Ws& W, const float* x, const float* y, const float* a, const float* b, float eps,
-                int n_iters, float* f, float* g, int check_every, float* resid_trace, hipStream_t s) {
+                int n_iters, float* f, float* g, int check_every, float* resid_trace, hipStream_t s,
+                const float* g_init = nullptr) {
     const Layout& L = W.L;
     const int64_t n = L.n, m = L.m;
     int st;
     if (n_iters == 0) {
         SK_TRY(launch_fill(f, n, 0.0f, s));
-        SK_TRY(launch_fill(g, m, 0.0f, s));
+        if (g_init == nullptr)
+            SK_TRY(launch_fill(g, m, 0.0f, s));
+        else if (g_init != g)
+            SK_TRY(hipMemcpyAsync(g, g_init, (size_t)m * sizeof(float), hipMemcpyDeviceToDevice, s));
         return SK_OK;
     }
     const int cap = pass_capacity(L.d);
     if (cap <= 0) return SK_ERR_HIP;
-    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 1, nullptr, s))) return st;
+    // the key biases of the first row pass encode the starting g; g itself is first written by a column pass
+    if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, g_init ? 2 : 1, g_init, s))) return st;
 
     PassArgs row = make_pass(W, true, eps, a, cap);
     row.fin.pot = f;
@@ -1371,6 +1377,56 @@ int sk_solve(const float* x, const float* y, const float* a, const float* b, int
     Ws W{L, static_cast<char*>(ws)};
     return solve_fixed(W, x, y, a, b, eps, n_iters, f, g, check_every, resid_trace,
                        reinterpret_cast<hipStream_t>(stream));
+}
+
+int sk_solve_warm(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+                  float eps, int32_t n_iters, const float* g_init, float* f, float* g, int32_t check_every,
+                  float* resid_trace, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !g_init || !f || !g) return SK_ERR_NULL;
+    int st = check_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    if (n_iters < 0) return SK_ERR_ITERS;
+    if (check_every < 0 || (check_every > 0 && n_iters / check_every > 0 && !resid_trace))
+        return SK_ERR_CHECK_EVERY;
+    const Layout L = make_layout(n, m, d);
+    if ((st = check_ws(ws, ws_bytes, L))) return st;
+    Ws W{L, static_cast<char*>(ws)};
+    return solve_fixed(W, x, y, a, b, eps, n_iters, f, g, check_every, resid_trace,
+                       reinterpret_cast<hipStream_t>(stream), g_init);
+}
+
+int sk_primal_cost(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m, int32_t d,
+                   float eps, const float* f, const float* g, double* out, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !a || !b || !f || !g || !out) return SK_ERR_NULL;
+    int st = check_transport_sizes(n, m, d);
+    if (st) return st;
+    if ((st = check_eps(eps))) return st;
+    const TLayout T = make_tlayout(n, m, d);
+    if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) % 256) != 0 || ws_bytes < T.total) return SK_ERR_WORKSPACE;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    Ws W{T.L, static_cast<char*>(ws)};
+    const Layout& L = T.L;
+    const int cap = pass_capacity(d);
+    if (cap <= 0) return SK_ERR_HIP;
+    if ((st = prepare(W, x, y, a, b, eps, 2, f, 2, g, s))) return st;
+    float* U = W.f(T.B);        // m x (d + 1): [y~_j, |y~_j|^2]
+    float* Tr = W.f(T.U);       // n x (d + 1): per-row sums of P U
+    float* r = W.f(T.diag);     // P 1
+    float* c = r + n;           // P^T 1
+    SK_TRY(launch_primal_payload(W.f(L.yp), L.P, d, W.f(L.ny), (int)m, U, s));
+    if (L.mfma) {
+        TimingPause pause;
+        if ((st = store_lse(W, true, eps, a, s))) return st;
+    }
+    if ((st = transport_cols(W, T, true, eps, U, d + 1, Tr, r, s))) return st;
+    PassArgs col = make_pass(W, false, eps, b, cap);
+    col.fin.mode = kFinMass;
+    col.fin.pot_in = g;
+    col.fin.rbuf = c;
+    if ((st = run_pass(W, col, s))) return st;
+    SK_TRY(launch_primal(a, b, f, g, r, c, W.f(L.xp), L.P, d, W.f(L.nx), Tr, (int)n, (int)m, eps, out, s));
+    return SK_OK;
 }
 
 int sk_solve_noalloc(const float* x, const float* y, const float* a, const float* b, int64_t n, int64_t m,

@@ -223,6 +223,60 @@ __global__ __launch_bounds__(1024) void k_cost(const float* __restrict__ a, cons
         out[0] = mass ? af + bg - (double)eps * (mp - sa * sb) : af + bg - (double)eps * sb * (1.0 - sa);
 }
 
+// Payload of the plan's transport cost: U_j = [y~_j (d values), |y~_j|^2], from the packed cloud.
+__global__ __launch_bounds__(kBlock) void k_primal_payload(const float* __restrict__ yp, int P, int d,
+                                                           const float* __restrict__ ny, int m,
+                                                           float* __restrict__ U) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= m) return;
+    float* u = U + (size_t)j * (d + 1);
+    for (int t = 0; t < d; ++t) u[t] = yp[(size_t)j * P + t];
+    u[d] = ny[j];
+}
+
+// Primal value of the plan P_ij = a_i b_j exp((f_i + g_j - C_ij)/eps) from its row sums r, column sums c
+// and per-row sums T_i = [sum_j P_ij y~_j, sum_j P_ij |y~_j|^2] (centred coordinates; C is unchanged by the
+// common shift).  With log(P_ij / (a_i b_j)) = (f_i + g_j - C_ij)/eps the generalised KL term collapses:
+//   out[0] = <P,C> + eps KL(P | a x b) = sum_i f_i r_i + sum_j g_j c_j - eps (sum_i r_i - sum(a) sum(b)),
+//   out[1] = <P,C> = sum_i (r_i |x~_i|^2 - 2 <x~_i, T_i> + T_i[d]).
+// One workgroup, float64 sums in a fixed order; rows and columns of zero weight carry no plan mass.
+__global__ __launch_bounds__(1024) void k_primal(const float* __restrict__ a, const float* __restrict__ b,
+                                                 const float* __restrict__ f, const float* __restrict__ g,
+                                                 const float* __restrict__ r, const float* __restrict__ c,
+                                                 const float* __restrict__ xp, int P, int d,
+                                                 const float* __restrict__ nx, const float* __restrict__ T,
+                                                 int n, int m, float eps, double* __restrict__ out) {
+    __shared__ double sh[1024];
+    double fr = 0.0, gc = 0.0, mp = 0.0, sa = 0.0, sb = 0.0, pc = 0.0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const float ai = a[i];
+        sa += (double)ai;
+        if (ai == 0.0f) continue;
+        const double ri = (double)r[i];
+        fr += (double)f[i] * ri;
+        mp += ri;
+        const float* t = T + (size_t)i * (d + 1);
+        double dot = 0.0;
+        for (int k = 0; k < d; ++k) dot += (double)xp[(size_t)i * P + k] * (double)t[k];
+        pc += ri * (double)nx[i] - 2.0 * dot + (double)t[d];
+    }
+    for (int j = threadIdx.x; j < m; j += blockDim.x) {
+        const float bj = b[j];
+        sb += (double)bj;
+        if (bj != 0.0f) gc += (double)g[j] * (double)c[j];
+    }
+    fr = block_sum_f64(fr, sh);
+    gc = block_sum_f64(gc, sh);
+    mp = block_sum_f64(mp, sh);
+    sa = block_sum_f64(sa, sh);
+    sb = block_sum_f64(sb, sh);
+    pc = block_sum_f64(pc, sh);
+    if (threadIdx.x == 0) {
+        out[0] = fr + gc - (double)eps * (mp - sa * sb);
+        out[1] = pc;
+    }
+}
+
 // Largest change of the potentials since the snapshot, then the snapshot is refreshed.
 // A check value may go to host memory: then `flag` (may be null) is set to
 // `seq` after it, behind a system-scope fence, so a host that sees the flag
@@ -348,6 +402,18 @@ hipError_t launch_pot_change(const float* f, float* sf, int n, const float* g, f
 hipError_t launch_cost_mass(const float* a, const float* b, const float* f, const float* g, const float* mass,
                             int n, int m, float eps, double* out, hipStream_t s) {
     hipLaunchKernelGGL(k_cost, dim3(1), dim3(1024), 0, s, a, b, f, g, mass, n, m, eps, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_primal_payload(const float* yp, int P, int d, const float* ny, int m, float* U, hipStream_t s) {
+    hipLaunchKernelGGL(k_primal_payload, dim3(grid_for(m, kBlock)), dim3(kBlock), 0, s, yp, P, d, ny, m, U);
+    return hipGetLastError();
+}
+
+hipError_t launch_primal(const float* a, const float* b, const float* f, const float* g, const float* r,
+                         const float* c, const float* xp, int P, int d, const float* nx, const float* T, int n,
+                         int m, float eps, double* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_primal, dim3(1), dim3(1024), 0, s, a, b, f, g, r, c, xp, P, d, nx, T, n, m, eps, out);
     return hipGetLastError();
 }
 

@@ -123,6 +123,29 @@ def test_noalloc_argument_errors(lib):
     assert lib.sk_workspace_bytes(16384, 16384, 64) <= limit and lib.sk_workspace_bytes(50000, 50000, 3) <= limit
 
 
+def test_warm_and_primal_argument_errors(lib):
+    wb = lib.sk_workspace_bytes(10, 12, 2)
+    tb = lib.sk_transport_workspace_bytes(10, 12, 2)
+
+    def warm(g_init=FAKE, n=10, iters=5, check_every=0, ws=FAKE, nbytes=wb):
+        return lib.sk_solve_warm(FAKE, FAKE, FAKE, FAKE, n, 12, 2, 0.1, iters, g_init, FAKE, FAKE, check_every,
+                                 None, ws, nbytes, None)
+
+    assert warm(g_init=None) == SK_ERR_NULL
+    assert warm(n=0) == SK_ERR_SHAPE
+    assert warm(iters=-1) == SK_ERR_ITERS
+    assert warm(check_every=1) == SK_ERR_CHECK_EVERY
+    assert warm(ws=None) == SK_ERR_WORKSPACE
+    assert warm(nbytes=wb - 1) == SK_ERR_WORKSPACE
+
+    def primal(out=FAKE, eps=0.1, nbytes=tb):
+        return lib.sk_primal_cost(FAKE, FAKE, FAKE, FAKE, 10, 12, 2, eps, FAKE, FAKE, out, FAKE, nbytes, None)
+
+    assert primal(out=None) == SK_ERR_NULL
+    assert primal(eps=0.0) == SK_ERR_EPS
+    assert primal(nbytes=wb) == SK_ERR_WORKSPACE  # needs the transport workspace
+
+
 def test_other_entry_points_argument_errors(lib):
     wb = lib.sk_workspace_bytes(10, 12, 2)
     assert lib.sk_cost(None, FAKE, FAKE, FAKE, 10, 12, 0.1, FAKE, None) == SK_ERR_NULL
