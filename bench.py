@@ -24,7 +24,13 @@ Printed (one JSON line):
                and the standalone two-pass marginal residual, with the solve's
                own pair-evals/s and iterations/s beside them;
   cpu_baseline the CPU oracle as it stands, timed on alternating iterations
-               of the same workload on this host (about 10 s of them).
+               of the same workload on this host (about 10 s of them);
+  extra        {"configs": [...]}: after the headline, one line per other
+               workload (EXTRA_CONFIGS), each timed the same way -- value,
+               iterations/s and the roofline of its pass kernel: the 1000-point
+               problem as HIP-graph replays, the 10k^2, 50k x 40k and d = 64
+               problems eagerly, and 2 of the 50 iterations of the 2^20-point
+               problem.
 
 Other steps (--mode, same workload and JSON fields; value counts the pair
 evaluations of the counted iterations only):
@@ -247,6 +253,8 @@ def main():
                     help="eps = n^(-2/3), the squared mean spacing of n points in the unit cube (the cluster_d3 "
                          "workload's rule) at the --size given")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the other workloads the default run times after the headline")
     ap.add_argument("--ceilings", action="store_true", help="run the issue-rate micro-benchmarks and exit")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step into a HIP graph and time its replays (kernel timing from an eager step)")
@@ -553,7 +561,99 @@ def main():
     }
     if not args.no_cpu_baseline and mode == "solve":
         out["cpu_baseline"] = cpu_baseline(x, y, a, b, eps, n, m)
+    if mode == "solve" and not args.graph and args.workload == "gmm8_d3_sq" and args.size is None \
+            and args.dim is None and args.iters is None and not args.no_extra_configs:
+        del X, Y, A, B, ws, f, g, grad
+        torch.cuda.empty_cache()
+        configs = []
+        for name, steps, use_graph, iters in EXTRA_CONFIGS:
+            configs.append(run_extra_config(name, steps, use_graph, iters, args.timing_stride))
+            print(f"extra config done: {name}", file=sys.stderr, flush=True)
+        out["extra"] = {"configs": configs}
     print(json.dumps(out), flush=True)
+
+
+# The other workloads, timed after the headline by the default run: (name, timed steps, HIP-graph replay,
+# iterations per step or None for the workload's own count).  The 2^20-point workload is timed on 2 of its
+# 50 iterations and the cost, without its gradient (a full step takes about 19 s); its entry says so.
+EXTRA_CONFIGS = [("gflow_d2", 20, True, None), ("gauss_d2", 5, False, None), ("gmm8_d3", 3, False, None),
+                 ("gauss_d64", 3, False, None), ("cluster_d3", 1, False, 2)]
+
+
+def run_extra_config(name: str, steps: int, graph: bool, iters, timing_stride: int) -> dict:
+    """One workload's step, as the default mode runs it (sk_solve with the workload's residual interval, sk_cost,
+    sk_grad_x when the workload has one), with one warm-up step; returns its line for extra.configs."""
+    import torch
+
+    import streaming_sinkhorn_solver_amd as sk
+    from sk_inputs import WORKLOADS, eps32, make_inputs
+
+    w = WORKLOADS[name]
+    n_iters = w.n_iters if iters is None else iters
+    eps = eps32(w.eps)
+    x, y, a, b = make_inputs(name)
+    n, m, d = x.shape[0], y.shape[0], x.shape[1]
+    dev = torch.device("cuda:0")
+    X, Y, A, B = (torch.from_numpy(v).to(dev) for v in (x, y, a, b))
+    ws = sk.workspace(n, m, d, dev)
+    f = torch.empty(n, dtype=torch.float32, device=dev)
+    g = torch.empty(m, dtype=torch.float32, device=dev)
+    ce = w.check_every if n_iters >= max(w.check_every, 1) else 0
+    trace = torch.empty(max(n_iters // ce, 1) if ce else 1, dtype=torch.float32, device=dev)
+    cost_out = torch.empty(1, dtype=torch.float64, device=dev)
+    grad = torch.empty((n, d), dtype=torch.float32, device=dev)
+    sk.check_inputs(X, Y, A, B, ws)
+
+    with_grad = w.grad and iters is None  # a step cut to a few iterations times the iterations alone
+
+    def step():
+        sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, check_every=ce, ws=ws, f=f, g=g, trace=trace, check=False)
+        sk.cost(A, B, f, g, eps=eps, out=cost_out)
+        if with_grad:
+            sk.grad_x(X, Y, A, B, g, eps=eps, ws=ws, out=grad)
+
+    step()
+    torch.cuda.synchronize()
+    sk.timing_enable(True, timing_stride)
+    cuda_graph = None
+    if graph:  # kernel durations from one eager step; the timed steps replay the graph
+        step()
+        torch.cuda.synchronize()
+        pass_ms, launches, pairs = sk.timing_read()
+        sk.timing_enable(False)
+        cuda_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cuda_graph):
+            step()
+        cuda_graph.replay()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        cuda_graph.replay() if cuda_graph is not None else step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    if cuda_graph is None:
+        pass_ms, launches, pairs = sk.timing_read()
+        sk.timing_enable(False)
+    avg_s = pass_ms * 1e-3 / launches
+    ppl = pairs / launches
+    if d <= 8:
+        roof = roofline_alu(d, ppl, avg_s)
+        roof["kernel"] = f"k_pass_small<{d}>" if ppl <= 2.0e6 else f"k_pass_valu<{d}>"
+        roof["traffic"] = load_traffic(f"{name}:pass", "valu")
+    else:
+        roof = roofline_split(d, ppl, avg_s)
+        roof["kernel"] = "k_pass_mfma<%d>" % packed_stride(d)
+        roof["traffic"] = load_traffic(f"{name}:pass", "mfma")
+    out = {"workload": name, "n": n, "m": m, "d": d, "eps": eps, "n_iters": n_iters, "check_every": ce,
+           "grad_x": bool(with_grad), "steps": steps, "hip_graph": graph, "ms_per_step": step_s * 1e3,
+           "value": 2.0 * n * m * n_iters / step_s, "unit": "pair-evals/s", "iters_per_s": n_iters / step_s,
+           "roofline": roof, "recipe": w.description}
+    if iters is not None:
+        out["note"] = (f"{n_iters} of the workload's {w.n_iters} iterations per timed step, with the cost and "
+                       f"without the gradient")
+    del X, Y, A, B, ws, f, g, grad
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(x, y, a, b, eps, n, m) -> dict:

@@ -186,7 +186,7 @@ def test_coarse_decisions_match_reference(eps, B, seed):
         "err/tol", err / (1e-4 * maxc))
     assert 1 < io["rounds"] < kw["max_rounds"]
     assert info["rounds"] == io["rounds"]
-    if io["checks"][-1] > np.finfo(np.float32).max:
+    if io["checks"][-1] > float(np.finfo(np.float32).max):
         assert info["last_check"] == np.inf
     else:
         assert abs(info["last_check"] - io["checks"][-1]) <= 0.05 * io["checks"][-1]

@@ -160,7 +160,8 @@ def test_hvp_translation_and_symmetry_at_size():
     got = host(out)
     want = 2 * a[:, None].astype(np.float64) * t
     say("translation: max err", np.abs(got - want).max(), "scale", np.abs(want).max(), "cg", float(host(res)[0]))
-    assert np.abs(got - want).max() <= 1e-3 * np.abs(want).max()
+    # observed 6e-6 relative (CG at its float32 floor)
+    assert np.abs(got - want).max() <= 1e-4 * np.abs(want).max()
     rng = np.random.default_rng(22)
     u = rng.normal(size=(20000, 3)).astype(np.float32)
     v = rng.normal(size=(20000, 3)).astype(np.float32)
@@ -168,4 +169,5 @@ def test_hvp_translation_and_symmetry_at_size():
     Hu, _ = sk.hvp(X, Y, A, B, F, G, dev(u)[0], eps=eps, cg_iters=100)
     lhs, rhs = float((u * host(Hv)).sum()), float((v * host(Hu)).sum())
     say("symmetry", lhs, rhs)
-    assert abs(lhs - rhs) <= 1e-3 * max(abs(lhs), abs(rhs))
+    # observed 1e-6 relative
+    assert abs(lhs - rhs) <= 2e-5 * max(abs(lhs), abs(rhs))
