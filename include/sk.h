@@ -443,11 +443,12 @@ int sk_fs2_solve(const float *x, const float *y, const float *a, const float *b,
 
 /*
  * Kernel timing of the streamed log-sum-exp passes (benchmark diagnostics).
- * sk_timing_enable(k) with k >= 1 resets the counters and from then on records
- * a HIP event pair on the launch stream around every k-th streamed-pass kernel
- * that the entry points enqueue (k = 1: every one; a larger k keeps the host
+ * sk_timing_enable(k) with k >= 1 resets the counters and from then on times
+ * every k-th streamed-pass kernel that the entry points enqueue with a HIP
+ * event pair recorded with the kernel's own dispatch (hipExtLaunchKernel: the
+ * pair spans the kernel alone) (k = 1: every one; a larger k keeps the host
  * cost of the events off small problems); the split merge and the other
- * kernels are outside the pairs.  Auxiliary passes are left out so that the
+ * kernels are not timed.  Auxiliary passes are left out so that the
  * timed launches are of one kernel: the store-lse passes of the transport
  * products and the Hessian-vector product, the HVP's products outside its
  * conjugate-gradient steps, and the coarse stage of sk_fs2_solve (whose timed

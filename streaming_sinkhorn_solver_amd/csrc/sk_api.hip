@@ -87,7 +87,7 @@ int rows_per_block(int d) {
 
 // Key-range split of the gradient pass (a plain split grid: it runs once per solve).
 Split grad_split(int64_t n, int64_t m, int d) {
-    return split_for(n, m, d <= kValuMaxD ? valu_rows_per_block() : mfma_grad_rows_per_block());
+    return split_for(n, m, d <= kValuMaxD ? valu_block_rows() : mfma_grad_rows_per_block());
 }
 
 // Upper bound on the workgroups of a streamed pass, from the sizes alone (the
@@ -1198,7 +1198,7 @@ int check_fs2(int64_t n, int64_t m, int32_t d, const Fs2Opts& o) {
     int st = check_sizes(n, m, d);
     if (st) return st;
     if (d > kValuMaxD) return SK_ERR_UNSUPPORTED_D;
-    if (o.B < 1 || o.B > valu_rows_per_block()) return SK_ERR_SHAPE;
+    if (o.B < 1 || o.B > valu_block_rows()) return SK_ERR_SHAPE;
     const int64_t nbx = (n + o.B - 1) / o.B, nby = (m + o.B - 1) / o.B;
     if (nbx * nby > kMaxTiles) return SK_ERR_SHAPE;
     if (o.delta <= 0.0f && nbx * nby > kMaxKeptTiles) return SK_ERR_SHAPE;  // delta 0 keeps every tile

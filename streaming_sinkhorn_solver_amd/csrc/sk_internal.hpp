@@ -20,10 +20,23 @@
 // expanded form loses little to fp32 cancellation.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
+
+// Launches a kernel; when the event pair e0 / e1 is given, the two events take
+// the kernel's own start and end times, recorded with its dispatch (no marker
+// packets of their own that would lengthen the measured interval of a short
+// kernel).  Timed launches never occur under graph capture.
+#define SK_LAUNCH_TIMED(kernel, grid, block, stream, e0, e1, ...)                                \
+    do {                                                                                          \
+        if (e0)                                                                                   \
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0, __VA_ARGS__);        \
+        else                                                                                      \
+            hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);                      \
+    } while (0)
 
 namespace sk {
 
@@ -304,7 +317,8 @@ hipError_t launch_resid_reduce(const float* rbuf, int cnt, float* out_max, float
 hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t ev0 = nullptr,
                             hipEvent_t ev1 = nullptr);
 hipError_t launch_grad_valu(const GradArgs& a, hipStream_t s);
-int valu_rows_per_block();
+int valu_rows_per_block();  // rows per row block of the dense pass
+int valu_block_rows();      // rows per workgroup of the gradient and block-sparse passes
 // Block-sparse vector-ALU pass (B <= 512 rows per query block).
 hipError_t launch_pass_sparse(const SparseArgs& a, int d, hipStream_t s, hipEvent_t ev0 = nullptr,
                               hipEvent_t ev1 = nullptr);

@@ -843,9 +843,7 @@ hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t
     constexpr int KA = (MODE == 1 || MODE == 2) ? P : 16 * NP;
     constexpr int rpb = kWaves * 16 * transport_nqb(P, NP, MODE);
     dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
-    if (ev0) (void)hipEventRecord(ev0, s);
-    hipLaunchKernelGGL((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), 0, s, a);
-    if (ev1) (void)hipEventRecord(ev1, s);
+    SK_LAUNCH_TIMED((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), s, ev0, ev1, a);
     if (a.nsplit > 1)
         hipLaunchKernelGGL(k_transport_mfma_merge, dim3((unsigned)(((int64_t)a.nq * (a.kout + 1) + kBlock - 1) / kBlock)),
                            dim3(kBlock), 0, s, a, KA);
@@ -867,10 +865,8 @@ hipError_t launch_transport_mfma_pp(const TransArgs& a, int mode, int kwidth, hi
 
 template <int P>
 hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (ev0) (void)hipEventRecord(ev0, s);
     if (!a.kb) return hipErrorInvalidValue;  // the split keys are written by every solver set-up
-    hipLaunchKernelGGL(k_pass_mfma<P>, dim3(a.W), dim3(kBlock), 0, s, a);
-    if (ev1) (void)hipEventRecord(ev1, s);
+    SK_LAUNCH_TIMED(k_pass_mfma<P>, dim3(a.W), dim3(kBlock), s, ev0, ev1, a);
     return launch_merge(a, s);
 }
 

@@ -65,51 +65,114 @@ __device__ __forceinline__ void stage_tile(float4* tile, const float4* __restric
     }
 }
 
+// One chunk of kTJ keys, read from an LDS tile at key offset c (broadcast:
+// every lane reads the same key), against the R query rows each lane holds:
+// scores, one running-max update per row and the rescaled sum (base 2).
+template <int D>
+__device__ __forceinline__ void lse_chunk(const float4* tile, int c, const float (&q)[kR][D], float (&M)[kR],
+                                          float (&S)[kR]) {
+    constexpr int P = ((D + 1 + 3) / 4) * 4;
+    constexpr int V = P / 4;
+    float kk[kTJ][P];
+#pragma unroll
+    for (int t = 0; t < kTJ; ++t)
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const float4 v = tile[(c + t) * V + u];
+            kk[t][4 * u + 0] = v.x;
+            kk[t][4 * u + 1] = v.y;
+            kk[t][4 * u + 2] = v.z;
+            kk[t][4 * u + 3] = v.w;
+        }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+        float s[kTJ];
+#pragma unroll
+        for (int t = 0; t < kTJ; ++t) {
+            float acc = kk[t][D];
+#pragma unroll
+            for (int dd = 0; dd < D; ++dd) acc = fmaf(q[r][dd], kk[t][dd], acc);
+            s[t] = acc;
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int t = 1; t < kTJ; ++t) mt = fmaxf(mt, s[t]);
+        const float mn = fmaxf(M[r], mt);
+        float acc = S[r] * ex2(M[r] - mn);
+#pragma unroll
+        for (int t = 0; t < kTJ; ++t) acc += ex2(s[t] - mn);
+        S[r] = acc;
+        M[r] = mn;
+    }
+}
+
 // Streams keys [j0, j1) past the R query rows each lane holds, updating the
-// running max M and rescaled sum S of every row (base 2).
+// running max M and rescaled sum S of every row (base 2).  The whole
+// workgroup stages each tile (the block-sparse pass, whose lanes hold
+// kBlock * kR rows).
 template <int D>
 __device__ __forceinline__ void scan_keys(float4* tile, const float4* __restrict__ kp, const float (&q)[kR][D],
                                           float (&M)[kR], float (&S)[kR], int j0, int j1) {
-    constexpr int P = ((D + 1 + 3) / 4) * 4;
-    constexpr int V = P / 4;
     for (int base = j0; base < j1; base += kTL) {
         __syncthreads();
         stage_tile<D>(tile, kp, base, j1);
         __syncthreads();
         const int ntile = min(kTL, j1 - base);
-        for (int c = 0; c < ntile; c += kTJ) {
-            float kk[kTJ][P];
+        for (int c = 0; c < ntile; c += kTJ) lse_chunk<D>(tile, c, q, M, S);
+    }
+}
+
+// Keys per wave-private LDS tile of the dense pass: at most 256 float4 (4 KB)
+// whatever d, a multiple of 64 keys (whole chunks, so a chunk never reads past
+// the tile, and whole float4s per lane when the wave stages it).
+template <int D>
+constexpr int wave_tile_keys() {
+    return 256 / (((D + 1 + 3) / 4) * 4 / 4) / 64 * 64;
+}
+static_assert(wave_tile_keys<8>() == 64 && wave_tile_keys<4>() == 128 && wave_tile_keys<3>() == 256, "tiles");
+static_assert(64 % kTJ == 0, "a tile holds whole chunks");
+
+// Orders one wave's LDS stores before its later LDS loads.  The lanes of a
+// wave issue LDS instructions in program order and the LDS performs them in
+// order, so no hardware barrier is needed; the fences keep the compiler from
+// moving the loads above the stores.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The same scan by one wave alone, through its own LDS tile: keys past j1 are
+// staged with zero coordinates and bias -inf and add exactly nothing.
+template <int D>
+__device__ __forceinline__ void scan_keys_wave(float4* tile, const float4* __restrict__ kp, const float (&q)[kR][D],
+                                               float (&M)[kR], float (&S)[kR], int j0, int j1, int lane) {
+    constexpr int P = ((D + 1 + 3) / 4) * 4;
+    constexpr int V = P / 4;
+    constexpr int TK = wave_tile_keys<D>();
+    static_assert((TK * V) % 64 == 0, "a tile is whole float4s per lane");
+    for (int base = j0; base < j1; base += TK) {
+        wave_lds_sync();
+        // all of a lane's loads in flight at once: clamped addresses, padding selected afterwards
+        float4 v[TK * V / 64];
 #pragma unroll
-            for (int t = 0; t < kTJ; ++t)
-#pragma unroll
-                for (int u = 0; u < V; ++u) {
-                    const float4 v = tile[(c + t) * V + u];
-                    kk[t][4 * u + 0] = v.x;
-                    kk[t][4 * u + 1] = v.y;
-                    kk[t][4 * u + 2] = v.z;
-                    kk[t][4 * u + 3] = v.w;
-                }
-#pragma unroll
-            for (int r = 0; r < kR; ++r) {
-                float s[kTJ];
-#pragma unroll
-                for (int t = 0; t < kTJ; ++t) {
-                    float acc = kk[t][D];
-#pragma unroll
-                    for (int dd = 0; dd < D; ++dd) acc = fmaf(q[r][dd], kk[t][dd], acc);
-                    s[t] = acc;
-                }
-                float mt = s[0];
-#pragma unroll
-                for (int t = 1; t < kTJ; ++t) mt = fmaxf(mt, s[t]);
-                const float mn = fmaxf(M[r], mt);
-                float acc = S[r] * ex2(M[r] - mn);
-#pragma unroll
-                for (int t = 0; t < kTJ; ++t) acc += ex2(s[t] - mn);
-                S[r] = acc;
-                M[r] = mn;
-            }
+        for (int k = 0; k < TK * V / 64; ++k) {
+            const int e = lane + 64 * k;
+            const int col = min(base + e / V, j1 - 1);
+            v[k] = kp[(size_t)col * V + e % V];
         }
+#pragma unroll
+        for (int k = 0; k < TK * V / 64; ++k) {
+            const int e = lane + 64 * k;
+            if (base + e / V >= j1) {
+                v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (e % V == D / 4) reinterpret_cast<float*>(&v[k])[D % 4] = -INFINITY;
+            }
+            tile[e] = v[k];
+        }
+        wave_lds_sync();
+        const int ntile = min(TK, j1 - base);
+        for (int c = 0; c < ntile; c += kTJ) lse_chunk<D>(tile, c, q, M, S);
     }
 }
 
@@ -202,11 +265,38 @@ __global__ __launch_bounds__(kBlock) void k_sparse_merge(SparseArgs A) {
     finalize(A.fin, i, M + lg2(S));
 }
 
+// The dense pass.  A row block is the kPassRows = 64 R rows of one wave's
+// lanes, and all kWaves waves of a workgroup hold the same rows: each wave
+// scans a chunk-aligned quarter of the segment's keys through its own LDS
+// tile (no workgroup barrier inside the scan), then the waves' (M, S) are
+// merged through LDS and one thread per row finishes the row or writes its
+// partial.  Sharing rows across the waves cuts the partials a stream-K range
+// leaves, and the merge that reads them, by kWaves against a workgroup of
+// kWaves * 64 R distinct rows, for the same work per lane.
+constexpr int kWaves = kBlock / 64;
+constexpr int kPassRows = 64 * kR;
+
+// Occupancy asked of the compiler (waves per SIMD).  Left to itself it
+// schedules the chunk loop for 5 waves at d = 2, 3 (87 and 95 VGPRs); held to
+// 7 (72 VGPRs) it spills a few values of the segment setup, none inside the
+// key loop.  Measured at 50,000^2, d = 3: 91.1 ms per 100-iteration solve at
+// 5 waves, against 88.1 ms for the block-wide kernel this one replaced.  The
+// larger d keep the occupancy that kernel had.
 template <int D>
-__global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
+constexpr int pass_min_waves() {
+    return D <= 3 ? 7 : (D == 4 ? 5 : (D <= 7 ? 4 : 3));
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(pass_min_waves<D>(), 8)))
+void k_pass_valu(PassArgs A) {
     constexpr int P = ((D + 1 + 3) / 4) * 4;
-    __shared__ float4 tile[kTL * (P / 4)];
+    constexpr int V = P / 4;
+    constexpr int TK = wave_tile_keys<D>();
+    __shared__ float4 tiles[kWaves][TK * V];
+    __shared__ float2 red[kWaves][kPassRows];
     const float4* kp = reinterpret_cast<const float4*>(A.k);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
     const int w = blockIdx.x;
     const int64_t lo = range_lo(w, A.total, A.W), hi = range_lo(w + 1, A.total, A.W);
@@ -214,13 +304,13 @@ __global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
         const int rb = (int)(u / A.nk);
         const int j0 = (int)(u - (int64_t)rb * A.nk);
         const int j1 = (int)min<int64_t>((int64_t)A.nk, (int64_t)j0 + (hi - u));
-        const int row0 = rb * A.rpb + threadIdx.x;
+        const int row0 = rb * kPassRows + lane;
 
         float q[kR][D];
         float M[kR], S[kR];
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
-            const int i = row0 + r * kBlock;
+            const int i = row0 + r * 64;
             const int ic = i < A.nq ? i : A.nq - 1;
             const float* qr = A.q + (size_t)ic * P;
 #pragma unroll
@@ -228,19 +318,32 @@ __global__ __launch_bounds__(kBlock) void k_pass_valu(PassArgs A) {
             M[r] = kNegBig;
             S[r] = 0.0f;
         }
-        scan_keys<D>(tile, kp, q, M, S, j0, j1);
-
-        const bool complete = (j0 == 0 && j1 == A.nk);
-        float2* slot = A.part + ((size_t)w * 2 + (u == lo ? 0 : 1)) * A.rpb;
+        // this wave's share of [j0, j1): whole chunks, the last wave taking the remainder
+        const int per = (j1 - j0 + kWaves * kTJ - 1) / (kWaves * kTJ) * kTJ;
+        const int wj0 = min(j1, j0 + wave * per), wj1 = min(j1, wj0 + per);
+        scan_keys_wave<D>(tiles[wave], kp, q, M, S, wj0, wj1, lane);
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
-            const int i = row0 + r * kBlock;
-            if (i >= A.nq) continue;
-            if (complete)
-                finalize(A.fin, i, M[r] + lg2(S[r]));
-            else
-                slot[r * kBlock + threadIdx.x] = make_float2(M[r], S[r]);
+        for (int r = 0; r < kR; ++r) red[wave][lane + r * 64] = make_float2(M[r], S[r]);
+        __syncthreads();
+        if (threadIdx.x < kPassRows) {
+            const int lr = threadIdx.x;
+            float m = red[0][lr].x, sum = red[0][lr].y;
+#pragma unroll
+            for (int k = 1; k < kWaves; ++k) {
+                const float2 p = red[k][lr];
+                const float mn = fmaxf(m, p.x);
+                sum = sum * ex2(m - mn) + p.y * ex2(p.x - mn);
+                m = mn;
+            }
+            const int i = rb * kPassRows + lr;
+            if (i < A.nq) {
+                if (j0 == 0 && j1 == A.nk)
+                    finalize(A.fin, i, m + lg2(sum));
+                else
+                    A.part[((size_t)w * 2 + (u == lo ? 0 : 1)) * A.rpb + lr] = make_float2(m, sum);
+            }
         }
+        __syncthreads();  // red is rewritten by the next segment
         u += j1 - j0;
     }
 }
@@ -522,14 +625,11 @@ __global__ __launch_bounds__(kBlock) void k_grad_merge(GradArgs A) {
 
 template <int D>
 hipError_t launch_pass_d(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (ev0) (void)hipEventRecord(ev0, s);
     if (a.small) {
-        hipLaunchKernelGGL(k_pass_small<D>, dim3((a.nq + kSmallRows - 1) / kSmallRows), dim3(kBlock), 0, s, a);
-        if (ev1) (void)hipEventRecord(ev1, s);
+        SK_LAUNCH_TIMED(k_pass_small<D>, dim3((a.nq + kSmallRows - 1) / kSmallRows), dim3(kBlock), s, ev0, ev1, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_pass_valu<D>, dim3(a.W), dim3(kBlock), 0, s, a);
-    if (ev1) (void)hipEventRecord(ev1, s);
+    SK_LAUNCH_TIMED(k_pass_valu<D>, dim3(a.W), dim3(kBlock), s, ev0, ev1, a);
     return launch_merge(a, s);
 }
 
@@ -554,7 +654,8 @@ hipError_t launch_grad_d(const GradArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int valu_rows_per_block() { return kBlock * kR; }
+int valu_rows_per_block() { return kPassRows; }
+int valu_block_rows() { return kBlock * kR; }
 
 hipError_t launch_merge(const PassArgs& a, hipStream_t s) {
     const int64_t n_row_blocks = a.total / a.nk;
@@ -594,9 +695,7 @@ hipError_t launch_pass_valu(const PassArgs& a, int d, hipStream_t s, hipEvent_t 
 
 template <int D>
 hipError_t launch_sparse_d(const SparseArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (ev0) (void)hipEventRecord(ev0, s);
-    hipLaunchKernelGGL(k_pass_sparse<D>, dim3(a.W), dim3(kBlock), 0, s, a);
-    if (ev1) (void)hipEventRecord(ev1, s);
+    SK_LAUNCH_TIMED(k_pass_sparse<D>, dim3(a.W), dim3(kBlock), s, ev0, ev1, a);
     hipLaunchKernelGGL(k_sparse_merge, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }

@@ -194,9 +194,7 @@ hipError_t launch_t(const TransArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_
     constexpr int KA = MODE == 0 ? K : D;
     const int rpb = kBlock * kTR;
     dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
-    if (ev0) (void)hipEventRecord(ev0, s);
-    hipLaunchKernelGGL((k_transport<D, K, MODE>), grid, dim3(kBlock), 0, s, a);
-    if (ev1) (void)hipEventRecord(ev1, s);
+    SK_LAUNCH_TIMED((k_transport<D, K, MODE>), grid, dim3(kBlock), s, ev0, ev1, a);
     if (a.nsplit > 1)
         hipLaunchKernelGGL(k_transport_merge<KA>, dim3((a.nq + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
     return hipGetLastError();
