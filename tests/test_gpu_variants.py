@@ -306,3 +306,59 @@ def test_nan_state_is_not_reported_converged(rule):
     assert np.isnan(host(tr)).all()
     r = host(sk.marginal_residual(X, Y, A, B, f, g, eps=eps))
     assert np.isnan(r[0]) or np.isnan(r[1])
+
+
+# ------------------------------------------------------------------ the process-wide pools under concurrent calls
+def test_concurrent_calls_from_two_threads():
+    """The library keeps two process-wide pools: pinned host slots for stop-rule check values and the events of
+    the pass timing.  Calls from two host threads at once, each on its own stream, with stop rules (both the
+    deferred and the immediate check path) and timing on, must return exactly what the same calls return one
+    after the other."""
+    import threading
+
+    # two stop at their first check, two run to the cap
+    cases = [(1300, 1100, 3, 61, "marginal", 1e30), (2200, 2000, 2, 62, "potential", 1e-9),
+             (900, 700, 64, 63, "marginal", 0.0), (1500, 1600, 3, 64, "potential", 1e30)]
+    probs = []
+    for n, m, d, seed, rule, tol in cases:
+        x, y, a, b = random_problem(n, m, d, seed, shift=0.3)
+        probs.append((dev(x, y, a, b), rule, tol, eps32(0.1 if d < 64 else 0.5)))
+
+    def run(k, out):
+        (X, Y, A, B), rule, tol, eps = probs[k]
+        f, g, it, conv, viol = sk.solve_ex(X, Y, A, B, eps=eps, stop_mode=rule, stop_tol=tol, max_iter=60,
+                                           check_every=5)
+        torch.cuda.current_stream().synchronize()
+        out[k] = (f.cpu().numpy(), g.cpu().numpy(), it, conv, viol)
+
+    seq = {}
+    for k in range(len(cases)):
+        run(k, seq)
+    torch.cuda.synchronize()
+    sk.timing_enable(True, 1)
+    par, errs = {}, []
+
+    def worker(ks):
+        try:
+            with torch.cuda.stream(torch.cuda.Stream()):
+                for k in ks:
+                    run(k, par)
+        except Exception as e:  # surfaced below
+            errs.append(e)
+
+    threads = [threading.Thread(target=worker, args=([0, 2],)), threading.Thread(target=worker, args=([1, 3],))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    _, launches, _ = sk.timing_read()
+    sk.timing_enable(False)
+    assert not errs and all(not t.is_alive() for t in threads)
+    assert launches > 0
+    for k in range(len(cases)):
+        fs, gs, its, cs, vs = seq[k]
+        fp, gp, itp, cp, vp = par[k]
+        say("concurrent", cases[k], its, itp)
+        assert its == itp and cs == cp and vs == vp
+        assert its == (5 if cases[k][5] > 1.0 else 60)
+        assert np.array_equal(fs, fp) and np.array_equal(gs, gp)
