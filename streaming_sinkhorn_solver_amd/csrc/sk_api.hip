@@ -91,13 +91,36 @@ Split grad_split(int64_t n, int64_t m, int d) {
 }
 
 // Upper bound on the workgroups of a streamed pass, from the sizes alone (the
-// workspace is sized with it): at most kMaxGroups, each with >= kMinKeysPerGroup keys.
-int64_t groups_bound(int64_t nq, int64_t nk, int rpb) {
+// workspace is sized with it): at most kMaxGroups (kMaxGroupsValu for the
+// vector-ALU pass, d <= 8), each with >= kMinKeysPerGroup keys.
+int64_t groups_bound(int64_t nq, int64_t nk, int rpb, bool valu) {
     const int64_t total = (nq + rpb - 1) / rpb * nk;
     int64_t w = (total + kMinKeysPerGroup - 1) / kMinKeysPerGroup;
-    w = std::min<int64_t>(w, kMaxGroups);
+    w = std::min<int64_t>(w, valu ? kMaxGroupsValu : kMaxGroups);
     w = std::min<int64_t>(w, ((int64_t)1 << 62) / total);  // keeps w * total in int64
     return std::max<int64_t>(w, 1);
+}
+
+// Workgroups of a streamed pass.  The matrix-core pass takes one resident
+// round (capacity).  The vector-ALU pass takes a whole number of resident
+// rounds: one more for every kRoundKeys (row block, key) units that a single
+// round would give each workgroup, at most kValuRounds.  Short problems keep
+// one round (more ranges would only add partials and merge work); long ones
+// run several rounds of shorter ranges, which the hardware hands out as slots
+// free up.  A fractional round would leave a ragged last one.  Measured per
+// 100-iteration solve at d = 3 (ms): 30,000^2 33.6 with one round, 33.1 with
+// two, 35.6 with 1.3; 50,000^2 88.6 / 86.6 / 85.9 / 86.3 with 1 / 2 / 3 / 4;
+// 50,000 x 40,000 71.4 / 70.1 / 69.5 / 70.0; 100,000^2 347.5 against 334.8
+// with 4; 10,000^2 at d = 2 (200 iterations) 10.9 against 11.9 with 2.
+int pass_groups(int64_t nq, int64_t nk, int rpb, int capacity, bool valu) {
+    const int64_t bound = groups_bound(nq, nk, rpb, valu);
+    const int64_t cap = std::max(capacity, 1);
+    int64_t rounds = 1;
+    if (valu) {
+        const int64_t total = (nq + rpb - 1) / rpb * nk;
+        rounds = std::min<int64_t>(std::max<int64_t>(total / (cap * kRoundKeys), 1), kValuRounds);
+    }
+    return (int)std::min<int64_t>(bound, rounds * cap);
 }
 
 // Workgroups the GPU holds at once for the d-dimensional pass, per device.
@@ -175,7 +198,7 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
     const int64_t nq = row_side ? L.n : L.m, nk = row_side ? L.m : L.n;
     p.rpb = rows_per_block(L.d);
     p.total = (nq + p.rpb - 1) / p.rpb * nk;
-    p.W = (int)std::min<int64_t>(groups_bound(nq, nk, p.rpb), std::max(capacity, 1));
+    p.W = pass_groups(nq, nk, p.rpb, capacity, !L.mfma);
     p.q = W.f(row_side ? L.xp : L.yp);
     p.k = W.f(row_side ? L.yp : L.xp);
     p.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
@@ -216,7 +239,7 @@ void retarget(PassArgs& p, const float* q, int64_t nq, const float* k, int64_t n
     p.nq = (int)nq;
     p.nk = (int)nk;
     p.total = (nq + p.rpb - 1) / p.rpb * nk;
-    p.W = (int)std::min<int64_t>(groups_bound(nq, nk, p.rpb), std::max(capacity, 1));
+    p.W = pass_groups(nq, nk, p.rpb, capacity, !p.kbias);
     p.small = (!(p.kbias) && (double)nq * (double)nk <= kSmallPairs) ? 1 : 0;
 }
 
@@ -325,7 +348,8 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.rbuf = take(umx * 4);
     const int rpb = rows_per_block(d);
     const Split sr = grad_split(n, m, d);
-    const size_t stream_k = (size_t)std::max(groups_bound(n, m, rpb), groups_bound(m, n, rpb)) * 2 * rpb;
+    const bool valu = d <= kValuMaxD;
+    const size_t stream_k = (size_t)std::max(groups_bound(n, m, rpb, valu), groups_bound(m, n, rpb, valu)) * 2 * rpb;
     const size_t part_rows = std::max((size_t)sr.nsplit * un, stream_k);
     L.part = take(part_rows * sizeof(float2));
     L.partA = take(sr.nsplit > 1 ? (size_t)sr.nsplit * un * P * 4 : 0);

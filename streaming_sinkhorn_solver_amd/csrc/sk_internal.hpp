@@ -48,7 +48,10 @@ constexpr int kMaxD = 256;
 constexpr int kValuMaxD = 8;              // d <= 8: vector-ALU kernels; else matrix cores
 constexpr int kRedBlocks = 512;           // fixed partial count of the 2-stage reductions
 constexpr int kMaxSplit = 64;             // column splits of one gradient pass
-constexpr int kMaxGroups = 2048;          // workgroups of one streamed pass (upper bound)
+constexpr int kMaxGroups = 2048;          // workgroups of one matrix-core streamed pass (upper bound)
+constexpr int kMaxGroupsValu = 8192;      // workgroups of one vector-ALU streamed pass (upper bound)
+constexpr int kValuRounds = 4;            // resident rounds of workgroups a vector-ALU pass may take
+constexpr int kRoundKeys = 1800;          // per-workgroup units of one round that call for another round
 #ifndef SK_MIN_KEYS
 #define SK_MIN_KEYS 64
 #endif

@@ -75,6 +75,119 @@ __global__ __launch_bounds__(256) void k_mix(float* out, int iters, float k0, fl
     out[blockIdx.x * blockDim.x + threadIdx.x] = r;
 }
 
+// NF FMAs and NE exp2 per chain and step, on independent chains (the exp2
+// chains never feed the FMA chains): does a v_exp_f32 take a vector-ALU issue
+// slot of its own, or does it run beside the FMAs?  Compare (6, 1) with (6, 0)
+// and (7, 0).
+template <int NF, int NE>
+__global__ __launch_bounds__(256) void k_fma_exp(float* out, int iters, float a, float b) {
+    float v[kChains], e[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+        v[c] = threadIdx.x * 1e-3f + c;
+        e[c] = threadIdx.x * 1e-4f + c * 0.1f;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+#pragma unroll
+                for (int f = 0; f < NF; ++f) v[c] = fmaf(v[c], a, b);
+#pragma unroll
+                for (int x = 0; x < NE; ++x) e[c] = __builtin_amdgcn_exp2f(-e[c]);
+            }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += v[c] + e[c];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The same with the exp2 in its plain (VOP1) form, as the streamed passes issue
+// it: the chain e <- exp2(e) carries no source modifier (its values run to
+// +inf, which the units process at full rate).
+template <int NF, int NE>
+__global__ __launch_bounds__(256) void k_fma_exp_plain(float* out, int iters, float a, float b) {
+    float v[kChains], e[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+        v[c] = threadIdx.x * 1e-3f + c;
+        e[c] = threadIdx.x * 1e-4f + c * 0.1f;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+#pragma unroll
+                for (int f = 0; f < NF; ++f) v[c] = fmaf(v[c], a, b);
+#pragma unroll
+                for (int x = 0; x < NE; ++x) e[c] = __builtin_amdgcn_exp2f(e[c]);
+            }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += v[c] + e[c];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// (6, 1) with the scheduler told to interleave: each chain step is issued as
+// six FMAs then one exp2 (left alone, the compiler gathers all exp2 of an
+// unrolled step into one block, and a block of back-to-back exp2 runs at the
+// transcendental unit's half rate with nothing beside it).  In the streamed
+// passes the exp2 sit between the subtracts, adds and FMAs, as here.
+__global__ __launch_bounds__(256) void k_fma_exp_interleaved(float* out, int iters, float a, float b) {
+    float v[kChains], e[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+        v[c] = threadIdx.x * 1e-3f + c;
+        e[c] = threadIdx.x * 1e-4f + c * 0.1f;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+#pragma unroll
+                for (int f = 0; f < 6; ++f) v[c] = fmaf(v[c], a, b);
+                e[c] = __builtin_amdgcn_exp2f(e[c]);
+            }
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+                __builtin_amdgcn_sched_group_barrier(0x0002, 6, 0);  // six VALU
+                __builtin_amdgcn_sched_group_barrier(0x0400, 1, 0);  // one TRANS
+            }
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += v[c] + e[c];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// Six fp32 operations of one kind per chain step on independent chains
+// (OP 0 add, 1 subtract, 2 multiply): the issue cost of the non-FMA
+// instructions of a pass, against k_fma_exp<6, 0>.
+template <int OP>
+__global__ __launch_bounds__(256) void k_valu_op(float* out, int iters, float a, float b) {
+    float v[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) v[c] = threadIdx.x * 1e-3f + c;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c)
+#pragma unroll
+                for (int f = 0; f < 6; ++f) v[c] = OP == 0 ? v[c] + b : (OP == 1 ? v[c] - a : v[c] * a);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += v[c];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 
@@ -199,6 +312,28 @@ int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
         hipLaunchKernelGGL(k_mfma_bf16, dim3(blocks), dim3(256), 0, s, out, iters);
     else if (kind == 6)
         hipLaunchKernelGGL(k_mfma_bf16_valu, dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 7)
+        hipLaunchKernelGGL((k_fma_exp<6, 0>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 8)
+        hipLaunchKernelGGL((k_fma_exp<6, 1>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 9)
+        hipLaunchKernelGGL((k_fma_exp<7, 0>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 10)
+        hipLaunchKernelGGL((k_fma_exp<4, 1>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 11)
+        hipLaunchKernelGGL((k_fma_exp<2, 1>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 12)
+        hipLaunchKernelGGL((k_fma_exp_plain<6, 1>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 13)
+        hipLaunchKernelGGL((k_fma_exp_plain<2, 1>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 14)
+        hipLaunchKernelGGL(k_fma_exp_interleaved, dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 15)
+        hipLaunchKernelGGL((k_valu_op<0>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 16)
+        hipLaunchKernelGGL((k_valu_op<1>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 17)
+        hipLaunchKernelGGL((k_valu_op<2>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
