@@ -277,14 +277,18 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kPassRows = 64 * kR;
 
 // Occupancy asked of the compiler (waves per SIMD).  Left to itself it
-// schedules the chunk loop for 5 waves at d = 2, 3 (87 and 95 VGPRs); held to
-// 7 (72 VGPRs) it spills a few values of the segment setup, none inside the
-// key loop.  Measured at 50,000^2, d = 3: 91.1 ms per 100-iteration solve at
-// 5 waves, against 88.1 ms for the block-wide kernel this one replaced.  The
-// larger d keep the occupancy that kernel had.
+// schedules the chunk loop for 5 waves at d = 2, 3 (87 and 95 VGPRs): 3.4%
+// slower at 50,000^2 than the 7 waves the previous layout of this pass ran
+// at.  Held to 6 (80 VGPRs) it needs no scratch.  Held to 7 (72 VGPRs) it
+// spills a few values of the segment set-up (none in the key loop); with
+// several resident rounds of workgroups those scratch lines reach HBM.
+// Measured with the round rule, per 100-iteration solve: 50,000^2 85.8 ms
+// at 6 waves against 86.4 at 7, with 6.5 against 23.0 MB written per pass
+// launch; 50,000 x 40,000 69.5 against 69.8 ms.  The larger d keep the
+// occupancy the previous layout had.
 template <int D>
 constexpr int pass_min_waves() {
-    return D <= 3 ? 7 : (D == 4 ? 5 : (D <= 7 ? 4 : 3));
+    return D <= 3 ? 6 : (D == 4 ? 5 : (D <= 7 ? 4 : 3));
 }
 
 template <int D>
