@@ -261,6 +261,24 @@ def run_ceilings():
         if kind == 7:
             mix_fma_rate = steps * nf  # FMA lane-ops/s with independent chains, no exp2
     res["fma_exp_mix"] = mix
+    # device-wide barrier of a cooperative launch: microseconds per grid.sync() at a few grid sizes
+    gs = {}
+    for nb in (8, 64, 256, 512):
+        rc = lib.sku_launch(18, nb, 10, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        if rc != 0:
+            gs[nb] = f"launch refused ({rc})"
+            continue
+        times = []
+        for it in (100, 1100):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lib.sku_launch(18, nb, it, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        gs[nb] = {"us_per_sync": (times[1] - times[0]) / 1000.0, "launch_us_100": times[0]}
+    res["grid_sync"] = gs
     res["lane_ops_per_s_nominal"] = LANE_OPS_PER_S
     print(json.dumps(res))
 

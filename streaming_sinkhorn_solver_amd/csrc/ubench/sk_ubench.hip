@@ -6,6 +6,7 @@
 // Each thread runs kChains independent dependency chains so issue rate, not
 // latency, is measured.  The kernels write one value per thread so the work
 // cannot be removed.
+#include <hip/hip_cooperative_groups.h>
 #include <hip/hip_runtime.h>
 
 namespace {
@@ -188,6 +189,19 @@ __global__ __launch_bounds__(256) void k_valu_op(float* out, int iters, float a,
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Cost of a device-wide barrier: iters grid-wide synchronisations of a
+// cooperative launch (every workgroup resident), each preceded by one store
+// per thread, as a persistent solver would pay between its half-steps.
+__global__ __launch_bounds__(256) void k_grid_sync(float* out, int iters) {
+    cooperative_groups::grid_group grid = cooperative_groups::this_grid();
+    float v = threadIdx.x * 1e-3f;
+    for (int it = 0; it < iters; ++it) {
+        v = fmaf(v, 0.999f, 1e-3f);
+        out[blockIdx.x * blockDim.x + threadIdx.x] = v;
+        grid.sync();
+    }
+}
+
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 
@@ -294,8 +308,10 @@ extern "C" {
 // iters * 64 v_mfma_f32_16x16x4f32 (2048 flops each); kind 4: each wave issues
 // iters * 64 v_mfma_f32_32x32x2f32 (4096 flops each); kind 5: each wave issues
 // iters * 64 v_mfma_f32_16x16x32_bf16 (16384 flops each); kind 6: as kind 5
-// with 8 vector FMAs per matrix instruction.  Launches `blocks` x 256
-// threads; out must hold blocks * 256 floats.  Returns a hipError_t.
+// with 8 vector FMAs per matrix instruction.  kind 18: iters device-wide
+// barriers under a cooperative launch (refused with an error when the grid
+// cannot be resident at once).  Launches `blocks` x 256 threads; out must
+// hold blocks * 256 floats.  Returns a hipError_t.
 int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (kind == 0)
@@ -334,6 +350,11 @@ int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
         hipLaunchKernelGGL((k_valu_op<1>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
     else if (kind == 17)
         hipLaunchKernelGGL((k_valu_op<2>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 18) {
+        void* args[] = {&out, &iters};
+        return (int)hipLaunchCooperativeKernel(reinterpret_cast<void*>(k_grid_sync), dim3(blocks), dim3(256), args,
+                                               0, s);
+    }
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
