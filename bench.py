@@ -135,6 +135,7 @@ def roofline_alu(d: int, pairs_per_launch: float, avg_launch_s: float, payload: 
 
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (the same rate as bf16)
 
 
 def roofline_mfma(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int = 0) -> dict:
@@ -155,15 +156,16 @@ def packed_stride(d: int) -> int:
 
 def roofline_split(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict:
     """Matrix-core roofline of the solver pass (and the one-column transport kernel), where the cross term
-    runs as six bf16 products of a three-part split of each coordinate: 12 d bf16 flops per pair evaluation
-    against the bf16 MFMA peak. The fp32-equivalent rate (2 d flops per pair, the fp32 contraction it
-    replaces) is reported beside it."""
-    ops = 12 * d
+    runs on fp16 matrix instructions from a scaled two-part split of each coordinate: three products
+    (6 d fp16 flops per pair evaluation) from 32 padded coordinates on, four in two instructions at a
+    padded width of 16 (8 d), against the dense fp16 MFMA peak. The fp32-equivalent rate (2 d flops per
+    pair, the fp32 contraction it replaces) is reported beside it."""
+    ops = (8 if packed_stride(d) == 16 else 6) * d
     achieved = pairs_per_launch * ops / avg_launch_s / 1e12
     fp32_eq = pairs_per_launch * 2 * d / avg_launch_s / 1e12
-    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None, "ops_per_pair": ops,
-            "mfma_dtype": "bf16 (three-part split of fp32, six products)",
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None, "ops_per_pair": ops,
+            "mfma_dtype": "fp16 (scaled two-part split of fp32: hh + hl + lh)",
             "fp32_equivalent": {"achieved": round(fp32_eq, 3), "ops_per_pair": 2 * d,
                                 "vs_fp32_mfma_peak": round(fp32_eq / MFMA_FP32_PEAK_TFLOPS, 4)},
             "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}

@@ -183,9 +183,10 @@ int prepare(const Ws& W, const float* x, const float* y, const float* a, const f
                        1.0f / eps, x_bias, f, u_x, s));
     SK_TRY(launch_pack(y, (int)L.m, L.d, L.P, L.mfma, centre, b, W.f(L.yp), W.f(L.ny), W.f(L.l2b), W.f(L.hy),
                        1.0f / eps, y_bias, g, u_y, s));
-    if (L.split) {  // keys of the bf16 matrix-core pass
-        SK_TRY(launch_split3(W.f(L.xp), L.n, L.P, W.h(L.xb), s));
-        SK_TRY(launch_split3(W.f(L.yp), L.m, L.P, W.h(L.yb), s));
+    if (L.split) {  // scales and keys of the fp16 matrix-core pass
+        SK_TRY(launch_absmax(W.f(L.xp), L.n * L.P, W.f(L.yp), L.m * L.P, W.f(L.amax_part), W.f(L.amax), s));
+        SK_TRY(launch_split2(W.f(L.xp), L.n, L.P, W.f(L.amax), W.h(L.xb), s));
+        SK_TRY(launch_split2(W.f(L.yp), L.m, L.P, W.f(L.amax) + 1, W.h(L.yb), s));
     }
     return SK_OK;
 }
@@ -203,6 +204,8 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
     p.k = W.f(row_side ? L.yp : L.xp);
     p.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
     p.kb = L.split ? W.h(row_side ? L.yb : L.xb) : nullptr;
+    p.qmax = L.split ? W.f(L.amax) + (row_side ? 0 : 1) : nullptr;
+    p.kmax = L.split ? W.f(L.amax) + (row_side ? 1 : 0) : nullptr;
     p.nq = (int)nq;
     p.nk = (int)nk;
     p.P = L.P;
@@ -236,6 +239,7 @@ void retarget(PassArgs& p, const float* q, int64_t nq, const float* k, int64_t n
     p.q = q;
     p.k = k;
     p.kb = nullptr;  // no split copy of other keys
+    p.qmax = p.kmax = nullptr;
     p.nq = (int)nq;
     p.nk = (int)nk;
     p.total = (nq + p.rpb - 1) / p.rpb * nk;
@@ -362,8 +366,10 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.snap_f = take(un * 4);
     L.snap_g = take(um * 4);
     L.split = L.mfma;
-    L.xb = take(L.split ? un * 3 * P * 2 : 0);
-    L.yb = take(L.split ? um * 3 * P * 2 : 0);
+    L.xb = take(L.split ? un * 2 * P * 2 : 0);
+    L.yb = take(L.split ? um * 2 * P * 2 : 0);
+    L.amax = take(L.split ? 2 * sizeof(float) : 0);
+    L.amax_part = take(L.split ? 2 * kAbsMaxBlocks * sizeof(float) : 0);
     L.total = off;
     return L;
 }
@@ -839,6 +845,8 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     t.k = W.f(row_side ? L.yp : L.xp);
     t.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
     t.kb = L.split ? W.h(row_side ? L.yb : L.xb) : nullptr;
+    t.qmax = L.split ? W.f(L.amax) + (row_side ? 0 : 1) : nullptr;
+    t.kmax = L.split ? W.f(L.amax) + (row_side ? 1 : 0) : nullptr;
     t.qbias = L.mfma ? W.f(row_side ? L.hx : L.hy) : nullptr;
     t.lse = L.mfma ? W.f(row_side ? L.lse_r : L.lse_c) : nullptr;
     t.pay = pay;

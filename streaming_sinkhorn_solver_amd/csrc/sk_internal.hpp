@@ -118,7 +118,9 @@ struct PassArgs {
     const float* q;      // query cloud, packed [nq][P]
     const float* k;      // key cloud, packed [nk][P]
     const float* kbias;  // separate key bias [nk] (matrix-core layout), else null
-    const uint16_t* kb;  // matrix-core layout, P >= 32: bf16 parts of the keys [nk][3][P] (h, m, l), else null
+    const uint16_t* kb;  // matrix-core layout: fp16 parts of the scaled keys [nk][2][P] (h, l), else null
+    const float* qmax;   // matrix-core layout: largest |packed coordinate| of the query cloud (device)
+    const float* kmax;   // matrix-core layout: the same of the key cloud (device)
     int nq, nk, P;
     float qscale;        // 2 log2e / eps
     int rpb;             // rows per block
@@ -184,7 +186,9 @@ struct TransArgs {
     const float* q;      // query cloud, packed [nq][P], bias slot = log2 w + log2e (pot - |q~|^2)/eps
     const float* k;      // key cloud, packed [nk][P], same bias from the key-side potential
     const float* kbias;  // matrix-core layout: key biases [nk], else null
-    const uint16_t* kb;  // matrix-core layout, P >= 32: bf16 parts of the keys [nk][3][P] (one-column mode)
+    const uint16_t* kb;  // matrix-core layout: fp16 parts of the scaled keys [nk][2][P] (one-column mode)
+    const float* qmax;   // matrix-core layout: largest |packed coordinate| of the query cloud (device)
+    const float* kmax;   // matrix-core layout: the same of the key cloud (device)
     const float* qbias;  // matrix-core layout: query biases [nq], else null
     const float* lse;    // matrix-core layout: row log-sum-exp of the scores [nq] (a first pass)
     const float* pay;    // payload: key j's columns at pay[j * ldp + c], c < kin
@@ -205,8 +209,9 @@ struct Layout {
     bool mfma;
     int64_t n, m;
     size_t xp, yp, hx, hy, nx, ny, l2a, l2b, lse_r, lse_c, rbuf, part, partA, red, cen, centre, chk;
-    size_t xb, yb;            // bf16 parts of the packed clouds (matrix-core layout, P >= 32)
+    size_t xb, yb;            // fp16 parts of the scaled packed clouds (matrix-core layout)
     bool split;               // xb, yb are in use
+    size_t amax, amax_part;   // largest |packed coordinate| of x and y (2 floats), and its per-block maxima
     size_t lse_r2, lse_c2;    // second state buffers (a check keeps the previous state)
     size_t snap_f, snap_g;    // potentials at the previous check (potential stop rule)
     size_t total;
@@ -332,8 +337,14 @@ hipError_t launch_merge(const PassArgs& a, hipStream_t s);
 hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 int mfma_rows_per_block(int P);
 int mfma_pass_capacity(int P);
-// bf16 parts (h, m, l) of rows x P packed floats into out [rows][3][P].
-hipError_t launch_split3(const float* in, int64_t rows, int P, uint16_t* out, hipStream_t s);
+// fp16 parts (h, l) of rows x P packed floats times 2^ek into out [rows][2][P],
+// ek from the cloud's largest |coordinate| *kmax (device).
+hipError_t launch_split2(const float* in, int64_t rows, int P, const float* kmax, uint16_t* out, hipStream_t s);
+// out[0] = max |x[e]| over nx floats, out[1] = the same over y (nx, ny multiples
+// of 4); part holds 2 * kAbsMaxBlocks floats.
+constexpr int kAbsMaxBlocks = 256;
+hipError_t launch_absmax(const float* x, int64_t nx, const float* y, int64_t ny, float* part, float* out,
+                         hipStream_t s);
 // Matrix-core gradient pass (needs the row lse of the same scores); rows per workgroup.
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
 int mfma_grad_rows_per_block();

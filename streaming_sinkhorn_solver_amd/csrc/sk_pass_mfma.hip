@@ -11,7 +11,7 @@
 //  * lane l = 16 g + c; D is 16 keys x 16 queries with lane l holding keys
 //    4g..4g+3 of query c, for both instructions used here:
 //    v_mfma_f32_16x16x4f32 (lane: key / query c, k slot g) and
-//    v_mfma_f32_16x16x32_bf16 (lane: key / query c, k slots 8g..8g+7);
+//    v_mfma_f32_16x16x32_f16 (lane: key / query c, k slots 8g..8g+7);
 //  * the contraction index is permuted so that lane group g owns the
 //    contiguous coordinate range [g P/4, (g+1) P/4). Each lane keeps its
 //    query's coordinates in registers for the whole pass (row-stationary) and
@@ -25,13 +25,14 @@
 // passes; a row block here is 4 waves x NQB x 16 queries.
 //
 // The solver pass and the one-column transport kernel take the cross term on
-// bf16 matrix cores from a three-part split of every fp32 coordinate that is
-// as exact as an fp32 dot product (split3, split_scores); the gradient and the
-// payload-carrying transport modes use fp32 instructions.
+// fp16 matrix cores from a scaled two-part split of every fp32 coordinate,
+// within a few fp32 unit roundoffs per term (split2, split_scores); the
+// gradient and the payload-carrying transport modes use fp32 instructions.
 #include "sk_internal.hpp"
 #include "sk_pass_common.hpp"
 
 #include <algorithm>
+#include <cfloat>
 #include <type_traits>
 
 namespace sk {
@@ -108,76 +109,159 @@ struct TileStage {
     }
 };
 
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
-#ifndef SK_MFMA3_TILE
-#define SK_MFMA3_TILE 4096
+#ifndef SK_MFMA2_TILE
+#define SK_MFMA2_TILE 4096
 #endif
 
-// ---- three-part bf16 split of fp32 values
+// ---- two-part fp16 split of scaled fp32 values
 //
-// v = h + m + l with h = bf16(v), m = bf16(v - h), l = bf16(v - h - m), each
-// rounded to nearest even. The two remainders are exact in fp32 (each part is
-// within a factor 2 of what it rounds), and |v - h - m - l| <= 2^-27 |v|. Then
-//   q.k ~ hq hk + hq mk + mq hk + hq lk + lq hk + mq mk:
-// every product of two bf16 values is exact in fp32, the matrix cores add in
-// fp32, and the dropped products (m l, l m, l l) are below 2^-26 of
-// |q_t k_t|, under the unit roundoff 2^-24 of an fp32 dot product. On gfx950
-// one v_mfma_f32_16x16x32_bf16 (16 keys x 16 queries x 32 coordinates) costs
-// half the issue time of one v_mfma_f32_16x16x4f32 (the bf16 rate is 16x the
-// fp32 rate), so the six products of 32 coordinates take 3/8 of the
+// Each side is first scaled by a power of two 2^e chosen from the largest
+// magnitude of its cloud (split_exp), so that its operands lie below 2^14,
+// within fp16's range and near its top. Then v = h + l with h = fp16(v) and
+// l = fp16(v - h), both rounded to nearest even: the remainder v - h is exact
+// in fp32 and |v - h - l| <= 2^-22 |v| + 2^-25, the second term from fp16's
+// subnormal spacing (it matters only for |v| below about 2^-3 at the scaled
+// size, against largest operands of 2^13 to 2^14). The score takes hq hk + hq lk + lq hk: each product of two fp16 values is
+// exact in fp32, the matrix cores add in fp32, and the dropped product lq lk
+// is below 2^-22 |q_t k_t|. This is the fp16 splitting of Ootomo and Yokota
+// ("Recovering single precision accuracy from Tensor Cores while surpassing
+// the FP32 theoretical peak performance", IJHPCA 2022), with a common scale
+// per side in place of their per-part scaling. Its error per term is a few
+// fp32 unit roundoffs (2^-22 against 2^-24). One v_mfma_f32_16x16x32_f16
+// (16 keys x 16 queries x 32 coordinates) runs at the bf16 rate, 16x the
+// fp32 matrix rate, so the three products of 32 coordinates take 3/16 of the
 // matrix-core time of the eight fp32 steps they replace.
-__device__ __forceinline__ unsigned bf16_rne(float x) {  // finite x
-    unsigned u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-__device__ __forceinline__ float bf16_value(unsigned h) { return __uint_as_float(h << 16); }
-__device__ __forceinline__ void split3(float v, unsigned& h, unsigned& m, unsigned& l) {
-    h = bf16_rne(v);
-    const float r = v - bf16_value(h);
-    m = bf16_rne(r);
-    l = bf16_rne(r - bf16_value(m));
+//
+// The matrix cores then return 2^(eq + ek) times the score (the key biases
+// are scaled the same way when a tile is staged); the log-sum-exp takes the
+// scale off inside its exponent with one fma, fma(D, r, -M r), r = 2^-(eq+ek).
+
+// The exponent e that puts the largest magnitude mx at mx 2^e in [2^13, 2^14)
+// (0 for a zero or non-finite mx).
+__device__ __forceinline__ int split_exp(float mx) {
+    if (!(mx > 0.0f) || !(mx <= FLT_MAX)) return 0;
+    int e;
+    (void)frexpf(mx, &e);  // mx = f 2^e, f in [0.5, 1)
+    return 14 - e;
 }
 
-// The parts of packed rows: out[i][part][t] (parts h, m, l) from in[i][t].
-__global__ __launch_bounds__(kBlock) void k_split3(const float* __restrict__ in, int64_t count, int P,
-                                                   uint16_t* __restrict__ out) {
+// Key-side exponent of a cloud whose largest |coordinate| is kmax; capped so
+// that the score scale 2^(eq + ek) stays at most 2^64.
+__device__ __forceinline__ int key_exp(float kmax) { return min(split_exp(kmax), 64); }
+
+// The scales of one pass: queries are fl(v qscale) 2^eq (the same fp32 query
+// value as an unsplit pass, shifted by a power of two), keys v 2^ek.
+struct SplitScale {
+    float qshift;  // 2^eq
+    float t;       // 2^(eq + ek): score scale of the matrix-core results and staged biases
+    float r;       // 2^-(eq + ek)
+    float m0;      // running-max start, kNegBig min(t, 1), so that -m0 r stays finite
+};
+
+__device__ __forceinline__ SplitScale split_scale(const float* qmax, const float* kmax, float qscale) {
+    const int ek = key_exp(*kmax);
+    const int eq = min(split_exp(*qmax * qscale), 64 - ek);
+    SplitScale z;
+    z.qshift = ldexpf(1.0f, eq);
+    z.t = ldexpf(1.0f, eq + ek);
+    z.r = ldexpf(1.0f, -(eq + ek));
+    z.m0 = z.t < 1.0f ? kNegBig * z.t : kNegBig;
+    return z;
+}
+
+__device__ __forceinline__ unsigned f16_bits(float x) {
+    return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)x);
+}
+__device__ __forceinline__ float f16_value(unsigned h) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+}
+__device__ __forceinline__ void split2(float v, unsigned& h, unsigned& l) {
+    h = f16_bits(v);
+    l = f16_bits(v - f16_value(h));
+}
+
+// The parts of packed key rows: out[i][part][t] (parts h, l) of in[i][t] 2^ek,
+// ek from the cloud's largest |coordinate| *kmax.
+__global__ __launch_bounds__(kBlock) void k_split2(const float* __restrict__ in, int64_t count, int P,
+                                                   const float* __restrict__ kmax, uint16_t* __restrict__ out) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= count) return;
+    const float sc = ldexpf(1.0f, key_exp(*kmax));
     const int64_t i = e / P;
     const int t = (int)(e - i * P);
-    unsigned h, m, l;
-    split3(in[e], h, m, l);
-    uint16_t* o = out + i * 3 * P + t;
+    unsigned h, l;
+    split2(in[e] * sc, h, l);
+    uint16_t* o = out + i * 2 * P + t;
     o[0] = (uint16_t)h;
-    o[P] = (uint16_t)m;
-    o[2 * P] = (uint16_t)l;
+    o[P] = (uint16_t)l;
 }
 
-// keys per LDS tile of the split pass (SK_MFMA3_TILE coordinates: 3 x 2 bytes each)
+// The largest |value| of each of two packed clouds: per-block maxima
+// (blockIdx.y picks the cloud), then one workgroup joins them.
+__global__ __launch_bounds__(kBlock) void k_absmax_part(const float4* __restrict__ x4, int64_t nx4,
+                                                        const float4* __restrict__ y4, int64_t ny4,
+                                                        float* __restrict__ part) {
+    const float4* v = blockIdx.y == 0 ? x4 : y4;
+    const int64_t cnt = blockIdx.y == 0 ? nx4 : ny4;
+    float mx = 0.0f;
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < cnt; e += (int64_t)gridDim.x * kBlock) {
+        const float4 w = v[e];
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(w.x), fabsf(w.y)), fmaxf(fabsf(w.z), fabsf(w.w))));
+    }
+    __shared__ float red[kBlock];
+    red[threadIdx.x] = mx;
+    __syncthreads();
+    for (int off = kBlock / 2; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[blockIdx.y * gridDim.x + blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(kBlock) void k_absmax_final(const float* __restrict__ part, int nb,
+                                                         float* __restrict__ out) {
+    __shared__ float red[kBlock];
+    for (int side = 0; side < 2; ++side) {
+        float mx = 0.0f;
+        for (int e = threadIdx.x; e < nb; e += kBlock) mx = fmaxf(mx, part[side * nb + e]);
+        red[threadIdx.x] = mx;
+        __syncthreads();
+        for (int off = kBlock / 2; off > 0; off >>= 1) {
+            if ((int)threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) out[side] = red[0];
+        __syncthreads();
+    }
+}
+
+// keys per LDS tile of the split pass (SK_MFMA2_TILE coordinates: 2 x 2 bytes each)
 template <int P>
-constexpr int mfma3_tile_keys() {
-    return SK_MFMA3_TILE / P < 16 ? 16 : SK_MFMA3_TILE / P;
+constexpr int mfma2_tile_keys() {
+    return SK_MFMA2_TILE / P < 16 ? 16 : SK_MFMA2_TILE / P;
 }
 
 // Register staging of one LDS tile of split keys: a key row is RU 16-byte
-// units (h, m, l parts of P coordinates), stored RU + 1 apart in LDS, an odd
+// units (h, l parts of P coordinates), stored RU + 1 apart in LDS, an odd
 // number of units, so 16 lanes reading 16 rows at one offset do not conflict.
+// The key biases are staged times the pass's score scale t.
 template <int P>
-struct TileStage3 {
-    static constexpr int TL = mfma3_tile_keys<P>();
-    static constexpr int RU = 3 * P / 8;
+struct TileStage2 {
+    static constexpr int TL = mfma2_tile_keys<P>();
+    static constexpr int RU = P / 4;
     static constexpr int RS = RU + 1;
     static constexpr int U = TL * RU / kBlock;
     static constexpr int NB = (TL + kBlock - 1) / kBlock;
     static_assert(TL * RU % kBlock == 0, "tile must split evenly over the workgroup");
+    static_assert(RS % 2 == 1, "odd row stride in 16-byte units");
     u4v v[U];
     float b[NB];
 
-    __device__ __forceinline__ void load(const u4v* __restrict__ kb, const float* __restrict__ kbias, int base,
-                                         int j1) {
+    __device__ __forceinline__ void load(const u4v* __restrict__ kb, const float* __restrict__ kbias, float t,
+                                         int base, int j1) {
 #pragma unroll
         for (int r = 0; r < U; ++r) {
             const int e = threadIdx.x + r * kBlock;
@@ -190,7 +274,7 @@ struct TileStage3 {
         for (int r = 0; r < NB; ++r) {
             const int col = base + threadIdx.x + r * kBlock;
             const float x = kbias[min(col, j1 - 1)];
-            b[r] = col < j1 ? x : -INFINITY;
+            b[r] = col < j1 ? x * t : -INFINITY;
         }
     }
 
@@ -209,75 +293,63 @@ struct TileStage3 {
     }
 };
 
-__device__ __forceinline__ f4 mfma_bf16(const u4v a, const u4v b, const f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0,
-                                                   0);
+__device__ __forceinline__ f4 mfma_f16(const u4v a, const u4v b, const f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
 }
 
-// Query operands per lane in the split form: P >= 32 keeps one (h, m, l)
-// triple of 8-coordinate chunks per chunk; P = 16 (4 coordinates per lane
-// group, half an operand) keeps three ready operands that pair two parts each.
+// Query operands per lane in the split form: P >= 32 keeps one (h, l) pair of
+// 8-coordinate chunks per chunk; P = 16 (4 coordinates per lane group, half an
+// operand) keeps two ready operands, (h, h) and (l, l).
 template <int P>
 constexpr int split_qops() {
     return P >= 32 ? P / 32 : 1;
 }
 
-// A lane's query row for the split form, from its P/4 coordinates at qr,
-// scaled. P >= 32: chunk kc of qh, qm, ql holds the h, m, l parts of
-// coordinates 8 kc .. 8 kc + 7. P = 16: qh = (h, h), qm = (m, h), ql = (l, m)
-// over the lane group's 4 coordinates, the B operands of the three products
-// split_scores<16> forms.
+// A lane's query row for the split form, from its P/4 coordinates at qr:
+// fl(v qscale) 2^eq, split. P >= 32: chunk kc of qh, ql holds the h, l parts
+// of coordinates 8 kc .. 8 kc + 7. P = 16: qh = (h, h), ql = (l, l) over the
+// lane group's 4 coordinates, the B operands of split_scores<16>.
 template <int P>
-__device__ __forceinline__ void load_query_split(const float* __restrict__ qr, float qscale,
-                                                 u4v (&qh)[split_qops<P>()], u4v (&qm)[split_qops<P>()],
-                                                 u4v (&ql)[split_qops<P>()]) {
+__device__ __forceinline__ void load_query_split(const float* __restrict__ qr, float qscale, float qshift,
+                                                 u4v (&qh)[split_qops<P>()], u4v (&ql)[split_qops<P>()]) {
     const float4* q4 = reinterpret_cast<const float4*>(qr);
-    if constexpr (P == 16) {
-        const float4 v = q4[0];
-        const float x[4] = {v.x * qscale, v.y * qscale, v.z * qscale, v.w * qscale};
-        unsigned hw[2], mw[2], lw[2];
+#pragma unroll
+    for (int t4 = 0; t4 < (P == 16 ? 1 : P / 16); ++t4) {
+        const float4 v = q4[t4];
+        const float x[4] = {(v.x * qscale) * qshift, (v.y * qscale) * qshift, (v.z * qscale) * qshift,
+                            (v.w * qscale) * qshift};
+        unsigned hw[2], lw[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            unsigned h0, m0, l0, h1, m1, l1;
-            split3(x[2 * e], h0, m0, l0);
-            split3(x[2 * e + 1], h1, m1, l1);
+            unsigned h0, l0, h1, l1;
+            split2(x[2 * e], h0, l0);
+            split2(x[2 * e + 1], h1, l1);
             hw[e] = h0 | (h1 << 16);
-            mw[e] = m0 | (m1 << 16);
             lw[e] = l0 | (l1 << 16);
         }
-        qh[0] = u4v{hw[0], hw[1], hw[0], hw[1]};
-        qm[0] = u4v{mw[0], mw[1], hw[0], hw[1]};
-        ql[0] = u4v{lw[0], lw[1], mw[0], mw[1]};
-    } else {
-#pragma unroll
-        for (int t4 = 0; t4 < P / 16; ++t4) {
-            const float4 v = q4[t4];
-            const float x[4] = {v.x * qscale, v.y * qscale, v.z * qscale, v.w * qscale};
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                unsigned h0, m0, l0, h1, m1, l1;
-                split3(x[2 * e], h0, m0, l0);
-                split3(x[2 * e + 1], h1, m1, l1);
-                const int kc = t4 / 2, wd = 2 * (t4 % 2) + e;
-                qh[kc][wd] = h0 | (h1 << 16);
-                qm[kc][wd] = m0 | (m1 << 16);
-                ql[kc][wd] = l0 | (l1 << 16);
-            }
+        if constexpr (P == 16) {
+            qh[0] = u4v{hw[0], hw[1], hw[0], hw[1]};
+            ql[0] = u4v{lw[0], lw[1], lw[0], lw[1]};
+        } else {
+            const int kc = t4 / 2, wd = 2 * (t4 % 2);
+            qh[kc][wd] = hw[0];
+            qh[kc][wd + 1] = hw[1];
+            ql[kc][wd] = lw[0];
+            ql[kc][wd + 1] = lw[1];
         }
     }
 }
 
-// Scores of one 16-key block for NQB query blocks in the split form: row is
-// the lane's key row in the LDS tile (parts h, m, l, P/8 units apart) and g its
-// lane group. P >= 32: six products per 8-coordinate chunk. P = 16: the lane
-// group's 4 coordinates fill half an operand, so the six products go in pairs
-// into three instructions, (h, m) x (h, h), (h, l) x (m, h), (h, m) x (l, m).
-// With four query blocks the four accumulator chains keep the matrix pipe busy;
-// with fewer, the small products go to a second accumulator per block (from
-// zero).
+// Scores (times the pass's scale t) of one 16-key block for NQB query blocks
+// in the split form: row is the lane's key row in the LDS tile (parts h, l,
+// P/8 units apart) and g its lane group. P >= 32: three products per
+// 8-coordinate chunk. P = 16: the lane group's 4 coordinates fill half an
+// operand, so A = (kh, kl) against B = (qh, qh) and then (ql, ql) gives all
+// four products in two instructions. With four query blocks the four
+// accumulator chains keep the matrix pipe busy; with fewer, the small products
+// go to a second accumulator per block (from zero).
 template <int P, int NQB>
 __device__ __forceinline__ void split_scores(const u4v* row, int g, const u4v (&qh)[NQB][split_qops<P>()],
-                                             const u4v (&qm)[NQB][split_qops<P>()],
                                              const u4v (&ql)[NQB][split_qops<P>()], const f4 bias,
                                              f4 (&acc)[NQB]) {
     constexpr bool kTwoAcc = NQB < 4;
@@ -291,32 +363,24 @@ __device__ __forceinline__ void split_scores(const u4v* row, int g, const u4v (&
     if constexpr (P == 16) {
         // 8 bytes per part and lane group: part p at uint2 index 4 p + g of the row
         const uint2* r2 = reinterpret_cast<const uint2*>(row);
-        const uint2 kh = r2[g], km = r2[4 + g], kl = r2[8 + g];
-        const u4v a1 = {kh.x, kh.y, km.x, km.y}, a2 = {kh.x, kh.y, kl.x, kl.y};
+        const uint2 kh = r2[g], kl = r2[4 + g];
+        const u4v a = {kh.x, kh.y, kl.x, kl.y};
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(a1, qh[qb][0], acc[qb]);
+        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_f16(a, qh[qb][0], acc[qb]);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(a2, qm[qb][0], small[qb]);
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(a1, ql[qb][0], acc[qb]);
+        for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_f16(a, ql[qb][0], small[qb]);
     } else {
         constexpr int KC = P / 32;
         const u4v* kr = row + g * KC;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            const u4v kh = kr[kc], km = kr[P / 8 + kc], kl = kr[2 * (P / 8) + kc];
+            const u4v kh = kr[kc], kl = kr[P / 8 + kc];
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qh[qb][kc], acc[qb]);
+            for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_f16(kh, qh[qb][kc], acc[qb]);
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kh, ql[qb][kc], small[qb]);
+            for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_f16(kh, ql[qb][kc], small[qb]);
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(kh, qm[qb][kc], acc[qb]);
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(kl, qh[qb][kc], small[qb]);
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_bf16(km, qh[qb][kc], acc[qb]);
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) small[qb] = mfma_bf16(km, qm[qb][kc], small[qb]);
+            for (int qb = 0; qb < NQB; ++qb) acc[qb] = mfma_f16(kl, qh[qb][kc], acc[qb]);
         }
     }
     if constexpr (kTwoAcc) {
@@ -340,46 +404,52 @@ __device__ __forceinline__ void load_keys(float (&kf)[KT], const float* ktile, i
 }
 
 // Online log-sum-exp over the four scores a lane holds for one 16-key block.
-__device__ __forceinline__ void lse_block(float& M, float& S, const f4 acc) {
+// Scores, M and the candidates are in the pass's scaled units (times t); the
+// exponents are taken back to base-2 units with one fma each, fma(x, r, -mn r)
+// = (x - mn) r rounded once, the same value as x r - mn r of unscaled scores.
+// M starts at SplitScale::m0, so -mn r is finite and an empty key set gives
+// fma(-inf, r, finite) = -inf, never inf - inf.
+__device__ __forceinline__ void lse_block(float& M, float& S, const f4 acc, float r) {
     const float mt = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     const float mn = fmaxf(M, mt);
-    float s = S * ex2(M - mn);
-    s += ex2(acc[0] - mn);
-    s += ex2(acc[1] - mn);
-    s += ex2(acc[2] - mn);
-    s += ex2(acc[3] - mn);
+    const float nm = -mn * r;
+    float s = S * ex2(fmaf(M, r, nm));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s += ex2(fmaf(acc[v], r, nm));
     S = s;
     M = mn;
 }
 
 // The same over the eight scores of two 16-key blocks (one rescale for both).
-__device__ __forceinline__ void lse_block2(float& M, float& S, const f4 a, const f4 b) {
+__device__ __forceinline__ void lse_block2(float& M, float& S, const f4 a, const f4 b, float r) {
     const float mt = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
     const float mn = fmaxf(M, mt);
-    float s = S * ex2(M - mn);
+    const float nm = -mn * r;
+    float s = S * ex2(fmaf(M, r, nm));
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s += ex2(a[v] - mn);
+    for (int v = 0; v < 4; ++v) s += ex2(fmaf(a[v], r, nm));
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s += ex2(b[v] - mn);
+    for (int v = 0; v < 4; ++v) s += ex2(fmaf(b[v], r, nm));
     S = s;
     M = mn;
 }
 
-__device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2) {
+__device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2, float r) {
     const float mn = fmaxf(M, m2);
-    S = S * ex2(M - mn) + s2 * ex2(m2 - mn);
+    const float nm = -mn * r;
+    S = S * ex2(fmaf(M, r, nm)) + s2 * ex2(fmaf(m2, r, nm));
     M = mn;
 }
 
-// The solver pass: the cross term on bf16 matrix cores from the three-part
-// split (keys split in memory by k_split3, queries split in registers when a
+// The solver pass: the cross term on fp16 matrix cores from the two-part
+// split (keys split in memory by k_split2, queries split in registers when a
 // segment starts). Lane group g owns the coordinates [g P/4, (g+1) P/4).
 template <int P>
 __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
     constexpr int KT = P / 4;            // coordinates per lane group
     constexpr int KQ = split_qops<P>();  // query operands per part
     constexpr int NQB = mfma_nqb<P>();   // 16-query blocks per wave
-    using Stage = TileStage3<P>;
+    using Stage = TileStage2<P>;
     constexpr int TL = Stage::TL;
     constexpr int RS = Stage::RS;
     __shared__ u4v ktile[TL * RS];
@@ -388,6 +458,7 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     const u4v* kb = reinterpret_cast<const u4v*>(A.kb);
+    const SplitScale sc = split_scale(A.qmax, A.kmax, A.qscale);
 
     const int w = blockIdx.x;
     const int64_t lo = range_lo(w, A.total, A.W), hi = range_lo(w + 1, A.total, A.W);
@@ -397,25 +468,25 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
         const int j1 = (int)min<int64_t>((int64_t)A.nk, (int64_t)j0 + (hi - u));
         const int qrow0 = rb * A.rpb + wave * (NQB * 16);
 
-        // queries, scaled, as h, m, l parts
-        u4v qh[NQB][KQ], qm[NQB][KQ], ql[NQB][KQ];
+        // queries, scaled, as h, l parts
+        u4v qh[NQB][KQ], ql[NQB][KQ];
         float M[NQB], S[NQB];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             const int i = qrow0 + qb * 16 + c;
             const int ic = i < A.nq ? i : A.nq - 1;
-            load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, qh[qb], qm[qb], ql[qb]);
-            M[qb] = kNegBig;
+            load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, sc.qshift, qh[qb], ql[qb]);
+            M[qb] = sc.m0;
             S[qb] = 0.0f;
         }
 
         Stage stage;
-        stage.load(kb, A.kbias, j0, j1);
+        stage.load(kb, A.kbias, sc.t, j0, j1);
         for (int base = j0; base < j1; base += TL) {
             __syncthreads();
             stage.store(ktile, btile);
             __syncthreads();
-            if (base + TL < j1) stage.load(kb, A.kbias, base + TL, j1);
+            if (base + TL < j1) stage.load(kb, A.kbias, sc.t, base + TL, j1);
             const int ntile = min(TL, j1 - base);
             if constexpr (TL >= 32) {
                 // two 16-key blocks per step, one rescale for both (3.5% faster at d = 64 than one block per
@@ -424,18 +495,18 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
                     const f4 bias0 = *reinterpret_cast<const f4*>(&btile[kb32 + 4 * g]);
                     const f4 bias1 = *reinterpret_cast<const f4*>(&btile[kb32 + 16 + 4 * g]);
                     f4 acc0[NQB], acc1[NQB];
-                    split_scores<P, NQB>(ktile + (kb32 + c) * RS, g, qh, qm, ql, bias0, acc0);
-                    split_scores<P, NQB>(ktile + (kb32 + 16 + c) * RS, g, qh, qm, ql, bias1, acc1);
+                    split_scores<P, NQB>(ktile + (kb32 + c) * RS, g, qh, ql, bias0, acc0);
+                    split_scores<P, NQB>(ktile + (kb32 + 16 + c) * RS, g, qh, ql, bias1, acc1);
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) lse_block2(M[qb], S[qb], acc0[qb], acc1[qb]);
+                    for (int qb = 0; qb < NQB; ++qb) lse_block2(M[qb], S[qb], acc0[qb], acc1[qb], sc.r);
                 }
             } else {
                 for (int kb16 = 0; kb16 < ntile; kb16 += 16) {
                     const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
                     f4 acc[NQB];
-                    split_scores<P, NQB>(ktile + (kb16 + c) * RS, g, qh, qm, ql, bias, acc);
+                    split_scores<P, NQB>(ktile + (kb16 + c) * RS, g, qh, ql, bias, acc);
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], acc[qb]);
+                    for (int qb = 0; qb < NQB; ++qb) lse_block(M[qb], S[qb], acc[qb], sc.r);
                 }
             }
         }
@@ -443,8 +514,8 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
         // the four lane groups hold disjoint key subsets of the same queries
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-            lse_merge(M[qb], S[qb], __shfl_xor(M[qb], 16), __shfl_xor(S[qb], 16));
-            lse_merge(M[qb], S[qb], __shfl_xor(M[qb], 32), __shfl_xor(S[qb], 32));
+            lse_merge(M[qb], S[qb], __shfl_xor(M[qb], 16), __shfl_xor(S[qb], 16), sc.r);
+            lse_merge(M[qb], S[qb], __shfl_xor(M[qb], 32), __shfl_xor(S[qb], 32), sc.r);
         }
         const bool complete = (j0 == 0 && j1 == A.nk);
         float2* slot = A.part + ((size_t)w * 2 + (u == lo ? 0 : 1)) * A.rpb;
@@ -453,10 +524,11 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
             for (int qb = 0; qb < NQB; ++qb) {
                 const int i = qrow0 + qb * 16 + c;
                 if (i >= A.nq) continue;
+                const float mu = M[qb] * sc.r;  // the running max in base-2 units (exact: a power-of-two scale)
                 if (complete)
-                    finalize(A.fin, i, M[qb] + lg2(S[qb]));
+                    finalize(A.fin, i, mu + lg2(S[qb]));
                 else
-                    slot[wave * (NQB * 16) + qb * 16 + c] = make_float2(M[qb], S[qb]);
+                    slot[wave * (NQB * 16) + qb * 16 + c] = make_float2(mu, S[qb]);
             }
         }
         u += j1 - j0;
@@ -636,10 +708,10 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     constexpr int PS = P + 4;
     constexpr int NB = (MODE == 1 || MODE == 2) ? P / 16 : NP;  // 16-column output blocks (unused in MODE 3)
     constexpr int KP = MODE == 0 ? 16 * NP : 1;  // payload floats per key in LDS
-    using Stage = std::conditional_t<SPLIT, TileStage3<P>, TileStage<P>>;
+    using Stage = std::conditional_t<SPLIT, TileStage2<P>, TileStage<P>>;
     constexpr int TL = Stage::TL;
     constexpr int NQB = transport_nqb(P, NP, MODE);
-    constexpr int LDS_WORDS = SPLIT ? TL * TileStage3<P>::RS * 4 : TL * PS;
+    constexpr int LDS_WORDS = SPLIT ? TL * TileStage2<P>::RS * 4 : TL * PS;
     __shared__ __align__(16) float ktile[LDS_WORDS];
     __shared__ __align__(16) float btile[TL];
     __shared__ __align__(16) float ptile[MODE == 1 ? 1 : TL * KP];
@@ -652,9 +724,12 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     const int c0 = split * A.cols_per_split;
     const int c1 = min(c0 + A.cols_per_split, A.nk);
     const int qrow0 = blockIdx.x * (kWaves * 16 * NQB) + wave * (16 * NQB);
+    // split form: scores come back times sc.t (key biases staged the same way)
+    SplitScale sc{1.0f, 1.0f, 1.0f, kNegBig};
+    if constexpr (SPLIT) sc = split_scale(A.qmax, A.kmax, A.qscale);
 
     float qf[SPLIT ? 1 : NQB][SPLIT ? 1 : KT], vf[MODE == 2 ? NQB : 1][KT];
-    u4v qh[SPLIT ? NQB : 1][SPLIT ? KQ : 1], qm[SPLIT ? NQB : 1][SPLIT ? KQ : 1], ql[SPLIT ? NQB : 1][SPLIT ? KQ : 1];
+    u4v qh[SPLIT ? NQB : 1][SPLIT ? KQ : 1], ql[SPLIT ? NQB : 1][SPLIT ? KQ : 1];
     float lse_c[NQB], S[NQB], Tv[NQB];
     f4 T[NQB][NB];
 #pragma unroll
@@ -662,7 +737,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
         const int i = qrow0 + qb * 16 + c;
         const int ic = i < A.nq ? i : A.nq - 1;
         if constexpr (SPLIT) {
-            load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, qh[qb], qm[qb], ql[qb]);
+            load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, sc.qshift, qh[qb], ql[qb]);
         } else {
             const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
 #pragma unroll
@@ -691,7 +766,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     Stage stage;
     if (c0 < c1) {
         if constexpr (SPLIT)
-            stage.load(kb, A.kbias, c0, c1);
+            stage.load(kb, A.kbias, sc.t, c0, c1);
         else
             stage.load(kp, A.kbias, c0, c1);
     }
@@ -710,7 +785,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
         __syncthreads();
         if (base + TL < c1) {
             if constexpr (SPLIT)
-                stage.load(kb, A.kbias, base + TL, c1);
+                stage.load(kb, A.kbias, sc.t, base + TL, c1);
             else
                 stage.load(kp, A.kbias, base + TL, c1);
         }
@@ -719,8 +794,8 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
             const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
             f4 acc[NQB], dv[NQB];
             if constexpr (SPLIT) {
-                constexpr int RS = TileStage3<P>::RS;
-                split_scores<P, NQB>(reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS, g, qh, qm, ql, bias, acc);
+                constexpr int RS = TileStage2<P>::RS;
+                split_scores<P, NQB>(reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS, g, qh, ql, bias, acc);
             } else {
                 float kf[KT];
                 load_keys<KT>(kf, ktile, (kb16 + c) * PS + g * KT);
@@ -748,7 +823,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
             for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float w = ex2(acc[qb][v] - lse_c[qb]);
+                    const float w = SPLIT ? ex2(fmaf(acc[qb][v], sc.r, -lse_c[qb])) : ex2(acc[qb][v] - lse_c[qb]);
                     S[qb] += w;
                     wv[qb][v] = MODE == 2 ? w * (ptile[kb16 + 4 * g + v] + dv[qb][v]) : w;
                 }
@@ -842,6 +917,7 @@ template <int P, int NP, int MODE>
 hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int KA = (MODE == 1 || MODE == 2) ? P : 16 * NP;
     constexpr int rpb = kWaves * 16 * transport_nqb(P, NP, MODE);
+    if (MODE == 3 && (!a.kb || !a.qmax || !a.kmax)) return hipErrorInvalidValue;
     dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
     SK_LAUNCH_TIMED((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), s, ev0, ev1, a);
     if (a.nsplit > 1)
@@ -865,7 +941,8 @@ hipError_t launch_transport_mfma_pp(const TransArgs& a, int mode, int kwidth, hi
 
 template <int P>
 hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (!a.kb) return hipErrorInvalidValue;  // the split keys are written by every solver set-up
+    // the split keys and the clouds' largest magnitudes are written by every solver set-up
+    if (!a.kb || !a.qmax || !a.kmax) return hipErrorInvalidValue;
     SK_LAUNCH_TIMED(k_pass_mfma<P>, dim3(a.W), dim3(kBlock), s, ev0, ev1, a);
     return launch_merge(a, s);
 }
@@ -973,10 +1050,19 @@ hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s) {
     }
 }
 
-hipError_t launch_split3(const float* in, int64_t rows, int P, uint16_t* out, hipStream_t s) {
+hipError_t launch_split2(const float* in, int64_t rows, int P, const float* kmax, uint16_t* out, hipStream_t s) {
     const int64_t count = rows * P;
-    hipLaunchKernelGGL(k_split3, dim3((unsigned)((count + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, in, count, P,
-                       out);
+    hipLaunchKernelGGL(k_split2, dim3((unsigned)((count + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, in, count, P,
+                       kmax, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_absmax(const float* x, int64_t nx, const float* y, int64_t ny, float* part, float* out,
+                         hipStream_t s) {
+    if (nx % 4 != 0 || ny % 4 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_absmax_part, dim3(kAbsMaxBlocks, 2), dim3(kBlock), 0, s, reinterpret_cast<const float4*>(x),
+                       nx / 4, reinterpret_cast<const float4*>(y), ny / 4, part);
+    hipLaunchKernelGGL(k_absmax_final, dim3(1), dim3(kBlock), 0, s, part, kAbsMaxBlocks, out);
     return hipGetLastError();
 }
 

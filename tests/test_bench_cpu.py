@@ -48,12 +48,15 @@ def test_traffic_record_matches_current_kernels_or_is_absent():
 
 
 def test_split_roofline_model():
-    # the split form: 12 d bf16 flops per pair against 2.5 PFLOP/s, the fp32-equivalent 2 d beside it
+    # the split form: 6 d fp16 flops per pair (three products) against 2.5 PFLOP/s, 8 d at a padded width of
+    # 16 (four products in two instructions); the fp32-equivalent 2 d beside it
     pairs = 16384.0 ** 2
-    r = bench.roofline_split(64, pairs, pairs * 768 / 2500e12)
-    assert abs(r["frac"] - 1.0) < 1e-4 and r["ops_per_pair"] == 768 and r["bound"] == "mfma"
+    r = bench.roofline_split(64, pairs, pairs * 384 / 2500e12)
+    assert abs(r["frac"] - 1.0) < 1e-4 and r["ops_per_pair"] == 384 and r["bound"] == "mfma"
     assert r["fp32_equivalent"]["ops_per_pair"] == 128
-    assert abs(r["fp32_equivalent"]["vs_fp32_mfma_peak"] - 2500.0 / 6 / 157.3) < 1e-3
+    assert abs(r["fp32_equivalent"]["vs_fp32_mfma_peak"] - 2500.0 / 3 / 157.3) < 1e-3
+    assert bench.roofline_split(12, pairs, 1.0)["ops_per_pair"] == 96
+    assert bench.roofline_split(17, pairs, 1.0)["ops_per_pair"] == 102
     assert [bench.packed_stride(d) for d in (9, 16, 17, 32, 33, 64, 65, 256)] == [16, 16, 32, 32, 64, 64, 128, 256]
 
 

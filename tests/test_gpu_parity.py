@@ -78,7 +78,7 @@ SHAPES = [
     (600, 700, 128, 0.5, 5, 21, 0.09, 0.0),
     (300, 500, 256, 0.5, 4, 22, 0.0625, 0.0),
     (17, 5, 64, 0.1, 3, 23, 0.125, 0.0),
-    (1200, 1000, 40, 0.3, 6, 24, 0.15, 0.1),  # the bf16 split form with zero weights (keys of bias -inf)
+    (1200, 1000, 40, 0.3, 6, 24, 0.15, 0.1),  # the fp16 split form with zero weights (keys of bias -inf)
 ]
 
 
@@ -103,12 +103,12 @@ def test_solve_matches_oracle(shape):
     assert abs(c_gpu - c_or) <= 1e-4 * abs(c_or) + 1e-12
 
 
-# The matrix-core pass forms the cross term from a three-part bf16 split of every coordinate (six products,
-# fp32 accumulation; at P = 16 two products share each instruction), which is as accurate as an fp32 dot
-# product. One iteration from g = 0 must then stay within a few float32 roundings of the exponent of the
-# oracle's iterate: 4 kappa eps, kappa as above. (Emulated on the CPU for
-# these inputs, the float32 rounding of q.y alone moves f by 0.07-0.3 kappa eps, the six products add under
-# 0.01 kappa eps, and keeping only the three largest products moves f by 2-7 kappa eps.)
+# The matrix-core pass forms the cross term from a scaled two-part fp16 split of every coordinate (three
+# products hh + hl + lh, fp32 accumulation; at P = 16 all four in two instructions): its error per term is a
+# few float32 unit roundoffs. One iteration from g = 0 must then stay within a few float32 roundings of the
+# exponent of the oracle's iterate: 4 kappa eps, kappa as above. (Emulated on the CPU for these inputs, the
+# float32 rounding of q.y alone moves f by 0.04-0.14 kappa eps and the split by 0.08-0.40 kappa eps, products
+# summed exactly; keeping only the three largest products of a three-part bf16 split would move it by 2-21.)
 SPLIT_SHAPES = [(1500, 1300, 16, 0.05, 81), (1500, 1300, 32, 0.05, 82), (1200, 1100, 64, 0.05, 83),
                 (700, 900, 100, 0.05, 84), (600, 700, 128, 0.05, 85), (300, 500, 256, 0.05, 86),
                 # ragged and tiny: partial 16-query blocks, a partial two-block step, one row or one key
@@ -157,6 +157,49 @@ def test_gradient_flow_workload_end_to_end():
     dg = np.max(np.abs(g - go))
     tol_e2e = tol_eval + 2 * a.max() * 2 * math.sqrt(maxc) * math.expm1(2 * dg / eps)
     assert np.max(np.abs(grad - gr_or)) <= tol_e2e
+
+
+# The split scales each side by a power of two from its cloud's largest |coordinate| (and the query side by
+# 2 log2e / eps as well), so the fp16 operands sit near the top of fp16's range at any data magnitude. These
+# cases move that magnitude far from 1 on one side or both, mix dimensions 1e4 apart, and collapse both
+# clouds onto one point (largest |coordinate| 0); one iteration is held to the same 4 kappa eps.
+def _scaled_problem(case):
+    n, m, d = 700, 900, 64
+    if case == "degenerate":
+        x = np.full((5, d), 0.75, np.float32)
+        return x, x[:3].copy(), np.full(5, 0.2, np.float32), np.full(3, 1.0 / 3.0, np.float32), 0.1
+    x, y, a, b = random_problem(n, m, d, 91, scale=1.0 / math.sqrt(d), shift=0.2)
+    if case == "tiny":
+        return x * np.float32(1e-6), y * np.float32(1e-6), a, b, 5e-14
+    if case == "huge":
+        return x * np.float32(1e4), y * np.float32(1e4), a, b, 5e6
+    if case == "unbalanced":
+        return x * np.float32(1e-3), y * np.float32(1e3), a, b, 5e4
+    if case == "mixed_dims":
+        x[:, : d // 2] *= np.float32(1e-4)
+        y[:, : d // 2] *= np.float32(1e-4)
+        return x, y, a, b, 0.02
+    if case == "small_eps":
+        return x, y, a, b, 2e-4
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("case", ["tiny", "huge", "unbalanced", "mixed_dims", "small_eps", "degenerate"])
+def test_split_scales_at_extreme_magnitudes(case):
+    x, y, a, b, eps = _scaled_problem(case)
+    eps = eps32(eps)
+    say("split scales", case)
+    f, g, _ = gpu_solve(x, y, a, b, eps, 1)
+    fo, go, _ = oracle.sinkhorn(x, y, a, b, eps, 1)
+    maxc = oracle.max_cost(x, y)
+    # kappa plus the float32 precision of the log-weights the biases carry (all that is left when the two
+    # clouds are one point and f, g and the costs vanish)
+    lw = max(np.abs(np.log2(a)).max(), np.abs(np.log2(b)).max())
+    tol = 4 * eps * (kappa(fo, go, maxc, eps) + U32 * lw)
+    assert np.all(np.isfinite(f)) and np.all(np.isfinite(g))
+    say("err/tol f", np.max(np.abs(f - fo)) / tol, "g", np.max(np.abs(g - go)) / tol)
+    assert np.max(np.abs(f - fo)) <= tol
+    assert np.max(np.abs(g - go)) <= tol
 
 
 GRAD_SHAPES = [(1, 5, 2, 0.1, 21), (700, 1300, 3, 0.05, 22), (2100, 2600, 2, 0.02, 23),
