@@ -242,6 +242,21 @@ def run_ceilings():
                                                                       "mfma_bf16_with_8_fma")):
         res[key] = res[name]["ms"] * 1e-3 * CLOCK_HZ / insts_per_simd
     res["exp2_issue_cost"] = res["fma"]["ops_per_s"] / res["exp2"]["ops_per_s"]
+    # fp16 matrix instructions with vector work beside each: SIMD cycles per matrix instruction
+    f16 = {}
+    for kind, name in ((19, "f16_alone"), (20, "f16+8fma"), (21, "f16+4exp"), (22, "f16+3fma+1exp"),
+                       (23, "f16+3fma+1exp_on_results"), (24, "f16+3fma_on_results")):
+        for _ in range(2):
+            lib.sku_launch(kind, blocks, 50, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = lib.sku_launch(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        e1.record()
+        torch.cuda.synchronize()
+        assert rc == 0, rc
+        secs = e0.elapsed_time(e1) * 1e-3
+        f16[name] = {"ms": secs * 1e3, "cycles_per_mfma": secs * CLOCK_HZ / insts_per_simd}
+    res["f16_mfma_mix"] = f16
     # does v_exp_f32 take an issue slot beside FMAs?  NF FMAs + NE exp2 per chain step: times of one launch
     mix = {}
     for kind, nf, ne in ((7, 6, 0), (8, 6, 1), (9, 7, 0), (10, 4, 1), (11, 2, 1), (12, 6, 1), (13, 2, 1), (14, 6, 1),

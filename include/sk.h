@@ -35,10 +35,12 @@
  *    A failed launch returns SK_ERR_HIP.
  *  - Supported dimensions: 1 <= d <= 256.  d <= 8 runs on the vector ALUs;
  *    9 <= d <= 256 computes the x.y cross term of the solver passes on matrix
- *    cores as six bf16 products of a three-part split of each fp32
- *    coordinate, accumulated in fp32 (the dropped terms lie below 2^-26 of
- *    |x_t y_t|, under the rounding of an fp32 dot product).  The workspace
- *    then also holds the keys' bf16 parts, 6 bytes per padded coordinate.
+ *    cores as three fp16 products of a two-part split of each fp32
+ *    coordinate, scaled per cloud by a power of two and accumulated in fp32
+ *    (the error per term lies within 2^-22 of |x_t y_t|, a few roundings of
+ *    an fp32 dot product).  The workspace then also holds the keys' fp16
+ *    parts, 4 bytes per padded coordinate, and each cloud's largest
+ *    |coordinate|.
  *
  * Sources (page title and section):
  *  FS   = "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",

@@ -299,6 +299,50 @@ __global__ __launch_bounds__(256) void k_mfma_bf16_valu(float* out, int iters) {
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// One v_mfma_f32_16x16x32_f16 per chain step with NF FMAs and NE exp2 beside
+// it: independent of the matrix results (DEP = 0), or reading the accumulator
+// of the chain issued kChains / 2 instructions earlier (DEP = 1, as a log-sum-
+// exp over the previous block's scores would).  Whether transcendentals and
+// consumers of matrix results co-execute with the fp16 matrix pipe.
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+template <int NF, int NE, int DEP>
+__global__ __launch_bounds__(256) void k_mfma_f16_mix(float* out, int iters) {
+    const unsigned t = threadIdx.x;
+    const u4v ua = {0x3C003C00u + (t & 7u), 0x38003800u, 0x34003400u, 0x3C003800u};
+    const u4v ub = {0x34003400u, 0x3C003800u + (t & 7u), 0x38003800u, 0x30003000u};
+    const h8 a = __builtin_bit_cast(h8, ua), b = __builtin_bit_cast(h8, ub);
+    f4 acc[kChains];
+    float v[NF > 0 ? NF : 1], e[NE > 0 ? NE : 1];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = f4{0.0f, 0.0f, 0.0f, (float)c};
+#pragma unroll
+    for (int x = 0; x < (NF > 0 ? NF : 1); ++x) v[x] = t * 1e-3f + x;
+#pragma unroll
+    for (int x = 0; x < (NE > 0 ? NE : 1); ++x) e[x] = t * 1e-4f + 0.25f * x;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int c = 0; c < kChains; ++c) {
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+                const f4 src = acc[(c + kChains / 2) % kChains];
+#pragma unroll
+                for (int x = 0; x < NF; ++x) v[x] = DEP ? fmaf(src[x & 3], 1e-12f, v[x]) : fmaf(v[x], 0.999f, 1e-3f);
+#pragma unroll
+                for (int x = 0; x < NE; ++x)
+                    e[x] = DEP ? __builtin_amdgcn_exp2f(fmaf(src[x & 3], -1e-12f, -e[x])) : __builtin_amdgcn_exp2f(-e[x]);
+            }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][3];
+#pragma unroll
+    for (int x = 0; x < NF; ++x) s += v[x];
+#pragma unroll
+    for (int x = 0; x < NE; ++x) s += e[x];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,7 +352,10 @@ extern "C" {
 // iters * 64 v_mfma_f32_16x16x4f32 (2048 flops each); kind 4: each wave issues
 // iters * 64 v_mfma_f32_32x32x2f32 (4096 flops each); kind 5: each wave issues
 // iters * 64 v_mfma_f32_16x16x32_bf16 (16384 flops each); kind 6: as kind 5
-// with 8 vector FMAs per matrix instruction.  kind 18: iters device-wide
+// with 8 vector FMAs per matrix instruction.  kinds 19-24: each wave issues
+// iters * 64 v_mfma_f32_16x16x32_f16 with (FMAs, exp2) beside each: (0, 0),
+// (8, 0), (0, 4), (3, 1), and (3, 1), (3, 0) reading earlier matrix results.
+// kind 18: iters device-wide
 // barriers under a cooperative launch (refused with an error when the grid
 // cannot be resident at once).  Launches `blocks` x 256 threads; out must
 // hold blocks * 256 floats.  Returns a hipError_t.
@@ -350,6 +397,18 @@ int sku_launch(int kind, int blocks, int iters, float* out, void* stream) {
         hipLaunchKernelGGL((k_valu_op<1>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
     else if (kind == 17)
         hipLaunchKernelGGL((k_valu_op<2>), dim3(blocks), dim3(256), 0, s, out, iters, 0.999f, 1e-3f);
+    else if (kind == 19)
+        hipLaunchKernelGGL((k_mfma_f16_mix<0, 0, 0>), dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 20)
+        hipLaunchKernelGGL((k_mfma_f16_mix<8, 0, 0>), dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 21)
+        hipLaunchKernelGGL((k_mfma_f16_mix<0, 4, 0>), dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 22)
+        hipLaunchKernelGGL((k_mfma_f16_mix<3, 1, 0>), dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 23)
+        hipLaunchKernelGGL((k_mfma_f16_mix<3, 1, 1>), dim3(blocks), dim3(256), 0, s, out, iters);
+    else if (kind == 24)
+        hipLaunchKernelGGL((k_mfma_f16_mix<3, 0, 1>), dim3(blocks), dim3(256), 0, s, out, iters);
     else if (kind == 18) {
         void* args[] = {&out, &iters};
         return (int)hipLaunchCooperativeKernel(reinterpret_cast<void*>(k_grid_sync), dim3(blocks), dim3(256), args,
