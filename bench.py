@@ -171,6 +171,27 @@ def roofline_split(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict
             "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
 
 
+def roofline_transport_split(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int) -> dict:
+    """Matrix-core roofline of one transport-product launch for d > 8 carrying `payload` columns (at most the
+    library's chunk: 64 from a padded width of 64, else 16): the scores in the fp16 split form (6 d fp16 flops
+    per pair, 8 d at a padded width of 16) and the weighted sums on fp32 matrix instructions (2 per column of
+    the launch's 16- or 64-column tile). The ceiling is the time the matrix pipe needs for both at their own
+    dense peaks; `achieved` and `peak` are stated in the method's flops per pair (2 d + 2 x payload), `peak`
+    being the rate that pipe time allows."""
+    f16_ops = (8 if packed_stride(d) == 16 else 6) * d
+    cols = 16 if payload <= 16 else 64
+    pipe_s_per_pair = f16_ops / (MFMA_F16_PEAK_TFLOPS * 1e12) + 2 * cols / (MFMA_FP32_PEAK_TFLOPS * 1e12)
+    ops = 2 * d + 2 * payload
+    achieved = pairs_per_launch * ops / avg_launch_s / 1e12
+    peak = ops / pipe_s_per_pair / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None, "ops_per_pair": ops,
+            "mfma_dtype": "fp16 split scores (%d flops per pair), fp32 weighted sums (%d)" % (f16_ops, 2 * cols),
+            "fp32_equivalent": {"achieved": round(achieved, 3), "ops_per_pair": ops,
+                                "vs_fp32_mfma_peak": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4)},
+            "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
+
+
 # Sources that determine each timed kernel's code (plus the device flags).
 KERNEL_SOURCES = {
     "valu": ["sk_pass_valu.hip", "sk_pass_common.hpp", "sk_internal.hpp"],
@@ -561,6 +582,8 @@ def main():
             roof["kernel"] = f"k_pass_sparse<{d}>"
     elif mode in ("hvp", "transport"):
         payload = 1 if mode == "hvp" else d  # columns of the dominant launches (CG steps / the product)
+        if d > 8 and payload > 1:
+            payload = min(payload, 64 if packed_stride(d) >= 64 else 16)  # one launch's chunk of columns
         if d <= 8:
             roof = roofline_alu(d, pairs_per_launch, avg_launch_s, payload)
             roof["kernel"] = "k_transport<%d,%d,0>" % (d, 1 if payload == 1 else (4 if payload <= 4 else 9))
@@ -570,10 +593,10 @@ def main():
                 # the one-column kernel forms its scores in the split form (payload FMAs on the vector ALUs)
                 roof = roofline_split(d, pairs_per_launch, avg_launch_s)
             else:
-                roof = roofline_mfma(d, pairs_per_launch, avg_launch_s, payload)
+                roof = roofline_transport_split(d, pairs_per_launch, avg_launch_s, payload)
             # one column: MODE 3 (vector-ALU payload); d columns: 16- or 64-column tiles (MODE 0)
             roof["kernel"] = ("k_transport_mfma<%d,1,3>" % p2 if payload == 1 else
-                              "k_transport_mfma<%d,%d,0>" % (p2, 1 if d <= 16 else 4))
+                              "k_transport_mfma<%d,%d,0>" % (p2, 4 if payload > 16 else 1))
     elif d <= 8:
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s)
         small = pairs_per_launch <= 2.0e6  # the library's single-kernel path for small passes

@@ -32,6 +32,7 @@ constexpr int64_t kTargetGroups = 2048;  // workgroups per pass: 8 per CU on 256
 // where an iteration takes ~10 us and a check's host round trip ~25 us).
 constexpr double kDeferPairs = 4.2e6;
 constexpr int64_t kMinColsPerSplit = 512;
+constexpr int kMfmaGradSplitRows = 64;  // rows per block that bound the matrix-core gradient's key splits
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -87,7 +88,9 @@ int rows_per_block(int d) {
 
 // Key-range split of the gradient pass (a plain split grid: it runs once per solve).
 Split grad_split(int64_t n, int64_t m, int d) {
-    return split_for(n, m, d <= kValuMaxD ? valu_block_rows() : mfma_grad_rows_per_block());
+    // d > 8: the bound of the matrix-core gradient's key splits (64-row blocks), which sizes its partials; the
+    // kernel runs as few splits as keep its workgroups resident, at most this many
+    return split_for(n, m, d <= kValuMaxD ? valu_block_rows() : kMfmaGradSplitRows);
 }
 
 // Upper bound on the workgroups of a streamed pass, from the sizes alone (the
@@ -726,32 +729,62 @@ int grad_core(const Ws& W, const float* x, const float* y, const float* a, const
     if (L.mfma && (cap = pass_capacity(d)) <= 0) return SK_ERR_HIP;
     if ((st = prepare(W, x, y, a, b, eps, 0, nullptr, 2, g, s))) return st;
 
-    GradArgs ga{};
-    const Split sp = grad_split(n, m, d);
-    ga.q = W.f(L.xp);
-    ga.k = W.f(L.yp);
-    ga.kbias = L.mfma ? W.f(L.hy) : nullptr;
-    ga.nq = (int)n;
-    ga.nk = (int)m;
-    ga.P = L.P;
-    ga.d = d;
-    ga.qscale = 2.0f * kLog2e / eps;
-    ga.cols_per_split = sp.cols;
-    ga.nsplit = sp.nsplit;
-    ga.part = reinterpret_cast<float2*>(W.base + L.part);
-    ga.partA = W.f(L.partA);
-    ga.w = a;
-    ga.grad = grad;
     if (!L.mfma) {
+        GradArgs ga{};
+        const Split sp = grad_split(n, m, d);
+        ga.q = W.f(L.xp);
+        ga.k = W.f(L.yp);
+        ga.kbias = nullptr;
+        ga.nq = (int)n;
+        ga.nk = (int)m;
+        ga.P = L.P;
+        ga.d = d;
+        ga.qscale = 2.0f * kLog2e / eps;
+        ga.cols_per_split = sp.cols;
+        ga.nsplit = sp.nsplit;
+        ga.part = reinterpret_cast<float2*>(W.base + L.part);
+        ga.partA = W.f(L.partA);
+        ga.w = a;
+        ga.grad = grad;
         SK_TRY(launch_grad_valu(ga, s));
         return SK_OK;
     }
     // d > 8: first the row lse of the same scores, then the weighted key sums
+    // (transport mode 4), with no more key splits than the workspace holds
     PassArgs lse_pass = make_pass(W, true, eps, a, cap);
     lse_pass.fin.mode = kFinStore;
     if ((st = run_pass(W, lse_pass, s))) return st;
-    ga.lse = W.f(L.lse_r);
-    SK_TRY(launch_grad_mfma(ga, s));
+    const int rpb = mfma_grad_rows_per_block(L.P);
+    const int gcap = transport_capacity_cached(L, 4, 16);
+    if (gcap <= 0) return SK_ERR_HIP;
+    Split sp = split_resident(n, m, rpb, gcap);
+    const Split lim = grad_split(n, m, d);  // the workspace holds this many splits' partials
+    if (sp.nsplit > lim.nsplit) {
+        const int64_t cols = (m + lim.nsplit - 1) / lim.nsplit;
+        sp = Split{(int)((m + cols - 1) / cols), (int)cols};
+    }
+    TransArgs t{};
+    t.q = W.f(L.xp);
+    t.k = W.f(L.yp);
+    t.kbias = W.f(L.hy);
+    t.kb = W.h(L.yb);
+    t.qmax = W.f(L.amax);
+    t.kmax = W.f(L.amax) + 1;
+    t.lse = W.f(L.lse_r);
+    t.nq = (int)n;
+    t.nk = (int)m;
+    t.P = L.P;
+    t.d = d;
+    t.qscale = 2.0f * kLog2e / eps;
+    t.cols_per_split = sp.cols;
+    t.nsplit = sp.nsplit;
+    t.part = reinterpret_cast<float2*>(W.base + L.part);
+    t.partA = W.f(L.partA);
+    t.out = grad;
+    t.ldo = d;
+    t.kout = d;
+    t.gw = a;
+    SK_TRY(launch_transport_mfma(t, 4, 16, s));
     return SK_OK;
 }
 

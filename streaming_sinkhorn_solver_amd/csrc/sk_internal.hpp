@@ -201,6 +201,7 @@ struct TransArgs {
     float* out;          // out[i * ldo + c], c < kout
     int ldo, kout, ldp, kin;
     float* mass;         // [nq] row sums of the plan, or null
+    const float* gw;     // matrix-core gradient (mode 4): the row weights a [nq], else null
 };
 
 // Workspace carve-up, a pure function of (n, m, d).
@@ -346,8 +347,8 @@ constexpr int kAbsMaxBlocks = 256;
 hipError_t launch_absmax(const float* x, int64_t nx, const float* y, int64_t ny, float* part, float* out,
                          hipStream_t s);
 // Matrix-core gradient pass (needs the row lse of the same scores); rows per workgroup.
-hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
-int mfma_grad_rows_per_block();
+// Rows per workgroup of the matrix-core gradient (transport mode 4) at padded stride P.
+int mfma_grad_rows_per_block(int P);
 // Workgroups of the d-dimensional pass kernel resident at once on the current
 // device (CUs x occupancy), 0 on failure.
 int valu_pass_capacity(int d);

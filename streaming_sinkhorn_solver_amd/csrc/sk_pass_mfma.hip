@@ -45,9 +45,6 @@ constexpr int kWaves = kBlock / 64;
 #ifndef SK_MFMA_NQB
 #define SK_MFMA_NQB 4
 #endif
-#ifndef SK_MFMA_TILE_FLOATS
-#define SK_MFMA_TILE_FLOATS 8192
-#endif
 
 // 16-query blocks per wave (register budget: NQB * P / 4 query VGPRs)
 template <int P>
@@ -55,28 +52,18 @@ constexpr int mfma_nqb() {
     return P <= 64 ? SK_MFMA_NQB : (P == 128 ? 2 : 1);
 }
 
-// keys per LDS tile (about SK_MFMA_TILE_FLOATS floats of coordinates)
-template <int P>
-constexpr int mfma_tile_keys() {
-    return SK_MFMA_TILE_FLOATS / P < 16 ? 16 : SK_MFMA_TILE_FLOATS / P;
-}
-
-// Register staging of one LDS tile of TL keys: each thread holds kStageF4
-// float4s of coordinates and up to kStageB biases.  Loads are unconditional
-// (clamped to the last valid key) and issued back to back, so a tile costs one
-// memory latency, and the loads for the next tile are issued before the
-// current tile is computed.
-template <int P>
-struct TileStage {
-    static constexpr int TL = mfma_tile_keys<P>();
+// Register staging of one fp32 LDS tile of TL keys (coordinates only; the
+// payload modes read a key's coordinates as their second operand): each
+// thread holds F4 float4s.  Loads are unconditional (clamped to the last valid
+// key) and issued back to back, so a tile costs one memory latency, and the
+// loads for the next tile are issued before the current tile is computed.
+template <int P, int TL>
+struct TileStageF {
     static constexpr int F4 = TL * (P / 4) / kBlock;
-    static constexpr int NB = (TL + kBlock - 1) / kBlock;
     static_assert(TL * (P / 4) % kBlock == 0, "tile must split evenly over the workgroup");
     float4 v[F4];
-    float b[NB];
 
-    __device__ __forceinline__ void load(const float4* __restrict__ kp, const float* __restrict__ kbias, int base,
-                                         int j1) {
+    __device__ __forceinline__ void load(const float4* __restrict__ kp, int base, int j1) {
 #pragma unroll
         for (int r = 0; r < F4; ++r) {
             const int e = threadIdx.x + r * kBlock;
@@ -85,26 +72,15 @@ struct TileStage {
             const float4 x = kp[(size_t)min(col, j1 - 1) * (P / 4) + part];
             v[r] = col < j1 ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
-#pragma unroll
-        for (int r = 0; r < NB; ++r) {
-            const int col = base + threadIdx.x + r * kBlock;
-            const float x = kbias[min(col, j1 - 1)];
-            b[r] = col < j1 ? x : -INFINITY;
-        }
     }
 
-    __device__ __forceinline__ void store(float* ktile, float* btile) const {
+    __device__ __forceinline__ void store(float* ktile) const {
         constexpr int PS = P + 4;
 #pragma unroll
         for (int r = 0; r < F4; ++r) {
             const int e = threadIdx.x + r * kBlock;
             const int key = e / (P / 4), part = e - key * (P / 4);
             *reinterpret_cast<float4*>(&ktile[key * PS + part * 4]) = v[r];
-        }
-#pragma unroll
-        for (int r = 0; r < NB; ++r) {
-            const int k = threadIdx.x + r * kBlock;
-            if (k < TL) btile[k] = b[r];
         }
     }
 };
@@ -535,186 +511,51 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
     }
 }
 
-// Gradient for d > 8: T_i = sum_j w_ij y_j with w_ij = 2^{s_ij - lse_i}, the
-// row lse coming from a first streamed pass over the same scores (so every
-// w_ij <= 1 and no rescaling is needed).  Per 16-key block the scores are
-// recomputed on the matrix cores exactly as in the pass, and T accumulates
-// with a second MFMA: A = weights (16 queries x 4 keys per step; a lane's own
-// four weights, keys 4g + v, are exactly its A operand for steps v = 0..3),
-// B = the block's key coordinates (4 keys x 16 dims, read from the LDS tile).
-// The output tile of dims [16 nb, 16 nb + 16) leaves lane l holding
-// T[query 4(l/16) + v][dim 16 nb + l%16].  grad_i = 2 a_i (x~_i - T_i / S_i)
-// with S_i = sum_j w_ij (1 up to rounding).  One 16-query block per wave; the
-// key range is split across workgroups (blockIdx.y) and partial (S, T) are
-// plain sums.
-template <int P>
-__global__ __launch_bounds__(kBlock) void k_grad_mfma(GradArgs A) {
-    constexpr int KT = P / 4;
-    constexpr int PS = P + 4;
-    constexpr int NB = P / 16;  // 16-dim output blocks
-    constexpr int TL = mfma_tile_keys<P>();
-    __shared__ __align__(16) float ktile[TL * PS];
-    __shared__ __align__(16) float btile[TL];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, c = lane & 15;
-    const float4* kp = reinterpret_cast<const float4*>(A.k);
-    const int split = blockIdx.y;
-    const int c0 = split * A.cols_per_split;
-    const int c1 = min(c0 + A.cols_per_split, A.nk);
-    const int qrow0 = blockIdx.x * (kWaves * 16) + wave * 16;
-
-    float qf[KT];
-    {
-        const int i = qrow0 + c;
-        const int ic = i < A.nq ? i : A.nq - 1;
-        const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
-#pragma unroll
-        for (int t4 = 0; t4 < KT / 4; ++t4) {
-            const float4 v = qr[t4];
-            qf[4 * t4 + 0] = v.x * A.qscale;
-            qf[4 * t4 + 1] = v.y * A.qscale;
-            qf[4 * t4 + 2] = v.z * A.qscale;
-            qf[4 * t4 + 3] = v.w * A.qscale;
-        }
-    }
-    const float lse_c = A.lse[min(qrow0 + c, A.nq - 1)];
-    float S = 0.0f;
-    f4 T[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) T[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    TileStage<P> stage;
-    if (c0 < c1) stage.load(kp, A.kbias, c0, c1);
-    for (int base = c0; base < c1; base += TL) {
-        __syncthreads();
-        stage.store(ktile, btile);
-        __syncthreads();
-        if (base + TL < c1) stage.load(kp, A.kbias, base + TL, c1);
-        const int ntile = min(TL, c1 - base);
-        for (int kb = 0; kb < ntile; kb += 16) {
-            float kf[KT];
-            const float4* kr = reinterpret_cast<const float4*>(&ktile[(kb + c) * PS + g * KT]);
-#pragma unroll
-            for (int t4 = 0; t4 < KT / 4; ++t4) {
-                const float4 v = kr[t4];
-                kf[4 * t4 + 0] = v.x;
-                kf[4 * t4 + 1] = v.y;
-                kf[4 * t4 + 2] = v.z;
-                kf[4 * t4 + 3] = v.w;
-            }
-            f4 acc = *reinterpret_cast<const f4*>(&btile[kb + 4 * g]);
-#pragma unroll
-            for (int t = 0; t < KT; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[t], acc, 0, 0, 0);
-            float wv[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                wv[v] = ex2(acc[v] - lse_c);
-                S += wv[v];
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    T[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[v], ktile[(kb + 4 * g + v) * PS + nb * 16 + c],
-                                                                 T[nb], 0, 0, 0);
-        }
-    }
-    // S: lane (g, c) summed keys 4g.. of query c; join the four groups
-    S += __shfl_xor(S, 16);
-    S += __shfl_xor(S, 32);
-    if (A.nsplit == 1) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int qi = 4 * g + v;                 // query of T[nb][v] in this lane
-            const float Sq = __shfl(S, qi);           // lane qi holds query qi's S
-            const int i = qrow0 + qi;
-            if (i >= A.nq) continue;
-            const float two_w = 2.0f * A.w[i];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int dim = nb * 16 + c;
-                if (dim < A.d) A.grad[(size_t)i * A.d + dim] = two_w * (A.q[(size_t)i * P + dim] - T[nb][v] / Sq);
-            }
-        }
-    } else {
-        if (g == 0 && qrow0 + c < A.nq) A.part[(size_t)split * A.nq + qrow0 + c] = make_float2(0.0f, S);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int i = qrow0 + 4 * g + v;
-            if (i >= A.nq) continue;
-            float* pa = A.partA + ((size_t)split * A.nq + i) * P;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) pa[nb * 16 + c] = T[nb][v];
-        }
-    }
-}
-
-// Sums the split partials (S, T) of the matrix-core gradient in split order.
-__global__ __launch_bounds__(kBlock) void k_grad_mfma_merge(GradArgs A) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= (int64_t)A.nq * A.d) return;
-    const int i = (int)(t / A.d), dim = (int)(t - (int64_t)i * A.d);
-    float S = 0.0f, T = 0.0f;
-    for (int s = 0; s < A.nsplit; ++s) {
-        S += A.part[(size_t)s * A.nq + i].y;
-        T += A.partA[((size_t)s * A.nq + i) * A.P + dim];
-    }
-    A.grad[t] = 2.0f * A.w[i] * (A.q[(size_t)i * A.P + dim] - T / S);
-}
-
-template <int P>
-hipError_t launch_grad_mfma_p(const GradArgs& a, hipStream_t s) {
-    dim3 grid((a.nq + kWaves * 16 - 1) / (kWaves * 16), a.nsplit);
-    hipLaunchKernelGGL(k_grad_mfma<P>, grid, dim3(kBlock), 0, s, a);
-    if (a.nsplit > 1)
-        hipLaunchKernelGGL(k_grad_mfma_merge, dim3((unsigned)(((int64_t)a.nq * a.d + kBlock - 1) / kBlock)),
-                           dim3(kBlock), 0, s, a);
-    return hipGetLastError();
-}
-
-
 // Transport products for d > 8 (see sk_transport.hip for the d <= 8 kernel and
-// the quantities).  As in the gradient, w_ij = 2^{s_ij - lse_i} <= 1 with lse
-// from a first pass over the same scores, and the payload sums accumulate with
-// a second MFMA whose A operand is the lane's own four weights:
+// the quantities).  w_ij = 2^{s_ij - lse_i} <= 1 with lse from a first pass
+// over the same scores, and the payload sums accumulate with a second MFMA
+// whose A operand is the lane's own four weights:
 //   T_i[col] = sum_j w_ij psi_j[col],   P psi = 2^{lse_i + h_i} T_i,
 //   row mass = 2^{lse_i + h_i} sum_j w_ij.
 //  MODE 0: psi_j = NP payload columns (16 * NP, zero-padded) staged in LDS;
-//  MODE 1: psi_j = the key's coordinates (read from the key tile);
+//  MODE 1: psi_j = the key's coordinates (read from an fp32 key tile);
 //  MODE 2: the key's coordinates with w_ij (pay_j + <y~_j, 2 v_i>), the inner
-//          product taken on the matrix cores like the score;
+//          product taken on fp32 matrix instructions like the weighted sums;
 //  MODE 3: one payload column, summed with four vector FMAs per lane and
-//          16 keys (a 16-column MFMA tile would be 15/16 padding).
+//          16 keys (a 16-column MFMA tile would be 15/16 padding);
+//  MODE 4: the gradient in x at fixed g: T_i as in MODE 1, then
+//          grad_i = 2 a_i (x~_i - T_i / S_i), S_i = sum_j w_ij (the plan's
+//          barycentric map; the plan scale cancels).
+// Every mode forms its scores in the fp16 split form of the solver pass (same
+// helpers and scales); the weighted sums keep fp32 matrix instructions.
 // 16-query blocks per wave of the transport kernel: their MFMA chains
-// interleave, at a register cost of NQB * P / 4 query VGPRs plus NQB output
-// tiles.  Measured at d = 64 (16384 x 16384): the 64-column product takes
-// 1019 / 727 / 606 us with 1 / 2 / 4 blocks, the per-row-direction pass
-// (MODE 2, 2 NQB P / 4 query VGPRs) 797 / 785 / 902 us, the single-column
-// product 402 / 355 / 358 us.
+// interleave, at a register cost of NQB * P / 8 query VGPRs plus NQB output
+// tiles.
 constexpr int transport_nqb(int P, int NP, int MODE) {
-    // the one-column kernel (split form): 4 blocks, 151 against 171 us with 2 at 16384^2, d = 64; an HVP
-    // at d = 16 4.93 against 5.18 ms
+    // the one-column kernel: 4 blocks, 151 against 171 us with 2 at 16384^2, d = 64 (bf16 split form); an
+    // HVP at d = 16 4.93 against 5.18 ms
     const int base = ((MODE == 0 && NP > 1) || MODE == 3) ? 4 : 2;
     return P <= 64 ? base : (P == 128 ? base / 2 : 1);
 }
 
 template <int P, int NP, int MODE>
 __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
-    // one payload column (MODE 3, the conjugate-gradient product) takes the split form from P = 32
-    constexpr bool SPLIT = MODE == 3;
     constexpr int KT = P / 4;
     constexpr int KQ = split_qops<P>();
     constexpr int PS = P + 4;
-    constexpr int NB = (MODE == 1 || MODE == 2) ? P / 16 : NP;  // 16-column output blocks (unused in MODE 3)
-    constexpr int KP = MODE == 0 ? 16 * NP : 1;  // payload floats per key in LDS
-    using Stage = std::conditional_t<SPLIT, TileStage2<P>, TileStage<P>>;
+    constexpr bool KEYS = MODE == 1 || MODE == 2 || MODE == 4;  // the fp32 key coordinates are an operand
+    constexpr int NB = KEYS ? P / 16 : NP;                       // 16-column output blocks (unused in MODE 3)
+    constexpr int KP = MODE == 0 ? 16 * NP : 1;                  // payload floats per key in LDS
+    constexpr bool PAY = MODE == 0 || MODE == 2 || MODE == 3;    // a payload tile
+    using Stage = TileStage2<P>;
+    using FStage = TileStageF<P, Stage::TL>;
     constexpr int TL = Stage::TL;
+    constexpr int RS = Stage::RS;
     constexpr int NQB = transport_nqb(P, NP, MODE);
-    constexpr int LDS_WORDS = SPLIT ? TL * TileStage2<P>::RS * 4 : TL * PS;
-    __shared__ __align__(16) float ktile[LDS_WORDS];
+    __shared__ u4v ktile[TL * RS];
+    __shared__ __align__(16) float ftile[KEYS ? TL * PS : 1];
     __shared__ __align__(16) float btile[TL];
-    __shared__ __align__(16) float ptile[MODE == 1 ? 1 : TL * KP];
+    __shared__ __align__(16) float ptile[PAY ? TL * KP : 1];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
@@ -724,31 +565,18 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     const int c0 = split * A.cols_per_split;
     const int c1 = min(c0 + A.cols_per_split, A.nk);
     const int qrow0 = blockIdx.x * (kWaves * 16 * NQB) + wave * (16 * NQB);
-    // split form: scores come back times sc.t (key biases staged the same way)
-    SplitScale sc{1.0f, 1.0f, 1.0f, kNegBig};
-    if constexpr (SPLIT) sc = split_scale(A.qmax, A.kmax, A.qscale);
+    // scores come back times sc.t (key biases staged the same way)
+    const SplitScale sc = split_scale(A.qmax, A.kmax, A.qscale);
 
-    float qf[SPLIT ? 1 : NQB][SPLIT ? 1 : KT], vf[MODE == 2 ? NQB : 1][KT];
-    u4v qh[SPLIT ? NQB : 1][SPLIT ? KQ : 1], ql[SPLIT ? NQB : 1][SPLIT ? KQ : 1];
+    float vf[MODE == 2 ? NQB : 1][KT];
+    u4v qh[NQB][KQ], ql[NQB][KQ];
     float lse_c[NQB], S[NQB], Tv[NQB];
     f4 T[NQB][NB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
         const int i = qrow0 + qb * 16 + c;
         const int ic = i < A.nq ? i : A.nq - 1;
-        if constexpr (SPLIT) {
-            load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, sc.qshift, qh[qb], ql[qb]);
-        } else {
-            const float4* qr = reinterpret_cast<const float4*>(A.q + (size_t)ic * P + g * KT);
-#pragma unroll
-            for (int t4 = 0; t4 < KT / 4; ++t4) {
-                const float4 v = qr[t4];
-                qf[qb][4 * t4 + 0] = v.x * A.qscale;
-                qf[qb][4 * t4 + 1] = v.y * A.qscale;
-                qf[qb][4 * t4 + 2] = v.z * A.qscale;
-                qf[qb][4 * t4 + 3] = v.w * A.qscale;
-            }
-        }
+        load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, sc.qshift, qh[qb], ql[qb]);
         if (MODE == 2) {
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
@@ -764,19 +592,16 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     }
 
     Stage stage;
+    FStage fstage;
     if (c0 < c1) {
-        if constexpr (SPLIT)
-            stage.load(kb, A.kbias, sc.t, c0, c1);
-        else
-            stage.load(kp, A.kbias, c0, c1);
+        stage.load(kb, A.kbias, sc.t, c0, c1);
+        if constexpr (KEYS) fstage.load(kp, c0, c1);
     }
     for (int base = c0; base < c1; base += TL) {
         __syncthreads();
-        if constexpr (SPLIT)
-            stage.store(reinterpret_cast<u4v*>(ktile), btile);
-        else
-            stage.store(ktile, btile);
-        if (MODE != 1)
+        stage.store(ktile, btile);
+        if constexpr (KEYS) fstage.store(ftile);
+        if constexpr (PAY)
             for (int e = threadIdx.x; e < TL * KP; e += kBlock) {
                 const int col = base + e / KP;
                 const int cc = e % KP;
@@ -784,50 +609,39 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
             }
         __syncthreads();
         if (base + TL < c1) {
-            if constexpr (SPLIT)
-                stage.load(kb, A.kbias, sc.t, base + TL, c1);
-            else
-                stage.load(kp, A.kbias, base + TL, c1);
+            stage.load(kb, A.kbias, sc.t, base + TL, c1);
+            if constexpr (KEYS) fstage.load(kp, base + TL, c1);
         }
         const int ntile = min(TL, c1 - base);
         for (int kb16 = 0; kb16 < ntile; kb16 += 16) {
             const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
             f4 acc[NQB], dv[NQB];
-            if constexpr (SPLIT) {
-                constexpr int RS = TileStage2<P>::RS;
-                split_scores<P, NQB>(reinterpret_cast<const u4v*>(ktile) + (kb16 + c) * RS, g, qh, ql, bias, acc);
-            } else {
+            split_scores<P, NQB>(ktile + (kb16 + c) * RS, g, qh, ql, bias, acc);
+            if constexpr (MODE == 2) {
                 float kf[KT];
-                load_keys<KT>(kf, ktile, (kb16 + c) * PS + g * KT);
+                load_keys<KT>(kf, ftile, (kb16 + c) * PS + g * KT);
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
-                    acc[qb] = bias;
-                    dv[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-                }
+                for (int qb = 0; qb < NQB; ++qb) dv[qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int t = 0; t < KT; ++t)
 #pragma unroll
                     for (int qb = 0; qb < NQB; ++qb)
-                        acc[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], qf[qb][t], acc[qb], 0, 0, 0);
-                if (MODE == 2) {
-#pragma unroll
-                    for (int t = 0; t < KT; ++t)
-#pragma unroll
-                        for (int qb = 0; qb < NQB; ++qb)
-                            dv[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], vf[MODE == 2 ? qb : 0][t], dv[qb], 0,
-                                                                          0, 0);
-                }
+                        dv[qb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t], vf[MODE == 2 ? qb : 0][t], dv[qb], 0, 0,
+                                                                      0);
             }
             float wv[NQB][4];
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float w = SPLIT ? ex2(fmaf(acc[qb][v], sc.r, -lse_c[qb])) : ex2(acc[qb][v] - lse_c[qb]);
+                    const float w = ex2(fmaf(acc[qb][v], sc.r, -lse_c[qb]));
                     S[qb] += w;
-                    wv[qb][v] = MODE == 2 ? w * (ptile[kb16 + 4 * g + v] + dv[qb][v]) : w;
+                    if constexpr (MODE == 2)
+                        wv[qb][v] = w * (ptile[kb16 + 4 * g + v] + dv[qb][v]);
+                    else
+                        wv[qb][v] = w;
                 }
-            if (MODE == 3) {
+            if constexpr (MODE == 3) {
                 // one payload column: four FMAs per lane beat a 16-column MFMA tile
                 const f4 pv = *reinterpret_cast<const f4*>(&ptile[kb16 + 4 * g]);
 #pragma unroll
@@ -840,7 +654,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const float b = MODE == 0 ? ptile[(kb16 + 4 * g + v) * KP + nb * 16 + c]
-                                                  : ktile[(kb16 + 4 * g + v) * PS + nb * 16 + c];
+                                                  : ftile[(kb16 + 4 * g + v) * PS + nb * 16 + c];
 #pragma unroll
                         for (int qb = 0; qb < NQB; ++qb)
                             T[qb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[qb][v], b, T[qb][nb], 0, 0, 0);
@@ -861,7 +675,22 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
             Tq += __shfl_xor(Tq, 16);
             Tq += __shfl_xor(Tq, 32);
         }
-        if (A.nsplit == 1) {
+        if (A.nsplit == 1 && MODE == 4) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int qi = 4 * g + v;        // query of T[qb][nb][v] in this lane
+                const float Si = __shfl(Sq, qi);  // lane qi holds query qi's sum
+                const int i = q0 + qi;
+                if (i >= A.nq) continue;
+                const float two_w = 2.0f * A.gw[i];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int dim = nb * 16 + c;
+                    if (dim < A.kout)
+                        A.out[(size_t)i * A.ldo + dim] = two_w * (A.q[(size_t)i * P + dim] - T[qb][nb][v] / Si);
+                }
+            }
+        } else if (A.nsplit == 1) {
             if (g == 0 && q0 + c < A.nq) {
                 const int i = q0 + c;
                 const float scale = ex2(A.lse[i] + A.qbias[i]);
@@ -913,14 +742,33 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma_merge(TransArgs A, in
     }
 }
 
+// MODE 4 with a split key range: sums the partials (S, T) in split order and
+// writes grad_i = 2 a_i (x~_i - T_i / S_i).
+__global__ __launch_bounds__(kBlock) void k_transport_grad_merge(TransArgs A) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)A.nq * A.kout) return;
+    const int i = (int)(t / A.kout), dim = (int)(t - (int64_t)i * A.kout);
+    float S = 0.0f, T = 0.0f;
+    for (int s = 0; s < A.nsplit; ++s) {
+        S += A.part[(size_t)s * A.nq + i].y;
+        T += A.partA[((size_t)s * A.nq + i) * A.P + dim];
+    }
+    A.out[(size_t)i * A.ldo + dim] = 2.0f * A.gw[i] * (A.q[(size_t)i * A.P + dim] - T / S);
+}
+
 template <int P, int NP, int MODE>
 hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    constexpr int KA = (MODE == 1 || MODE == 2) ? P : 16 * NP;
+    constexpr int KA = (MODE == 1 || MODE == 2 || MODE == 4) ? P : 16 * NP;
     constexpr int rpb = kWaves * 16 * transport_nqb(P, NP, MODE);
-    if (MODE == 3 && (!a.kb || !a.qmax || !a.kmax)) return hipErrorInvalidValue;
+    // the split keys and the clouds' largest magnitudes are written by every set-up
+    if (!a.kb || !a.qmax || !a.kmax) return hipErrorInvalidValue;
+    if (MODE == 4 && (!a.gw || a.kout > P)) return hipErrorInvalidValue;
     dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
     SK_LAUNCH_TIMED((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), s, ev0, ev1, a);
-    if (a.nsplit > 1)
+    if (a.nsplit > 1 && MODE == 4)
+        hipLaunchKernelGGL(k_transport_grad_merge, dim3((unsigned)(((int64_t)a.nq * a.kout + kBlock - 1) / kBlock)),
+                           dim3(kBlock), 0, s, a);
+    else if (a.nsplit > 1)
         hipLaunchKernelGGL(k_transport_mfma_merge, dim3((unsigned)(((int64_t)a.nq * (a.kout + 1) + kBlock - 1) / kBlock)),
                            dim3(kBlock), 0, s, a, KA);
     return hipGetLastError();
@@ -932,6 +780,7 @@ hipError_t launch_transport_mfma_pp(const TransArgs& a, int mode, int kwidth, hi
     if (mode == 1) return launch_transport_mfma_p<P, 1, 1>(a, s, ev0, ev1);
     if (mode == 2) return launch_transport_mfma_p<P, 1, 2>(a, s, ev0, ev1);
     if (mode == 3) return launch_transport_mfma_p<P, 1, 3>(a, s, ev0, ev1);
+    if (mode == 4) return launch_transport_mfma_p<P, 1, 4>(a, s, ev0, ev1);
     if (kwidth == 16) return launch_transport_mfma_p<P, 1, 0>(a, s, ev0, ev1);
     if constexpr (P >= 64) {  // a 64-column payload tile fits LDS beside the key tile from P = 64 on
         if (kwidth == 64) return launch_transport_mfma_p<P, 4, 0>(a, s, ev0, ev1);
@@ -962,6 +811,7 @@ int capacity_tpp(int mode, int kwidth) {
     if (mode == 1) return capacity_tp<P, 1, 1>();
     if (mode == 2) return capacity_tp<P, 1, 2>();
     if (mode == 3) return capacity_tp<P, 1, 3>();
+    if (mode == 4) return capacity_tp<P, 1, 4>();
     if (kwidth == 16) return capacity_tp<P, 1, 0>();
     if constexpr (P >= 64) {
         if (kwidth == 64) return capacity_tp<P, 4, 0>();
@@ -1003,7 +853,7 @@ hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hi
     }
 }
 
-int mfma_grad_rows_per_block() { return kWaves * 16; }
+int mfma_grad_rows_per_block(int P) { return kWaves * 16 * transport_nqb(P, 1, 4); }
 
 int mfma_transport_rows_per_block(int P, int mode, int kwidth) {
     return kWaves * 16 * transport_nqb(P, kwidth > 16 ? 4 : 1, mode);
@@ -1022,7 +872,7 @@ int mfma_transport_capacity(int P, int mode, int kwidth) {
 
 int mfma_transport_max_rows_per_block(int P) {
     int r = 0;
-    for (int mode = 0; mode <= 3; ++mode)
+    for (int mode = 0; mode <= 4; ++mode)
         for (int kw : {16, 64}) r = std::max(r, mfma_transport_rows_per_block(P, mode, kw));
     return r;
 }
@@ -1035,17 +885,6 @@ hipError_t launch_transport_mfma(const TransArgs& a, int mode, int kwidth, hipSt
         case 64: return launch_transport_mfma_pp<64>(a, mode, kwidth, s, ev0, ev1);
         case 128: return launch_transport_mfma_pp<128>(a, mode, kwidth, s, ev0, ev1);
         case 256: return launch_transport_mfma_pp<256>(a, mode, kwidth, s, ev0, ev1);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s) {
-    switch (a.P) {
-        case 16: return launch_grad_mfma_p<16>(a, s);
-        case 32: return launch_grad_mfma_p<32>(a, s);
-        case 64: return launch_grad_mfma_p<64>(a, s);
-        case 128: return launch_grad_mfma_p<128>(a, s);
-        case 256: return launch_grad_mfma_p<256>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -60,6 +60,22 @@ def test_split_roofline_model():
     assert [bench.packed_stride(d) for d in (9, 16, 17, 32, 33, 64, 65, 256)] == [16, 16, 32, 32, 64, 64, 128, 256]
 
 
+def test_transport_split_roofline_model():
+    # fp16 split scores (6 d) and fp32 weighted sums (2 per padded payload column) share the matrix pipe: at
+    # d = 64 with 64 columns one pair needs 384 / 2500e12 + 128 / 157.3e12 s of it
+    pairs = 16384.0 ** 2
+    pipe = 384 / 2500e12 + 128 / 157.3e12
+    r = bench.roofline_transport_split(64, pairs, pairs * pipe, 64)
+    assert abs(r["frac"] - 1.0) < 1e-3 and r["ops_per_pair"] == 256 and r["bound"] == "mfma"
+    assert abs(r["peak"] - 256 / pipe / 1e12) < 1e-2
+    # a launch of 20 columns runs a 64-column tile; one of 9 a 16-column tile
+    r20 = bench.roofline_transport_split(33, pairs, 1.0, 20)
+    assert r20["ops_per_pair"] == 2 * 33 + 40 and "weighted sums (128)" in r20["mfma_dtype"]
+    r9 = bench.roofline_transport_split(12, pairs, 1.0, 9)
+    assert r9["ops_per_pair"] == 2 * 12 + 18 and "(96 flops per pair)" in r9["mfma_dtype"]
+    assert "weighted sums (32)" in r9["mfma_dtype"]
+
+
 def test_inputs_dimension_override():
     from sk_inputs import make_inputs
 
