@@ -44,6 +44,7 @@ constexpr int kBlock = 256;               // threads per workgroup (4 wave64s)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -3.402823466e38f;  // running-max start: -FLT_MAX, never -inf
+constexpr int kXcds = 8;                     // XCDs (each with its own L2) that workgroups are dealt to
 constexpr int kMaxD = 256;
 constexpr int kValuMaxD = 8;              // d <= 8: vector-ALU kernels; else matrix cores
 constexpr int kRedBlocks = 512;           // fixed partial count of the 2-stage reductions

@@ -79,6 +79,17 @@ __device__ __forceinline__ void finalize(const Fin& F, int i, float lse) { final
 
 __device__ __forceinline__ int64_t range_lo(int w, int64_t total, int W) { return (int64_t)w * total / W; }
 
+// The stream-K range that workgroup b of W takes. The hardware deals
+// workgroups to the chip's kXcds XCDs round-robin (b mod kXcds), and each XCD
+// has its own L2; numbering the ranges XCD by XCD gives every XCD a contiguous
+// run of ranges, so a row block's query rows are fetched into one or two L2s
+// instead of all of them. A bijection on [0, W); partial slots and the merge
+// use the range index, so results do not depend on it.
+__device__ __forceinline__ int xcd_range(int b, int W) {
+    const int q = W / kXcds, r = W % kXcds, x = b % kXcds;
+    return x * q + min(x, r) + b / kXcds;
+}
+
 // The workgroup whose range holds unit u: the largest w with range_lo(w) <= u.
 __device__ __forceinline__ int range_owner(int64_t u, int64_t total, int W) {
     return (int)(((u + 1) * W + total - 1) / total) - 1;

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
     const u4v* kb = reinterpret_cast<const u4v*>(A.kb);
     const SplitScale sc = split_scale(A.qmax, A.kmax, A.qscale);
 
-    const int w = blockIdx.x;
+    const int w = xcd_range(blockIdx.x, A.W);
     const int64_t lo = range_lo(w, A.total, A.W), hi = range_lo(w + 1, A.total, A.W);
     for (int64_t u = lo; u < hi;) {
         const int rb = (int)(u / A.nk);

@@ -302,7 +302,7 @@ void k_pass_valu(PassArgs A) {
     const float4* kp = reinterpret_cast<const float4*>(A.k);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
-    const int w = blockIdx.x;
+    const int w = xcd_range(blockIdx.x, A.W);
     const int64_t lo = range_lo(w, A.total, A.W), hi = range_lo(w + 1, A.total, A.W);
     for (int64_t u = lo; u < hi;) {
         const int rb = (int)(u / A.nk);
