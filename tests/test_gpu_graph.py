@@ -16,14 +16,18 @@ from sk_inputs import eps32, make_inputs, random_problem
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("case", ["gflow_d2", "ragged_d3"])
+@pytest.mark.parametrize("case", ["gflow_d2", "ragged_d3", "split_d40", "split_d64"])
 def test_graph_replay_matches_eager(case):
     if case == "gflow_d2":
         x, y, a, b = make_inputs("gflow_d2")
         eps, iters, ce = eps32(0.01), 40, 10
-    else:
+    elif case == "ragged_d3":
         x, y, a, b = random_problem(2600, 1900, 3, 77)
         eps, iters, ce = eps32(0.05), 12, 4
+    else:  # the matrix-core path: scale reduction, key split, split passes, gradient as transport mode 4
+        d = 40 if case == "split_d40" else 64
+        x, y, a, b = random_problem(1700, 2100, d, 78 + d, scale=1.0 / np.sqrt(d), shift=0.2)
+        eps, iters, ce = eps32(0.3), 10, 5
     dev = torch.device("cuda:0")
     X, Y, A, B = (torch.from_numpy(v).to(dev) for v in (x, y, a, b))
     n, m, d = x.shape[0], y.shape[0], x.shape[1]
