@@ -24,10 +24,11 @@
 // Work is split across workgroups with the same stream-K ranges as the vector
 // passes; a row block here is 4 waves x NQB x 16 queries.
 //
-// The solver pass and the one-column transport kernel take the cross term on
-// fp16 matrix cores from a scaled two-part split of every fp32 coordinate,
-// within a few fp32 unit roundoffs per term (split2, split_scores); the
-// gradient and the payload-carrying transport modes use fp32 instructions.
+// The solver pass and every transport mode (the d > 8 gradient among them)
+// take the cross term on fp16 matrix cores from a scaled two-part split of
+// every fp32 coordinate, within a few fp32 unit roundoffs per term (split2,
+// split_scores); the weighted key sums of the payload modes use fp32 matrix
+// instructions.
 #include "sk_internal.hpp"
 #include "sk_pass_common.hpp"
 
