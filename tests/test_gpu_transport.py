@@ -69,6 +69,8 @@ TRANSPORT_CASES = [
     (300, 500, 130, 0.5, 4, 5, False, 11, 0.0),
     (17, 5, 64, 0.2, 3, 3, True, 12, 0.0),
     (2600, 3100, 33, 0.3, 4, 16, False, 13, 0.0),
+    (900, 800, 100, 0.5, 4, 40, False, 18, 0.0),  # a 64-column tile at P = 128
+    (500, 600, 12, 0.3, 5, 20, True, 19, 0.05),   # two 16-column chunks at P = 16
     # one payload column on the vector ALUs inside the matrix-core kernel, split key range; its scores take
     # the fp16 split form (P = 32, 64, 128, 256 below)
     (1500, 2100, 64, 0.5, 5, 1, True, 14, 0.05),
