@@ -252,6 +252,7 @@ __global__ __launch_bounds__(kBlock) void k_sparse_merge(SparseArgs A) {
     if (p0 >= p1) return;  // no tiles (every block keeps one, so this does not occur)
     const int w0 = range_owner(p0, nnz, A.W), w1 = range_owner(p1 - 1, nnz, A.W);
     if (w0 == w1) return;  // finished in place
+    const FinIn pre = fin_load(A.fin, i);  // issued before the partials' loads
     float M = kNegBig, S = 0.0f;
     for (int w = w0; w <= w1; ++w) {
         const int64_t lo = range_lo(w, nnz, A.W);
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kBlock) void k_sparse_merge(SparseArgs A) {
         S = S * ex2(M - mn) + p.y * ex2(p.x - mn);
         M = mn;
     }
-    finalize(A.fin, i, M + lg2(S));
+    finalize(A.fin, i, M + lg2(S), pre);
 }
 
 // The dense pass.  A row block is the kPassRows = 64 R rows of one wave's
@@ -491,6 +492,8 @@ __global__ __launch_bounds__(kBlock) void k_merge(PassArgs A) {
     const int rb = ic / A.rpb, lr = ic - rb * A.rpb;
     const int64_t u0 = (int64_t)rb * A.nk, u1 = u0 + A.nk;
     const int wf = range_owner(u0, A.total, A.W), wl = range_owner(u1 - 1, A.total, A.W);
+    // the row's finalisation inputs, loaded now so that their latency overlaps the partials' loads
+    const FinIn pre = fin_load(A.fin, ic);
     float M = kNegBig, S = 0.0f;
     for (int w = wf + sub; w <= wl; w += kMergeLanes) {
         const int slot = range_lo(w, A.total, A.W) >= u0 ? 0 : 1;
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(PassArgs A) {
         M = mn;
     }
     // a row block held whole by one workgroup was finished by the pass itself
-    if (live && sub == 0 && wf != wl) finalize(A.fin, i, M + lg2(S));
+    if (live && sub == 0 && wf != wl) finalize(A.fin, i, M + lg2(S), pre);
 }
 
 // Gradient pass: the same traversal with the running weighted key sum
