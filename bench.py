@@ -50,6 +50,10 @@ evaluations of the counted iterations only):
               before timing: (3 + 2 cg_iters) n m pair evaluations;
   transport   one transport product P Y~-sized: sk_transport with a k = d
               payload (the barycentric numerator), n m pair evaluations.
+  grad        one sk_grad_x at the potentials of an n_iters solve done
+              before timing: n m pair evaluations, twice that for d > 8
+              (a store-lse pass, then the weighted key sums), whose roofline
+              the line reports.
   fs2         the two-stage block-sparse solver sk_fs2_solve to a marginal
               target of --fs2-tol-rel times the largest point mass; value
               counts the dense-equivalent 2 n m evaluations per fine
@@ -171,15 +175,18 @@ def roofline_split(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict
             "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
 
 
-def roofline_transport_split(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int) -> dict:
+def roofline_transport_split(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int,
+                             cols: int | None = None) -> dict:
     """Matrix-core roofline of one transport-product launch for d > 8 carrying `payload` columns (at most the
     library's chunk: 64 from a padded width of 64, else 16): the scores in the fp16 split form (6 d fp16 flops
     per pair, 8 d at a padded width of 16) and the weighted sums on fp32 matrix instructions (2 per column of
     the launch's 16- or 64-column tile). The ceiling is the time the matrix pipe needs for both at their own
     dense peaks; `achieved` and `peak` are stated in the method's flops per pair (2 d + 2 x payload), `peak`
-    being the rate that pipe time allows."""
+    being the rate that pipe time allows. `cols` overrides the tile width (the gradient's weighted key sums
+    run over all P padded coordinates)."""
     f16_ops = (8 if packed_stride(d) == 16 else 6) * d
-    cols = 16 if payload <= 16 else 64
+    if cols is None:
+        cols = 16 if payload <= 16 else 64
     pipe_s_per_pair = f16_ops / (MFMA_F16_PEAK_TFLOPS * 1e12) + 2 * cols / (MFMA_FP32_PEAK_TFLOPS * 1e12)
     ops = 2 * d + 2 * payload
     achieved = pairs_per_launch * ops / avg_launch_s / 1e12
@@ -344,7 +351,7 @@ def main():
     ap.add_argument("--timing-stride", type=int, default=7,
                     help="time every k-th pass launch with HIP events (odd, so row and column passes alternate)")
     ap.add_argument("--mode", default="solve",
-                    choices=["solve", "symmetric", "marginal", "potential", "divergence", "flow", "hvp", "transport",
+                    choices=["solve", "symmetric", "marginal", "potential", "divergence", "flow", "hvp", "transport", "grad",
                              "fs2"])
     ap.add_argument("--fs2-block", type=int, default=512)
     ap.add_argument("--fs2-tol-rel", type=float, default=0.01, help="target residual / largest point mass")
@@ -410,7 +417,7 @@ def main():
         fs2_tol = args.fs2_tol_rel * float(max(A.max().item(), B.max().item()))
         nb = sk.load_library().sk_fs2_workspace_bytes(n, m, d, args.fs2_block, 1024)
         ws_fs2 = torch.empty(nb, dtype=torch.uint8, device=dev)
-    if mode in ("hvp", "transport"):
+    if mode in ("hvp", "transport", "grad"):
         # potentials of a full solve, outside the timed region
         sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, ws=ws, f=f, g=g, check=False)
         ws_t = sk.transport_workspace(n, m, d, dev)
@@ -441,6 +448,8 @@ def main():
             sk.hvp(X, Y, A, B, f, g, v_dir, eps=eps, cg_iters=args.cg_iters, ws=ws_t, out=hv_out, cg_resid=cg_res)
         elif mode == "transport":
             sk.transport(X, Y, A, B, f, g, y_pay, eps=eps, ws=ws_t, out=hv_out)
+        elif mode == "grad":
+            sk.grad_x(X, Y, A, B, g, eps=eps, ws=ws, out=grad)
         elif mode == "fs2":
             _, _, inf = sk.fs2_solve(X, Y, A, B, eps=eps, block=args.fs2_block, tol=fs2_tol, delta=args.fs2_delta,
                                      max_iters=args.fs2_max_iters, ws=ws_fs2, f=f, g=g, check=False)
@@ -496,6 +505,8 @@ def main():
         pair_evals = (3.0 + 2.0 * args.cg_iters) * n * m
     if mode == "transport":
         pair_evals = 1.0 * n * m
+    if mode == "grad":
+        pair_evals = (2.0 if d > 8 else 1.0) * n * m  # d > 8: the store-lse pass, then the weighted sums
     if mode == "fs2":
         pair_evals = 2.0 * n * m * fs2_info["fine_iters"]
     extra = {}
@@ -580,6 +591,13 @@ def main():
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s) if launches else None
         if roof is not None:
             roof["kernel"] = f"k_pass_sparse<{d}>"
+    elif mode == "grad":
+        if d > 8:
+            # transport mode 4: split scores, then the key coordinates as a P-column fp32 payload
+            roof = roofline_transport_split(d, pairs_per_launch, avg_launch_s, d, cols=packed_stride(d))
+            roof["kernel"] = "k_transport_mfma<%d,1,4>" % packed_stride(d)
+        else:
+            roof = None  # the vector-ALU gradient is timed as a part of the default solve step (components_ms)
     elif mode in ("hvp", "transport"):
         payload = 1 if mode == "hvp" else d  # columns of the dominant launches (CG steps / the product)
         if d > 8 and payload > 1:

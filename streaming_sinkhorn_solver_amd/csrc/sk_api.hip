@@ -753,7 +753,10 @@ int grad_core(const Ws& W, const float* x, const float* y, const float* a, const
     // (transport mode 4), with no more key splits than the workspace holds
     PassArgs lse_pass = make_pass(W, true, eps, a, cap);
     lse_pass.fin.mode = kFinStore;
-    if ((st = run_pass(W, lse_pass, s))) return st;
+    {
+        TimingPause pause;  // the pass timing covers the gradient kernel
+        if ((st = run_pass(W, lse_pass, s))) return st;
+    }
     const int rpb = mfma_grad_rows_per_block(L.P);
     const int gcap = transport_capacity_cached(L, 4, 16);
     if (gcap <= 0) return SK_ERR_HIP;
@@ -784,7 +787,9 @@ int grad_core(const Ws& W, const float* x, const float* y, const float* a, const
     t.ldo = d;
     t.kout = d;
     t.gw = a;
-    SK_TRY(launch_transport_mfma(t, 4, 16, s));
+    hipEvent_t e0, e1;
+    if ((st = timing_events(n, m, s, &e0, &e1))) return st;
+    SK_TRY(launch_transport_mfma(t, 4, 16, s, e0, e1));
     return SK_OK;
 }
 

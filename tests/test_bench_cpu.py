@@ -71,6 +71,9 @@ def test_transport_split_roofline_model():
     # a launch of 20 columns runs a 64-column tile; one of 9 a 16-column tile
     r20 = bench.roofline_transport_split(33, pairs, 1.0, 20)
     assert r20["ops_per_pair"] == 2 * 33 + 40 and "weighted sums (128)" in r20["mfma_dtype"]
+    # the gradient (transport mode 4): the weighted key sums run over all P = 128 padded coordinates
+    rg = bench.roofline_transport_split(100, pairs, 1.0, 100, cols=128)
+    assert rg["ops_per_pair"] == 400 and "weighted sums (256)" in rg["mfma_dtype"]
     r9 = bench.roofline_transport_split(12, pairs, 1.0, 9)
     assert r9["ops_per_pair"] == 2 * 12 + 18 and "(96 flops per pair)" in r9["mfma_dtype"]
     assert "weighted sums (32)" in r9["mfma_dtype"]
