@@ -217,15 +217,15 @@ def kernel_source_hash(family: str) -> str:
     return h.hexdigest()
 
 
-def load_traffic(kernel_key: str, family: str):
+def load_traffic(kernel_key: str, family: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they
-    were taken on the current source of that kernel (else None)."""
+    were taken of this kernel, on its current source (else None)."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     entry = rec.get(kernel_key)
-    if not entry or entry.get("source_sha256") != kernel_source_hash(family):
+    if not entry or entry.get("kernel") != kernel or entry.get("source_sha256") != kernel_source_hash(family):
         return None
     return entry.get("bytes_per_launch")
 
@@ -624,7 +624,7 @@ def main():
         roof["kernel"] = "k_pass_mfma<%d>" % packed_stride(d)
     if roof is not None and mode != "fs2" and args.size is None and args.dim is None:
         # the counter runs were taken on the workload at its own shape
-        roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma")
+        roof["traffic"] = load_traffic(f"{args.workload}:pass", "valu" if d <= 8 else "mfma", roof["kernel"])
     elif roof is not None and mode != "fs2":
         roof["traffic"] = None
     elif roof is not None:
@@ -740,11 +740,11 @@ def run_extra_config(name: str, steps: int, graph: bool, iters, timing_stride: i
     if d <= 8:
         roof = roofline_alu(d, ppl, avg_s)
         roof["kernel"] = f"k_pass_small<{d}>" if ppl <= 2.0e6 else f"k_pass_valu<{d}>"
-        roof["traffic"] = load_traffic(f"{name}:pass", "valu")
+        roof["traffic"] = load_traffic(f"{name}:pass", "valu", roof["kernel"])
     else:
         roof = roofline_split(d, ppl, avg_s)
         roof["kernel"] = "k_pass_mfma<%d>" % packed_stride(d)
-        roof["traffic"] = load_traffic(f"{name}:pass", "mfma")
+        roof["traffic"] = load_traffic(f"{name}:pass", "mfma", roof["kernel"])
     out = {"workload": name, "n": n, "m": m, "d": d, "eps": eps, "n_iters": n_iters, "check_every": ce,
            "grad_x": bool(with_grad), "steps": steps, "hip_graph": graph, "ms_per_step": step_s * 1e3,
            "value": 2.0 * n * m * n_iters / step_s, "unit": "pair-evals/s", "iters_per_s": n_iters / step_s,

@@ -42,9 +42,12 @@ def test_mfma_roofline_model():
 
 def test_traffic_record_matches_current_kernels_or_is_absent():
     # a stale record must read as None, never as a number for changed kernels
-    for key, fam in (("gmm8_d3_sq:pass", "valu"), ("gauss_d64:pass", "mfma")):
-        t = bench.load_traffic(key, fam)
+    for key, fam, kernel in (("gmm8_d3_sq:pass", "valu", "k_pass_valu<3>"),
+                             ("gauss_d64:pass", "mfma", "k_pass_mfma<64>")):
+        t = bench.load_traffic(key, fam, kernel)
         assert t is None or t > 0
+        # the record of a pass is never reported for another kernel of the same workload (a transport launch)
+        assert bench.load_traffic(key, fam, "k_transport_mfma<64,1,4>") is None
 
 
 def test_split_roofline_model():
