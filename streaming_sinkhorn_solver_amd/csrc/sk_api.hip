@@ -173,6 +173,11 @@ int check_ws(void* ws, size_t ws_bytes, const Layout& L) {
         if ((expr) != hipSuccess) return SK_ERR_HIP; \
     } while (0)
 
+// The scale of both clouds' fp16 split parts: fl(sqrt(2 log2e / eps)), from
+// the same float 2 log2e / eps every pass takes, so that the split kernel and
+// the passes agree on every bit.
+float split_root(float eps) { return (float)std::sqrt((double)(2.0f * kLog2e / eps)); }
+
 // Shifts both clouds by their common centre and packs them.  x_bias / y_bias:
 // 0 = none, 1 = zero potential, 2 = from the given potential.
 // u_x / u_y (may be null) receive the states that the initial biases encode.
@@ -188,8 +193,9 @@ int prepare(const Ws& W, const float* x, const float* y, const float* a, const f
                        1.0f / eps, y_bias, g, u_y, s));
     if (L.split) {  // scales and keys of the fp16 matrix-core pass
         SK_TRY(launch_absmax(W.f(L.xp), L.n * L.P, W.f(L.yp), L.m * L.P, W.f(L.amax_part), W.f(L.amax), s));
-        SK_TRY(launch_split2(W.f(L.xp), L.n, L.P, W.f(L.amax), W.h(L.xb), s));
-        SK_TRY(launch_split2(W.f(L.yp), L.m, L.P, W.f(L.amax) + 1, W.h(L.yb), s));
+        const float rq = split_root(eps);
+        SK_TRY(launch_split2(W.f(L.xp), L.n, L.P, W.f(L.amax), rq, W.h(L.xb), s));
+        SK_TRY(launch_split2(W.f(L.yp), L.m, L.P, W.f(L.amax) + 1, rq, W.h(L.yb), s));
     }
     return SK_OK;
 }
@@ -207,6 +213,8 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
     p.k = W.f(row_side ? L.yp : L.xp);
     p.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
     p.kb = L.split ? W.h(row_side ? L.yb : L.xb) : nullptr;
+    p.qb = L.split ? W.h(row_side ? L.xb : L.yb) : nullptr;
+    p.rq = split_root(eps);
     p.qmax = L.split ? W.f(L.amax) + (row_side ? 0 : 1) : nullptr;
     p.kmax = L.split ? W.f(L.amax) + (row_side ? 1 : 0) : nullptr;
     p.nq = (int)nq;
@@ -241,7 +249,7 @@ PassArgs make_pass(const Ws& W, bool row_side, float eps, const float* w_q, int 
 void retarget(PassArgs& p, const float* q, int64_t nq, const float* k, int64_t nk, int capacity) {
     p.q = q;
     p.k = k;
-    p.kb = nullptr;  // no split copy of other keys
+    p.kb = p.qb = nullptr;  // no split copy of other keys
     p.qmax = p.kmax = nullptr;
     p.nq = (int)nq;
     p.nk = (int)nk;
@@ -771,6 +779,8 @@ int grad_core(const Ws& W, const float* x, const float* y, const float* a, const
     t.k = W.f(L.yp);
     t.kbias = W.f(L.hy);
     t.kb = W.h(L.yb);
+    t.qb = W.h(L.xb);
+    t.rq = split_root(eps);
     t.qmax = W.f(L.amax);
     t.kmax = W.f(L.amax) + 1;
     t.lse = W.f(L.lse_r);
@@ -883,6 +893,8 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     t.k = W.f(row_side ? L.yp : L.xp);
     t.kbias = L.mfma ? W.f(row_side ? L.hy : L.hx) : nullptr;
     t.kb = L.split ? W.h(row_side ? L.yb : L.xb) : nullptr;
+    t.qb = L.split ? W.h(row_side ? L.xb : L.yb) : nullptr;
+    t.rq = split_root(eps);
     t.qmax = L.split ? W.f(L.amax) + (row_side ? 0 : 1) : nullptr;
     t.kmax = L.split ? W.f(L.amax) + (row_side ? 1 : 0) : nullptr;
     t.qbias = L.mfma ? W.f(row_side ? L.hx : L.hy) : nullptr;

@@ -120,10 +120,12 @@ struct PassArgs {
     const float* k;      // key cloud, packed [nk][P]
     const float* kbias;  // separate key bias [nk] (matrix-core layout), else null
     const uint16_t* kb;  // matrix-core layout: fp16 parts of the scaled keys [nk][2][P] (h, l), else null
+    const uint16_t* qb;  // matrix-core layout: the same parts of the queries [nq][2][P], else null
     const float* qmax;   // matrix-core layout: largest |packed coordinate| of the query cloud (device)
     const float* kmax;   // matrix-core layout: the same of the key cloud (device)
     int nq, nk, P;
     float qscale;        // 2 log2e / eps
+    float rq;            // matrix-core layout: fl(sqrt(qscale)), the scale of both clouds' split parts
     int rpb;             // rows per block
     int W;               // workgroups
     int64_t total;       // n_row_blocks * nk
@@ -187,9 +189,11 @@ struct TransArgs {
     const float* q;      // query cloud, packed [nq][P], bias slot = log2 w + log2e (pot - |q~|^2)/eps
     const float* k;      // key cloud, packed [nk][P], same bias from the key-side potential
     const float* kbias;  // matrix-core layout: key biases [nk], else null
-    const uint16_t* kb;  // matrix-core layout: fp16 parts of the scaled keys [nk][2][P] (one-column mode)
+    const uint16_t* kb;  // matrix-core layout: fp16 parts of the scaled keys [nk][2][P]
+    const uint16_t* qb;  // matrix-core layout: the same parts of the queries [nq][2][P]
     const float* qmax;   // matrix-core layout: largest |packed coordinate| of the query cloud (device)
     const float* kmax;   // matrix-core layout: the same of the key cloud (device)
+    float rq;            // matrix-core layout: fl(sqrt(2 log2e / eps)), the scale of the split parts
     const float* qbias;  // matrix-core layout: query biases [nq], else null
     const float* lse;    // matrix-core layout: row log-sum-exp of the scores [nq] (a first pass)
     const float* pay;    // payload: key j's columns at pay[j * ldp + c], c < kin
@@ -339,9 +343,11 @@ hipError_t launch_merge(const PassArgs& a, hipStream_t s);
 hipError_t launch_pass_mfma(const PassArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 int mfma_rows_per_block(int P);
 int mfma_pass_capacity(int P);
-// fp16 parts (h, l) of rows x P packed floats times 2^ek into out [rows][2][P],
-// ek from the cloud's largest |coordinate| *kmax (device).
-hipError_t launch_split2(const float* in, int64_t rows, int P, const float* kmax, uint16_t* out, hipStream_t s);
+// fp16 parts (h, l) of rows x P packed floats times rq and a power of two into
+// out [rows][2][P], the exponent from the cloud's largest |coordinate| *cmax
+// (device) times rq.
+hipError_t launch_split2(const float* in, int64_t rows, int P, const float* cmax, float rq, uint16_t* out,
+                         hipStream_t s);
 // out[0] = max |x[e]| over nx floats, out[1] = the same over y (nx, ny multiples
 // of 4); part holds 2 * kAbsMaxBlocks floats.
 constexpr int kAbsMaxBlocks = 256;

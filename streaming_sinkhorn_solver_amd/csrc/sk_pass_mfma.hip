@@ -14,8 +14,8 @@
 //    v_mfma_f32_16x16x32_f16 (lane: key / query c, k slots 8g..8g+7);
 //  * the contraction index is permuted so that lane group g owns the
 //    contiguous coordinate range [g P/4, (g+1) P/4). Each lane keeps its
-//    query's coordinates in registers for the whole pass (row-stationary) and
-//    reads its key's from a padded LDS tile;
+//    query's split coordinates in registers for a whole segment
+//    (row-stationary) and reads its key's from a padded LDS tile;
 //  * the accumulator starts at the key biases, so the bias add is free;
 //  * each lane runs an online (M, S) over the keys it sees; the four lane
 //    groups that share a query are merged with two cross-lane exchanges at
@@ -95,13 +95,18 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
 // ---- two-part fp16 split of scaled fp32 values
 //
-// Each side is first scaled by a power of two 2^e chosen from the largest
-// magnitude of its cloud (split_exp), so that its operands lie below 2^14,
-// within fp16's range and near its top. Then v = h + l with h = fp16(v) and
-// l = fp16(v - h), both rounded to nearest even: the remainder v - h is exact
+// Both clouds are scaled by rq = fl(sqrt(2 log2e / eps)), so that the score's
+// cross term <q, k> = (2 log2e / eps) <x~, y~> is the product of the two
+// scaled clouds, and each cloud once more by a power of two 2^e chosen from
+// its largest scaled magnitude (split_exp), so that its operands lie below
+// 2^14, within fp16's range and near its top. One split per cloud and solve
+// then serves it as queries in one half-step and as keys in the other.
+// Then v = h + l with h = fp16(v) and l = fp16(v - h), both rounded to
+// nearest even: the remainder v - h is exact
 // in fp32 and |v - h - l| <= 2^-22 |v| + 2^-25, the second term from fp16's
 // subnormal spacing (it matters only for |v| below about 2^-3 at the scaled
-// size, against largest operands of 2^13 to 2^14). The score takes hq hk + hq lk + lq hk: each product of two fp16 values is
+// size, against largest operands of 2^13 to 2^14). The score takes
+// hq hk + hq lk + lq hk: each product of two fp16 values is
 // exact in fp32, the matrix cores add in fp32, and the dropped product lq lk
 // is below 2^-22 |q_t k_t|. This is the fp16 splitting of Ootomo and Yokota
 // ("Recovering single precision accuracy from Tensor Cores while surpassing
@@ -115,6 +120,9 @@ typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 // The matrix cores then return 2^(eq + ek) times the score (the key biases
 // are scaled the same way when a tile is staged); the log-sum-exp takes the
 // scale off inside its exponent with one fma, fma(D, r, -M r), r = 2^-(eq+ek).
+// Each scaled coordinate carries one rounding, and rq^2 is 2 log2e / eps to
+// within an fp32 roundoff, the same order as the rounding of an unsplit
+// fl(x~ 2 log2e / eps).
 
 // The exponent e that puts the largest magnitude mx at mx 2^e in [2^13, 2^14)
 // (0 for a zero or non-finite mx).
@@ -125,26 +133,27 @@ __device__ __forceinline__ int split_exp(float mx) {
     return 14 - e;
 }
 
-// Key-side exponent of a cloud whose largest |coordinate| is kmax; capped so
-// that the score scale 2^(eq + ek) stays at most 2^64.
-__device__ __forceinline__ int key_exp(float kmax) { return min(split_exp(kmax), 64); }
+// The power-of-two exponent of a cloud whose largest |coordinate| is cmax,
+// scaled by rq. Capped at 48, so that the score scale 2^(eq + ek) stays at
+// most 2^96 and staged biases up to 2^32 in magnitude stay finite. The cap
+// binds only for a cloud whose scaled coordinates all lie below 2^-34; its
+// parts then carry an absolute error of at most 2^-73 beside the relative
+// 2^-22, for each coordinate of it.
+__device__ __forceinline__ int cloud_exp(float cmax, float rq) { return min(split_exp(cmax * rq), 48); }
 
-// The scales of one pass: queries are fl(v qscale) 2^eq (the same fp32 query
-// value as an unsplit pass, shifted by a power of two), keys v 2^ek.
+// The scales of one pass: query parts are those of fl(v rq) 2^eq, key parts
+// those of fl(v rq) 2^ek (each cloud's own exponent).
 struct SplitScale {
-    float qshift;  // 2^eq
-    float t;       // 2^(eq + ek): score scale of the matrix-core results and staged biases
-    float r;       // 2^-(eq + ek)
-    float m0;      // running-max start, kNegBig min(t, 1), so that -m0 r stays finite
+    float t;   // 2^(eq + ek): score scale of the matrix-core results and staged biases
+    float r;   // 2^-(eq + ek)
+    float m0;  // running-max start, kNegBig min(t, 1), so that -m0 r stays finite
 };
 
-__device__ __forceinline__ SplitScale split_scale(const float* qmax, const float* kmax, float qscale) {
-    const int ek = key_exp(*kmax);
-    const int eq = min(split_exp(*qmax * qscale), 64 - ek);
+__device__ __forceinline__ SplitScale split_scale(const float* qmax, const float* kmax, float rq) {
+    const int e = cloud_exp(*qmax, rq) + cloud_exp(*kmax, rq);
     SplitScale z;
-    z.qshift = ldexpf(1.0f, eq);
-    z.t = ldexpf(1.0f, eq + ek);
-    z.r = ldexpf(1.0f, -(eq + ek));
+    z.t = ldexpf(1.0f, e);
+    z.r = ldexpf(1.0f, -e);
     z.m0 = z.t < 1.0f ? kNegBig * z.t : kNegBig;
     return z;
 }
@@ -160,17 +169,18 @@ __device__ __forceinline__ void split2(float v, unsigned& h, unsigned& l) {
     l = f16_bits(v - f16_value(h));
 }
 
-// The parts of packed key rows: out[i][part][t] (parts h, l) of in[i][t] 2^ek,
-// ek from the cloud's largest |coordinate| *kmax.
+// The parts of packed rows: out[i][part][t] (parts h, l) of fl(in[i][t] rq) 2^e,
+// e = cloud_exp of the cloud's largest |coordinate| *cmax.
 __global__ __launch_bounds__(kBlock) void k_split2(const float* __restrict__ in, int64_t count, int P,
-                                                   const float* __restrict__ kmax, uint16_t* __restrict__ out) {
+                                                   const float* __restrict__ cmax, float rq,
+                                                   uint16_t* __restrict__ out) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= count) return;
-    const float sc = ldexpf(1.0f, key_exp(*kmax));
+    const float sc = ldexpf(1.0f, cloud_exp(*cmax, rq));
     const int64_t i = e / P;
     const int t = (int)(e - i * P);
     unsigned h, l;
-    split2(in[e] * sc, h, l);
+    split2((in[e] * rq) * sc, h, l);
     uint16_t* o = out + i * 2 * P + t;
     o[0] = (uint16_t)h;
     o[P] = (uint16_t)l;
@@ -282,37 +292,27 @@ constexpr int split_qops() {
     return P >= 32 ? P / 32 : 1;
 }
 
-// A lane's query row for the split form, from its P/4 coordinates at qr:
-// fl(v qscale) 2^eq, split. P >= 32: chunk kc of qh, ql holds the h, l parts
-// of coordinates 8 kc .. 8 kc + 7. P = 16: qh = (h, h), ql = (l, l) over the
-// lane group's 4 coordinates, the B operands of split_scores<16>.
+// A lane's query operands for the split form, from the query's row of split
+// parts (parts h, l, P/8 16-byte units apart; the same layout and lane-group
+// map as a key row). P >= 32: chunk kc of qh, ql holds the h, l parts of
+// coordinates 8 kc .. 8 kc + 7 of the lane group. P = 16: qh = (h, h),
+// ql = (l, l) over the lane group's 4 coordinates, the B operands of
+// split_scores<16>.
 template <int P>
-__device__ __forceinline__ void load_query_split(const float* __restrict__ qr, float qscale, float qshift,
-                                                 u4v (&qh)[split_qops<P>()], u4v (&ql)[split_qops<P>()]) {
-    const float4* q4 = reinterpret_cast<const float4*>(qr);
+__device__ __forceinline__ void load_query_parts(const u4v* __restrict__ row, int g, u4v (&qh)[split_qops<P>()],
+                                                 u4v (&ql)[split_qops<P>()]) {
+    if constexpr (P == 16) {
+        const uint2* r2 = reinterpret_cast<const uint2*>(row);
+        const uint2 h = r2[g], l = r2[4 + g];
+        qh[0] = u4v{h.x, h.y, h.x, h.y};
+        ql[0] = u4v{l.x, l.y, l.x, l.y};
+    } else {
+        constexpr int KC = P / 32;
+        const u4v* kr = row + g * KC;
 #pragma unroll
-    for (int t4 = 0; t4 < (P == 16 ? 1 : P / 16); ++t4) {
-        const float4 v = q4[t4];
-        const float x[4] = {(v.x * qscale) * qshift, (v.y * qscale) * qshift, (v.z * qscale) * qshift,
-                            (v.w * qscale) * qshift};
-        unsigned hw[2], lw[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            unsigned h0, l0, h1, l1;
-            split2(x[2 * e], h0, l0);
-            split2(x[2 * e + 1], h1, l1);
-            hw[e] = h0 | (h1 << 16);
-            lw[e] = l0 | (l1 << 16);
-        }
-        if constexpr (P == 16) {
-            qh[0] = u4v{hw[0], hw[1], hw[0], hw[1]};
-            ql[0] = u4v{lw[0], lw[1], lw[0], lw[1]};
-        } else {
-            const int kc = t4 / 2, wd = 2 * (t4 % 2);
-            qh[kc][wd] = hw[0];
-            qh[kc][wd + 1] = hw[1];
-            ql[kc][wd] = lw[0];
-            ql[kc][wd + 1] = lw[1];
+        for (int kc = 0; kc < KC; ++kc) {
+            qh[kc] = kr[kc];
+            ql[kc] = kr[P / 8 + kc];
         }
     }
 }
@@ -419,11 +419,21 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2
 }
 
 // The solver pass: the cross term on fp16 matrix cores from the two-part
-// split (keys split in memory by k_split2, queries split in registers when a
-// segment starts). Lane group g owns the coordinates [g P/4, (g+1) P/4).
+// split (both clouds split in memory by k_split2; a lane loads its query's
+// parts once per segment and keeps them in registers). Lane group g owns the
+// coordinates [g P/4, (g+1) P/4).
+// Waves per SIMD the solver pass is compiled for: four at P = 16 (128 VGPRs)
+// and P = 256, three otherwise (165 VGPRs at P = 64, where the compiler left
+// alone takes 175 and two). No spills at any P; at 16384^2 d = 16 and 32 ran
+// 2% faster than without the bound, d = 64 the same.
 template <int P>
-__global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
-    constexpr int KT = P / 4;            // coordinates per lane group
+constexpr int pass_waves() {
+    return (P == 16 || P == 256) ? 4 : 3;
+}
+
+template <int P>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(pass_waves<P>()))) void k_pass_mfma(
+    PassArgs A) {
     constexpr int KQ = split_qops<P>();  // query operands per part
     constexpr int NQB = mfma_nqb<P>();   // 16-query blocks per wave
     using Stage = TileStage2<P>;
@@ -435,7 +445,8 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c = lane & 15;
     const u4v* kb = reinterpret_cast<const u4v*>(A.kb);
-    const SplitScale sc = split_scale(A.qmax, A.kmax, A.qscale);
+    const u4v* qbp = reinterpret_cast<const u4v*>(A.qb);
+    const SplitScale sc = split_scale(A.qmax, A.kmax, A.rq);
 
     const int w = xcd_range(blockIdx.x, A.W);
     const int64_t lo = range_lo(w, A.total, A.W), hi = range_lo(w + 1, A.total, A.W);
@@ -452,7 +463,7 @@ __global__ __launch_bounds__(kBlock) void k_pass_mfma(PassArgs A) {
         for (int qb = 0; qb < NQB; ++qb) {
             const int i = qrow0 + qb * 16 + c;
             const int ic = i < A.nq ? i : A.nq - 1;
-            load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, sc.qshift, qh[qb], ql[qb]);
+            load_query_parts<P>(qbp + (size_t)ic * (P / 4), g, qh[qb], ql[qb]);
             M[qb] = sc.m0;
             S[qb] = 0.0f;
         }
@@ -567,7 +578,8 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     const int c1 = min(c0 + A.cols_per_split, A.nk);
     const int qrow0 = blockIdx.x * (kWaves * 16 * NQB) + wave * (16 * NQB);
     // scores come back times sc.t (key biases staged the same way)
-    const SplitScale sc = split_scale(A.qmax, A.kmax, A.qscale);
+    const SplitScale sc = split_scale(A.qmax, A.kmax, A.rq);
+    const u4v* qbp = reinterpret_cast<const u4v*>(A.qb);
 
     float vf[MODE == 2 ? NQB : 1][KT];
     u4v qh[NQB][KQ], ql[NQB][KQ];
@@ -577,7 +589,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     for (int qb = 0; qb < NQB; ++qb) {
         const int i = qrow0 + qb * 16 + c;
         const int ic = i < A.nq ? i : A.nq - 1;
-        load_query_split<P>(A.q + (size_t)ic * P + g * KT, A.qscale, sc.qshift, qh[qb], ql[qb]);
+        load_query_parts<P>(qbp + (size_t)ic * (P / 4), g, qh[qb], ql[qb]);
         if (MODE == 2) {
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
@@ -762,7 +774,7 @@ hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t
     constexpr int KA = (MODE == 1 || MODE == 2 || MODE == 4) ? P : 16 * NP;
     constexpr int rpb = kWaves * 16 * transport_nqb(P, NP, MODE);
     // the split keys and the clouds' largest magnitudes are written by every set-up
-    if (!a.kb || !a.qmax || !a.kmax) return hipErrorInvalidValue;
+    if (!a.kb || !a.qb || !a.qmax || !a.kmax) return hipErrorInvalidValue;
     if (MODE == 4 && (!a.gw || a.kout > P)) return hipErrorInvalidValue;
     dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
     SK_LAUNCH_TIMED((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), s, ev0, ev1, a);
@@ -792,7 +804,7 @@ hipError_t launch_transport_mfma_pp(const TransArgs& a, int mode, int kwidth, hi
 template <int P>
 hipError_t launch_mfma_p(const PassArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     // the split keys and the clouds' largest magnitudes are written by every solver set-up
-    if (!a.kb || !a.qmax || !a.kmax) return hipErrorInvalidValue;
+    if (!a.kb || !a.qb || !a.qmax || !a.kmax) return hipErrorInvalidValue;
     SK_LAUNCH_TIMED(k_pass_mfma<P>, dim3(a.W), dim3(kBlock), s, ev0, ev1, a);
     return launch_merge(a, s);
 }
@@ -890,10 +902,11 @@ hipError_t launch_transport_mfma(const TransArgs& a, int mode, int kwidth, hipSt
     }
 }
 
-hipError_t launch_split2(const float* in, int64_t rows, int P, const float* kmax, uint16_t* out, hipStream_t s) {
+hipError_t launch_split2(const float* in, int64_t rows, int P, const float* cmax, float rq, uint16_t* out,
+                         hipStream_t s) {
     const int64_t count = rows * P;
     hipLaunchKernelGGL(k_split2, dim3((unsigned)((count + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, in, count, P,
-                       kmax, out);
+                       cmax, rq, out);
     return hipGetLastError();
 }
 

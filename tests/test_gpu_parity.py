@@ -107,8 +107,9 @@ def test_solve_matches_oracle(shape):
 # products hh + hl + lh, fp32 accumulation; at P = 16 all four in two instructions): its error per term is a
 # few float32 unit roundoffs. One iteration from g = 0 must then stay within a few float32 roundings of the
 # exponent of the oracle's iterate: 4 kappa eps, kappa as above. (Emulated on the CPU for these inputs, the
-# float32 rounding of q.y alone moves f by 0.04-0.14 kappa eps and the split by 0.08-0.40 kappa eps, products
-# summed exactly; keeping only the three largest products of a three-part bf16 split would move it by 2-21.)
+# float32 rounding of q.y alone moves f by 0.04-0.14 kappa eps and the split, both clouds scaled by
+# fl(sqrt(2 log2e / eps)), by 0.13-0.42 kappa eps, products summed exactly; keeping only the three largest
+# products of a three-part bf16 split would move it by 2-21.)
 SPLIT_SHAPES = [(1500, 1300, 16, 0.05, 81), (1500, 1300, 32, 0.05, 82), (1200, 1100, 64, 0.05, 83),
                 (700, 900, 100, 0.05, 84), (600, 700, 128, 0.05, 85), (300, 500, 256, 0.05, 86),
                 # ragged and tiny: partial 16-query blocks, a partial two-block step, one row or one key
@@ -159,10 +160,11 @@ def test_gradient_flow_workload_end_to_end():
     assert np.max(np.abs(grad - gr_or)) <= tol_e2e
 
 
-# The split scales each side by a power of two from its cloud's largest |coordinate| (and the query side by
-# 2 log2e / eps as well), so the fp16 operands sit near the top of fp16's range at any data magnitude. These
-# cases move that magnitude far from 1 on one side or both, mix dimensions 1e4 apart, and collapse both
-# clouds onto one point (largest |coordinate| 0); one iteration is held to the same 4 kappa eps.
+# The split scales both clouds by fl(sqrt(2 log2e / eps)) and each by a power of two from its largest scaled
+# |coordinate|, so the fp16 operands sit near the top of fp16's range at any data magnitude. These cases move
+# that magnitude far from 1 on one side or both, mix dimensions 1e4 apart, put both clouds below the point
+# where the power of two is capped (2^48), and collapse both clouds onto one point (largest |coordinate| 0);
+# one iteration is held to the same 4 kappa eps.
 def _scaled_problem(case):
     n, m, d = 700, 900, 64
     if case == "degenerate":
@@ -175,6 +177,9 @@ def _scaled_problem(case):
         return x * np.float32(1e4), y * np.float32(1e4), a, b, 5e6
     if case == "unbalanced":
         return x * np.float32(1e-3), y * np.float32(1e3), a, b, 5e4
+    if case == "vanishing":
+        # scaled coordinates below 2^-38: the exponent of both clouds is capped, the score scale is 2^96
+        return x * np.float32(1e-12), y * np.float32(1e-12), a, b, 1.0
     if case == "mixed_dims":
         x[:, : d // 2] *= np.float32(1e-4)
         y[:, : d // 2] *= np.float32(1e-4)
@@ -184,7 +189,8 @@ def _scaled_problem(case):
     raise ValueError(case)
 
 
-@pytest.mark.parametrize("case", ["tiny", "huge", "unbalanced", "mixed_dims", "small_eps", "degenerate"])
+@pytest.mark.parametrize("case", ["tiny", "huge", "unbalanced", "vanishing", "mixed_dims", "small_eps",
+                                  "degenerate"])
 def test_split_scales_at_extreme_magnitudes(case):
     x, y, a, b, eps = _scaled_problem(case)
     eps = eps32(eps)
