@@ -176,24 +176,30 @@ def roofline_split(d: int, pairs_per_launch: float, avg_launch_s: float) -> dict
 
 
 def roofline_transport_split(d: int, pairs_per_launch: float, avg_launch_s: float, payload: int,
-                             cols: int | None = None) -> dict:
+                             cols: int | None = None, split_sums: bool = False) -> dict:
     """Matrix-core roofline of one transport-product launch for d > 8 carrying `payload` columns (at most the
     library's chunk: 64 from a padded width of 64, else 16): the scores in the fp16 split form (6 d fp16 flops
     per pair, 8 d at a padded width of 16) and the weighted sums on fp32 matrix instructions (2 per column of
     the launch's 16- or 64-column tile). The ceiling is the time the matrix pipe needs for both at their own
     dense peaks; `achieved` and `peak` are stated in the method's flops per pair (2 d + 2 x payload), `peak`
     being the rate that pipe time allows. `cols` overrides the tile width (the gradient's weighted key sums
-    run over all P padded coordinates)."""
+    run over all P padded coordinates). `split_sums`: the weighted sums run on fp16 matrix instructions as three
+    products of two-part splits (6 fp16 flops per pair and column; the gradient up to a padded width of 64)."""
     f16_ops = (8 if packed_stride(d) == 16 else 6) * d
     if cols is None:
         cols = 16 if payload <= 16 else 64
-    pipe_s_per_pair = f16_ops / (MFMA_F16_PEAK_TFLOPS * 1e12) + 2 * cols / (MFMA_FP32_PEAK_TFLOPS * 1e12)
+    if split_sums:
+        pipe_s_per_pair = (f16_ops + 6 * cols) / (MFMA_F16_PEAK_TFLOPS * 1e12)
+        sums = "fp16 split weighted sums (%d)" % (6 * cols)
+    else:
+        pipe_s_per_pair = f16_ops / (MFMA_F16_PEAK_TFLOPS * 1e12) + 2 * cols / (MFMA_FP32_PEAK_TFLOPS * 1e12)
+        sums = "fp32 weighted sums (%d)" % (2 * cols)
     ops = 2 * d + 2 * payload
     achieved = pairs_per_launch * ops / avg_launch_s / 1e12
     peak = ops / pipe_s_per_pair / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": None, "ops_per_pair": ops,
-            "mfma_dtype": "fp16 split scores (%d flops per pair), fp32 weighted sums (%d)" % (f16_ops, 2 * cols),
+            "mfma_dtype": "fp16 split scores (%d flops per pair), %s" % (f16_ops, sums),
             "fp32_equivalent": {"achieved": round(achieved, 3), "ops_per_pair": ops,
                                 "vs_fp32_mfma_peak": round(achieved / MFMA_FP32_PEAK_TFLOPS, 4)},
             "pairs_per_launch": pairs_per_launch, "avg_launch_us": round(avg_launch_s * 1e6, 3)}
@@ -593,8 +599,10 @@ def main():
             roof["kernel"] = f"k_pass_sparse<{d}>"
     elif mode == "grad":
         if d > 8:
-            # transport mode 4: split scores, then the key coordinates as a P-column fp32 payload
-            roof = roofline_transport_split(d, pairs_per_launch, avg_launch_s, d, cols=packed_stride(d))
+            # transport mode 4: split scores, then the key coordinates as a P-column payload (the weighted sums
+            # in the fp16 split form up to a padded width of 64, fp32 beyond)
+            roof = roofline_transport_split(d, pairs_per_launch, avg_launch_s, d, cols=packed_stride(d),
+                                            split_sums=packed_stride(d) <= 64)
             roof["kernel"] = "k_transport_mfma<%d,1,4>" % packed_stride(d)
         else:
             roof = None  # the vector-ALU gradient is timed as a part of the default solve step (components_ms)

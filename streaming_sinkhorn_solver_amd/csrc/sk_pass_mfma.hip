@@ -84,7 +84,20 @@ struct TileStageF {
             *reinterpret_cast<float4*>(&ktile[key * PS + part * 4]) = v[r];
         }
     }
+
+    // The fp16 parts (h, l) of the coordinates times ys (a power of two),
+    // transposed: yt[part][coordinate][key], rows YS halves apart (see
+    // ysplit_stride).
+    __device__ __forceinline__ void store_split_t(uint16_t* yt, float ys) const;
 };
+
+// Row stride (halves) of a transposed split key tile of TL keys: a multiple of
+// 4, so that a lane group's 4 keys are one 8-byte read, padded so that the 16
+// rows a wave reads at once start in different banks.
+template <int TL>
+constexpr int ysplit_stride() {
+    return TL + 8;
+}
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));
@@ -167,6 +180,24 @@ __device__ __forceinline__ float f16_value(unsigned h) {
 __device__ __forceinline__ void split2(float v, unsigned& h, unsigned& l) {
     h = f16_bits(v);
     l = f16_bits(v - f16_value(h));
+}
+
+template <int P, int TL>
+__device__ __forceinline__ void TileStageF<P, TL>::store_split_t(uint16_t* yt, float ys) const {
+    constexpr int YS = ysplit_stride<TL>();
+#pragma unroll
+    for (int r = 0; r < F4; ++r) {
+        const int e = threadIdx.x + r * kBlock;
+        const int key = e / (P / 4), t0 = (e - key * (P / 4)) * 4;
+        const float c4[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            unsigned h, l;
+            split2(c4[i] * ys, h, l);
+            yt[(t0 + i) * YS + key] = (uint16_t)h;
+            yt[(P + t0 + i) * YS + key] = (uint16_t)l;
+        }
+    }
 }
 
 // The parts of packed rows: out[i][part][t] (parts h, l) of fl(in[i][t] rq) 2^e,
@@ -539,10 +570,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(pass_wav
 //          grad_i = 2 a_i (x~_i - T_i / S_i), S_i = sum_j w_ij (the plan's
 //          barycentric map; the plan scale cancels).
 // Every mode forms its scores in the fp16 split form of the solver pass (same
-// helpers and scales); the weighted sums keep fp32 matrix instructions.
+// helpers and scales).  The weighted sums of MODES 1 and 4 up to P = 64 take
+// the fp16 split form too (weights and key coordinates as two fp16 parts each,
+// three products); the other modes and widths keep fp32 matrix instructions.
 // 16-query blocks per wave of the transport kernel: their MFMA chains
 // interleave, at a register cost of NQB * P / 8 query VGPRs plus NQB output
 // tiles.
+// Exponent of the power of two the split weighted sums scale their weights by:
+// a weight w <= 1 becomes w 2^14 <= 2^14, within fp16's range, and the parts of
+// weights down to 2^-28 stay normal fp16 numbers (smaller ones add at most
+// 2^-39 each in absolute terms).
+constexpr int kWScaleExp = 14;
+
 constexpr int transport_nqb(int P, int NP, int MODE) {
     // the one-column kernel: 4 blocks, 151 against 171 us with 2 at 16384^2, d = 64 (bf16 split form); an
     // HVP at d = 16 4.93 against 5.18 ms
@@ -564,8 +603,17 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     constexpr int TL = Stage::TL;
     constexpr int RS = Stage::RS;
     constexpr int NQB = transport_nqb(P, NP, MODE);
+    // Modes whose payload is the key cloud (1, 4) take the weighted sums on fp16
+    // matrix instructions too, up to P = 64: weights and key coordinates as two
+    // fp16 parts each (three products), 32 keys per step.  Each workgroup splits
+    // and transposes its key tiles in LDS; at P = 128 a tile is one 32-key step,
+    // and that staging made the gradient slower (1.8 against 1.23 ms at 16384^2)
+    // instead of faster (0.55 against 0.63 ms at d = 64), so wider P keep fp32.
+    constexpr bool SPLITW = (MODE == 1 || MODE == 4) && TL >= 32 && P <= 64;
+    constexpr int YS = ysplit_stride<TL>();
     __shared__ u4v ktile[TL * RS];
-    __shared__ __align__(16) float ftile[KEYS ? TL * PS : 1];
+    __shared__ __align__(16) float ftile[KEYS && !SPLITW ? TL * PS : 1];
+    __shared__ __align__(16) uint16_t ytile[SPLITW ? 2 * P * YS : 1];
     __shared__ __align__(16) float btile[TL];
     __shared__ __align__(16) float ptile[PAY ? TL * KP : 1];
 
@@ -580,6 +628,12 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     // scores come back times sc.t (key biases staged the same way)
     const SplitScale sc = split_scale(A.qmax, A.kmax, A.rq);
     const u4v* qbp = reinterpret_cast<const u4v*>(A.qb);
+    // SPLITW: the key coordinates are split times 2^ey (their largest magnitude
+    // into [2^13, 2^14); capped so that 2^ey and 2^-(ey + kWScaleExp) stay
+    // normal floats) and the weights times 2^kWScaleExp, exact scalings taken
+    // off T and S before the epilogue
+    const int ey = SPLITW ? min(split_exp(*A.kmax), 100) : 0;
+    const float wofs = SPLITW ? (float)kWScaleExp : 0.0f;
 
     float vf[MODE == 2 ? NQB : 1][KT];
     u4v qh[NQB][KQ], ql[NQB][KQ];
@@ -597,7 +651,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
                 vf[MODE == 2 ? qb : 0][t] = dim < A.d ? 2.0f * A.rowv[(size_t)ic * A.d + dim] : 0.0f;
             }
         }
-        lse_c[qb] = A.lse[ic];
+        lse_c[qb] = A.lse[ic] - wofs;
         S[qb] = 0.0f;
         Tv[qb] = 0.0f;
 #pragma unroll
@@ -613,7 +667,10 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     for (int base = c0; base < c1; base += TL) {
         __syncthreads();
         stage.store(ktile, btile);
-        if constexpr (KEYS) fstage.store(ftile);
+        if constexpr (SPLITW)
+            fstage.store_split_t(ytile, ldexpf(1.0f, ey));
+        else if constexpr (KEYS)
+            fstage.store(ftile);
         if constexpr (PAY)
             for (int e = threadIdx.x; e < TL * KP; e += kBlock) {
                 const int col = base + e / KP;
@@ -626,6 +683,53 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
             if constexpr (KEYS) fstage.load(kp, base + TL, c1);
         }
         const int ntile = min(TL, c1 - base);
+        if constexpr (SPLITW) {
+            // Two 16-key blocks per step.  Contraction slot 8g + e of the weighted
+            // sums is key 4g + e of the first block (e < 4) and 16 + 4g + e - 4 of
+            // the second: the A operand is the lane's own eight weights (query c),
+            // the B operand 8 of those keys' parts of one coordinate, two 8-byte
+            // runs of the transposed tile.  Keys past the segment hold bias -inf,
+            // weight 0.
+            for (int k0 = 0; k0 < ntile; k0 += 32) {
+                f4 acc0[NQB], acc1[NQB];
+                const f4 bias0 = *reinterpret_cast<const f4*>(&btile[k0 + 4 * g]);
+                const f4 bias1 = *reinterpret_cast<const f4*>(&btile[k0 + 16 + 4 * g]);
+                split_scores<P, NQB>(ktile + (k0 + c) * RS, g, qh, ql, bias0, acc0);
+                split_scores<P, NQB>(ktile + (k0 + 16 + c) * RS, g, qh, ql, bias1, acc1);
+                u4v wh[NQB], wl[NQB];
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+                    unsigned hb[8], lb[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = e < 4 ? acc0[qb][e] : acc1[qb][e - 4];
+                        const float w = ex2(fmaf(x, sc.r, -lse_c[qb]));  // the weight times 2^kWScaleExp
+                        S[qb] += w;
+                        split2(w, hb[e], lb[e]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        wh[qb][j] = hb[2 * j] | (hb[2 * j + 1] << 16);
+                        wl[qb][j] = lb[2 * j] | (lb[2 * j + 1] << 16);
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const uint16_t* rh = ytile + (nb * 16 + c) * YS + k0 + 4 * g;
+                    const uint16_t* rl = rh + P * YS;
+                    const uint2 h0 = *reinterpret_cast<const uint2*>(rh), h1 = *reinterpret_cast<const uint2*>(rh + 16);
+                    const uint2 l0 = *reinterpret_cast<const uint2*>(rl), l1 = *reinterpret_cast<const uint2*>(rl + 16);
+                    const u4v yh = {h0.x, h0.y, h1.x, h1.y}, yl = {l0.x, l0.y, l1.x, l1.y};
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) T[qb][nb] = mfma_f16(wh[qb], yh, T[qb][nb]);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) T[qb][nb] = mfma_f16(wh[qb], yl, T[qb][nb]);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) T[qb][nb] = mfma_f16(wl[qb], yh, T[qb][nb]);
+                }
+            }
+            continue;
+        }
         for (int kb16 = 0; kb16 < ntile; kb16 += 16) {
             const f4 bias = *reinterpret_cast<const f4*>(&btile[kb16 + 4 * g]);
             f4 acc[NQB], dv[NQB];
@@ -676,6 +780,16 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
         }
     }
     constexpr int KA = 16 * NB;
+    if constexpr (SPLITW) {
+        // take off the exact scalings: weights 2^kWScaleExp, coordinates 2^ey
+        const float rw = ldexpf(1.0f, -kWScaleExp), rt = ldexpf(1.0f, -kWScaleExp - ey);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            S[qb] *= rw;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) T[qb][nb] *= rt;
+        }
+    }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
         const int q0 = qrow0 + qb * 16;

@@ -75,6 +75,9 @@ def test_transport_split_roofline_model():
     r20 = bench.roofline_transport_split(33, pairs, 1.0, 20)
     assert r20["ops_per_pair"] == 2 * 33 + 40 and "weighted sums (128)" in r20["mfma_dtype"]
     # the gradient (transport mode 4): the weighted key sums run over all P = 128 padded coordinates
+    # the gradient up to a padded width of 64: the weighted sums as three fp16 products too, 6 flops per column
+    rs = bench.roofline_transport_split(64, pairs, pairs * (384 + 384) / 2500e12, 64, cols=64, split_sums=True)
+    assert abs(rs["frac"] - 1.0) < 1e-3 and "fp16 split weighted sums (384)" in rs["mfma_dtype"]
     rg = bench.roofline_transport_split(100, pairs, 1.0, 100, cols=128)
     assert rg["ops_per_pair"] == 400 and "weighted sums (256)" in rg["mfma_dtype"]
     r9 = bench.roofline_transport_split(12, pairs, 1.0, 9)
