@@ -184,7 +184,7 @@ def roofline_transport_split(d: int, pairs_per_launch: float, avg_launch_s: floa
     dense peaks; `achieved` and `peak` are stated in the method's flops per pair (2 d + 2 x payload), `peak`
     being the rate that pipe time allows. `cols` overrides the tile width (the gradient's weighted key sums
     run over all P padded coordinates). `split_sums`: the weighted sums run on fp16 matrix instructions as three
-    products of two-part splits (6 fp16 flops per pair and column; the gradient up to a padded width of 64)."""
+    products of two-part splits (6 fp16 flops per pair and column; the gradient up to a padded width of 128)."""
     f16_ops = (8 if packed_stride(d) == 16 else 6) * d
     if cols is None:
         cols = 16 if payload <= 16 else 64
@@ -600,9 +600,9 @@ def main():
     elif mode == "grad":
         if d > 8:
             # transport mode 4: split scores, then the key coordinates as a P-column payload (the weighted sums
-            # in the fp16 split form up to a padded width of 64, fp32 beyond)
+            # in the fp16 split form up to a padded width of 128, fp32 beyond)
             roof = roofline_transport_split(d, pairs_per_launch, avg_launch_s, d, cols=packed_stride(d),
-                                            split_sums=packed_stride(d) <= 64)
+                                            split_sums=packed_stride(d) <= 128)
             roof["kernel"] = "k_transport_mfma<%d,1,4>" % packed_stride(d)
         else:
             roof = None  # the vector-ALU gradient is timed as a part of the default solve step (components_ms)

@@ -56,6 +56,13 @@ Split split_for(int64_t nq, int64_t nk, int rows_per_block) {
 // workspace is sized by it), but when the row blocks fit the GPU's resident
 // workgroups (cap) at once, only as many splits as keep them all resident, so
 // the grid runs as one full wave instead of a full wave and a ragged one.
+// The same split with its key columns per split rounded up to a multiple of
+// align (never more splits than before, so the workspace still holds them).
+Split align_split(Split s, int64_t nk, int align) {
+    const int64_t cols = ((int64_t)s.cols + align - 1) / align * align;
+    return Split{(int)((nk + cols - 1) / cols), (int)cols};
+}
+
 Split split_resident(int64_t nq, int64_t nk, int rows_per_block, int cap) {
     const Split base = split_for(nq, nk, rows_per_block);
     const int64_t row_blocks = (nq + rows_per_block - 1) / rows_per_block;
@@ -381,6 +388,7 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.yb = take(L.split ? um * 2 * P * 2 : 0);
     L.amax = take(L.split ? 2 * sizeof(float) : 0);
     L.amax_part = take(L.split ? 2 * kAbsMaxBlocks * sizeof(float) : 0);
+    L.kt = take(L.mfma ? (umx + kTransColAlign - 1) / kTransColAlign * kTransColAlign * 2 * P * 2 : 0);
     L.total = off;
     return L;
 }
@@ -774,6 +782,7 @@ int grad_core(const Ws& W, const float* x, const float* y, const float* a, const
         const int64_t cols = (m + lim.nsplit - 1) / lim.nsplit;
         sp = Split{(int)((m + cols - 1) / cols), (int)cols};
     }
+    sp = align_split(sp, m, kTransColAlign);
     TransArgs t{};
     t.q = W.f(L.xp);
     t.k = W.f(L.yp);
@@ -797,6 +806,7 @@ int grad_core(const Ws& W, const float* x, const float* y, const float* a, const
     t.ldo = d;
     t.kout = d;
     t.gw = a;
+    t.kt = W.h(L.kt);
     hipEvent_t e0, e1;
     if ((st = timing_events(n, m, s, &e0, &e1))) return st;
     SK_TRY(launch_transport_mfma(t, 4, 16, s, e0, e1));
@@ -907,10 +917,14 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     // a single payload column runs on the vector ALUs inside the matrix-core kernel
     const int kmode = (L.mfma && mode == 0 && kin == 1) ? 3 : mode;
     const int kwidth = L.mfma ? (kin <= 16 ? 16 : 64) : (kin <= 1 ? 1 : (kin <= 4 ? 4 : kTransMaxK));
-    const Split sp = split_resident(t.nq, t.nk,
-                                    L.mfma ? mfma_transport_rows_per_block(L.P, kmode, kwidth)
-                                           : transport_rows_per_block(),
-                                    transport_capacity_cached(L, kmode, kwidth));
+    Split sp = split_resident(t.nq, t.nk,
+                              L.mfma ? mfma_transport_rows_per_block(L.P, kmode, kwidth)
+                                     : transport_rows_per_block(),
+                              transport_capacity_cached(L, kmode, kwidth));
+    if (L.mfma) {
+        sp = align_split(sp, t.nk, kTransColAlign);
+        t.kt = W.h(L.kt);
+    }
     t.cols_per_split = sp.cols;
     t.nsplit = sp.nsplit;
     t.part = reinterpret_cast<float2*>(W.base + T.part);

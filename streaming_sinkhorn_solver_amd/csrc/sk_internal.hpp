@@ -207,6 +207,8 @@ struct TransArgs {
     int ldo, kout, ldp, kin;
     float* mass;         // [nq] row sums of the plan, or null
     const float* gw;     // matrix-core gradient (mode 4): the row weights a [nq], else null
+    uint16_t* kt;        // matrix-core layout: room for the key coordinates' fp16 parts transposed in blocks
+                         // of 32 keys, [ceil(nk / 32)][2][P][32] (written by the launch of modes 1 and 4)
 };
 
 // Workspace carve-up, a pure function of (n, m, d).
@@ -220,6 +222,7 @@ struct Layout {
     size_t amax, amax_part;   // largest |packed coordinate| of x and y (2 floats), and its per-block maxima
     size_t lse_r2, lse_c2;    // second state buffers (a check keeps the previous state)
     size_t snap_f, snap_g;    // potentials at the previous check (potential stop rule)
+    size_t kt;                // matrix-core layout: transposed fp16 key parts of the weighted sums (TransArgs::kt)
     size_t total;
 };
 
@@ -228,6 +231,9 @@ Layout make_layout(int64_t n, int64_t m, int d);
 // Split policy of a streamed pass: number of column splits for nq queries
 // against nk keys when one workgroup covers rows_per_block queries.
 int plan_split(int64_t nq, int64_t nk, int rows_per_block);
+// Key columns per split of the matrix-core transport kernels are a multiple of
+// this (the transposed key parts are staged in whole blocks of 32 keys).
+constexpr int kTransColAlign = 32;
 
 // ----- launchers (return hipError_t of the launch) --------------------------------
 hipError_t launch_centre(const float* x, const float* y, int n, int m, int d, double* partials,

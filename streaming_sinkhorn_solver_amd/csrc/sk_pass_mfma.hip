@@ -84,11 +84,6 @@ struct TileStageF {
             *reinterpret_cast<float4*>(&ktile[key * PS + part * 4]) = v[r];
         }
     }
-
-    // The fp16 parts (h, l) of the coordinates times ys (a power of two),
-    // transposed: yt[part][coordinate][key], rows YS halves apart (see
-    // ysplit_stride).
-    __device__ __forceinline__ void store_split_t(uint16_t* yt, float ys) const;
 };
 
 // Row stride (halves) of a transposed split key tile of TL keys: a multiple of
@@ -182,23 +177,71 @@ __device__ __forceinline__ void split2(float v, unsigned& h, unsigned& l) {
     l = f16_bits(v - f16_value(h));
 }
 
+// ---- the weighted sums of the key-payload transports in the split form
+//
+// The key coordinates are split once per launch by k_split_keys_t into fp16
+// parts times 2^ey (payload_exp: the cloud's largest |coordinate| into
+// [2^13, 2^14), capped so that 2^ey and 2^-(ey + kWScaleExp) stay normal
+// floats), transposed in blocks of 32 keys: kt[(j / 32) 2P + part P + t][j % 32],
+// keys past nk zero.  A workgroup stages a tile of them with plain 16-byte
+// copies (TileStageT) into yt[part P + t][key] (rows YS halves apart).
+__device__ __forceinline__ int payload_exp(const float* kmax) { return min(split_exp(*kmax), 100); }
+
+__global__ __launch_bounds__(kBlock) void k_split_keys_t(const float* __restrict__ k, int nk, int P,
+                                                         const float* __restrict__ kmax, uint16_t* __restrict__ kt) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nkp = (int64_t)(nk + kTransColAlign - 1) / kTransColAlign * kTransColAlign;
+    if (e >= nkp * P) return;
+    // 32 consecutive threads take the 32 keys of one block at one coordinate: each wave writes two 64-byte runs
+    const int jj = (int)(e % kTransColAlign);
+    const int64_t rest = e / kTransColAlign;
+    const int t = (int)(rest % P);
+    const int64_t blk = rest / P;
+    const int64_t j = blk * kTransColAlign + jj;
+    unsigned h = 0, l = 0;
+    if (j < nk) split2(k[j * P + t] * ldexpf(1.0f, payload_exp(kmax)), h, l);
+    kt[((blk * 2) * P + t) * kTransColAlign + jj] = (uint16_t)h;
+    kt[((blk * 2 + 1) * P + t) * kTransColAlign + jj] = (uint16_t)l;
+}
+
+// Register staging of one tile of TL keys of the transposed parts (TL a
+// multiple of 32, the tile's first key a multiple of 32): TL / 32 blocks of 2P
+// rows of 32 halves (four 16-byte units each).  Blocks past the array read as
+// zero; keys past the segment inside a block carry weight 0.
 template <int P, int TL>
-__device__ __forceinline__ void TileStageF<P, TL>::store_split_t(uint16_t* yt, float ys) const {
-    constexpr int YS = ysplit_stride<TL>();
+struct TileStageT {
+    static constexpr int UNITS = TL / 32 * 2 * P * 4;
+    static constexpr int U = UNITS / kBlock;
+    static_assert(TL % 32 == 0 && UNITS % kBlock == 0, "tile must split evenly over the workgroup");
+    u4v v[U];
+
+    __device__ __forceinline__ void load(const u4v* __restrict__ kt, int base, int nk) {
+        const int nblk = (nk + 31) / 32;
 #pragma unroll
-    for (int r = 0; r < F4; ++r) {
-        const int e = threadIdx.x + r * kBlock;
-        const int key = e / (P / 4), t0 = (e - key * (P / 4)) * 4;
-        const float c4[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            unsigned h, l;
-            split2(c4[i] * ys, h, l);
-            yt[(t0 + i) * YS + key] = (uint16_t)h;
-            yt[(P + t0 + i) * YS + key] = (uint16_t)l;
+        for (int r = 0; r < U; ++r) {
+            const int e = threadIdx.x + r * kBlock;
+            const int blk = e / (2 * P * 4), rem = e - blk * (2 * P * 4);
+            const int b = base / 32 + blk;
+            const u4v x = kt[((size_t)min(b, nblk - 1) * 2 * P) * 4 + rem];
+            v[r] = b < nblk ? x : u4v{0u, 0u, 0u, 0u};
         }
     }
-}
+
+    __device__ __forceinline__ void store(uint16_t* yt) const {
+        constexpr int YS = ysplit_stride<TL>();
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+            const int e = threadIdx.x + r * kBlock;
+            const int blk = e / (2 * P * 4), rem = e - blk * (2 * P * 4);
+            const int row = rem / 4, q = rem - row * 4;
+            *reinterpret_cast<u4v*>(yt + row * YS + blk * 32 + q * 8) = v[r];
+        }
+    }
+};
+
+// Whether a transport mode takes its weighted sums in the split form: the
+// key-payload modes up to P = 128 (a key tile then holds at least 32 keys).
+constexpr bool split_sums(int P, int MODE) { return (MODE == 1 || MODE == 4) && P <= 128; }
 
 // The parts of packed rows: out[i][part][t] (parts h, l) of fl(in[i][t] rq) 2^e,
 // e = cloud_exp of the cloud's largest |coordinate| *cmax.
@@ -570,7 +613,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(pass_wav
 //          grad_i = 2 a_i (x~_i - T_i / S_i), S_i = sum_j w_ij (the plan's
 //          barycentric map; the plan scale cancels).
 // Every mode forms its scores in the fp16 split form of the solver pass (same
-// helpers and scales).  The weighted sums of MODES 1 and 4 up to P = 64 take
+// helpers and scales).  The weighted sums of MODES 1 and 4 up to P = 128 take
 // the fp16 split form too (weights and key coordinates as two fp16 parts each,
 // three products); the other modes and widths keep fp32 matrix instructions.
 // 16-query blocks per wave of the transport kernel: their MFMA chains
@@ -604,12 +647,10 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     constexpr int RS = Stage::RS;
     constexpr int NQB = transport_nqb(P, NP, MODE);
     // Modes whose payload is the key cloud (1, 4) take the weighted sums on fp16
-    // matrix instructions too, up to P = 64: weights and key coordinates as two
-    // fp16 parts each (three products), 32 keys per step.  Each workgroup splits
-    // and transposes its key tiles in LDS; at P = 128 a tile is one 32-key step,
-    // and that staging made the gradient slower (1.8 against 1.23 ms at 16384^2)
-    // instead of faster (0.55 against 0.63 ms at d = 64), so wider P keep fp32.
-    constexpr bool SPLITW = (MODE == 1 || MODE == 4) && TL >= 32 && P <= 64;
+    // matrix instructions too, up to P = 128: weights and key coordinates as
+    // two fp16 parts each (three products), 32 keys per step.
+    constexpr bool SPLITW = split_sums(P, MODE);
+    static_assert(!SPLITW || TL >= 32, "the split weighted sums take 32 keys per step");
     constexpr int YS = ysplit_stride<TL>();
     __shared__ u4v ktile[TL * RS];
     __shared__ __align__(16) float ftile[KEYS && !SPLITW ? TL * PS : 1];
@@ -628,11 +669,11 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     // scores come back times sc.t (key biases staged the same way)
     const SplitScale sc = split_scale(A.qmax, A.kmax, A.rq);
     const u4v* qbp = reinterpret_cast<const u4v*>(A.qb);
-    // SPLITW: the key coordinates are split times 2^ey (their largest magnitude
-    // into [2^13, 2^14); capped so that 2^ey and 2^-(ey + kWScaleExp) stay
-    // normal floats) and the weights times 2^kWScaleExp, exact scalings taken
-    // off T and S before the epilogue
-    const int ey = SPLITW ? min(split_exp(*A.kmax), 100) : 0;
+    // SPLITW: the key coordinates come split times 2^ey (k_split_keys_t) and the
+    // weights are split times 2^kWScaleExp, exact scalings taken off T and S
+    // before the epilogue
+    const int ey = SPLITW ? payload_exp(A.kmax) : 0;
+    const u4v* ktp = reinterpret_cast<const u4v*>(A.kt);
     const float wofs = SPLITW ? (float)kWScaleExp : 0.0f;
 
     float vf[MODE == 2 ? NQB : 1][KT];
@@ -660,15 +701,20 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
 
     Stage stage;
     FStage fstage;
+    struct NoStage {};
+    std::conditional_t<SPLITW, TileStageT<P, TL>, NoStage> tstage;
     if (c0 < c1) {
         stage.load(kb, A.kbias, sc.t, c0, c1);
-        if constexpr (KEYS) fstage.load(kp, c0, c1);
+        if constexpr (SPLITW)
+            tstage.load(ktp, c0, A.nk);
+        else if constexpr (KEYS)
+            fstage.load(kp, c0, c1);
     }
     for (int base = c0; base < c1; base += TL) {
         __syncthreads();
         stage.store(ktile, btile);
         if constexpr (SPLITW)
-            fstage.store_split_t(ytile, ldexpf(1.0f, ey));
+            tstage.store(ytile);
         else if constexpr (KEYS)
             fstage.store(ftile);
         if constexpr (PAY)
@@ -680,7 +726,10 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
         __syncthreads();
         if (base + TL < c1) {
             stage.load(kb, A.kbias, sc.t, base + TL, c1);
-            if constexpr (KEYS) fstage.load(kp, base + TL, c1);
+            if constexpr (SPLITW)
+                tstage.load(ktp, base + TL, A.nk);
+            else if constexpr (KEYS)
+                fstage.load(kp, base + TL, c1);
         }
         const int ntile = min(TL, c1 - base);
         if constexpr (SPLITW) {
@@ -890,6 +939,13 @@ hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t
     // the split keys and the clouds' largest magnitudes are written by every set-up
     if (!a.kb || !a.qb || !a.qmax || !a.kmax) return hipErrorInvalidValue;
     if (MODE == 4 && (!a.gw || a.kout > P)) return hipErrorInvalidValue;
+    if constexpr (split_sums(P, MODE)) {
+        // the split weighted sums stage whole 32-key blocks: every key split starts on a block
+        if (!a.kt || (a.nsplit > 1 && a.cols_per_split % kTransColAlign != 0)) return hipErrorInvalidValue;
+        const int64_t elems = (int64_t)(a.nk + kTransColAlign - 1) / kTransColAlign * kTransColAlign * P;
+        hipLaunchKernelGGL(k_split_keys_t, dim3((unsigned)((elems + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, a.k,
+                           a.nk, P, a.kmax, a.kt);
+    }
     dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
     SK_LAUNCH_TIMED((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), s, ev0, ev1, a);
     if (a.nsplit > 1 && MODE == 4)
