@@ -184,7 +184,7 @@ def roofline_transport_split(d: int, pairs_per_launch: float, avg_launch_s: floa
     dense peaks; `achieved` and `peak` are stated in the method's flops per pair (2 d + 2 x payload), `peak`
     being the rate that pipe time allows. `cols` overrides the tile width (the gradient's weighted key sums
     run over all P padded coordinates). `split_sums`: the weighted sums run on fp16 matrix instructions as three
-    products of two-part splits (6 fp16 flops per pair and column; the gradient up to a padded width of 128)."""
+    products of two-part splits (6 fp16 flops per pair and column; modes 0, 1 and 4 up to a padded width of 128)."""
     f16_ops = (8 if packed_stride(d) == 16 else 6) * d
     if cols is None:
         cols = 16 if payload <= 16 else 64
@@ -619,7 +619,8 @@ def main():
                 # the one-column kernel forms its scores in the split form (payload FMAs on the vector ALUs)
                 roof = roofline_split(d, pairs_per_launch, avg_launch_s)
             else:
-                roof = roofline_transport_split(d, pairs_per_launch, avg_launch_s, payload)
+                # the payload's weighted sums in the fp16 split form up to a padded width of 128
+                roof = roofline_transport_split(d, pairs_per_launch, avg_launch_s, payload, split_sums=p2 <= 128)
             # one column: MODE 3 (vector-ALU payload); d columns: 16- or 64-column tiles (MODE 0)
             roof["kernel"] = ("k_transport_mfma<%d,1,3>" % p2 if payload == 1 else
                               "k_transport_mfma<%d,%d,0>" % (p2, 4 if payload > 16 else 1))

@@ -389,6 +389,7 @@ Layout make_layout(int64_t n, int64_t m, int d) {
     L.amax = take(L.split ? 2 * sizeof(float) : 0);
     L.amax_part = take(L.split ? 2 * kAbsMaxBlocks * sizeof(float) : 0);
     L.kt = take(L.mfma ? (umx + kTransColAlign - 1) / kTransColAlign * kTransColAlign * 2 * P * 2 : 0);
+    L.pmax = take(L.mfma ? 64 * sizeof(float) : 0);
     L.total = off;
     return L;
 }
@@ -924,6 +925,7 @@ int transport_pass(const Ws& W, const TLayout& T, bool row_side, float eps, int 
     if (L.mfma) {
         sp = align_split(sp, t.nk, kTransColAlign);
         t.kt = W.h(L.kt);
+        t.pmax = W.f(L.pmax);
     }
     t.cols_per_split = sp.cols;
     t.nsplit = sp.nsplit;

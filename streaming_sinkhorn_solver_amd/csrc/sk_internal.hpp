@@ -207,8 +207,10 @@ struct TransArgs {
     int ldo, kout, ldp, kin;
     float* mass;         // [nq] row sums of the plan, or null
     const float* gw;     // matrix-core gradient (mode 4): the row weights a [nq], else null
-    uint16_t* kt;        // matrix-core layout: room for the key coordinates' fp16 parts transposed in blocks
-                         // of 32 keys, [ceil(nk / 32)][2][P][32] (written by the launch of modes 1 and 4)
+    uint16_t* kt;        // matrix-core layout: room for the payload's fp16 parts (the key coordinates in modes 1
+                         // and 4, the payload columns in mode 0) transposed in blocks of 32 keys,
+                         // [ceil(nk / 32)][2][columns][32] (written by the launch)
+    float* pmax;         // matrix-core layout: room for the payload columns' largest magnitudes (64 floats, mode 0)
 };
 
 // Workspace carve-up, a pure function of (n, m, d).
@@ -222,7 +224,8 @@ struct Layout {
     size_t amax, amax_part;   // largest |packed coordinate| of x and y (2 floats), and its per-block maxima
     size_t lse_r2, lse_c2;    // second state buffers (a check keeps the previous state)
     size_t snap_f, snap_g;    // potentials at the previous check (potential stop rule)
-    size_t kt;                // matrix-core layout: transposed fp16 key parts of the weighted sums (TransArgs::kt)
+    size_t kt;                // matrix-core layout: transposed fp16 payload parts of the weighted sums (TransArgs::kt)
+    size_t pmax;              // matrix-core layout: largest magnitude of each payload column (TransArgs::pmax)
     size_t total;
 };
 

@@ -179,7 +179,7 @@ __device__ __forceinline__ void split2(float v, unsigned& h, unsigned& l) {
 
 // ---- the weighted sums of the key-payload transports in the split form
 //
-// The key coordinates are split once per launch by k_split_keys_t into fp16
+// The key coordinates are split once per launch by k_split_cols_t into fp16
 // parts times 2^ey (payload_exp: the cloud's largest |coordinate| into
 // [2^13, 2^14), capped so that 2^ey and 2^-(ey + kWScaleExp) stay normal
 // floats), transposed in blocks of 32 keys: kt[(j / 32) 2P + part P + t][j % 32],
@@ -187,32 +187,54 @@ __device__ __forceinline__ void split2(float v, unsigned& h, unsigned& l) {
 // copies (TileStageT) into yt[part P + t][key] (rows YS halves apart).
 __device__ __forceinline__ int payload_exp(const float* kmax) { return min(split_exp(*kmax), 100); }
 
-__global__ __launch_bounds__(kBlock) void k_split_keys_t(const float* __restrict__ k, int nk, int P,
-                                                         const float* __restrict__ kmax, uint16_t* __restrict__ kt) {
+// The general payload of mode 0 takes the same layout with KA columns (zero
+// past its kin) and a power of two per column, from that column's largest
+// magnitude (k_col_absmax), so a column of small values keeps its precision.
+__global__ __launch_bounds__(kBlock) void k_split_cols_t(const float* __restrict__ v, int nk, int ld, int ncols,
+                                                         int KA, const float* __restrict__ cmax, int per_col,
+                                                         uint16_t* __restrict__ kt) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nkp = (int64_t)(nk + kTransColAlign - 1) / kTransColAlign * kTransColAlign;
-    if (e >= nkp * P) return;
-    // 32 consecutive threads take the 32 keys of one block at one coordinate: each wave writes two 64-byte runs
+    if (e >= nkp * KA) return;
+    // 32 consecutive threads take the 32 keys of one block at one column: each wave writes two 64-byte runs
     const int jj = (int)(e % kTransColAlign);
     const int64_t rest = e / kTransColAlign;
-    const int t = (int)(rest % P);
-    const int64_t blk = rest / P;
+    const int t = (int)(rest % KA);
+    const int64_t blk = rest / KA;
     const int64_t j = blk * kTransColAlign + jj;
     unsigned h = 0, l = 0;
-    if (j < nk) split2(k[j * P + t] * ldexpf(1.0f, payload_exp(kmax)), h, l);
-    kt[((blk * 2) * P + t) * kTransColAlign + jj] = (uint16_t)h;
-    kt[((blk * 2 + 1) * P + t) * kTransColAlign + jj] = (uint16_t)l;
+    if (j < nk && t < ncols) split2(v[j * ld + t] * ldexpf(1.0f, payload_exp(per_col ? cmax + t : cmax)), h, l);
+    kt[((blk * 2) * KA + t) * kTransColAlign + jj] = (uint16_t)h;
+    kt[((blk * 2 + 1) * KA + t) * kTransColAlign + jj] = (uint16_t)l;
 }
 
-// Register staging of one tile of TL keys of the transposed parts (TL a
-// multiple of 32, the tile's first key a multiple of 32): TL / 32 blocks of 2P
-// rows of 32 halves (four 16-byte units each).  Blocks past the array read as
-// zero; keys past the segment inside a block carry weight 0.
+// Largest |v[j ld + t]| over the nk rows of each column t < ncols (0 for
+// ncols <= t < KA); one workgroup per column.
+__global__ __launch_bounds__(kBlock) void k_col_absmax(const float* __restrict__ v, int nk, int ld, int ncols,
+                                                       float* __restrict__ out) {
+    __shared__ float sh[kBlock];
+    const int t = blockIdx.x;
+    float mx = 0.0f;
+    if (t < ncols)
+        for (int j = threadIdx.x; j < nk; j += kBlock) mx = fmaxf(mx, fabsf(v[(size_t)j * ld + t]));
+    sh[threadIdx.x] = mx;
+    __syncthreads();
+    for (int w = kBlock / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) sh[threadIdx.x] = fmaxf(sh[threadIdx.x], sh[threadIdx.x + w]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[t] = sh[0];
+}
+
+// Register staging of one tile of TL keys of the transposed parts of P
+// columns (TL a multiple of 32, the tile's first key a multiple of 32): TL / 32
+// blocks of 2P rows of 32 halves (four 16-byte units each).  Blocks past the
+// array read as zero; keys past the segment inside a block carry weight 0.
 template <int P, int TL>
 struct TileStageT {
     static constexpr int UNITS = TL / 32 * 2 * P * 4;
-    static constexpr int U = UNITS / kBlock;
-    static_assert(TL % 32 == 0 && UNITS % kBlock == 0, "tile must split evenly over the workgroup");
+    static constexpr int U = (UNITS + kBlock - 1) / kBlock;  // the last round may be partial (16 columns, P = 128)
+    static_assert(TL % 32 == 0 && (UNITS % kBlock == 0 || UNITS < kBlock), "tile must split over the workgroup");
     u4v v[U];
 
     __device__ __forceinline__ void load(const u4v* __restrict__ kt, int base, int nk) {
@@ -220,6 +242,7 @@ struct TileStageT {
 #pragma unroll
         for (int r = 0; r < U; ++r) {
             const int e = threadIdx.x + r * kBlock;
+            if (UNITS % kBlock != 0 && e >= UNITS) continue;
             const int blk = e / (2 * P * 4), rem = e - blk * (2 * P * 4);
             const int b = base / 32 + blk;
             const u4v x = kt[((size_t)min(b, nblk - 1) * 2 * P) * 4 + rem];
@@ -232,6 +255,7 @@ struct TileStageT {
 #pragma unroll
         for (int r = 0; r < U; ++r) {
             const int e = threadIdx.x + r * kBlock;
+            if (UNITS % kBlock != 0 && e >= UNITS) continue;
             const int blk = e / (2 * P * 4), rem = e - blk * (2 * P * 4);
             const int row = rem / 4, q = rem - row * 4;
             *reinterpret_cast<u4v*>(yt + row * YS + blk * 32 + q * 8) = v[r];
@@ -240,8 +264,9 @@ struct TileStageT {
 };
 
 // Whether a transport mode takes its weighted sums in the split form: the
-// key-payload modes up to P = 128 (a key tile then holds at least 32 keys).
-constexpr bool split_sums(int P, int MODE) { return (MODE == 1 || MODE == 4) && P <= 128; }
+// key-payload modes and the general payload (mode 0) up to P = 128 (a key tile
+// then holds at least 32 keys); not MODE 2, whose weights carry a signed factor.
+constexpr bool split_sums(int P, int MODE) { return (MODE == 0 || MODE == 1 || MODE == 4) && P <= 128; }
 
 // The parts of packed rows: out[i][part][t] (parts h, l) of fl(in[i][t] rq) 2^e,
 // e = cloud_exp of the cloud's largest |coordinate| *cmax.
@@ -640,7 +665,6 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     constexpr bool KEYS = MODE == 1 || MODE == 2 || MODE == 4;  // the fp32 key coordinates are an operand
     constexpr int NB = KEYS ? P / 16 : NP;                       // 16-column output blocks (unused in MODE 3)
     constexpr int KP = MODE == 0 ? 16 * NP : 1;                  // payload floats per key in LDS
-    constexpr bool PAY = MODE == 0 || MODE == 2 || MODE == 3;    // a payload tile
     using Stage = TileStage2<P>;
     using FStage = TileStageF<P, Stage::TL>;
     constexpr int TL = Stage::TL;
@@ -652,9 +676,11 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     constexpr bool SPLITW = split_sums(P, MODE);
     static_assert(!SPLITW || TL >= 32, "the split weighted sums take 32 keys per step");
     constexpr int YS = ysplit_stride<TL>();
+    constexpr int KA = KEYS ? P : 16 * NP;                        // columns of the weighted sums
+    constexpr bool PAY = (MODE == 0 && !SPLITW) || MODE == 2 || MODE == 3;  // an fp32 payload tile
     __shared__ u4v ktile[TL * RS];
     __shared__ __align__(16) float ftile[KEYS && !SPLITW ? TL * PS : 1];
-    __shared__ __align__(16) uint16_t ytile[SPLITW ? 2 * P * YS : 1];
+    __shared__ __align__(16) uint16_t ytile[SPLITW ? 2 * KA * YS : 1];
     __shared__ __align__(16) float btile[TL];
     __shared__ __align__(16) float ptile[PAY ? TL * KP : 1];
 
@@ -669,10 +695,10 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     // scores come back times sc.t (key biases staged the same way)
     const SplitScale sc = split_scale(A.qmax, A.kmax, A.rq);
     const u4v* qbp = reinterpret_cast<const u4v*>(A.qb);
-    // SPLITW: the key coordinates come split times 2^ey (k_split_keys_t) and the
+    // SPLITW: the key coordinates come split times 2^ey (k_split_cols_t) and the
     // weights are split times 2^kWScaleExp, exact scalings taken off T and S
     // before the epilogue
-    const int ey = SPLITW ? payload_exp(A.kmax) : 0;
+    const int ey = SPLITW && KEYS ? payload_exp(A.kmax) : 0;
     const u4v* ktp = reinterpret_cast<const u4v*>(A.kt);
     const float wofs = SPLITW ? (float)kWScaleExp : 0.0f;
 
@@ -702,7 +728,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
     Stage stage;
     FStage fstage;
     struct NoStage {};
-    std::conditional_t<SPLITW, TileStageT<P, TL>, NoStage> tstage;
+    std::conditional_t<SPLITW, TileStageT<KA, TL>, NoStage> tstage;
     if (c0 < c1) {
         stage.load(kb, A.kbias, sc.t, c0, c1);
         if constexpr (SPLITW)
@@ -765,7 +791,7 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const uint16_t* rh = ytile + (nb * 16 + c) * YS + k0 + 4 * g;
-                    const uint16_t* rl = rh + P * YS;
+                    const uint16_t* rl = rh + KA * YS;
                     const uint2 h0 = *reinterpret_cast<const uint2*>(rh), h1 = *reinterpret_cast<const uint2*>(rh + 16);
                     const uint2 l0 = *reinterpret_cast<const uint2*>(rl), l1 = *reinterpret_cast<const uint2*>(rl + 16);
                     const u4v yh = {h0.x, h0.y, h1.x, h1.y}, yl = {l0.x, l0.y, l1.x, l1.y};
@@ -828,16 +854,20 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
             }
         }
     }
-    constexpr int KA = 16 * NB;
+    static_assert(KA == 16 * NB, "one 16-column block per output tile");
     if constexpr (SPLITW) {
-        // take off the exact scalings: weights 2^kWScaleExp, coordinates 2^ey
-        const float rw = ldexpf(1.0f, -kWScaleExp), rt = ldexpf(1.0f, -kWScaleExp - ey);
+        // take off the exact scalings: weights 2^kWScaleExp, payload 2^ey (mode 0:
+        // per column, this lane's column nb 16 + c)
+        const float rw = ldexpf(1.0f, -kWScaleExp);
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            S[qb] *= rw;
+        for (int nb = 0; nb < NB; ++nb) {
+            const int e = MODE == 0 ? payload_exp(A.pmax + nb * 16 + c) : ey;
+            const float rt = ldexpf(1.0f, -kWScaleExp - e);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) T[qb][nb] *= rt;
+            for (int qb = 0; qb < NQB; ++qb) T[qb][nb] *= rt;
         }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) S[qb] *= rw;
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -942,9 +972,17 @@ hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t
     if constexpr (split_sums(P, MODE)) {
         // the split weighted sums stage whole 32-key blocks: every key split starts on a block
         if (!a.kt || (a.nsplit > 1 && a.cols_per_split % kTransColAlign != 0)) return hipErrorInvalidValue;
-        const int64_t elems = (int64_t)(a.nk + kTransColAlign - 1) / kTransColAlign * kTransColAlign * P;
-        hipLaunchKernelGGL(k_split_keys_t, dim3((unsigned)((elems + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, a.k,
-                           a.nk, P, a.kmax, a.kt);
+        constexpr int KS = MODE == 0 ? 16 * NP : P;  // columns of the split payload (<= P)
+        const int64_t elems = (int64_t)(a.nk + kTransColAlign - 1) / kTransColAlign * kTransColAlign * KS;
+        const dim3 sgrid((unsigned)((elems + kBlock - 1) / kBlock));
+        if constexpr (MODE == 0) {
+            if (!a.pay || !a.pmax || a.kin < 1 || a.kin > KS) return hipErrorInvalidValue;
+            hipLaunchKernelGGL(k_col_absmax, dim3(KS), dim3(kBlock), 0, s, a.pay, a.nk, a.ldp, a.kin, a.pmax);
+            hipLaunchKernelGGL(k_split_cols_t, sgrid, dim3(kBlock), 0, s, a.pay, a.nk, a.ldp, a.kin, KS,
+                               (const float*)a.pmax, 1, a.kt);
+        } else {
+            hipLaunchKernelGGL(k_split_cols_t, sgrid, dim3(kBlock), 0, s, a.k, a.nk, P, P, P, a.kmax, 0, a.kt);
+        }
     }
     dim3 grid((a.nq + rpb - 1) / rpb, a.nsplit);
     SK_LAUNCH_TIMED((k_transport_mfma<P, NP, MODE>), grid, dim3(kBlock), s, ev0, ev1, a);
