@@ -95,6 +95,8 @@ constexpr int ysplit_stride() {
 }
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
 #ifndef SK_MFMA2_TILE
@@ -774,18 +776,22 @@ __global__ __launch_bounds__(kBlock) void k_transport_mfma(TransArgs A) {
                 u4v wh[NQB], wl[NQB];
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
-                    unsigned hb[8], lb[8];
+                    float wv8[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float x = e < 4 ? acc0[qb][e] : acc1[qb][e - 4];
-                        const float w = ex2(fmaf(x, sc.r, -lse_c[qb]));  // the weight times 2^kWScaleExp
-                        S[qb] += w;
-                        split2(w, hb[e], lb[e]);
+                        wv8[e] = ex2(fmaf(x, sc.r, -lse_c[qb]));  // the weight times 2^kWScaleExp
+                        S[qb] += wv8[e];
                     }
+                    // the parts of split2, two weights per packed conversion (v_cvt_pk_f16_f32, rounding to
+                    // nearest even): h = fp16(w), l = fp16(w - h)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        wh[qb][j] = hb[2 * j] | (hb[2 * j + 1] << 16);
-                        wl[qb][j] = lb[2 * j] | (lb[2 * j + 1] << 16);
+                        const f2v p = {wv8[2 * j], wv8[2 * j + 1]};
+                        const h2v hp = __builtin_convertvector(p, h2v);
+                        const h2v lp = __builtin_convertvector(p - __builtin_convertvector(hp, f2v), h2v);
+                        wh[qb][j] = __builtin_bit_cast(unsigned, hp);
+                        wl[qb][j] = __builtin_bit_cast(unsigned, lp);
                     }
                 }
 #pragma unroll
