@@ -107,6 +107,37 @@ def test_transport_matches_oracle(case):
         assert np.all(np.abs(got1 - ref) <= 32 * kap * ref + 1e-30)
 
 
+# The matrix-core products split their payload into fp16 parts with a power of two per column: columns whose
+# magnitudes lie 1e20 apart (and an all-zero one) must each keep the elementwise bound of their own column,
+# which a single scale for all columns would lose to fp16 underflow. 40 columns: a 64-column tile with 24 padded.
+COLUMN_SCALE_CASES = [(900, 700, 64, 0.5, 5, False, 21), (600, 800, 100, 0.4, 4, True, 22), (700, 500, 20, 0.3, 5, False, 23)]
+
+
+@pytest.mark.parametrize("case", COLUMN_SCALE_CASES, ids=[f"{c[0]}x{c[1]}d{c[2]}{'T' if c[5] else ''}"
+                                                          for c in COLUMN_SCALE_CASES])
+def test_transport_payload_columns_far_apart(case):
+    n, m, d, eps, iters, transpose, seed = case
+    x, y, a, b = random_problem(n, m, d, seed, scale=1.0 / math.sqrt(d), shift=0.3)
+    eps = eps32(eps)
+    f, g = gpu_potentials(x, y, a, b, eps, iters)
+    rows_in = n if transpose else m
+    k = 40 if d >= 64 else 16
+    col_scale = np.array([10.0 ** (20 * ((c % 3) - 1)) for c in range(k)], dtype=np.float64)  # 1e-20, 1, 1e20
+    v = np.random.default_rng(seed + 50).normal(size=(rows_in, k)) * col_scale
+    v[:, 1] = 0.0
+    v = v.astype(np.float32)
+    say("transport columns far apart", case)
+    X, Y, A, B, F, G, Vt = dev(x, y, a, b, f, g, v)
+    got = host(sk.transport(X, Y, A, B, F, G, Vt, eps=eps, transpose=transpose))
+    want = T.transport(x, y, a, b, f, g, eps, v, transpose=transpose)
+    scale = T.transport(x, y, a, b, f, g, eps, np.abs(v), transpose=transpose)
+    kap = kappa(f, g, oracle.max_cost(x, y), eps)
+    err = np.abs(got - want)
+    say("max err / bound", (err / (32 * kap * scale + 1e-300)).max(), "kappa", kap)
+    assert np.all(got[:, 1] == 0.0)
+    assert np.all(err <= 32 * kap * scale + 1e-300)
+
+
 HVP_CASES = [
     # n, m, d, eps, solve iters, cg iters, seed
     (1, 6, 2, 0.3, 200, 20, 11),
