@@ -27,8 +27,9 @@
 // The solver pass and every transport mode (the d > 8 gradient among them)
 // take the cross term on fp16 matrix cores from a scaled two-part split of
 // every fp32 coordinate, within a few fp32 unit roundoffs per term (split2,
-// split_scores); the weighted key sums of the payload modes use fp32 matrix
-// instructions.
+// split_scores).  The weighted sums of the payload modes 0, 1 and 4 take the
+// same split form up to P = 128 (weights and payload in two fp16 parts each);
+// MODE 2 and P = 256 keep fp32 matrix instructions for them.
 #include "sk_internal.hpp"
 #include "sk_pass_common.hpp"
 
@@ -626,12 +627,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(pass_wav
 
 // Transport products for d > 8 (see sk_transport.hip for the d <= 8 kernel and
 // the quantities).  w_ij = 2^{s_ij - lse_i} <= 1 with lse from a first pass
-// over the same scores, and the payload sums accumulate with a second MFMA
-// whose A operand is the lane's own four weights:
+// over the same scores, and the payload sums accumulate with a second matrix
+// contraction over the keys whose A operand is the lane's own weights (eight
+// fp16 parts per 32 keys in the split form, four fp32 values per 16 keys
+// otherwise):
 //   T_i[col] = sum_j w_ij psi_j[col],   P psi = 2^{lse_i + h_i} T_i,
 //   row mass = 2^{lse_i + h_i} sum_j w_ij.
-//  MODE 0: psi_j = NP payload columns (16 * NP, zero-padded) staged in LDS;
-//  MODE 1: psi_j = the key's coordinates (read from an fp32 key tile);
+//  MODE 0: psi_j = NP payload columns (16 * NP, zero-padded);
+//  MODE 1: psi_j = the key's coordinates;
 //  MODE 2: the key's coordinates with w_ij (pay_j + <y~_j, 2 v_i>), the inner
 //          product taken on fp32 matrix instructions like the weighted sums;
 //  MODE 3: one payload column, summed with four vector FMAs per lane and
@@ -640,9 +643,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(pass_wav
 //          grad_i = 2 a_i (x~_i - T_i / S_i), S_i = sum_j w_ij (the plan's
 //          barycentric map; the plan scale cancels).
 // Every mode forms its scores in the fp16 split form of the solver pass (same
-// helpers and scales).  The weighted sums of MODES 1 and 4 up to P = 128 take
-// the fp16 split form too (weights and key coordinates as two fp16 parts each,
-// three products); the other modes and widths keep fp32 matrix instructions.
+// helpers and scales).  The weighted sums of MODES 0, 1 and 4 up to P = 128
+// take the fp16 split form too (split_sums: weights and payload as two fp16
+// parts each, three products, the payload split per launch by k_split_cols_t);
+// MODE 2 and P = 256 keep fp32 matrix instructions, the key coordinates read
+// from an fp32 key tile and a general payload from an fp32 payload tile.
 // 16-query blocks per wave of the transport kernel: their MFMA chains
 // interleave, at a register cost of NQB * P / 8 query VGPRs plus NQB output
 // tiles.
