@@ -876,7 +876,7 @@ TLayout make_tlayout(int64_t n, int64_t m, int d) {
     T.res = take(N * 4);
     T.p = take(N * 4);
     T.prod = take(N * 4);
-    T.scal = take(4 * sizeof(double));
+    T.scal = take((4 + 3 * kCgBlocks) * sizeof(double));
     T.total = off;
     return T;
 }

@@ -301,6 +301,8 @@ hipError_t launch_cg_init(int N, int n, const float* diag, const float* rhs, flo
 hipError_t launch_cg_step(int N, int n, const float* diag, const float* prod, float* z, float* zb, float* res, float* p,
                           double* scal, hipStream_t s);
 hipError_t launch_cg_report(const double* scal, float* out, hipStream_t s);
+// Workgroups of a CG step's kernels; the step's scalars take 4 + 3 kCgBlocks doubles.
+constexpr int kCgBlocks = 128;
 
 // Two-stage block-sparse solver pieces (sk_fs2.hip).
 hipError_t launch_bbox(const float* x, int n, const float* y, int m, int d, float* part, float* box, hipStream_t s);

@@ -308,14 +308,21 @@ __device__ inline double wg_sum(double v, double* sh) {
     return r;
 }
 
+// The CG kernels run in one workgroup: unrolling each strided loop by 8 keeps
+// eight elements' loads in flight per thread instead of one (each thread still
+// takes its elements, and sums them, in the same order).
+#define CG_UNROLL _Pragma("unroll 8")
+
 // res <- res - (<res, e> / N) e, then p = D^-1 res (init) and rz.
 __device__ inline double project_and_precondition(int N, int n, const float* __restrict__ diag, float* __restrict__ res,
                                                   float* __restrict__ pre_out, double* sh) {
     double re = 0.0;
+    CG_UNROLL
     for (int k = threadIdx.x; k < N; k += blockDim.x) re += k < n ? (double)res[k] : -(double)res[k];
     re = wg_sum(re, sh);
     const float mu = (float)(re / N);
     double rz = 0.0;
+    CG_UNROLL
     for (int k = threadIdx.x; k < N; k += blockDim.x) {
         const float rk = res[k] - (k < n ? mu : -mu);
         res[k] = rk;
@@ -332,6 +339,7 @@ __global__ __launch_bounds__(1024) void k_cg_init(int N, int n, const float* __r
                                                   float* __restrict__ zb, float* __restrict__ res,
                                                   float* __restrict__ p, double* __restrict__ scal) {
     __shared__ double sh[1024];
+    CG_UNROLL
     for (int k = threadIdx.x; k < N; k += blockDim.x) {
         z[k] = 0.0f;
         zb[k] = 0.0f;
@@ -343,48 +351,113 @@ __global__ __launch_bounds__(1024) void k_cg_init(int N, int n, const float* __r
         scal[0] = rz;
         scal[1] = rz;
         scal[2] = rz;
+        scal[3] = rz;
     }
 }
 
-__global__ __launch_bounds__(1024) void k_cg_step(int N, int n, const float* __restrict__ diag,
-                                                  const float* __restrict__ prod, float* __restrict__ z,
-                                                  float* __restrict__ zb, float* __restrict__ res,
-                                                  float* __restrict__ p, double* __restrict__ scal) {
-    __shared__ double sh[1024];
+// One CG step in four kernels over kCgBlocks workgroups (a single workgroup
+// is bound by one CU's bandwidth: 57 us per step at N = 32,768, 159 us at
+// 100,000).  Each kernel writes one partial per workgroup, and every
+// workgroup of the next reduces all of them with the same fixed tree, so the
+// scalars are bit-identical across workgroups and runs.  scal: [0] rz,
+// [1] rz at the start, [2] the best rz so far, [3] the step's new rz (committed
+// into [0] and [2] by the next step's first kernel, which reads neither),
+// [4 ..] the partials.
+static_assert(kCgBlocks <= kBlock, "a workgroup reduces all partials in one pass");
+__device__ inline double cg_total(const double* part, double* sh) {
+    return wg_sum(threadIdx.x < kCgBlocks ? part[threadIdx.x] : 0.0, sh);
+}
+
+// Commit the previous step's rz, then <p, K p> per workgroup.
+__global__ __launch_bounds__(kBlock) void k_cg_a(int N, const float* __restrict__ diag, const float* __restrict__ prod,
+                                                 const float* __restrict__ p, double* __restrict__ scal) {
+    __shared__ double sh[kBlock];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        const double rzn = scal[3];
+        if (rzn < scal[2]) scal[2] = rzn;
+        scal[0] = rzn;
+    }
     double pkp = 0.0;
-    for (int k = threadIdx.x; k < N; k += blockDim.x) {
+    CG_UNROLL
+    for (int k = blockIdx.x * kBlock + threadIdx.x; k < N; k += kCgBlocks * kBlock) {
         const float kp = fmaf(diag[k], p[k], prod[k]);
         pkp += (double)p[k] * (double)kp;
     }
     pkp = wg_sum(pkp, sh);
+    if (threadIdx.x == 0) scal[4 + blockIdx.x] = pkp;
+}
+
+// z += alpha p, res -= alpha K p, then <res, e> per workgroup (e = +1 on the
+// first n entries, -1 on the rest).
+__global__ __launch_bounds__(kBlock) void k_cg_b(int N, int n, const float* __restrict__ diag,
+                                                 const float* __restrict__ prod, const float* __restrict__ p,
+                                                 float* __restrict__ z, float* __restrict__ res,
+                                                 double* __restrict__ scal) {
+    __shared__ double sh[kBlock];
+    const double pkp = cg_total(scal + 4, sh);
     const double rz = scal[0];
     const float alpha = (pkp > 0.0 && rz > 0.0) ? (float)(rz / pkp) : 0.0f;
-    for (int k = threadIdx.x; k < N; k += blockDim.x) {
+    double re = 0.0;
+    CG_UNROLL
+    for (int k = blockIdx.x * kBlock + threadIdx.x; k < N; k += kCgBlocks * kBlock) {
         const float kp = fmaf(diag[k], p[k], prod[k]);
         z[k] = fmaf(alpha, p[k], z[k]);
-        res[k] = fmaf(-alpha, kp, res[k]);
+        const float r = fmaf(-alpha, kp, res[k]);
+        res[k] = r;
+        re += k < n ? (double)r : -(double)r;
     }
-    __syncthreads();
-    const double rz_new = project_and_precondition(N, n, diag, res, nullptr, sh);
+    re = wg_sum(re, sh);
+    if (threadIdx.x == 0) scal[4 + kCgBlocks + blockIdx.x] = re;
+}
+
+// res <- res - (<res, e> / N) e, then <res, D^-1 res> per workgroup.
+__global__ __launch_bounds__(kBlock) void k_cg_c(int N, int n, const float* __restrict__ diag, float* __restrict__ res,
+                                                 double* __restrict__ scal) {
+    __shared__ double sh[kBlock];
+    const float mu = (float)(cg_total(scal + 4 + kCgBlocks, sh) / N);
+    double rz = 0.0;
+    CG_UNROLL
+    for (int k = blockIdx.x * kBlock + threadIdx.x; k < N; k += kCgBlocks * kBlock) {
+        const float rk = res[k] - (k < n ? mu : -mu);
+        res[k] = rk;
+        const float dk = diag[k];
+        const float pre = dk > 0.0f ? rk / dk : 0.0f;
+        rz += (double)rk * (double)pre;
+    }
+    rz = wg_sum(rz, sh);
+    if (threadIdx.x == 0) scal[4 + 2 * kCgBlocks + blockIdx.x] = rz;
+}
+
+// p <- D^-1 res + beta p, keep z if this step's rz is the best so far, and
+// leave the new rz in scal[3].
+__global__ __launch_bounds__(kBlock) void k_cg_d(int N, const float* __restrict__ diag, const float* __restrict__ res,
+                                                 const float* __restrict__ z, float* __restrict__ p,
+                                                 float* __restrict__ zb, double* __restrict__ scal) {
+    __shared__ double sh[kBlock];
+    const double rz_new = cg_total(scal + 4 + 2 * kCgBlocks, sh);
+    const double rz = scal[0];
     const float beta = rz > 0.0 ? (float)(rz_new / rz) : 0.0f;
     const bool best = rz_new < scal[2];
-    for (int k = threadIdx.x; k < N; k += blockDim.x) {
+    CG_UNROLL
+    for (int k = blockIdx.x * kBlock + threadIdx.x; k < N; k += kCgBlocks * kBlock) {
         const float dk = diag[k];
         const float pre = dk > 0.0f ? res[k] / dk : 0.0f;
         p[k] = fmaf(beta, p[k], pre);
-        if (best) zb[k] = z[k];
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        scal[0] = rz_new;
-        if (best) scal[2] = rz_new;
+    if (best) {  // the same in every workgroup
+        CG_UNROLL
+        for (int k = blockIdx.x * kBlock + threadIdx.x; k < N; k += kCgBlocks * kBlock) zb[k] = z[k];
     }
+    if (blockIdx.x == 0 && threadIdx.x == 0) scal[3] = rz_new;
 }
 
 // sqrt(rz_best / rz0): the preconditioned residual of the kept iterate relative to the start.
+// The last step's rz is still pending in scal[3].
 __global__ void k_cg_report(const double* __restrict__ scal, float* __restrict__ out) {
-    if (threadIdx.x == 0 && blockIdx.x == 0)
-        out[0] = scal[1] > 0.0 ? (float)sqrt(fmax(scal[2], 0.0) / scal[1]) : 0.0f;
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        const double best = scal[3] < scal[2] ? scal[3] : scal[2];
+        out[0] = scal[1] > 0.0 ? (float)sqrt(fmax(best, 0.0) / scal[1]) : 0.0f;
+    }
 }
 
 inline int grid_of(int64_t count) { return (int)((count + kBlock - 1) / kBlock); }
@@ -446,7 +519,10 @@ hipError_t launch_cg_init(int N, int n, const float* diag, const float* rhs, flo
 
 hipError_t launch_cg_step(int N, int n, const float* diag, const float* prod, float* z, float* zb, float* res, float* p,
                           double* scal, hipStream_t s) {
-    hipLaunchKernelGGL(k_cg_step, dim3(1), dim3(1024), 0, s, N, n, diag, prod, z, zb, res, p, scal);
+    hipLaunchKernelGGL(k_cg_a, dim3(kCgBlocks), dim3(kBlock), 0, s, N, diag, prod, p, scal);
+    hipLaunchKernelGGL(k_cg_b, dim3(kCgBlocks), dim3(kBlock), 0, s, N, n, diag, prod, p, z, res, scal);
+    hipLaunchKernelGGL(k_cg_c, dim3(kCgBlocks), dim3(kBlock), 0, s, N, n, diag, res, scal);
+    hipLaunchKernelGGL(k_cg_d, dim3(kCgBlocks), dim3(kBlock), 0, s, N, diag, res, z, p, zb, scal);
     return hipGetLastError();
 }
 
