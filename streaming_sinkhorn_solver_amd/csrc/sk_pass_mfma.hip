@@ -212,21 +212,25 @@ __global__ __launch_bounds__(kBlock) void k_split_cols_t(const float* __restrict
 }
 
 // Largest |v[j ld + t]| over the nk rows of each column t < ncols (0 for
-// ncols <= t < KA); one workgroup per column.
-__global__ __launch_bounds__(kBlock) void k_col_absmax(const float* __restrict__ v, int nk, int ld, int ncols,
-                                                       float* __restrict__ out) {
+// ncols <= t < KS; out cleared to 0 first).  Thread x takes column x % KS of
+// every (kBlock / KS)-th row, so a wave reads whole rows; each workgroup then
+// folds its row lanes and adds its maxima with an integer atomicMax on the
+// bits of the non-negative floats, which orders them as the floats (the
+// result does not depend on the order of the workgroups).
+__global__ __launch_bounds__(kBlock) void k_col_absmax(const float* __restrict__ v, int nk, int ld, int ncols, int KS,
+                                                       unsigned* __restrict__ out) {
     __shared__ float sh[kBlock];
-    const int t = blockIdx.x;
+    const int c = threadIdx.x % KS, r0 = threadIdx.x / KS, rstep = kBlock / KS;
     float mx = 0.0f;
-    if (t < ncols)
-        for (int j = threadIdx.x; j < nk; j += kBlock) mx = fmaxf(mx, fabsf(v[(size_t)j * ld + t]));
+    if (c < ncols)
+        for (int j = blockIdx.x * rstep + r0; j < nk; j += gridDim.x * rstep)
+            mx = fmaxf(mx, fabsf(v[(size_t)j * ld + c]));
     sh[threadIdx.x] = mx;
     __syncthreads();
-    for (int w = kBlock / 2; w > 0; w >>= 1) {
-        if (threadIdx.x < w) sh[threadIdx.x] = fmaxf(sh[threadIdx.x], sh[threadIdx.x + w]);
-        __syncthreads();
+    if (r0 == 0) {
+        for (int r = 1; r < rstep; ++r) mx = fmaxf(mx, sh[r * KS + c]);
+        atomicMax(out + c, __float_as_uint(mx));
     }
-    if (threadIdx.x == 0) out[t] = sh[0];
 }
 
 // Register staging of one tile of TL keys of the transposed parts of P
@@ -988,7 +992,12 @@ hipError_t launch_transport_mfma_p(const TransArgs& a, hipStream_t s, hipEvent_t
         const dim3 sgrid((unsigned)((elems + kBlock - 1) / kBlock));
         if constexpr (MODE == 0) {
             if (!a.pay || !a.pmax || a.kin < 1 || a.kin > KS) return hipErrorInvalidValue;
-            hipLaunchKernelGGL(k_col_absmax, dim3(KS), dim3(kBlock), 0, s, a.pay, a.nk, a.ldp, a.kin, a.pmax);
+            static_assert(kBlock % KS == 0, "whole row lanes per workgroup");
+            const int rows = kBlock / KS;
+            const int gblocks = (int)std::min<int64_t>(256, ((int64_t)a.nk + rows - 1) / rows);
+            if (launch_fill(a.pmax, KS, 0.0f, s) != hipSuccess) return hipGetLastError();
+            hipLaunchKernelGGL(k_col_absmax, dim3(gblocks), dim3(kBlock), 0, s, a.pay, a.nk, a.ldp, a.kin, KS,
+                               reinterpret_cast<unsigned*>(a.pmax));
             hipLaunchKernelGGL(k_split_cols_t, sgrid, dim3(kBlock), 0, s, a.pay, a.nk, a.ldp, a.kin, KS,
                                (const float*)a.pmax, 1, a.kt);
         } else {
