@@ -486,6 +486,14 @@ __device__ __forceinline__ void load_keys(float (&kf)[KT], const float* ktile, i
     }
 }
 
+// The larger of two scores, NaN-propagating (IEEE 754-2019 maximum). On
+// gfx950 this is v_maximum3_f32, which takes three operands and reads matrix
+// results as they are; fmaxf, whose NaN rule drops a quiet NaN, first quiets
+// each matrix result with one v_max_f32 of its own (nine instructions for the
+// nine candidates of one update instead of four).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 // Online log-sum-exp over the four scores a lane holds for one 16-key block.
 // Scores, M and the candidates are in the pass's scaled units (times t); the
 // exponents are taken back to base-2 units with one fma each, fma(x, r, -mn r)
@@ -493,8 +501,7 @@ __device__ __forceinline__ void load_keys(float (&kf)[KT], const float* ktile, i
 // M starts at SplitScale::m0, so -mn r is finite and an empty key set gives
 // fma(-inf, r, finite) = -inf, never inf - inf.
 __device__ __forceinline__ void lse_block(float& M, float& S, const f4 acc, float r) {
-    const float mt = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-    const float mn = fmaxf(M, mt);
+    const float mn = vmax3(vmax3(acc[0], acc[1], acc[2]), acc[3], M);
     const float nm = -mn * r;
     float s = S * ex2(fmaf(M, r, nm));
 #pragma unroll
@@ -505,8 +512,7 @@ __device__ __forceinline__ void lse_block(float& M, float& S, const f4 acc, floa
 
 // The same over the eight scores of two 16-key blocks (one rescale for both).
 __device__ __forceinline__ void lse_block2(float& M, float& S, const f4 a, const f4 b, float r) {
-    const float mt = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
-    const float mn = fmaxf(M, mt);
+    const float mn = vmax3(vmax3(a[0], a[1], a[2]), vmax3(a[3], b[0], b[1]), vmax3(b[2], b[3], M));
     const float nm = -mn * r;
     float s = S * ex2(fmaf(M, r, nm));
 #pragma unroll
@@ -518,7 +524,7 @@ __device__ __forceinline__ void lse_block2(float& M, float& S, const f4 a, const
 }
 
 __device__ __forceinline__ void lse_merge(float& M, float& S, float m2, float s2, float r) {
-    const float mn = fmaxf(M, m2);
+    const float mn = vmax(M, m2);
     const float nm = -mn * r;
     S = S * ex2(fmaf(M, r, nm)) + s2 * ex2(fmaf(m2, r, nm));
     M = mn;
