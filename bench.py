@@ -236,6 +236,54 @@ def load_traffic(kernel_key: str, family: str, kernel: str):
     return entry.get("bytes_per_launch")
 
 
+def counter_per_launch(run_dir: str, counter: str, kernel_pattern: str, largest: bool = False) -> float:
+    """KiB per dispatch of one rocprofv3 --pmc counter for the kernels whose name
+    contains kernel_pattern, averaged over their dispatches (or the largest
+    dispatch, for the calibration copy), from the CSV files under run_dir."""
+    import csv
+    import glob
+
+    per = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter or kernel_pattern not in row.get("Kernel_Name", ""):
+                    continue
+                key = (path, row.get("Dispatch_Id") or row.get("Correlation_Id"))
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} records of a kernel named like {kernel_pattern!r} under {run_dir}")
+    vals = list(per.values())
+    return max(vals) if largest else sum(vals) / len(vals)
+
+
+def record_traffic(key: str, kernel: str, family: str, fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
+    """Writes the calibrated HBM bytes per launch of `kernel` into the traffic
+    record: FETCH_SIZE and WRITE_SIZE (KiB, separate runs of bench.py with
+    --copy-calibration copy_mib under rocprofv3 --pmc), each divided by what the
+    same counter reads for the copy of known size in the same run."""
+    pattern = kernel + "("
+    true_kib = copy_mib * 1024.0
+    fetch = counter_per_launch(fetch_dir, "FETCH_SIZE", pattern)
+    write = counter_per_launch(write_dir, "WRITE_SIZE", pattern)
+    fetch_factor = counter_per_launch(fetch_dir, "FETCH_SIZE", "copyBuffer", largest=True) / true_kib
+    write_factor = counter_per_launch(write_dir, "WRITE_SIZE", "copyBuffer", largest=True) / true_kib
+    entry = {"kernel": kernel,
+             "bytes_per_launch": (fetch / fetch_factor + write / write_factor) * 1024.0,
+             "fetch_kib_raw": fetch, "write_kib_raw": write,
+             "fetch_factor": fetch_factor, "write_factor": write_factor,
+             "source_sha256": kernel_source_hash(family), "sources": KERNEL_SOURCES[family]}
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        rec = {}
+    rec[key] = entry
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return entry
+
+
 def run_ceilings():
     import ctypes
 
@@ -369,7 +417,22 @@ def main():
     ap.add_argument("--alpha", type=float, default=0.5, help="blend of the symmetric variant")
     ap.add_argument("--stop-tol", type=float, default=1e-5, help="tolerance of the marginal / potential stop rule")
     ap.add_argument("--check-every", type=int, default=10, help="check interval of the stop rules")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("KEY", "FAMILY", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the calibrated HBM bytes per launch of the workload's dominant pass kernel (FAMILY "
+                         "valu or mfma) from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into the traffic "
+                         "record under KEY, and exit (no GPU use; needs --copy-calibration and --dim as in the runs)")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        key, family, fetch_dir, write_dir = args.record_traffic
+        if not args.copy_calibration:
+            sys.exit("--record-traffic needs --copy-calibration MIB, the size the runs copied")
+        from sk_inputs import WORKLOADS
+
+        d = args.dim or WORKLOADS[args.workload].d
+        kernel = f"k_pass_valu<{d}>" if family == "valu" else f"k_pass_mfma<{packed_stride(d)}>"
+        print(json.dumps(record_traffic(key, kernel, family, fetch_dir, write_dir, args.copy_calibration)))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "

@@ -94,3 +94,31 @@ def test_inputs_dimension_override():
     assert (x == x2).all()  # seeded
     x64, _, _, _ = make_inputs("gauss_d64", n=40, m=30)
     assert x64.shape == (40, 64)
+
+
+def test_record_traffic_from_counter_csv(tmp_path, monkeypatch):
+    # two rocprofv3-style counter CSVs: the pass launched twice, one 256 MiB calibration copy and a small copy
+    header = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+
+    def write(run, counter, copy_kib, pass_kib):
+        d = tmp_path / run / "host" / "123"
+        d.mkdir(parents=True)
+        rows = [f'1,"__amd_rocclr_copyBuffer",{counter},40.0',
+                f'2,"__amd_rocclr_copyBuffer",{counter},{copy_kib}',
+                f'3,"void sk::(anonymous namespace)::k_pass_valu<3>(sk::PassArgs)",{counter},{pass_kib[0]}',
+                f'4,"void sk::(anonymous namespace)::k_merge(sk::PassArgs)",{counter},999.0',
+                f'5,"void sk::(anonymous namespace)::k_pass_valu<3>(sk::PassArgs)",{counter},{pass_kib[1]}']
+        (d / "p_counter_collection.csv").write_text(header + "\n".join(rows) + "\n")
+        return str(tmp_path / run)
+
+    fetch_dir = write("fetch", "FETCH_SIZE", 131072.0, (3000.0, 3200.0))  # FETCH reads half the true bytes
+    write_dir = write("write", "WRITE_SIZE", 262144.0, (6400.0, 6400.0))
+    rec = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(rec))
+    e = bench.record_traffic("w:pass", "k_pass_valu<3>", "valu", fetch_dir, write_dir, 256)
+    assert e["fetch_factor"] == 0.5 and e["write_factor"] == 1.0
+    assert e["fetch_kib_raw"] == 3100.0 and e["write_kib_raw"] == 6400.0
+    assert e["bytes_per_launch"] == (6200.0 + 6400.0) * 1024.0
+    # the record is read back while the kernel's sources hash the same
+    assert bench.load_traffic("w:pass", "valu", "k_pass_valu<3>") == e["bytes_per_launch"]
+    assert bench.load_traffic("w:pass", "mfma", "k_pass_valu<3>") is None
