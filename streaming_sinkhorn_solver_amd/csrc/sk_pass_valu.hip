@@ -484,19 +484,31 @@ __global__ __launch_bounds__(kBlock) void k_pass_small(PassArgs A) {
 // xor-shuffle tree joins them (the order is fixed, so results are repeatable).
 constexpr int kMergeLanes = 8;
 
+//
+// A wave's 64 lanes hold 64 / kMergeLanes consecutive rows from a multiple of
+// that count, and a row block (rpb rows, a multiple of it) never splits such a
+// group, so the row block and its range bookkeeping are wave-uniform: taken
+// from the first lane, they are computed once per wave on the scalar unit
+// instead of as 64-bit divisions in every lane. Of the ranges that meet the
+// block only the first, wf, can start before it (the owner of u0 is the last
+// range starting at or before u0), so its range start decides the one slot
+// that is not 0.
+static_assert(kPassRows % kMergeLanes == 0 && 64 % kMergeLanes == 0, "a lane group never splits a row block");
+
 __global__ __launch_bounds__(kBlock) void k_merge(PassArgs A) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     const int i = t / kMergeLanes, sub = t % kMergeLanes;
     const bool live = i < A.nq;
     const int ic = live ? i : A.nq - 1;
-    const int rb = ic / A.rpb, lr = ic - rb * A.rpb;
+    const int rb = __builtin_amdgcn_readfirstlane(ic / A.rpb), lr = ic - rb * A.rpb;
     const int64_t u0 = (int64_t)rb * A.nk, u1 = u0 + A.nk;
     const int wf = range_owner(u0, A.total, A.W), wl = range_owner(u1 - 1, A.total, A.W);
+    const bool first_starts_before = range_lo(wf, A.total, A.W) < u0;
     // the row's finalisation inputs, loaded now so that their latency overlaps the partials' loads
     const FinIn pre = fin_load(A.fin, ic);
     float M = kNegBig, S = 0.0f;
     for (int w = wf + sub; w <= wl; w += kMergeLanes) {
-        const int slot = range_lo(w, A.total, A.W) >= u0 ? 0 : 1;
+        const int slot = (w == wf && first_starts_before) ? 1 : 0;
         const float2 p = A.part[((size_t)w * 2 + slot) * A.rpb + lr];
         const float mn = fmaxf(M, p.x);
         S = S * ex2(M - mn) + p.y * ex2(p.x - mn);
@@ -668,6 +680,7 @@ int valu_rows_per_block() { return kPassRows; }
 int valu_block_rows() { return kBlock * kR; }
 
 hipError_t launch_merge(const PassArgs& a, hipStream_t s) {
+    if (a.rpb % (64 / kMergeLanes) != 0) return hipErrorInvalidValue;  // k_merge takes a wave's row block as uniform
     const int64_t n_row_blocks = a.total / a.nk;
     if (a.W > n_row_blocks || a.total % a.W != 0 || (a.total / a.W) % a.nk != 0)
         hipLaunchKernelGGL(k_merge, dim3(((int64_t)a.nq * kMergeLanes + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a);
