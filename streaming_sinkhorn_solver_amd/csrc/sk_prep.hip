@@ -194,6 +194,10 @@ __global__ __launch_bounds__(kBlock) void k_check_final(const double* __restrict
     result[3] = sb;
 }
 
+// Elements a thread of the single-workgroup reductions loads before it folds
+// them in: their loads are in flight together instead of one latency each.
+constexpr int kRedUnroll = 8;
+
 // Cost: one workgroup walks both vectors in a fixed order with float64 sums.
 // With `mass` (per-row plan sums) the plan mass is their sum; without it the
 // potentials are taken to come out of a column half-step, whose plan mass is sum(b).
@@ -203,13 +207,45 @@ __global__ __launch_bounds__(1024) void k_cost(const float* __restrict__ a, cons
                                                double* __restrict__ out) {
     __shared__ double sh[1024];
     double af = 0.0, sa = 0.0, bg = 0.0, sb = 0.0, mp = 0.0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int T = blockDim.x;
+    int i = threadIdx.x;
+    // kRedUnroll elements per thread in flight at once, summed in the same order as one at a time
+    for (; i + (kRedUnroll - 1) * T < n; i += kRedUnroll * T) {
+        float av[kRedUnroll], fv[kRedUnroll], mv[kRedUnroll];
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            av[k] = a[i + k * T];
+            fv[k] = f[i + k * T];
+            mv[k] = mass ? mass[i + k * T] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            if (av[k] != 0.0f) af += (double)av[k] * (double)fv[k];
+            sa += (double)av[k];
+            if (mass) mp += (double)mv[k];
+        }
+    }
+    for (; i < n; i += T) {
         float ai = a[i];
         if (ai != 0.0f) af += (double)ai * (double)f[i];
         sa += (double)ai;
         if (mass) mp += (double)mass[i];
     }
-    for (int j = threadIdx.x; j < m; j += blockDim.x) {
+    int j = threadIdx.x;
+    for (; j + (kRedUnroll - 1) * T < m; j += kRedUnroll * T) {
+        float bv[kRedUnroll], gv[kRedUnroll];
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            bv[k] = b[j + k * T];
+            gv[k] = g[j + k * T];
+        }
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            if (bv[k] != 0.0f) bg += (double)bv[k] * (double)gv[k];
+            sb += (double)bv[k];
+        }
+    }
+    for (; j < m; j += T) {
         float bj = b[j];
         if (bj != 0.0f) bg += (double)bj * (double)g[j];
         sb += (double)bj;
@@ -320,7 +356,19 @@ __global__ __launch_bounds__(1024) void k_resid_reduce(const float* __restrict__
     __shared__ float shf[1024];
     float mx = 0.0f;
     double sm = 0.0;
-    for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+    const int T = blockDim.x;
+    int i = threadIdx.x;
+    for (; i + (kRedUnroll - 1) * T < cnt; i += kRedUnroll * T) {
+        float v[kRedUnroll];
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) v[k] = r[i + k * T];
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            mx = max_nan(mx, v[k]);
+            sm += (double)v[k];
+        }
+    }
+    for (; i < cnt; i += T) {
         float v = r[i];
         mx = max_nan(mx, v);
         sm += (double)v;
@@ -339,7 +387,16 @@ __global__ __launch_bounds__(1024) void k_max_reduce(const float* __restrict__ v
                                                      int* flag, int seq) {
     __shared__ float shw[16];
     float mx = -INFINITY;
-    for (int i = threadIdx.x; i < cnt; i += blockDim.x) mx = max_nan(mx, v[i]);
+    const int T = blockDim.x;
+    int i = threadIdx.x;
+    for (; i + (kRedUnroll - 1) * T < cnt; i += kRedUnroll * T) {
+        float w[kRedUnroll];
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) w[k] = v[i + k * T];
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) mx = max_nan(mx, w[k]);
+    }
+    for (; i < cnt; i += T) mx = max_nan(mx, v[i]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = max_nan(mx, __shfl_xor(mx, off));
     const int wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
