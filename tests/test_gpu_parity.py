@@ -273,6 +273,34 @@ def test_residual_trace_matches_oracle_at_same_iterates():
         assert abs(tr[idx] - max(ro[0], ro[1])) <= 32 * kap * (a.max() + ro[0]), (k, tr[idx], ro)
 
 
+# Sizes around one round of the one-workgroup reductions (1024 threads x 8 loads = 8192 elements) on each side.
+REDUCTION_SHAPES = [(1, 7), (7, 8192), (1023, 8193), (8191, 300), (8192, 1), (8193, 9000), (16385, 64), (24577, 100)]
+
+
+@pytest.mark.parametrize("n,m", REDUCTION_SHAPES)
+def test_reductions_across_unroll_boundaries(n, m):
+    """The cost equals its float64 sum at the GPU's own potentials, and the fused residual trace the oracle's
+    residual at the same iterates, at sizes below, at and past whole rounds of the reductions' loads."""
+    x, y, a, b = random_problem(n, m, 2, 97 + n % 13, zero_frac=0.05)
+    eps = eps32(0.1)
+    X, Y, A, B = dev(x, y, a, b)
+    say("reductions", (n, m))
+    f_t, g_t, tr_t = sk.solve(X, Y, A, B, eps=eps, n_iters=6, check_every=3)
+    f, g, tr = host(f_t), host(g_t), host(tr_t)
+    c = float(host(sk.cost(A, B, f_t, g_t, eps=eps))[0])
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    ka, kb = a != 0, b != 0  # zero weights add nothing (their potentials are not read)
+    af, bg = np.dot(a64[ka], f[ka]), np.dot(b64[kb], g[kb])
+    c_ref = float(af + bg - eps * b64.sum() * (1.0 - a64.sum()))
+    scale = np.dot(a64[ka], np.abs(f[ka])) + np.dot(b64[kb], np.abs(g[kb])) + eps * b64.sum()
+    say("cost err / scale", abs(c - c_ref) / scale)
+    assert abs(c - c_ref) <= 1e-12 * scale
+    ro = oracle.residual(x, y, a, b, f, g, eps)
+    kap = kappa(f, g, oracle.max_cost(x, y), eps)
+    assert tr.shape == (2,)
+    assert abs(tr[-1] - max(ro[0], ro[1])) <= 32 * kap * (a.max() + ro[0]), (tr[-1], ro)
+
+
 def test_deterministic_and_zero_iterations():
     x, y, a, b = random_problem(3000, 2000, 3, 41)
     say("determinism")
