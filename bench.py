@@ -406,7 +406,7 @@ def main():
                     help="time every k-th pass launch with HIP events (odd, so row and column passes alternate)")
     ap.add_argument("--mode", default="solve",
                     choices=["solve", "symmetric", "marginal", "potential", "divergence", "flow", "hvp", "transport", "grad",
-                             "fs2"])
+                             "fs2", "primal"])
     ap.add_argument("--fs2-block", type=int, default=512)
     ap.add_argument("--fs2-tol-rel", type=float, default=0.01, help="target residual / largest point mass")
     ap.add_argument("--fs2-delta", type=float, default=1e-6)
@@ -486,7 +486,7 @@ def main():
         fs2_tol = args.fs2_tol_rel * float(max(A.max().item(), B.max().item()))
         nb = sk.load_library().sk_fs2_workspace_bytes(n, m, d, args.fs2_block, 1024)
         ws_fs2 = torch.empty(nb, dtype=torch.uint8, device=dev)
-    if mode in ("hvp", "transport", "grad"):
+    if mode in ("hvp", "transport", "grad", "primal"):
         # potentials of a full solve, outside the timed region
         sk.solve(X, Y, A, B, eps=eps, n_iters=n_iters, ws=ws, f=f, g=g, check=False)
         ws_t = sk.transport_workspace(n, m, d, dev)
@@ -495,6 +495,7 @@ def main():
         cg_res = torch.empty(1, dtype=torch.float32, device=dev)
         y_pay = Y.contiguous()
     dv_out = torch.empty(4, dtype=torch.float64, device=dev)
+    primal_out = torch.empty(2, dtype=torch.float64, device=dev)
     ws_div = sk.divergence_workspace(n, m, d, dev) if mode == "divergence" else None
 
     def step():
@@ -519,6 +520,8 @@ def main():
             sk.transport(X, Y, A, B, f, g, y_pay, eps=eps, ws=ws_t, out=hv_out)
         elif mode == "grad":
             sk.grad_x(X, Y, A, B, g, eps=eps, ws=ws, out=grad)
+        elif mode == "primal":
+            sk.primal_cost(X, Y, A, B, f, g, eps=eps, ws=ws_t, out=primal_out)
         elif mode == "fs2":
             _, _, inf = sk.fs2_solve(X, Y, A, B, eps=eps, block=args.fs2_block, tol=fs2_tol, delta=args.fs2_delta,
                                      max_iters=args.fs2_max_iters, ws=ws_fs2, f=f, g=g, check=False)
@@ -575,7 +578,9 @@ def main():
     if mode == "transport":
         pair_evals = 1.0 * n * m
     if mode == "grad":
-        pair_evals = (2.0 if d > 8 else 1.0) * n * m  # d > 8: the store-lse pass, then the weighted sums
+        pair_evals = (2.0 if d > 8 else 1.0) * n * m
+    if mode == "primal":
+        pair_evals = (3.0 if d > 8 else 2.0) * n * m  # (d > 8: the store-lse pass,) the weighted row pass, the column pass  # d > 8: the store-lse pass, then the weighted sums
     if mode == "fs2":
         pair_evals = 2.0 * n * m * fs2_info["fine_iters"]
     extra = {}
@@ -655,7 +660,9 @@ def main():
     value = pair_evals / step_s
     avg_launch_s = pass_ms * 1e-3 / launches if launches else float("nan")
     pairs_per_launch = pairs / launches if launches else float("nan")
-    if mode == "fs2":
+    if mode == "primal":
+        roof = None  # two kinds of pass per call (a weighted transport pass and a column pass): timed as a whole
+    elif mode == "fs2":
         # the block-sparse pass over the kept tiles: the dense pass's per-pair work
         roof = roofline_alu(d, pairs_per_launch, avg_launch_s) if launches else None
         if roof is not None:
@@ -726,10 +733,11 @@ def main():
         "iters_per_s": (3 * n_iters if mode == "divergence" else
                         fs2_info["fine_iters"] if mode == "fs2" else counted_iters) / step_s,
         "hip_graph": bool(args.graph),
-        "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s if launches else None,
+        "pass_pair_evals_per_s": pairs_per_launch / avg_launch_s if (launches and mode != "primal") else None,
         "roofline": roof,
         "final_residual": float(trace[n_iters // ce - 1].item()) if (ce and mode == "solve") else None,
-        "cost": float(cost_out.item()) if mode not in ("divergence", "hvp", "transport", "fs2") else None,
+        "cost": (float(cost_out.item()) if mode not in ("divergence", "hvp", "transport", "fs2", "primal") else
+                 float(primal_out[0].item()) if mode == "primal" else None),
         **extra,
     }
     if not args.no_cpu_baseline and mode == "solve":

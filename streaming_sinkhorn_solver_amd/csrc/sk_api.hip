@@ -837,7 +837,7 @@ int dual_cost(const Ws& W, const float* x, const float* y, const float* a, const
 struct TLayout {
     Layout L;
     size_t part, partA;
-    size_t A, st, U, B, E, diag, rhs, z, zb, res, p, prod, scal;
+    size_t A, st, U, B, E, diag, rhs, z, zb, res, p, prod, scal, pv;
     size_t total;
 };
 constexpr int kTransMaxK = 9;  // payload columns per vector-ALU transport pass
@@ -877,6 +877,7 @@ TLayout make_tlayout(int64_t n, int64_t m, int d) {
     T.p = take(N * 4);
     T.prod = take(N * 4);
     T.scal = take((4 + 3 * kCgBlocks) * sizeof(double));
+    T.pv = take(un * sizeof(double));  // the primal value's per-row terms
     T.total = off;
     return T;
 }
@@ -1523,7 +1524,8 @@ int sk_primal_cost(const float* x, const float* y, const float* a, const float* 
     col.fin.pot_in = g;
     col.fin.rbuf = c;
     if ((st = run_pass(W, col, s))) return st;
-    SK_TRY(launch_primal(a, b, f, g, r, c, W.f(L.xp), L.P, d, W.f(L.nx), Tr, (int)n, (int)m, eps, out, s));
+    SK_TRY(launch_primal(a, b, f, g, r, c, W.f(L.xp), L.P, d, W.f(L.nx), Tr, (int)n, (int)m, eps,
+                         reinterpret_cast<double*>(W.f(T.pv)), out, s));
     return SK_OK;
 }
 

@@ -269,10 +269,10 @@ hipError_t launch_cost_mass(const float* a, const float* b, const float* f, cons
 // U (m x (d + 1)) = [y~_j, |y~_j|^2], the payload of the plan's transport cost.
 hipError_t launch_primal_payload(const float* yp, int P, int d, const float* ny, int m, float* U, hipStream_t s);
 // out[0] = <P,C> + eps KL(P | a x b), out[1] = <P,C> from the plan's row sums r, column sums c and per-row
-// payload sums T (n x (d + 1)) of U.
+// payload sums T (n x (d + 1)) of U; pv is scratch for n doubles (each row's share of <P,C>).
 hipError_t launch_primal(const float* a, const float* b, const float* f, const float* g, const float* r,
                          const float* c, const float* xp, int P, int d, const float* nx, const float* T, int n,
-                         int m, float eps, double* out, hipStream_t s);
+                         int m, float eps, double* pv, double* out, hipStream_t s);
 // Transport products (sk_transport.hip).  mode 0: K-column payload, kwidth in
 // {1, 4, 9} (>= kin); mode 2: the Hessian-vector product's weighted pass.
 int transport_rows_per_block();

@@ -275,28 +275,79 @@ __global__ __launch_bounds__(kBlock) void k_primal_payload(const float* __restri
 // common shift).  With log(P_ij / (a_i b_j)) = (f_i + g_j - C_ij)/eps the generalised KL term collapses:
 //   out[0] = <P,C> + eps KL(P | a x b) = sum_i f_i r_i + sum_j g_j c_j - eps (sum_i r_i - sum(a) sum(b)),
 //   out[1] = <P,C> = sum_i (r_i |x~_i|^2 - 2 <x~_i, T_i> + T_i[d]).
-// One workgroup, float64 sums in a fixed order; rows and columns of zero weight carry no plan mass.
+// Each row's term of out[1] is formed by one thread per row over the whole grid (k_primal_rows, the
+// coordinates in order); one workgroup then takes all the float64 sums in a fixed order (k_primal). Rows
+// and columns of zero weight carry no plan mass.
+__global__ __launch_bounds__(kBlock) void k_primal_rows(const float* __restrict__ a, const float* __restrict__ r,
+                                                        const float* __restrict__ xp, int P, int d,
+                                                        const float* __restrict__ nx, const float* __restrict__ T,
+                                                        int n, double* __restrict__ pv) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    if (a[i] == 0.0f) {
+        pv[i] = 0.0;
+        return;
+    }
+    const double ri = (double)r[i];
+    const float* t = T + (size_t)i * (d + 1);
+    double dot = 0.0;
+    for (int k = 0; k < d; ++k) dot += (double)xp[(size_t)i * P + k] * (double)t[k];
+    pv[i] = ri * (double)nx[i] - 2.0 * dot + (double)t[d];
+}
+
 __global__ __launch_bounds__(1024) void k_primal(const float* __restrict__ a, const float* __restrict__ b,
                                                  const float* __restrict__ f, const float* __restrict__ g,
                                                  const float* __restrict__ r, const float* __restrict__ c,
-                                                 const float* __restrict__ xp, int P, int d,
-                                                 const float* __restrict__ nx, const float* __restrict__ T,
-                                                 int n, int m, float eps, double* __restrict__ out) {
+                                                 const double* __restrict__ pv, int n, int m, float eps,
+                                                 double* __restrict__ out) {
     __shared__ double sh[1024];
     double fr = 0.0, gc = 0.0, mp = 0.0, sa = 0.0, sb = 0.0, pc = 0.0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int T = blockDim.x;
+    int i = threadIdx.x;
+    for (; i + (kRedUnroll - 1) * T < n; i += kRedUnroll * T) {
+        float av[kRedUnroll], rv[kRedUnroll], fv[kRedUnroll];
+        double pw[kRedUnroll];
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            av[k] = a[i + k * T];
+            rv[k] = r[i + k * T];
+            fv[k] = f[i + k * T];
+            pw[k] = pv[i + k * T];
+        }
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            sa += (double)av[k];
+            if (av[k] == 0.0f) continue;
+            fr += (double)fv[k] * (double)rv[k];
+            mp += (double)rv[k];
+            pc += pw[k];
+        }
+    }
+    for (; i < n; i += T) {
         const float ai = a[i];
         sa += (double)ai;
         if (ai == 0.0f) continue;
         const double ri = (double)r[i];
         fr += (double)f[i] * ri;
         mp += ri;
-        const float* t = T + (size_t)i * (d + 1);
-        double dot = 0.0;
-        for (int k = 0; k < d; ++k) dot += (double)xp[(size_t)i * P + k] * (double)t[k];
-        pc += ri * (double)nx[i] - 2.0 * dot + (double)t[d];
+        pc += pv[i];
     }
-    for (int j = threadIdx.x; j < m; j += blockDim.x) {
+    int j = threadIdx.x;
+    for (; j + (kRedUnroll - 1) * T < m; j += kRedUnroll * T) {
+        float bv[kRedUnroll], gv[kRedUnroll], cv[kRedUnroll];
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            bv[k] = b[j + k * T];
+            gv[k] = g[j + k * T];
+            cv[k] = c[j + k * T];
+        }
+#pragma unroll
+        for (int k = 0; k < kRedUnroll; ++k) {
+            sb += (double)bv[k];
+            if (bv[k] != 0.0f) gc += (double)gv[k] * (double)cv[k];
+        }
+    }
+    for (; j < m; j += T) {
         const float bj = b[j];
         sb += (double)bj;
         if (bj != 0.0f) gc += (double)g[j] * (double)c[j];
@@ -469,8 +520,9 @@ hipError_t launch_primal_payload(const float* yp, int P, int d, const float* ny,
 
 hipError_t launch_primal(const float* a, const float* b, const float* f, const float* g, const float* r,
                          const float* c, const float* xp, int P, int d, const float* nx, const float* T, int n,
-                         int m, float eps, double* out, hipStream_t s) {
-    hipLaunchKernelGGL(k_primal, dim3(1), dim3(1024), 0, s, a, b, f, g, r, c, xp, P, d, nx, T, n, m, eps, out);
+                         int m, float eps, double* pv, double* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_primal_rows, dim3(grid_for(n, kBlock)), dim3(kBlock), 0, s, a, r, xp, P, d, nx, T, n, pv);
+    hipLaunchKernelGGL(k_primal, dim3(1), dim3(1024), 0, s, a, b, f, g, r, c, pv, n, m, eps, out);
     return hipGetLastError();
 }
 
