@@ -176,22 +176,29 @@ __global__ __launch_bounds__(kBlock) void k_check_partial(const float* __restric
 }
 
 // result: [nonfinite, negative weight, sum a, sum b]; partials holds 4 arrays x, y, a, b.
+// One workgroup: each thread folds a fixed stride of the 4 nblk partial records, then fixed-order trees.
 __global__ __launch_bounds__(kBlock) void k_check_final(const double* __restrict__ partial, int nblk,
                                                         double* __restrict__ result) {
-    if (threadIdx.x != 0) return;
+    __shared__ double sh[kBlock];
     double bad = 0.0, neg = 0.0, sa = 0.0, sb = 0.0;
-    for (int arr = 0; arr < 4; ++arr)
-        for (int b = 0; b < nblk; ++b) {
-            const double* p = partial + (size_t)(arr * nblk + b) * 3;
-            bad += p[0];
-            if (arr >= 2) neg += p[1];
-            if (arr == 2) sa += p[2];
-            if (arr == 3) sb += p[2];
-        }
-    result[0] = bad;
-    result[1] = neg;
-    result[2] = sa;
-    result[3] = sb;
+    for (int e = threadIdx.x; e < 4 * nblk; e += blockDim.x) {
+        const int arr = e / nblk;
+        const double* p = partial + (size_t)e * 3;
+        bad += p[0];
+        if (arr >= 2) neg += p[1];
+        if (arr == 2) sa += p[2];
+        if (arr == 3) sb += p[2];
+    }
+    bad = block_sum_f64(bad, sh);
+    neg = block_sum_f64(neg, sh);
+    sa = block_sum_f64(sa, sh);
+    sb = block_sum_f64(sb, sh);
+    if (threadIdx.x == 0) {
+        result[0] = bad;
+        result[1] = neg;
+        result[2] = sa;
+        result[3] = sb;
+    }
 }
 
 // Elements a thread of the single-workgroup reductions loads before it folds
@@ -381,15 +388,31 @@ __global__ __launch_bounds__(1024) void k_pot_change(const float* __restrict__ f
                                                      float* __restrict__ out, int* flag, int seq) {
     __shared__ float shf[1024];
     float mx = 0.0f;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const float v = f[i];
-        mx = max_nan(mx, fabsf(v - sf[i]));
-        sf[i] = v;
-    }
-    for (int j = threadIdx.x; j < m; j += blockDim.x) {
-        const float v = g[j];
-        mx = max_nan(mx, fabsf(v - sg[j]));
-        sg[j] = v;
+    const int T = blockDim.x;
+    // each side: kRedUnroll elements per thread loaded at once (a max does not depend on the order)
+    for (int side = 0; side < 2; ++side) {
+        const float* __restrict__ v = side ? g : f;
+        float* __restrict__ sv = side ? sg : sf;
+        const int cnt = side ? m : n;
+        int i = threadIdx.x;
+        for (; i + (kRedUnroll - 1) * T < cnt; i += kRedUnroll * T) {
+            float cur[kRedUnroll], old[kRedUnroll];
+#pragma unroll
+            for (int k = 0; k < kRedUnroll; ++k) {
+                cur[k] = v[i + k * T];
+                old[k] = sv[i + k * T];
+            }
+#pragma unroll
+            for (int k = 0; k < kRedUnroll; ++k) {
+                mx = max_nan(mx, fabsf(cur[k] - old[k]));
+                sv[i + k * T] = cur[k];
+            }
+        }
+        for (; i < cnt; i += T) {
+            const float c = v[i];
+            mx = max_nan(mx, fabsf(c - sv[i]));
+            sv[i] = c;
+        }
     }
     mx = block_max_f32(mx, shf);
     if (threadIdx.x == 0) publish(out, mx, flag, seq);
@@ -550,7 +573,7 @@ hipError_t launch_check(const float* x, const float* y, const float* a, const fl
     for (int k = 0; k < 4; ++k)
         hipLaunchKernelGGL(k_check_partial, dim3(kRedBlocks), dim3(kBlock), 0, s, arrs[k], lens[k],
                            partials + (size_t)k * kRedBlocks * 3);
-    hipLaunchKernelGGL(k_check_final, dim3(1), dim3(64), 0, s, partials, kRedBlocks, result);
+    hipLaunchKernelGGL(k_check_final, dim3(1), dim3(kBlock), 0, s, partials, kRedBlocks, result);
     return hipGetLastError();
 }
 
